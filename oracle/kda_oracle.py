@@ -1,0 +1,191 @@
+"""fp64 reference for the segmented KDA forward pass (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It is deliberately slow and literal: one token at
+a time, no chunking, no blocking, no reordering beyond what the definitions
+below state.  See ``oracle/__init__.py`` for the page citations.
+
+Arrays (numpy, float64 after decoding):
+    q, k, g : [T, H, K]      packed-THD, tokens of all sequences back to back
+    v       : [T, H, V]
+    beta    : [T, H]
+    cu_seqlens : [N+1] int   sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+State matrices are [H, K, V] (K-major, "non-transposed").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16",
+    "kda_step",
+    "recurrence",
+    "segment_updates",
+    "segment_transitions",
+    "compose",
+    "compose_pair",
+    "segmented_forward",
+]
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """BF16 bit patterns (uint16 / int16 array) -> exact float64 values.
+
+    The device receives the same bytes ([cuLA#110] Supported configuration:
+    BF16 KDA inputs), so the oracle decodes them bit for bit: a bfloat16 is the
+    top half of an IEEE binary32, which float64 holds exactly.
+    """
+    b = np.ascontiguousarray(np.asarray(bits).view(np.uint16)).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def kda_step(S, q_t, k_t, v_t, g_t, beta_t):
+    """One token of the gated delta rule for all heads at once.
+
+    S: [H, K, V]; q_t, k_t, g_t: [H, K]; v_t: [H, V]; beta_t: [H].
+    Order of operations (the reading of the recurrence's factor order):
+      1. decay      S <- Diag(exp g_t) S                (per key channel)
+      2. erase      S <- S - beta_t k_t (k_t^T S)
+      3. write      S <- S + beta_t k_t v_t^T
+      4. read       o_t = S^T q_t                       (post-update state)
+    Returns (S_new, o_t [H, V]).
+    """
+    S = np.exp(g_t)[:, :, None] * S
+    kS = np.einsum("hk,hkv->hv", k_t, S)
+    bk = beta_t[:, None] * k_t
+    S = S - bk[:, :, None] * kS[:, None, :]
+    S = S + bk[:, :, None] * v_t[:, None, :]
+    o_t = np.einsum("hk,hkv->hv", q_t, S)
+    return S, o_t
+
+
+def _seq_starts(cu_seqlens, T):
+    starts = np.zeros(T + 1, dtype=bool)
+    for n in range(len(cu_seqlens) - 1):
+        starts[int(cu_seqlens[n])] = True
+    return starts
+
+
+def recurrence(q, k, v, g, beta, cu_seqlens, h0=None):
+    """Monolithic recurrence over every packed sequence.
+
+    Each sequence starts from a zero state (the configurations state no initial
+    state), or from ``h0[n]`` ([N, H, K, V]) when given.  Returns
+    ``(o [T, H, V], final [N, H, K, V])`` where ``final[n]`` is the state after
+    the sequence's last token.
+    """
+    T, H, K = k.shape
+    V = v.shape[2]
+    N = len(cu_seqlens) - 1
+    o = np.zeros((T, H, V))
+    final = np.zeros((N, H, K, V))
+    for n in range(N):
+        bos, eos = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
+        S = np.zeros((H, K, V)) if h0 is None else np.array(h0[n], dtype=np.float64)
+        for t in range(bos, eos):
+            S, o[t] = kda_step(S, q[t], k[t], v[t], g[t], beta[t])
+        final[n] = S
+    return o, final
+
+
+def segment_updates(k, v, g, beta, cu_seqlens, bounds):
+    """B_r: the state at the end of segment r when the segment starts from zero.
+
+    [cuLA#136] Summary names the pair preceding_state_update /
+    preceding_transition; the update is the affine map's constant term, i.e.
+    the segment run from a zero state, with the state reset to zero at every
+    sequence start inside the segment.  Returns [R, H, K, V].
+    """
+    T, H, K = k.shape
+    V = v.shape[2]
+    starts = _seq_starts(cu_seqlens, T)
+    R = len(bounds) - 1
+    B = np.zeros((R, H, K, V))
+    zeros_q = np.zeros((H, K))
+    for r in range(R):
+        S = np.zeros((H, K, V))
+        for t in range(int(bounds[r]), int(bounds[r + 1])):
+            if starts[t]:
+                S = np.zeros((H, K, V))
+            S, _ = kda_step(S, zeros_q, k[t], v[t], g[t], beta[t])
+        B[r] = S
+    return B
+
+
+def segment_transitions(k, g, beta, cu_seqlens, bounds):
+    """A_r: the K x K linear part of segment r's affine map.
+
+    The product of the per-token maps M_t = (I - beta_t k_t k_t^T) Diag(exp g_t),
+    latest on the left, so that S_out = A_r S_in + B_r.  A sequence start inside
+    the segment (or at its first token) resets the state, whose linear part is
+    the zero map, so the running product becomes 0 there.
+    Returns [R, H, K, K].
+    """
+    T, H, K = k.shape
+    starts = _seq_starts(cu_seqlens, T)
+    R = len(bounds) - 1
+    A = np.zeros((R, H, K, K))
+    for r in range(R):
+        Phi = np.broadcast_to(np.eye(K), (H, K, K)).copy()
+        for t in range(int(bounds[r]), int(bounds[r + 1])):
+            if starts[t]:
+                Phi = np.zeros((H, K, K))
+            Phi = np.exp(g[t])[:, :, None] * Phi
+            kPhi = np.einsum("hk,hkj->hj", k[t], Phi)
+            Phi = Phi - (beta[t][:, None] * k[t])[:, :, None] * kPhi[:, None, :]
+        A[r] = Phi
+    return A
+
+
+def compose_pair(second, first):
+    """Affine composition (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2).
+
+    Applying ``first`` and then ``second`` to a state S gives
+    A2 (A1 S + B1) + B2.  [cuLA#136] Summary: affine summary composition.
+    """
+    A2, B2 = second
+    A1, B1 = first
+    return A2 @ A1, A2 @ B1 + B2
+
+
+def compose(A, B):
+    """Ordered scan of the segment summaries into carry-in states.
+
+    C_0 = 0 and C_{r+1} = A_r C_r + B_r; C_r is the state entering segment r
+    ([cuLA#136] Summary: preceding_state_update / preceding_transition and
+    their composition; [cuLA#110] Motivation: assembling the state from every
+    predecessor).  Returns C [R, H, K, V]; also returns the state after the last
+    segment as the second value.
+    """
+    R = A.shape[0]
+    C = np.zeros_like(B)
+    cur = np.zeros_like(B[0])
+    for r in range(R):
+        C[r] = cur
+        cur = A[r] @ cur + B[r]
+    return C, cur
+
+
+def segmented_forward(q, k, v, g, beta, cu_seqlens, bounds, C):
+    """Re-run each segment from its carry-in C_r (reset at sequence starts).
+
+    This is the segmented execution the pages' context-parallel forward
+    performs once every rank has its predecessors' summaries ([cuLA#136]
+    Sequence Diagram).  Returns (o, final) like :func:`recurrence`.
+    """
+    T, H, K = k.shape
+    V = v.shape[2]
+    N = len(cu_seqlens) - 1
+    starts = _seq_starts(cu_seqlens, T)
+    ends = {int(cu_seqlens[n + 1]) - 1: n for n in range(N)}
+    o = np.zeros((T, H, V))
+    final = np.zeros((N, H, K, V))
+    for r in range(len(bounds) - 1):
+        S = np.array(C[r], dtype=np.float64)
+        for t in range(int(bounds[r]), int(bounds[r + 1])):
+            if starts[t]:
+                S = np.zeros((H, K, V))
+            S, o[t] = kda_step(S, q[t], k[t], v[t], g[t], beta[t])
+            if t in ends:
+                final[ends[t]] = S
+    return o, final
