@@ -1,0 +1,130 @@
+// C-ABI entry points of the segmented KDA forward pass: host-side argument
+// validation and kernel launches.  Every check runs before anything is
+// enqueued; an error returns a negative kda_status and enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda.h"
+#include "kda_internal.h"
+#include "kda_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kThreads = 256;
+constexpr int kComposeColumnBlocks = 4;   // 128 state columns / 32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V) {
+  if (plan == nullptr || plan_dev == nullptr) return KDA_ERR_INVALID_ARG;
+  if (H <= 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
+  if (K != 128 || V != 128) return KDA_ERR_UNSUPPORTED;
+  if (H > 65535) return KDA_ERR_UNSUPPORTED;
+  if (!aligned16(plan_dev)) return KDA_ERR_MISALIGNED;
+  return KDA_OK;
+}
+
+int check_tensors(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    if (p == nullptr) return KDA_ERR_INVALID_ARG;
+  }
+  for (const void* p : ptrs) {
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  }
+  return KDA_OK;
+}
+
+int finish_launch() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" int kda_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
+                                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* g, const uint16_t* beta, int32_t H,
+                                     int32_t K, int32_t V, float* o, float* final_state,
+                                     float* transitions, float* updates, hipStream_t stream) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_tensors({q, k, v, g, beta, o, final_state, transitions, updates});
+  if (st != KDA_OK) return st;
+  kda::ChunkParams p{};
+  p.plan = plan_dev;
+  p.L = plan->layout;
+  p.H = H;
+  p.pass = 1;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.o = o;
+  p.final_state = final_state;
+  p.transitions = transitions;
+  p.updates = updates;
+  p.carry = nullptr;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 2), dim3(kThreads), 0, stream, p);
+  return finish_launch();
+}
+
+extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
+                                     const float* transitions, const float* updates, int32_t H,
+                                     int32_t K, int32_t V, float* carry_in, hipStream_t stream) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_tensors({transitions, updates, carry_in});
+  if (st != KDA_OK) return st;
+  kda::ComposeParams p{};
+  p.plan = plan_dev;
+  p.L = plan->layout;
+  p.H = H;
+  p.S = plan->S;
+  p.transitions = transitions;
+  p.updates = updates;
+  p.carry = carry_in;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(H, kComposeColumnBlocks), dim3(kThreads), 0,
+                     stream, p);
+  return finish_launch();
+}
+
+extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q,
+                               const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                               const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                               const float* carry_in, float* o, float* final_state,
+                               hipStream_t stream) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_tensors({q, k, v, g, beta, carry_in, o, final_state});
+  if (st != KDA_OK) return st;
+  kda::ChunkParams p{};
+  p.plan = plan_dev;
+  p.L = plan->layout;
+  p.H = H;
+  p.pass = 2;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.o = o;
+  p.final_state = final_state;
+  p.transitions = nullptr;
+  p.updates = nullptr;
+  p.carry = carry_in;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kThreads), 0, stream, p);
+  return finish_launch();
+}

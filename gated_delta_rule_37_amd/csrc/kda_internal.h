@@ -1,0 +1,52 @@
+// Internal declarations shared by the host planner, the C-ABI layer and the
+// HIP kernels of the segmented KDA forward pass.
+#ifndef KDA_INTERNAL_H_
+#define KDA_INTERNAL_H_
+
+#include <cstdint>
+#include <vector>
+
+namespace kda {
+
+// Fragment flag bits, as serialised in the plan blob.
+constexpr int32_t kFragCarried = 1;  // first fragment of a segment that continues a sequence
+constexpr int32_t kFragSegLast = 2;  // ends at its segment's end (its state is B_r)
+constexpr int32_t kFragSeqEnd = 4;   // ends at its sequence's end (owns final_state)
+
+// Largest supported packed token count: a chunk-count times 64 times the head
+// count stays far inside 32-bit grid arithmetic.
+constexpr int32_t kMaxTokens = (1 << 30);
+
+// Word offsets of the arrays inside the plan blob (see kda_plan_blob()).
+struct BlobLayout {
+  int32_t seg_bounds, seg_first_seq, seg_last_seq, seg_carry_in, seg_transition_live,
+      seg_frag_ptr, frag_seq, frag_begin, frag_end, frag_seg, frag_flags, seq_end_seg;
+};
+
+inline BlobLayout blob_layout(int32_t S, int32_t F) {
+  BlobLayout L;
+  int32_t o = 4;
+  L.seg_bounds = o;          o += S + 1;
+  L.seg_first_seq = o;       o += S;
+  L.seg_last_seq = o;        o += S;
+  L.seg_carry_in = o;        o += S;
+  L.seg_transition_live = o; o += S;
+  L.seg_frag_ptr = o;        o += S + 1;
+  L.frag_seq = o;            o += F;
+  L.frag_begin = o;          o += F;
+  L.frag_end = o;            o += F;
+  L.frag_seg = o;            o += F;
+  L.frag_flags = o;          o += F;
+  L.seq_end_seg = o;
+  return L;
+}
+
+}  // namespace kda
+
+struct kda_plan {
+  int32_t T = 0, N = 0, S = 0, F = 0;
+  kda::BlobLayout layout{};
+  std::vector<int32_t> blob;
+};
+
+#endif  // KDA_INTERNAL_H_

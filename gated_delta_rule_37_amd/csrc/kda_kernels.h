@@ -1,0 +1,46 @@
+// Kernel parameter blocks and entry points shared by the C-ABI layer and the
+// HIP kernels of the segmented KDA forward pass.
+#ifndef KDA_KERNELS_H_
+#define KDA_KERNELS_H_
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+struct ChunkParams {
+  const int32_t* plan;   // device copy of the plan blob
+  BlobLayout L;
+  int32_t H;
+  int32_t pass;          // 1: zero-start pass (summaries), 2: carried fragments
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  float* o;
+  float* final_state;
+  float* transitions;
+  float* updates;
+  const float* carry;
+};
+
+struct ComposeParams {
+  const int32_t* plan;
+  BlobLayout L;
+  int32_t H;
+  int32_t S;
+  const float* transitions;
+  const float* updates;
+  float* carry;
+};
+
+__global__ void kda_chunk_kernel(ChunkParams p);
+__global__ void kda_compose_kernel(ComposeParams p);
+
+}  // namespace kda
+
+#endif  // KDA_KERNELS_H_

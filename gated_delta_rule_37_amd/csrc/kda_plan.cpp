@@ -1,0 +1,154 @@
+// Host-side segment planner for the segmented KDA forward pass.
+//
+// Builds the contiguous segment plan over packed sequences (inclusionAI/cuLA
+// pull request #136 "feat(kda): add cuDNN concatenated-summary Kimi CP",
+// Walkthrough, "Packed-shard planning": CPU-only balanced or custom contiguous
+// shards over the global sequence boundaries, with input validation) and its
+// canonical int32 serialisation, which the device kernels read.  No HIP call
+// is made here.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+// Index n such that bounds[n] <= t < bounds[n + 1] (bounds strictly increasing).
+int32_t locate(const std::vector<int32_t>& bounds, int32_t t) {
+  auto it = std::upper_bound(bounds.begin(), bounds.end(), t);
+  return static_cast<int32_t>(it - bounds.begin()) - 1;
+}
+
+}  // namespace
+
+extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t num_segments, const int32_t* custom_bounds,
+                                 kda_plan** out) {
+  if (cu_seqlens == nullptr || out == nullptr) return KDA_ERR_INVALID_ARG;
+  if (num_seqs < 1) return KDA_ERR_BAD_CU_SEQLENS;
+  if (cu_seqlens[0] != 0) return KDA_ERR_BAD_CU_SEQLENS;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    if (cu_seqlens[n + 1] <= cu_seqlens[n]) return KDA_ERR_BAD_CU_SEQLENS;
+  }
+  const int32_t T = cu_seqlens[num_seqs];
+  // Token offsets times H * 128 stay well inside size_t, but a chunk index
+  // times the head count must fit int32 in the launch grid.
+  if (T > kda::kMaxTokens) return KDA_ERR_UNSUPPORTED;
+  const int32_t S = num_segments;
+  if (S < 1 || S > T) return KDA_ERR_BAD_SEGMENTS;
+
+  std::vector<int32_t> cu(cu_seqlens, cu_seqlens + num_seqs + 1);
+  std::vector<int32_t> b(S + 1);
+  if (custom_bounds == nullptr) {
+    for (int32_t r = 0; r <= S; ++r) {
+      b[r] = static_cast<int32_t>((static_cast<int64_t>(r) * T) / S);
+    }
+  } else {
+    for (int32_t r = 0; r <= S; ++r) b[r] = custom_bounds[r];
+    if (b[0] != 0 || b[S] != T) return KDA_ERR_BAD_SEGMENTS;
+    for (int32_t r = 0; r < S; ++r) {
+      if (b[r + 1] <= b[r]) return KDA_ERR_BAD_SEGMENTS;
+    }
+  }
+
+  kda_plan* plan = new (std::nothrow) kda_plan;
+  if (plan == nullptr) return KDA_ERR_NO_MEMORY;
+  try {
+    plan->T = T;
+    plan->N = num_seqs;
+    plan->S = S;
+    std::vector<int32_t> first(S), last(S), carry(S), live(S), frag_ptr(S + 1);
+    std::vector<int32_t> f_seq, f_beg, f_end, f_seg, f_flags;
+    frag_ptr[0] = 0;
+    for (int32_t r = 0; r < S; ++r) {
+      first[r] = locate(cu, b[r]);
+      last[r] = locate(cu, b[r + 1] - 1);
+      const bool starts_here = cu[first[r]] == b[r];
+      carry[r] = (r > 0 && !starts_here) ? 1 : 0;
+      live[r] = (carry[r] && first[r] == last[r]) ? 1 : 0;
+      for (int32_t n = first[r]; n <= last[r]; ++n) {
+        const int32_t lo = std::max(b[r], cu[n]);
+        const int32_t hi = std::min(b[r + 1], cu[n + 1]);
+        int32_t flags = 0;
+        if (lo == b[r] && carry[r]) flags |= kda::kFragCarried;
+        if (hi == b[r + 1]) flags |= kda::kFragSegLast;
+        if (hi == cu[n + 1]) flags |= kda::kFragSeqEnd;
+        f_seq.push_back(n);
+        f_beg.push_back(lo);
+        f_end.push_back(hi);
+        f_seg.push_back(r);
+        f_flags.push_back(flags);
+      }
+      frag_ptr[r + 1] = static_cast<int32_t>(f_seq.size());
+    }
+    const int32_t F = static_cast<int32_t>(f_seq.size());
+    plan->F = F;
+    std::vector<int32_t> end_seg(num_seqs);
+    for (int32_t n = 0; n < num_seqs; ++n) end_seg[n] = locate(b, cu[n + 1] - 1);
+
+    std::vector<int32_t>& blob = plan->blob;
+    blob.reserve(4 + (S + 1) * 2 + S * 4 + F * 5 + num_seqs);
+    blob.insert(blob.end(), {T, num_seqs, S, F});
+    auto append = [&blob](const std::vector<int32_t>& a) { blob.insert(blob.end(), a.begin(), a.end()); };
+    append(b);
+    append(first);
+    append(last);
+    append(carry);
+    append(live);
+    append(frag_ptr);
+    append(f_seq);
+    append(f_beg);
+    append(f_end);
+    append(f_seg);
+    append(f_flags);
+    append(end_seg);
+    plan->layout = kda::blob_layout(S, F);
+  } catch (const std::bad_alloc&) {
+    delete plan;
+    return KDA_ERR_NO_MEMORY;
+  }
+  *out = plan;
+  return KDA_OK;
+}
+
+extern "C" int kda_plan_blob(const kda_plan* plan, const int32_t** blob, size_t* n_int32) {
+  if (plan == nullptr || blob == nullptr || n_int32 == nullptr) return KDA_ERR_INVALID_ARG;
+  *blob = plan->blob.data();
+  *n_int32 = plan->blob.size();
+  return KDA_OK;
+}
+
+extern "C" int kda_plan_info(const kda_plan* plan, int32_t* T, int32_t* N, int32_t* S,
+                             int32_t* F) {
+  if (plan == nullptr) return KDA_ERR_INVALID_ARG;
+  if (T) *T = plan->T;
+  if (N) *N = plan->N;
+  if (S) *S = plan->S;
+  if (F) *F = plan->F;
+  return KDA_OK;
+}
+
+extern "C" void kda_plan_destroy(kda_plan* plan) { delete plan; }
+
+extern "C" size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V) {
+  if (plan == nullptr || H <= 0 || K <= 0 || V <= 0) return 0;
+  const size_t per_head = static_cast<size_t>(K) * K + static_cast<size_t>(K) * V;
+  return static_cast<size_t>(plan->S) * static_cast<size_t>(H) * per_head * sizeof(float);
+}
+
+extern "C" const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_BAD_CU_SEQLENS: return "KDA_ERR_BAD_CU_SEQLENS";
+    case KDA_ERR_BAD_SEGMENTS: return "KDA_ERR_BAD_SEGMENTS";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_NO_MEMORY: return "KDA_ERR_NO_MEMORY";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}

@@ -1,0 +1,249 @@
+"""Thin Python binding of the segmented KDA C-ABI library (``libkda.so``).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind ``include/kda.h``.  PyTorch provides device memory and the
+stream.  If the compiled library is missing, importing the entry points fails
+loudly; there is no CPU fallback.
+
+Entry points mirror the C names:
+
+* :class:`Plan` (``kda_plan_segments`` / ``kda_plan_blob`` / ``kda_plan_destroy``)
+* :func:`segment_summaries` (``kda_segment_summaries``)
+* :func:`compose_summaries` (``kda_compose_summaries``)
+* :func:`apply_carry` (``kda_apply_carry``)
+* :func:`forward` runs the three device calls in order on fresh output buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+STATUS = {
+    0: "KDA_OK",
+    -1: "KDA_ERR_INVALID_ARG",
+    -2: "KDA_ERR_BAD_CU_SEQLENS",
+    -3: "KDA_ERR_BAD_SEGMENTS",
+    -4: "KDA_ERR_UNSUPPORTED",
+    -5: "KDA_ERR_MISALIGNED",
+    -6: "KDA_ERR_HIP",
+    -7: "KDA_ERR_NO_MEMORY",
+}
+
+# Every symbol include/kda.h declares.
+SYMBOLS = (
+    "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
+    "kda_summary_bytes", "kda_segment_summaries", "kda_compose_summaries",
+    "kda_apply_carry", "kda_status_string", "kda_last_hip_error",
+)
+
+
+class KdaError(RuntimeError):
+    """A negative status returned by the C library."""
+
+    def __init__(self, status: int, where: str):
+        name = STATUS.get(status, f"status {status}")
+        extra = ""
+        if status == -6:
+            extra = f" (hipError_t {lib().kda_last_hip_error()})"
+        super().__init__(f"{where}: {name}{extra}")
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libkda.so`` (built by ``__graft_entry__.build()``) once."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, p, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    L.kda_plan_segments.argtypes = [p, i32, i32, p, ctypes.POINTER(p)]
+    L.kda_plan_segments.restype = ctypes.c_int
+    L.kda_plan_blob.argtypes = [p, ctypes.POINTER(p), ctypes.POINTER(sz)]
+    L.kda_plan_blob.restype = ctypes.c_int
+    L.kda_plan_info.argtypes = [p, p, p, p, p]
+    L.kda_plan_info.restype = ctypes.c_int
+    L.kda_plan_destroy.argtypes = [p]
+    L.kda_plan_destroy.restype = None
+    L.kda_summary_bytes.argtypes = [p, i32, i32, i32]
+    L.kda_summary_bytes.restype = sz
+    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p]
+    L.kda_segment_summaries.restype = ctypes.c_int
+    L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, p, p]
+    L.kda_compose_summaries.restype = ctypes.c_int
+    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
+    L.kda_apply_carry.restype = ctypes.c_int
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_last_hip_error.argtypes = []
+    L.kda_last_hip_error.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KdaError(status, where)
+
+
+class Plan:
+    """Host-side segment plan (``kda_plan_segments``); reusable across calls."""
+
+    def __init__(self, cu_seqlens, num_segments: int, custom_bounds=None):
+        L = lib()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        self._cu = cu
+        bounds = None
+        if custom_bounds is not None:
+            bounds = np.ascontiguousarray(np.asarray(custom_bounds, dtype=np.int32))
+        self._bounds = bounds
+        handle = ctypes.c_void_p()
+        st = L.kda_plan_segments(
+            cu.ctypes.data, int(len(cu) - 1), int(num_segments),
+            None if bounds is None else bounds.ctypes.data, ctypes.byref(handle))
+        _check(st, "kda_plan_segments")
+        self._h = handle
+        ptr = ctypes.c_void_p()
+        n = ctypes.c_size_t()
+        _check(L.kda_plan_blob(self._h, ctypes.byref(ptr), ctypes.byref(n)), "kda_plan_blob")
+        arr = (ctypes.c_int32 * n.value).from_address(ptr.value)
+        self.blob = np.array(arr, dtype=np.int32, copy=True)
+        self.T, self.N, self.S, self.F = (int(x) for x in self.blob[:4])
+        self._dev = {}
+
+    @property
+    def handle(self):
+        return self._h
+
+    def device_blob(self, device) -> torch.Tensor:
+        """The caller-owned device copy of the blob (cached per device)."""
+        device = torch.device(device)
+        t = self._dev.get(device)
+        if t is None:
+            t = torch.from_numpy(self.blob.copy()).to(device)
+            self._dev[device] = t
+        return t
+
+    def summary_bytes(self, H: int, K: int = 128, V: int = 128) -> int:
+        return int(lib().kda_summary_bytes(self._h, H, K, V))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().kda_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr(t: torch.Tensor, dtype, shape, name: str) -> int:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _inputs(plan: Plan, q, k, v, g, beta):
+    T, H, K = q.shape
+    V = v.shape[2]
+    if T != plan.T:
+        raise ValueError(f"inputs hold {T} tokens, the plan {plan.T}")
+    return H, K, V, [
+        _ptr(q, torch.bfloat16, (T, H, K), "q"), _ptr(k, torch.bfloat16, (T, H, K), "k"),
+        _ptr(v, torch.bfloat16, (T, H, V), "v"), _ptr(g, torch.bfloat16, (T, H, K), "g"),
+        _ptr(beta, torch.bfloat16, (T, H), "beta"),
+    ]
+
+
+def segment_summaries(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, o, final_state,
+                      transitions, updates, stream=None):
+    """``kda_segment_summaries``: zero-start pass over every segment."""
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta)
+    outs = [
+        _ptr(o, torch.float32, (plan.T, H, V), "o"),
+        _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state"),
+        _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
+        _ptr(updates, torch.float32, (plan.S, H, K, V), "updates"),
+    ]
+    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
+    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *outs, _stream(q, stream))
+    _check(st, "kda_segment_summaries")
+
+
+def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, carry_in,
+                      stream=None):
+    """``kda_compose_summaries``: ordered FP32 scan of the summaries."""
+    S, H, K, _ = transitions.shape
+    V = updates.shape[3]
+    a = _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions")
+    b = _ptr(updates, torch.float32, (plan.S, H, K, V), "updates")
+    c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
+    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
+    st = lib().kda_compose_summaries(plan.handle, pd, a, b, H, K, V, c,
+                                     _stream(transitions, stream))
+    _check(st, "kda_compose_summaries")
+
+
+def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
+                stream=None):
+    """``kda_apply_carry``: re-run each carrying segment's first fragment from C_r."""
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta)
+    c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
+    oo = _ptr(o, torch.float32, (plan.T, H, V), "o")
+    ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
+    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
+    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, c, oo, ff, _stream(q, stream))
+    _check(st, "kda_apply_carry")
+
+
+def alloc_outputs(plan: Plan, H: int, K: int, V: int, device):
+    """Fresh output buffers (o, final_state, transitions, updates, carry_in)."""
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(
+        o=torch.empty(plan.T, H, V, **f32),
+        final_state=torch.empty(plan.N, H, K, V, **f32),
+        transitions=torch.empty(plan.S, H, K, K, **f32),
+        updates=torch.empty(plan.S, H, K, V, **f32),
+        carry_in=torch.empty(plan.S, H, K, V, **f32),
+    )
+
+
+def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None):
+    """The whole segmented forward: summaries, compose, carry.  Returns ``out``."""
+    T, H, K = q.shape
+    V = v.shape[2]
+    if out is None:
+        out = alloc_outputs(plan, H, K, V, q.device)
+    pd = plan.device_blob(q.device)
+    segment_summaries(plan, pd, q, k, v, g, beta, out["o"], out["final_state"],
+                      out["transitions"], out["updates"], stream)
+    compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], stream)
+    apply_carry(plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"], stream)
+    return out

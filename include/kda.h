@@ -1,0 +1,193 @@
+/*
+ * kda.h -- C ABI of the segmented KDA (Kimi Delta Attention) forward pass on
+ * MI355X (gfx950).
+ *
+ * The method (sources: inclusionAI/cuLA pull request #110 "feat(cp): add
+ * opt-in NVSHMEM CP state handoff", and pull request #136 "feat(kda): add
+ * cuDNN concatenated-summary Kimi CP"):
+ *
+ *   per head, with a K x V state S (FP32, K-major "non-transposed" layout,
+ *   #110 Supported configuration) and BF16 inputs (#110 Supported
+ *   configuration), the gated delta rule
+ *       S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *       o_t = S_t^T q_t
+ *   runs over packed sequences (THD layout with cu_seqlens, #136 Summary by
+ *   CodeRabbit).  The token range is cut into contiguous segments (the
+ *   context-parallel shards of #136 Walkthrough, "Packed-shard planning").
+ *   Each segment r yields an affine FP32 summary S_out = A_r S_in + B_r: the
+ *   K x K transition A_r and the K x V update B_r (#136 Summary:
+ *   preceding_transition / preceding_state_update; #110 Motivation: affine
+ *   recurrence state).  An ordered FP32 scan composes them into carry-in
+ *   states C_r (#136 Summary: affine summary composition in FP32), and each
+ *   segment whose first token continues a sequence re-runs its first
+ *   fragment from C_r (#136 Sequence Diagram: the forward consumes the
+ *   gathered preceding summaries).
+ *
+ * Call order for one forward pass, all on one stream:
+ *     kda_plan_segments        (host, once; reusable)
+ *     kda_segment_summaries    (device)
+ *     kda_compose_summaries    (device)
+ *     kda_apply_carry          (device)
+ * After the three device calls, o and final_state hold the monolithic
+ * recurrence's results.
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: KDA_OK (0) or a negative kda_status.  Every check runs on
+ *     the host before anything is enqueued; on error nothing is enqueued and
+ *     no output is touched.  There is no fallback path of any kind.
+ *   - Device pointers are plain device addresses owned by the caller; the
+ *     library never allocates or frees device memory and keeps no global
+ *     state.  Distinct plans may be used from distinct threads.
+ *   - BF16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *   - Tensors are dense and contiguous; every tensor pointer must be 16-byte
+ *     aligned (KDA_ERR_MISALIGNED otherwise).
+ *   - Shapes: T packed tokens, N sequences, S segments, H heads, K = V = 128
+ *     (other K, V return KDA_ERR_UNSUPPORTED).
+ *       q, k, g : [T, H, K] bf16        v : [T, H, V] bf16
+ *       beta    : [T, H]    bf16
+ *       o       : [T, H, V] fp32        final_state : [N, H, K, V] fp32
+ *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
+ *   - Device calls are asynchronous on `stream`; launch failures are reported
+ *     as KDA_ERR_HIP (kda_last_hip_error() gives the hipError_t).
+ *   - Supported gate domain: g <= 0 and finite, with the decay mass of any 16
+ *     consecutive tokens of one chunk below about 85 nats per channel (so that
+ *     the in-chunk exponential factors stay inside the FP32 range).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = -1,    /* null pointer, non-positive size, plan_dev missing */
+  KDA_ERR_BAD_CU_SEQLENS = -2, /* cu_seqlens not 0 = c_0 < c_1 < ... (empty sequence) */
+  KDA_ERR_BAD_SEGMENTS = -3,   /* num_segments outside [1, T] or bad custom bounds */
+  KDA_ERR_UNSUPPORTED = -4,    /* K or V other than 128, H out of range, T too large */
+  KDA_ERR_MISALIGNED = -5,     /* a tensor pointer is not 16-byte aligned */
+  KDA_ERR_HIP = -6,            /* a HIP launch failed; see kda_last_hip_error() */
+  KDA_ERR_NO_MEMORY = -7       /* host allocation for the plan failed */
+} kda_status;
+
+/* Opaque host-side plan; immutable once built. */
+typedef struct kda_plan kda_plan;
+
+/*
+ * kda_plan_segments -- contiguous segment plan over packed sequences.
+ * #136 Walkthrough ("Packed-shard planning": CPU-only, balanced or custom
+ * contiguous shards over the global sequence boundaries, validated).
+ *
+ *   cu_seqlens    host [num_seqs + 1]; must satisfy 0 = c_0 < c_1 < ... < c_N = T.
+ *   num_seqs      N >= 1.
+ *   num_segments  S with 1 <= S <= T.
+ *   custom_bounds host [S + 1] with 0 = b_0 < ... < b_S = T, or NULL for the
+ *                 balanced bounds b_r = floor(r * T / S).
+ *   out           receives the plan (owned by the caller; free with
+ *                 kda_plan_destroy).  Untouched on error.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_BAD_CU_SEQLENS, KDA_ERR_BAD_SEGMENTS,
+ * KDA_ERR_UNSUPPORTED (T >= 2^31 / 256), KDA_ERR_NO_MEMORY.
+ */
+int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_segments,
+                      const int32_t* custom_bounds, kda_plan** out);
+
+/*
+ * kda_plan_blob -- the plan's canonical int32 serialisation.  The device
+ * entry points read a device copy of exactly these n_int32 words
+ * (`plan_dev`).  Layout:
+ *   header [T, N, S, F]
+ *   seg_bounds[S+1] seg_first_seq[S] seg_last_seq[S] seg_carry_in[S]
+ *   seg_transition_live[S] seg_frag_ptr[S+1]
+ *   frag_seq[F] frag_begin[F] frag_end[F] frag_seg[F] frag_flags[F]
+ *   seq_end_seg[N]
+ * A fragment is the part of one sequence inside one segment.  frag_flags bit
+ * 1: first fragment of a segment that continues a sequence (it carries in);
+ * bit 2: ends at its segment's end; bit 4: ends at its sequence's end.
+ * `*blob` stays valid until kda_plan_destroy.
+ */
+int kda_plan_blob(const kda_plan* plan, const int32_t** blob, size_t* n_int32);
+
+/* Sizes of a plan: tokens, sequences, segments, fragments (any may be NULL). */
+int kda_plan_info(const kda_plan* plan, int32_t* T, int32_t* N, int32_t* S, int32_t* F);
+
+void kda_plan_destroy(kda_plan* plan);
+
+/*
+ * kda_summary_bytes -- bytes of the FP32 summary workspace (transitions plus
+ * updates) for this plan: S * H * (K*K + K*V) * 4.  At S = 64, H = 32,
+ * K = V = 128 this is 256 MiB, the figure #136 Latest cuDNN compatibility
+ * gives for the prepared CP64 summary workspace.  Returns 0 for a NULL plan
+ * or non-positive sizes.
+ */
+size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
+
+/*
+ * kda_segment_summaries -- every segment from a zero state.
+ * #136 Summary (preceding_state_update / preceding_transition), #110
+ * Motivation (each producer computes its affine recurrence state).
+ *
+ * Writes:
+ *   updates[r]      = B_r, the state at the end of segment r run from zero
+ *                     (reset at each sequence start inside it);
+ *   transitions[r]  = A_r, the product of the per-token maps of segment r,
+ *                     latest on the left, when segment r carries in and no
+ *                     sequence starts inside it; otherwise exactly 0 (the
+ *                     reset's linear part);
+ *   o[t]            for every token t outside the first fragment of a
+ *                     carrying segment (those tokens start from a true zero
+ *                     state, so o is final there);
+ *   final_state[n]  for every sequence whose last token lies outside the
+ *                     first fragment of a carrying segment.
+ * The remaining rows of o and final_state are written by kda_apply_carry.
+ *   plan_dev  device copy of kda_plan_blob(plan).
+ */
+int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
+                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const uint16_t* g, const uint16_t* beta,
+                          int32_t H, int32_t K, int32_t V,
+                          float* o, float* final_state, float* transitions, float* updates,
+                          hipStream_t stream);
+
+/*
+ * kda_compose_summaries -- ordered FP32 scan C_0 = 0, C_{r+1} = A_r C_r + B_r.
+ * #136 Summary (affine summary composition in FP32), #110 Motivation (a
+ * consumer assembles the state from every predecessor in one kernel).
+ * carry_in[r] is the state entering segment r (all r in [0, S)).  Where the
+ * plan says A_r is structurally zero the product is skipped (C_{r+1} = B_r).
+ */
+int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
+                          const float* transitions, const float* updates,
+                          int32_t H, int32_t K, int32_t V, float* carry_in,
+                          hipStream_t stream);
+
+/*
+ * kda_apply_carry -- apply each carrying segment's carry-in C_r to its
+ * outputs: re-run the segment's first fragment starting from C_r, writing
+ * its rows of o and, when the fragment ends a sequence, that sequence's
+ * final_state.  #136 Summary (the forward that consumes
+ * preceding_state_update / preceding_transition), #110 Motivation (rank 1
+ * consumes only the V-state it needs).
+ */
+int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
+                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* g, const uint16_t* beta,
+                    int32_t H, int32_t K, int32_t V, const float* carry_in,
+                    float* o, float* final_state, hipStream_t stream);
+
+/* Human-readable name of a kda_status value. */
+const char* kda_status_string(int status);
+
+/* hipError_t of the last KDA_ERR_HIP returned on this thread (0 if none). */
+int kda_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,139 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function ``include/kda.h`` declares, builds
+plans bit-identical to the reference plan, and rejects bad arguments with the
+documented status before anything reaches the device.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_37_amd import kda
+from oracle import plan_oracle as po
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "plan_cases.json")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = kda.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(kda.SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = kda.lib()
+    for code, name in kda.STATUS.items():
+        assert L.kda_status_string(code).decode() == name
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_plan_blob_matches_golden(case):
+    plan = kda.Plan(case["cu_seqlens"], case["segments"], case["custom_bounds"])
+    assert plan.blob.tolist() == case["blob"]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_blob_matches_oracle_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.integers(1, 30))
+    lens = rng.integers(1, 300, size=N)
+    cu = [0] + np.cumsum(lens).astype(int).tolist()
+    T = cu[-1]
+    S = int(rng.integers(1, min(T, 70) + 1))
+    bounds = None
+    if seed % 3 == 0 and S > 1:
+        cuts = sorted(rng.choice(np.arange(1, T), size=S - 1, replace=False).tolist())
+        bounds = [0] + cuts + [T]
+    want = po.build_plan(cu, S, bounds)["blob"]
+    got = kda.Plan(cu, S, bounds).blob
+    np.testing.assert_array_equal(got, want)
+
+
+def test_plan_blob_matches_oracle_workloads():
+    from gated_delta_rule_37_amd import synth
+    import torch
+    for w in synth.WORKLOADS.values():
+        if w.varlen:
+            gen = torch.Generator("cpu").manual_seed(w.seed)
+            lens = synth.draw_lengths(gen, w.T, w.min_len, w.max_len)
+            cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+        else:
+            cu = [0, w.T]
+        np.testing.assert_array_equal(kda.Plan(cu, w.segments).blob,
+                                      po.build_plan(cu, w.segments)["blob"])
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["invalid"])
+def test_plan_rejects_invalid(case):
+    with pytest.raises(kda.KdaError) as e:
+        kda.Plan(case["cu_seqlens"], case["segments"], case["custom_bounds"])
+    assert e.value.name == "KDA_ERR_" + case["kind"]
+
+
+def test_summary_workspace_64_segments_32_heads_is_256_mib():
+    # 64 shards, H = 32, K = V = 128: the prepared summary workspace of
+    # cuLA PR #136, Latest cuDNN compatibility, is 256 MiB.
+    plan = kda.Plan([0, 65536], 64)
+    assert plan.summary_bytes(32, 128, 128) == 256 * 1024 * 1024
+
+
+# ------------------------------------------------ device entry points: host checks
+
+_FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereferenced
+
+
+def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, q=_FAKE, o=_FAKE):
+    L = kda.lib()
+    return L.kda_segment_summaries(plan.handle, plan_dev, q, _FAKE, _FAKE, _FAKE, _FAKE,
+                                   H, K, V, o, _FAKE, _FAKE, _FAKE, None)
+
+
+def test_device_calls_validate_before_launch():
+    plan = kda.Plan([0, 100], 2)
+    assert _call_summaries(plan, K=64) == -4
+    assert _call_summaries(plan, V=256) == -4
+    assert _call_summaries(plan, H=0) == -1
+    assert _call_summaries(plan, H=70000) == -4
+    assert _call_summaries(plan, plan_dev=0) == -1
+    assert _call_summaries(plan, q=0) == -1
+    assert _call_summaries(plan, q=_FAKE + 2) == -5
+    assert _call_summaries(plan, o=_FAKE + 8) == -5
+    assert _call_summaries(plan, plan_dev=_FAKE + 4) == -5
+    L = kda.lib()
+    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                                   _FAKE, _FAKE, _FAKE, _FAKE, None) == -1
+    assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, _FAKE, None) == -4
+    assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, _FAKE, None) == -1
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                             _FAKE + 4, _FAKE, _FAKE, None) == -5
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                             _FAKE, 0, _FAKE, None) == -1
+    assert L.kda_last_hip_error() == 0
+
+
+def test_plan_info_and_null_handling():
+    L = kda.lib()
+    plan = kda.Plan([0, 5, 9], 3)
+    T, N, S, F = (ctypes.c_int32() for _ in range(4))
+    assert L.kda_plan_info(plan.handle, ctypes.byref(T), ctypes.byref(N), ctypes.byref(S),
+                           ctypes.byref(F)) == 0
+    assert (T.value, N.value, S.value, F.value) == (9, 2, 3, plan.F)
+    assert L.kda_plan_info(None, None, None, None, None) == -1
+    assert L.kda_summary_bytes(None, 1, 128, 128) == 0
+    out = ctypes.c_void_p()
+    assert L.kda_plan_segments(None, 1, 1, None, ctypes.byref(out)) == -1
+    L.kda_plan_destroy(None)
