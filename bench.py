@@ -1,0 +1,268 @@
+"""Benchmark of the segmented KDA forward pass on one MI355X.
+
+One step = one whole forward over one batch of resident synthetic input:
+kda_segment_summaries + kda_compose_summaries + kda_apply_carry (the plan is
+built once and reused, as the pages' reusable shard plans are).  Prints one
+JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Workload default: 65536 packed tokens of one sequence, H = 32, K = V = 128, 64
+equal segments (the 64-shard, 32-head configuration whose FP32 summary
+workspace is 256 MiB).  Inputs follow gated_delta_rule_37_amd/synth.py.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+# Algorithmic multiply-adds per token-head of the chunked method at chunk C=32,
+# K = V = 128 (triangular products counted exactly, FP32-grade):
+C, K, V = 32, 128, 128
+TRI_STRICT = (C - 1) / 2 * K      # A = beta (K K^T) strictly lower
+TRI_INCL = (C + 1) / 2 * K        # P, W = T(...), U~ = T V, P U (lower incl. diagonal)
+STATE = K * V                     # one K x V product per token (W S, Q S, K^T U)
+MACS = {
+    "fwd": TRI_STRICT + 4 * TRI_INCL + 3 * STATE,
+    "sum_s": TRI_STRICT + 2 * TRI_INCL + 2 * STATE,
+    "sum_phi": TRI_STRICT + TRI_INCL + 2 * K * K,
+}
+# bf16 MFMA work as executed: split operands cost three products, raw BF16 V
+# against a split operand two.
+MFMA_MACS = {
+    "fwd": 3 * MACS["fwd"] - TRI_INCL,
+    "sum_s": 3 * MACS["sum_s"] - TRI_INCL,
+    "sum_phi": 3 * MACS["sum_phi"],
+}
+# HBM bytes per token-head: bf16 inputs read, fp32 o written.
+BYTES = {
+    "fwd": 4 * 2 * K + 2 + 4 * V,   # q, k, v, g, beta in; o out
+    "sum_s": 3 * 2 * K + 2,         # k, v, g, beta
+    "sum_phi": 2 * 2 * K + 2,       # k, g, beta
+}
+STATE_BYTES = K * V * 4
+
+
+def chunk_kernel_work(blob, H):
+    """Algorithmic MACs, executed bf16 MFMA MACs and HBM bytes of the two
+    launches of the chunk kernel, from the plan blob."""
+    T, N, S, F = (int(x) for x in blob[:4])
+    o = 4
+    o += S + 1          # seg_bounds
+    o += 4 * S          # first, last, carry, live
+    o += S + 1          # frag_ptr
+    f_seq = blob[o:o + F]; o += F
+    f_beg = blob[o:o + F]; o += F
+    f_end = blob[o:o + F]; o += F
+    o += F              # frag_seg
+    f_flags = blob[o:o + F]
+    work = {"macs": 0.0, "mfma_macs": 0.0, "bytes": 0.0}
+
+    def add(mode, L):
+        work["macs"] += MACS[mode] * L * H
+        work["mfma_macs"] += MFMA_MACS[mode] * L * H
+        work["bytes"] += BYTES[mode] * L * H
+
+    for f in range(F):
+        L = int(f_end[f] - f_beg[f])
+        fl = int(f_flags[f])
+        if fl & 1:                       # carried first fragment
+            if fl & 2:                   # pass 1: B_r and A_r from zero / identity
+                add("sum_s", L)
+                add("sum_phi", L)
+                work["bytes"] += 2 * STATE_BYTES * H
+            add("fwd", L)                # pass 2: forward from C_r
+            work["bytes"] += STATE_BYTES * H * (1 + ((fl & 4) > 0))
+        else:
+            add("fwd", L)
+            work["bytes"] += STATE_BYTES * H * (((fl & 2) > 0) + ((fl & 4) > 0))
+    return work
+
+
+def compose_work(S, H, live_count):
+    macs = live_count * H * K * K * V
+    bytes_ = (S - 1) * H * (K * V * 4) + live_count * H * K * K * 4 + S * H * K * V * 4
+    return {"macs": macs, "mfma_macs": 3 * macs, "bytes": bytes_}
+
+
+def cpu_baseline(x, w, heads=4, tokens=12288):
+    """The fp64 oracle on a bounded sample: `heads` heads x the first `tokens`
+    tokens, with the workload's segment length; full method (recurrence,
+    updates, transitions, composition)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from gated_delta_rule_37_amd import synth
+    from oracle import kda_oracle as ko
+
+    seg_len = w.T // w.segments
+    tokens = min(tokens, w.T)
+    f = {n: ko.decode_bf16(synth.bits(x[n][:tokens, :heads])) for n in ("q", "k", "v", "g", "beta")}
+    cu = [0, tokens]
+    bounds = list(range(0, tokens, seg_len)) + [tokens]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ko.recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], cu)
+        A = ko.segment_transitions(f["k"], f["g"], f["beta"], cu, bounds)
+        B = ko.segment_updates(f["k"], f["v"], f["g"], f["beta"], cu, bounds)
+        ko.compose(A, B)
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(tokens * heads / w.H / dt, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"heads 0..{heads - 1} of {w.H}, tokens [0, {tokens}) of {w.name}, "
+                  f"{len(bounds) - 1} segments of {seg_len}; monolithic o+final, "
+                  f"transitions, updates, composition; fp64 numpy, 1 thread; {dt:.1f} s",
+    }
+
+
+def traffic_from_profile():
+    """HBM bytes per chunk-kernel launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "chunk_kernel_t65536_h32_s64_traffic.json")
+    src = os.path.join(ROOT, "gated_delta_rule_37_amd", "csrc", "kda_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t65536_h32_s64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=12288)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the segments stand in for the "
+              "context-parallel ranks on that GPU (no collectives). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_37_amd import kda, synth
+
+    w = synth.WORKLOADS.get(args.workload) or synth.STRESS[args.workload]
+    x = synth.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    cu = x["cu_seqlens"].tolist()
+    plan = kda.Plan(cu, w.segments)
+    pd = plan.device_blob(dev)
+    out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kda.segment_summaries(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["o"],
+                              out["final_state"], out["transitions"], out["updates"])
+        if ev is not None:
+            ev[1].record()
+        kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"])
+        if ev is not None:
+            ev[2].record()
+        kda.apply_carry(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["carry_in"],
+                        out["o"], out["final_state"])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    sums = [0.0, 0.0, 0.0]
+    for ev in events:
+        for j in range(3):
+            sums[j] += ev[j].elapsed_time(ev[j + 1])
+    pass1_ms, compose_ms, pass2_ms = (s / args.steps for s in sums)
+
+    blob = plan.blob
+    cw = chunk_kernel_work(blob, w.H)
+    chunk_ms_total = pass1_ms + pass2_ms          # two launches of kda_chunk_kernel
+    chunk_ms_avg = chunk_ms_total / 2
+    t_mfma = cw["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    t_hbm = cw["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+    traffic = traffic_from_profile()
+    if t_mfma >= t_hbm:
+        achieved = cw["mfma_macs"] * 2 / 2 / (chunk_ms_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = cw["bytes"] / 2 / (chunk_ms_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = "kda_chunk_kernel"
+    roof["launch_ms_avg"] = round(chunk_ms_avg, 4)
+
+    S = plan.S
+    live = int(sum(blob[4 + (S + 1) + 3 * S: 4 + (S + 1) + 4 * S]))
+    comp = compose_work(S, w.H, live)
+
+    res = {
+        "metric": "KDA fwd tokens/s at H=32,K=V=128 (segmented+compose)",
+        "value": round(w.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 state (split-bf16 MFMA)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
+                   "segments": w.segments, "sequences": plan.N, "seed": w.seed},
+        "roofline": roof,
+        "kernels_ms": {"segment_summaries": round(pass1_ms, 4),
+                       "compose_summaries": round(compose_ms, 4),
+                       "apply_carry": round(pass2_ms, 4)},
+        "compose_roofline": {
+            "achieved_tflops_bf16": round(comp["mfma_macs"] * 2 / (compose_ms * 1e-3) / 1e12, 2),
+            "achieved_gbs": round(comp["bytes"] / (compose_ms * 1e-3) / 1e9, 1),
+            "bound_ms_hbm": round(comp["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+            "bound_ms_mfma": round(comp["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 4),
+        },
+        "chunk_bounds_ms": {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads, args.cpu_tokens)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@ SMALL = [
     ("varlen_custom_bounds", 260, 3, [0, 90, 260], 3, [0, 45, 90, 260], 0.05),
     ("one_token_segments", 6, 1, [0, 6], 6, None, 0.05),
     ("many_segments_slow", 512, 2, [0, 512], 8, None, 0.01),
+    ("near_identity_transitions", 256, 2, [0, 256], 8, None, 0.001),
 ]
 
 
