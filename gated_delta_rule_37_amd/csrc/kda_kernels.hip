@@ -21,8 +21,8 @@
 // Kr = k e^{G-a}, Kc = k e^{a-G}, Qr = q e^{G-a}, so every in-chunk pair
 // (i, j) sees e^{G_i - G_j} = e^{G_i - a} e^{a - G_j} with each factor bounded
 // by the decay mass of at most 16 tokens.  Then W = e^a o (T diag(beta) Kr)
-// (column scaling), K^ = e^{G_C - a} o Kc, and the state update becomes
-//     S <- e^{G_C - a} o (e^a o S + Kc^T U)              (row scalings).
+// (a column scaling of the product), K^ = e^{G_C - a} o Kc element by element,
+// and Q o e^G = e^a o Qr.
 //
 // Precision: every product that feeds the state uses split bfloat16
 // operands x = x_hi + x_lo on the bf16 matrix cores (three MFMAs:
@@ -52,6 +52,9 @@ constexpr int NS = 136;   // row stride (bf16) of token-major [32][128] tiles
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
 constexpr float kLog2e = 1.4426950408889634f;
+// Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access;
+// accesses at or past num_records read zero and drop writes.
+constexpr int kBufDword3 = 0x00020000;
 
 enum Mode { kModeFwd = 0, kModeSumS = 1, kModeSumPhi = 2 };
 
@@ -101,6 +104,20 @@ __device__ __forceinline__ void tile_rows_to_b(const f32x16& t, int s, float out
   }
 }
 
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split two floats into packed (hi, lo) bf16 pairs: x = hi + lo to ~16 bits.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  bf16x2 h;
+  h[0] = static_cast<bf16>(x0);
+  h[1] = static_cast<bf16>(x1);
+  bf16x2 l;
+  l[0] = static_cast<bf16>(x0 - static_cast<float>(h[0]));
+  l[1] = static_cast<bf16>(x1 - static_cast<float>(h[1]));
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -117,7 +134,7 @@ struct ChunkSmem {
   bf16 qr_h[CH * NS], qr_l[CH * NS];   // Qr, token-major
   bf16 qg_h[CH * NS], qg_l[CH * NS];   // Q o e^G, token-major
   bf16 krt_h[KD * TS], krt_l[KD * TS]; // Kr, channel-major
-  bf16 kct_h[KD * TS], kct_l[KD * TS]; // Kc, channel-major
+  bf16 kht_h[KD * TS], kht_l[KD * TS]; // K^ = k e^{G_C - G}, channel-major
   bf16 vt[VD * TS];                    // V, channel-major (exact)
   bf16 tb_h[CH * TS], tb_l[CH * TS];   // T diag(beta), [i][j]
   bf16 p_h[CH * TS], p_l[CH * TS];     // P, [i][j]
@@ -126,9 +143,9 @@ struct ChunkSmem {
   float tt[CH * FS];                   // tt[c][i] = T[i][c] (diagonal blocks)
   float tn[CH * FS];                   // tn[i][c] = T[i][c] (diagonal blocks)
   float xt[16 * 17];                   // X = A10 T00, stored xt[c][i]
-  float tot[8 * KD];                   // per 4-token group gate sums
+  float tot[4 * KD];                   // per 8-token group gate sums
   float ea[KD];                        // e^{a}
-  float ega[KD];                       // e^{G_C - a}
+  float gam[KD];                       // e^{G_C}
   float beta[CH];
 };
 
@@ -171,7 +188,9 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   const int f = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index, made provably uniform so that wave-derived addresses and
+  // buffer resources live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int ln = lane & 31;   // MFMA row/column index of this lane
   const int lh = lane >> 5;   // MFMA half (k-group) of this lane
@@ -194,166 +213,204 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   const int mode = work.mode;
   const bool fwd = mode == kModeFwd;
   const bool use_v = mode != kModeSumPhi;
-
-  // ---- initial state: accumulator tile dt holds rows 32dt + 8r + 4lh + e
-  f32x16 S[4];
   const int col = 32 * wave + ln;
+
+  // ---- initial state: tile dt, register 4r+e holds row 32dt + 8r + 4lh + e
+  f32x16 S[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < 4; ++dt) S[dt] = zero16();
+  if (mode == kModeSumPhi) {
+    // identity: column col has its one in tile col/32, row col%32
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 32 * dt + 8 * r + 4 * lh + e;
-        float x = 0.f;
-        if (mode == kModeSumPhi) x = (d == col) ? 1.f : 0.f;
-        else if (work.from_carry)
-          x = p.carry[((static_cast<size_t>(seg) * H + h) * KD + d) * VD + col];
-        S[dt][4 * r + e] = x;
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          S[dt][4 * r + e] = (32 * dt + 8 * r + 4 * lh + e == col) ? 1.f : 0.f;
+        }
+      }
+    }
+  } else if (work.from_carry) {
+    const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
       }
     }
   }
 
-  const int cg = tid & 31;   // channel group: channels 4cg .. 4cg+3
-  const int tg = tid >> 5;   // token group: tokens 4tg .. 4tg+3 of the chunk
+  // P0 thread layout: wave w handles tokens 8w .. 8w+7 of the chunk, lane l
+  // channels 2l and 2l+1 (so every token row is one coalesced 256-byte read).
+  const int cp = lane;
+  const int tg = wave;
+  const int row_bytes = H * KD * 2;                       // one token of q, k, g, v
+  const int in_voff = (8 * tg) * row_bytes + 4 * cp;      // this thread's first element
+  const int o_row = H * VD * 4;                           // one token of o (bytes)
+  const int o_voff = (4 * lh) * o_row + 4 * (32 * wave + ln);
+
+  // raw BF16 pairs of the chunk being prefetched (registers, one chunk ahead);
+  // buffer loads past the fragment's last token return zero
+  uint32_t rk[8], rg[8], rq[8], rv[8];
+  float rb = 0.f;
+  auto fetch = [&](int cs) {
+    const int nn = min(CH, end - cs);
+    const size_t base = (static_cast<size_t>(cs) * H + h) * KD;
+    const int nrec = (nn - 1) * row_bytes + KD * 2;
+    const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + base), 0, nrec, kBufDword3);
+    const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.g + base), 0, nrec, kBufDword3);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int off = in_voff + m * row_bytes;
+      rk[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsk, off, 0, 0));
+      rg[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsg, off, 0, 0));
+    }
+    if (fwd) {
+      const auto rsq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, nrec, kBufDword3);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        rq[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsq, in_voff + m * row_bytes, 0, 0));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) rq[m] = 0u;
+    }
+    if (use_v) {
+      const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, nrec, kBufDword3);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        rv[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsv, in_voff + m * row_bytes, 0, 0));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) rv[m] = 0u;
+    }
+    if (tg == 0 && lane < CH) {
+      const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(p.beta + static_cast<size_t>(cs) * H + h), 0, (nn - 1) * H * 2 + 2, kBufDword3);
+      const uint32_t bb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane * H * 2, 0, 0));
+      rb = __uint_as_float(bb << 16);
+    }
+  };
+  fetch(beg);
 
   for (int c0 = beg; c0 < end; c0 += CH) {
     const int n = min(CH, end - c0);
 
-    // ================= P0: load the chunk, gate prefix, derived operands
-    float kf[4][4], qf[4][4], G[4][4];
-    uint16_t vb[4][4];
+    // ================= P0: gate prefix and the derived operands of the chunk
+    float kf[8][2], qf[8][2], G[8][2];
+    uint32_t vcur[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = 4 * tg + m;
-      uint2 kk = make_uint2(0, 0), qq = make_uint2(0, 0), gg = make_uint2(0, 0),
-            vv = make_uint2(0, 0);
-      if (i < n) {
-        const size_t row = (static_cast<size_t>(c0 + i) * H + h) * KD + 4 * cg;
-        kk = *reinterpret_cast<const uint2*>(p.k + row);
-        gg = *reinterpret_cast<const uint2*>(p.g + row);
-        if (fwd) qq = *reinterpret_cast<const uint2*>(p.q + row);
-        if (use_v) vv = *reinterpret_cast<const uint2*>(p.v + row);
-      }
-      const uint16_t ks[4] = {static_cast<uint16_t>(kk.x & 0xffff), static_cast<uint16_t>(kk.x >> 16),
-                              static_cast<uint16_t>(kk.y & 0xffff), static_cast<uint16_t>(kk.y >> 16)};
-      const uint16_t qs[4] = {static_cast<uint16_t>(qq.x & 0xffff), static_cast<uint16_t>(qq.x >> 16),
-                              static_cast<uint16_t>(qq.y & 0xffff), static_cast<uint16_t>(qq.y >> 16)};
-      const uint16_t gs[4] = {static_cast<uint16_t>(gg.x & 0xffff), static_cast<uint16_t>(gg.x >> 16),
-                              static_cast<uint16_t>(gg.y & 0xffff), static_cast<uint16_t>(gg.y >> 16)};
-      vb[m][0] = static_cast<uint16_t>(vv.x & 0xffff);
-      vb[m][1] = static_cast<uint16_t>(vv.x >> 16);
-      vb[m][2] = static_cast<uint16_t>(vv.y & 0xffff);
-      vb[m][3] = static_cast<uint16_t>(vv.y >> 16);
+    for (int m = 0; m < 8; ++m) {
+      kf[m][0] = __uint_as_float(rk[m] << 16);
+      kf[m][1] = __uint_as_float(rk[m] & 0xffff0000u);
+      qf[m][0] = __uint_as_float(rq[m] << 16);
+      qf[m][1] = __uint_as_float(rq[m] & 0xffff0000u);
+      G[m][0] = __uint_as_float(rg[m] << 16) * kLog2e;
+      G[m][1] = __uint_as_float(rg[m] & 0xffff0000u) * kLog2e;
+      vcur[m] = rv[m];
+    }
+    if (tg == 0 && lane < CH) sm.beta[lane] = rb;
+    if (c0 + CH < end) fetch(c0 + CH);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kf[m][c] = bf2f(ks[c]);
-        qf[m][c] = bf2f(qs[c]);
-        G[m][c] = bf2f(gs[c]) * kLog2e;
-      }
+    for (int m = 1; m < 8; ++m) {
+      G[m][0] += G[m - 1][0];
+      G[m][1] += G[m - 1][1];
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      G[1][c] += G[0][c];
-      G[2][c] += G[1][c];
-      G[3][c] += G[2][c];
-    }
-    *reinterpret_cast<float4*>(&sm.tot[tg * KD + 4 * cg]) = make_float4(G[3][0], G[3][1], G[3][2], G[3][3]);
-    if (tid < CH) {
-      sm.beta[tid] = (tid < n) ? bf2f(p.beta[static_cast<size_t>(c0 + tid) * H + h]) : 0.f;
-    }
+    *reinterpret_cast<float2*>(&sm.tot[tg * KD + 2 * cp]) = make_float2(G[7][0], G[7][1]);
     __syncthreads();
 
-    float pre[4] = {0.f, 0.f, 0.f, 0.f}, a[4], gc[4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float4 v4 = *reinterpret_cast<const float4*>(&sm.tot[t * KD + 4 * cg]);
-      const float vals[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (t < tg) pre[c] += vals[c];
-      }
-    }
-    // anchor a = G at token 15 and G_C = G at the chunk's last token, summed
-    // in the same order as the per-thread prefixes
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) s += sm.tot[t * KD + 4 * cg + c];
-      a[c] = s;
-#pragma unroll
-      for (int t = 4; t < 8; ++t) s += sm.tot[t * KD + 4 * cg + c];
-      gc[c] = s;
-    }
-    float eac[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      eac[c] = exp2f(a[c]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) G[m][c] += pre[c];
-    }
+    // anchor a = G at token 15 (end of token group 1), G_C = G at the last token
+    const float2 t0 = *reinterpret_cast<const float2*>(&sm.tot[0 * KD + 2 * cp]);
+    const float2 t1 = *reinterpret_cast<const float2*>(&sm.tot[1 * KD + 2 * cp]);
+    const float2 t2 = *reinterpret_cast<const float2*>(&sm.tot[2 * KD + 2 * cp]);
+    const float2 t3 = *reinterpret_cast<const float2*>(&sm.tot[3 * KD + 2 * cp]);
+    const float a[2] = {t0.x + t1.x, t0.y + t1.y};
+    const float gc[2] = {a[0] + t2.x + t3.x, a[1] + t2.y + t3.y};
+    float pre[2] = {0.f, 0.f};
+    if (tg == 1) { pre[0] = t0.x; pre[1] = t0.y; }
+    if (tg == 2) { pre[0] = a[0]; pre[1] = a[1]; }
+    if (tg == 3) { pre[0] = a[0] + t2.x; pre[1] = a[1] + t2.y; }
+    const float shift[2] = {pre[0] - a[0], pre[1] - a[1]};
+    const float ea[2] = {__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1])};
+    const float ega[2] = {__builtin_amdgcn_exp2f(gc[0] - a[0]), __builtin_amdgcn_exp2f(gc[1] - a[1])};
     if (tg == 0) {
-      *reinterpret_cast<float4*>(&sm.ea[4 * cg]) = make_float4(eac[0], eac[1], eac[2], eac[3]);
-      *reinterpret_cast<float4*>(&sm.ega[4 * cg]) =
-          make_float4(exp2f(gc[0] - a[0]), exp2f(gc[1] - a[1]), exp2f(gc[2] - a[2]), exp2f(gc[3] - a[3]));
+      *reinterpret_cast<float2*>(&sm.ea[2 * cp]) = make_float2(ea[0], ea[1]);
+      *reinterpret_cast<float2*>(&sm.gam[2 * cp]) =
+          make_float2(__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]));
     }
 
-    bf16 krh[4][4], krl[4][4], kch[4][4], kcl[4][4];
+    // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, K^ = Kc e^{G_C-a}, Qr, Qg = q e^G
+    uint32_t krh[8], krl[8], khh[4][2], khl[4][2];
+    float kh_prev[2] = {0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bf16x4 w_krh, w_krl, w_kch, w_kcl, w_qrh, w_qrl, w_qgh, w_qgl;
+    for (int m = 0; m < 8; ++m) {
+      float kr[2], kc[2], kh[2], qr[2], qg[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float x = G[m][c] - a[c];
-        const float er = exp2f(x);
-        const float ec = exp2f(-x);
-        split(kf[m][c] * er, krh[m][c], krl[m][c]);
-        split(kf[m][c] * ec, kch[m][c], kcl[m][c]);
-        w_krh[c] = krh[m][c];
-        w_krl[c] = krl[m][c];
-        w_kch[c] = kch[m][c];
-        w_kcl[c] = kcl[m][c];
-        if (fwd) {
-          const float qr = qf[m][c] * er;
-          bf16 hh, ll;
-          split(qr, hh, ll);
-          w_qrh[c] = hh;
-          w_qrl[c] = ll;
-          split(qr * eac[c], hh, ll);
-          w_qgh[c] = hh;
-          w_qgl[c] = ll;
-        }
+      for (int c = 0; c < 2; ++c) {
+        const float x = G[m][c] + shift[c];
+        const float er = __builtin_amdgcn_exp2f(x);
+        const float ec = __builtin_amdgcn_exp2f(-x);
+        kr[c] = kf[m][c] * er;
+        kc[c] = kf[m][c] * ec;
+        kh[c] = kc[c] * ega[c];
+        qr[c] = qf[m][c] * er;
+        qg[c] = qr[c] * ea[c];
       }
-      const int i = 4 * tg + m;
-      *reinterpret_cast<bf16x4*>(&sm.kr_h[i * NS + 4 * cg]) = w_krh;
-      *reinterpret_cast<bf16x4*>(&sm.kr_l[i * NS + 4 * cg]) = w_krl;
-      *reinterpret_cast<bf16x4*>(&sm.kc_h[i * NS + 4 * cg]) = w_kch;
-      *reinterpret_cast<bf16x4*>(&sm.kc_l[i * NS + 4 * cg]) = w_kcl;
+      const int i = 8 * tg + m;
+      uint32_t hh, ll;
+      split_pair(kr[0], kr[1], krh[m], krl[m]);
+      *reinterpret_cast<uint32_t*>(&sm.kr_h[i * NS + 2 * cp]) = krh[m];
+      *reinterpret_cast<uint32_t*>(&sm.kr_l[i * NS + 2 * cp]) = krl[m];
+      split_pair(kc[0], kc[1], hh, ll);
+      *reinterpret_cast<uint32_t*>(&sm.kc_h[i * NS + 2 * cp]) = hh;
+      *reinterpret_cast<uint32_t*>(&sm.kc_l[i * NS + 2 * cp]) = ll;
       if (fwd) {
-        *reinterpret_cast<bf16x4*>(&sm.qr_h[i * NS + 4 * cg]) = w_qrh;
-        *reinterpret_cast<bf16x4*>(&sm.qr_l[i * NS + 4 * cg]) = w_qrl;
-        *reinterpret_cast<bf16x4*>(&sm.qg_h[i * NS + 4 * cg]) = w_qgh;
-        *reinterpret_cast<bf16x4*>(&sm.qg_l[i * NS + 4 * cg]) = w_qgl;
+        split_pair(qr[0], qr[1], hh, ll);
+        *reinterpret_cast<uint32_t*>(&sm.qr_h[i * NS + 2 * cp]) = hh;
+        *reinterpret_cast<uint32_t*>(&sm.qr_l[i * NS + 2 * cp]) = ll;
+        split_pair(qg[0], qg[1], hh, ll);
+        *reinterpret_cast<uint32_t*>(&sm.qg_h[i * NS + 2 * cp]) = hh;
+        *reinterpret_cast<uint32_t*>(&sm.qg_l[i * NS + 2 * cp]) = ll;
+      }
+      // K^ packed along tokens (channel-major layout): pairs (m-1, m)
+      if (m & 1) {
+        split_pair(kh_prev[0], kh[0], khh[m >> 1][0], khl[m >> 1][0]);
+        split_pair(kh_prev[1], kh[1], khh[m >> 1][1], khl[m >> 1][1]);
+      } else {
+        kh_prev[0] = kh[0];
+        kh_prev[1] = kh[1];
       }
     }
+    // channel-major rows d = 2cp + c, tokens 8tg .. 8tg+7 (16 bytes each)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = 4 * cg + c;
-      bf16x4 t_krh, t_krl, t_kch, t_kcl, t_v;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        t_krh[m] = krh[m][c];
-        t_krl[m] = krl[m][c];
-        t_kch[m] = kch[m][c];
-        t_kcl[m] = kcl[m][c];
-        t_v[m] = __builtin_bit_cast(bf16, vb[m][c]);
+    for (int c = 0; c < 2; ++c) {
+      const int d = 2 * cp + c;
+      const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;  // low / high halves
+      uint4 wh, wl;
+      wh.x = __builtin_amdgcn_perm(krh[1], krh[0], sel);
+      wh.y = __builtin_amdgcn_perm(krh[3], krh[2], sel);
+      wh.z = __builtin_amdgcn_perm(krh[5], krh[4], sel);
+      wh.w = __builtin_amdgcn_perm(krh[7], krh[6], sel);
+      wl.x = __builtin_amdgcn_perm(krl[1], krl[0], sel);
+      wl.y = __builtin_amdgcn_perm(krl[3], krl[2], sel);
+      wl.z = __builtin_amdgcn_perm(krl[5], krl[4], sel);
+      wl.w = __builtin_amdgcn_perm(krl[7], krl[6], sel);
+      *reinterpret_cast<uint4*>(&sm.krt_h[d * TS + 8 * tg]) = wh;
+      *reinterpret_cast<uint4*>(&sm.krt_l[d * TS + 8 * tg]) = wl;
+      *reinterpret_cast<uint4*>(&sm.kht_h[d * TS + 8 * tg]) =
+          make_uint4(khh[0][c], khh[1][c], khh[2][c], khh[3][c]);
+      *reinterpret_cast<uint4*>(&sm.kht_l[d * TS + 8 * tg]) =
+          make_uint4(khl[0][c], khl[1][c], khl[2][c], khl[3][c]);
+      if (use_v) {
+        uint4 wv;
+        wv.x = __builtin_amdgcn_perm(vcur[1], vcur[0], sel);
+        wv.y = __builtin_amdgcn_perm(vcur[3], vcur[2], sel);
+        wv.z = __builtin_amdgcn_perm(vcur[5], vcur[4], sel);
+        wv.w = __builtin_amdgcn_perm(vcur[7], vcur[6], sel);
+        *reinterpret_cast<uint4*>(&sm.vt[d * TS + 8 * tg]) = wv;
       }
-      *reinterpret_cast<bf16x4*>(&sm.krt_h[d * TS + 4 * tg]) = t_krh;
-      *reinterpret_cast<bf16x4*>(&sm.krt_l[d * TS + 4 * tg]) = t_krl;
-      *reinterpret_cast<bf16x4*>(&sm.kct_h[d * TS + 4 * tg]) = t_kch;
-      *reinterpret_cast<bf16x4*>(&sm.kct_l[d * TS + 4 * tg]) = t_kcl;
-      if (use_v) *reinterpret_cast<bf16x4*>(&sm.vt[d * TS + 4 * tg]) = t_v;
     }
     __syncthreads();
 
@@ -402,18 +459,6 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         }
       }
     }
-
-    // every wave: its state columns as split B operands (rows of S = k index)
-    bf16x8 sbh[8], sbl[8];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float x[8];
-        tile_rows_to_b(S[dt], s, x);
-        split8(x, sbh[2 * dt + s], sbl[2 * dt + s]);
-      }
-    }
     __syncthreads();
 
     // ================= P2: T = (I + A)^{-1} by 16 x 16 blocks
@@ -427,17 +472,16 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const float* arow = &sm.at[(base + jj) * FS + base];
-        float av[16];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
+        for (int q4 = jj / 4; q4 < 4; ++q4) {
           const float4 t4 = *reinterpret_cast<const float4*>(&arow[4 * q4]);
-          av[4 * q4 + 0] = t4.x;
-          av[4 * q4 + 1] = t4.y;
-          av[4 * q4 + 2] = t4.z;
-          av[4 * q4 + 3] = t4.w;
-        }
+          const float av[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-        for (int i = jj + 1; i < 16; ++i) x[i] -= av[i] * x[jj];
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            if (i > jj) x[i] -= av[e] * x[jj];
+          }
+        }
       }
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -495,17 +539,11 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
       for (int r = 0; r < 4; ++r) {
         const int d0 = 32 * wave + 8 * r + 4 * lh;
         const float4 e4 = *reinterpret_cast<const float4*>(&sm.ea[d0]);
-        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-        bf16x4 wh, wl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16 hh, ll;
-          split(-ev[e] * acc[4 * r + e], hh, ll);
-          wh[e] = hh;
-          wl[e] = ll;
-        }
-        *reinterpret_cast<bf16x4*>(&sm.kr_h[ln * NS + d0]) = wh;
-        *reinterpret_cast<bf16x4*>(&sm.kr_l[ln * NS + d0]) = wl;
+        uint32_t h01, l01, h23, l23;
+        split_pair(-e4.x * acc[4 * r + 0], -e4.y * acc[4 * r + 1], h01, l01);
+        split_pair(-e4.z * acc[4 * r + 2], -e4.w * acc[4 * r + 3], h23, l23);
+        *reinterpret_cast<uint2*>(&sm.kr_h[ln * NS + d0]) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(&sm.kr_l[ln * NS + d0]) = make_uint2(l01, l23);
       }
     }
     f32x16 U = zero16();
@@ -520,20 +558,21 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     }
     __syncthreads();
 
-    // ================= P4: U -= W S, O = Qg S + P U, S <- e^{G_C-a}(e^a S + Kc^T U)
+    // ================= P4: U -= W S, O = Qg S + P U, S <- e^{G_C} S + K^^T U
+    // The state's rows are split into B operands one k-step at a time.
+    f32x16 O = zero16();
 #pragma unroll
     for (int kk = 0; kk < KD / 16; ++kk) {
+      float x[8];
+      tile_rows_to_b(S[kk >> 1], kk & 1, x);
+      bf16x8 sbh, sbl;
+      split8(x, sbh, sbl);
       const int off = ln * NS + 16 * kk + 8 * lh;
       U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
-                *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh[kk], sbl[kk], U);
-    }
-    f32x16 O = zero16();
-    if (fwd) {
-#pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        const int off = ln * NS + 16 * kk + 8 * lh;
+                *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, U);
+      if (fwd) {
         O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.qg_h[off]),
-                  *reinterpret_cast<const bf16x8*>(&sm.qg_l[off]), sbh[kk], sbl[kk], O);
+                  *reinterpret_cast<const bf16x8*>(&sm.qg_l[off]), sbh, sbl, O);
       }
     }
     bf16x8 ubh[2], ubl[2];
@@ -550,12 +589,26 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]),
                   *reinterpret_cast<const bf16x8*>(&sm.p_l[off]), ubh[s], ubl[s], O);
       }
+      // rows past the fragment's end fall outside the buffer and are dropped
+      const auto rso = __builtin_amdgcn_make_buffer_rsrc(
+          p.o + (static_cast<size_t>(c0) * H + h) * VD, 0, (n - 1) * o_row + 4 * VD, kBufDword3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (an element of an ext_vector must go through a scalar first:
+          // __builtin_bit_cast on the element reads element 0)
+          const float ov = O[4 * r + e];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff + (8 * r + e) * o_row,
+                                                0, 0);
+        }
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.ea[32 * dt + 8 * r + 4 * lh]);
+        const float4 e4 = *reinterpret_cast<const float4*>(&sm.gam[32 * dt + 8 * r + 4 * lh]);
         S[dt][4 * r + 0] *= e4.x;
         S[dt][4 * r + 1] *= e4.y;
         S[dt][4 * r + 2] *= e4.z;
@@ -564,29 +617,12 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int off = (32 * dt + ln) * TS + 16 * s + 8 * lh;
-        S[dt] = mfma3(*reinterpret_cast<const bf16x8*>(&sm.kct_h[off]),
-                      *reinterpret_cast<const bf16x8*>(&sm.kct_l[off]), ubh[s], ubl[s], S[dt]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.ega[32 * dt + 8 * r + 4 * lh]);
-        S[dt][4 * r + 0] *= e4.x;
-        S[dt][4 * r + 1] *= e4.y;
-        S[dt][4 * r + 2] *= e4.z;
-        S[dt][4 * r + 3] *= e4.w;
+        S[dt] = mfma3(*reinterpret_cast<const bf16x8*>(&sm.kht_h[off]),
+                      *reinterpret_cast<const bf16x8*>(&sm.kht_l[off]), ubh[s], ubl[s], S[dt]);
       }
     }
-    if (fwd) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * r + 4 * lh + e;
-          if (i < n) p.o[(static_cast<size_t>(c0 + i) * H + h) * VD + col] = O[4 * r + e];
-        }
-      }
-    }
-    __syncthreads();
+    // no barrier here: the next chunk writes only tot and beta before its first
+    // barrier, and P4 reads neither
   }
 
   // ---- the fragment's final state
@@ -601,17 +637,21 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     if (p.pass == 1 && (flags & kFragSegLast))
       dst1 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
   }
+  if (dst0) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 32 * dt + 8 * r + 4 * lh + e;
-        if (dst0) dst0[d * VD + col] = S[dt][4 * r + e];
-        if (dst1) dst1[d * VD + col] = S[dt][4 * r + e];
-      }
-    }
+        for (int e = 0; e < 4; ++e) dst0[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = S[dt][4 * r + e];
+  }
+  if (dst1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst1[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = S[dt][4 * r + e];
   }
 }
 
