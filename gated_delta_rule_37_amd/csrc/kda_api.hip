@@ -13,9 +13,6 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kThreads = 256;
-constexpr int kComposeColumnBlocks = 4;   // 128 state columns / 32
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V) {
@@ -75,7 +72,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.updates = updates;
   p.carry = nullptr;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 2), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 2), dim3(kda::kChunkThreads), 0, stream, p);
   return finish_launch();
 }
 
@@ -95,7 +92,7 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
   p.updates = updates;
   p.carry = carry_in;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(H, kComposeColumnBlocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(H, kda::kComposeColumnBlocks), dim3(kda::kComposeThreads), 0,
                      stream, p);
   return finish_launch();
 }
@@ -125,6 +122,6 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.updates = nullptr;
   p.carry = carry_in;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kda::kChunkThreads), 0, stream, p);
   return finish_launch();
 }

@@ -11,6 +11,10 @@
 
 namespace kda {
 
+constexpr int kChunkThreads = 512;    // kda_chunk_kernel workgroup size
+constexpr int kComposeThreads = 256;  // kda_compose_kernel workgroup size
+constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
+
 struct ChunkParams {
   const int32_t* plan;   // device copy of the plan blob
   BlobLayout L;

@@ -47,7 +47,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
 constexpr int CH = 32;    // chunk length (tokens)
-constexpr int NT = 256;   // threads per workgroup (4 waves of 64)
+constexpr int NT = kChunkThreads;     // chunk kernel: 8 waves of 64
+constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 136;   // row stride (bf16) of token-major [32][128] tiles
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
@@ -78,6 +79,56 @@ __device__ __forceinline__ f32x16 mfma3(const bf16x8& ah, const bf16x8& al, cons
   acc = mfma(ah, bl, acc);
   acc = mfma(al, bh, acc);
   return acc;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += a * b (16x16x32) with split operands (hi*hi + hi*lo + lo*hi).
+__device__ __forceinline__ f32x4 mfma16x3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                          const bf16x8& bl, f32x4 acc) {
+  acc = mfma16(ah, bh, acc);
+  acc = mfma16(ah, bl, acc);
+  acc = mfma16(al, bh, acc);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z;
+  z[0] = z[1] = z[2] = z[3] = 0.f;
+  return z;
+}
+
+// Wait states between an MFMA that wrote t0/t1 and the permlane swaps that read
+// them.  The compiler does not always pad this dependency (seen when the last
+// MFMA of a chain sits in another basic block), and a swap that reads the
+// registers early picks up the accumulator without its last product.  The
+// swaps consume the asm's outputs, so they cannot be scheduled before it; 20
+// wait states cover a 16-pass MFMA.
+__device__ __forceinline__ void mfma_result_fence(f32x4& t0, f32x4& t1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t0), "+v"(t1));
+}
+__device__ __forceinline__ void mfma_result_fence(f32x16& t) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t));
+}
+
+// Two 16 x 16 accumulator tiles t0 (rows 0..15) and t1 (rows 16..31) hold, in
+// lane l and register e, rows 4(l/16) + e of column l%16.  A B operand of the
+// 16x16x32 MFMA needs rows 8(l/16) + 0..7 of one column per lane.  A 32-lane
+// swap of (t0, t1) followed by a 16-lane swap regroups them (checked on gfx950:
+// permlane32_swap(x, y) -> (x_lo|y_lo, x_hi|y_hi); permlane16_swap(x, y) ->
+// (x0 y0 x2 y2, x1 y1 x3 y3) by 16-lane rows).
+__device__ __forceinline__ void tiles16_to_b(const f32x4& t0, const f32x4& t1, float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[e]), __float_as_uint(t1[e]), false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(p[0], p[1], false, false);
+    out[e] = __uint_as_float(q[0]);
+    out[4 + e] = __uint_as_float(q[1]);
+  }
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -143,7 +194,7 @@ struct ChunkSmem {
   float tt[CH * FS];                   // tt[c][i] = T[i][c] (diagonal blocks)
   float tn[CH * FS];                   // tn[i][c] = T[i][c] (diagonal blocks)
   float xt[16 * 17];                   // X = A10 T00, stored xt[c][i]
-  float tot[4 * KD];                   // per 8-token group gate sums
+  float tot[8 * KD];                   // per 4-token group gate sums
   float ea[KD];                        // e^{a}
   float gam[KD];                       // e^{G_C}
   float beta[CH];
@@ -182,7 +233,8 @@ __device__ __forceinline__ Work decode_work(const ChunkParams& p, int32_t flags,
 
 // One workgroup runs one fragment (a run of tokens of one sequence inside one
 // segment) of one head, chunk after chunk, holding the state in registers.
-// Wave w owns state columns [32w, 32w + 32).
+// Eight waves; wave w owns state columns [16w, 16w + 16) as eight 16 x 16 FP32
+// accumulator tiles.
 __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ ChunkSmem sm;
   const int f = blockIdx.x;
@@ -192,8 +244,10 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   // buffer resources live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int ln = lane & 31;   // MFMA row/column index of this lane
-  const int lh = lane >> 5;   // MFMA half (k-group) of this lane
+  const int ln = lane & 31;   // 32x32x16 MFMA: row/column index of this lane
+  const int lh = lane >> 5;   // 32x32x16 MFMA: k-group of this lane
+  const int lm = lane & 15;   // 16x16x32 MFMA: row/column index of this lane
+  const int lg = lane >> 4;   // 16x16x32 MFMA: k-group / row group of this lane
   const int H = p.H;
 
   const int32_t flags = p.plan[p.L.frag_flags + f];
@@ -213,48 +267,39 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   const int mode = work.mode;
   const bool fwd = mode == kModeFwd;
   const bool use_v = mode != kModeSumPhi;
-  const int col = 32 * wave + ln;
+  const int col = 16 * wave + lm;
 
-  // ---- initial state: tile dt, register 4r+e holds row 32dt + 8r + 4lh + e
-  f32x16 S[4];
+  // ---- initial state: tile dt, register e holds row 16dt + 4lg + e
+  f32x4 S[8];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) S[dt] = zero16();
+  for (int dt = 0; dt < 8; ++dt) S[dt] = zero4();
   if (mode == kModeSumPhi) {
-    // identity: column col has its one in tile col/32, row col%32
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          S[dt][4 * r + e] = (32 * dt + 8 * r + 4 * lh + e == col) ? 1.f : 0.f;
-        }
-      }
+      for (int e = 0; e < 4; ++e) S[dt][e] = (16 * dt + 4 * lg + e == col) ? 1.f : 0.f;
     }
   } else if (work.from_carry) {
     const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
-      }
+      for (int e = 0; e < 4; ++e) S[dt][e] = src[(16 * dt + 4 * lg + e) * VD];
     }
   }
 
-  // P0 thread layout: wave w handles tokens 8w .. 8w+7 of the chunk, lane l
+  // P0 thread layout: wave w handles tokens 4w .. 4w+3 of the chunk, lane l
   // channels 2l and 2l+1 (so every token row is one coalesced 256-byte read).
   const int cp = lane;
   const int tg = wave;
   const int row_bytes = H * KD * 2;                       // one token of q, k, g, v
-  const int in_voff = (8 * tg) * row_bytes + 4 * cp;      // this thread's first element
+  const int in_voff = (4 * tg) * row_bytes + 4 * cp;      // this thread's first element
   const int o_row = H * VD * 4;                           // one token of o (bytes)
-  const int o_voff = (4 * lh) * o_row + 4 * (32 * wave + ln);
+  const int o_voff = (4 * lg) * o_row + 4 * col;
 
   // raw BF16 pairs of the chunk being prefetched (registers, one chunk ahead);
   // buffer loads past the fragment's last token return zero
-  uint32_t rk[8], rg[8], rq[8], rv[8];
+  uint32_t rk[4], rg[4], rq[4], rv[4];
   float rb = 0.f;
   auto fetch = [&](int cs) {
     const int nn = min(CH, end - cs);
@@ -263,7 +308,7 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + base), 0, nrec, kBufDword3);
     const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.g + base), 0, nrec, kBufDword3);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       const int off = in_voff + m * row_bytes;
       rk[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsk, off, 0, 0));
       rg[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsg, off, 0, 0));
@@ -271,20 +316,20 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     if (fwd) {
       const auto rsq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, nrec, kBufDword3);
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 4; ++m)
         rq[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsq, in_voff + m * row_bytes, 0, 0));
     } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) rq[m] = 0u;
+      for (int m = 0; m < 4; ++m) rq[m] = 0u;
     }
     if (use_v) {
       const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, nrec, kBufDword3);
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 4; ++m)
         rv[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsv, in_voff + m * row_bytes, 0, 0));
     } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) rv[m] = 0u;
+      for (int m = 0; m < 4; ++m) rv[m] = 0u;
     }
     if (tg == 0 && lane < CH) {
       const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
@@ -299,10 +344,10 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     const int n = min(CH, end - c0);
 
     // ================= P0: gate prefix and the derived operands of the chunk
-    float kf[8][2], qf[8][2], G[8][2];
-    uint32_t vcur[8];
+    float kf[4][2], qf[4][2], G[4][2];
+    uint32_t vcur[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       kf[m][0] = __uint_as_float(rk[m] << 16);
       kf[m][1] = __uint_as_float(rk[m] & 0xffff0000u);
       qf[m][0] = __uint_as_float(rq[m] << 16);
@@ -314,24 +359,24 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     if (tg == 0 && lane < CH) sm.beta[lane] = rb;
     if (c0 + CH < end) fetch(c0 + CH);
 #pragma unroll
-    for (int m = 1; m < 8; ++m) {
+    for (int m = 1; m < 4; ++m) {
       G[m][0] += G[m - 1][0];
       G[m][1] += G[m - 1][1];
     }
-    *reinterpret_cast<float2*>(&sm.tot[tg * KD + 2 * cp]) = make_float2(G[7][0], G[7][1]);
+    *reinterpret_cast<float2*>(&sm.tot[tg * KD + 2 * cp]) = make_float2(G[3][0], G[3][1]);
     __syncthreads();
 
-    // anchor a = G at token 15 (end of token group 1), G_C = G at the last token
-    const float2 t0 = *reinterpret_cast<const float2*>(&sm.tot[0 * KD + 2 * cp]);
-    const float2 t1 = *reinterpret_cast<const float2*>(&sm.tot[1 * KD + 2 * cp]);
-    const float2 t2 = *reinterpret_cast<const float2*>(&sm.tot[2 * KD + 2 * cp]);
-    const float2 t3 = *reinterpret_cast<const float2*>(&sm.tot[3 * KD + 2 * cp]);
-    const float a[2] = {t0.x + t1.x, t0.y + t1.y};
-    const float gc[2] = {a[0] + t2.x + t3.x, a[1] + t2.y + t3.y};
-    float pre[2] = {0.f, 0.f};
-    if (tg == 1) { pre[0] = t0.x; pre[1] = t0.y; }
-    if (tg == 2) { pre[0] = a[0]; pre[1] = a[1]; }
-    if (tg == 3) { pre[0] = a[0] + t2.x; pre[1] = a[1] + t2.y; }
+    // prefix of the earlier token groups, the anchor a = G at token 15 (end of
+    // group 3) and G_C = G at the last token, all summed in group order
+    float pre[2] = {0.f, 0.f}, a[2] = {0.f, 0.f}, gc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float2 tv = *reinterpret_cast<const float2*>(&sm.tot[t * KD + 2 * cp]);
+      if (t == tg) { pre[0] = gc[0]; pre[1] = gc[1]; }
+      if (t == 4) { a[0] = gc[0]; a[1] = gc[1]; }
+      gc[0] += tv.x;
+      gc[1] += tv.y;
+    }
     const float shift[2] = {pre[0] - a[0], pre[1] - a[1]};
     const float ea[2] = {__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1])};
     const float ega[2] = {__builtin_amdgcn_exp2f(gc[0] - a[0]), __builtin_amdgcn_exp2f(gc[1] - a[1])};
@@ -342,10 +387,10 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     }
 
     // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, K^ = Kc e^{G_C-a}, Qr, Qg = q e^G
-    uint32_t krh[8], krl[8], khh[4][2], khl[4][2];
+    uint32_t krh[4], krl[4], khh[2][2], khl[2][2];
     float kh_prev[2] = {0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       float kr[2], kc[2], kh[2], qr[2], qg[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -358,7 +403,7 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         qr[c] = qf[m][c] * er;
         qg[c] = qr[c] * ea[c];
       }
-      const int i = 8 * tg + m;
+      const int i = 4 * tg + m;
       uint32_t hh, ll;
       split_pair(kr[0], kr[1], krh[m], krl[m]);
       *reinterpret_cast<uint32_t*>(&sm.kr_h[i * NS + 2 * cp]) = krh[m];
@@ -383,33 +428,20 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         kh_prev[1] = kh[1];
       }
     }
-    // channel-major rows d = 2cp + c, tokens 8tg .. 8tg+7 (16 bytes each)
+    // channel-major rows d = 2cp + c, tokens 4tg .. 4tg+3 (8 bytes each)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int d = 2 * cp + c;
       const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;  // low / high halves
-      uint4 wh, wl;
-      wh.x = __builtin_amdgcn_perm(krh[1], krh[0], sel);
-      wh.y = __builtin_amdgcn_perm(krh[3], krh[2], sel);
-      wh.z = __builtin_amdgcn_perm(krh[5], krh[4], sel);
-      wh.w = __builtin_amdgcn_perm(krh[7], krh[6], sel);
-      wl.x = __builtin_amdgcn_perm(krl[1], krl[0], sel);
-      wl.y = __builtin_amdgcn_perm(krl[3], krl[2], sel);
-      wl.z = __builtin_amdgcn_perm(krl[5], krl[4], sel);
-      wl.w = __builtin_amdgcn_perm(krl[7], krl[6], sel);
-      *reinterpret_cast<uint4*>(&sm.krt_h[d * TS + 8 * tg]) = wh;
-      *reinterpret_cast<uint4*>(&sm.krt_l[d * TS + 8 * tg]) = wl;
-      *reinterpret_cast<uint4*>(&sm.kht_h[d * TS + 8 * tg]) =
-          make_uint4(khh[0][c], khh[1][c], khh[2][c], khh[3][c]);
-      *reinterpret_cast<uint4*>(&sm.kht_l[d * TS + 8 * tg]) =
-          make_uint4(khl[0][c], khl[1][c], khl[2][c], khl[3][c]);
+      *reinterpret_cast<uint2*>(&sm.krt_h[d * TS + 4 * tg]) =
+          make_uint2(__builtin_amdgcn_perm(krh[1], krh[0], sel), __builtin_amdgcn_perm(krh[3], krh[2], sel));
+      *reinterpret_cast<uint2*>(&sm.krt_l[d * TS + 4 * tg]) =
+          make_uint2(__builtin_amdgcn_perm(krl[1], krl[0], sel), __builtin_amdgcn_perm(krl[3], krl[2], sel));
+      *reinterpret_cast<uint2*>(&sm.kht_h[d * TS + 4 * tg]) = make_uint2(khh[0][c], khh[1][c]);
+      *reinterpret_cast<uint2*>(&sm.kht_l[d * TS + 4 * tg]) = make_uint2(khl[0][c], khl[1][c]);
       if (use_v) {
-        uint4 wv;
-        wv.x = __builtin_amdgcn_perm(vcur[1], vcur[0], sel);
-        wv.y = __builtin_amdgcn_perm(vcur[3], vcur[2], sel);
-        wv.z = __builtin_amdgcn_perm(vcur[5], vcur[4], sel);
-        wv.w = __builtin_amdgcn_perm(vcur[7], vcur[6], sel);
-        *reinterpret_cast<uint4*>(&sm.vt[d * TS + 8 * tg]) = wv;
+        *reinterpret_cast<uint2*>(&sm.vt[d * TS + 4 * tg]) =
+            make_uint2(__builtin_amdgcn_perm(vcur[1], vcur[0], sel), __builtin_amdgcn_perm(vcur[3], vcur[2], sel));
       }
     }
     __syncthreads();
@@ -492,16 +524,16 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
       for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
     }
     __syncthreads();
-    const int ti = tid >> 4;   // row within a 16 x 16 block
-    const int tc = tid & 15;   // column within a 16 x 16 block
-    {
+    const int ti = (tid >> 4) & 15;   // row within a 16 x 16 block
+    const int tc = tid & 15;          // column within a 16 x 16 block
+    if (tid < 256) {
       float xs = 0.f;
 #pragma unroll
       for (int kx = 0; kx < 16; ++kx) xs += sm.an[(16 + ti) * FS + kx] * sm.tt[tc * FS + kx];
       sm.xt[tc * 17 + ti] = xs;
     }
     __syncthreads();
-    {
+    if (tid < 256) {
       float t10 = 0.f;
 #pragma unroll
       for (int kx = 0; kx < 16; ++kx) t10 -= sm.tn[(16 + ti) * FS + 16 + kx] * sm.xt[tc * 17 + kx];
@@ -522,8 +554,9 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     }
     __syncthreads();
 
-    // ================= P3: -W (token-major, into kr_*) and U~ = T diag(beta) V
-    {
+    // ================= P3: -W (token-major, into kr_*; waves 0-3) and
+    // U~ = T diag(beta) V (every wave, its own 16 columns)
+    if (wave < 4) {
       f32x16 acc = zero16();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -546,80 +579,74 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         *reinterpret_cast<uint2*>(&sm.kr_l[ln * NS + d0]) = make_uint2(l01, l23);
       }
     }
-    f32x16 U = zero16();
+    f32x4 U[2] = {zero4(), zero4()};
     if (use_v) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[col * TS + 8 * lg]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int aoff = ln * TS + 16 * s + 8 * lh;
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[(32 * wave + ln) * TS + 16 * s + 8 * lh]);
-        U = mfma(*reinterpret_cast<const bf16x8*>(&sm.tb_h[aoff]), bv, U);
-        U = mfma(*reinterpret_cast<const bf16x8*>(&sm.tb_l[aoff]), bv, U);
+      for (int rt = 0; rt < 2; ++rt) {
+        const int aoff = (16 * rt + lm) * TS + 8 * lg;
+        U[rt] = mfma16(*reinterpret_cast<const bf16x8*>(&sm.tb_h[aoff]), bv, U[rt]);
+        U[rt] = mfma16(*reinterpret_cast<const bf16x8*>(&sm.tb_l[aoff]), bv, U[rt]);
       }
     }
     __syncthreads();
 
     // ================= P4: U -= W S, O = Qg S + P U, S <- e^{G_C} S + K^^T U
-    // The state's rows are split into B operands one k-step at a time.
-    f32x16 O = zero16();
+    // The state's rows are split into B operands one 32-row k-step at a time.
+    f32x4 O[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int kk = 0; kk < KD / 16; ++kk) {
+    for (int kk = 0; kk < KD / 32; ++kk) {
       float x[8];
-      tile_rows_to_b(S[kk >> 1], kk & 1, x);
+      tiles16_to_b(S[2 * kk], S[2 * kk + 1], x);
       bf16x8 sbh, sbl;
       split8(x, sbh, sbl);
-      const int off = ln * NS + 16 * kk + 8 * lh;
-      U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
-                *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, U);
-      if (fwd) {
-        O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.qg_h[off]),
-                  *reinterpret_cast<const bf16x8*>(&sm.qg_l[off]), sbh, sbl, O);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int off = (16 * rt + lm) * NS + 32 * kk + 8 * lg;
+        U[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
+                         *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, U[rt]);
+        if (fwd) {
+          O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.qg_h[off]),
+                           *reinterpret_cast<const bf16x8*>(&sm.qg_l[off]), sbh, sbl, O[rt]);
+        }
       }
     }
-    bf16x8 ubh[2], ubl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    bf16x8 ubh, ubl;
+    {
       float x[8];
-      tile_rows_to_b(U, s, x);
-      split8(x, ubh[s], ubl[s]);
+      mfma_result_fence(U[0], U[1]);
+      tiles16_to_b(U[0], U[1], x);
+      split8(x, ubh, ubl);
     }
     if (fwd) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int off = ln * TS + 16 * s + 8 * lh;
-        O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]),
-                  *reinterpret_cast<const bf16x8*>(&sm.p_l[off]), ubh[s], ubl[s], O);
-      }
       // rows past the fragment's end fall outside the buffer and are dropped
       const auto rso = __builtin_amdgcn_make_buffer_rsrc(
           p.o + (static_cast<size_t>(c0) * H + h) * VD, 0, (n - 1) * o_row + 4 * VD, kBufDword3);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int rt = 0; rt < 2; ++rt) {
+        const int off = (16 * rt + lm) * TS + 8 * lg;
+        O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]),
+                         *reinterpret_cast<const bf16x8*>(&sm.p_l[off]), ubh, ubl, O[rt]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // (an element of an ext_vector must go through a scalar first:
+          // (an element of an ext_vector goes through a scalar first:
           // __builtin_bit_cast on the element reads element 0)
-          const float ov = O[4 * r + e];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff + (8 * r + e) * o_row,
+          const float ov = O[rt][e];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff + (16 * rt + e) * o_row,
                                                 0, 0);
         }
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.gam[32 * dt + 8 * r + 4 * lh]);
-        S[dt][4 * r + 0] *= e4.x;
-        S[dt][4 * r + 1] *= e4.y;
-        S[dt][4 * r + 2] *= e4.z;
-        S[dt][4 * r + 3] *= e4.w;
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int off = (32 * dt + ln) * TS + 16 * s + 8 * lh;
-        S[dt] = mfma3(*reinterpret_cast<const bf16x8*>(&sm.kht_h[off]),
-                      *reinterpret_cast<const bf16x8*>(&sm.kht_l[off]), ubh[s], ubl[s], S[dt]);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const float4 e4 = *reinterpret_cast<const float4*>(&sm.gam[16 * dt + 4 * lg]);
+      S[dt][0] *= e4.x;
+      S[dt][1] *= e4.y;
+      S[dt][2] *= e4.z;
+      S[dt][3] *= e4.w;
+      const int off = (16 * dt + lm) * TS + 8 * lg;
+      S[dt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kht_h[off]),
+                       *reinterpret_cast<const bf16x8*>(&sm.kht_l[off]), ubh, ubl, S[dt]);
     }
     // no barrier here: the next chunk writes only tot and beta before its first
     // barrier, and P4 reads neither
@@ -639,26 +666,22 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   }
   if (dst0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst0[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = S[dt][4 * r + e];
+      for (int e = 0; e < 4; ++e) dst0[(16 * dt + 4 * lg + e) * VD + col] = S[dt][e];
   }
   if (dst1) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst1[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = S[dt][4 * r + e];
+      for (int e = 0; e < 4; ++e) dst1[(16 * dt + 4 * lg + e) * VD + col] = S[dt][e];
   }
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of
 // 32 state columns.  Wave w computes rows [32w, 32w + 32); the current carry
 // is shared through LDS as split B operands.
-__global__ void __launch_bounds__(NT, 1) kda_compose_kernel(ComposeParams p) {
+__global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
   __shared__ bf16x8 cbh[8][64];
   __shared__ bf16x8 cbl[8][64];
   const int h = blockIdx.x;
@@ -688,6 +711,7 @@ __global__ void __launch_bounds__(NT, 1) kda_compose_kernel(ComposeParams p) {
       for (int e = 0; e < 4; ++e) nxt[4 * q + e] = bsrc[(32 * wave + 8 * q + 4 * lh + e) * VD + col];
     }
     if (p.plan[p.L.seg_transition_live + r]) {
+      mfma_result_fence(cur);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float x[8];
