@@ -13,16 +13,14 @@
 // g up to token i, all exponent arithmetic in log2 units):
 //     A[i][j] = beta_i sum_d k_id k_jd e^{G_id - G_jd}     (j < i)
 //     T       = (I + A)^{-1}                              (unit lower triangular)
-//     W       = T diag(beta) (K o e^G)                    U~ = T diag(beta) V
-//     U       = U~ - W S
+//     U       = T diag(beta) (V - (K o e^G) S)            (the delta-rule targets)
 //     O       = (Q o e^G) S + P U,  P[i][j] = sum_d q_id k_jd e^{G_id - G_jd} (j <= i)
 //     S      <- Diag(e^{G_C}) S + K^^T U,  K^[j][d] = k_jd e^{G_Cd - G_jd}
 // The exponential factors are split around one anchor per chunk (token 15):
 // Kr = k e^{G-a}, Kc = k e^{a-G}, Qr = q e^{G-a}, so every in-chunk pair
 // (i, j) sees e^{G_i - G_j} = e^{G_i - a} e^{a - G_j} with each factor bounded
-// by the decay mass of at most 16 tokens.  Then W = e^a o (T diag(beta) Kr)
-// (a column scaling of the product), K^ = e^{G_C - a} o Kc element by element,
-// and Q o e^G = e^a o Qr.
+// by the decay mass of at most 16 tokens.  Then (K o e^G) S = Kr (e^a o S),
+// (Q o e^G) S = Qr (e^a o S) and K^ = e^{G_C - a} o Kc.
 //
 // Precision: every product that feeds the state uses split bfloat16
 // operands x = x_hi + x_lo on the bf16 matrix cores (three MFMAs:
@@ -52,6 +50,7 @@ constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 136;   // row stride (bf16) of token-major [32][128] tiles
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
+constexpr int XS = 20;    // row stride (fp32) of the 16 x 16 off-diagonal product
 constexpr float kLog2e = 1.4426950408889634f;
 // Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access;
 // accesses at or past num_records read zero and drop writes.
@@ -180,11 +179,9 @@ __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo)
 }
 
 struct ChunkSmem {
-  bf16 kr_h[CH * NS], kr_l[CH * NS];   // Kr, token-major; holds -W after the A product
-  bf16 kc_h[CH * NS], kc_l[CH * NS];   // Kc, token-major
-  bf16 qr_h[CH * NS], qr_l[CH * NS];   // Qr, token-major
-  bf16 qg_h[CH * NS], qg_l[CH * NS];   // Q o e^G, token-major
-  bf16 krt_h[KD * TS], krt_l[KD * TS]; // Kr, channel-major
+  bf16 kr_h[CH * NS], kr_l[CH * NS];   // Kr = k e^{G-a}, token-major
+  bf16 kc_h[CH * NS], kc_l[CH * NS];   // Kc = k e^{a-G}, token-major
+  bf16 qr_h[CH * NS], qr_l[CH * NS];   // Qr = q e^{G-a}, token-major
   bf16 kht_h[KD * TS], kht_l[KD * TS]; // K^ = k e^{G_C - G}, channel-major
   bf16 vt[VD * TS];                    // V, channel-major (exact)
   bf16 tb_h[CH * TS], tb_l[CH * TS];   // T diag(beta), [i][j]
@@ -193,7 +190,7 @@ struct ChunkSmem {
   float an[CH * FS];                   // an[i][j] = A[i][j]
   float tt[CH * FS];                   // tt[c][i] = T[i][c] (diagonal blocks)
   float tn[CH * FS];                   // tn[i][c] = T[i][c] (diagonal blocks)
-  float xt[16 * 17];                   // X = A10 T00, stored xt[c][i]
+  float xt[16 * XS];                   // X = A10 T00, stored xt[c][i]
   float tot[8 * KD];                   // per 4-token group gate sums
   float ea[KD];                        // e^{a}
   float gam[KD];                       // e^{G_C}
@@ -235,6 +232,16 @@ __device__ __forceinline__ Work decode_work(const ChunkParams& p, int32_t flags,
 // segment) of one head, chunk after chunk, holding the state in registers.
 // Eight waves; wave w owns state columns [16w, 16w + 16) as eight 16 x 16 FP32
 // accumulator tiles.
+//
+// Per chunk:
+//   P0  (all)      load (prefetched one chunk ahead), gate prefix, Kr, Kc, Qr
+//                  (token-major) and K^, V (channel-major) into LDS
+//   P1  (waves 0-3) A = beta o (Kr Kc^T) and P = Qr Kc^T, 16 x 16 tiles
+//   P2  wave 0 lanes 0-31: diagonal 16 x 16 blocks of T = (I + A)^{-1};
+//       every other wave meanwhile: Y = Kr (e^a o S) and O = Qr (e^a o S)
+//   P2b wave 5: off-diagonal block of T and T diag(beta); wave 0: its Y, O
+//   P3  (all)      U = T diag(beta) (V - Y), O += P U, S <- e^{G_C} o S + K^^T U
+// using W S = T diag(beta) (K o e^G) S, K o e^G = e^a o Kr, Q o e^G = e^a o Qr.
 __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ ChunkSmem sm;
   const int f = blockIdx.x;
@@ -244,8 +251,6 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   // buffer resources live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int ln = lane & 31;   // 32x32x16 MFMA: row/column index of this lane
-  const int lh = lane >> 5;   // 32x32x16 MFMA: k-group of this lane
   const int lm = lane & 15;   // 16x16x32 MFMA: row/column index of this lane
   const int lg = lane >> 4;   // 16x16x32 MFMA: k-group / row group of this lane
   const int H = p.H;
@@ -300,43 +305,35 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   // raw BF16 pairs of the chunk being prefetched (registers, one chunk ahead);
   // buffer loads past the fragment's last token return zero
   uint32_t rk[4], rg[4], rq[4], rv[4];
-  float rb = 0.f;
+  uint32_t rb = 0u;   // beta's raw bits: converted only when used, so that no
+                      // wait on the prefetch is forced inside fetch()
+  // Branch-free, so that the loads and the use of the previous chunk's
+  // registers share one basic block: loads a mode does not need, and loads
+  // past the fragment, get a zero-size buffer (they return zero and touch no
+  // memory).
   auto fetch = [&](int cs) {
     const int nn = min(CH, end - cs);
-    const size_t base = (static_cast<size_t>(cs) * H + h) * KD;
-    const int nrec = (nn - 1) * row_bytes + KD * 2;
+    const size_t base = (static_cast<size_t>(min(cs, end - 1)) * H + h) * KD;
+    const int nrec = nn > 0 ? (nn - 1) * row_bytes + KD * 2 : 0;
     const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + base), 0, nrec, kBufDword3);
     const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.g + base), 0, nrec, kBufDword3);
+    const auto rsq =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, fwd ? nrec : 0, kBufDword3);
+    const auto rsv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, use_v ? nrec : 0, kBufDword3);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int off = in_voff + m * row_bytes;
       rk[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsk, off, 0, 0));
       rg[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsg, off, 0, 0));
+      rq[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsq, off, 0, 0));
+      rv[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsv, off, 0, 0));
     }
-    if (fwd) {
-      const auto rsq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, nrec, kBufDword3);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        rq[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsq, in_voff + m * row_bytes, 0, 0));
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) rq[m] = 0u;
-    }
-    if (use_v) {
-      const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, nrec, kBufDword3);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        rv[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsv, in_voff + m * row_bytes, 0, 0));
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) rv[m] = 0u;
-    }
-    if (tg == 0 && lane < CH) {
-      const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(p.beta + static_cast<size_t>(cs) * H + h), 0, (nn - 1) * H * 2 + 2, kBufDword3);
-      const uint32_t bb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane * H * 2, 0, 0));
-      rb = __uint_as_float(bb << 16);
-    }
+    // beta: wave 0's first 32 lanes read one value per token
+    const int nb = (tg == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
+    const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.beta + static_cast<size_t>(min(cs, end - 1)) * H + h), 0, nb, kBufDword3);
+    rb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane < CH ? lane * H * 2 : nb, 0, 0));
   };
   fetch(beg);
 
@@ -356,8 +353,13 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
       G[m][1] = __uint_as_float(rg[m] & 0xffff0000u) * kLog2e;
       vcur[m] = rv[m];
     }
-    if (tg == 0 && lane < CH) sm.beta[lane] = rb;
-    if (c0 + CH < end) fetch(c0 + CH);
+    if (tg == 0 && lane < CH) sm.beta[lane] = __uint_as_float(rb << 16);
+    // Consume the prefetched registers before the next prefetch is issued: the
+    // q/v/beta loads are conditional, so if the scheduler hoisted the new loads
+    // above these uses, the inserted memory wait would have to cover the
+    // shortest load path and stall on the new loads.
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(c0 + CH);
 #pragma unroll
     for (int m = 1; m < 4; ++m) {
       G[m][0] += G[m - 1][0];
@@ -378,20 +380,20 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
       gc[1] += tv.y;
     }
     const float shift[2] = {pre[0] - a[0], pre[1] - a[1]};
-    const float ea[2] = {__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1])};
     const float ega[2] = {__builtin_amdgcn_exp2f(gc[0] - a[0]), __builtin_amdgcn_exp2f(gc[1] - a[1])};
     if (tg == 0) {
-      *reinterpret_cast<float2*>(&sm.ea[2 * cp]) = make_float2(ea[0], ea[1]);
+      *reinterpret_cast<float2*>(&sm.ea[2 * cp]) =
+          make_float2(__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1]));
       *reinterpret_cast<float2*>(&sm.gam[2 * cp]) =
           make_float2(__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]));
     }
 
-    // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, K^ = Kc e^{G_C-a}, Qr, Qg = q e^G
-    uint32_t krh[4], krl[4], khh[2][2], khl[2][2];
+    // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, K^ = Kc e^{G_C-a}, Qr = q e^{G-a}
+    uint32_t khh[2][2], khl[2][2];
     float kh_prev[2] = {0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      float kr[2], kc[2], kh[2], qr[2], qg[2];
+      float kr[2], kc[2], kh[2], qr[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const float x = G[m][c] + shift[c];
@@ -401,13 +403,12 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         kc[c] = kf[m][c] * ec;
         kh[c] = kc[c] * ega[c];
         qr[c] = qf[m][c] * er;
-        qg[c] = qr[c] * ea[c];
       }
       const int i = 4 * tg + m;
       uint32_t hh, ll;
-      split_pair(kr[0], kr[1], krh[m], krl[m]);
-      *reinterpret_cast<uint32_t*>(&sm.kr_h[i * NS + 2 * cp]) = krh[m];
-      *reinterpret_cast<uint32_t*>(&sm.kr_l[i * NS + 2 * cp]) = krl[m];
+      split_pair(kr[0], kr[1], hh, ll);
+      *reinterpret_cast<uint32_t*>(&sm.kr_h[i * NS + 2 * cp]) = hh;
+      *reinterpret_cast<uint32_t*>(&sm.kr_l[i * NS + 2 * cp]) = ll;
       split_pair(kc[0], kc[1], hh, ll);
       *reinterpret_cast<uint32_t*>(&sm.kc_h[i * NS + 2 * cp]) = hh;
       *reinterpret_cast<uint32_t*>(&sm.kc_l[i * NS + 2 * cp]) = ll;
@@ -415,9 +416,6 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         split_pair(qr[0], qr[1], hh, ll);
         *reinterpret_cast<uint32_t*>(&sm.qr_h[i * NS + 2 * cp]) = hh;
         *reinterpret_cast<uint32_t*>(&sm.qr_l[i * NS + 2 * cp]) = ll;
-        split_pair(qg[0], qg[1], hh, ll);
-        *reinterpret_cast<uint32_t*>(&sm.qg_h[i * NS + 2 * cp]) = hh;
-        *reinterpret_cast<uint32_t*>(&sm.qg_l[i * NS + 2 * cp]) = ll;
       }
       // K^ packed along tokens (channel-major layout): pairs (m-1, m)
       if (m & 1) {
@@ -433,10 +431,6 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     for (int c = 0; c < 2; ++c) {
       const int d = 2 * cp + c;
       const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;  // low / high halves
-      *reinterpret_cast<uint2*>(&sm.krt_h[d * TS + 4 * tg]) =
-          make_uint2(__builtin_amdgcn_perm(krh[1], krh[0], sel), __builtin_amdgcn_perm(krh[3], krh[2], sel));
-      *reinterpret_cast<uint2*>(&sm.krt_l[d * TS + 4 * tg]) =
-          make_uint2(__builtin_amdgcn_perm(krl[1], krl[0], sel), __builtin_amdgcn_perm(krl[3], krl[2], sel));
       *reinterpret_cast<uint2*>(&sm.kht_h[d * TS + 4 * tg]) = make_uint2(khh[0][c], khh[1][c]);
       *reinterpret_cast<uint2*>(&sm.kht_l[d * TS + 4 * tg]) = make_uint2(khl[0][c], khl[1][c]);
       if (use_v) {
@@ -446,43 +440,50 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     }
     __syncthreads();
 
-    // ================= P1: A = beta (Kr Kc^T) (wave 0) and P = Qr Kc^T (wave 1)
-    if (wave == 0 || (wave == 1 && fwd)) {
-      const bf16* xh = wave == 0 ? sm.kr_h : sm.qr_h;
-      const bf16* xl = wave == 0 ? sm.kr_l : sm.qr_l;
-      f32x16 acc = zero16();
+    // ================= P1: A (waves 0, 1) and P (waves 2, 3) by 16-row blocks
+    // (the all-zero block above the diagonal is not computed)
+    if (wave < 2 || (wave < 4 && fwd)) {
+      const int rb = wave & 1;                  // row block: rows 16rb .. 16rb+15
+      const bool is_a = wave < 2;
+      const bf16* xh = is_a ? sm.kr_h : sm.qr_h;
+      const bf16* xl = is_a ? sm.kr_l : sm.qr_l;
+      f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        const int off = ln * NS + 16 * kk + 8 * lh;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&xh[off]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&xl[off]);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&sm.kc_h[off]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&sm.kc_l[off]);
-        acc = mfma3(ah, al, bh, bl, acc);
+      for (int kk = 0; kk < KD / 32; ++kk) {
+        const int aoff = (16 * rb + lm) * NS + 32 * kk + 8 * lg;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&xh[aoff]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&xl[aoff]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          if (ct > rb) continue;
+          const int boff = (16 * ct + lm) * NS + 32 * kk + 8 * lg;
+          acc[ct] = mfma16x3(ah, al, *reinterpret_cast<const bf16x8*>(&sm.kc_h[boff]),
+                             *reinterpret_cast<const bf16x8*>(&sm.kc_l[boff]), acc[ct]);
+        }
       }
-      // lane holds rows i = 8r + 4lh + e of column j = ln
-      const int j = ln;
-      if (wave == 0) {
+      mfma_result_fence(acc[0], acc[1]);
+      // tile ct holds rows i = 16rb + 4lg + e of column j = 16ct + lm
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+      for (int ct = 0; ct < 2; ++ct) {
+        const int j = 16 * ct + lm;
+        const int i0 = 16 * rb + 4 * lg;
+        if (is_a) {
+          if (ct > rb) continue;
           float4 v4;
           float* vp = reinterpret_cast<float*>(&v4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 8 * r + 4 * lh + e;
-            const float x = (j < i) ? sm.beta[i] * acc[4 * r + e] : 0.f;
+            const int i = i0 + e;
+            const float x = (j < i) ? sm.beta[i] * acc[ct][e] : 0.f;
             vp[e] = x;
             sm.an[i * FS + j] = x;
           }
-          *reinterpret_cast<float4*>(&sm.at[j * FS + 8 * r + 4 * lh]) = v4;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<float4*>(&sm.at[j * FS + i0]) = v4;
+        } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 8 * r + 4 * lh + e;
-            const float x = (j <= i) ? acc[4 * r + e] : 0.f;
+            const int i = i0 + e;
+            const float x = (ct <= rb && j <= i) ? acc[ct][e] : 0.f;
             bf16 hh, ll;
             split(x, hh, ll);
             sm.p_h[i * TS + j] = hh;
@@ -493,122 +494,171 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     }
     __syncthreads();
 
-    // ================= P2: T = (I + A)^{-1} by 16 x 16 blocks
-    if (wave == 0 && lane < 32) {
-      const int b = lane >> 4;   // diagonal block
-      const int c = lane & 15;   // column of the block solved by this lane
-      const int base = 16 * b;
-      float x[16];
+    // Y = Kr (e^a o S) and O = Qr (e^a o S), this wave's 16 columns; the
+    // state is scaled and split into B operands one 32-row k-step at a time
+    f32x4 Y[2] = {zero4(), zero4()};
+    f32x4 O[2] = {zero4(), zero4()};
+    auto state_products = [&]() {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+      for (int kk = 0; kk < KD / 32; ++kk) {
+        float x[8];
+        tiles16_to_b(S[2 * kk], S[2 * kk + 1], x);
+        const float4 e0 = *reinterpret_cast<const float4*>(&sm.ea[32 * kk + 8 * lg]);
+        const float4 e1 = *reinterpret_cast<const float4*>(&sm.ea[32 * kk + 8 * lg + 4]);
+        x[0] *= e0.x; x[1] *= e0.y; x[2] *= e0.z; x[3] *= e0.w;
+        x[4] *= e1.x; x[5] *= e1.y; x[6] *= e1.z; x[7] *= e1.w;
+        bf16x8 sbh, sbl;
+        split8(x, sbh, sbl);
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float* arow = &sm.at[(base + jj) * FS + base];
-#pragma unroll
-        for (int q4 = jj / 4; q4 < 4; ++q4) {
-          const float4 t4 = *reinterpret_cast<const float4*>(&arow[4 * q4]);
-          const float av[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q4 + e;
-            if (i > jj) x[i] -= av[e] * x[jj];
+        for (int rt = 0; rt < 2; ++rt) {
+          const int off = (16 * rt + lm) * NS + 32 * kk + 8 * lg;
+          Y[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
+                           *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, Y[rt]);
+          if (fwd) {
+            O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.qr_h[off]),
+                             *reinterpret_cast<const bf16x8*>(&sm.qr_l[off]), sbh, sbl, O[rt]);
           }
         }
       }
+    };
+
+    // ================= P2: diagonal blocks of T (wave 0), state products (rest)
+    if (wave == 0) {
+      if (lane < 32) {
+        const int b = lane >> 4;   // diagonal block
+        const int c = lane & 15;   // column of the block solved by this lane
+        const int base = 16 * b;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const float* arow = &sm.at[(base + jj) * FS + base];
+#pragma unroll
+          for (int q4 = jj / 4; q4 < 4; ++q4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(&arow[4 * q4]);
+            const float av[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * q4 + e;
+              if (i > jj) x[i] -= av[e] * x[jj];
+            }
+          }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          *reinterpret_cast<float4*>(&sm.tt[(base + c) * FS + base + 4 * q4]) =
+              make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
+      }
+    } else {
+      state_products();
+    }
+    __syncthreads();
+
+    // ================= P2b: T10 = -T11 A10 T00 and T diag(beta) (wave 5);
+    // wave 0's state products meanwhile.  Wave 5 exchanges X through LDS with
+    // itself only, and a wave's LDS accesses complete in order, so no barrier
+    // is needed between writing X and reading it back.
+    if (wave == 5) {
+      // lane: column tc of the block, rows ti = 4qq + (lane / 16), qq = 0..3.
+      // Every operand row is loaded whole with independent 16-byte reads.
+      const int tc = lane & 15;
+      const int tr = lane >> 4;
+      float tcol[16];   // T00[:, tc] (row tc of tt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        *reinterpret_cast<float4*>(&sm.tt[(base + c) * FS + base + 4 * q4]) =
-            make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+        const float4 v4 = *reinterpret_cast<const float4*>(&sm.tt[tc * FS + 4 * q4]);
+        tcol[4 * q4] = v4.x; tcol[4 * q4 + 1] = v4.y; tcol[4 * q4 + 2] = v4.z; tcol[4 * q4 + 3] = v4.w;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
-    }
-    __syncthreads();
-    const int ti = (tid >> 4) & 15;   // row within a 16 x 16 block
-    const int tc = tid & 15;          // column within a 16 x 16 block
-    if (tid < 256) {
-      float xs = 0.f;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int ti = 4 * qq + tr;
+        float arow[16];   // A10[ti, :]
 #pragma unroll
-      for (int kx = 0; kx < 16; ++kx) xs += sm.an[(16 + ti) * FS + kx] * sm.tt[tc * FS + kx];
-      sm.xt[tc * 17 + ti] = xs;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      float t10 = 0.f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&sm.an[(16 + ti) * FS + 4 * q4]);
+          arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
+        }
+        float xs = 0.f;
 #pragma unroll
-      for (int kx = 0; kx < 16; ++kx) t10 -= sm.tn[(16 + ti) * FS + 16 + kx] * sm.xt[tc * 17 + kx];
+        for (int kx = 0; kx < 16; ++kx) xs += arow[kx] * tcol[kx];
+        sm.xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
+      }
+      // the wave's own LDS writes complete in order before its later reads
+      float xcol[16];   // X[:, tc]
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&sm.xt[tc * XS + 4 * q4]);
+        xcol[4 * q4] = v4.x; xcol[4 * q4 + 1] = v4.y; xcol[4 * q4 + 2] = v4.z; xcol[4 * q4 + 3] = v4.w;
+      }
       const float b0 = sm.beta[tc];
       const float b1 = sm.beta[16 + tc];
-      bf16 hh, ll;
-      split(sm.tn[ti * FS + tc] * b0, hh, ll);
-      sm.tb_h[ti * TS + tc] = hh;
-      sm.tb_l[ti * TS + tc] = ll;
-      split(sm.tn[(16 + ti) * FS + 16 + tc] * b1, hh, ll);
-      sm.tb_h[(16 + ti) * TS + 16 + tc] = hh;
-      sm.tb_l[(16 + ti) * TS + 16 + tc] = ll;
-      split(t10 * b0, hh, ll);
-      sm.tb_h[(16 + ti) * TS + tc] = hh;
-      sm.tb_l[(16 + ti) * TS + tc] = ll;
-      sm.tb_h[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
-      sm.tb_l[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
-    }
-    __syncthreads();
-
-    // ================= P3: -W (token-major, into kr_*; waves 0-3) and
-    // U~ = T diag(beta) V (every wave, its own 16 columns)
-    if (wave < 4) {
-      f32x16 acc = zero16();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int aoff = (32 * wave + ln) * TS + 16 * s + 8 * lh;
-        const int boff = ln * TS + 16 * s + 8 * lh;
-        acc = mfma3(*reinterpret_cast<const bf16x8*>(&sm.krt_h[aoff]),
-                    *reinterpret_cast<const bf16x8*>(&sm.krt_l[aoff]),
-                    *reinterpret_cast<const bf16x8*>(&sm.tb_h[boff]),
-                    *reinterpret_cast<const bf16x8*>(&sm.tb_l[boff]), acc);
-      }
-      // acc: W^T rows d = 32 wave + 8r + 4lh + e, column i = ln
+      for (int qq = 0; qq < 4; ++qq) {
+        const int ti = 4 * qq + tr;
+        float trow[16];   // T11[ti, :]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * wave + 8 * r + 4 * lh;
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.ea[d0]);
-        uint32_t h01, l01, h23, l23;
-        split_pair(-e4.x * acc[4 * r + 0], -e4.y * acc[4 * r + 1], h01, l01);
-        split_pair(-e4.z * acc[4 * r + 2], -e4.w * acc[4 * r + 3], h23, l23);
-        *reinterpret_cast<uint2*>(&sm.kr_h[ln * NS + d0]) = make_uint2(h01, h23);
-        *reinterpret_cast<uint2*>(&sm.kr_l[ln * NS + d0]) = make_uint2(l01, l23);
-      }
-    }
-    f32x4 U[2] = {zero4(), zero4()};
-    if (use_v) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[col * TS + 8 * lg]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int aoff = (16 * rt + lm) * TS + 8 * lg;
-        U[rt] = mfma16(*reinterpret_cast<const bf16x8*>(&sm.tb_h[aoff]), bv, U[rt]);
-        U[rt] = mfma16(*reinterpret_cast<const bf16x8*>(&sm.tb_l[aoff]), bv, U[rt]);
-      }
-    }
-    __syncthreads();
-
-    // ================= P4: U -= W S, O = Qg S + P U, S <- e^{G_C} S + K^^T U
-    // The state's rows are split into B operands one 32-row k-step at a time.
-    f32x4 O[2] = {zero4(), zero4()};
-#pragma unroll
-    for (int kk = 0; kk < KD / 32; ++kk) {
-      float x[8];
-      tiles16_to_b(S[2 * kk], S[2 * kk + 1], x);
-      bf16x8 sbh, sbl;
-      split8(x, sbh, sbl);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int off = (16 * rt + lm) * NS + 32 * kk + 8 * lg;
-        U[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
-                         *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, U[rt]);
-        if (fwd) {
-          O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.qg_h[off]),
-                           *reinterpret_cast<const bf16x8*>(&sm.qg_l[off]), sbh, sbl, O[rt]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&sm.tn[(16 + ti) * FS + 16 + 4 * q4]);
+          trow[4 * q4] = v4.x; trow[4 * q4 + 1] = v4.y; trow[4 * q4 + 2] = v4.z; trow[4 * q4 + 3] = v4.w;
         }
+        float t10 = 0.f;
+#pragma unroll
+        for (int kx = 0; kx < 16; ++kx) t10 -= trow[kx] * xcol[kx];
+        bf16 hh, ll;
+        split(sm.tn[ti * FS + tc] * b0, hh, ll);
+        sm.tb_h[ti * TS + tc] = hh;
+        sm.tb_l[ti * TS + tc] = ll;
+        split(trow[tc] * b1, hh, ll);
+        sm.tb_h[(16 + ti) * TS + 16 + tc] = hh;
+        sm.tb_l[(16 + ti) * TS + 16 + tc] = ll;
+        split(t10 * b0, hh, ll);
+        sm.tb_h[(16 + ti) * TS + tc] = hh;
+        sm.tb_l[(16 + ti) * TS + tc] = ll;
+        sm.tb_h[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
+        sm.tb_l[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
+      }
+    } else if (wave == 0) {
+      state_products();
+    }
+    __syncthreads();
+
+    // ================= P3: U = T diag(beta) (V - Y), O += P U, state update
+    // Land the next chunk's prefetch here, most of a chunk after it was issued:
+    // the empty asm takes the registers as operands, so the memory wait is
+    // placed before it and none is left for the next chunk's first use.
+    asm volatile("" : "+v"(rk[0]), "+v"(rk[1]), "+v"(rk[2]), "+v"(rk[3]), "+v"(rg[0]), "+v"(rg[1]),
+                 "+v"(rg[2]), "+v"(rg[3]), "+v"(rq[0]), "+v"(rq[1]), "+v"(rq[2]), "+v"(rq[3]),
+                 "+v"(rv[0]), "+v"(rv[1]), "+v"(rv[2]), "+v"(rv[3]), "+v"(rb));
+    f32x4 U[2] = {zero4(), zero4()};
+    {
+      f32x4 D[2];
+      mfma_result_fence(Y[0], Y[1]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        float vv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (use_v) {
+          const uint2 v2 = *reinterpret_cast<const uint2*>(&sm.vt[col * TS + 16 * rt + 4 * lg]);
+          vv[0] = __uint_as_float(v2.x << 16);
+          vv[1] = __uint_as_float(v2.x & 0xffff0000u);
+          vv[2] = __uint_as_float(v2.y << 16);
+          vv[3] = __uint_as_float(v2.y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[rt][e] = vv[e] - Y[rt][e];
+      }
+      float x[8];
+      tiles16_to_b(D[0], D[1], x);
+      bf16x8 dbh, dbl;
+      split8(x, dbh, dbl);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int off = (16 * rt + lm) * TS + 8 * lg;
+        U[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]),
+                         *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]), dbh, dbl, U[rt]);
       }
     }
     bf16x8 ubh, ubl;
@@ -627,6 +677,10 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
         const int off = (16 * rt + lm) * TS + 8 * lg;
         O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]),
                          *reinterpret_cast<const bf16x8*>(&sm.p_l[off]), ubh, ubl, O[rt]);
+      }
+      mfma_result_fence(O[0], O[1]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // (an element of an ext_vector goes through a scalar first:
@@ -648,8 +702,10 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
       S[dt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kht_h[off]),
                        *reinterpret_cast<const bf16x8*>(&sm.kht_l[off]), ubh, ubl, S[dt]);
     }
-    // no barrier here: the next chunk writes only tot and beta before its first
-    // barrier, and P4 reads neither
+    // The next chunk's first barrier orders its LDS writes after every read
+    // of this chunk: before that barrier it writes only tot and beta, which
+    // P3 does not read.  The state tiles are read next at least a P0 and two
+    // barriers later, far past the MFMA result latency.
   }
 
   // ---- the fragment's final state
@@ -664,6 +720,8 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     if (p.pass == 1 && (flags & kFragSegLast))
       dst1 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
   }
+#pragma unroll
+  for (int dt = 0; dt < 8; dt += 2) mfma_result_fence(S[dt], S[dt + 1]);
   if (dst0) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
