@@ -96,7 +96,7 @@ def compose_work(S, H, live_count):
     return {"macs": macs, "mfma_macs": 3 * macs, "bytes": bytes_}
 
 
-def cpu_baseline(x, w, heads=4, tokens=12288):
+def cpu_baseline(x, w, heads=8, tokens=16384):
     """The fp64 oracle on a bounded sample: `heads` heads x the first `tokens`
     tokens, with the workload's segment length; full method (recurrence,
     updates, transitions, composition)."""
@@ -132,15 +132,70 @@ def cpu_baseline(x, w, heads=4, tokens=12288):
 def traffic_from_profile():
     """HBM bytes per chunk-kernel launch from the committed PMC summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "chunk_kernel_t65536_h32_s64_traffic.json")
-    src = os.path.join(ROOT, "gated_delta_rule_37_amd", "csrc", "kda_kernels.hip")
+    path = TRAFFIC_JSON
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if rec.get("kernel_source_sha256") != digest:
         return None
     return rec.get("bytes_per_launch")
+
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "chunk_kernel_t65536_h32_s64_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_37_amd", "csrc", "kda_kernels.hip")
+
+
+def _pmc_per_dispatch(csv_path, counter, name_part):
+    """Per-dispatch values of one counter for kernels whose name contains name_part."""
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+            continue
+        vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=int)]
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """HBM bytes per chunk-kernel launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for a plain
+    device copy of copy_bytes (FETCH reads and WRITE writes copy_bytes once)."""
+    cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copy")
+    cw = _pmc_per_dispatch(copy_write_csv, "WRITE_SIZE", "copy")
+    big_f = max(cf)
+    big_w = max(cw)
+    f_scale = copy_bytes / (big_f * 1024.0)
+    w_scale = copy_bytes / (big_w * 1024.0)
+    kf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", "kda_chunk_kernel")
+    kw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", "kda_chunk_kernel")
+    fetch_b = sum(kf) / len(kf) * 1024.0 * f_scale
+    write_b = sum(kw) / len(kw) * 1024.0 * w_scale
+    rec = {
+        "kernel": "kda_chunk_kernel",
+        "workload": "t65536_h32_s64",
+        "bytes_per_launch": round(fetch_b + write_b),
+        "fetch_bytes_per_launch": round(fetch_b),
+        "write_bytes_per_launch": round(write_b),
+        "launches_averaged": len(kf),
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": big_f, "write_kib": big_w,
+                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+    }
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of nbytes, run three times (PMC calibration)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes}))
 
 
 def main():
@@ -150,9 +205,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t65536_h32_s64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
-    ap.add_argument("--cpu-tokens", type=int, default=12288)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (PMC calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
+                    help="fetch.csv write.csv copy_fetch.csv copy_write.csv from rocprofv3 --pmc runs")
+    ap.add_argument("--copy-bytes-used", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.copy_bytes_used)
+        return
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -228,23 +228,14 @@ __device__ __forceinline__ Work decode_work(const ChunkParams& p, int32_t flags,
 
 }  // namespace
 
-// One workgroup runs one fragment (a run of tokens of one sequence inside one
-// segment) of one head, chunk after chunk, holding the state in registers.
-// Eight waves; wave w owns state columns [16w, 16w + 16) as eight 16 x 16 FP32
-// accumulator tiles.
-//
-// Per chunk:
-//   P0  (all)      load (prefetched one chunk ahead), gate prefix, Kr, Kc, Qr
-//                  (token-major) and K^, V (channel-major) into LDS
-//   P1  (waves 0-3) A = beta o (Kr Kc^T) and P = Qr Kc^T, 16 x 16 tiles
-//   P2  wave 0 lanes 0-31: diagonal 16 x 16 blocks of T = (I + A)^{-1};
-//       every other wave meanwhile: Y = Kr (e^a o S) and O = Qr (e^a o S)
-//   P2b wave 5: off-diagonal block of T and T diag(beta); wave 0: its Y, O
-//   P3  (all)      U = T diag(beta) (V - Y), O += P U, S <- e^{G_C} o S + K^^T U
-// using W S = T diag(beta) (K o e^G) S, K o e^G = e^a o Kr, Q o e^G = e^a o Qr.
-__global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
-  __shared__ ChunkSmem sm;
-  const int f = blockIdx.x;
+// The body for one fragment, specialised on the mode so that the unrolled
+// chunk loop carries no mode branches (branches would split it into many
+// basic blocks and keep the scheduler from running operand loads ahead).
+template <int MODE>
+__device__ __forceinline__ void run_fragment(const ChunkParams& p, ChunkSmem& sm, const int f,
+                                             const int32_t flags, const int32_t seg,
+                                             const int32_t seq, const int32_t beg,
+                                             const int32_t end, const bool from_carry) {
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   // wave index, made provably uniform so that wave-derived addresses and
@@ -254,24 +245,9 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   const int lm = lane & 15;   // 16x16x32 MFMA: row/column index of this lane
   const int lg = lane >> 4;   // 16x16x32 MFMA: k-group / row group of this lane
   const int H = p.H;
-
-  const int32_t flags = p.plan[p.L.frag_flags + f];
-  const int32_t seg = p.plan[p.L.frag_seg + f];
-  const int32_t seq = p.plan[p.L.frag_seq + f];
-  const int32_t beg = p.plan[p.L.frag_begin + f];
-  const int32_t end = p.plan[p.L.frag_end + f];
-  const Work work = decode_work(p, flags, seg);
-
-  if (work.zero_a) {
-    float4* dst = reinterpret_cast<float4*>(p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD);
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = tid; i < KD * KD / 4; i += NT) dst[i] = z;
-    return;
-  }
-  if (work.mode < 0) return;
-  const int mode = work.mode;
-  const bool fwd = mode == kModeFwd;
-  const bool use_v = mode != kModeSumPhi;
+  constexpr int mode = MODE;
+  constexpr bool fwd = MODE == kModeFwd;
+  constexpr bool use_v = MODE != kModeSumPhi;
   const int col = 16 * wave + lm;
 
   // ---- initial state: tile dt, register e holds row 16dt + 4lg + e
@@ -284,7 +260,7 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[dt][e] = (16 * dt + 4 * lg + e == col) ? 1.f : 0.f;
     }
-  } else if (work.from_carry) {
+  } else if (from_carry) {
     const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -733,6 +709,50 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst1[(16 * dt + 4 * lg + e) * VD + col] = S[dt][e];
+  }
+}
+
+
+// One workgroup runs one fragment (a run of tokens of one sequence inside one
+// segment) of one head, chunk after chunk, holding the state in registers.
+// Eight waves; wave w owns state columns [16w, 16w + 16) as eight 16 x 16 FP32
+// accumulator tiles.
+//
+// Per chunk:
+//   P0  (all)      load (prefetched one chunk ahead), gate prefix, Kr, Kc, Qr
+//                  (token-major) and K^, V (channel-major) into LDS
+//   P1  (waves 0-3) A = beta o (Kr Kc^T) and P = Qr Kc^T, 16 x 16 tiles
+//   P2  wave 0 lanes 0-31: diagonal 16 x 16 blocks of T = (I + A)^{-1};
+//       every other wave meanwhile: Y = Kr (e^a o S) and O = Qr (e^a o S)
+//   P2b wave 5: off-diagonal block of T and T diag(beta); wave 0: its Y, O
+//   P3  (all)      U = T diag(beta) (V - Y), O += P U, S <- e^{G_C} o S + K^^T U
+// using W S = T diag(beta) (K o e^G) S, K o e^G = e^a o Kr, Q o e^G = e^a o Qr.
+__global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
+  __shared__ ChunkSmem sm;
+  const int f = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int H = p.H;
+
+  const int32_t flags = p.plan[p.L.frag_flags + f];
+  const int32_t seg = p.plan[p.L.frag_seg + f];
+  const int32_t seq = p.plan[p.L.frag_seq + f];
+  const int32_t beg = p.plan[p.L.frag_begin + f];
+  const int32_t end = p.plan[p.L.frag_end + f];
+  const Work work = decode_work(p, flags, seg);
+
+  if (work.zero_a) {
+    float4* dst = reinterpret_cast<float4*>(p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = tid; i < KD * KD / 4; i += NT) dst[i] = z;
+    return;
+  }
+  if (work.mode == kModeFwd) {
+    run_fragment<kModeFwd>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
+  } else if (work.mode == kModeSumS) {
+    run_fragment<kModeSumS>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
+  } else if (work.mode == kModeSumPhi) {
+    run_fragment<kModeSumPhi>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
   }
 }
 
