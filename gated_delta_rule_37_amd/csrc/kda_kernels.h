@@ -11,7 +11,7 @@
 
 namespace kda {
 
-constexpr int kChunkThreads = 512;    // kda_chunk_kernel workgroup size
+constexpr int kChunkThreads = 512;    // kda_chunk_kernel workgroup size (8 waves)
 constexpr int kComposeThreads = 256;  // kda_compose_kernel workgroup size
 constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
 

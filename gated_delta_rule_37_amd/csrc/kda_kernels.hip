@@ -45,7 +45,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
 constexpr int CH = 32;    // chunk length (tokens)
-constexpr int NT = kChunkThreads;     // chunk kernel: 8 waves of 64
+constexpr int NT = kChunkThreads;     // chunk kernel: owner and helper waves
+constexpr int NOWN = 4;               // owner waves: the state, 32 columns each
+constexpr int NHELP = 4;              // helper waves: the next chunk's operands
+static_assert(NHELP * 32 == KD, "each helper covers 32 channels in the chunk prologue");
+static_assert((NOWN + NHELP) * 64 == NT, "chunk kernel wave roles");
+constexpr int KSPLIT = 4;             // owner k-steps before the T merge barrier
 constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 136;   // row stride (bf16) of token-major [32][128] tiles
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
@@ -81,6 +86,13 @@ __device__ __forceinline__ f32x16 mfma3(const bf16x8& ah, const bf16x8& al, cons
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS accesses through native vector types (HIP's float4/uint4
+// structs are split into pairs of 8-byte accesses)
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, const f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st4(bf16* p, const u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -178,22 +190,23 @@ __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo)
   }
 }
 
+// Shared memory of one workgroup (about 115 KB).  Helpers write the operands
+// of chunk n while owners still use chunk n-1's: Kc and V, which owners read in
+// the same step as helpers write the next chunk's, are double-buffered; every
+// other buffer is written only after its last reader of the previous chunk has
+// passed a barrier.
 struct ChunkSmem {
-  bf16 kr_h[CH * NS], kr_l[CH * NS];   // Kr = k e^{G-a}, token-major
-  bf16 kc_h[CH * NS], kc_l[CH * NS];   // Kc = k e^{a-G}, token-major
-  bf16 qr_h[CH * NS], qr_l[CH * NS];   // Qr = q e^{G-a}, token-major
-  bf16 kht_h[KD * TS], kht_l[KD * TS]; // K^ = k e^{G_C - G}, channel-major
-  bf16 vt[VD * TS];                    // V, channel-major (exact)
-  bf16 tb_h[CH * TS], tb_l[CH * TS];   // T diag(beta), [i][j]
-  bf16 p_h[CH * TS], p_l[CH * TS];     // P, [i][j]
-  float at[CH * FS];                   // at[j][i] = A[i][j]
-  float an[CH * FS];                   // an[i][j] = A[i][j]
-  float tt[CH * FS];                   // tt[c][i] = T[i][c] (diagonal blocks)
-  float tn[CH * FS];                   // tn[i][c] = T[i][c] (diagonal blocks)
-  float xt[16 * XS];                   // X = A10 T00, stored xt[c][i]
-  float tot[8 * KD];                   // per 4-token group gate sums
-  float ea[KD];                        // e^{a}
-  float gam[KD];                       // e^{G_C}
+  bf16 kr_h[CH * NS], kr_l[CH * NS];          // Kr = k e^{G-a}, token-major
+  bf16 qr_h[CH * NS], qr_l[CH * NS];          // Qr = q e^{G-a}, token-major
+  bf16 kc_h[2][CH * NS], kc_l[2][CH * NS];    // Kc = k e^{a-G}, token-major
+  bf16 vv[2][CH * NS];                        // V, token-major (exact)
+  bf16 tb_h[CH * TS], tb_l[CH * TS];          // T diag(beta), [i][j]
+  bf16 p_h[CH * TS], p_l[CH * TS];            // P, [i][j]
+  float an[CH * FS];                          // an[i][j] = A[i][j], j < i
+  float tt[CH * FS];                          // tt[c][i] = T[i][c] (diagonal blocks)
+  float tn[CH * FS];                          // tn[i][c] = T[i][c] (diagonal blocks)
+  float xt[16 * XS];                          // X = A10 T00, stored xt[c][i]
+  float fac[KD];                              // state rescale between two chunks
   float beta[CH];
 };
 
@@ -226,67 +239,314 @@ __device__ __forceinline__ Work decode_work(const ChunkParams& p, int32_t flags,
   return w;
 }
 
+// Returns x unchanged, but the compiler cannot see through it: lane indices
+// taken through it at each step make the step recompute its LDS addresses
+// (one add each) instead of keeping dozens of them live across the chunk loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Workgroup barrier for the two wave roles.  Owners and helpers run separate
+// loops (so that neither holds the other's registers), and both execute the
+// same sequence of barriers: s_barrier counts arriving waves, wherever they
+// are in the program.
+__device__ __forceinline__ void block_sync() { __syncthreads(); }
+
+// Orders a wave's own LDS writes before its later reads of other lanes'
+// values (LDS accesses of one wave complete in program order; this keeps the
+// compiler from moving the reads up).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// 32 x 32 accumulator tile -> B operands (hi, lo) of its two 16-row k-blocks.
+__device__ __forceinline__ void tile_to_b_split(const f32x16& t, bf16x8 bh[2], bf16x8 bl[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float x[8];
+    tile_rows_to_b(t, s, x);
+    split8(x, bh[s], bl[s]);
+  }
+}
+
 }  // namespace
 
-// The body for one fragment, specialised on the mode so that the unrolled
-// chunk loop carries no mode branches (branches would split it into many
-// basic blocks and keep the scheduler from running operand loads ahead).
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte chunks addressed by lanes
+// i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (checked on gfx950).  Pointing lane s at
+// row r0 + s/4, columns c0 + 4(s%4) of a row-major bf16 matrix therefore gives
+// lane i the column c0 + i, rows r0 .. r0+3: a column fragment of a matrix
+// stored by rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ s16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
+}
+__device__ __forceinline__ bf16x8 join8(const s16x4 a, const s16x4 b) {
+  const s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Owner waves (0 .. NOWN-1): wave w keeps the state columns [32w, 32w + 32) as
+// four 32 x 32 FP32 accumulator tiles R[dt] (rows 32dt + 8r + 4(l/32) + e in
+// lane l, register 4r + e; column 32w + l%32).  R is the state scaled by the
+// anchor of the chunk it enters, e^{a} o S, which is the operand Kr and Qr
+// multiply; one update is
+//     S_new = Diag(e^{G_C}) S + K^^T U = Diag(e^{G_C - a}) (R + Kc^T U)
+// and the helpers supply fac = e^{a_next + G_C - a} to re-anchor it for the
+// next chunk (e^{G_C - a} after the last one, which leaves S itself).
+//
+// Iteration it finishes chunk it-1 and starts chunk it:
+//   step 1  D = V - Y, U = T diag(beta) D, O += P U, store o, R += Kc^T U
+//   step 2  R *= fac; Y = Kr R, O = Qr R, first KSPLIT k-steps
+//   step 3  the remaining k-steps
 template <int MODE>
-__device__ __forceinline__ void run_fragment(const ChunkParams& p, ChunkSmem& sm, const int f,
-                                             const int32_t flags, const int32_t seg,
-                                             const int32_t seq, const int32_t beg,
-                                             const int32_t end, const bool from_carry) {
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  // wave index, made provably uniform so that wave-derived addresses and
-  // buffer resources live in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int lm = lane & 15;   // 16x16x32 MFMA: row/column index of this lane
-  const int lg = lane >> 4;   // 16x16x32 MFMA: k-group / row group of this lane
-  const int H = p.H;
-  constexpr int mode = MODE;
+__device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& sm, const int32_t flags,
+                                               const int32_t seg, const int32_t seq, const int32_t beg,
+                                               const int32_t end, const bool from_carry) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
-  const int col = 16 * wave + lm;
+  const int h = blockIdx.y;
+  const int H = p.H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  const int col = 32 * wave + ln;
+  const int nc = (end - beg + CH - 1) / CH;
+  const int o_row = H * VD * 4;   // one token of o (bytes)
 
-  // ---- initial state: tile dt, register e holds row 16dt + 4lg + e
-  f32x4 S[8];
+  f32x16 R[4];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) S[dt] = zero4();
-  if (mode == kModeSumPhi) {
+  for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
+  if (MODE == kModeSumPhi) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[dt][e] = (16 * dt + 4 * lg + e == col) ? 1.f : 0.f;
-    }
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = (32 * dt + 8 * r + 4 * lh + e == col) ? 1.f : 0.f;
   } else if (from_carry) {
     const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[dt][e] = src[(16 * dt + 4 * lg + e) * VD];
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
+  }
+
+  f32x16 Y = zero16(), O = zero16();
+
+  // A operands of k-step kk (channels 16kk .. 16kk+15): Kr and Qr, hi and lo
+  auto load_ops = [&](bf16x8 (&o)[4], const int kk, const int ln, const int lh) {
+    const int off = ln * NS + 16 * kk + 8 * lh;
+    o[0] = *reinterpret_cast<const bf16x8*>(&sm.kr_h[off]);
+    o[1] = *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]);
+    if (fwd) {
+      o[2] = *reinterpret_cast<const bf16x8*>(&sm.qr_h[off]);
+      o[3] = *reinterpret_cast<const bf16x8*>(&sm.qr_l[off]);
+    }
+  };
+  // rescale factors of the rows of tile dt held by this lane
+  auto load_fac = [&](f32x4 (&f)[4], const int dt, const int lh) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = ld4(&sm.fac[32 * dt + 8 * r + 4 * lh]);
+  };
+  auto rescale = [&](const int dt, const f32x4 (&f)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R[dt][4 * r + e] *= f[r][e];
+    }
+  };
+
+  for (int it = 0; it <= nc; ++it) {
+    // ---- step 1: finish chunk it-1
+    if (it >= 1) {
+      const int lane_s = opaque(lane);
+      const int ln = lane_s & 31;
+      const int lh = lane_s >> 5;
+      const int col = 32 * wave + ln;
+      // transposed-read coordinates: group gq of 16 lanes, source index sq
+      const int gq = lane_s >> 4;
+      const int sq = lane_s & 15;
+      const int b = (it - 1) & 1;
+      const int c0 = beg + (it - 1) * CH;
+      const int n = min(CH, end - c0);
+      mfma_result_fence(Y);
+      f32x16 D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float vv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (use_v) {
+          // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
+          const s16x4 v4 = lds_read_tr(
+              &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * wave + 16 * (gq & 1) + 4 * (sq & 3)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
+      }
+      bf16x8 dh[2], dl[2];
+      tile_to_b_split(D, dh, dl);
+      f32x16 U = zero16();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = ln * TS + 16 * s + 8 * lh;
+        U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
+                  dh[s], dl[s], U);
+      }
+      mfma_result_fence(U);
+      bf16x8 ubh[2], ubl[2];
+      tile_to_b_split(U, ubh, ubl);
+      if (fwd) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int off = ln * TS + 16 * s + 8 * lh;
+          O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
+                    ubh[s], ubl[s], O);
+        }
+      }
+      // R += Kc^T U: the A operand (row = channel 32dt + l%32, k = token
+      // 16s + 8(l/32) + 0..7) is a column fragment of the token-major Kc
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int off = (16 * s + 8 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
+          const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 4 * NS]));
+          const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 4 * NS]));
+          R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
+        }
+      }
+      if (fwd) {
+        mfma_result_fence(O);
+        // rows past the fragment's end fall outside the buffer and are dropped
+        const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
+                                                           (n - 1) * o_row + 4 * VD, kBufDword3);
+        const int o_voff = 4 * lh * o_row + 4 * col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (an element of an ext_vector goes through a scalar first:
+            // __builtin_bit_cast on the element reads element 0)
+            const float ov = O[4 * r + e];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+          }
+        }
+      }
+    }
+    block_sync();
+    // ---- step 2: re-anchor R (each tile just before its first use), then
+    // the products of chunk it.  Operand loads run one k-step ahead; the T
+    // merge barrier splits the k-steps between steps 2 and 3.
+    const int lane2 = opaque(lane);
+    const int ln2 = lane2 & 31;
+    const int lh2 = lane2 >> 5;
+    mfma_result_fence(R[0]);
+    mfma_result_fence(R[1]);
+    mfma_result_fence(R[2]);
+    mfma_result_fence(R[3]);
+    if (it < nc) {
+      Y = zero16();
+      O = zero16();
+      bf16x8 opa[2][4];
+      f32x4 fa[4];   // factors of the next tile to rescale
+      load_ops(opa[0], 0, ln2, lh2);
+      load_fac(fa, 0, lh2);
+#pragma unroll
+      for (int kk = 0; kk < KD / 16; ++kk) {
+        if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], kk + 1, ln2, lh2);
+        if ((kk & 1) == 0) rescale(kk >> 1, fa);
+        if ((kk & 1) == 1 && kk + 1 < KD / 16) load_fac(fa, (kk + 1) >> 1, lh2);
+        float x[8];
+        tile_rows_to_b(R[kk >> 1], kk & 1, x);
+        bf16x8 bh, bl;
+        split8(x, bh, bl);
+        const bf16x8(&o)[4] = opa[kk & 1];
+        Y = mfma3(o[0], o[1], bh, bl, Y);
+        if (fwd) O = mfma3(o[2], o[3], bh, bl, O);
+        if (kk == KSPLIT - 1) block_sync();   // ---- step 3 from here
+      }
+      block_sync();
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        f32x4 f[4];
+        load_fac(f, dt, lh2);
+        rescale(dt, f);
+      }
     }
   }
 
-  // P0 thread layout: wave w handles tokens 4w .. 4w+3 of the chunk, lane l
-  // channels 2l and 2l+1 (so every token row is one coalesced 256-byte read).
-  const int cp = lane;
-  const int tg = wave;
-  const int row_bytes = H * KD * 2;                       // one token of q, k, g, v
-  const int in_voff = (4 * tg) * row_bytes + 4 * cp;      // this thread's first element
-  const int o_row = H * VD * 4;                           // one token of o (bytes)
-  const int o_voff = (4 * lg) * o_row + 4 * col;
+  // ---- the fragment's final state (R was rescaled by e^{G_C - a} last)
+  float* dst0 = nullptr;
+  float* dst1 = nullptr;
+  if (MODE == kModeSumPhi) {
+    dst0 = p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD;
+  } else if (MODE == kModeSumS) {
+    dst0 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
+  } else {
+    if (flags & kFragSeqEnd) dst0 = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
+    if (p.pass == 1 && (flags & kFragSegLast)) dst1 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
+  }
+  if (dst0) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst0[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
+  }
+  if (dst1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst1[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
+  }
+}
 
-  // raw BF16 pairs of the chunk being prefetched (registers, one chunk ahead);
-  // buffer loads past the fragment's last token return zero
-  uint32_t rk[4], rg[4], rq[4], rv[4];
-  uint32_t rb = 0u;   // beta's raw bits: converted only when used, so that no
-                      // wait on the prefetch is forced inside fetch()
-  // Branch-free, so that the loads and the use of the previous chunk's
-  // registers share one basic block: loads a mode does not need, and loads
-  // past the fragment, get a zero-size buffer (they return zero and touch no
-  // memory).
+// ---------------------------------------------------------------------------
+// Helper waves (NOWN .. NOWN+NHELP-1), helper index hw: chunk it's operands
+// while the owners finish chunk it-1.
+//   step 1  land the prefetched inputs (issued one iteration earlier), gate
+//           prefix, anchor a (token 15), G_C; Kr, Qr, Kc, V (token-major),
+//           beta and the owners' rescale fac; issue the next chunk's loads
+//   step 2  A = beta o (Kr Kc^T) by 16-row blocks (hw 0, 1), each followed by
+//           the inverse of its diagonal block of I + A; P = Qr Kc^T (hw 2, 3)
+//   step 3  T10 = -T11 A10 T00 and T diag(beta), four columns per helper
+// Thread layout of step 1: helper hw covers the channels [32hw, 32hw + 32);
+// lane l takes the eight channels 32hw + 8(l/16) .. +7 of the tokens l%16 and
+// 16 + l%16 (16-byte loads; the 16 lanes of a row hold one channel octet for
+// 16 consecutive tokens, so the gate prefix is a scan across the row).
+template <int MODE>
+__device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int32_t beg,
+                                                const int32_t end) {
+  constexpr bool fwd = MODE == kModeFwd;
+  constexpr bool use_v = MODE != kModeSumPhi;
+  const int h = blockIdx.y;
+  const int H = p.H;
+  const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - NOWN;
+  const int lane = threadIdx.x & 63;
+  const int tk = lane & 15;                    // tokens tk and 16 + tk
+  const int c8 = 32 * hw + 8 * (lane >> 4);    // first of this lane's eight channels
+  const int nc = (end - beg + CH - 1) / CH;
+  const int row_bytes = H * KD * 2;            // one token of q, k, g, v
+  const int in_voff = tk * row_bytes + 2 * c8;
+
+  // raw BF16 of the chunk being prefetched (two tokens x eight channels per
+  // tensor); loads past the fragment's last token return zero
+  typedef uint32_t u32x4 __attribute__((vector_size(16)));
+  u32x4 rk[2], rg[2], rq[2], rv[2];
+  uint32_t rb = 0u;   // beta's raw bits
+  // Branch-free: loads a mode does not need, and loads past the fragment, get
+  // a zero-size buffer (they return zero and touch no memory).
   auto fetch = [&](int cs) {
     const int nn = min(CH, end - cs);
     const size_t base = (static_cast<size_t>(min(cs, end - 1)) * H + h) * KD;
@@ -298,129 +558,133 @@ __device__ __forceinline__ void run_fragment(const ChunkParams& p, ChunkSmem& sm
     const auto rsv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, use_v ? nrec : 0, kBufDword3);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int off = in_voff + m * row_bytes;
-      rk[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsk, off, 0, 0));
-      rg[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsg, off, 0, 0));
-      rq[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsq, off, 0, 0));
-      rv[m] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsv, off, 0, 0));
+    for (int j = 0; j < 2; ++j) {
+      const int off = in_voff + 16 * j * row_bytes;
+      rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
+      rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
+      rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
+      rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
     }
-    // beta: wave 0's first 32 lanes read one value per token
-    const int nb = (tg == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
+    // beta: helper 0's first 32 lanes read one value per token
+    const int nb = (hw == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
     const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.beta + static_cast<size_t>(min(cs, end - 1)) * H + h), 0, nb, kBufDword3);
     rb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane < CH ? lane * H * 2 : nb, 0, 0));
   };
   fetch(beg);
 
-  for (int c0 = beg; c0 < end; c0 += CH) {
-    const int n = min(CH, end - c0);
+  // (G_C - a) of the previous chunk for this lane's eight channels (log2 units)
+  float dprev[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
 
-    // ================= P0: gate prefix and the derived operands of the chunk
-    float kf[4][2], qf[4][2], G[4][2];
-    uint32_t vcur[4];
+  for (int it = 0; it <= nc; ++it) {
+    // ---- step 1: operands of chunk it, and the owners' rescale
+    if (it < nc) {
+      const int b = it & 1;
+      float kf[2][8], qf[2][8], G[2][8];
+      u32x4 vcur[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      kf[m][0] = __uint_as_float(rk[m] << 16);
-      kf[m][1] = __uint_as_float(rk[m] & 0xffff0000u);
-      qf[m][0] = __uint_as_float(rq[m] << 16);
-      qf[m][1] = __uint_as_float(rq[m] & 0xffff0000u);
-      G[m][0] = __uint_as_float(rg[m] << 16) * kLog2e;
-      G[m][1] = __uint_as_float(rg[m] & 0xffff0000u) * kLog2e;
-      vcur[m] = rv[m];
-    }
-    if (tg == 0 && lane < CH) sm.beta[lane] = __uint_as_float(rb << 16);
-    // Consume the prefetched registers before the next prefetch is issued: the
-    // q/v/beta loads are conditional, so if the scheduler hoisted the new loads
-    // above these uses, the inserted memory wait would have to cover the
-    // shortest load path and stall on the new loads.
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(c0 + CH);
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int m = 1; m < 4; ++m) {
-      G[m][0] += G[m - 1][0];
-      G[m][1] += G[m - 1][1];
-    }
-    *reinterpret_cast<float2*>(&sm.tot[tg * KD + 2 * cp]) = make_float2(G[3][0], G[3][1]);
-    __syncthreads();
+        for (int w = 0; w < 4; ++w) {
+          kf[j][2 * w] = __uint_as_float(rk[j][w] << 16);
+          kf[j][2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
+          qf[j][2 * w] = __uint_as_float(rq[j][w] << 16);
+          qf[j][2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
+          G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
+          G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
+        }
+        vcur[j] = rv[j];
+      }
+      if (hw == 0 && lane < CH) sm.beta[lane] = __uint_as_float(rb << 16);
+      // consume the landed registers before the next loads overwrite them
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(beg + (it + 1) * CH);
 
-    // prefix of the earlier token groups, the anchor a = G at token 15 (end of
-    // group 3) and G_C = G at the last token, all summed in group order
-    float pre[2] = {0.f, 0.f}, a[2] = {0.f, 0.f}, gc[2] = {0.f, 0.f};
+      // inclusive gate prefix over the 16 tokens of each row (row_shr scan),
+      // then across the two halves: a = G at token 15, G_C = G at token 31
+      float a[8], gc[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float2 tv = *reinterpret_cast<const float2*>(&sm.tot[t * KD + 2 * cp]);
-      if (t == tg) { pre[0] = gc[0]; pre[1] = gc[1]; }
-      if (t == 4) { a[0] = gc[0]; a[1] = gc[1]; }
-      gc[0] += tv.x;
-      gc[1] += tv.y;
-    }
-    const float shift[2] = {pre[0] - a[0], pre[1] - a[1]};
-    const float ega[2] = {__builtin_amdgcn_exp2f(gc[0] - a[0]), __builtin_amdgcn_exp2f(gc[1] - a[1])};
-    if (tg == 0) {
-      *reinterpret_cast<float2*>(&sm.ea[2 * cp]) =
-          make_float2(__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1]));
-      *reinterpret_cast<float2*>(&sm.gam[2 * cp]) =
-          make_float2(__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]));
-    }
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float x = G[j][c];
+          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+          G[j][c] = x;
+        }
+        // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
+        a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
+        const float t1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[1][c]), 0x1F0));
+        G[1][c] += a[c];
+        gc[c] = a[c] + t1;
+      }
+      if (tk == 0) {
+        float fv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(a[c] + dprev[c]);
+        st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+        st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dprev[c] = gc[c] - a[c];
 
-    // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, K^ = Kc e^{G_C-a}, Qr = q e^{G-a}
-    uint32_t khh[2][2], khl[2][2];
-    float kh_prev[2] = {0.f, 0.f};
+      // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, Qr = q e^{G-a}
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float kr[2], kc[2], kh[2], qr[2];
+      for (int j = 0; j < 2; ++j) {
+        const int i = 16 * j + tk;
+        uint32_t krh[4], krl[4], kch[4], kcl[4], qrh[4], qrl[4];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float x = G[m][c] + shift[c];
-        const float er = __builtin_amdgcn_exp2f(x);
-        const float ec = __builtin_amdgcn_exp2f(-x);
-        kr[c] = kf[m][c] * er;
-        kc[c] = kf[m][c] * ec;
-        kh[c] = kc[c] * ega[c];
-        qr[c] = qf[m][c] * er;
+        for (int w = 0; w < 4; ++w) {
+          float kr[2], kc[2], qr[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float x = G[j][2 * w + c] - a[2 * w + c];
+            const float er = __builtin_amdgcn_exp2f(x);
+            const float ec = __builtin_amdgcn_exp2f(-x);
+            kr[c] = kf[j][2 * w + c] * er;
+            kc[c] = kf[j][2 * w + c] * ec;
+            qr[c] = qf[j][2 * w + c] * er;
+          }
+          split_pair(kr[0], kr[1], krh[w], krl[w]);
+          split_pair(kc[0], kc[1], kch[w], kcl[w]);
+          if (fwd) split_pair(qr[0], qr[1], qrh[w], qrl[w]);
+        }
+        const int off = i * NS + c8;
+        st4(&sm.kr_h[off], u32x4{krh[0], krh[1], krh[2], krh[3]});
+        st4(&sm.kr_l[off], u32x4{krl[0], krl[1], krl[2], krl[3]});
+        st4(&sm.kc_h[b][off], u32x4{kch[0], kch[1], kch[2], kch[3]});
+        st4(&sm.kc_l[b][off], u32x4{kcl[0], kcl[1], kcl[2], kcl[3]});
+        if (fwd) {
+          st4(&sm.qr_h[off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
+          st4(&sm.qr_l[off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
+        }
+        if (use_v) {
+          st4(&sm.vv[b][off], u32x4{vcur[j][0], vcur[j][1], vcur[j][2], vcur[j][3]});
+        }
       }
-      const int i = 4 * tg + m;
-      uint32_t hh, ll;
-      split_pair(kr[0], kr[1], hh, ll);
-      *reinterpret_cast<uint32_t*>(&sm.kr_h[i * NS + 2 * cp]) = hh;
-      *reinterpret_cast<uint32_t*>(&sm.kr_l[i * NS + 2 * cp]) = ll;
-      split_pair(kc[0], kc[1], hh, ll);
-      *reinterpret_cast<uint32_t*>(&sm.kc_h[i * NS + 2 * cp]) = hh;
-      *reinterpret_cast<uint32_t*>(&sm.kc_l[i * NS + 2 * cp]) = ll;
-      if (fwd) {
-        split_pair(qr[0], qr[1], hh, ll);
-        *reinterpret_cast<uint32_t*>(&sm.qr_h[i * NS + 2 * cp]) = hh;
-        *reinterpret_cast<uint32_t*>(&sm.qr_l[i * NS + 2 * cp]) = ll;
-      }
-      // K^ packed along tokens (channel-major layout): pairs (m-1, m)
-      if (m & 1) {
-        split_pair(kh_prev[0], kh[0], khh[m >> 1][0], khl[m >> 1][0]);
-        split_pair(kh_prev[1], kh[1], khh[m >> 1][1], khl[m >> 1][1]);
-      } else {
-        kh_prev[0] = kh[0];
-        kh_prev[1] = kh[1];
-      }
+    } else if (tk == 0) {
+      // after the last chunk: R *= e^{G_C - a} turns R back into S
+      float fv[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
+      st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+      st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
     }
-    // channel-major rows d = 2cp + c, tokens 4tg .. 4tg+3 (8 bytes each)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int d = 2 * cp + c;
-      const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;  // low / high halves
-      *reinterpret_cast<uint2*>(&sm.kht_h[d * TS + 4 * tg]) = make_uint2(khh[0][c], khh[1][c]);
-      *reinterpret_cast<uint2*>(&sm.kht_l[d * TS + 4 * tg]) = make_uint2(khl[0][c], khl[1][c]);
-      if (use_v) {
-        *reinterpret_cast<uint2*>(&sm.vt[d * TS + 4 * tg]) =
-            make_uint2(__builtin_amdgcn_perm(vcur[1], vcur[0], sel), __builtin_amdgcn_perm(vcur[3], vcur[2], sel));
-      }
-    }
-    __syncthreads();
+    block_sync();
+    if (it == nc) break;
 
-    // ================= P1: A (waves 0, 1) and P (waves 2, 3) by 16-row blocks
-    // (the all-zero block above the diagonal is not computed)
-    if (wave < 2 || (wave < 4 && fwd)) {
-      const int rb = wave & 1;                  // row block: rows 16rb .. 16rb+15
-      const bool is_a = wave < 2;
+    // ---- step 2: A (hw 0, 1) with the diagonal blocks of T; P (hw 2, 3)
+    if (hw < 2 || fwd) {
+      const int b = it & 1;
+      const int lane_s = opaque(lane);
+      const int lm = lane_s & 15;             // 16x16x32 MFMA: row/column index
+      const int lg = lane_s >> 4;             // 16x16x32 MFMA: k-group / row group
+      const int rb = hw & 1;                  // row block: rows 16rb .. 16rb+15
+      const bool is_a = hw < 2;
       const bf16* xh = is_a ? sm.kr_h : sm.qr_h;
       const bf16* xl = is_a ? sm.kr_l : sm.qr_l;
       f32x4 acc[2] = {zero4(), zero4()};
@@ -433,300 +697,127 @@ __device__ __forceinline__ void run_fragment(const ChunkParams& p, ChunkSmem& sm
         for (int ct = 0; ct < 2; ++ct) {
           if (ct > rb) continue;
           const int boff = (16 * ct + lm) * NS + 32 * kk + 8 * lg;
-          acc[ct] = mfma16x3(ah, al, *reinterpret_cast<const bf16x8*>(&sm.kc_h[boff]),
-                             *reinterpret_cast<const bf16x8*>(&sm.kc_l[boff]), acc[ct]);
+          acc[ct] = mfma16x3(ah, al, *reinterpret_cast<const bf16x8*>(&sm.kc_h[b][boff]),
+                             *reinterpret_cast<const bf16x8*>(&sm.kc_l[b][boff]), acc[ct]);
         }
       }
       mfma_result_fence(acc[0], acc[1]);
       // tile ct holds rows i = 16rb + 4lg + e of column j = 16ct + lm
+      if (!is_a) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int j = 16 * ct + lm;
-        const int i0 = 16 * rb + 4 * lg;
-        if (is_a) {
-          if (ct > rb) continue;
-          float4 v4;
-          float* vp = reinterpret_cast<float*>(&v4);
+        for (int ct = 0; ct < 2; ++ct) {
+          const int j = 16 * ct + lm;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            const float x = (j < i) ? sm.beta[i] * acc[ct][e] : 0.f;
-            vp[e] = x;
-            sm.an[i * FS + j] = x;
-          }
-          *reinterpret_cast<float4*>(&sm.at[j * FS + i0]) = v4;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            const float x = (ct <= rb && j <= i) ? acc[ct][e] : 0.f;
+            const int i = 16 * rb + 4 * lg + e;
             bf16 hh, ll;
-            split(x, hh, ll);
+            split((ct <= rb && j <= i) ? acc[ct][e] : 0.f, hh, ll);
             sm.p_h[i * TS + j] = hh;
             sm.p_l[i * TS + j] = ll;
           }
         }
-      }
-    }
-    __syncthreads();
-
-    // Y = Kr (e^a o S) and O = Qr (e^a o S), this wave's 16 columns; the
-    // state is scaled and split into B operands one 32-row k-step at a time
-    f32x4 Y[2] = {zero4(), zero4()};
-    f32x4 O[2] = {zero4(), zero4()};
-    auto state_products = [&]() {
+      } else {
+        const f32x4 brow = ld4(&sm.beta[16 * rb + 4 * lg]);
 #pragma unroll
-      for (int kk = 0; kk < KD / 32; ++kk) {
-        float x[8];
-        tiles16_to_b(S[2 * kk], S[2 * kk + 1], x);
-        const float4 e0 = *reinterpret_cast<const float4*>(&sm.ea[32 * kk + 8 * lg]);
-        const float4 e1 = *reinterpret_cast<const float4*>(&sm.ea[32 * kk + 8 * lg + 4]);
-        x[0] *= e0.x; x[1] *= e0.y; x[2] *= e0.z; x[3] *= e0.w;
-        x[4] *= e1.x; x[5] *= e1.y; x[6] *= e1.z; x[7] *= e1.w;
-        bf16x8 sbh, sbl;
-        split8(x, sbh, sbl);
+        for (int ct = 0; ct < 2; ++ct) {
+          if (ct > rb) continue;
+          const int j = 16 * ct + lm;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const int off = (16 * rt + lm) * NS + 32 * kk + 8 * lg;
-          Y[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kr_h[off]),
-                           *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]), sbh, sbl, Y[rt]);
-          if (fwd) {
-            O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.qr_h[off]),
-                             *reinterpret_cast<const bf16x8*>(&sm.qr_l[off]), sbh, sbl, O[rt]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * rb + 4 * lg + e;
+            sm.an[i * FS + j] = (j < i) ? brow[e] * acc[ct][e] : 0.f;
           }
         }
-      }
-    };
-
-    // ================= P2: diagonal blocks of T (wave 0), state products (rest)
-    if (wave == 0) {
-      if (lane < 32) {
-        const int b = lane >> 4;   // diagonal block
-        const int c = lane & 15;   // column of the block solved by this lane
-        const int base = 16 * b;
+        // Diagonal block rb of T = (I + A)^{-1} from this wave's own A rows
+        // (the wave's LDS accesses complete in order): every lane loads the
+        // block's strictly lower part first, then lane c computes column c row
+        // by row, x_i = [i == c] - sum_{j<i} A_ij x_j (rows above c come out
+        // zero).  Lanes 16..63 repeat lanes 0..15's work.
+        wave_lds_order();
+        const int base = 16 * rb;
+        f32x4 arow[16][4];
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < (i + 3) / 4; ++q4)
+            arow[i][q4] = ld4(&sm.an[(base + i) * FS + base + 4 * q4]);
+        const int c = lm;
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          float acc_i = (i == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float* arow = &sm.at[(base + jj) * FS + base];
-#pragma unroll
-          for (int q4 = jj / 4; q4 < 4; ++q4) {
-            const float4 t4 = *reinterpret_cast<const float4*>(&arow[4 * q4]);
-            const float av[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * q4 + e;
-              if (i > jj) x[i] -= av[e] * x[jj];
-            }
+          for (int jj = 0; jj < i; ++jj) {
+            acc_i -= arow[i][jj >> 2][jj & 3] * x[jj];
           }
+          x[i] = acc_i;
         }
+        if (lane_s < 16) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          *reinterpret_cast<float4*>(&sm.tt[(base + c) * FS + base + 4 * q4]) =
-              make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            st4(&sm.tt[(base + c) * FS + base + 4 * q4], f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
       }
-    } else {
-      state_products();
     }
-    __syncthreads();
+    block_sync();
 
-    // ================= P2b: T10 = -T11 A10 T00 and T diag(beta) (wave 5);
-    // wave 0's state products meanwhile.  Wave 5 exchanges X through LDS with
-    // itself only, and a wave's LDS accesses complete in order, so no barrier
-    // is needed between writing X and reading it back.
-    if (wave == 5) {
-      // lane: column tc of the block, rows ti = 4qq + (lane / 16), qq = 0..3.
-      // Every operand row is loaded whole with independent 16-byte reads.
-      const int tc = lane & 15;
-      const int tr = lane >> 4;
-      float tcol[16];   // T00[:, tc] (row tc of tt)
+    // ---- step 3: T10 = -T11 A10 T00 and T diag(beta).  Helper hw takes the
+    // columns tc = 4hw .. 4hw+3, lane (row ti, column tc); X = A10 T00 goes
+    // through LDS inside the wave, which needs no barrier.
+    {
+      const int lane_s = opaque(lane);
+      const int ti = lane_s & 15;
+      const int tc = 4 * hw + (lane_s >> 4);
+      f32x4 u[4], w[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&sm.tt[tc * FS + 4 * q4]);
-        tcol[4 * q4] = v4.x; tcol[4 * q4 + 1] = v4.y; tcol[4 * q4 + 2] = v4.z; tcol[4 * q4 + 3] = v4.w;
+        u[q4] = ld4(&sm.an[(16 + ti) * FS + 4 * q4]);   // A10[ti, :]
+        w[q4] = ld4(&sm.tt[tc * FS + 4 * q4]);          // T00[:, tc]
       }
+      float xs = 0.f;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int ti = 4 * qq + tr;
-        float arow[16];   // A10[ti, :]
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&sm.an[(16 + ti) * FS + 4 * q4]);
-          arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
-        }
-        float xs = 0.f;
-#pragma unroll
-        for (int kx = 0; kx < 16; ++kx) xs += arow[kx] * tcol[kx];
-        sm.xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
-      }
-      // the wave's own LDS writes complete in order before its later reads
-      float xcol[16];   // X[:, tc]
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&sm.xt[tc * XS + 4 * q4]);
-        xcol[4 * q4] = v4.x; xcol[4 * q4 + 1] = v4.y; xcol[4 * q4 + 2] = v4.z; xcol[4 * q4 + 3] = v4.w;
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        xs += u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
+      sm.xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
+      const float t00 = sm.tn[ti * FS + tc];
+      const float t11 = sm.tn[(16 + ti) * FS + 16 + tc];
       const float b0 = sm.beta[tc];
       const float b1 = sm.beta[16 + tc];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int ti = 4 * qq + tr;
-        float trow[16];   // T11[ti, :]
+      for (int q4 = 0; q4 < 4; ++q4)
+        u[q4] = ld4(&sm.tn[(16 + ti) * FS + 16 + 4 * q4]);   // T11[ti, :]
+      wave_lds_order();
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&sm.tn[(16 + ti) * FS + 16 + 4 * q4]);
-          trow[4 * q4] = v4.x; trow[4 * q4 + 1] = v4.y; trow[4 * q4 + 2] = v4.z; trow[4 * q4 + 3] = v4.w;
-        }
-        float t10 = 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) w[q4] = ld4(&sm.xt[tc * XS + 4 * q4]);  // X[:, tc]
+      float t10 = 0.f;
 #pragma unroll
-        for (int kx = 0; kx < 16; ++kx) t10 -= trow[kx] * xcol[kx];
-        bf16 hh, ll;
-        split(sm.tn[ti * FS + tc] * b0, hh, ll);
-        sm.tb_h[ti * TS + tc] = hh;
-        sm.tb_l[ti * TS + tc] = ll;
-        split(trow[tc] * b1, hh, ll);
-        sm.tb_h[(16 + ti) * TS + 16 + tc] = hh;
-        sm.tb_l[(16 + ti) * TS + 16 + tc] = ll;
-        split(t10 * b0, hh, ll);
-        sm.tb_h[(16 + ti) * TS + tc] = hh;
-        sm.tb_l[(16 + ti) * TS + tc] = ll;
-        sm.tb_h[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
-        sm.tb_l[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
-      }
-    } else if (wave == 0) {
-      state_products();
+      for (int q4 = 0; q4 < 4; ++q4)
+        t10 -= u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
+      bf16 hh, ll;
+      split(t00 * b0, hh, ll);
+      sm.tb_h[ti * TS + tc] = hh;
+      sm.tb_l[ti * TS + tc] = ll;
+      split(t11 * b1, hh, ll);
+      sm.tb_h[(16 + ti) * TS + 16 + tc] = hh;
+      sm.tb_l[(16 + ti) * TS + 16 + tc] = ll;
+      split(t10 * b0, hh, ll);
+      sm.tb_h[(16 + ti) * TS + tc] = hh;
+      sm.tb_l[(16 + ti) * TS + tc] = ll;
+      sm.tb_h[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
+      sm.tb_l[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
     }
-    __syncthreads();
-
-    // ================= P3: U = T diag(beta) (V - Y), O += P U, state update
-    // Land the next chunk's prefetch here, most of a chunk after it was issued:
-    // the empty asm takes the registers as operands, so the memory wait is
-    // placed before it and none is left for the next chunk's first use.
-    asm volatile("" : "+v"(rk[0]), "+v"(rk[1]), "+v"(rk[2]), "+v"(rk[3]), "+v"(rg[0]), "+v"(rg[1]),
-                 "+v"(rg[2]), "+v"(rg[3]), "+v"(rq[0]), "+v"(rq[1]), "+v"(rq[2]), "+v"(rq[3]),
-                 "+v"(rv[0]), "+v"(rv[1]), "+v"(rv[2]), "+v"(rv[3]), "+v"(rb));
-    f32x4 U[2] = {zero4(), zero4()};
-    {
-      f32x4 D[2];
-      mfma_result_fence(Y[0], Y[1]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        float vv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (use_v) {
-          const uint2 v2 = *reinterpret_cast<const uint2*>(&sm.vt[col * TS + 16 * rt + 4 * lg]);
-          vv[0] = __uint_as_float(v2.x << 16);
-          vv[1] = __uint_as_float(v2.x & 0xffff0000u);
-          vv[2] = __uint_as_float(v2.y << 16);
-          vv[3] = __uint_as_float(v2.y & 0xffff0000u);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) D[rt][e] = vv[e] - Y[rt][e];
-      }
-      float x[8];
-      tiles16_to_b(D[0], D[1], x);
-      bf16x8 dbh, dbl;
-      split8(x, dbh, dbl);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int off = (16 * rt + lm) * TS + 8 * lg;
-        U[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]),
-                         *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]), dbh, dbl, U[rt]);
-      }
-    }
-    bf16x8 ubh, ubl;
-    {
-      float x[8];
-      mfma_result_fence(U[0], U[1]);
-      tiles16_to_b(U[0], U[1], x);
-      split8(x, ubh, ubl);
-    }
-    if (fwd) {
-      // rows past the fragment's end fall outside the buffer and are dropped
-      const auto rso = __builtin_amdgcn_make_buffer_rsrc(
-          p.o + (static_cast<size_t>(c0) * H + h) * VD, 0, (n - 1) * o_row + 4 * VD, kBufDword3);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int off = (16 * rt + lm) * TS + 8 * lg;
-        O[rt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]),
-                         *reinterpret_cast<const bf16x8*>(&sm.p_l[off]), ubh, ubl, O[rt]);
-      }
-      mfma_result_fence(O[0], O[1]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (an element of an ext_vector goes through a scalar first:
-          // __builtin_bit_cast on the element reads element 0)
-          const float ov = O[rt][e];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff + (16 * rt + e) * o_row,
-                                                0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const float4 e4 = *reinterpret_cast<const float4*>(&sm.gam[16 * dt + 4 * lg]);
-      S[dt][0] *= e4.x;
-      S[dt][1] *= e4.y;
-      S[dt][2] *= e4.z;
-      S[dt][3] *= e4.w;
-      const int off = (16 * dt + lm) * TS + 8 * lg;
-      S[dt] = mfma16x3(*reinterpret_cast<const bf16x8*>(&sm.kht_h[off]),
-                       *reinterpret_cast<const bf16x8*>(&sm.kht_l[off]), ubh, ubl, S[dt]);
-    }
-    // The next chunk's first barrier orders its LDS writes after every read
-    // of this chunk: before that barrier it writes only tot and beta, which
-    // P3 does not read.  The state tiles are read next at least a P0 and two
-    // barriers later, far past the MFMA result latency.
-  }
-
-  // ---- the fragment's final state
-  float* dst0 = nullptr;
-  float* dst1 = nullptr;
-  if (mode == kModeSumPhi) {
-    dst0 = p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD;
-  } else if (mode == kModeSumS) {
-    dst0 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
-  } else {
-    if (flags & kFragSeqEnd) dst0 = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
-    if (p.pass == 1 && (flags & kFragSegLast))
-      dst1 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
-  }
-#pragma unroll
-  for (int dt = 0; dt < 8; dt += 2) mfma_result_fence(S[dt], S[dt + 1]);
-  if (dst0) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst0[(16 * dt + 4 * lg + e) * VD + col] = S[dt][e];
-  }
-  if (dst1) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst1[(16 * dt + 4 * lg + e) * VD + col] = S[dt][e];
+    block_sync();
   }
 }
 
-
 // One workgroup runs one fragment (a run of tokens of one sequence inside one
-// segment) of one head, chunk after chunk, holding the state in registers.
-// Eight waves; wave w owns state columns [16w, 16w + 16) as eight 16 x 16 FP32
-// accumulator tiles.
-//
-// Per chunk:
-//   P0  (all)      load (prefetched one chunk ahead), gate prefix, Kr, Kc, Qr
-//                  (token-major) and K^, V (channel-major) into LDS
-//   P1  (waves 0-3) A = beta o (Kr Kc^T) and P = Qr Kc^T, 16 x 16 tiles
-//   P2  wave 0 lanes 0-31: diagonal 16 x 16 blocks of T = (I + A)^{-1};
-//       every other wave meanwhile: Y = Kr (e^a o S) and O = Qr (e^a o S)
-//   P2b wave 5: off-diagonal block of T and T diag(beta); wave 0: its Y, O
-//   P3  (all)      U = T diag(beta) (V - Y), O += P U, S <- e^{G_C} o S + K^^T U
-// using W S = T diag(beta) (K o e^G) S, K o e^G = e^a o Kr, Q o e^G = e^a o Qr.
+// segment) of one head, chunk after chunk, as a two-stage pipeline: NOWN owner
+// waves hold the state in registers and apply chunk n-1 while NHELP helper
+// waves build chunk n's operands in LDS (see owner_fragment and
+// helper_fragment); three barriers per chunk.
 __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ ChunkSmem sm;
   const int f = blockIdx.x;
@@ -747,12 +838,16 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
     for (int i = tid; i < KD * KD / 4; i += NT) dst[i] = z;
     return;
   }
+  const bool owner = __builtin_amdgcn_readfirstlane(tid >> 6) < NOWN;
   if (work.mode == kModeFwd) {
-    run_fragment<kModeFwd>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
+    if (owner) owner_fragment<kModeFwd>(p, sm, flags, seg, seq, beg, end, work.from_carry);
+    else helper_fragment<kModeFwd>(p, sm, beg, end);
   } else if (work.mode == kModeSumS) {
-    run_fragment<kModeSumS>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
+    if (owner) owner_fragment<kModeSumS>(p, sm, flags, seg, seq, beg, end, false);
+    else helper_fragment<kModeSumS>(p, sm, beg, end);
   } else if (work.mode == kModeSumPhi) {
-    run_fragment<kModeSumPhi>(p, sm, f, flags, seg, seq, beg, end, work.from_carry);
+    if (owner) owner_fragment<kModeSumPhi>(p, sm, flags, seg, seq, beg, end, false);
+    else helper_fragment<kModeSumPhi>(p, sm, beg, end);
   }
 }
 
