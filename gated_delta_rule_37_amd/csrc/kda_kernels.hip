@@ -52,7 +52,7 @@ static_assert(NHELP * 32 == KD, "each helper covers 32 channels in the chunk pro
 static_assert((NOWN + NHELP) * 64 == NT, "chunk kernel wave roles");
 constexpr int KSPLIT = 4;             // owner k-steps before the T merge barrier
 constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
-constexpr int NS = 136;   // row stride (bf16) of token-major [32][128] tiles
+constexpr int NS = 152;   // row stride (bf16) of token-major [32][128] tiles (conflict-free row and transposed reads)
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
 constexpr int XS = 20;    // row stride (fp32) of the 16 x 16 off-diagonal product
@@ -512,6 +512,17 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
   }
 }
 
+// One step of an inclusive scan across each 16-lane row for sixteen values:
+// x += (x of the lane CTRL's row shift away; zero past the row's start).
+template <int CTRL>
+__device__ __forceinline__ void scan_stage(float (&G)[2][8]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      G[j][c] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G[j][c]), CTRL, 0xf, 0xf, true));
+}
+
 // ---------------------------------------------------------------------------
 // Helper waves (NOWN .. NOWN+NHELP-1), helper index hw: chunk it's operands
 // while the owners finish chunk it-1.
@@ -602,25 +613,24 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
       __builtin_amdgcn_sched_barrier(0);
       fetch(beg + (it + 1) * CH);
 
-      // inclusive gate prefix over the 16 tokens of each row (row_shr scan),
+      // inclusive gate prefix over the 16 tokens of each row (row_shr scan,
+      // stage by stage over all sixteen values so the DPP latencies overlap),
       // then across the two halves: a = G at token 15, G_C = G at token 31
+      scan_stage<0x111>(G);   // row_shr:1
+      scan_stage<0x112>(G);   // row_shr:2
+      scan_stage<0x114>(G);   // row_shr:4
+      scan_stage<0x118>(G);   // row_shr:8
+      // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
       float a[8], gc[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float x = G[j][c];
-          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
-          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
-          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
-          x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
-          G[j][c] = x;
-        }
-        // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
         a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
-        const float t1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[1][c]), 0x1F0));
+        gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[1][c]), 0x1F0));
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
         G[1][c] += a[c];
-        gc[c] = a[c] + t1;
+        gc[c] += a[c];
       }
       if (tk == 0) {
         float fv[8];
