@@ -92,8 +92,9 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
   p.updates = updates;
   p.carry = carry_in;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(H, kda::kComposeColumnBlocks), dim3(kda::kComposeThreads), 0,
-                     stream, p);
+  // one workgroup per (head, column block), heads padded to a multiple of 8
+  const int blocks = ((H + 7) / 8) * 8 * kda::kComposeColumnBlocks;
+  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(blocks), dim3(kda::kComposeThreads), 0, stream, p);
   return finish_launch();
 }
 

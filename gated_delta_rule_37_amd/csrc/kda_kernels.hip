@@ -863,21 +863,68 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of
 // 32 state columns.  Wave w computes rows [32w, 32w + 32); the current carry
-// is shared through LDS as split B operands.
+// is shared through LDS as split B operands.  A_r and B_r do not depend on
+// the carry, so each step's operands are loaded one step ahead.  Blocks are
+// numbered so that the column blocks of one head run on one XCD (workgroups
+// are dealt to the eight XCDs in turn) and share its L2 copy of A_r.
 __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
   __shared__ bf16x8 cbh[8][64];
   __shared__ bf16x8 cbl[8][64];
-  const int h = blockIdx.x;
-  const int cb = blockIdx.y;
+  const int H = p.H;
+  const int xcd = blockIdx.x % 8;
+  const int kq = blockIdx.x / 8;
+  const int cb = kq % kComposeColumnBlocks;
+  const int h = xcd + 8 * (kq / kComposeColumnBlocks);
+  if (h >= H) return;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int ln = lane & 31;
   const int lh = lane >> 5;
-  const int H = p.H;
   const int col = 32 * cb + ln;
 
+  // this lane's operands of step r: B_r (accumulator layout) and, when the
+  // transition is live, its row 32w + l%32 of A_r in k-step order
+  auto load_step = [&](const int r, const bool live, f32x4 (&a)[KD / 16][2], f32x16& bv) {
+    const float* bsrc = p.updates + (static_cast<size_t>(r) * H + h) * KD * VD;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[4 * q + e] = bsrc[(32 * wave + 8 * q + 4 * lh + e) * VD + col];
+    }
+    if (live) {
+      const float* arow = p.transitions + ((static_cast<size_t>(r) * H + h) * KD + 32 * wave + ln) * KD;
+#pragma unroll
+      for (int kk = 0; kk < KD / 16; ++kk) {
+        a[kk][0] = *reinterpret_cast<const f32x4*>(&arow[16 * kk + 8 * lh]);
+        a[kk][1] = *reinterpret_cast<const f32x4*>(&arow[16 * kk + 8 * lh + 4]);
+      }
+    }
+  };
+
+  // transition flags of steps [lbase, lbase + 64) as a wave-wide bit mask.
+  // (A plan read inside the loop would be a vector load whose wait also
+  // drains the prefetches and the carry stores in flight.)
+  uint64_t lmask = 0;
+  int lbase = -64;
+  auto live_at = [&](const int r) {
+    if (r - lbase >= 64) {
+      lbase = r & ~63;
+      const int idx = lbase + lane;
+      const bool f = idx < p.S - 1 && p.plan[p.L.seg_transition_live + idx] != 0;
+      lmask = __builtin_amdgcn_ballot_w64(f);
+    }
+    return ((lmask >> (r - lbase)) & 1ull) != 0;
+  };
+
   f32x16 cur = zero16();
+  f32x4 a_n[KD / 16][2];
+  f32x16 b_n = zero16();
+  bool live_n = false;
+  if (p.S > 1) {
+    live_n = live_at(0);
+    load_step(0, live_n, a_n, b_n);
+  }
   for (int r = 0; r < p.S; ++r) {
     float* cdst = p.carry + (static_cast<size_t>(r) * H + h) * KD * VD;
 #pragma unroll
@@ -886,14 +933,28 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
       for (int e = 0; e < 4; ++e) cdst[(32 * wave + 8 * q + 4 * lh + e) * VD + col] = cur[4 * q + e];
     }
     if (r == p.S - 1) break;
-    const float* bsrc = p.updates + (static_cast<size_t>(r) * H + h) * KD * VD;
-    f32x16 nxt;
+    // take step r's operands, then issue step r+1's loads
+    f32x4 a_c[KD / 16][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) nxt[4 * q + e] = bsrc[(32 * wave + 8 * q + 4 * lh + e) * VD + col];
+    for (int kk = 0; kk < KD / 16; ++kk) {
+      a_c[kk][0] = a_n[kk][0];
+      a_c[kk][1] = a_n[kk][1];
     }
-    if (p.plan[p.L.seg_transition_live + r]) {
+    f32x16 nxt = b_n;
+    const bool live = live_n;
+    if (r + 1 < p.S - 1) {
+      live_n = live_at(r + 1);
+      load_step(r + 1, live_n, a_n, b_n);
+    }
+    if (live) {
+      // A_r's rows, split (independent of the carry, so before the barrier)
+      bf16x8 ah[KD / 16], al[KD / 16];
+#pragma unroll
+      for (int kk = 0; kk < KD / 16; ++kk) {
+        const float xv[8] = {a_c[kk][0][0], a_c[kk][0][1], a_c[kk][0][2], a_c[kk][0][3],
+                             a_c[kk][1][0], a_c[kk][1][1], a_c[kk][1][2], a_c[kk][1][3]};
+        split8(xv, ah[kk], al[kk]);
+      }
       mfma_result_fence(cur);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -902,16 +963,18 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
         split8(x, cbh[2 * wave + s][lane], cbl[2 * wave + s][lane]);
       }
       __syncthreads();
-      const float* arow = p.transitions + ((static_cast<size_t>(r) * H + h) * KD + 32 * wave + ln) * KD;
+      // two accumulation chains (even and odd k-steps) halve the dependent
+      // MFMA sequence
+      f32x16 acc1 = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&arow[16 * kk + 8 * lh]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&arow[16 * kk + 8 * lh + 4]);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        bf16x8 ah, al;
-        split8(xv, ah, al);
-        nxt = mfma3(ah, al, cbh[kk][lane], cbl[kk][lane], nxt);
+      for (int kk = 0; kk < KD / 16; kk += 2) {
+        nxt = mfma3(ah[kk], al[kk], cbh[kk][lane], cbl[kk][lane], nxt);
+        acc1 = mfma3(ah[kk + 1], al[kk + 1], cbh[kk + 1][lane], cbl[kk + 1][lane], acc1);
       }
+      mfma_result_fence(nxt);
+      mfma_result_fence(acc1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) nxt[i] += acc1[i];
       __syncthreads();
     }
     cur = nxt;
