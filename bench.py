@@ -55,38 +55,45 @@ STATE_BYTES = K * V * 4
 
 
 def chunk_kernel_work(blob, H):
-    """Algorithmic MACs, executed bf16 MFMA MACs and HBM bytes of the two
-    launches of the chunk kernel, from the plan blob."""
+    """Algorithmic MACs, executed bf16 MFMA MACs and HBM bytes of the two chunk
+    launches, from the plan blob: {"summaries": ..., "carry": ...}
+    (kda_chunk_kernel, then kda_carry_kernel)."""
     T, N, S, F = (int(x) for x in blob[:4])
     o = 4
     o += S + 1          # seg_bounds
-    o += 4 * S          # first, last, carry, live
+    o += 2 * S          # first, last
+    o += S              # carry
+    seg_live = blob[o:o + S]; o += S
     o += S + 1          # frag_ptr
     f_seq = blob[o:o + F]; o += F
     f_beg = blob[o:o + F]; o += F
     f_end = blob[o:o + F]; o += F
-    o += F              # frag_seg
+    f_seg = blob[o:o + F]; o += F
     f_flags = blob[o:o + F]
-    work = {"macs": 0.0, "mfma_macs": 0.0, "bytes": 0.0}
+    work = {k: {"macs": 0.0, "mfma_macs": 0.0, "bytes": 0.0} for k in ("summaries", "carry")}
 
-    def add(mode, L):
-        work["macs"] += MACS[mode] * L * H
-        work["mfma_macs"] += MFMA_MACS[mode] * L * H
-        work["bytes"] += BYTES[mode] * L * H
+    def add(launch, mode, L):
+        work[launch]["macs"] += MACS[mode] * L * H
+        work[launch]["mfma_macs"] += MFMA_MACS[mode] * L * H
+        work[launch]["bytes"] += BYTES[mode] * L * H
 
     for f in range(F):
         L = int(f_end[f] - f_beg[f])
         fl = int(f_flags[f])
+        seg_last, seq_end = (fl & 2) > 0, (fl & 4) > 0
         if fl & 1:                       # carried first fragment
-            if fl & 2:                   # pass 1: B_r and A_r from zero / identity
-                add("sum_s", L)
-                add("sum_phi", L)
-                work["bytes"] += 2 * STATE_BYTES * H
-            add("fwd", L)                # pass 2: forward from C_r
-            work["bytes"] += STATE_BYTES * H * (1 + ((fl & 4) > 0))
+            if seg_last:                 # summaries: B_r from zero, A_r from identity
+                add("summaries", "sum_s", L)
+                live = int(seg_live[int(f_seg[f])]) != 0
+                if live:                 # one workgroup builds both: inputs read once
+                    work["summaries"]["macs"] += MACS["sum_phi"] * L * H
+                    work["summaries"]["mfma_macs"] += MFMA_MACS["sum_phi"] * L * H
+                work["summaries"]["bytes"] += 2 * STATE_BYTES * H
+            add("carry", "fwd", L)       # carry: forward from C_r
+            work["carry"]["bytes"] += STATE_BYTES * H * (1 + seq_end)
         else:
-            add("fwd", L)
-            work["bytes"] += STATE_BYTES * H * (((fl & 2) > 0) + ((fl & 4) > 0))
+            add("summaries", "fwd", L)
+            work["summaries"]["bytes"] += STATE_BYTES * H * (2 * seg_last + seq_end)
     return work
 
 
@@ -129,8 +136,8 @@ def cpu_baseline(x, w, heads=8, tokens=16384):
     }
 
 
-def traffic_from_profile():
-    """HBM bytes per chunk-kernel launch from the committed PMC summary, if it was
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, if it was
     taken on the current kernel source; else None."""
     path = TRAFFIC_JSON
     if not os.path.exists(path):
@@ -139,7 +146,8 @@ def traffic_from_profile():
     digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if rec.get("kernel_source_sha256") != digest:
         return None
-    return rec.get("bytes_per_launch")
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "chunk_kernel_t65536_h32_s64_traffic.json")
@@ -158,26 +166,31 @@ def _pmc_per_dispatch(csv_path, counter, name_part):
 
 
 def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
-    """HBM bytes per chunk-kernel launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-    runs (KiB per dispatch), each scaled by what the same counter reads for a plain
-    device copy of copy_bytes (FETCH reads and WRITE writes copy_bytes once)."""
+    """HBM bytes per launch of each chunk kernel from rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter reads
+    for a plain device copy of copy_bytes (FETCH reads and WRITE writes copy_bytes
+    once)."""
     cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copy")
     cw = _pmc_per_dispatch(copy_write_csv, "WRITE_SIZE", "copy")
     big_f = max(cf)
     big_w = max(cw)
     f_scale = copy_bytes / (big_f * 1024.0)
     w_scale = copy_bytes / (big_w * 1024.0)
-    kf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", "kda_chunk_kernel")
-    kw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", "kda_chunk_kernel")
-    fetch_b = sum(kf) / len(kf) * 1024.0 * f_scale
-    write_b = sum(kw) / len(kw) * 1024.0 * w_scale
+    kernels = {}
+    for name in ("kda_chunk_kernel", "kda_carry_kernel"):
+        kf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", name)
+        kw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", name)
+        if not kf or not kw:
+            continue
+        fetch_b = sum(kf) / len(kf) * 1024.0 * f_scale
+        write_b = sum(kw) / len(kw) * 1024.0 * w_scale
+        kernels[name] = {"bytes_per_launch": round(fetch_b + write_b),
+                         "fetch_bytes_per_launch": round(fetch_b),
+                         "write_bytes_per_launch": round(write_b),
+                         "launches_averaged": len(kf)}
     rec = {
-        "kernel": "kda_chunk_kernel",
         "workload": "t65536_h32_s64",
-        "bytes_per_launch": round(fetch_b + write_b),
-        "fetch_bytes_per_launch": round(fetch_b),
-        "write_bytes_per_launch": round(write_b),
-        "launches_averaged": len(kf),
+        "kernels": kernels,
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": big_f, "write_kib": big_w,
                              "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
         "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
@@ -275,22 +288,30 @@ def main():
 
     blob = plan.blob
     cw = chunk_kernel_work(blob, w.H)
-    chunk_ms_total = pass1_ms + pass2_ms          # two launches of kda_chunk_kernel
-    chunk_ms_avg = chunk_ms_total / 2
-    t_mfma = cw["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3
-    t_hbm = cw["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
-    traffic = traffic_from_profile()
-    if t_mfma >= t_hbm:
-        achieved = cw["mfma_macs"] * 2 / 2 / (chunk_ms_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    else:
-        achieved = cw["bytes"] / 2 / (chunk_ms_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = traffic
-    roof["kernel"] = "kda_chunk_kernel"
-    roof["launch_ms_avg"] = round(chunk_ms_avg, 4)
+    launches = {"kda_chunk_kernel": (cw["summaries"], pass1_ms), "kda_carry_kernel": (cw["carry"], pass2_ms)}
+
+    def roofline(name):
+        wk, ms = launches[name]
+        t_mfma = wk["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        t_hbm = wk["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+        if t_mfma >= t_hbm:
+            achieved = wk["mfma_macs"] * 2 / (ms * 1e-3) / 1e12
+            r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        else:
+            achieved = wk["bytes"] / (ms * 1e-3) / 1e9
+            r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        r["traffic"] = traffic_from_profile(name)
+        r["kernel"] = name
+        r["launch_ms_avg"] = round(ms, 4)
+        r["bounds_ms"] = {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)}
+        return r
+
+    # the dominant kernel of the step is the longer of the two chunk launches
+    dominant = "kda_chunk_kernel" if pass1_ms >= pass2_ms else "kda_carry_kernel"
+    roof = roofline(dominant)
+    other = roofline("kda_carry_kernel" if dominant == "kda_chunk_kernel" else "kda_chunk_kernel")
 
     S = plan.S
     live = int(sum(blob[4 + (S + 1) + 3 * S: 4 + (S + 1) + 4 * S]))
@@ -321,7 +342,7 @@ def main():
             "bound_ms_hbm": round(comp["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
             "bound_ms_mfma": round(comp["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 4),
         },
-        "chunk_bounds_ms": {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)},
+        "other_chunk_roofline": other,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads, args.cpu_tokens)

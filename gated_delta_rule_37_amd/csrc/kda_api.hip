@@ -72,7 +72,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.updates = updates;
   p.carry = nullptr;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 2), dim3(kda::kChunkThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kda::kSummaryThreads), 0, stream, p);
   return finish_launch();
 }
 
@@ -123,6 +123,6 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.updates = nullptr;
   p.carry = carry_in;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kda::kChunkThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, H, 1), dim3(kda::kCarryThreads), 0, stream, p);
   return finish_launch();
 }

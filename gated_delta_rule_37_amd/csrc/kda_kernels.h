@@ -11,7 +11,8 @@
 
 namespace kda {
 
-constexpr int kChunkThreads = 512;    // kda_chunk_kernel workgroup size (8 waves)
+constexpr int kSummaryThreads = 768;  // kda_chunk_kernel (summaries launch): 12 waves
+constexpr int kCarryThreads = 512;    // kda_carry_kernel (carry launch): 8 waves
 constexpr int kComposeThreads = 256;  // kda_compose_kernel workgroup size
 constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
 
@@ -43,6 +44,7 @@ struct ComposeParams {
 };
 
 __global__ void kda_chunk_kernel(ChunkParams p);
+__global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_compose_kernel(ComposeParams p);
 
 }  // namespace kda

@@ -45,11 +45,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
 constexpr int CH = 32;    // chunk length (tokens)
-constexpr int NT = kChunkThreads;     // chunk kernel: owner and helper waves
-constexpr int NOWN = 4;               // owner waves: the state, 32 columns each
+constexpr int NOWN = 4;               // owner waves per state: 32 columns each
 constexpr int NHELP = 4;              // helper waves: the next chunk's operands
 static_assert(NHELP * 32 == KD, "each helper covers 32 channels in the chunk prologue");
-static_assert((NOWN + NHELP) * 64 == NT, "chunk kernel wave roles");
+// summaries kernel: owners of S (waves 0-3) and of the transition (4-7), helpers 8-11
+static_assert((2 * NOWN + NHELP) * 64 == kSummaryThreads, "summaries kernel wave roles");
+// carry kernel: owners 0-3, helpers 4-7
+static_assert((NOWN + NHELP) * 64 == kCarryThreads, "carry kernel wave roles");
 constexpr int KSPLIT = 4;             // owner k-steps before the T merge barrier
 constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 152;   // row stride (bf16) of token-major [32][128] tiles (conflict-free row and transposed reads)
@@ -210,31 +212,31 @@ struct ChunkSmem {
   float beta[CH];
 };
 
+// What one workgroup of the summaries launch does with its fragment.
 struct Work {
-  int mode;         // Mode, or -1 for none
-  bool from_carry;  // FWD starting from carry_in[seg]
-  bool zero_a;      // write a zero transition and stop
+  int mode;         // kModeFwd, kModeSumS, or -1 for nothing
+  bool phi;         // also build the segment's transition (waves NOWN..2NOWN-1)
+  bool zero_a;      // write a zero transition (a sequence starts in the segment)
 };
 
-__device__ __forceinline__ Work decode_work(const ChunkParams& p, int32_t flags, int32_t seg) {
+// Summaries launch: a fragment that starts at a sequence start runs the
+// forward (o, final state, and B_r if it ends the segment); a carried fragment
+// that ends its segment builds B_r from zero and, from the identity, A_r.  The
+// transition of a segment whose last fragment is not carried is zero (the
+// reset's linear part).  Carried fragments that end inside the segment are left
+// to the carry launch.
+__device__ __forceinline__ Work decode_summary(const ChunkParams& p, int32_t flags, int32_t seg) {
   Work w{-1, false, false};
-  const int role = blockIdx.z;
-  if (p.pass == 1) {
-    if (role == 0) {
-      if (flags & kFragCarried) {
-        if (flags & kFragSegLast) w.mode = kModeSumS;
-      } else {
-        w.mode = kModeFwd;
-      }
-    } else if (flags & kFragSegLast) {
-      if (p.plan[p.L.seg_transition_live + seg]) w.mode = kModeSumPhi;
+  const bool seg_last = (flags & kFragSegLast) != 0;
+  if (flags & kFragCarried) {
+    if (seg_last) {
+      w.mode = kModeSumS;
+      if (p.plan[p.L.seg_transition_live + seg]) w.phi = true;
       else w.zero_a = true;
     }
   } else {
-    if (flags & kFragCarried) {
-      w.mode = kModeFwd;
-      w.from_carry = true;
-    }
+    w.mode = kModeFwd;
+    w.zero_a = seg_last;
   }
   return w;
 }
@@ -265,6 +267,20 @@ __device__ __forceinline__ void tile_to_b_split(const f32x16& t, bf16x8 bh[2], b
     float x[8];
     tile_rows_to_b(t, s, x);
     split8(x, bh[s], bl[s]);
+  }
+}
+
+// Barrier sequence of an owner slot with no state to keep (a forward fragment
+// in the summaries launch needs one state block only): the same barriers as
+// owner_fragment, nothing else.
+__device__ __forceinline__ void idle_owner(const int32_t beg, const int32_t end) {
+  const int nc = (end - beg + CH - 1) / CH;
+  for (int it = 0; it <= nc; ++it) {
+    block_sync();
+    if (it < nc) {
+      block_sync();
+      block_sync();
+    }
   }
 }
 
@@ -302,18 +318,17 @@ __device__ __forceinline__ bf16x8 join8(const s16x4 a, const s16x4 b) {
 //   step 2  R *= fac; Y = Kr R, O = Qr R, first KSPLIT k-steps
 //   step 3  the remaining k-steps
 template <int MODE>
-__device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& sm, const int32_t flags,
-                                               const int32_t seg, const int32_t seq, const int32_t beg,
-                                               const int32_t end, const bool from_carry) {
+__device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& sm, const int ow,
+                                               const int32_t flags, const int32_t seg, const int32_t seq,
+                                               const int32_t beg, const int32_t end, const bool from_carry) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
   const int h = blockIdx.y;
   const int H = p.H;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31;
   const int lh = lane >> 5;
-  const int col = 32 * wave + ln;
+  const int col = 32 * ow + ln;
   const int nc = (end - beg + CH - 1) / CH;
   const int o_row = H * VD * 4;   // one token of o (bytes)
 
@@ -368,7 +383,7 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
       const int lane_s = opaque(lane);
       const int ln = lane_s & 31;
       const int lh = lane_s >> 5;
-      const int col = 32 * wave + ln;
+      const int col = 32 * ow + ln;
       // transposed-read coordinates: group gq of 16 lanes, source index sq
       const int gq = lane_s >> 4;
       const int sq = lane_s & 15;
@@ -383,7 +398,7 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
         if (use_v) {
           // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
           const s16x4 v4 = lds_read_tr(
-              &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * wave + 16 * (gq & 1) + 4 * (sq & 3)]);
+              &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
         }
@@ -537,13 +552,12 @@ __device__ __forceinline__ void scan_stage(float (&G)[2][8]) {
 // 16 + l%16 (16-byte loads; the 16 lanes of a row hold one channel octet for
 // 16 consecutive tokens, so the gate prefix is a scan across the row).
 template <int MODE>
-__device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int32_t beg,
-                                                const int32_t end) {
+__device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int hw,
+                                                const int32_t beg, const int32_t end) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
   const int h = blockIdx.y;
   const int H = p.H;
-  const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - NOWN;
   const int lane = threadIdx.x & 63;
   const int tk = lane & 15;                    // tokens tk and 16 + tk
   const int c8 = 32 * hw + 8 * (lane >> 4);    // first of this lane's eight channels
@@ -824,11 +838,15 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
 }
 
 // One workgroup runs one fragment (a run of tokens of one sequence inside one
-// segment) of one head, chunk after chunk, as a two-stage pipeline: NOWN owner
-// waves hold the state in registers and apply chunk n-1 while NHELP helper
-// waves build chunk n's operands in LDS (see owner_fragment and
-// helper_fragment); three barriers per chunk.
-__global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
+// segment) of one head, chunk after chunk, as a two-stage pipeline: owner waves
+// hold the state in registers and apply chunk n-1 while NHELP helper waves build
+// chunk n's operands in LDS (see owner_fragment and helper_fragment); three
+// barriers per chunk.
+//
+// Summaries launch: waves 0-3 own S (forward or zero-start update), waves 4-7
+// own the transition Phi when the fragment needs one, waves 8-11 are helpers;
+// S and Phi share every operand the helpers build.
+__global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ ChunkSmem sm;
   const int f = blockIdx.x;
   const int h = blockIdx.y;
@@ -840,25 +858,46 @@ __global__ void __launch_bounds__(NT, 1) kda_chunk_kernel(ChunkParams p) {
   const int32_t seq = p.plan[p.L.frag_seq + f];
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
-  const Work work = decode_work(p, flags, seg);
+  const Work work = decode_summary(p, flags, seg);
+  if (work.mode < 0) return;
 
-  if (work.zero_a) {
-    float4* dst = reinterpret_cast<float4*>(p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD);
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = tid; i < KD * KD / 4; i += NT) dst[i] = z;
-    return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < NOWN) {
+    if (work.mode == kModeFwd) owner_fragment<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, false);
+    else owner_fragment<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, false);
+  } else if (wave < 2 * NOWN) {
+    if (work.phi) {
+      owner_fragment<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, false);
+    } else {
+      if (work.zero_a) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int i = tid - NOWN * 64; i < KD * KD / 4; i += NOWN * 64) dst[i] = z;
+      }
+      idle_owner(beg, end);
+    }
+  } else {
+    if (work.mode == kModeFwd) helper_fragment<kModeFwd>(p, sm, wave - 2 * NOWN, beg, end);
+    else helper_fragment<kModeSumS>(p, sm, wave - 2 * NOWN, beg, end);
   }
-  const bool owner = __builtin_amdgcn_readfirstlane(tid >> 6) < NOWN;
-  if (work.mode == kModeFwd) {
-    if (owner) owner_fragment<kModeFwd>(p, sm, flags, seg, seq, beg, end, work.from_carry);
-    else helper_fragment<kModeFwd>(p, sm, beg, end);
-  } else if (work.mode == kModeSumS) {
-    if (owner) owner_fragment<kModeSumS>(p, sm, flags, seg, seq, beg, end, false);
-    else helper_fragment<kModeSumS>(p, sm, beg, end);
-  } else if (work.mode == kModeSumPhi) {
-    if (owner) owner_fragment<kModeSumPhi>(p, sm, flags, seg, seq, beg, end, false);
-    else helper_fragment<kModeSumPhi>(p, sm, beg, end);
-  }
+}
+
+// Carry launch: each carried fragment runs again from its carry-in C_r with the
+// forward body (o and, where a sequence ends, the final state); waves 0-3 own
+// the state, waves 4-7 are helpers.
+__global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams p) {
+  __shared__ ChunkSmem sm;
+  const int f = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t flags = p.plan[p.L.frag_flags + f];
+  if (!(flags & kFragCarried)) return;
+  const int32_t seg = p.plan[p.L.frag_seg + f];
+  const int32_t seq = p.plan[p.L.frag_seq + f];
+  const int32_t beg = p.plan[p.L.frag_begin + f];
+  const int32_t end = p.plan[p.L.frag_end + f];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < NOWN) owner_fragment<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, true);
+  else helper_fragment<kModeFwd>(p, sm, wave - NOWN, beg, end);
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of
