@@ -169,27 +169,33 @@ __device__ __forceinline__ void tile_rows_to_b(const f32x16& t, int s, float out
 }
 
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even), x0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+  const f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 // Split two floats into packed (hi, lo) bf16 pairs: x = hi + lo to ~16 bits.
+// hi is unpacked with integer ops (bf16 is the upper half of a float), so a
+// pair costs two conversions, two bit operations and two subtractions.
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  bf16x2 h;
-  h[0] = static_cast<bf16>(x0);
-  h[1] = static_cast<bf16>(x1);
-  bf16x2 l;
-  l[0] = static_cast<bf16>(x0 - static_cast<float>(h[0]));
-  l[1] = static_cast<bf16>(x1 - static_cast<float>(h[1]));
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
+  hi = pack_bf16(x0, x1);
+  lo = pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 a, b;
-    split(x[e], a, b);
-    hi[e] = a;
-    lo[e] = b;
+  for (int w = 0; w < 4; ++w) {
+    uint32_t a, b;
+    split_pair(x[2 * w], x[2 * w + 1], a, b);
+    h[w] = a;
+    l[w] = b;
   }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Shared memory of one workgroup (about 115 KB).  Helpers write the operands
@@ -197,7 +203,7 @@ __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo)
 // the same step as helpers write the next chunk's, are double-buffered; every
 // other buffer is written only after its last reader of the previous chunk has
 // passed a barrier.
-struct ChunkSmem {
+struct alignas(16) ChunkSmem {
   bf16 kr_h[CH * NS], kr_l[CH * NS];          // Kr = k e^{G-a}, token-major
   bf16 qr_h[CH * NS], qr_l[CH * NS];          // Qr = q e^{G-a}, token-major
   bf16 kc_h[2][CH * NS], kc_l[2][CH * NS];    // Kc = k e^{a-G}, token-major
@@ -377,85 +383,85 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
     }
   };
 
-  for (int it = 0; it <= nc; ++it) {
-    // ---- step 1: finish chunk it-1
-    if (it >= 1) {
-      const int lane_s = opaque(lane);
-      const int ln = lane_s & 31;
-      const int lh = lane_s >> 5;
-      const int col = 32 * ow + ln;
-      // transposed-read coordinates: group gq of 16 lanes, source index sq
-      const int gq = lane_s >> 4;
-      const int sq = lane_s & 15;
-      const int b = (it - 1) & 1;
-      const int c0 = beg + (it - 1) * CH;
-      const int n = min(CH, end - c0);
-      mfma_result_fence(Y);
-      f32x16 D;
+  // step 1: finish chunk it-1 (it >= 1)
+  auto finish = [&](const int it) __attribute__((always_inline)) {
+    const int lane_s = opaque(lane);
+    const int ln = lane_s & 31;
+    const int lh = lane_s >> 5;
+    const int col = 32 * ow + ln;
+    // transposed-read coordinates: group gq of 16 lanes, source index sq
+    const int gq = lane_s >> 4;
+    const int sq = lane_s & 15;
+    const int b = (it - 1) & 1;
+    const int c0 = beg + (it - 1) * CH;
+    const int n = min(CH, end - c0);
+    mfma_result_fence(Y);
+    f32x16 D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float vv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (use_v) {
-          // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
-          const s16x4 v4 = lds_read_tr(
-              &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
+    for (int r = 0; r < 4; ++r) {
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (use_v) {
+        // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
+        const s16x4 v4 = lds_read_tr(
+            &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
+        for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
       }
-      bf16x8 dh[2], dl[2];
-      tile_to_b_split(D, dh, dl);
-      f32x16 U = zero16();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
+    }
+    bf16x8 dh[2], dl[2];
+    tile_to_b_split(D, dh, dl);
+    f32x16 U = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int off = ln * TS + 16 * s + 8 * lh;
+      U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
+                dh[s], dl[s], U);
+    }
+    mfma_result_fence(U);
+    bf16x8 ubh[2], ubl[2];
+    tile_to_b_split(U, ubh, ubl);
+    if (fwd) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int off = ln * TS + 16 * s + 8 * lh;
-        U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
-                  dh[s], dl[s], U);
+        O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
+                  ubh[s], ubl[s], O);
       }
-      mfma_result_fence(U);
-      bf16x8 ubh[2], ubl[2];
-      tile_to_b_split(U, ubh, ubl);
-      if (fwd) {
+    }
+    // R += Kc^T U: the A operand (row = channel 32dt + l%32, k = token
+    // 16s + 8(l/32) + 0..7) is a column fragment of the token-major Kc
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int off = ln * TS + 16 * s + 8 * lh;
-          O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
-                    ubh[s], ubl[s], O);
-        }
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = (16 * s + 8 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
+        const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 4 * NS]));
+        const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 4 * NS]));
+        R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
       }
-      // R += Kc^T U: the A operand (row = channel 32dt + l%32, k = token
-      // 16s + 8(l/32) + 0..7) is a column fragment of the token-major Kc
+    }
+    if (fwd) {
+      mfma_result_fence(O);
+      // rows past the fragment's end fall outside the buffer and are dropped
+      const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
+                                                         (n - 1) * o_row + 4 * VD, kBufDword3);
+      const int o_voff = 4 * lh * o_row + 4 * col;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int off = (16 * s + 8 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
-          const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 4 * NS]));
-          const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 4 * NS]));
-          R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
-        }
-      }
-      if (fwd) {
-        mfma_result_fence(O);
-        // rows past the fragment's end fall outside the buffer and are dropped
-        const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
-                                                           (n - 1) * o_row + 4 * VD, kBufDword3);
-        const int o_voff = 4 * lh * o_row + 4 * col;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // (an element of an ext_vector goes through a scalar first:
-            // __builtin_bit_cast on the element reads element 0)
-            const float ov = O[4 * r + e];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
-          }
+        for (int e = 0; e < 4; ++e) {
+          // (an element of an ext_vector goes through a scalar first:
+          // __builtin_bit_cast on the element reads element 0)
+          const float ov = O[4 * r + e];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
         }
       }
     }
-    block_sync();
+  };
+  // steps 2 and 3: re-anchor R, then the products of chunk it (it < nc)
+  auto products = [&](const int it) __attribute__((always_inline)) {
     // ---- step 2: re-anchor R (each tile just before its first use), then
     // the products of chunk it.  Operand loads run one k-step ahead; the T
     // merge barrier splits the k-steps between steps 2 and 3.
@@ -466,35 +472,48 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
     mfma_result_fence(R[1]);
     mfma_result_fence(R[2]);
     mfma_result_fence(R[3]);
-    if (it < nc) {
-      Y = zero16();
-      O = zero16();
-      bf16x8 opa[2][4];
-      f32x4 fa[4];   // factors of the next tile to rescale
-      load_ops(opa[0], 0, ln2, lh2);
-      load_fac(fa, 0, lh2);
+    Y = zero16();
+    O = zero16();
+    bf16x8 opa[2][4];
+    f32x4 fa[4];   // factors of the next tile to rescale
+    load_ops(opa[0], 0, ln2, lh2);
+    load_fac(fa, 0, lh2);
 #pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], kk + 1, ln2, lh2);
-        if ((kk & 1) == 0) rescale(kk >> 1, fa);
-        if ((kk & 1) == 1 && kk + 1 < KD / 16) load_fac(fa, (kk + 1) >> 1, lh2);
-        float x[8];
-        tile_rows_to_b(R[kk >> 1], kk & 1, x);
-        bf16x8 bh, bl;
-        split8(x, bh, bl);
-        const bf16x8(&o)[4] = opa[kk & 1];
-        Y = mfma3(o[0], o[1], bh, bl, Y);
-        if (fwd) O = mfma3(o[2], o[3], bh, bl, O);
-        if (kk == KSPLIT - 1) block_sync();   // ---- step 3 from here
-      }
-      block_sync();
-    } else {
+    for (int kk = 0; kk < KD / 16; ++kk) {
+      if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], kk + 1, ln2, lh2);
+      if ((kk & 1) == 0) rescale(kk >> 1, fa);
+      if ((kk & 1) == 1 && kk + 1 < KD / 16) load_fac(fa, (kk + 1) >> 1, lh2);
+      float x[8];
+      tile_rows_to_b(R[kk >> 1], kk & 1, x);
+      bf16x8 bh, bl;
+      split8(x, bh, bl);
+      const bf16x8(&o)[4] = opa[kk & 1];
+      Y = mfma3(o[0], o[1], bh, bl, Y);
+      if (fwd) O = mfma3(o[2], o[3], bh, bl, O);
+      if (kk == KSPLIT - 1) block_sync();   // ---- step 3 from here
+    }
+    block_sync();
+  };
+
+  for (int it = 0; it < nc; ++it) {
+    if (it >= 1) finish(it);
+    block_sync();
+    products(it);
+  }
+  finish(nc);
+  block_sync();
+  {
+    // after the last chunk: fac = e^{G_C - a} turns R back into S
+    const int lh2 = opaque(lane) >> 5;
+    mfma_result_fence(R[0]);
+    mfma_result_fence(R[1]);
+    mfma_result_fence(R[2]);
+    mfma_result_fence(R[3]);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        f32x4 f[4];
-        load_fac(f, dt, lh2);
-        rescale(dt, f);
-      }
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 f[4];
+      load_fac(f, dt, lh2);
+      rescale(dt, f);
     }
   }
 
