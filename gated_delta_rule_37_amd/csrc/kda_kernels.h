@@ -12,7 +12,7 @@
 namespace kda {
 
 constexpr int kSummaryThreads = 768;  // kda_chunk_kernel (summaries launch): 12 waves
-constexpr int kCarryThreads = 512;    // kda_carry_kernel (carry launch): 8 waves
+constexpr int kCarryThreads = 768;    // kda_carry_kernel (carry launch): 12 waves
 constexpr int kComposeThreads = 256;  // kda_compose_kernel workgroup size
 constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
 

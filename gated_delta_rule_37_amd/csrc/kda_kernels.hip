@@ -46,12 +46,11 @@ constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
 constexpr int CH = 32;    // chunk length (tokens)
 constexpr int NOWN = 4;               // owner waves per state: 32 columns each
-constexpr int NHELP = 4;              // helper waves: the next chunk's operands
-static_assert(NHELP * 32 == KD, "each helper covers 32 channels in the chunk prologue");
+constexpr int NHELP_SUM = 4;          // helper waves of the summaries kernel
 // summaries kernel: owners of S (waves 0-3) and of the transition (4-7), helpers 8-11
-static_assert((2 * NOWN + NHELP) * 64 == kSummaryThreads, "summaries kernel wave roles");
+static_assert((2 * NOWN + NHELP_SUM) * 64 == kSummaryThreads, "summaries kernel wave roles");
 // carry kernel: owners 0-3, helpers 4-7
-static_assert((NOWN + NHELP) * 64 == kCarryThreads, "carry kernel wave roles");
+static_assert(3 * NOWN * 64 == kCarryThreads, "carry kernel: owners, operand helpers, T helpers");
 constexpr int KSPLIT = 4;             // owner k-steps before the T merge barrier
 constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 152;   // row stride (bf16) of token-major [32][128] tiles (conflict-free row and transposed reads)
@@ -123,6 +122,12 @@ __device__ __forceinline__ f32x4 zero4() {
 // wait states cover a 16-pass MFMA.
 __device__ __forceinline__ void mfma_result_fence(f32x4& t0, f32x4& t1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t0), "+v"(t1));
+}
+__device__ __forceinline__ void mfma_result_fence(f32x4& t) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t));
+}
+__device__ __forceinline__ void mfma_result_fence(f32x16& t0, f32x16& t1, f32x16& t2, f32x16& t3) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3));
 }
 __device__ __forceinline__ void mfma_result_fence(f32x16& t) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t));
@@ -210,9 +215,9 @@ struct alignas(16) ChunkSmem {
   bf16 vv[2][CH * NS];                        // V, token-major (exact)
   bf16 tb_h[CH * TS], tb_l[CH * TS];          // T diag(beta), [i][j]
   bf16 p_h[CH * TS], p_l[CH * TS];            // P, [i][j]
-  float an[CH * FS];                          // an[i][j] = A[i][j], j < i
-  float tt[CH * FS];                          // tt[c][i] = T[i][c] (diagonal blocks)
-  float tn[CH * FS];                          // tn[i][c] = T[i][c] (diagonal blocks)
+  float an[CH * FS];                          // A10 by rows, diagonal blocks transposed
+  float tt[CH * FS];                          // tt[c][i] = T00[i][c]
+  float tn[CH * FS];                          // tn[16 + i][16 + c] = T11[i][c]
   float xt[16 * XS];                          // X = A10 T00, stored xt[c][i]
   float fac[KD];                              // state rescale between two chunks
   float beta[CH];
@@ -275,6 +280,44 @@ __device__ __forceinline__ void tile_to_b_split(const f32x16& t, bf16x8 bh[2], b
     split8(x, bh[s], bl[s]);
   }
 }
+
+// k-slot order used with accumulator tiles as B operands.  A 32 x 32 tile t
+// (rows 16s .. 16s+15 of it feeding k-step s) becomes a B operand without any
+// cross-lane move when the k slot (l/32, j) of the MFMA stands for row
+// 16s + 4(l/32) + j (j < 4) or 16s + 8 + 4(l/32) + j - 4 (j >= 4): those are
+// the lane's own registers 8s + j and 8s + 4 + j - 4.  The dot product does
+// not depend on the order of k, so the A operand only has to take its k
+// columns in the same order: two 8-byte pieces, at columns 16s + 4(l/32) and
+// 16s + 8 + 4(l/32).
+__device__ __forceinline__ void tile_kslots(const f32x16& t, const int s, float out[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[j] = t[8 * s + j];
+    out[4 + j] = t[8 * s + 4 + j];
+  }
+}
+__device__ __forceinline__ void tile_kslots_split(const f32x16& t, bf16x8 bh[2], bf16x8 bl[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float x[8];
+    tile_kslots(t, s, x);
+    split8(x, bh[s], bl[s]);
+  }
+}
+// A operand in k-slot order from a row-major bf16 matrix: row + c and
+// row + c + 8 (c = 16s + 4(l/32) for k-step s), as two 8-byte reads (the
+// second address goes through opaque() so that the pair is not fused into one
+// ds_read2_b64, which takes four times as long on gfx950).
+__device__ __forceinline__ bf16x8 ld_kslots(const bf16* row, const int c) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(&row[c]);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(&row[opaque(c + 8)]);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Matrices whose columns only ever feed k-slot A operands (T diag(beta) and P,
+// columns = tokens) are stored with the columns in k-slot order, so that
+// the operand is one contiguous 16-byte read at 16s + 8(l/32): column t of
+// each 16-column group sits at position t with bits 2 and 3 swapped.
+__device__ __forceinline__ int kslot_col(const int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
 // Barrier sequence of an owner slot with no state to keep (a forward fragment
 // in the summaries launch needs one state block only): the same barriers as
@@ -410,8 +453,10 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
 #pragma unroll
       for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
     }
+    // D and U feed the products below as B operands in k-slot order (tokens):
+    // T diag(beta) and P are stored in that column order, Kc^T is read in it
     bf16x8 dh[2], dl[2];
-    tile_to_b_split(D, dh, dl);
+    tile_kslots_split(D, dh, dl);
     f32x16 U = zero16();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -421,7 +466,7 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
     }
     mfma_result_fence(U);
     bf16x8 ubh[2], ubl[2];
-    tile_to_b_split(U, ubh, ubl);
+    tile_kslots_split(U, ubh, ubl);
     if (fwd) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -430,15 +475,16 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
                   ubh[s], ubl[s], O);
       }
     }
-    // R += Kc^T U: the A operand (row = channel 32dt + l%32, k = token
-    // 16s + 8(l/32) + 0..7) is a column fragment of the token-major Kc
+    // R += Kc^T U: the A operand (row = channel 32dt + l%32, k slots = tokens
+    // 16s + 4(l/32) + 0..3 and 16s + 8 + 4(l/32) + 0..3) is read as column
+    // fragments of the token-major Kc
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int off = (16 * s + 8 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
-        const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 4 * NS]));
-        const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 4 * NS]));
+        const int off = (16 * s + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
+        const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 8 * NS]));
+        const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 8 * NS]));
         R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
       }
     }
@@ -546,48 +592,224 @@ __device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& 
   }
 }
 
-// One step of an inclusive scan across each 16-lane row for sixteen values:
-// x += (x of the lane CTRL's row shift away; zero past the row's start).
-template <int CTRL>
-__device__ __forceinline__ void scan_stage(float (&G)[2][8]) {
+// One step of an inclusive scan across each 16-lane row: x += (x of the lane
+// CTRL's row shift away; zero past the row's start).
+template <int CTRL, int TPL>
+__device__ __forceinline__ void scan_stage(float (&G)[TPL][8]) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < TPL; ++j)
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       G[j][c] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G[j][c]), CTRL, 0xf, 0xf, true));
 }
 
+// 16 x 16 tile of X Kc^T over the 128 channels: rows 16rb .. 16rb+15 of X
+// (Kr or Qr) against rows 16ct .. 16ct+15 of Kc, split operands.  Lane l
+// receives rows 16rb + 4(l/16) + e, e = 0..3, of column 16ct + l%16.
+__device__ __forceinline__ f32x4 tile16(const bf16* xh, const bf16* xl, const bf16* ch, const bf16* cl,
+                                        const int rb, const int ct, const int lm, const int lg) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kk = 0; kk < KD / 32; ++kk) {
+    const int aoff = (16 * rb + lm) * NS + 32 * kk + 8 * lg;
+    const int boff = (16 * ct + lm) * NS + 32 * kk + 8 * lg;
+    acc = mfma16x3(*reinterpret_cast<const bf16x8*>(&xh[aoff]), *reinterpret_cast<const bf16x8*>(&xl[aoff]),
+                   *reinterpret_cast<const bf16x8*>(&ch[boff]), *reinterpret_cast<const bf16x8*>(&cl[boff]), acc);
+  }
+  mfma_result_fence(acc);
+  return acc;
+}
+
+// Diagonal block rb of A = beta o (Kr Kc^T) and the inverse of that block of
+// I + A.  The block goes to LDS transposed (an[16rb + j][16rb + i] = A_ij,
+// one 16-byte store per lane), and the wave reads its own columns back
+// without a barrier (its LDS accesses complete in order).  Lanes c = 0..15
+// then solve for one line of the inverse each (lanes 16..63 repeat them):
+//   rb = 0: column c of T00 by forward substitution, right-looking
+//           (x_j final, then x_i -= A_ij x_j for i > j), stored by column:
+//           tt[c][i] = T00[i][c];
+//   rb = 1: row c of T11, i.e. column c of (I + A11^T)^{-1}, by back
+//           substitution, y_i = [i == c] - sum_{j>i} A_ji y_j, stored by row:
+//           tn[16 + c][16 + i] = T11[c][i].
+// The merge reads T00 by columns and T11 by rows only.
+__device__ __forceinline__ void a_diag_solve(const bf16* krh, const bf16* krl, const bf16* kch, const bf16* kcl,
+                                             const float* beta, float* an, float* tt, float* tn, const int rb,
+                                             const int lane_s) {
+  const int lm = lane_s & 15;
+  const int lg = lane_s >> 4;
+  const f32x4 acc = tile16(krh, krl, kch, kcl, rb, rb, lm, lg);
+  const f32x4 brow = ld4(&beta[16 * rb + 4 * lg]);
+  const int base = 16 * rb;
+  {
+    // lane (lg, lm) holds A[4lg + e][lm], e = 0..3: column lm, four rows
+    f32x4 col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) col[e] = (lm < 4 * lg + e) ? brow[e] * acc[e] : 0.f;
+    st4(&an[(base + lm) * FS + base + 4 * lg], col);
+  }
+  wave_lds_order();
+  const int c = lm;
+  float x[16];
+  if (rb == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      // column j of A, rows j+1 .. 15
+#pragma unroll
+      for (int q4 = (j + 1) / 4; q4 < 4; ++q4) {
+        const f32x4 a = ld4(&an[(base + j) * FS + base + 4 * q4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e > j) x[4 * q4 + e] -= a[e] * x[j];
+      }
+    }
+    if (lane_s < 16) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        st4(&tt[c * FS + 4 * q4], f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
+    }
+  } else {
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      float yi = (i == c) ? 1.f : 0.f;
+      // column i of A, rows i+1 .. 15
+#pragma unroll
+      for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+        const f32x4 a = ld4(&an[(base + i) * FS + base + 4 * q4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e > i) yi -= a[e] * x[4 * q4 + e];
+      }
+      x[i] = yi;
+    }
+    if (lane_s < 16) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        st4(&tn[(base + c) * FS + base + 4 * q4], f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
+    }
+  }
+}
+
+// A10 = beta o (Kr Kc^T), rows 16..31 and columns 0..15, into an.
+__device__ __forceinline__ void a_offdiag(const bf16* krh, const bf16* krl, const bf16* kch, const bf16* kcl,
+                                          const float* beta, float* an, const int lane_s) {
+  const int lm = lane_s & 15;
+  const int lg = lane_s >> 4;
+  const f32x4 acc = tile16(krh, krl, kch, kcl, 1, 0, lm, lg);
+  const f32x4 brow = ld4(&beta[16 + 4 * lg]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) an[(16 + 4 * lg + e) * FS + lm] = brow[e] * acc[e];
+}
+
+// One 16 x 16 block (rbp, ctp) of P, ctp <= rbp, as split bf16 (entries above
+// the diagonal zero; columns in k-slot order); block (0, 0) also writes the
+// zero block (0, 1).
+__device__ __forceinline__ void p_store(const f32x4& acc, const int rbp, const int ctp, bf16* ph, bf16* pl,
+                                        const int lane_s) {
+  const int lm = lane_s & 15;
+  const int lg = lane_s >> 4;
+  const int j = 16 * ctp + lm;
+  const int jp = 16 * ctp + kslot_col(lm);   // stored column of j
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 16 * rbp + 4 * lg + e;
+    bf16 hh, ll;
+    split(j <= i ? acc[e] : 0.f, hh, ll);
+    ph[i * TS + jp] = hh;
+    pl[i * TS + jp] = ll;
+    if (rbp == 0) {
+      ph[i * TS + 16 + kslot_col(lm)] = static_cast<bf16>(0.f);
+      pl[i * TS + 16 + kslot_col(lm)] = static_cast<bf16>(0.f);
+    }
+  }
+}
+
+// T10 = -T11 A10 T00 and T diag(beta) as split bf16 (columns in k-slot
+// order), for the columns
+// tc = 4q .. 4q+3 (q = 0..3), lane (row ti, column tc); X = A10 T00 goes
+// through LDS inside the wave, which needs no barrier.
+__device__ __forceinline__ void t_merge(const float* an, const float* tt, const float* tn, float* xt,
+                                        const float* beta, bf16* tbh, bf16* tbl, const int q, const int lane_s) {
+  const int ti = lane_s & 15;
+  const int tc = 4 * q + (lane_s >> 4);
+  f32x4 u[4], w[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    u[q4] = ld4(&an[(16 + ti) * FS + 4 * q4]);   // A10[ti, :]
+    w[q4] = ld4(&tt[tc * FS + 4 * q4]);          // T00[:, tc]
+  }
+  float xs = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    xs += u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
+  xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
+  const float t00 = tt[tc * FS + ti];               // T00[ti][tc]
+  const float t11 = tn[(16 + ti) * FS + 16 + tc];    // T11[ti][tc]
+  const float b0 = beta[tc];
+  const float b1 = beta[16 + tc];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) u[q4] = ld4(&tn[(16 + ti) * FS + 16 + 4 * q4]);   // T11[ti, :]
+  wave_lds_order();
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) w[q4] = ld4(&xt[tc * XS + 4 * q4]);   // X[:, tc]
+  float t10 = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    t10 -= u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
+  const int cp = kslot_col(tc);   // stored column of tc (and of 16 + tc)
+  bf16 hh, ll;
+  split(t00 * b0, hh, ll);
+  tbh[ti * TS + cp] = hh;
+  tbl[ti * TS + cp] = ll;
+  split(t11 * b1, hh, ll);
+  tbh[(16 + ti) * TS + 16 + cp] = hh;
+  tbl[(16 + ti) * TS + 16 + cp] = ll;
+  split(t10 * b0, hh, ll);
+  tbh[(16 + ti) * TS + cp] = hh;
+  tbl[(16 + ti) * TS + cp] = ll;
+  tbh[ti * TS + 16 + cp] = static_cast<bf16>(0.f);
+  tbl[ti * TS + 16 + cp] = static_cast<bf16>(0.f);
+}
+
 // ---------------------------------------------------------------------------
-// Helper waves (NOWN .. NOWN+NHELP-1), helper index hw: chunk it's operands
-// while the owners finish chunk it-1.
+// Helper waves (NH of them, index hw): chunk it's operands while the owners
+// finish chunk it-1.
 //   step 1  land the prefetched inputs (issued one iteration earlier), gate
 //           prefix, anchor a (token 15), G_C; Kr, Qr, Kc, V (token-major),
 //           beta and the owners' rescale fac; issue the next chunk's loads
-//   step 2  A = beta o (Kr Kc^T) by 16-row blocks (hw 0, 1), each followed by
-//           the inverse of its diagonal block of I + A; P = Qr Kc^T (hw 2, 3)
+//   step 2  16 x 16 tile jobs: the two diagonal blocks of A = beta o (Kr Kc^T),
+//           each followed by the inverse of its block of I + A; the block A10;
+//           the three blocks of P = Qr Kc^T on or below the diagonal
 //   step 3  T10 = -T11 A10 T00 and T diag(beta), four columns per helper
-// Thread layout of step 1: helper hw covers the channels [32hw, 32hw + 32);
-// lane l takes the eight channels 32hw + 8(l/16) .. +7 of the tokens l%16 and
-// 16 + l%16 (16-byte loads; the 16 lanes of a row hold one channel octet for
-// 16 consecutive tokens, so the gate prefix is a scan across the row).
-template <int MODE>
+//           (helpers 0..3)
+// Thread layout of step 1: helper hw covers the channels [CPH hw, CPH hw +
+// CPH), CPH = 128 / NH.  Lane l loads one channel octet per token (16-byte
+// loads) and the 16 lanes of a DPP row hold 16 consecutive tokens of one
+// octet, so the gate prefix is a scan across the row:
+//   NH = 4: octet l/16, tokens l%16 and 16 + l%16 (two per lane)
+//   NH = 8: octet l/32, token l%32 (rows 2q and 2q+1 carry tokens 0..15 and
+//           16..31 of octet q)
+template <int MODE, int NH>
 __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int hw,
                                                 const int32_t beg, const int32_t end) {
+  static_assert(NH == 4 || NH == 8, "helper layouts");
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
+  constexpr int TPL = NH == 4 ? 2 : 1;         // tokens per lane in step 1
+  constexpr int CPH = KD / NH;                 // channels per helper in step 1
   const int h = blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
-  const int tk = lane & 15;                    // tokens tk and 16 + tk
-  const int c8 = 32 * hw + 8 * (lane >> 4);    // first of this lane's eight channels
+  const int tk = NH == 4 ? (lane & 15) : (lane & 31);   // tokens tk + 16j, j < TPL
+  const int c8 = CPH * hw + 8 * (NH == 4 ? (lane >> 4) : (lane >> 5));
   const int nc = (end - beg + CH - 1) / CH;
   const int row_bytes = H * KD * 2;            // one token of q, k, g, v
   const int in_voff = tk * row_bytes + 2 * c8;
 
-  // raw BF16 of the chunk being prefetched (two tokens x eight channels per
+  // raw BF16 of the chunk being prefetched (TPL tokens x eight channels per
   // tensor); loads past the fragment's last token return zero
-  typedef uint32_t u32x4 __attribute__((vector_size(16)));
-  u32x4 rk[2], rg[2], rq[2], rv[2];
+  u32x4 rk[TPL], rg[TPL], rq[TPL], rv[TPL];
   uint32_t rb = 0u;   // beta's raw bits
   // Branch-free: loads a mode does not need, and loads past the fragment, get
   // a zero-size buffer (they return zero and touch no memory).
@@ -602,7 +824,7 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
     const auto rsv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, use_v ? nrec : 0, kBufDword3);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TPL; ++j) {
       const int off = in_voff + 16 * j * row_bytes;
       rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
       rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
@@ -622,14 +844,13 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
 #pragma unroll
   for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
 
-  for (int it = 0; it <= nc; ++it) {
+  for (int it = 0; it < nc; ++it) {
     // ---- step 1: operands of chunk it, and the owners' rescale
-    if (it < nc) {
+    {
       const int b = it & 1;
-      float kf[2][8], qf[2][8], G[2][8];
-      u32x4 vcur[2];
+      float kf[TPL][8], qf[TPL][8], G[TPL][8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < TPL; ++j) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           kf[j][2 * w] = __uint_as_float(rk[j][w] << 16);
@@ -639,7 +860,7 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
           G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
           G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
         }
-        vcur[j] = rv[j];
+        if (use_v) st4(&sm.vv[b][(tk + 16 * j) * NS + c8], rv[j]);
       }
       if (hw == 0 && lane < CH) sm.beta[lane] = __uint_as_float(rb << 16);
       // consume the landed registers before the next loads overwrite them
@@ -647,23 +868,37 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
       fetch(beg + (it + 1) * CH);
 
       // inclusive gate prefix over the 16 tokens of each row (row_shr scan,
-      // stage by stage over all sixteen values so the DPP latencies overlap),
-      // then across the two halves: a = G at token 15, G_C = G at token 31
-      scan_stage<0x111>(G);   // row_shr:1
-      scan_stage<0x112>(G);   // row_shr:2
-      scan_stage<0x114>(G);   // row_shr:4
-      scan_stage<0x118>(G);   // row_shr:8
-      // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
+      // stage by stage over all values so the DPP latencies overlap), then
+      // across the two halves: a = G at token 15, G_C = G at token 31
+      scan_stage<0x111, TPL>(G);   // row_shr:1
+      scan_stage<0x112, TPL>(G);   // row_shr:2
+      scan_stage<0x114, TPL>(G);   // row_shr:4
+      scan_stage<0x118, TPL>(G);   // row_shr:8
       float a[8], gc[8];
+      if (NH == 4) {
+        // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
-        gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[1][c]), 0x1F0));
-      }
+        for (int c = 0; c < 8; ++c) {
+          a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
+          gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[TPL - 1][c]), 0x1F0));
+        }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        G[1][c] += a[c];
-        gc[c] += a[c];
+        for (int c = 0; c < 8; ++c) {
+          G[TPL - 1][c] += a[c];
+          gc[c] += a[c];
+        }
+      } else {
+        // rows 1 and 3 (tokens 16..31) add the totals of rows 0 and 2
+        // (row_bcast:15), then a and G_C are lanes 15 and 31 of each half wave
+        // (swizzle: or 0x0f, or 0x1f)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          G[0][c] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G[0][c]), 0x142, 0xa, 0xf, false));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1E0));
+          gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x3E0));
+        }
       }
       if (tk == 0) {
         float fv[8];
@@ -677,8 +912,7 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
 
       // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, Qr = q e^{G-a}
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = 16 * j + tk;
+      for (int j = 0; j < TPL; ++j) {
         uint32_t krh[4], krl[4], kch[4], kcl[4], qrh[4], qrl[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -696,7 +930,7 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
           split_pair(kc[0], kc[1], kch[w], kcl[w]);
           if (fwd) split_pair(qr[0], qr[1], qrh[w], qrl[w]);
         }
-        const int off = i * NS + c8;
+        const int off = (tk + 16 * j) * NS + c8;
         st4(&sm.kr_h[off], u32x4{krh[0], krh[1], krh[2], krh[3]});
         st4(&sm.kr_l[off], u32x4{krl[0], krl[1], krl[2], krl[3]});
         st4(&sm.kc_h[b][off], u32x4{kch[0], kch[1], kch[2], kch[3]});
@@ -705,160 +939,457 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
           st4(&sm.qr_h[off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
           st4(&sm.qr_l[off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
         }
-        if (use_v) {
-          st4(&sm.vv[b][off], u32x4{vcur[j][0], vcur[j][1], vcur[j][2], vcur[j][3]});
-        }
       }
-    } else if (tk == 0) {
-      // after the last chunk: R *= e^{G_C - a} turns R back into S
-      float fv[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
-      st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
-      st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
     }
     block_sync();
-    if (it == nc) break;
 
-    // ---- step 2: A (hw 0, 1) with the diagonal blocks of T; P (hw 2, 3)
-    if (hw < 2 || fwd) {
+    // ---- step 2: tile jobs.  Diagonal blocks of A and T: helpers 0 and 1;
+    // A10: helper 2; P (forward only): P00 and the zero block above it, P10,
+    // P11 on helpers 3, 4, 5 (NH = 8) or helpers 2, 3, 3 (NH = 4).
+    {
       const int b = it & 1;
       const int lane_s = opaque(lane);
-      const int lm = lane_s & 15;             // 16x16x32 MFMA: row/column index
-      const int lg = lane_s >> 4;             // 16x16x32 MFMA: k-group / row group
-      const int rb = hw & 1;                  // row block: rows 16rb .. 16rb+15
-      const bool is_a = hw < 2;
-      const bf16* xh = is_a ? sm.kr_h : sm.qr_h;
-      const bf16* xl = is_a ? sm.kr_l : sm.qr_l;
-      f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int kk = 0; kk < KD / 32; ++kk) {
-        const int aoff = (16 * rb + lm) * NS + 32 * kk + 8 * lg;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&xh[aoff]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&xl[aoff]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          if (ct > rb) continue;
-          const int boff = (16 * ct + lm) * NS + 32 * kk + 8 * lg;
-          acc[ct] = mfma16x3(ah, al, *reinterpret_cast<const bf16x8*>(&sm.kc_h[b][boff]),
-                             *reinterpret_cast<const bf16x8*>(&sm.kc_l[b][boff]), acc[ct]);
-        }
-      }
-      mfma_result_fence(acc[0], acc[1]);
-      // tile ct holds rows i = 16rb + 4lg + e of column j = 16ct + lm
-      if (!is_a) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int j = 16 * ct + lm;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * rb + 4 * lg + e;
-            bf16 hh, ll;
-            split((ct <= rb && j <= i) ? acc[ct][e] : 0.f, hh, ll);
-            sm.p_h[i * TS + j] = hh;
-            sm.p_l[i * TS + j] = ll;
-          }
-        }
-      } else {
-        const f32x4 brow = ld4(&sm.beta[16 * rb + 4 * lg]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          if (ct > rb) continue;
-          const int j = 16 * ct + lm;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * rb + 4 * lg + e;
-            sm.an[i * FS + j] = (j < i) ? brow[e] * acc[ct][e] : 0.f;
-          }
-        }
-        // Diagonal block rb of T = (I + A)^{-1} from this wave's own A rows
-        // (the wave's LDS accesses complete in order): every lane loads the
-        // block's strictly lower part first, then lane c computes column c row
-        // by row, x_i = [i == c] - sum_{j<i} A_ij x_j (rows above c come out
-        // zero).  Lanes 16..63 repeat lanes 0..15's work.
-        wave_lds_order();
-        const int base = 16 * rb;
-        f32x4 arow[16][4];
-#pragma unroll
-        for (int i = 1; i < 16; ++i)
-#pragma unroll
-          for (int q4 = 0; q4 < (i + 3) / 4; ++q4)
-            arow[i][q4] = ld4(&sm.an[(base + i) * FS + base + 4 * q4]);
-        const int c = lm;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc_i = (i == c) ? 1.f : 0.f;
-#pragma unroll
-          for (int jj = 0; jj < i; ++jj) {
-            acc_i -= arow[i][jj >> 2][jj & 3] * x[jj];
-          }
-          x[i] = acc_i;
-        }
-        if (lane_s < 16) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            st4(&sm.tt[(base + c) * FS + base + 4 * q4], f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sm.tn[(base + i) * FS + base + c] = x[i];
+      const int lm = lane_s & 15;
+      const int lg = lane_s >> 4;
+      auto p_tile = [&](const int rbp, const int ctp) __attribute__((always_inline)) {
+        p_store(tile16(sm.qr_h, sm.qr_l, sm.kc_h[b], sm.kc_l[b], rbp, ctp, lm, lg), rbp, ctp, sm.p_h, sm.p_l,
+                lane_s);
+      };
+      if (hw < 2) {
+        a_diag_solve(sm.kr_h, sm.kr_l, sm.kc_h[b], sm.kc_l[b], sm.beta, sm.an, sm.tt, sm.tn, hw, lane_s);
+      } else if (hw == 2) {
+        a_offdiag(sm.kr_h, sm.kr_l, sm.kc_h[b], sm.kc_l[b], sm.beta, sm.an, lane_s);
+        if (NH == 4 && fwd) p_tile(0, 0);
+      } else if (fwd) {
+        if (NH == 4) {
+          p_tile(1, 0);
+          p_tile(1, 1);
+        } else if (hw < 6) {
+          const int q = hw - 3;   // P00, P10, P11
+          p_tile(q == 0 ? 0 : 1, q == 2 ? 1 : 0);
         }
       }
     }
     block_sync();
 
-    // ---- step 3: T10 = -T11 A10 T00 and T diag(beta).  Helper hw takes the
-    // columns tc = 4hw .. 4hw+3, lane (row ti, column tc); X = A10 T00 goes
-    // through LDS inside the wave, which needs no barrier.
-    {
-      const int lane_s = opaque(lane);
-      const int ti = lane_s & 15;
-      const int tc = 4 * hw + (lane_s >> 4);
-      f32x4 u[4], w[4];
+    // ---- step 3: T10 = -T11 A10 T00 and T diag(beta), helpers 0..3
+    if (hw < 4) t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta, sm.tb_h, sm.tb_l, hw, opaque(lane));
+    block_sync();
+  }
+
+  // after the last chunk: R *= e^{G_C - a} turns R back into S
+  if (tk == 0) {
+    float fv[8];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u[q4] = ld4(&sm.an[(16 + ti) * FS + 4 * q4]);   // A10[ti, :]
-        w[q4] = ld4(&sm.tt[tc * FS + 4 * q4]);          // T00[:, tc]
+    for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
+    st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+    st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+  }
+  block_sync();
+}
+
+// ===========================================================================
+// Carry launch: a two-step pipeline with three wave roles, so that the
+// operands and the UT transform of later chunks are built while the owners
+// work on the current one.
+//
+//   owners (waves 0-3)           step 2n: products of chunk n
+//                                step 2n+1: finish chunk n
+//   operand helpers (waves 4-7)  steps 2m-3, 2m-2: operands of chunk m
+//   T helpers (waves 8-11)       steps 2m-1, 2m: A, T diag(beta), P of chunk m
+//
+// A fragment of nc chunks takes the steps -3 .. 2nc-1, each ending with a
+// workgroup barrier (every role executes 2nc + 3 of them).  Kr, Qr, Kc, V,
+// fac and beta are double-buffered by chunk parity; T diag(beta), P and the
+// solve scratch are single.  Who writes what, and when (m = chunk):
+//   Kr, Qr, fac, beta (m)  step 2m-3   last readers of chunk m-2: step 2m-4
+//   Kc, V (m)              step 2m-2   last reader of chunk m-2:  step 2m-3
+//   an, tt, tn (m)         step 2m-1   last reader of chunk m-1:  step 2m-2
+//   T diag(beta), P (m)    step 2m     last reader of chunk m-1:  step 2m-1
+// ===========================================================================
+struct alignas(16) PipeSmem {
+  bf16 kr_h[2][CH * NS], kr_l[2][CH * NS];    // Kr = k e^{G-a}, token-major
+  bf16 qr_h[2][CH * NS], qr_l[2][CH * NS];    // Qr = q e^{G-a}, token-major
+  bf16 kc_h[2][CH * NS], kc_l[2][CH * NS];    // Kc = k e^{a-G}, token-major
+  bf16 vv[2][CH * NS];                        // V, token-major (exact)
+  bf16 tb_h[CH * TS], tb_l[CH * TS];          // T diag(beta), [i][j]
+  bf16 p_h[CH * TS], p_l[CH * TS];            // P, [i][j]
+  float an[CH * FS];                          // A10 by rows, diagonal blocks transposed
+  float tt[CH * FS];                          // tt[c][i] = T00[i][c]
+  float tn[CH * FS];                          // tn[16 + i][16 + c] = T11[i][c]
+  float xt[16 * XS];                          // X = A10 T00, stored xt[c][i]
+  float fac[2][KD];                           // state rescale before chunk m
+  float beta[2][CH];
+};
+
+// Owner wave ow of the pipeline: the forward body (o and the final state) of
+// one fragment, from the carry-in or from zero.  R, Y, O as in owner_fragment.
+__device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, const int ow, const int32_t flags,
+                                           const int32_t seg, const int32_t seq, const int32_t beg,
+                                           const int32_t end, const bool from_carry) {
+  const int h = blockIdx.y;
+  const int H = p.H;
+  const int lane = threadIdx.x & 63;
+  const int lh = lane >> 5;
+  const int col = 32 * ow + (lane & 31);
+  const int nc = (end - beg + CH - 1) / CH;
+  const int o_row = H * VD * 4;   // one token of o (bytes)
+
+  f32x16 R[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
+  if (from_carry) {
+    const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
+  }
+  f32x16 Y = zero16(), O = zero16();
+
+  // A operands of k-step kk (channels 16kk .. 16kk+15, k-slot order)
+  auto load_ops = [&](bf16x8 (&o)[4], const int b, const int kk, const int ln, const int lh) {
+    const int row = ln * NS;
+    const int c = 16 * kk + 4 * lh;
+    o[0] = ld_kslots(&sm.kr_h[b][row], c);
+    o[1] = ld_kslots(&sm.kr_l[b][row], c);
+    o[2] = ld_kslots(&sm.qr_h[b][row], c);
+    o[3] = ld_kslots(&sm.qr_l[b][row], c);
+  };
+  auto load_fac = [&](f32x4 (&f)[4], const int b, const int dt, const int lh) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = ld4(&sm.fac[b][32 * dt + 8 * r + 4 * lh]);
+  };
+  auto rescale = [&](const int dt, const f32x4 (&f)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R[dt][4 * r + e] *= f[r][e];
+  };
+
+  // step 2n: Y = Kr R and O = Qr R (R already anchored for chunk n), operand
+  // loads one k-step ahead
+  auto products = [&](const int n) __attribute__((always_inline)) {
+    const int b = n & 1;
+    const int lane2 = opaque(lane);
+    const int ln2 = lane2 & 31;
+    const int lh2 = lane2 >> 5;
+    Y = zero16();
+    O = zero16();
+    bf16x8 opa[2][4];
+    load_ops(opa[0], b, 0, ln2, lh2);
+#pragma unroll
+    for (int kk = 0; kk < KD / 16; ++kk) {
+      if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], b, kk + 1, ln2, lh2);
+      float x[8];
+      tile_kslots(R[kk >> 1], kk & 1, x);
+      bf16x8 bh, bl;
+      split8(x, bh, bl);
+      const bf16x8(&o)[4] = opa[kk & 1];
+      Y = mfma3(o[0], o[1], bh, bl, Y);
+      O = mfma3(o[2], o[3], bh, bl, O);
+    }
+  };
+
+  // step 2n+1: D = V - Y, U = T diag(beta) D, O += P U, store o, R += Kc^T U
+  auto finish = [&](const int n) __attribute__((always_inline)) {
+    const int lane_s = opaque(lane);
+    const int ln = lane_s & 31;
+    const int lh = lane_s >> 5;
+    const int col = 32 * ow + ln;
+    const int gq = lane_s >> 4;   // transposed reads: group of 16 lanes
+    const int sq = lane_s & 15;   // and source index inside it
+    const int b = n & 1;
+    const int c0 = beg + n * CH;
+    const int nn = min(CH, end - c0);
+    mfma_result_fence(Y);
+    f32x16 D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
+      const s16x4 v4 = lds_read_tr(
+          &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) D[4 * r + e] = bf2f(static_cast<uint16_t>(v4[e])) - Y[4 * r + e];
+    }
+    // D and U feed the next products as B operands in k-slot order (tokens):
+    // T diag(beta) and P are stored in that column order, Kc^T is read in it
+    bf16x8 dh[2], dl[2];
+    tile_kslots_split(D, dh, dl);
+    f32x16 U = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int off = ln * TS + 16 * s + 8 * lh;   // columns stored in k-slot order
+      U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
+                dh[s], dl[s], U);
+    }
+    mfma_result_fence(U);
+    bf16x8 ubh[2], ubl[2];
+    tile_kslots_split(U, ubh, ubl);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int off = ln * TS + 16 * s + 8 * lh;
+      O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
+                ubh[s], ubl[s], O);
+    }
+    // R += Kc^T U: the A operand (row = channel 32dt + l%32, k slots = tokens
+    // 16s + 4(l/32) + 0..3 and 16s + 8 + 4(l/32) + 0..3) is read as column
+    // fragments of the token-major Kc
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = (16 * s + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
+        const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 8 * NS]));
+        const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 8 * NS]));
+        R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
       }
-      float xs = 0.f;
+    }
+    // re-anchor for chunk n+1 (after the last chunk: e^{G_C - a}, which
+    // leaves S itself)
+    mfma_result_fence(R[0], R[1], R[2], R[3]);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        xs += u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
-      sm.xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
-      const float t00 = sm.tn[ti * FS + tc];
-      const float t11 = sm.tn[(16 + ti) * FS + 16 + tc];
-      const float b0 = sm.beta[tc];
-      const float b1 = sm.beta[16 + tc];
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 f[4];
+      load_fac(f, (n + 1) & 1, dt, lh);
+      rescale(dt, f);
+    }
+    mfma_result_fence(O);
+    // rows past the fragment's end fall outside the buffer and are dropped
+    const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
+                                                       (nn - 1) * o_row + 4 * VD, kBufDword3);
+    const int o_voff = 4 * lh * o_row + 4 * col;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        u[q4] = ld4(&sm.tn[(16 + ti) * FS + 16 + 4 * q4]);   // T11[ti, :]
-      wave_lds_order();
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) w[q4] = ld4(&sm.xt[tc * XS + 4 * q4]);  // X[:, tc]
-      float t10 = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float ov = O[4 * r + e];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+      }
+    }
+  };
+
+  block_sync();   // steps -3 .. -1: the helpers fill the pipeline
+  block_sync();
+  block_sync();
+  {
+    // anchor the starting state for chunk 0
+    const int lh2 = opaque(lane) >> 5;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        t10 -= u[q4][0] * w[q4][0] + u[q4][1] * w[q4][1] + u[q4][2] * w[q4][2] + u[q4][3] * w[q4][3];
-      bf16 hh, ll;
-      split(t00 * b0, hh, ll);
-      sm.tb_h[ti * TS + tc] = hh;
-      sm.tb_l[ti * TS + tc] = ll;
-      split(t11 * b1, hh, ll);
-      sm.tb_h[(16 + ti) * TS + 16 + tc] = hh;
-      sm.tb_l[(16 + ti) * TS + 16 + tc] = ll;
-      split(t10 * b0, hh, ll);
-      sm.tb_h[(16 + ti) * TS + tc] = hh;
-      sm.tb_l[(16 + ti) * TS + tc] = ll;
-      sm.tb_h[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
-      sm.tb_l[ti * TS + 16 + tc] = static_cast<bf16>(0.f);
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 f[4];
+      load_fac(f, 0, dt, lh2);
+      rescale(dt, f);
+    }
+  }
+  for (int n = 0; n < nc; ++n) {
+    products(n);
+    block_sync();
+    finish(n);
+    block_sync();
+  }
+  if (flags & kFragSeqEnd) {
+    float* dst = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
+  }
+}
+
+// Operand helper oh (0..3) of the pipeline: channels [32oh, 32oh + 32); lane
+// l holds octet 32oh + 8(l/16) of the tokens l%16 and 16 + l%16 (the layout
+// of helper_fragment with four helpers).  Part 1 of chunk m (step 2m-3):
+// land the inputs loaded two steps earlier, issue the next chunk's loads, gate
+// prefix, fac, beta, Kr, Qr; Kc and V stay in registers until part 2 (step
+// 2m-2), when the owners are done with chunk m-2's.
+__device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm, const int oh, const int32_t beg,
+                                              const int32_t end) {
+  const int h = blockIdx.y;
+  const int H = p.H;
+  const int lane = threadIdx.x & 63;
+  const int tk = lane & 15;                    // tokens tk and 16 + tk
+  const int c8 = 32 * oh + 8 * (lane >> 4);    // first of this lane's eight channels
+  const int nc = (end - beg + CH - 1) / CH;
+  const int row_bytes = H * KD * 2;
+  const int in_voff = tk * row_bytes + 2 * c8;
+
+  u32x4 rk[2], rg[2], rq[2], rv[2];
+  uint32_t rb = 0u;
+  auto fetch = [&](int cs) {
+    const int nn = min(CH, end - cs);
+    const size_t base = (static_cast<size_t>(min(cs, end - 1)) * H + h) * KD;
+    const int nrec = nn > 0 ? (nn - 1) * row_bytes + KD * 2 : 0;
+    const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + base), 0, nrec, kBufDword3);
+    const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.g + base), 0, nrec, kBufDword3);
+    const auto rsq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, nrec, kBufDword3);
+    const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, nrec, kBufDword3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int off = in_voff + 16 * j * row_bytes;
+      rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
+      rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
+      rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
+      rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
+    }
+    const int nb = (oh == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
+    const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.beta + static_cast<size_t>(min(cs, end - 1)) * H + h), 0, nb, kBufDword3);
+    rb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane < CH ? lane * H * 2 : nb, 0, 0));
+  };
+  fetch(beg);
+
+  float dprev[8];   // (G_C - a) of the previous chunk, log2 units
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
+
+  for (int m = 0; m < nc; ++m) {
+    const int b = m & 1;
+    uint32_t kch[2][4], kcl[2][4];
+    u32x4 vkeep[2];
+    // ---- part 1 (step 2m-3)
+    {
+      float kf[2][8], qf[2][8], G[2][8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kf[j][2 * w] = __uint_as_float(rk[j][w] << 16);
+          kf[j][2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
+          qf[j][2 * w] = __uint_as_float(rq[j][w] << 16);
+          qf[j][2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
+          G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
+          G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
+        }
+        vkeep[j] = rv[j];
+      }
+      if (oh == 0 && lane < CH) sm.beta[b][lane] = __uint_as_float(rb << 16);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(beg + (m + 1) * CH);
+
+      scan_stage<0x111, 2>(G);   // row_shr:1
+      scan_stage<0x112, 2>(G);   // row_shr:2
+      scan_stage<0x114, 2>(G);   // row_shr:4
+      scan_stage<0x118, 2>(G);   // row_shr:8
+      float a[8], gc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
+        gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[1][c]), 0x1F0));
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        G[1][c] += a[c];
+        gc[c] += a[c];
+      }
+      if (tk == 0) {
+        float fv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(a[c] + dprev[c]);
+        st4(&sm.fac[b][c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+        st4(&sm.fac[b][c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dprev[c] = gc[c] - a[c];
+
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t krh[4], krl[4], qrh[4], qrl[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float kr[2], kc[2], qr[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float x = G[j][2 * w + c] - a[2 * w + c];
+            const float er = __builtin_amdgcn_exp2f(x);
+            const float ec = __builtin_amdgcn_exp2f(-x);
+            kr[c] = kf[j][2 * w + c] * er;
+            kc[c] = kf[j][2 * w + c] * ec;
+            qr[c] = qf[j][2 * w + c] * er;
+          }
+          split_pair(kr[0], kr[1], krh[w], krl[w]);
+          split_pair(kc[0], kc[1], kch[j][w], kcl[j][w]);
+          split_pair(qr[0], qr[1], qrh[w], qrl[w]);
+        }
+        const int off = (tk + 16 * j) * NS + c8;
+        st4(&sm.kr_h[b][off], u32x4{krh[0], krh[1], krh[2], krh[3]});
+        st4(&sm.kr_l[b][off], u32x4{krl[0], krl[1], krl[2], krl[3]});
+        st4(&sm.qr_h[b][off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
+        st4(&sm.qr_l[b][off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
+      }
+    }
+    block_sync();
+    // ---- part 2 (step 2m-2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int off = (tk + 16 * j) * NS + c8;
+      st4(&sm.kc_h[b][off], u32x4{kch[j][0], kch[j][1], kch[j][2], kch[j][3]});
+      st4(&sm.kc_l[b][off], u32x4{kcl[j][0], kcl[j][1], kcl[j][2], kcl[j][3]});
+      st4(&sm.vv[b][off], vkeep[j]);
     }
     block_sync();
   }
+  // step 2nc-3: R *= e^{G_C - a} after the last chunk turns R back into S
+  if (tk == 0) {
+    float fv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
+    st4(&sm.fac[nc & 1][c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+    st4(&sm.fac[nc & 1][c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+  }
+  block_sync();
+  block_sync();   // steps 2nc-2, 2nc-1
+  block_sync();
+}
+
+// T helper th (0..3) of the pipeline.  Part 1 of chunk m (step 2m-1): the
+// diagonal blocks of A and their inverses (th 0, 1), A10 (th 2), the three
+// blocks of P (th 3, kept in registers); part 2 (step 2m): T diag(beta) by
+// four columns per helper, and th 3 stores P.
+__device__ __forceinline__ void pipe_thelper(PipeSmem& sm, const int th, const int32_t beg, const int32_t end) {
+  const int lane = threadIdx.x & 63;
+  const int nc = (end - beg + CH - 1) / CH;
+  block_sync();   // steps -3, -2: the operands of chunk 0 are being built
+  block_sync();
+  for (int m = 0; m < nc; ++m) {
+    const int b = m & 1;
+    f32x4 pacc[3];
+    {
+      const int lane_s = opaque(lane);
+      if (th < 2) {
+        a_diag_solve(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, sm.tt, sm.tn, th, lane_s);
+      } else if (th == 2) {
+        a_offdiag(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
+      } else {
+        const int lm = lane_s & 15;
+        const int lg = lane_s >> 4;
+        pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
+        pacc[1] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
+        pacc[2] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 1, lm, lg);
+      }
+    }
+    block_sync();
+    {
+      const int lane_s = opaque(lane);
+      t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
+      if (th == 3) {
+        p_store(pacc[0], 0, 0, sm.p_h, sm.p_l, lane_s);
+        p_store(pacc[1], 1, 0, sm.p_h, sm.p_l, lane_s);
+        p_store(pacc[2], 1, 1, sm.p_h, sm.p_l, lane_s);
+      }
+    }
+    block_sync();
+  }
+  block_sync();   // step 2nc-1
 }
 
 // One workgroup runs one fragment (a run of tokens of one sequence inside one
 // segment) of one head, chunk after chunk, as a two-stage pipeline: owner waves
-// hold the state in registers and apply chunk n-1 while NHELP helper waves build
+// hold the state in registers and apply chunk n-1 while helper waves build
 // chunk n's operands in LDS (see owner_fragment and helper_fragment); three
 // barriers per chunk.
 //
@@ -896,16 +1427,16 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
       idle_owner(beg, end);
     }
   } else {
-    if (work.mode == kModeFwd) helper_fragment<kModeFwd>(p, sm, wave - 2 * NOWN, beg, end);
-    else helper_fragment<kModeSumS>(p, sm, wave - 2 * NOWN, beg, end);
+    if (work.mode == kModeFwd) helper_fragment<kModeFwd, NHELP_SUM>(p, sm, wave - 2 * NOWN, beg, end);
+    else helper_fragment<kModeSumS, NHELP_SUM>(p, sm, wave - 2 * NOWN, beg, end);
   }
 }
 
 // Carry launch: each carried fragment runs again from its carry-in C_r with the
-// forward body (o and, where a sequence ends, the final state); waves 0-3 own
-// the state, waves 4-7 are helpers.
+// forward body (o and, where a sequence ends, the final state), as the
+// three-role pipeline above.
 __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams p) {
-  __shared__ ChunkSmem sm;
+  __shared__ PipeSmem sm;
   const int f = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t flags = p.plan[p.L.frag_flags + f];
@@ -915,8 +1446,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave < NOWN) owner_fragment<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, true);
-  else helper_fragment<kModeFwd>(p, sm, wave - NOWN, beg, end);
+  if (wave < NOWN) pipe_owner(p, sm, wave, flags, seg, seq, beg, end, true);
+  else if (wave < 2 * NOWN) pipe_ophelper(p, sm, wave - NOWN, beg, end);
+  else pipe_thelper(sm, wave - 2 * NOWN, beg, end);
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of
