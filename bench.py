@@ -257,14 +257,15 @@ def main():
         if ev is not None:
             ev[0].record()
         kda.segment_summaries(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["o"],
-                              out["final_state"], out["transitions"], out["updates"])
+                              out["final_state"], out["transitions"], out["updates"],
+                              out["chunk_cache"])
         if ev is not None:
             ev[1].record()
         kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"])
         if ev is not None:
             ev[2].record()
         kda.apply_carry(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["carry_in"],
-                        out["o"], out["final_state"])
+                        out["o"], out["final_state"], out["chunk_cache"])
         if ev is not None:
             ev[3].record()
 

@@ -47,14 +47,21 @@ int finish_launch() {
 
 extern "C" int kda_last_hip_error(void) { return g_last_hip_error; }
 
+extern "C" size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H) {
+  if (plan == nullptr || H <= 0) return 0;
+  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
+  return slots * static_cast<size_t>(H) * kda::kChunkCacheBytes;
+}
+
 extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* g, const uint16_t* beta, int32_t H,
                                      int32_t K, int32_t V, float* o, float* final_state,
-                                     float* transitions, float* updates, hipStream_t stream) {
+                                     float* transitions, float* updates, void* chunk_cache,
+                                     hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
-  st = check_tensors({q, k, v, g, beta, o, final_state, transitions, updates});
+  st = check_tensors({q, k, v, g, beta, o, final_state, transitions, updates, chunk_cache});
   if (st != KDA_OK) return st;
   kda::ChunkParams p{};
   p.plan = plan_dev;
@@ -71,6 +78,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.transitions = transitions;
   p.updates = updates;
   p.carry = nullptr;
+  p.chunk_cache = static_cast<uint16_t*>(chunk_cache);
   (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kda::kSummaryThreads), 0, stream, p);
   return finish_launch();
@@ -102,10 +110,10 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
                                const uint16_t* k, const uint16_t* v, const uint16_t* g,
                                const uint16_t* beta, int32_t H, int32_t K, int32_t V,
                                const float* carry_in, float* o, float* final_state,
-                               hipStream_t stream) {
+                               const void* chunk_cache, hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
-  st = check_tensors({q, k, v, g, beta, carry_in, o, final_state});
+  st = check_tensors({q, k, v, g, beta, carry_in, o, final_state, chunk_cache});
   if (st != KDA_OK) return st;
   kda::ChunkParams p{};
   p.plan = plan_dev;
@@ -122,6 +130,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.transitions = nullptr;
   p.updates = nullptr;
   p.carry = carry_in;
+  p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(chunk_cache));
   (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, H, 1), dim3(kda::kCarryThreads), 0, stream, p);
   return finish_launch();

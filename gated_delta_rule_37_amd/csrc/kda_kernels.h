@@ -31,7 +31,17 @@ struct ChunkParams {
   float* transitions;
   float* updates;
   const float* carry;
+  uint16_t* chunk_cache;  // T diag(beta) per chunk of the carrying fragments
 };
+
+// Chunk cache: slot of chunk `it` of the carrying fragment of segment r that
+// starts at token b_r is floor(b_r / 32) + r + it (fragments of distinct
+// segments never share a slot); a slot holds, per head, T diag(beta) as
+// [hi | lo] x [32 rows] x [32 columns in k-slot order] bf16 = 4096 bytes.
+constexpr int kChunkCacheBytes = 4096;
+__host__ __device__ inline int64_t chunk_cache_slot(int32_t seg, int32_t frag_begin, int32_t it) {
+  return static_cast<int64_t>(frag_begin / 32) + seg + it;
+}
 
 struct ComposeParams {
   const int32_t* plan;

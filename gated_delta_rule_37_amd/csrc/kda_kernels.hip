@@ -772,6 +772,24 @@ __device__ __forceinline__ void t_merge(const float* an, const float* tt, const 
   tbl[ti * TS + 16 + cp] = static_cast<bf16>(0.f);
 }
 
+// Chunk cache transfer of T diag(beta) (4 KB per chunk and head): the 256
+// lanes of four waves (index 0..255 = 64 wave + lane) each move 16 bytes,
+// lane i taking half i/128 (hi, lo), row (i/4) % 32 and quarter i % 4.
+__device__ __forceinline__ size_t cache_elem(const ChunkParams& p, const int32_t seg, const int32_t beg,
+                                             const int it, const int i) {
+  const int which = i >> 7;
+  const int row = (i >> 2) & 31;
+  const int q = i & 3;
+  return (static_cast<size_t>(chunk_cache_slot(seg, beg, it)) * p.H + blockIdx.y) * (kChunkCacheBytes / 2) +
+         which * (CH * CH) + row * CH + 8 * q;
+}
+__device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) * TS + 8 * (i & 3); }
+__device__ __forceinline__ void tb_to_cache(const ChunkParams& p, const bf16* tbh, const bf16* tbl,
+                                            const int32_t seg, const int32_t beg, const int it, const int i) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(&((i >> 7) ? tbl : tbh)[cache_lds(i)]);
+  *reinterpret_cast<u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, it, i)) = v;
+}
+
 // ---------------------------------------------------------------------------
 // Helper waves (NH of them, index hw): chunk it's operands while the owners
 // finish chunk it-1.
@@ -792,7 +810,7 @@ __device__ __forceinline__ void t_merge(const float* an, const float* tt, const 
 //           16..31 of octet q)
 template <int MODE, int NH>
 __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int hw,
-                                                const int32_t beg, const int32_t end) {
+                                                const int32_t seg, const int32_t beg, const int32_t end) {
   static_assert(NH == 4 || NH == 8, "helper layouts");
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
@@ -848,6 +866,9 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
     // ---- step 1: operands of chunk it, and the owners' rescale
     {
       const int b = it & 1;
+      // update mode (a carrying fragment that ends its segment): the carry
+      // pass re-runs this fragment and reads T diag(beta) back from the cache
+      if (MODE == kModeSumS && NH == 4 && it >= 1) tb_to_cache(p, sm.tb_h, sm.tb_l, seg, beg, it - 1, 64 * hw + lane);
       float kf[TPL][8], qf[TPL][8], G[TPL][8];
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
@@ -978,6 +999,7 @@ __device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem&
   }
 
   // after the last chunk: R *= e^{G_C - a} turns R back into S
+  if (MODE == kModeSumS && NH == 4) tb_to_cache(p, sm.tb_h, sm.tb_l, seg, beg, nc - 1, 64 * hw + lane);
   if (tk == 0) {
     float fv[8];
 #pragma unroll
@@ -1346,25 +1368,35 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
   block_sync();
 }
 
-// T helper th (0..3) of the pipeline.  Part 1 of chunk m (step 2m-1): the
-// diagonal blocks of A and their inverses (th 0, 1), A10 (th 2), the three
-// blocks of P (th 3, kept in registers); part 2 (step 2m): T diag(beta) by
-// four columns per helper, and th 3 stores P.
-__device__ __forceinline__ void pipe_thelper(PipeSmem& sm, const int th, const int32_t beg, const int32_t end) {
+// T helper th (0..3) of the pipeline.  A carrying fragment that ends its
+// segment ran in the summaries launch, which left T diag(beta) of each of its
+// chunks in the chunk cache: part 1 of chunk m (step 2m-1) loads it, part 2
+// (step 2m) stores it to LDS.  Otherwise part 1 computes the diagonal blocks
+// of A and their inverses (th 0, 1) and A10 (th 2), and part 2 merges them
+// into T diag(beta), four columns per helper.  Either way th 3 computes the
+// three blocks of P in part 1 and stores them in part 2.
+__device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int th, const int32_t flags,
+                                             const int32_t seg, const int32_t beg, const int32_t end) {
   const int lane = threadIdx.x & 63;
   const int nc = (end - beg + CH - 1) / CH;
+  const bool cached = (flags & kFragSegLast) != 0;
+  const int ci = 64 * th + lane;   // this lane's 16 bytes of a cached chunk
   block_sync();   // steps -3, -2: the operands of chunk 0 are being built
   block_sync();
   for (int m = 0; m < nc; ++m) {
     const int b = m & 1;
     f32x4 pacc[3];
+    u32x4 tbv;
     {
       const int lane_s = opaque(lane);
-      if (th < 2) {
+      if (cached) {
+        tbv = *reinterpret_cast<const u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, m, ci));
+      } else if (th < 2) {
         a_diag_solve(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, sm.tt, sm.tn, th, lane_s);
       } else if (th == 2) {
         a_offdiag(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
-      } else {
+      }
+      if (th == 3) {
         const int lm = lane_s & 15;
         const int lg = lane_s >> 4;
         pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
@@ -1375,7 +1407,8 @@ __device__ __forceinline__ void pipe_thelper(PipeSmem& sm, const int th, const i
     block_sync();
     {
       const int lane_s = opaque(lane);
-      t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
+      if (cached) st4(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)], tbv);
+      else t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
       if (th == 3) {
         p_store(pacc[0], 0, 0, sm.p_h, sm.p_l, lane_s);
         p_store(pacc[1], 1, 0, sm.p_h, sm.p_l, lane_s);
@@ -1427,8 +1460,8 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
       idle_owner(beg, end);
     }
   } else {
-    if (work.mode == kModeFwd) helper_fragment<kModeFwd, NHELP_SUM>(p, sm, wave - 2 * NOWN, beg, end);
-    else helper_fragment<kModeSumS, NHELP_SUM>(p, sm, wave - 2 * NOWN, beg, end);
+    if (work.mode == kModeFwd) helper_fragment<kModeFwd, NHELP_SUM>(p, sm, wave - 2 * NOWN, seg, beg, end);
+    else helper_fragment<kModeSumS, NHELP_SUM>(p, sm, wave - 2 * NOWN, seg, beg, end);
   }
 }
 
@@ -1448,7 +1481,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < NOWN) pipe_owner(p, sm, wave, flags, seg, seq, beg, end, true);
   else if (wave < 2 * NOWN) pipe_ophelper(p, sm, wave - NOWN, beg, end);
-  else pipe_thelper(sm, wave - 2 * NOWN, beg, end);
+  else pipe_thelper(p, sm, wave - 2 * NOWN, flags, seg, beg, end);
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of

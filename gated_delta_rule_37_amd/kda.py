@@ -38,7 +38,7 @@ STATUS = {
 # Every symbol include/kda.h declares.
 SYMBOLS = (
     "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
-    "kda_summary_bytes", "kda_segment_summaries", "kda_compose_summaries",
+    "kda_summary_bytes", "kda_chunk_cache_bytes", "kda_segment_summaries", "kda_compose_summaries",
     "kda_apply_carry", "kda_status_string", "kda_last_hip_error",
 )
 
@@ -80,11 +80,13 @@ def lib() -> ctypes.CDLL:
     L.kda_plan_destroy.restype = None
     L.kda_summary_bytes.argtypes = [p, i32, i32, i32]
     L.kda_summary_bytes.restype = sz
-    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p]
+    L.kda_chunk_cache_bytes.argtypes = [p, i32]
+    L.kda_chunk_cache_bytes.restype = sz
+    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p, p]
     L.kda_segment_summaries.restype = ctypes.c_int
     L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, p, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
+    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p]
     L.kda_apply_carry.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -140,6 +142,9 @@ class Plan:
     def summary_bytes(self, H: int, K: int = 128, V: int = 128) -> int:
         return int(lib().kda_summary_bytes(self._h, H, K, V))
 
+    def chunk_cache_bytes(self, H: int) -> int:
+        return int(lib().kda_chunk_cache_bytes(self._h, H))
+
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
             lib().kda_plan_destroy(self._h)
@@ -182,8 +187,13 @@ def _inputs(plan: Plan, q, k, v, g, beta):
     ]
 
 
+def _cache_ptr(plan: Plan, H: int, chunk_cache) -> int:
+    n = plan.chunk_cache_bytes(H)
+    return _ptr(chunk_cache, torch.uint8, (n,), "chunk_cache")
+
+
 def segment_summaries(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, o, final_state,
-                      transitions, updates, stream=None):
+                      transitions, updates, chunk_cache, stream=None):
     """``kda_segment_summaries``: zero-start pass over every segment."""
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
     outs = [
@@ -191,6 +201,7 @@ def segment_summaries(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, o, f
         _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state"),
         _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
         _ptr(updates, torch.float32, (plan.S, H, K, V), "updates"),
+        _cache_ptr(plan, H, chunk_cache),
     ]
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
     st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *outs, _stream(q, stream))
@@ -212,19 +223,21 @@ def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, 
 
 
 def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
-                stream=None):
+                chunk_cache, stream=None):
     """``kda_apply_carry``: re-run each carrying segment's first fragment from C_r."""
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
     oo = _ptr(o, torch.float32, (plan.T, H, V), "o")
     ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
+    cc = _cache_ptr(plan, H, chunk_cache)
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, c, oo, ff, _stream(q, stream))
+    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, c, oo, ff, cc, _stream(q, stream))
     _check(st, "kda_apply_carry")
 
 
 def alloc_outputs(plan: Plan, H: int, K: int, V: int, device):
-    """Fresh output buffers (o, final_state, transitions, updates, carry_in)."""
+    """Fresh output buffers (o, final_state, transitions, updates, carry_in) and
+    the chunk cache shared by the summaries and carry passes."""
     f32 = dict(dtype=torch.float32, device=device)
     return dict(
         o=torch.empty(plan.T, H, V, **f32),
@@ -232,6 +245,7 @@ def alloc_outputs(plan: Plan, H: int, K: int, V: int, device):
         transitions=torch.empty(plan.S, H, K, K, **f32),
         updates=torch.empty(plan.S, H, K, V, **f32),
         carry_in=torch.empty(plan.S, H, K, V, **f32),
+        chunk_cache=torch.empty(plan.chunk_cache_bytes(H), dtype=torch.uint8, device=device),
     )
 
 
@@ -243,7 +257,8 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None):
         out = alloc_outputs(plan, H, K, V, q.device)
     pd = plan.device_blob(q.device)
     segment_summaries(plan, pd, q, k, v, g, beta, out["o"], out["final_state"],
-                      out["transitions"], out["updates"], stream)
+                      out["transitions"], out["updates"], out["chunk_cache"], stream)
     compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], stream)
-    apply_carry(plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"], stream)
+    apply_carry(plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
+                out["chunk_cache"], stream)
     return out

@@ -47,6 +47,7 @@
  *       beta    : [T, H]    bf16
  *       o       : [T, H, V] fp32        final_state : [N, H, K, V] fp32
  *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
+ *       chunk_cache : kda_chunk_cache_bytes(plan, H) bytes of device memory
  *   - Device calls are asynchronous on `stream`; launch failures are reported
  *     as KDA_ERR_HIP (kda_last_hip_error() gives the hipError_t).
  *   - Supported gate domain: g <= 0 and finite, with the decay mass of any 16
@@ -128,6 +129,18 @@ void kda_plan_destroy(kda_plan* plan);
 size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 
 /*
+ * kda_chunk_cache_bytes -- bytes of the chunk cache that kda_segment_summaries
+ * fills and kda_apply_carry reads: the per-chunk factor T diag(beta) of the
+ * UT form of the recurrence (T = (I + A)^{-1}, A_ij = beta_i k_i^T
+ * Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token chunk) of the
+ * carrying fragments, so that the carry pass does not rebuild it.  This is
+ * an implementation cache, not part of the method: its contents are opaque
+ * and valid only between the two calls on the same plan, H and inputs.
+ * Size: (ceil(T / 32) + S) * H * 4096.  Returns 0 for a NULL plan or H <= 0.
+ */
+size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
+
+/*
  * kda_segment_summaries -- every segment from a zero state.
  * #136 Summary (preceding_state_update / preceding_transition), #110
  * Motivation (each producer computes its affine recurrence state).
@@ -144,15 +157,19 @@ size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
  *                     state, so o is final there);
  *   final_state[n]  for every sequence whose last token lies outside the
  *                     first fragment of a carrying segment.
+ *   chunk_cache     the chunk factors of every carrying fragment that ends
+ *                   its segment (kda_chunk_cache_bytes).
  * The remaining rows of o and final_state are written by kda_apply_carry.
- *   plan_dev  device copy of kda_plan_blob(plan).
+ *   plan_dev     device copy of kda_plan_blob(plan).
+ *   chunk_cache  device buffer of kda_chunk_cache_bytes(plan, H) bytes,
+ *                16-byte aligned, owned by the caller.
  */
 int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           const uint16_t* g, const uint16_t* beta,
                           int32_t H, int32_t K, int32_t V,
                           float* o, float* final_state, float* transitions, float* updates,
-                          hipStream_t stream);
+                          void* chunk_cache, hipStream_t stream);
 
 /*
  * kda_compose_summaries -- ordered FP32 scan C_0 = 0, C_{r+1} = A_r C_r + B_r.
@@ -173,12 +190,15 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
  * final_state.  #136 Summary (the forward that consumes
  * preceding_state_update / preceding_transition), #110 Motivation (rank 1
  * consumes only the V-state it needs).
+ *   chunk_cache  the buffer kda_segment_summaries filled for the same plan,
+ *                H and inputs (read only).
  */
 int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* g, const uint16_t* beta,
                     int32_t H, int32_t K, int32_t V, const float* carry_in,
-                    float* o, float* final_state, hipStream_t stream);
+                    float* o, float* final_state, const void* chunk_cache,
+                    hipStream_t stream);
 
 /* Human-readable name of a kda_status value. */
 const char* kda_status_string(int status);

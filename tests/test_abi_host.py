@@ -91,15 +91,25 @@ def test_summary_workspace_64_segments_32_heads_is_256_mib():
     assert plan.summary_bytes(32, 128, 128) == 256 * 1024 * 1024
 
 
+def test_chunk_cache_bytes():
+    # (ceil(T / 32) + S) slots of 4096 bytes per head
+    assert kda.Plan([0, 65536], 64).chunk_cache_bytes(32) == (2048 + 64) * 32 * 4096
+    assert kda.Plan([0, 100], 3).chunk_cache_bytes(2) == (4 + 3) * 2 * 4096
+    assert kda.Plan([0, 1], 1).chunk_cache_bytes(1) == 2 * 4096
+    L = kda.lib()
+    assert L.kda_chunk_cache_bytes(None, 4) == 0
+    assert kda.Plan([0, 100], 3).chunk_cache_bytes(0) == 0
+
+
 # ------------------------------------------------ device entry points: host checks
 
 _FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereferenced
 
 
-def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, q=_FAKE, o=_FAKE):
+def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, q=_FAKE, o=_FAKE, cache=_FAKE):
     L = kda.lib()
     return L.kda_segment_summaries(plan.handle, plan_dev, q, _FAKE, _FAKE, _FAKE, _FAKE,
-                                   H, K, V, o, _FAKE, _FAKE, _FAKE, None)
+                                   H, K, V, o, _FAKE, _FAKE, _FAKE, cache, None)
 
 
 def test_device_calls_validate_before_launch():
@@ -113,15 +123,19 @@ def test_device_calls_validate_before_launch():
     assert _call_summaries(plan, q=_FAKE + 2) == -5
     assert _call_summaries(plan, o=_FAKE + 8) == -5
     assert _call_summaries(plan, plan_dev=_FAKE + 4) == -5
+    assert _call_summaries(plan, cache=0) == -1
+    assert _call_summaries(plan, cache=_FAKE + 8) == -5
     L = kda.lib()
     assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                                   _FAKE, _FAKE, _FAKE, _FAKE, None) == -1
+                                   _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None) == -1
     assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, _FAKE, None) == -4
     assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, _FAKE, None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                             _FAKE + 4, _FAKE, _FAKE, None) == -5
+                             _FAKE + 4, _FAKE, _FAKE, _FAKE, None) == -5
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                             _FAKE, 0, _FAKE, None) == -1
+                             _FAKE, 0, _FAKE, _FAKE, None) == -1
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                             _FAKE, _FAKE, _FAKE, 0, None) == -1
     assert L.kda_last_hip_error() == 0
 
 
