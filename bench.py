@@ -35,6 +35,9 @@ TRI_INCL = (C + 1) / 2 * K        # P, W = T(...), U~ = T V, P U (lower incl. di
 STATE = K * V                     # one K x V product per token (W S, Q S, K^T U)
 MACS = {
     "fwd": TRI_STRICT + 4 * TRI_INCL + 3 * STATE,
+    # forward over chunks whose T diag(beta) the summaries launch left in the
+    # chunk cache: no A, no T
+    "fwd_cached": 3 * TRI_INCL + 3 * STATE,
     "sum_s": TRI_STRICT + 2 * TRI_INCL + 2 * STATE,
     "sum_phi": TRI_STRICT + TRI_INCL + 2 * K * K,
 }
@@ -42,6 +45,7 @@ MACS = {
 # against a split operand two.
 MFMA_MACS = {
     "fwd": 3 * MACS["fwd"] - TRI_INCL,
+    "fwd_cached": 3 * MACS["fwd_cached"] - TRI_INCL,
     "sum_s": 3 * MACS["sum_s"] - TRI_INCL,
     "sum_phi": 3 * MACS["sum_phi"],
 }
@@ -80,20 +84,18 @@ def chunk_kernel_work(blob, H):
     for f in range(F):
         L = int(f_end[f] - f_beg[f])
         fl = int(f_flags[f])
-        seg_last, seq_end = (fl & 2) > 0, (fl & 4) > 0
-        if fl & 1:                       # carried first fragment
-            if seg_last:                 # summaries: B_r from zero, A_r from identity
-                add("summaries", "sum_s", L)
-                live = int(seg_live[int(f_seg[f])]) != 0
-                if live:                 # one workgroup builds both: inputs read once
-                    work["summaries"]["macs"] += MACS["sum_phi"] * L * H
-                    work["summaries"]["mfma_macs"] += MFMA_MACS["sum_phi"] * L * H
-                work["summaries"]["bytes"] += 2 * STATE_BYTES * H
-            add("carry", "fwd", L)       # carry: forward from C_r
-            work["carry"]["bytes"] += STATE_BYTES * H * (1 + seq_end)
-        else:
-            add("summaries", "fwd", L)
-            work["summaries"]["bytes"] += STATE_BYTES * H * (2 * seg_last + seq_end)
+        carried, seg_last, seq_end = (fl & 1) > 0, (fl & 2) > 0, (fl & 4) > 0
+        if seg_last:                     # summaries: B_r from zero, A_r from identity
+            add("summaries", "sum_s", L)
+            if carried and int(seg_live[int(f_seg[f])]) != 0:
+                # one workgroup builds both: inputs read once
+                work["summaries"]["macs"] += MACS["sum_phi"] * L * H
+                work["summaries"]["mfma_macs"] += MFMA_MACS["sum_phi"] * L * H
+            work["summaries"]["bytes"] += 2 * STATE_BYTES * H
+        # carry: o and the final state of every fragment, from C_r or zero
+        work["carry"]["macs"] += MACS["fwd_cached" if seg_last else "fwd"] * L * H
+        work["carry"]["mfma_macs"] += MFMA_MACS["fwd_cached" if seg_last else "fwd"] * L * H
+        work["carry"]["bytes"] += BYTES["fwd"] * L * H + STATE_BYTES * H * (carried + seq_end)
     return work
 
 
@@ -256,9 +258,8 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        kda.segment_summaries(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["o"],
-                              out["final_state"], out["transitions"], out["updates"],
-                              out["chunk_cache"])
+        kda.segment_summaries(plan, pd, d["k"], d["v"], d["g"], d["beta"], out["transitions"],
+                              out["updates"], out["chunk_cache"])
         if ev is not None:
             ev[1].record()
         kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"])

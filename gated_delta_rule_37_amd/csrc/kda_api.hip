@@ -54,27 +54,25 @@ extern "C" size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H) {
 }
 
 extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* g, const uint16_t* beta, int32_t H,
-                                     int32_t K, int32_t V, float* o, float* final_state,
+                                     const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                                     const uint16_t* beta, int32_t H, int32_t K, int32_t V,
                                      float* transitions, float* updates, void* chunk_cache,
                                      hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
-  st = check_tensors({q, k, v, g, beta, o, final_state, transitions, updates, chunk_cache});
+  st = check_tensors({k, v, g, beta, transitions, updates, chunk_cache});
   if (st != KDA_OK) return st;
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
   p.H = H;
-  p.pass = 1;
-  p.q = q;
+  p.q = nullptr;
   p.k = k;
   p.v = v;
   p.g = g;
   p.beta = beta;
-  p.o = o;
-  p.final_state = final_state;
+  p.o = nullptr;
+  p.final_state = nullptr;
   p.transitions = transitions;
   p.updates = updates;
   p.carry = nullptr;
@@ -119,7 +117,6 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.plan = plan_dev;
   p.L = plan->layout;
   p.H = H;
-  p.pass = 2;
   p.q = q;
   p.k = k;
   p.v = v;

@@ -11,7 +11,7 @@
 
 namespace kda {
 
-constexpr int kSummaryThreads = 768;  // kda_chunk_kernel (summaries launch): 12 waves
+constexpr int kSummaryThreads = 1024;  // kda_chunk_kernel (summaries launch): 16 waves
 constexpr int kCarryThreads = 768;    // kda_carry_kernel (carry launch): 12 waves
 constexpr int kComposeThreads = 256;  // kda_compose_kernel workgroup size
 constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
@@ -20,7 +20,6 @@ struct ChunkParams {
   const int32_t* plan;   // device copy of the plan blob
   BlobLayout L;
   int32_t H;
-  int32_t pass;          // 1: zero-start pass (summaries), 2: carried fragments
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -31,12 +30,14 @@ struct ChunkParams {
   float* transitions;
   float* updates;
   const float* carry;
-  uint16_t* chunk_cache;  // T diag(beta) per chunk of the carrying fragments
+  uint16_t* chunk_cache;  // T diag(beta) per chunk of the fragments that end a segment
 };
 
-// Chunk cache: slot of chunk `it` of the carrying fragment of segment r that
-// starts at token b_r is floor(b_r / 32) + r + it (fragments of distinct
-// segments never share a slot); a slot holds, per head, T diag(beta) as
+// Chunk cache: slot of chunk `it` of the fragment that ends segment r and
+// starts at token b_r is floor(b_r / 32) + r + it (its last slot is below
+// ceil(e_r / 32) + r for the segment end e_r, the next segment's first is at
+// least floor(e_r / 32) + r + 1, so segments never share one); a slot holds,
+// per head, T diag(beta) as
 // [hi | lo] x [32 rows] x [32 columns in k-slot order] bf16 = 4096 bytes.
 constexpr int kChunkCacheBytes = 4096;
 __host__ __device__ inline int64_t chunk_cache_slot(int32_t seg, int32_t frag_begin, int32_t it) {

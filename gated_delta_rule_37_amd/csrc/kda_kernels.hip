@@ -45,13 +45,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
 constexpr int CH = 32;    // chunk length (tokens)
-constexpr int NOWN = 4;               // owner waves per state: 32 columns each
-constexpr int NHELP_SUM = 4;          // helper waves of the summaries kernel
+constexpr int NOWN = 4;               // waves per role: owners (32 columns each), helpers (32 channels each)
 // summaries kernel: owners of S (waves 0-3) and of the transition (4-7), helpers 8-11
-static_assert((2 * NOWN + NHELP_SUM) * 64 == kSummaryThreads, "summaries kernel wave roles");
-// carry kernel: owners 0-3, helpers 4-7
+static_assert(4 * NOWN * 64 == kSummaryThreads, "summaries kernel wave roles");
 static_assert(3 * NOWN * 64 == kCarryThreads, "carry kernel: owners, operand helpers, T helpers");
-constexpr int KSPLIT = 4;             // owner k-steps before the T merge barrier
 constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 152;   // row stride (bf16) of token-major [32][128] tiles (conflict-free row and transposed reads)
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
@@ -203,51 +200,21 @@ __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo)
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Shared memory of one workgroup (about 115 KB).  Helpers write the operands
-// of chunk n while owners still use chunk n-1's: Kc and V, which owners read in
-// the same step as helpers write the next chunk's, are double-buffered; every
-// other buffer is written only after its last reader of the previous chunk has
-// passed a barrier.
-struct alignas(16) ChunkSmem {
-  bf16 kr_h[CH * NS], kr_l[CH * NS];          // Kr = k e^{G-a}, token-major
-  bf16 qr_h[CH * NS], qr_l[CH * NS];          // Qr = q e^{G-a}, token-major
-  bf16 kc_h[2][CH * NS], kc_l[2][CH * NS];    // Kc = k e^{a-G}, token-major
-  bf16 vv[2][CH * NS];                        // V, token-major (exact)
-  bf16 tb_h[CH * TS], tb_l[CH * TS];          // T diag(beta), [i][j]
-  bf16 p_h[CH * TS], p_l[CH * TS];            // P, [i][j]
-  float an[CH * FS];                          // A10 by rows, diagonal blocks transposed
-  float tt[CH * FS];                          // tt[c][i] = T00[i][c]
-  float tn[CH * FS];                          // tn[16 + i][16 + c] = T11[i][c]
-  float xt[16 * XS];                          // X = A10 T00, stored xt[c][i]
-  float fac[KD];                              // state rescale between two chunks
-  float beta[CH];
-};
-
-// What one workgroup of the summaries launch does with its fragment.
+// What one workgroup of the summaries launch does with its fragment.  Only
+// the last fragment of each segment runs there: its state from zero is B_r
+// (waves 0-3); waves 4-7 build A_r from the identity when the fragment carries
+// in (no sequence starts inside the segment), and otherwise write the zero
+// transition (the reset's linear part).  Every fragment's o and final state
+// come from the carry launch.
 struct Work {
-  int mode;         // kModeFwd, kModeSumS, or -1 for nothing
-  bool phi;         // also build the segment's transition (waves NOWN..2NOWN-1)
-  bool zero_a;      // write a zero transition (a sequence starts in the segment)
+  bool run;
+  bool phi;
 };
-
-// Summaries launch: a fragment that starts at a sequence start runs the
-// forward (o, final state, and B_r if it ends the segment); a carried fragment
-// that ends its segment builds B_r from zero and, from the identity, A_r.  The
-// transition of a segment whose last fragment is not carried is zero (the
-// reset's linear part).  Carried fragments that end inside the segment are left
-// to the carry launch.
 __device__ __forceinline__ Work decode_summary(const ChunkParams& p, int32_t flags, int32_t seg) {
-  Work w{-1, false, false};
-  const bool seg_last = (flags & kFragSegLast) != 0;
-  if (flags & kFragCarried) {
-    if (seg_last) {
-      w.mode = kModeSumS;
-      if (p.plan[p.L.seg_transition_live + seg]) w.phi = true;
-      else w.zero_a = true;
-    }
-  } else {
-    w.mode = kModeFwd;
-    w.zero_a = seg_last;
+  Work w{false, false};
+  if (flags & kFragSegLast) {
+    w.run = true;
+    w.phi = (flags & kFragCarried) && p.plan[p.L.seg_transition_live + seg];
   }
   return w;
 }
@@ -270,16 +237,6 @@ __device__ __forceinline__ void block_sync() { __syncthreads(); }
 // values (LDS accesses of one wave complete in program order; this keeps the
 // compiler from moving the reads up).
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
-
-// 32 x 32 accumulator tile -> B operands (hi, lo) of its two 16-row k-blocks.
-__device__ __forceinline__ void tile_to_b_split(const f32x16& t, bf16x8 bh[2], bf16x8 bl[2]) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float x[8];
-    tile_rows_to_b(t, s, x);
-    split8(x, bh[s], bl[s]);
-  }
-}
 
 // k-slot order used with accumulator tiles as B operands.  A 32 x 32 tile t
 // (rows 16s .. 16s+15 of it feeding k-step s) becomes a B operand without any
@@ -319,20 +276,6 @@ __device__ __forceinline__ bf16x8 ld_kslots(const bf16* row, const int c) {
 // each 16-column group sits at position t with bits 2 and 3 swapped.
 __device__ __forceinline__ int kslot_col(const int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
-// Barrier sequence of an owner slot with no state to keep (a forward fragment
-// in the summaries launch needs one state block only): the same barriers as
-// owner_fragment, nothing else.
-__device__ __forceinline__ void idle_owner(const int32_t beg, const int32_t end) {
-  const int nc = (end - beg + CH - 1) / CH;
-  for (int it = 0; it <= nc; ++it) {
-    block_sync();
-    if (it < nc) {
-      block_sync();
-      block_sync();
-    }
-  }
-}
-
 }  // namespace
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
@@ -350,246 +293,6 @@ __device__ __forceinline__ s16x4 lds_read_tr(const bf16* p) {
 __device__ __forceinline__ bf16x8 join8(const s16x4 a, const s16x4 b) {
   const s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
-}
-
-// ---------------------------------------------------------------------------
-// Owner waves (0 .. NOWN-1): wave w keeps the state columns [32w, 32w + 32) as
-// four 32 x 32 FP32 accumulator tiles R[dt] (rows 32dt + 8r + 4(l/32) + e in
-// lane l, register 4r + e; column 32w + l%32).  R is the state scaled by the
-// anchor of the chunk it enters, e^{a} o S, which is the operand Kr and Qr
-// multiply; one update is
-//     S_new = Diag(e^{G_C}) S + K^^T U = Diag(e^{G_C - a}) (R + Kc^T U)
-// and the helpers supply fac = e^{a_next + G_C - a} to re-anchor it for the
-// next chunk (e^{G_C - a} after the last one, which leaves S itself).
-//
-// Iteration it finishes chunk it-1 and starts chunk it:
-//   step 1  D = V - Y, U = T diag(beta) D, O += P U, store o, R += Kc^T U
-//   step 2  R *= fac; Y = Kr R, O = Qr R, first KSPLIT k-steps
-//   step 3  the remaining k-steps
-template <int MODE>
-__device__ __forceinline__ void owner_fragment(const ChunkParams& p, ChunkSmem& sm, const int ow,
-                                               const int32_t flags, const int32_t seg, const int32_t seq,
-                                               const int32_t beg, const int32_t end, const bool from_carry) {
-  constexpr bool fwd = MODE == kModeFwd;
-  constexpr bool use_v = MODE != kModeSumPhi;
-  const int h = blockIdx.y;
-  const int H = p.H;
-  const int lane = threadIdx.x & 63;
-  const int ln = lane & 31;
-  const int lh = lane >> 5;
-  const int col = 32 * ow + ln;
-  const int nc = (end - beg + CH - 1) / CH;
-  const int o_row = H * VD * 4;   // one token of o (bytes)
-
-  f32x16 R[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
-  if (MODE == kModeSumPhi) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = (32 * dt + 8 * r + 4 * lh + e == col) ? 1.f : 0.f;
-  } else if (from_carry) {
-    const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
-  }
-
-  f32x16 Y = zero16(), O = zero16();
-
-  // A operands of k-step kk (channels 16kk .. 16kk+15): Kr and Qr, hi and lo
-  auto load_ops = [&](bf16x8 (&o)[4], const int kk, const int ln, const int lh) {
-    const int off = ln * NS + 16 * kk + 8 * lh;
-    o[0] = *reinterpret_cast<const bf16x8*>(&sm.kr_h[off]);
-    o[1] = *reinterpret_cast<const bf16x8*>(&sm.kr_l[off]);
-    if (fwd) {
-      o[2] = *reinterpret_cast<const bf16x8*>(&sm.qr_h[off]);
-      o[3] = *reinterpret_cast<const bf16x8*>(&sm.qr_l[off]);
-    }
-  };
-  // rescale factors of the rows of tile dt held by this lane
-  auto load_fac = [&](f32x4 (&f)[4], const int dt, const int lh) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) f[r] = ld4(&sm.fac[32 * dt + 8 * r + 4 * lh]);
-  };
-  auto rescale = [&](const int dt, const f32x4 (&f)[4]) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) R[dt][4 * r + e] *= f[r][e];
-    }
-  };
-
-  // step 1: finish chunk it-1 (it >= 1)
-  auto finish = [&](const int it) __attribute__((always_inline)) {
-    const int lane_s = opaque(lane);
-    const int ln = lane_s & 31;
-    const int lh = lane_s >> 5;
-    const int col = 32 * ow + ln;
-    // transposed-read coordinates: group gq of 16 lanes, source index sq
-    const int gq = lane_s >> 4;
-    const int sq = lane_s & 15;
-    const int b = (it - 1) & 1;
-    const int c0 = beg + (it - 1) * CH;
-    const int n = min(CH, end - c0);
-    mfma_result_fence(Y);
-    f32x16 D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float vv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (use_v) {
-        // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
-        const s16x4 v4 = lds_read_tr(
-            &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
-    }
-    // D and U feed the products below as B operands in k-slot order (tokens):
-    // T diag(beta) and P are stored in that column order, Kc^T is read in it
-    bf16x8 dh[2], dl[2];
-    tile_kslots_split(D, dh, dl);
-    f32x16 U = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int off = ln * TS + 16 * s + 8 * lh;
-      U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
-                dh[s], dl[s], U);
-    }
-    mfma_result_fence(U);
-    bf16x8 ubh[2], ubl[2];
-    tile_kslots_split(U, ubh, ubl);
-    if (fwd) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int off = ln * TS + 16 * s + 8 * lh;
-        O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
-                  ubh[s], ubl[s], O);
-      }
-    }
-    // R += Kc^T U: the A operand (row = channel 32dt + l%32, k slots = tokens
-    // 16s + 4(l/32) + 0..3 and 16s + 8 + 4(l/32) + 0..3) is read as column
-    // fragments of the token-major Kc
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int off = (16 * s + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
-        const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 8 * NS]));
-        const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 8 * NS]));
-        R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
-      }
-    }
-    if (fwd) {
-      mfma_result_fence(O);
-      // rows past the fragment's end fall outside the buffer and are dropped
-      const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
-                                                         (n - 1) * o_row + 4 * VD, kBufDword3);
-      const int o_voff = 4 * lh * o_row + 4 * col;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (an element of an ext_vector goes through a scalar first:
-          // __builtin_bit_cast on the element reads element 0)
-          const float ov = O[4 * r + e];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
-        }
-      }
-    }
-  };
-  // steps 2 and 3: re-anchor R, then the products of chunk it (it < nc)
-  auto products = [&](const int it) __attribute__((always_inline)) {
-    // ---- step 2: re-anchor R (each tile just before its first use), then
-    // the products of chunk it.  Operand loads run one k-step ahead; the T
-    // merge barrier splits the k-steps between steps 2 and 3.
-    const int lane2 = opaque(lane);
-    const int ln2 = lane2 & 31;
-    const int lh2 = lane2 >> 5;
-    mfma_result_fence(R[0]);
-    mfma_result_fence(R[1]);
-    mfma_result_fence(R[2]);
-    mfma_result_fence(R[3]);
-    Y = zero16();
-    O = zero16();
-    bf16x8 opa[2][4];
-    f32x4 fa[4];   // factors of the next tile to rescale
-    load_ops(opa[0], 0, ln2, lh2);
-    load_fac(fa, 0, lh2);
-#pragma unroll
-    for (int kk = 0; kk < KD / 16; ++kk) {
-      if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], kk + 1, ln2, lh2);
-      if ((kk & 1) == 0) rescale(kk >> 1, fa);
-      if ((kk & 1) == 1 && kk + 1 < KD / 16) load_fac(fa, (kk + 1) >> 1, lh2);
-      float x[8];
-      tile_rows_to_b(R[kk >> 1], kk & 1, x);
-      bf16x8 bh, bl;
-      split8(x, bh, bl);
-      const bf16x8(&o)[4] = opa[kk & 1];
-      Y = mfma3(o[0], o[1], bh, bl, Y);
-      if (fwd) O = mfma3(o[2], o[3], bh, bl, O);
-      if (kk == KSPLIT - 1) block_sync();   // ---- step 3 from here
-    }
-    block_sync();
-  };
-
-  for (int it = 0; it < nc; ++it) {
-    if (it >= 1) finish(it);
-    block_sync();
-    products(it);
-  }
-  finish(nc);
-  block_sync();
-  {
-    // after the last chunk: fac = e^{G_C - a} turns R back into S
-    const int lh2 = opaque(lane) >> 5;
-    mfma_result_fence(R[0]);
-    mfma_result_fence(R[1]);
-    mfma_result_fence(R[2]);
-    mfma_result_fence(R[3]);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      f32x4 f[4];
-      load_fac(f, dt, lh2);
-      rescale(dt, f);
-    }
-  }
-
-  // ---- the fragment's final state (R was rescaled by e^{G_C - a} last)
-  float* dst0 = nullptr;
-  float* dst1 = nullptr;
-  if (MODE == kModeSumPhi) {
-    dst0 = p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD;
-  } else if (MODE == kModeSumS) {
-    dst0 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
-  } else {
-    if (flags & kFragSeqEnd) dst0 = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
-    if (p.pass == 1 && (flags & kFragSegLast)) dst1 = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
-  }
-  if (dst0) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst0[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
-  }
-  if (dst1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst1[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
-  }
 }
 
 // One step of an inclusive scan across each 16-lane row: x += (x of the lane
@@ -784,250 +487,28 @@ __device__ __forceinline__ size_t cache_elem(const ChunkParams& p, const int32_t
          which * (CH * CH) + row * CH + 8 * q;
 }
 __device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) * TS + 8 * (i & 3); }
-__device__ __forceinline__ void tb_to_cache(const ChunkParams& p, const bf16* tbh, const bf16* tbl,
-                                            const int32_t seg, const int32_t beg, const int it, const int i) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(&((i >> 7) ? tbl : tbh)[cache_lds(i)]);
-  *reinterpret_cast<u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, it, i)) = v;
-}
-
-// ---------------------------------------------------------------------------
-// Helper waves (NH of them, index hw): chunk it's operands while the owners
-// finish chunk it-1.
-//   step 1  land the prefetched inputs (issued one iteration earlier), gate
-//           prefix, anchor a (token 15), G_C; Kr, Qr, Kc, V (token-major),
-//           beta and the owners' rescale fac; issue the next chunk's loads
-//   step 2  16 x 16 tile jobs: the two diagonal blocks of A = beta o (Kr Kc^T),
-//           each followed by the inverse of its block of I + A; the block A10;
-//           the three blocks of P = Qr Kc^T on or below the diagonal
-//   step 3  T10 = -T11 A10 T00 and T diag(beta), four columns per helper
-//           (helpers 0..3)
-// Thread layout of step 1: helper hw covers the channels [CPH hw, CPH hw +
-// CPH), CPH = 128 / NH.  Lane l loads one channel octet per token (16-byte
-// loads) and the 16 lanes of a DPP row hold 16 consecutive tokens of one
-// octet, so the gate prefix is a scan across the row:
-//   NH = 4: octet l/16, tokens l%16 and 16 + l%16 (two per lane)
-//   NH = 8: octet l/32, token l%32 (rows 2q and 2q+1 carry tokens 0..15 and
-//           16..31 of octet q)
-template <int MODE, int NH>
-__device__ __forceinline__ void helper_fragment(const ChunkParams& p, ChunkSmem& sm, const int hw,
-                                                const int32_t seg, const int32_t beg, const int32_t end) {
-  static_assert(NH == 4 || NH == 8, "helper layouts");
-  constexpr bool fwd = MODE == kModeFwd;
-  constexpr bool use_v = MODE != kModeSumPhi;
-  constexpr int TPL = NH == 4 ? 2 : 1;         // tokens per lane in step 1
-  constexpr int CPH = KD / NH;                 // channels per helper in step 1
-  const int h = blockIdx.y;
-  const int H = p.H;
-  const int lane = threadIdx.x & 63;
-  const int tk = NH == 4 ? (lane & 15) : (lane & 31);   // tokens tk + 16j, j < TPL
-  const int c8 = CPH * hw + 8 * (NH == 4 ? (lane >> 4) : (lane >> 5));
-  const int nc = (end - beg + CH - 1) / CH;
-  const int row_bytes = H * KD * 2;            // one token of q, k, g, v
-  const int in_voff = tk * row_bytes + 2 * c8;
-
-  // raw BF16 of the chunk being prefetched (TPL tokens x eight channels per
-  // tensor); loads past the fragment's last token return zero
-  u32x4 rk[TPL], rg[TPL], rq[TPL], rv[TPL];
-  uint32_t rb = 0u;   // beta's raw bits
-  // Branch-free: loads a mode does not need, and loads past the fragment, get
-  // a zero-size buffer (they return zero and touch no memory).
-  auto fetch = [&](int cs) {
-    const int nn = min(CH, end - cs);
-    const size_t base = (static_cast<size_t>(min(cs, end - 1)) * H + h) * KD;
-    const int nrec = nn > 0 ? (nn - 1) * row_bytes + KD * 2 : 0;
-    const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + base), 0, nrec, kBufDword3);
-    const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.g + base), 0, nrec, kBufDword3);
-    const auto rsq =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.q + base), 0, fwd ? nrec : 0, kBufDword3);
-    const auto rsv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, use_v ? nrec : 0, kBufDword3);
-#pragma unroll
-    for (int j = 0; j < TPL; ++j) {
-      const int off = in_voff + 16 * j * row_bytes;
-      rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
-      rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
-      rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
-      rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
-    }
-    // beta: helper 0's first 32 lanes read one value per token
-    const int nb = (hw == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
-    const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.beta + static_cast<size_t>(min(cs, end - 1)) * H + h), 0, nb, kBufDword3);
-    rb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane < CH ? lane * H * 2 : nb, 0, 0));
-  };
-  fetch(beg);
-
-  // (G_C - a) of the previous chunk for this lane's eight channels (log2 units)
-  float dprev[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
-
-  for (int it = 0; it < nc; ++it) {
-    // ---- step 1: operands of chunk it, and the owners' rescale
-    {
-      const int b = it & 1;
-      // update mode (a carrying fragment that ends its segment): the carry
-      // pass re-runs this fragment and reads T diag(beta) back from the cache
-      if (MODE == kModeSumS && NH == 4 && it >= 1) tb_to_cache(p, sm.tb_h, sm.tb_l, seg, beg, it - 1, 64 * hw + lane);
-      float kf[TPL][8], qf[TPL][8], G[TPL][8];
-#pragma unroll
-      for (int j = 0; j < TPL; ++j) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kf[j][2 * w] = __uint_as_float(rk[j][w] << 16);
-          kf[j][2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
-          qf[j][2 * w] = __uint_as_float(rq[j][w] << 16);
-          qf[j][2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
-          G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
-          G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
-        }
-        if (use_v) st4(&sm.vv[b][(tk + 16 * j) * NS + c8], rv[j]);
-      }
-      if (hw == 0 && lane < CH) sm.beta[lane] = __uint_as_float(rb << 16);
-      // consume the landed registers before the next loads overwrite them
-      __builtin_amdgcn_sched_barrier(0);
-      fetch(beg + (it + 1) * CH);
-
-      // inclusive gate prefix over the 16 tokens of each row (row_shr scan,
-      // stage by stage over all values so the DPP latencies overlap), then
-      // across the two halves: a = G at token 15, G_C = G at token 31
-      scan_stage<0x111, TPL>(G);   // row_shr:1
-      scan_stage<0x112, TPL>(G);   // row_shr:2
-      scan_stage<0x114, TPL>(G);   // row_shr:4
-      scan_stage<0x118, TPL>(G);   // row_shr:8
-      float a[8], gc[8];
-      if (NH == 4) {
-        // lane 15 of each row holds the row's total (swizzle: and 0x10, or 0x0f)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1F0));
-          gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[TPL - 1][c]), 0x1F0));
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          G[TPL - 1][c] += a[c];
-          gc[c] += a[c];
-        }
-      } else {
-        // rows 1 and 3 (tokens 16..31) add the totals of rows 0 and 2
-        // (row_bcast:15), then a and G_C are lanes 15 and 31 of each half wave
-        // (swizzle: or 0x0f, or 0x1f)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          G[0][c] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G[0][c]), 0x142, 0xa, 0xf, false));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          a[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x1E0));
-          gc[c] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(G[0][c]), 0x3E0));
-        }
-      }
-      if (tk == 0) {
-        float fv[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(a[c] + dprev[c]);
-        st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
-        st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dprev[c] = gc[c] - a[c];
-
-      // per element: Kr = k e^{G-a}, Kc = k e^{a-G}, Qr = q e^{G-a}
-#pragma unroll
-      for (int j = 0; j < TPL; ++j) {
-        uint32_t krh[4], krl[4], kch[4], kcl[4], qrh[4], qrl[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float kr[2], kc[2], qr[2];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const float x = G[j][2 * w + c] - a[2 * w + c];
-            const float er = __builtin_amdgcn_exp2f(x);
-            const float ec = __builtin_amdgcn_exp2f(-x);
-            kr[c] = kf[j][2 * w + c] * er;
-            kc[c] = kf[j][2 * w + c] * ec;
-            qr[c] = qf[j][2 * w + c] * er;
-          }
-          split_pair(kr[0], kr[1], krh[w], krl[w]);
-          split_pair(kc[0], kc[1], kch[w], kcl[w]);
-          if (fwd) split_pair(qr[0], qr[1], qrh[w], qrl[w]);
-        }
-        const int off = (tk + 16 * j) * NS + c8;
-        st4(&sm.kr_h[off], u32x4{krh[0], krh[1], krh[2], krh[3]});
-        st4(&sm.kr_l[off], u32x4{krl[0], krl[1], krl[2], krl[3]});
-        st4(&sm.kc_h[b][off], u32x4{kch[0], kch[1], kch[2], kch[3]});
-        st4(&sm.kc_l[b][off], u32x4{kcl[0], kcl[1], kcl[2], kcl[3]});
-        if (fwd) {
-          st4(&sm.qr_h[off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
-          st4(&sm.qr_l[off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
-        }
-      }
-    }
-    block_sync();
-
-    // ---- step 2: tile jobs.  Diagonal blocks of A and T: helpers 0 and 1;
-    // A10: helper 2; P (forward only): P00 and the zero block above it, P10,
-    // P11 on helpers 3, 4, 5 (NH = 8) or helpers 2, 3, 3 (NH = 4).
-    {
-      const int b = it & 1;
-      const int lane_s = opaque(lane);
-      const int lm = lane_s & 15;
-      const int lg = lane_s >> 4;
-      auto p_tile = [&](const int rbp, const int ctp) __attribute__((always_inline)) {
-        p_store(tile16(sm.qr_h, sm.qr_l, sm.kc_h[b], sm.kc_l[b], rbp, ctp, lm, lg), rbp, ctp, sm.p_h, sm.p_l,
-                lane_s);
-      };
-      if (hw < 2) {
-        a_diag_solve(sm.kr_h, sm.kr_l, sm.kc_h[b], sm.kc_l[b], sm.beta, sm.an, sm.tt, sm.tn, hw, lane_s);
-      } else if (hw == 2) {
-        a_offdiag(sm.kr_h, sm.kr_l, sm.kc_h[b], sm.kc_l[b], sm.beta, sm.an, lane_s);
-        if (NH == 4 && fwd) p_tile(0, 0);
-      } else if (fwd) {
-        if (NH == 4) {
-          p_tile(1, 0);
-          p_tile(1, 1);
-        } else if (hw < 6) {
-          const int q = hw - 3;   // P00, P10, P11
-          p_tile(q == 0 ? 0 : 1, q == 2 ? 1 : 0);
-        }
-      }
-    }
-    block_sync();
-
-    // ---- step 3: T10 = -T11 A10 T00 and T diag(beta), helpers 0..3
-    if (hw < 4) t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta, sm.tb_h, sm.tb_l, hw, opaque(lane));
-    block_sync();
-  }
-
-  // after the last chunk: R *= e^{G_C - a} turns R back into S
-  if (MODE == kModeSumS && NH == 4) tb_to_cache(p, sm.tb_h, sm.tb_l, seg, beg, nc - 1, 64 * hw + lane);
-  if (tk == 0) {
-    float fv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
-    st4(&sm.fac[c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
-    st4(&sm.fac[c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
-  }
-  block_sync();
-}
 
 // ===========================================================================
-// Carry launch: a two-step pipeline with three wave roles, so that the
-// operands and the UT transform of later chunks are built while the owners
-// work on the current one.
+// Both sequential kernels run each fragment as a two-step pipeline of wave
+// roles, so that the operands and the UT transform of later chunks are built
+// while the owners work on the current one:
 //
-//   owners (waves 0-3)           step 2n: products of chunk n
-//                                step 2n+1: finish chunk n
-//   operand helpers (waves 4-7)  steps 2m-3, 2m-2: operands of chunk m
-//   T helpers (waves 8-11)       steps 2m-1, 2m: A, T diag(beta), P of chunk m
+//   owners                 step 2n: products of chunk n
+//                          step 2n+1: finish chunk n
+//   operand helpers        steps 2m-3, 2m-2: operands of chunk m
+//   T helpers              steps 2m-1, 2m: A, T diag(beta), P of chunk m
 //
 // A fragment of nc chunks takes the steps -3 .. 2nc-1, each ending with a
-// workgroup barrier (every role executes 2nc + 3 of them).  Kr, Qr, Kc, V,
+// workgroup barrier (every wave executes 2nc + 3 of them).  Kr, Qr, Kc, V,
 // fac and beta are double-buffered by chunk parity; T diag(beta), P and the
 // solve scratch are single.  Who writes what, and when (m = chunk):
-//   Kr, Qr, fac, beta (m)  step 2m-3   last readers of chunk m-2: step 2m-4
+//   Kr, Qr, fac, beta (m)  step 2m-3   last readers of chunk m-2: step 2m-3
+//                                      at the latest (fac), else 2m-4
 //   Kc, V (m)              step 2m-2   last reader of chunk m-2:  step 2m-3
 //   an, tt, tn (m)         step 2m-1   last reader of chunk m-1:  step 2m-2
 //   T diag(beta), P (m)    step 2m     last reader of chunk m-1:  step 2m-1
+// fac(m) re-anchors the state for chunk m; the owners apply it at the end of
+// finish(m-1) (and fac(0) before the first chunk).
 // ===========================================================================
 struct alignas(16) PipeSmem {
   bf16 kr_h[2][CH * NS], kr_l[2][CH * NS];    // Kr = k e^{G-a}, token-major
@@ -1044,11 +525,24 @@ struct alignas(16) PipeSmem {
   float beta[2][CH];
 };
 
-// Owner wave ow of the pipeline: the forward body (o and the final state) of
-// one fragment, from the carry-in or from zero.  R, Y, O as in owner_fragment.
+// Owner wave ow: the state columns [32ow, 32ow + 32) as four 32 x 32 FP32
+// accumulator tiles R[dt] (rows 32dt + 8r + 4(l/32) + e in lane l, register
+// 4r + e; column 32ow + l%32).  R is the state scaled by the anchor of the
+// chunk it enters, e^{a} o S, which is the operand Kr and Qr multiply; one
+// update is
+//     S_new = Diag(e^{G_C}) S + K^^T U = Diag(e^{G_C - a}) (R + Kc^T U)
+// and fac = e^{a_next + G_C - a} re-anchors it for the next chunk
+// (e^{G_C - a} after the last one, which leaves S itself).  Modes:
+//   kModeFwd    from zero or from the carry-in: o and, at a sequence end,
+//               the final state
+//   kModeSumS   from zero, no o: B_r
+//   kModeSumPhi from the identity with V = 0, no o: A_r
+template <int MODE>
 __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, const int ow, const int32_t flags,
                                            const int32_t seg, const int32_t seq, const int32_t beg,
                                            const int32_t end, const bool from_carry) {
+  constexpr bool fwd = MODE == kModeFwd;
+  constexpr bool use_v = MODE != kModeSumPhi;
   const int h = blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
@@ -1060,7 +554,17 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
   f32x16 R[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
-  if (from_carry) {
+  if (MODE == kModeSumPhi) {
+    // the diagonal element of column col sits in tile col/32, register
+    // 4((col%32)/8) + col%4, of the lanes with l/32 = (col/4)%2
+    const int ln_s = opaque(lane) & 31;
+    const bool own = ((ln_s >> 2) & 1) == (lane >> 5);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        R[dt][i] = (own && dt == ow && i == 4 * (ln_s >> 3) + (ln_s & 3)) ? 1.f : 0.f;
+  } else if (from_carry) {
     const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -1077,8 +581,10 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     const int c = 16 * kk + 4 * lh;
     o[0] = ld_kslots(&sm.kr_h[b][row], c);
     o[1] = ld_kslots(&sm.kr_l[b][row], c);
-    o[2] = ld_kslots(&sm.qr_h[b][row], c);
-    o[3] = ld_kslots(&sm.qr_l[b][row], c);
+    if (fwd) {
+      o[2] = ld_kslots(&sm.qr_h[b][row], c);
+      o[3] = ld_kslots(&sm.qr_l[b][row], c);
+    }
   };
   auto load_fac = [&](f32x4 (&f)[4], const int b, const int dt, const int lh) {
 #pragma unroll
@@ -1099,7 +605,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     const int ln2 = lane2 & 31;
     const int lh2 = lane2 >> 5;
     Y = zero16();
-    O = zero16();
+    if (fwd) O = zero16();
     bf16x8 opa[2][4];
     load_ops(opa[0], b, 0, ln2, lh2);
 #pragma unroll
@@ -1111,7 +617,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
       split8(x, bh, bl);
       const bf16x8(&o)[4] = opa[kk & 1];
       Y = mfma3(o[0], o[1], bh, bl, Y);
-      O = mfma3(o[2], o[3], bh, bl, O);
+      if (fwd) O = mfma3(o[2], o[3], bh, bl, O);
     }
   };
 
@@ -1130,11 +636,16 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     f32x16 D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
-      const s16x4 v4 = lds_read_tr(
-          &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (use_v) {
+        // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
+        const s16x4 v4 = lds_read_tr(
+            &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) D[4 * r + e] = bf2f(static_cast<uint16_t>(v4[e])) - Y[4 * r + e];
+        for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
     }
     // D and U feed the next products as B operands in k-slot order (tokens):
     // T diag(beta) and P are stored in that column order, Kc^T is read in it
@@ -1150,11 +661,13 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     mfma_result_fence(U);
     bf16x8 ubh[2], ubl[2];
     tile_kslots_split(U, ubh, ubl);
+    if (fwd) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int off = ln * TS + 16 * s + 8 * lh;
-      O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
-                ubh[s], ubl[s], O);
+      for (int s = 0; s < 2; ++s) {
+        const int off = ln * TS + 16 * s + 8 * lh;
+        O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
+                  ubh[s], ubl[s], O);
+      }
     }
     // R += Kc^T U: the A operand (row = channel 32dt + l%32, k slots = tokens
     // 16s + 4(l/32) + 0..3 and 16s + 8 + 4(l/32) + 0..3) is read as column
@@ -1178,17 +691,19 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
       load_fac(f, (n + 1) & 1, dt, lh);
       rescale(dt, f);
     }
-    mfma_result_fence(O);
-    // rows past the fragment's end fall outside the buffer and are dropped
-    const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
-                                                       (nn - 1) * o_row + 4 * VD, kBufDword3);
-    const int o_voff = 4 * lh * o_row + 4 * col;
+    if (fwd) {
+      mfma_result_fence(O);
+      // rows past the fragment's end fall outside the buffer and are dropped
+      const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
+                                                         (nn - 1) * o_row + 4 * VD, kBufDword3);
+      const int o_voff = 4 * lh * o_row + 4 * col;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ov = O[4 * r + e];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+        for (int e = 0; e < 4; ++e) {
+          const float ov = O[4 * r + e];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+        }
       }
     }
   };
@@ -1212,25 +727,34 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     finish(n);
     block_sync();
   }
-  if (flags & kFragSeqEnd) {
-    float* dst = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
+  const int lane_e = opaque(lane);
+  const int lh_e = lane_e >> 5;
+  const int col_e = 32 * ow + (lane_e & 31);
+  float* dst = nullptr;
+  if (MODE == kModeSumPhi) dst = p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD;
+  else if (MODE == kModeSumS) dst = p.updates + (static_cast<size_t>(seg) * H + h) * KD * VD;
+  else if (flags & kFragSeqEnd) dst = p.final_state + (static_cast<size_t>(seq) * H + h) * KD * VD;
+  if (dst) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = R[dt][4 * r + e];
+        for (int e = 0; e < 4; ++e) dst[(32 * dt + 8 * r + 4 * lh_e + e) * (MODE == kModeSumPhi ? KD : VD) + col_e] =
+            R[dt][4 * r + e];
   }
 }
 
 // Operand helper oh (0..3) of the pipeline: channels [32oh, 32oh + 32); lane
-// l holds octet 32oh + 8(l/16) of the tokens l%16 and 16 + l%16 (the layout
-// of helper_fragment with four helpers).  Part 1 of chunk m (step 2m-3):
-// land the inputs loaded two steps earlier, issue the next chunk's loads, gate
-// prefix, fac, beta, Kr, Qr; Kc and V stay in registers until part 2 (step
-// 2m-2), when the owners are done with chunk m-2's.
+// l holds octet 32oh + 8(l/16) of the tokens l%16 and 16 + l%16.  Part 1 of
+// chunk m (step 2m-3): land the inputs loaded two steps earlier, issue the
+// next chunk's loads, gate prefix, fac, beta, Kr and (with o) Qr; Kc and V
+// stay in registers until part 2 (step 2m-2), when the owners are done with
+// chunk m-2's.
+template <int MODE>
 __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm, const int oh, const int32_t beg,
                                               const int32_t end) {
+  constexpr bool fwd = MODE == kModeFwd;
   const int h = blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
@@ -1255,7 +779,7 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
       const int off = in_voff + 16 * j * row_bytes;
       rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
       rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
-      rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
+      if (fwd) rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
       rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
     }
     const int nb = (oh == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
@@ -1282,8 +806,10 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
         for (int w = 0; w < 4; ++w) {
           kf[j][2 * w] = __uint_as_float(rk[j][w] << 16);
           kf[j][2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
-          qf[j][2 * w] = __uint_as_float(rq[j][w] << 16);
-          qf[j][2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
+          if (fwd) {
+            qf[j][2 * w] = __uint_as_float(rq[j][w] << 16);
+            qf[j][2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
+          }
           G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
           G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
         }
@@ -1331,17 +857,19 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
             const float ec = __builtin_amdgcn_exp2f(-x);
             kr[c] = kf[j][2 * w + c] * er;
             kc[c] = kf[j][2 * w + c] * ec;
-            qr[c] = qf[j][2 * w + c] * er;
+            if (fwd) qr[c] = qf[j][2 * w + c] * er;
           }
           split_pair(kr[0], kr[1], krh[w], krl[w]);
           split_pair(kc[0], kc[1], kch[j][w], kcl[j][w]);
-          split_pair(qr[0], qr[1], qrh[w], qrl[w]);
+          if (fwd) split_pair(qr[0], qr[1], qrh[w], qrl[w]);
         }
         const int off = (tk + 16 * j) * NS + c8;
         st4(&sm.kr_h[b][off], u32x4{krh[0], krh[1], krh[2], krh[3]});
         st4(&sm.kr_l[b][off], u32x4{krl[0], krl[1], krl[2], krl[3]});
-        st4(&sm.qr_h[b][off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
-        st4(&sm.qr_l[b][off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
+        if (fwd) {
+          st4(&sm.qr_h[b][off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
+          st4(&sm.qr_l[b][off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
+        }
       }
     }
     block_sync();
@@ -1368,19 +896,26 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
   block_sync();
 }
 
-// T helper th (0..3) of the pipeline.  A carrying fragment that ends its
-// segment ran in the summaries launch, which left T diag(beta) of each of its
-// chunks in the chunk cache: part 1 of chunk m (step 2m-1) loads it, part 2
-// (step 2m) stores it to LDS.  Otherwise part 1 computes the diagonal blocks
-// of A and their inverses (th 0, 1) and A10 (th 2), and part 2 merges them
-// into T diag(beta), four columns per helper.  Either way th 3 computes the
-// three blocks of P in part 1 and stores them in part 2.
+// T helper th (0..3) of the pipeline.  Part 1 of chunk m (step 2m-1) computes
+// the diagonal blocks of A and their inverses (th 0, 1) and A10 (th 2), and
+// part 2 (step 2m) merges them into T diag(beta), four columns per helper.
+// The summaries launch (FILL) also copies each chunk's T diag(beta) into the
+// chunk cache during the next chunk's part 1, while it is still in LDS.  The
+// carry launch instead loads it from the cache in part 1 and stores it to LDS
+// in part 2 for every fragment that the summaries launch ran (those that end
+// their segment), and th 3 computes the three blocks of P in part 1 and
+// stores them in part 2.
+template <bool FILL>
 __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int th, const int32_t flags,
                                              const int32_t seg, const int32_t beg, const int32_t end) {
   const int lane = threadIdx.x & 63;
   const int nc = (end - beg + CH - 1) / CH;
-  const bool cached = (flags & kFragSegLast) != 0;
+  const bool cached = !FILL && (flags & kFragSegLast) != 0;
   const int ci = 64 * th + lane;   // this lane's 16 bytes of a cached chunk
+  auto to_cache = [&](const int m) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)]);
+    *reinterpret_cast<u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, m, ci)) = v;
+  };
   block_sync();   // steps -3, -2: the operands of chunk 0 are being built
   block_sync();
   for (int m = 0; m < nc; ++m) {
@@ -1389,6 +924,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
     u32x4 tbv;
     {
       const int lane_s = opaque(lane);
+      if (FILL && m > 0) to_cache(m - 1);
       if (cached) {
         tbv = *reinterpret_cast<const u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, m, ci));
       } else if (th < 2) {
@@ -1396,7 +932,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       } else if (th == 2) {
         a_offdiag(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
       }
-      if (th == 3) {
+      if (!FILL && th == 3) {
         const int lm = lane_s & 15;
         const int lg = lane_s >> 4;
         pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
@@ -1409,7 +945,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       const int lane_s = opaque(lane);
       if (cached) st4(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)], tbv);
       else t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
-      if (th == 3) {
+      if (!FILL && th == 3) {
         p_store(pacc[0], 0, 0, sm.p_h, sm.p_l, lane_s);
         p_store(pacc[1], 1, 0, sm.p_h, sm.p_l, lane_s);
         p_store(pacc[2], 1, 1, sm.p_h, sm.p_l, lane_s);
@@ -1417,71 +953,68 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
     }
     block_sync();
   }
+  if (FILL) to_cache(nc - 1);
   block_sync();   // step 2nc-1
 }
 
-// One workgroup runs one fragment (a run of tokens of one sequence inside one
-// segment) of one head, chunk after chunk, as a two-stage pipeline: owner waves
-// hold the state in registers and apply chunk n-1 while helper waves build
-// chunk n's operands in LDS (see owner_fragment and helper_fragment); three
-// barriers per chunk.
-//
-// Summaries launch: waves 0-3 own S (forward or zero-start update), waves 4-7
-// own the transition Phi when the fragment needs one, waves 8-11 are helpers;
-// S and Phi share every operand the helpers build.
+// Helper wave with nothing to compute: keeps the barrier count of a fragment.
+__device__ __forceinline__ void pipe_idle(const int32_t beg, const int32_t end) {
+  const int nc = (end - beg + CH - 1) / CH;
+  for (int i = 0; i < 2 * nc + 3; ++i) block_sync();
+}
+
+// Summaries launch: one workgroup per fragment that ends its segment and
+// head.  Waves 0-3 own the update B_r (the fragment from a zero state),
+// waves 4-7 the transition A_r (from the identity with V = 0) when the
+// segment's sequence runs through it, else they write A_r = 0; waves 8-11
+// are the operand helpers and 12-15 the T helpers, shared by both states.
 __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkParams p) {
-  __shared__ ChunkSmem sm;
+  __shared__ PipeSmem sm;
   const int f = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int H = p.H;
-
   const int32_t flags = p.plan[p.L.frag_flags + f];
   const int32_t seg = p.plan[p.L.frag_seg + f];
+  const Work work = decode_summary(p, flags, seg);
+  if (!work.run) return;
   const int32_t seq = p.plan[p.L.frag_seq + f];
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
-  const Work work = decode_summary(p, flags, seg);
-  if (work.mode < 0) return;
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < NOWN) {
-    if (work.mode == kModeFwd) owner_fragment<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, false);
-    else owner_fragment<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, false);
+    pipe_owner<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, false);
   } else if (wave < 2 * NOWN) {
     if (work.phi) {
-      owner_fragment<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, false);
+      pipe_owner<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, false);
     } else {
-      if (work.zero_a) {
-        f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * H + h) * KD * KD);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        for (int i = tid - NOWN * 64; i < KD * KD / 4; i += NOWN * 64) dst[i] = z;
-      }
-      idle_owner(beg, end);
+      f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * p.H + h) * KD * KD);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int i = tid - NOWN * 64; i < KD * KD / 4; i += NOWN * 64) dst[i] = z;
+      pipe_idle(beg, end);
     }
+  } else if (wave < 3 * NOWN) {
+    pipe_ophelper<kModeSumS>(p, sm, wave - 2 * NOWN, beg, end);
   } else {
-    if (work.mode == kModeFwd) helper_fragment<kModeFwd, NHELP_SUM>(p, sm, wave - 2 * NOWN, seg, beg, end);
-    else helper_fragment<kModeSumS, NHELP_SUM>(p, sm, wave - 2 * NOWN, seg, beg, end);
+    pipe_thelper<true>(p, sm, wave - 3 * NOWN, flags, seg, beg, end);
   }
 }
 
-// Carry launch: each carried fragment runs again from its carry-in C_r with the
-// forward body (o and, where a sequence ends, the final state), as the
-// three-role pipeline above.
+// Carry launch: every fragment runs with the forward body (o and, where a
+// sequence ends, the final state), from its segment's carry-in C_r when it
+// continues a sequence, else from zero.
 __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams p) {
   __shared__ PipeSmem sm;
   const int f = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t flags = p.plan[p.L.frag_flags + f];
-  if (!(flags & kFragCarried)) return;
   const int32_t seg = p.plan[p.L.frag_seg + f];
   const int32_t seq = p.plan[p.L.frag_seq + f];
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave < NOWN) pipe_owner(p, sm, wave, flags, seg, seq, beg, end, true);
-  else if (wave < 2 * NOWN) pipe_ophelper(p, sm, wave - NOWN, beg, end);
-  else pipe_thelper(p, sm, wave - 2 * NOWN, flags, seg, beg, end);
+  if (wave < NOWN) pipe_owner<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, (flags & kFragCarried) != 0);
+  else if (wave < 2 * NOWN) pipe_ophelper<kModeFwd>(p, sm, wave - NOWN, beg, end);
+  else pipe_thelper<false>(p, sm, wave - 2 * NOWN, flags, seg, beg, end);
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of

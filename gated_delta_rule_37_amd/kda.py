@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.kda_summary_bytes.restype = sz
     L.kda_chunk_cache_bytes.argtypes = [p, i32]
     L.kda_chunk_cache_bytes.restype = sz
-    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p, p]
+    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
     L.kda_segment_summaries.restype = ctypes.c_int
     L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, p, p]
     L.kda_compose_summaries.restype = ctypes.c_int
@@ -176,14 +176,15 @@ def _stream(t: torch.Tensor, stream):
 
 
 def _inputs(plan: Plan, q, k, v, g, beta):
-    T, H, K = q.shape
+    """Shapes and device addresses of (q,) k, v, g, beta; q may be None."""
+    T, H, K = k.shape
     V = v.shape[2]
     if T != plan.T:
         raise ValueError(f"inputs hold {T} tokens, the plan {plan.T}")
-    return H, K, V, [
-        _ptr(q, torch.bfloat16, (T, H, K), "q"), _ptr(k, torch.bfloat16, (T, H, K), "k"),
-        _ptr(v, torch.bfloat16, (T, H, V), "v"), _ptr(g, torch.bfloat16, (T, H, K), "g"),
-        _ptr(beta, torch.bfloat16, (T, H), "beta"),
+    ptrs = [] if q is None else [_ptr(q, torch.bfloat16, (T, H, K), "q")]
+    return H, K, V, ptrs + [
+        _ptr(k, torch.bfloat16, (T, H, K), "k"), _ptr(v, torch.bfloat16, (T, H, V), "v"),
+        _ptr(g, torch.bfloat16, (T, H, K), "g"), _ptr(beta, torch.bfloat16, (T, H), "beta"),
     ]
 
 
@@ -192,19 +193,17 @@ def _cache_ptr(plan: Plan, H: int, chunk_cache) -> int:
     return _ptr(chunk_cache, torch.uint8, (n,), "chunk_cache")
 
 
-def segment_summaries(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, o, final_state,
-                      transitions, updates, chunk_cache, stream=None):
-    """``kda_segment_summaries``: zero-start pass over every segment."""
-    H, K, V, ins = _inputs(plan, q, k, v, g, beta)
+def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transitions, updates,
+                      chunk_cache, stream=None):
+    """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment."""
+    H, K, V, ins = _inputs(plan, None, k, v, g, beta)
     outs = [
-        _ptr(o, torch.float32, (plan.T, H, V), "o"),
-        _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state"),
         _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
         _ptr(updates, torch.float32, (plan.S, H, K, V), "updates"),
         _cache_ptr(plan, H, chunk_cache),
     ]
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *outs, _stream(q, stream))
+    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *outs, _stream(k, stream))
     _check(st, "kda_segment_summaries")
 
 
@@ -224,7 +223,7 @@ def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, 
 
 def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
                 chunk_cache, stream=None):
-    """``kda_apply_carry``: re-run each carrying segment's first fragment from C_r."""
+    """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r."""
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
     oo = _ptr(o, torch.float32, (plan.T, H, V), "o")
@@ -256,8 +255,8 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None):
     if out is None:
         out = alloc_outputs(plan, H, K, V, q.device)
     pd = plan.device_blob(q.device)
-    segment_summaries(plan, pd, q, k, v, g, beta, out["o"], out["final_state"],
-                      out["transitions"], out["updates"], out["chunk_cache"], stream)
+    segment_summaries(plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"],
+                      stream)
     compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], stream)
     apply_carry(plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
                 out["chunk_cache"], stream)

@@ -18,10 +18,10 @@
  *   K x K transition A_r and the K x V update B_r (#136 Summary:
  *   preceding_transition / preceding_state_update; #110 Motivation: affine
  *   recurrence state).  An ordered FP32 scan composes them into carry-in
- *   states C_r (#136 Summary: affine summary composition in FP32), and each
- *   segment whose first token continues a sequence re-runs its first
- *   fragment from C_r (#136 Sequence Diagram: the forward consumes the
- *   gathered preceding summaries).
+ *   states C_r (#136 Summary: affine summary composition in FP32), and the
+ *   forward runs every segment from its carry-in, writing o and the final
+ *   states (#136 Sequence Diagram: the forward consumes the gathered
+ *   preceding summaries).
  *
  * Call order for one forward pass, all on one stream:
  *     kda_plan_segments        (host, once; reusable)
@@ -132,8 +132,9 @@ size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
  * kda_chunk_cache_bytes -- bytes of the chunk cache that kda_segment_summaries
  * fills and kda_apply_carry reads: the per-chunk factor T diag(beta) of the
  * UT form of the recurrence (T = (I + A)^{-1}, A_ij = beta_i k_i^T
- * Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token chunk) of the
- * carrying fragments, so that the carry pass does not rebuild it.  This is
+ * Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token chunk) of every
+ * fragment that ends its segment, so that the carry pass does not rebuild
+ * it.  This is
  * an implementation cache, not part of the method: its contents are opaque
  * and valid only between the two calls on the same plan, H and inputs.
  * Size: (ceil(T / 32) + S) * H * 4096.  Returns 0 for a NULL plan or H <= 0.
@@ -141,7 +142,7 @@ size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
 
 /*
- * kda_segment_summaries -- every segment from a zero state.
+ * kda_segment_summaries -- the affine summary of every segment.
  * #136 Summary (preceding_state_update / preceding_transition), #110
  * Motivation (each producer computes its affine recurrence state).
  *
@@ -152,24 +153,18 @@ size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
  *                     latest on the left, when segment r carries in and no
  *                     sequence starts inside it; otherwise exactly 0 (the
  *                     reset's linear part);
- *   o[t]            for every token t outside the first fragment of a
- *                     carrying segment (those tokens start from a true zero
- *                     state, so o is final there);
- *   final_state[n]  for every sequence whose last token lies outside the
- *                     first fragment of a carrying segment.
- *   chunk_cache     the chunk factors of every carrying fragment that ends
- *                   its segment (kda_chunk_cache_bytes).
- * The remaining rows of o and final_state are written by kda_apply_carry.
+ *   chunk_cache     the chunk factors of every fragment that ends its
+ *                   segment (kda_chunk_cache_bytes).
+ * It reads no q and writes no o or final state: kda_apply_carry does.
  *   plan_dev     device copy of kda_plan_blob(plan).
  *   chunk_cache  device buffer of kda_chunk_cache_bytes(plan, H) bytes,
  *                16-byte aligned, owned by the caller.
  */
 int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                          const uint16_t* g, const uint16_t* beta,
-                          int32_t H, int32_t K, int32_t V,
-                          float* o, float* final_state, float* transitions, float* updates,
-                          void* chunk_cache, hipStream_t stream);
+                          const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                          const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                          float* transitions, float* updates, void* chunk_cache,
+                          hipStream_t stream);
 
 /*
  * kda_compose_summaries -- ordered FP32 scan C_0 = 0, C_{r+1} = A_r C_r + B_r.
@@ -184,10 +179,12 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
                           hipStream_t stream);
 
 /*
- * kda_apply_carry -- apply each carrying segment's carry-in C_r to its
- * outputs: re-run the segment's first fragment starting from C_r, writing
- * its rows of o and, when the fragment ends a sequence, that sequence's
- * final_state.  #136 Summary (the forward that consumes
+ * kda_apply_carry -- the forward with the carry applied: every fragment (a
+ * run of one sequence's tokens inside one segment) starts from its
+ * segment's carry-in C_r when it continues a sequence, else from zero, and
+ * writes its rows of o and, when it ends a sequence, that sequence's
+ * final_state.  Every row of o and every final state is written here.
+ * #136 Summary (the forward that consumes
  * preceding_state_update / preceding_transition), #110 Motivation (rank 1
  * consumes only the V-state it needs).
  *   chunk_cache  the buffer kda_segment_summaries filled for the same plan,

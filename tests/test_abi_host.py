@@ -106,10 +106,10 @@ def test_chunk_cache_bytes():
 _FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereferenced
 
 
-def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, q=_FAKE, o=_FAKE, cache=_FAKE):
+def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, k=_FAKE, upd=_FAKE, cache=_FAKE):
     L = kda.lib()
-    return L.kda_segment_summaries(plan.handle, plan_dev, q, _FAKE, _FAKE, _FAKE, _FAKE,
-                                   H, K, V, o, _FAKE, _FAKE, _FAKE, cache, None)
+    return L.kda_segment_summaries(plan.handle, plan_dev, k, _FAKE, _FAKE, _FAKE,
+                                   H, K, V, _FAKE, upd, cache, None)
 
 
 def test_device_calls_validate_before_launch():
@@ -119,15 +119,15 @@ def test_device_calls_validate_before_launch():
     assert _call_summaries(plan, H=0) == -1
     assert _call_summaries(plan, H=70000) == -4
     assert _call_summaries(plan, plan_dev=0) == -1
-    assert _call_summaries(plan, q=0) == -1
-    assert _call_summaries(plan, q=_FAKE + 2) == -5
-    assert _call_summaries(plan, o=_FAKE + 8) == -5
+    assert _call_summaries(plan, k=0) == -1
+    assert _call_summaries(plan, k=_FAKE + 2) == -5
+    assert _call_summaries(plan, upd=_FAKE + 8) == -5
     assert _call_summaries(plan, plan_dev=_FAKE + 4) == -5
     assert _call_summaries(plan, cache=0) == -1
     assert _call_summaries(plan, cache=_FAKE + 8) == -5
     L = kda.lib()
-    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                                   _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None) == -1
+    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                                   _FAKE, _FAKE, _FAKE, None) == -1
     assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, _FAKE, None) == -4
     assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, _FAKE, None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
