@@ -187,12 +187,33 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   lo = pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
 }
 
+// The same split for inputs that are dead afterwards, one instruction
+// cheaper per element: v_dot2c_f32_bf16 adds the exact bf16 products
+// h.e * m.e to x in place, and with m = (-1, 0) or (0, -1) the result x - h.e
+// is representable, hence exact (checked bitwise on gfx950 against the
+// subtraction above).  The multipliers go through an SGPR because the
+// compiler would otherwise encode them as the inline constant -1.0, which the
+// instruction reads as the 32-bit float, not as a bf16 pair.
+__device__ __forceinline__ bf16x2 sgpr_bf16x2(uint32_t bits) {
+  asm("" : "+s"(bits));
+  return __builtin_bit_cast(bf16x2, bits);
+}
+__device__ __forceinline__ void split_pair_dead(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const f32x2 v = {x0, x1};
+  const bf16x2 h = __builtin_convertvector(v, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = pack_bf16(__builtin_amdgcn_fdot2_f32_bf16(h, sgpr_bf16x2(0x0000bf80u), x0, false),
+                 __builtin_amdgcn_fdot2_f32_bf16(h, sgpr_bf16x2(0xbf800000u), x1, false));
+}
+
+template <bool DEAD = false>
 __device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo) {
   u32x4 h, l;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t a, b;
-    split_pair(x[2 * w], x[2 * w + 1], a, b);
+    if (DEAD) split_pair_dead(x[2 * w], x[2 * w + 1], a, b);
+    else split_pair(x[2 * w], x[2 * w + 1], a, b);
     h[w] = a;
     l[w] = b;
   }
@@ -258,7 +279,7 @@ __device__ __forceinline__ void tile_kslots_split(const f32x16& t, bf16x8 bh[2],
   for (int s = 0; s < 2; ++s) {
     float x[8];
     tile_kslots(t, s, x);
-    split8(x, bh[s], bl[s]);
+    split8<true>(x, bh[s], bl[s]);
   }
 }
 // A operand in k-slot order from a row-major bf16 matrix: row + c and
@@ -797,7 +818,9 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
     const int b = m & 1;
     uint32_t kch[2][4], kcl[2][4];
     u32x4 vkeep[2];
-    // ---- part 1 (step 2m-3)
+    // ---- part 1 (step 2m-3); in the carry launch this is the longest
+    // chain of its step, so it goes ahead of the (younger) T helpers
+    if (fwd) __builtin_amdgcn_s_setprio(2);
     {
       float kf[2][8], qf[2][8], G[2][8];
 #pragma unroll
@@ -859,9 +882,9 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
             kc[c] = kf[j][2 * w + c] * ec;
             if (fwd) qr[c] = qf[j][2 * w + c] * er;
           }
-          split_pair(kr[0], kr[1], krh[w], krl[w]);
-          split_pair(kc[0], kc[1], kch[j][w], kcl[j][w]);
-          if (fwd) split_pair(qr[0], qr[1], qrh[w], qrl[w]);
+          split_pair_dead(kr[0], kr[1], krh[w], krl[w]);
+          split_pair_dead(kc[0], kc[1], kch[j][w], kcl[j][w]);
+          if (fwd) split_pair_dead(qr[0], qr[1], qrh[w], qrl[w]);
         }
         const int off = (tk + 16 * j) * NS + c8;
         st4(&sm.kr_h[b][off], u32x4{krh[0], krh[1], krh[2], krh[3]});
@@ -873,6 +896,7 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
       }
     }
     block_sync();
+    if (fwd) __builtin_amdgcn_s_setprio(0);
     // ---- part 2 (step 2m-2)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -922,6 +946,10 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
     const int b = m & 1;
     f32x4 pacc[3];
     u32x4 tbv;
+    // the solves are the longest chain of the summaries launch's step 2m-1;
+    // without a raised priority the T helpers, the youngest waves, lose
+    // every issue slot to the others
+    if (FILL) __builtin_amdgcn_s_setprio(3);
     {
       const int lane_s = opaque(lane);
       if (FILL && m > 0) to_cache(m - 1);
@@ -941,6 +969,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       }
     }
     block_sync();
+    if (FILL) __builtin_amdgcn_s_setprio(0);
     {
       const int lane_s = opaque(lane);
       if (cached) st4(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)], tbv);

@@ -81,6 +81,8 @@ def state_errors(got, ref, min_scale=0.0):
         for h in range(ref.shape[1]):
             scale = float(np.abs(ref[idx, h]).max())
             err = float(np.abs(got[idx, h] - ref[idx, h]).max())
+            if not np.isfinite(err):
+                return float("inf")   # a NaN must not vanish in max()
             if min_scale > 0.0 and scale < min_scale:
                 continue
             if scale == 0.0:
@@ -93,6 +95,9 @@ def state_errors(got, ref, min_scale=0.0):
 
 def compare(got, ref, label=""):
     """Assert every tolerance; return the measured errors for reporting."""
+    for key in ("o", "final", "A", "B", "C"):
+        if key in got and (key != "o" or "o" in ref):
+            assert np.isfinite(got[key]).all(), f"[{label}] non-finite values in {key}"
     errs = {}
     if "o" in ref:
         errs["o_abs"] = float(np.abs(got["o"] - ref["o"]).max())
