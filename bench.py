@@ -1,11 +1,13 @@
 """Benchmark of the segmented KDA forward pass on one MI355X.
 
 One step = one whole forward over one batch of resident synthetic input:
-kda_segment_summaries + kda_compose_summaries + kda_apply_carry (the plan is
-built once and reused, as the pages' reusable shard plans are).  Prints one
-JSON line.
+kda_segment_summaries + kda_compose_summaries + kda_apply_carry over all
+heads (the plan is built once and reused, as the pages' reusable shard plans
+are).  The heads are cut into --groups groups: summaries and carry launches run
+on the main stream, each group's compose on a second stream once that group's
+summaries are done.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--groups G]
 
 Workload default: 65536 packed tokens of one sequence, H = 32, K = V = 128, 64
 equal segments (the 64-shard, 32-head configuration whose FP32 summary
@@ -219,6 +221,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t65536_h32_s64")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="head groups per step; each group's compose overlaps other groups' work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=16384)
@@ -256,44 +260,39 @@ def main():
     out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev)
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        kda.segment_summaries(plan, pd, d["k"], d["v"], d["g"], d["beta"], out["transitions"],
-                              out["updates"], out["chunk_cache"])
-        if ev is not None:
-            ev[1].record()
-        kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"])
-        if ev is not None:
-            ev[2].record()
-        kda.apply_carry(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["carry_in"],
-                        out["o"], out["final_state"], out["chunk_cache"])
-        if ev is not None:
-            ev[3].record()
+        kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], out=out, groups=args.groups,
+                    events=ev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    sums = [0.0, 0.0, 0.0]
-    for ev in events:
-        for j in range(3):
-            sums[j] += ev[j].elapsed_time(ev[j + 1])
-    pass1_ms, compose_ms, pass2_ms = (s / args.steps for s in sums)
+    # per launch: each kind has steps * groups launches, each over one head group
+    n_launch = {kind: len(pairs) for kind, pairs in events.items()}
+    launch_ms = {kind: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+                 for kind, pairs in events.items()}
+    per_step = {kind: launch_ms[kind] * n_launch[kind] / args.steps for kind in launch_ms}
+    groups = n_launch["summaries"] // args.steps
+    pass1_ms, compose_ms, pass2_ms = per_step["summaries"], per_step["compose"], per_step["carry"]
 
     blob = plan.blob
     cw = chunk_kernel_work(blob, w.H)
-    launches = {"kda_chunk_kernel": (cw["summaries"], pass1_ms), "kda_carry_kernel": (cw["carry"], pass2_ms)}
+    # one launch covers 1/groups of the heads: its work is the step's / groups
+    # (groups of equal size; the bench workload's 32 heads split evenly)
+    launches = {"kda_chunk_kernel": (cw["summaries"], launch_ms["summaries"]),
+                "kda_carry_kernel": (cw["carry"], launch_ms["carry"])}
 
     def roofline(name):
         wk, ms = launches[name]
+        wk = {key: val / groups for key, val in wk.items()}
         t_mfma = wk["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3
         t_hbm = wk["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
         if t_mfma >= t_hbm:
@@ -307,11 +306,12 @@ def main():
         r["traffic"] = traffic_from_profile(name)
         r["kernel"] = name
         r["launch_ms_avg"] = round(ms, 4)
+        r["launches_per_step"] = groups
         r["bounds_ms"] = {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)}
         return r
 
     # the dominant kernel of the step is the longer of the two chunk launches
-    dominant = "kda_chunk_kernel" if pass1_ms >= pass2_ms else "kda_carry_kernel"
+    dominant = "kda_chunk_kernel" if launch_ms["summaries"] >= launch_ms["carry"] else "kda_carry_kernel"
     roof = roofline(dominant)
     other = roofline("kda_carry_kernel" if dominant == "kda_chunk_kernel" else "kda_chunk_kernel")
 
@@ -333,8 +333,11 @@ def main():
         "dtype": "bf16 in, fp32 state (split-bf16 MFMA)",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
-                   "segments": w.segments, "sequences": plan.N, "seed": w.seed},
+                   "segments": w.segments, "sequences": plan.N, "seed": w.seed,
+                   "head_groups": groups},
         "roofline": roof,
+        # summed launch durations per step; with head groups the compose
+        # launches overlap the other two on a second stream
         "kernels_ms": {"segment_summaries": round(pass1_ms, 4),
                        "compose_summaries": round(compose_ms, 4),
                        "apply_carry": round(pass2_ms, 4)},

@@ -24,6 +24,11 @@ int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t
   return KDA_OK;
 }
 
+int check_heads(int32_t H, int32_t head_begin, int32_t head_count) {
+  if (head_begin < 0 || head_count <= 0 || head_count > H - head_begin) return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
 int check_tensors(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs) {
     if (p == nullptr) return KDA_ERR_INVALID_ARG;
@@ -56,9 +61,12 @@ extern "C" size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H) {
 extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                                      const uint16_t* k, const uint16_t* v, const uint16_t* g,
                                      const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                                     int32_t head_begin, int32_t head_count,
                                      float* transitions, float* updates, void* chunk_cache,
                                      hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   st = check_tensors({k, v, g, beta, transitions, updates, chunk_cache});
   if (st != KDA_OK) return st;
@@ -66,6 +74,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.plan = plan_dev;
   p.L = plan->layout;
   p.H = H;
+  p.h0 = head_begin;
   p.q = nullptr;
   p.k = k;
   p.v = v;
@@ -78,14 +87,17 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.carry = nullptr;
   p.chunk_cache = static_cast<uint16_t*>(chunk_cache);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, H, 1), dim3(kda::kSummaryThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, head_count, 1), dim3(kda::kSummaryThreads), 0, stream, p);
   return finish_launch();
 }
 
 extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
                                      const float* transitions, const float* updates, int32_t H,
-                                     int32_t K, int32_t V, float* carry_in, hipStream_t stream) {
+                                     int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                                     float* carry_in, hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   st = check_tensors({transitions, updates, carry_in});
   if (st != KDA_OK) return st;
@@ -93,13 +105,15 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
   p.plan = plan_dev;
   p.L = plan->layout;
   p.H = H;
+  p.h0 = head_begin;
+  p.hn = head_count;
   p.S = plan->S;
   p.transitions = transitions;
   p.updates = updates;
   p.carry = carry_in;
   (void)hipGetLastError();
   // one workgroup per (head, column block), heads padded to a multiple of 8
-  const int blocks = ((H + 7) / 8) * 8 * kda::kComposeColumnBlocks;
+  const int blocks = ((head_count + 7) / 8) * 8 * kda::kComposeColumnBlocks;
   hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(blocks), dim3(kda::kComposeThreads), 0, stream, p);
   return finish_launch();
 }
@@ -107,9 +121,12 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
 extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q,
                                const uint16_t* k, const uint16_t* v, const uint16_t* g,
                                const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                               int32_t head_begin, int32_t head_count,
                                const float* carry_in, float* o, float* final_state,
                                const void* chunk_cache, hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   st = check_tensors({q, k, v, g, beta, carry_in, o, final_state, chunk_cache});
   if (st != KDA_OK) return st;
@@ -117,6 +134,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.plan = plan_dev;
   p.L = plan->layout;
   p.H = H;
+  p.h0 = head_begin;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -129,6 +147,6 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.carry = carry_in;
   p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(chunk_cache));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, H, 1), dim3(kda::kCarryThreads), 0, stream, p);
+  hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, head_count, 1), dim3(kda::kCarryThreads), 0, stream, p);
   return finish_launch();
 }

@@ -19,7 +19,8 @@ constexpr int kComposeColumnBlocks = 4;  // 128 state columns / 32 per workgroup
 struct ChunkParams {
   const int32_t* plan;   // device copy of the plan blob
   BlobLayout L;
-  int32_t H;
+  int32_t H;             // heads in the tensors (their stride)
+  int32_t h0;            // first head of this launch (grid y covers the rest)
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -47,7 +48,9 @@ __host__ __device__ inline int64_t chunk_cache_slot(int32_t seg, int32_t frag_be
 struct ComposeParams {
   const int32_t* plan;
   BlobLayout L;
-  int32_t H;
+  int32_t H;    // heads in the tensors
+  int32_t h0;   // heads [h0, h0 + hn) are composed by this launch
+  int32_t hn;
   int32_t S;
   const float* transitions;
   const float* updates;

@@ -504,7 +504,7 @@ __device__ __forceinline__ size_t cache_elem(const ChunkParams& p, const int32_t
   const int which = i >> 7;
   const int row = (i >> 2) & 31;
   const int q = i & 3;
-  return (static_cast<size_t>(chunk_cache_slot(seg, beg, it)) * p.H + blockIdx.y) * (kChunkCacheBytes / 2) +
+  return (static_cast<size_t>(chunk_cache_slot(seg, beg, it)) * p.H + p.h0 + blockIdx.y) * (kChunkCacheBytes / 2) +
          which * (CH * CH) + row * CH + 8 * q;
 }
 __device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) * TS + 8 * (i & 3); }
@@ -564,7 +564,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
                                            const int32_t end, const bool from_carry) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
-  const int h = blockIdx.y;
+  const int h = p.h0 + blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
   const int lh = lane >> 5;
@@ -776,7 +776,7 @@ template <int MODE>
 __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm, const int oh, const int32_t beg,
                                               const int32_t end) {
   constexpr bool fwd = MODE == kModeFwd;
-  const int h = blockIdx.y;
+  const int h = p.h0 + blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
   const int tk = lane & 15;                    // tokens tk and 16 + tk
@@ -1000,7 +1000,7 @@ __device__ __forceinline__ void pipe_idle(const int32_t beg, const int32_t end) 
 __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ PipeSmem sm;
   const int f = blockIdx.x;
-  const int h = blockIdx.y;
+  const int h = p.h0 + blockIdx.y;
   const int tid = threadIdx.x;
   const int32_t flags = p.plan[p.L.frag_flags + f];
   const int32_t seg = p.plan[p.L.frag_seg + f];
@@ -1059,8 +1059,9 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
   const int xcd = blockIdx.x % 8;
   const int kq = blockIdx.x / 8;
   const int cb = kq % kComposeColumnBlocks;
-  const int h = xcd + 8 * (kq / kComposeColumnBlocks);
-  if (h >= H) return;
+  const int hl = xcd + 8 * (kq / kComposeColumnBlocks);
+  if (hl >= p.hn) return;
+  const int h = p.h0 + hl;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -1138,14 +1139,14 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
       for (int kk = 0; kk < KD / 16; ++kk) {
         const float xv[8] = {a_c[kk][0][0], a_c[kk][0][1], a_c[kk][0][2], a_c[kk][0][3],
                              a_c[kk][1][0], a_c[kk][1][1], a_c[kk][1][2], a_c[kk][1][3]};
-        split8(xv, ah[kk], al[kk]);
+        split8<true>(xv, ah[kk], al[kk]);
       }
       mfma_result_fence(cur);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float x[8];
         tile_rows_to_b(cur, s, x);
-        split8(x, cbh[2 * wave + s][lane], cbl[2 * wave + s][lane]);
+        split8<true>(x, cbh[2 * wave + s][lane], cbl[2 * wave + s][lane]);
       }
       __syncthreads();
       // two accumulation chains (even and odd k-steps) halve the dependent

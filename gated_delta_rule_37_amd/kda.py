@@ -11,7 +11,8 @@ Entry points mirror the C names:
 * :func:`segment_summaries` (``kda_segment_summaries``)
 * :func:`compose_summaries` (``kda_compose_summaries``)
 * :func:`apply_carry` (``kda_apply_carry``)
-* :func:`forward` runs the three device calls in order on fresh output buffers.
+* :func:`forward` runs the three device calls in order (optionally per head
+  group, with the compose launches on a second stream) on fresh output buffers.
 """
 from __future__ import annotations
 
@@ -82,11 +83,11 @@ def lib() -> ctypes.CDLL:
     L.kda_summary_bytes.restype = sz
     L.kda_chunk_cache_bytes.argtypes = [p, i32]
     L.kda_chunk_cache_bytes.restype = sz
-    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, i32, i32, i32, p, p, p, p]
+    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p]
     L.kda_segment_summaries.restype = ctypes.c_int
-    L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, p, p]
+    L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, p, p, p, p]
+    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p]
     L.kda_apply_carry.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -188,14 +189,20 @@ def _inputs(plan: Plan, q, k, v, g, beta):
     ]
 
 
+def _heads(H: int, heads):
+    """(head_begin, head_count) of a call: all heads when ``heads`` is None."""
+    return (0, H) if heads is None else (int(heads[0]), int(heads[1]))
+
+
 def _cache_ptr(plan: Plan, H: int, chunk_cache) -> int:
     n = plan.chunk_cache_bytes(H)
     return _ptr(chunk_cache, torch.uint8, (n,), "chunk_cache")
 
 
 def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transitions, updates,
-                      chunk_cache, stream=None):
-    """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment."""
+                      chunk_cache, stream=None, heads=None):
+    """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment,
+    for the heads ``heads = (begin, count)`` (default: all)."""
     H, K, V, ins = _inputs(plan, None, k, v, g, beta)
     outs = [
         _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
@@ -203,12 +210,13 @@ def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transit
         _cache_ptr(plan, H, chunk_cache),
     ]
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *outs, _stream(k, stream))
+    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), *outs,
+                                     _stream(k, stream))
     _check(st, "kda_segment_summaries")
 
 
 def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, carry_in,
-                      stream=None):
+                      stream=None, heads=None):
     """``kda_compose_summaries``: ordered FP32 scan of the summaries."""
     S, H, K, _ = transitions.shape
     V = updates.shape[3]
@@ -216,13 +224,13 @@ def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, 
     b = _ptr(updates, torch.float32, (plan.S, H, K, V), "updates")
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_compose_summaries(plan.handle, pd, a, b, H, K, V, c,
+    st = lib().kda_compose_summaries(plan.handle, pd, a, b, H, K, V, *_heads(H, heads), c,
                                      _stream(transitions, stream))
     _check(st, "kda_compose_summaries")
 
 
 def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
-                chunk_cache, stream=None):
+                chunk_cache, stream=None, heads=None):
     """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r."""
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
@@ -230,7 +238,8 @@ def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, 
     ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
     cc = _cache_ptr(plan, H, chunk_cache)
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, c, oo, ff, cc, _stream(q, stream))
+    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), c, oo, ff, cc,
+                               _stream(q, stream))
     _check(st, "kda_apply_carry")
 
 
@@ -248,16 +257,93 @@ def alloc_outputs(plan: Plan, H: int, K: int, V: int, device):
     )
 
 
-def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None):
-    """The whole segmented forward: summaries, compose, carry.  Returns ``out``."""
+def head_groups(H: int, groups: int):
+    """Split heads 0..H-1 into at most ``groups`` contiguous (begin, count) runs."""
+    groups = max(1, min(int(groups), H))
+    base, extra = divmod(H, groups)
+    runs, h = [], 0
+    for i in range(groups):
+        n = base + (1 if i < extra else 0)
+        runs.append((h, n))
+        h += n
+    return runs
+
+
+_side_streams = {}
+
+
+def _side_stream(device) -> torch.cuda.Stream:
+    """A second stream per device (default priority) for the compose launches."""
+    device = torch.device(device)
+    s = _side_streams.get(device)
+    if s is None:
+        s = torch.cuda.Stream(device=device)
+        _side_streams[device] = s
+    return s
+
+
+def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, events=None):
+    """The whole segmented forward: summaries, compose, carry.  Returns ``out``.
+
+    With ``groups`` > 1 the heads are cut into that many groups.  Summaries and
+    carry launches of every group run in order on ``stream``; each group's
+    compose runs on a second stream as soon as its summaries are done, so it
+    overlaps the next groups' summaries and the earlier groups' carry.  Heads
+    are independent, so the results do not depend on ``groups``.
+
+    ``events``, if given, is a dict that receives per-launch (start, end) HIP
+    event pairs under "summaries", "compose" and "carry", each recorded on the
+    stream of its launch (for timing)."""
     T, H, K = q.shape
     V = v.shape[2]
     if out is None:
         out = alloc_outputs(plan, H, K, V, q.device)
     pd = plan.device_blob(q.device)
-    segment_summaries(plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"],
-                      stream)
-    compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], stream)
-    apply_carry(plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-                out["chunk_cache"], stream)
+    main = torch.cuda.current_stream(q.device) if stream is None else stream
+    runs = head_groups(H, groups)
+
+    def timed(kind, st, fn):
+        if events is None:
+            fn()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        events.setdefault(kind, []).append((e0, e1))
+
+    if len(runs) == 1:
+        timed("summaries", main, lambda: segment_summaries(
+            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main))
+        timed("compose", main, lambda: compose_summaries(
+            plan, pd, out["transitions"], out["updates"], out["carry_in"], main))
+        timed("carry", main, lambda: apply_carry(
+            plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
+            out["chunk_cache"], main))
+        return out
+
+    side = _side_stream(q.device)
+    done_s, done_c = [], []
+    for hr in runs:
+        timed("summaries", main, lambda hr=hr: segment_summaries(
+            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main,
+            heads=hr))
+        ev = torch.cuda.Event()
+        ev.record(main)
+        done_s.append(ev)
+    for hr, ev in zip(runs, done_s):
+        side.wait_event(ev)
+        timed("compose", side, lambda hr=hr: compose_summaries(
+            plan, pd, out["transitions"], out["updates"], out["carry_in"], side, heads=hr))
+        evc = torch.cuda.Event()
+        evc.record(side)
+        done_c.append(evc)
+    for hr, evc in zip(runs, done_c):
+        main.wait_event(evc)
+        timed("carry", main, lambda hr=hr: apply_carry(
+            plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
+            out["chunk_cache"], main, heads=hr))
+    # every launch on the side stream precedes the last carry launch on main,
+    # so work issued later on main is ordered after all of it
     return out

@@ -48,6 +48,14 @@
  *       o       : [T, H, V] fp32        final_state : [N, H, K, V] fp32
  *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
  *       chunk_cache : kda_chunk_cache_bytes(plan, H) bytes of device memory
+ *   - Head range: each device call works on the heads [head_begin,
+ *     head_begin + head_count) of tensors that hold H heads, and touches no
+ *     other head's data (outputs included).  Heads are independent, so the
+ *     three calls may be issued per head group, and the compose of one group
+ *     may run on another stream while the next group's summaries run; the
+ *     caller orders the calls of one group (summaries, compose, carry).
+ *     head_begin < 0, head_count < 1 or head_begin + head_count > H gives
+ *     KDA_ERR_INVALID_ARG.
  *   - Device calls are asynchronous on `stream`; launch failures are reported
  *     as KDA_ERR_HIP (kda_last_hip_error() gives the hipError_t).
  *   - Supported gate domain: g <= 0 and finite, with the decay mass of any 16
@@ -134,9 +142,9 @@ size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
  * UT form of the recurrence (T = (I + A)^{-1}, A_ij = beta_i k_i^T
  * Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token chunk) of every
  * fragment that ends its segment, so that the carry pass does not rebuild
- * it.  This is
- * an implementation cache, not part of the method: its contents are opaque
- * and valid only between the two calls on the same plan, H and inputs.
+ * it.  This is an implementation cache, not part of the method: its contents
+ * are opaque, and what kda_segment_summaries writes for a head is valid for
+ * kda_apply_carry on the same plan, H, head and inputs.
  * Size: (ceil(T / 32) + S) * H * 4096.  Returns 0 for a NULL plan or H <= 0.
  */
 size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
@@ -163,6 +171,7 @@ size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
 int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                           const uint16_t* k, const uint16_t* v, const uint16_t* g,
                           const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                          int32_t head_begin, int32_t head_count,
                           float* transitions, float* updates, void* chunk_cache,
                           hipStream_t stream);
 
@@ -175,7 +184,8 @@ int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
  */
 int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
                           const float* transitions, const float* updates,
-                          int32_t H, int32_t K, int32_t V, float* carry_in,
+                          int32_t H, int32_t K, int32_t V,
+                          int32_t head_begin, int32_t head_count, float* carry_in,
                           hipStream_t stream);
 
 /*
@@ -193,7 +203,8 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
 int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* g, const uint16_t* beta,
-                    int32_t H, int32_t K, int32_t V, const float* carry_in,
+                    int32_t H, int32_t K, int32_t V,
+                    int32_t head_begin, int32_t head_count, const float* carry_in,
                     float* o, float* final_state, const void* chunk_cache,
                     hipStream_t stream);
 

@@ -106,10 +106,38 @@ def test_chunk_cache_bytes():
 _FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereferenced
 
 
-def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, k=_FAKE, upd=_FAKE, cache=_FAKE):
+def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, k=_FAKE, upd=_FAKE, cache=_FAKE,
+                    h0=0, hn=None):
     L = kda.lib()
     return L.kda_segment_summaries(plan.handle, plan_dev, k, _FAKE, _FAKE, _FAKE,
-                                   H, K, V, _FAKE, upd, cache, None)
+                                   H, K, V, h0, H if hn is None else hn, _FAKE, upd, cache, None)
+
+
+def test_head_ranges_validate_before_launch():
+    plan = kda.Plan([0, 100], 2)
+    L = kda.lib()
+    # every call below also has a misaligned pointer (checked after the head
+    # range), so a range check that let one through returns -5 and still
+    # launches nothing
+    bad = _FAKE + 4
+    for h0, hn in ((0, 0), (-1, 2), (1, 2), (0, 3), (2, 1), (0, -1)):
+        assert _call_summaries(plan, k=bad, h0=h0, hn=hn) == -1, (h0, hn)
+        assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 128, 128, h0, hn,
+                                       bad, None) == -1, (h0, hn)
+        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+                                 h0, hn, bad, _FAKE, _FAKE, _FAKE, None) == -1, (h0, hn)
+    # a valid range reaches the pointer checks
+    assert _call_summaries(plan, k=bad, h0=1, hn=1) == -5
+
+
+def test_head_groups_cover_every_head_once():
+    for H in (1, 3, 4, 7, 32, 33):
+        for groups in (1, 2, 4, 5, 64):
+            runs = kda.head_groups(H, groups)
+            assert len(runs) == min(groups, H)
+            heads = [h for b, n in runs for h in range(b, b + n)]
+            assert heads == list(range(H))
+            assert max(n for _, n in runs) - min(n for _, n in runs) <= 1
 
 
 def test_device_calls_validate_before_launch():
@@ -126,16 +154,18 @@ def test_device_calls_validate_before_launch():
     assert _call_summaries(plan, cache=0) == -1
     assert _call_summaries(plan, cache=_FAKE + 8) == -5
     L = kda.lib()
-    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128, 0, 2,
                                    _FAKE, _FAKE, _FAKE, None) == -1
-    assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, _FAKE, None) == -4
-    assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, _FAKE, None) == -1
+    assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, 0, 2, _FAKE,
+                                   None) == -4
+    assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, 0, 2, _FAKE,
+                                   None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                             _FAKE + 4, _FAKE, _FAKE, _FAKE, None) == -5
+                             0, 2, _FAKE + 4, _FAKE, _FAKE, _FAKE, None) == -5
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                             _FAKE, 0, _FAKE, _FAKE, None) == -1
+                             0, 2, _FAKE, 0, _FAKE, _FAKE, None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
-                             _FAKE, _FAKE, _FAKE, 0, None) == -1
+                             0, 2, _FAKE, _FAKE, _FAKE, 0, None) == -1
     assert L.kda_last_hip_error() == 0
 
 

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_37_amd import synth
+from gated_delta_rule_37_amd import kda, synth
 import parity_utils as pu
 
 pytestmark = pytest.mark.gpu
@@ -98,3 +98,47 @@ def test_determinism_three_launches(gs):
     for o in outs[1:]:
         for key in o:
             assert torch.equal(o[key], outs[0][key]), key
+
+
+@pytest.mark.parametrize("groups", [2, 3, 4])
+def test_head_groups_match_single_launch(groups):
+    """Per-group launches (compose on a second stream) give bitwise the same
+    results as one launch over all heads, and match the oracle."""
+    T, H, cu, S = 400, 4, [0, 150, 400], 4
+    print(f"case head groups={groups}: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=12, cu_seqlens=cu, gate_scale=0.3)
+    plan, ref_out = pu.run_gpu(x, cu, S)
+    d = pu.to_device(x)
+    out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], groups=groups)
+    torch.cuda.synchronize()
+    out.pop("chunk_cache")
+    for key in ref_out:
+        assert torch.equal(out[key], ref_out[key]), key
+    pu.compare(pu.gpu_numpy(out), pu.run_oracle(x, cu, plan), f"groups={groups}")
+
+
+def test_head_range_touches_only_its_heads():
+    """Each device call with a head range writes those heads' rows of its
+    outputs and nothing else (the other heads keep a sentinel)."""
+    T, H, cu, S = 160, 3, [0, 90, 160], 2
+    print(f"case head range: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=13, cu_seqlens=cu)
+    plan = kda.Plan(cu, S)
+    d = pu.to_device(x)
+    out = kda.alloc_outputs(plan, H, 128, 128, "cuda:0")
+    for key in ("o", "final_state", "transitions", "updates", "carry_in"):
+        out[key].fill_(-7.0)
+    pd = plan.device_blob("cuda:0")
+    hr = (1, 1)
+    kda.segment_summaries(plan, pd, d["k"], d["v"], d["g"], d["beta"], out["transitions"],
+                          out["updates"], out["chunk_cache"], heads=hr)
+    kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], heads=hr)
+    kda.apply_carry(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["carry_in"], out["o"],
+                    out["final_state"], out["chunk_cache"], heads=hr)
+    torch.cuda.synchronize()
+    for key in ("o", "final_state", "transitions", "updates", "carry_in"):
+        t = out[key]
+        assert bool((t[:, 0] == -7.0).all()) and bool((t[:, 2] == -7.0).all()), key
+        assert not bool((t[:, 1] == -7.0).any()), key
+    got = pu.gpu_numpy(out, heads=[1])
+    pu.compare(got, pu.run_oracle(x, cu, plan, heads=[1]), "head 1 only")
