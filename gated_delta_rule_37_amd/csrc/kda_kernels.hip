@@ -282,13 +282,15 @@ __device__ __forceinline__ void tile_kslots_split(const f32x16& t, bf16x8 bh[2],
     split8<true>(x, bh[s], bl[s]);
   }
 }
-// A operand in k-slot order from a row-major bf16 matrix: row + c and
-// row + c + 8 (c = 16s + 4(l/32) for k-step s), as two 8-byte reads (the
-// second address goes through opaque() so that the pair is not fused into one
-// ds_read2_b64, which takes four times as long on gfx950).
-__device__ __forceinline__ bf16x8 ld_kslots(const bf16* row, const int c) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(&row[c]);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(&row[opaque(c + 8)]);
+// A operand in k-slot order from a row-major bf16 matrix at p = row + c
+// (c = 16s + 4(l/32) for k-step s): p[0..3] and p[8..11], as two 8-byte reads.
+// They are volatile LDS loads, which keeps the compiler from fusing them into
+// one ds_read2_b64 (four times as slow on gfx950) while a fixed per-lane base
+// with immediate offsets still serves every k-step.
+typedef const volatile __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x8 ld_kslots_at(const bf16* p) {
+  const bf16x4 a = *(lds_bf16x4*)(const_cast<bf16*>(p));
+  const bf16x4 b = *(lds_bf16x4*)(const_cast<bf16*>(p + 8));
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // Matrices whose columns only ever feed k-slot A operands (T diag(beta) and P,
@@ -597,14 +599,17 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
   f32x16 Y = zero16(), O = zero16();
 
   // A operands of k-step kk (channels 16kk .. 16kk+15, k-slot order)
-  auto load_ops = [&](bf16x8 (&o)[4], const int b, const int kk, const int ln, const int lh) {
-    const int row = ln * NS;
-    const int c = 16 * kk + 4 * lh;
-    o[0] = ld_kslots(&sm.kr_h[b][row], c);
-    o[1] = ld_kslots(&sm.kr_l[b][row], c);
+  // per-lane LDS element offsets, fixed for the whole fragment
+  const int prod_off = (lane & 31) * NS + 4 * (lane >> 5);   // A operand rows of Kr, Qr
+  const int tr_off = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * NS + 16 * ((lane >> 4) & 1) +
+                     4 * ((lane & 15) & 3);                     // transposed reads of V, Kc
+  const int tb_off = (lane & 31) * TS + 8 * (lane >> 5);    // rows of T diag(beta), P
+  auto load_ops = [&](bf16x8 (&o)[4], const int b, const int kk) {
+    o[0] = ld_kslots_at(&sm.kr_h[b][prod_off + 16 * kk]);
+    o[1] = ld_kslots_at(&sm.kr_l[b][prod_off + 16 * kk]);
     if (fwd) {
-      o[2] = ld_kslots(&sm.qr_h[b][row], c);
-      o[3] = ld_kslots(&sm.qr_l[b][row], c);
+      o[2] = ld_kslots_at(&sm.qr_h[b][prod_off + 16 * kk]);
+      o[3] = ld_kslots_at(&sm.qr_l[b][prod_off + 16 * kk]);
     }
   };
   auto load_fac = [&](f32x4 (&f)[4], const int b, const int dt, const int lh) {
@@ -622,16 +627,13 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
   // loads one k-step ahead
   auto products = [&](const int n) __attribute__((always_inline)) {
     const int b = n & 1;
-    const int lane2 = opaque(lane);
-    const int ln2 = lane2 & 31;
-    const int lh2 = lane2 >> 5;
     Y = zero16();
     if (fwd) O = zero16();
     bf16x8 opa[2][4];
-    load_ops(opa[0], b, 0, ln2, lh2);
+    load_ops(opa[0], b, 0);
 #pragma unroll
     for (int kk = 0; kk < KD / 16; ++kk) {
-      if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], b, kk + 1, ln2, lh2);
+      if (kk + 1 < KD / 16) load_ops(opa[(kk + 1) & 1], b, kk + 1);
       float x[8];
       tile_kslots(R[kk >> 1], kk & 1, x);
       bf16x8 bh, bl;
@@ -644,12 +646,6 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 
   // step 2n+1: D = V - Y, U = T diag(beta) D, O += P U, store o, R += Kc^T U
   auto finish = [&](const int n) __attribute__((always_inline)) {
-    const int lane_s = opaque(lane);
-    const int ln = lane_s & 31;
-    const int lh = lane_s >> 5;
-    const int col = 32 * ow + ln;
-    const int gq = lane_s >> 4;   // transposed reads: group of 16 lanes
-    const int sq = lane_s & 15;   // and source index inside it
     const int b = n & 1;
     const int c0 = beg + n * CH;
     const int nn = min(CH, end - c0);
@@ -660,8 +656,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
       float vv[4] = {0.f, 0.f, 0.f, 0.f};
       if (use_v) {
         // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
-        const s16x4 v4 = lds_read_tr(
-            &sm.vv[b][(8 * r + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * ow + 16 * (gq & 1) + 4 * (sq & 3)]);
+        const s16x4 v4 = lds_read_tr(&sm.vv[b][tr_off + 8 * r * NS + 32 * ow]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
       }
@@ -675,7 +670,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     f32x16 U = zero16();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int off = ln * TS + 16 * s + 8 * lh;   // columns stored in k-slot order
+      const int off = tb_off + 16 * s;   // columns stored in k-slot order
       U = mfma3(*reinterpret_cast<const bf16x8*>(&sm.tb_h[off]), *reinterpret_cast<const bf16x8*>(&sm.tb_l[off]),
                 dh[s], dl[s], U);
     }
@@ -685,7 +680,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     if (fwd) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int off = ln * TS + 16 * s + 8 * lh;
+        const int off = tb_off + 16 * s;
         O = mfma3(*reinterpret_cast<const bf16x8*>(&sm.p_h[off]), *reinterpret_cast<const bf16x8*>(&sm.p_l[off]),
                   ubh[s], ubl[s], O);
       }
@@ -697,7 +692,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int off = (16 * s + 4 * (gq >> 1) + (sq >> 2)) * NS + 32 * dt + 16 * (gq & 1) + 4 * (sq & 3);
+        const int off = tr_off + 16 * s * NS + 32 * dt;
         const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 8 * NS]));
         const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 8 * NS]));
         R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
