@@ -531,7 +531,10 @@ __device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) *
 //   an, tt, tn (m)         step 2m-1   last reader of chunk m-1:  step 2m-2
 //   T diag(beta), P (m)    step 2m     last reader of chunk m-1:  step 2m-1
 // fac(m) re-anchors the state for chunk m; the owners apply it at the end of
-// finish(m-1) (and fac(0) before the first chunk).
+// finish(m-1) (and fac(0) before the first chunk).  fac spans the decay of
+// up to 32 tokens; where one FP32 factor would underflow it is split into a
+// normal factor and a power of two (fexp, flagged per operand helper in
+// fsplit), which the owners apply with ldexp on those rows only.
 // ===========================================================================
 struct alignas(16) PipeSmem {
   bf16 kr_h[2][CH * NS], kr_l[2][CH * NS];    // Kr = k e^{G-a}, token-major
@@ -546,6 +549,8 @@ struct alignas(16) PipeSmem {
   float xt[16 * XS];                          // X = A10 T00, stored xt[c][i]
   float fac[2][KD];                           // state rescale before chunk m
   float beta[2][CH];
+  alignas(16) int16_t fexp[2][KD];            // power-of-two part of fac (0: none)
+  int32_t fsplit[2][NOWN];                    // per operand helper: some fac split
 };
 
 // Owner wave ow: the state columns [32ow, 32ow + 32) as four 32 x 32 FP32
@@ -621,6 +626,22 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) R[dt][4 * r + e] *= f[r][e];
+  };
+  // the power-of-two part of fac, on the rare chunks where some channel has it
+  // (rows 32dt .. 32dt+31 are operand helper dt's channels, so its flag
+  // covers tile dt)
+  auto rescale_exp = [&](const int b, const int lh) {
+    const u32x4 fl = *reinterpret_cast<const u32x4*>(&sm.fsplit[b][0]);
+    if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      if (__builtin_amdgcn_readfirstlane(fl[dt]) == 0) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          R[dt][4 * r + e] = __builtin_ldexpf(R[dt][4 * r + e], sm.fexp[b][32 * dt + 8 * r + 4 * lh + e]);
+    }
   };
 
   // step 2n: Y = Kr R and O = Qr R (R already anchored for chunk n), operand
@@ -722,6 +743,8 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
         }
       }
     }
+    // last, so that the rare branch does not cut the step's code in two
+    rescale_exp((n + 1) & 1, lh);
   };
 
   block_sync();   // steps -3 .. -1: the helpers fill the pipeline
@@ -736,6 +759,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
       load_fac(f, 0, dt, lh2);
       rescale(dt, f);
     }
+    rescale_exp(0, lh2);
   }
   for (int n = 0; n < nc; ++n) {
     products(n);
@@ -805,6 +829,38 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
   };
   fetch(beg);
 
+  // fac = 2^t for this lane's eight channels (t in log2 units), written by
+  // the lanes with tk = 0.  Where 2^t would leave the FP32 normal range (the
+  // decay of the 32 tokens between two anchors beyond ~83 nats), it is
+  // stored as 2^(t - e) with an integer e < 0 in fexp, applied by ldexp; the
+  // wave's flag tells the owners whether any channel needs it.
+  auto store_fac = [&](const int b, const float (&t)[8]) {
+    float tmin = t[0];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) tmin = fminf(tmin, t[c]);
+    const bool split = __builtin_amdgcn_ballot_w64(tk == 0 && tmin < -120.f) != 0;
+    float fv[8];
+    if (split) {
+      uint32_t ev[4] = {0u, 0u, 0u, 0u};   // eight int16 exponents, two per word
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int e = t[c] < -120.f ? static_cast<int>(floorf(t[c])) + 60 : 0;
+        ev[c >> 1] |= (static_cast<uint32_t>(e) & 0xffffu) << (16 * (c & 1));
+        fv[c] = __builtin_amdgcn_exp2f(t[c] - static_cast<float>(e));
+      }
+      // the owners read these only for the rows of a helper that set its flag
+      if (tk == 0) *reinterpret_cast<u32x4*>(&sm.fexp[b][c8]) = u32x4{ev[0], ev[1], ev[2], ev[3]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(t[c]);
+    }
+    if (tk == 0) {
+      st4(&sm.fac[b][c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
+      st4(&sm.fac[b][c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+    }
+    if (lane == 0) sm.fsplit[b][oh] = split ? 1 : 0;
+  };
+
   float dprev[8];   // (G_C - a) of the previous chunk, log2 units
 #pragma unroll
   for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
@@ -852,12 +908,11 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
         G[1][c] += a[c];
         gc[c] += a[c];
       }
-      if (tk == 0) {
-        float fv[8];
+      {
+        float t[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(a[c] + dprev[c]);
-        st4(&sm.fac[b][c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
-        st4(&sm.fac[b][c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
+        for (int c = 0; c < 8; ++c) t[c] = a[c] + dprev[c];
+        store_fac(b, t);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) dprev[c] = gc[c] - a[c];
@@ -903,13 +958,7 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
     block_sync();
   }
   // step 2nc-3: R *= e^{G_C - a} after the last chunk turns R back into S
-  if (tk == 0) {
-    float fv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) fv[c] = __builtin_amdgcn_exp2f(dprev[c]);
-    st4(&sm.fac[nc & 1][c8], f32x4{fv[0], fv[1], fv[2], fv[3]});
-    st4(&sm.fac[nc & 1][c8 + 4], f32x4{fv[4], fv[5], fv[6], fv[7]});
-  }
+  store_fac(nc & 1, dprev);
   block_sync();
   block_sync();   // steps 2nc-2, 2nc-1
   block_sync();

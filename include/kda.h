@@ -59,8 +59,11 @@
  *   - Device calls are asynchronous on `stream`; launch failures are reported
  *     as KDA_ERR_HIP (kda_last_hip_error() gives the hipError_t).
  *   - Supported gate domain: g <= 0 and finite, with the decay mass of any 16
- *     consecutive tokens of one chunk below about 85 nats per channel (so that
- *     the in-chunk exponential factors stay inside the FP32 range).
+ *     consecutive tokens of one 32-token chunk below about 60 nats per
+ *     channel.  The in-chunk exponential factors and the chunk-anchored copy
+ *     of the state then stay inside the FP32 normal range; the re-anchoring
+ *     between two chunks, which spans up to 32 tokens, is applied in two
+ *     factors where one would underflow.
  */
 #ifndef KDA_H_
 #define KDA_H_

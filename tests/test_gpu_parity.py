@@ -25,9 +25,10 @@ SMALL = [
     ("one_token_segments", 6, 1, [0, 6], 6, None, 0.05),
     ("many_segments_slow", 512, 2, [0, 512], 8, None, 0.01),
     ("near_identity_transitions", 256, 2, [0, 256], 8, None, 0.001),
-    # about 3 nats of decay per token and channel: 16 tokens hold ~50 nats,
-    # inside the supported gate domain, and every transition underflows
-    ("fast_decay", 200, 2, [0, 200], 3, None, 4.0),
+    # about 2 nats of decay per token and channel: 16 tokens hold at most
+    # ~55 nats (inside the supported gate domain), while the 32 tokens between
+    # two chunk anchors reach ~95 in places, beyond a single FP32 factor
+    ("fast_decay", 200, 2, [0, 200], 3, None, 2.5),
     # sequences of 1 to 33 tokens, several inside one chunk and one segment
     ("short_sequences", 100, 2, [0, 3, 10, 11, 40, 64, 65, 98, 100], 5, None, 1.0),
 ]
