@@ -971,8 +971,9 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
 // chunk cache during the next chunk's part 1, while it is still in LDS.  The
 // carry launch instead loads it from the cache in part 1 and stores it to LDS
 // in part 2 for every fragment that the summaries launch ran (those that end
-// their segment), and th 3 computes the three blocks of P in part 1 and
-// stores them in part 2.
+// their segment).  It also computes the three blocks of P in part 1 and
+// stores them in part 2: one block on each of th 0-2 where T diag(beta) comes
+// from the cache, all three on th 3 where th 0-2 build it.
 template <bool FILL>
 __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int th, const int32_t flags,
                                              const int32_t seg, const int32_t beg, const int32_t end) {
@@ -1004,12 +1005,17 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       } else if (th == 2) {
         a_offdiag(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
       }
-      if (!FILL && th == 3) {
+      if (!FILL) {
         const int lm = lane_s & 15;
         const int lg = lane_s >> 4;
-        pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
-        pacc[1] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
-        pacc[2] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 1, lm, lg);
+        if (cached) {
+          // T helpers 0-2 are free here: one P block each
+          if (th < 3) pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], th > 0, th > 1, lm, lg);
+        } else if (th == 3) {
+          pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
+          pacc[1] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
+          pacc[2] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 1, lm, lg);
+        }
       }
     }
     block_sync();
@@ -1018,10 +1024,14 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       const int lane_s = opaque(lane);
       if (cached) st4(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)], tbv);
       else t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
-      if (!FILL && th == 3) {
-        p_store(pacc[0], 0, 0, sm.p_h, sm.p_l, lane_s);
-        p_store(pacc[1], 1, 0, sm.p_h, sm.p_l, lane_s);
-        p_store(pacc[2], 1, 1, sm.p_h, sm.p_l, lane_s);
+      if (!FILL) {
+        if (cached) {
+          if (th < 3) p_store(pacc[0], th > 0, th > 1, sm.p_h, sm.p_l, lane_s);
+        } else if (th == 3) {
+          p_store(pacc[0], 0, 0, sm.p_h, sm.p_l, lane_s);
+          p_store(pacc[1], 1, 0, sm.p_h, sm.p_l, lane_s);
+          p_store(pacc[2], 1, 1, sm.p_h, sm.p_l, lane_s);
+        }
       }
     }
     block_sync();
