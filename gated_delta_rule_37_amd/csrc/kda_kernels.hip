@@ -293,11 +293,26 @@ __device__ __forceinline__ bf16x8 ld_kslots_at(const bf16* p) {
   const bf16x4 b = *(lds_bf16x4*)(const_cast<bf16*>(p + 8));
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// The same 16 bytes with the two 8-byte halves exchanged (two 8-byte reads,
+// high half first), for rows stored with their halves exchanged.
+__device__ __forceinline__ bf16x8 ld_halves_swapped(const bf16* p) {
+  const bf16x4 a = *(lds_bf16x4*)(const_cast<bf16*>(p + 4));
+  const bf16x4 b = *(lds_bf16x4*)(const_cast<bf16*>(p));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 // Matrices whose columns only ever feed k-slot A operands (T diag(beta) and P,
 // columns = tokens) are stored with the columns in k-slot order, so that
 // the operand is one contiguous 16-byte read at 16s + 8(l/32): column t of
 // each 16-column group sits at position t with bits 2 and 3 swapped.
 __device__ __forceinline__ int kslot_col(const int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+// 16 bytes of a token-major tile row for st4, halves exchanged when the row
+// is stored that way (hi_rows)
+__device__ __forceinline__ u32x4 sw_rows(const int hi_rows, const uint32_t (&w)[4]) {
+  return hi_rows ? u32x4{w[2], w[3], w[0], w[1]} : u32x4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ u32x4 sw_rows(const int hi_rows, const u32x4& w) {
+  return hi_rows ? u32x4{w[2], w[3], w[0], w[1]} : w;
+}
 
 }  // namespace
 
@@ -331,7 +346,11 @@ __device__ __forceinline__ void scan_stage(float (&G)[TPL][8]) {
 
 // 16 x 16 tile of X Kc^T over the 128 channels: rows 16rb .. 16rb+15 of X
 // (Kr or Qr) against rows 16ct .. 16ct+15 of Kc, split operands.  Lane l
-// receives rows 16rb + 4(l/16) + e, e = 0..3, of column 16ct + l%16.
+// receives rows 16rb + 4(l/16) + e, e = 0..3, of column 16ct + l%16.  Where
+// both row blocks are stored alike the order of the eight channels inside a
+// lane's 16 bytes cancels out of the dot product; SWAP serves rb = 1, ct = 0
+// in the exchanged-half layout.
+template <bool SWAP = false>
 __device__ __forceinline__ f32x4 tile16(const bf16* xh, const bf16* xl, const bf16* ch, const bf16* cl,
                                         const int rb, const int ct, const int lm, const int lg) {
   f32x4 acc = zero4();
@@ -339,8 +358,17 @@ __device__ __forceinline__ f32x4 tile16(const bf16* xh, const bf16* xl, const bf
   for (int kk = 0; kk < KD / 32; ++kk) {
     const int aoff = (16 * rb + lm) * NS + 32 * kk + 8 * lg;
     const int boff = (16 * ct + lm) * NS + 32 * kk + 8 * lg;
-    acc = mfma16x3(*reinterpret_cast<const bf16x8*>(&xh[aoff]), *reinterpret_cast<const bf16x8*>(&xl[aoff]),
-                   *reinterpret_cast<const bf16x8*>(&ch[boff]), *reinterpret_cast<const bf16x8*>(&cl[boff]), acc);
+    bf16x8 ah, al;
+    if (SWAP) {
+      // the A rows are stored with exchanged halves and the Kc rows are not:
+      // read A back in channel order
+      ah = ld_halves_swapped(&xh[aoff]);
+      al = ld_halves_swapped(&xl[aoff]);
+    } else {
+      ah = *reinterpret_cast<const bf16x8*>(&xh[aoff]);
+      al = *reinterpret_cast<const bf16x8*>(&xl[aoff]);
+    }
+    acc = mfma16x3(ah, al, *reinterpret_cast<const bf16x8*>(&ch[boff]), *reinterpret_cast<const bf16x8*>(&cl[boff]), acc);
   }
   mfma_result_fence(acc);
   return acc;
@@ -418,11 +446,12 @@ __device__ __forceinline__ void a_diag_solve(const bf16* krh, const bf16* krl, c
 }
 
 // A10 = beta o (Kr Kc^T), rows 16..31 and columns 0..15, into an.
+template <bool SWZ>
 __device__ __forceinline__ void a_offdiag(const bf16* krh, const bf16* krl, const bf16* kch, const bf16* kcl,
                                           const float* beta, float* an, const int lane_s) {
   const int lm = lane_s & 15;
   const int lg = lane_s >> 4;
-  const f32x4 acc = tile16(krh, krl, kch, kcl, 1, 0, lm, lg);
+  const f32x4 acc = tile16<SWZ>(krh, krl, kch, kcl, 1, 0, lm, lg);
   const f32x4 brow = ld4(&beta[16 + 4 * lg]);
 #pragma unroll
   for (int e = 0; e < 4; ++e) an[(16 + 4 * lg + e) * FS + lm] = brow[e] * acc[e];
@@ -536,6 +565,13 @@ __device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) *
 // normal factor and a power of two (fexp, flagged per operand helper in
 // fsplit), which the owners apply with ldexp on those rows only.
 // ===========================================================================
+// Token-major tiles in the carry launch hold rows 16 .. 31 with the two 8-byte
+// halves of every 16-byte group exchanged (element c at c ^ 4).  At this row
+// stride rows r and r + 16 fall on the same banks, so the owners' 8-byte reads
+// of 32 rows met two to a bank; exchanged, they cover all 64 banks once.  The
+// summaries launch keeps the plain layout: there the T helpers' off-diagonal
+// block of A, which pays for the exchange with twice the reads, is on the
+// longest chain of its step.
 struct alignas(16) PipeSmem {
   bf16 kr_h[2][CH * NS], kr_l[2][CH * NS];    // Kr = k e^{G-a}, token-major
   bf16 qr_h[2][CH * NS], qr_l[2][CH * NS];    // Qr = q e^{G-a}, token-major
@@ -605,9 +641,11 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 
   // A operands of k-step kk (channels 16kk .. 16kk+15, k-slot order)
   // per-lane LDS element offsets, fixed for the whole fragment
-  const int prod_off = (lane & 31) * NS + 4 * (lane >> 5);   // A operand rows of Kr, Qr
+  constexpr bool xrows = fwd;   // rows 16 .. 31 stored with exchanged halves
+  const int prod_off = (lane & 31) * NS + 4 * ((lane >> 5) ^ (xrows ? (lane >> 4) & 1 : 0));   // A operand rows of Kr, Qr
   const int tr_off = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * NS + 16 * ((lane >> 4) & 1) +
                      4 * ((lane & 15) & 3);                     // transposed reads of V, Kc
+  const int tr_sw = xrows ? tr_off ^ 4 : tr_off;              // the same in rows 16 .. 31
   const int tb_off = (lane & 31) * TS + 8 * (lane >> 5);    // rows of T diag(beta), P
   auto load_ops = [&](bf16x8 (&o)[4], const int b, const int kk) {
     o[0] = ld_kslots_at(&sm.kr_h[b][prod_off + 16 * kk]);
@@ -677,7 +715,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
       float vv[4] = {0.f, 0.f, 0.f, 0.f};
       if (use_v) {
         // V[8r + 4lh + e][col], e = 0..3, from the token-major copy
-        const s16x4 v4 = lds_read_tr(&sm.vv[b][tr_off + 8 * r * NS + 32 * ow]);
+        const s16x4 v4 = lds_read_tr(&sm.vv[b][(r >= 2 ? tr_sw : tr_off) + 8 * r * NS + 32 * ow]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vv[e] = bf2f(static_cast<uint16_t>(v4[e]));
       }
@@ -713,7 +751,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int off = tr_off + 16 * s * NS + 32 * dt;
+        const int off = (s ? tr_sw : tr_off) + 16 * s * NS + 32 * dt;
         const bf16x8 ah = join8(lds_read_tr(&sm.kc_h[b][off]), lds_read_tr(&sm.kc_h[b][off + 8 * NS]));
         const bf16x8 al = join8(lds_read_tr(&sm.kc_l[b][off]), lds_read_tr(&sm.kc_l[b][off + 8 * NS]));
         R[dt] = mfma3(ah, al, ubh[s], ubl[s], R[dt]);
@@ -937,11 +975,12 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
           if (fwd) split_pair_dead(qr[0], qr[1], qrh[w], qrl[w]);
         }
         const int off = (tk + 16 * j) * NS + c8;
-        st4(&sm.kr_h[b][off], u32x4{krh[0], krh[1], krh[2], krh[3]});
-        st4(&sm.kr_l[b][off], u32x4{krl[0], krl[1], krl[2], krl[3]});
+        // rows 16 .. 31 with exchanged halves in the carry launch
+        st4(&sm.kr_h[b][off], sw_rows(fwd && j, krh));
+        st4(&sm.kr_l[b][off], sw_rows(fwd && j, krl));
         if (fwd) {
-          st4(&sm.qr_h[b][off], u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
-          st4(&sm.qr_l[b][off], u32x4{qrl[0], qrl[1], qrl[2], qrl[3]});
+          st4(&sm.qr_h[b][off], sw_rows(j, qrh));
+          st4(&sm.qr_l[b][off], sw_rows(j, qrl));
         }
       }
     }
@@ -951,9 +990,9 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int off = (tk + 16 * j) * NS + c8;
-      st4(&sm.kc_h[b][off], u32x4{kch[j][0], kch[j][1], kch[j][2], kch[j][3]});
-      st4(&sm.kc_l[b][off], u32x4{kcl[j][0], kcl[j][1], kcl[j][2], kcl[j][3]});
-      st4(&sm.vv[b][off], vkeep[j]);
+      st4(&sm.kc_h[b][off], sw_rows(fwd && j, kch[j]));
+      st4(&sm.kc_l[b][off], sw_rows(fwd && j, kcl[j]));
+      st4(&sm.vv[b][off], sw_rows(fwd && j, vkeep[j]));
     }
     block_sync();
   }
@@ -1003,17 +1042,18 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       } else if (th < 2) {
         a_diag_solve(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, sm.tt, sm.tn, th, lane_s);
       } else if (th == 2) {
-        a_offdiag(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
+        a_offdiag<!FILL>(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, lane_s);
       }
       if (!FILL) {
         const int lm = lane_s & 15;
         const int lg = lane_s >> 4;
         if (cached) {
           // T helpers 0-2 are free here: one P block each
-          if (th < 3) pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], th > 0, th > 1, lm, lg);
+          if (th == 1) pacc[0] = tile16<true>(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
+          else if (th < 3) pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], th > 0, th > 1, lm, lg);
         } else if (th == 3) {
           pacc[0] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 0, 0, lm, lg);
-          pacc[1] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
+          pacc[1] = tile16<true>(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 0, lm, lg);
           pacc[2] = tile16(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], 1, 1, lm, lg);
         }
       }
