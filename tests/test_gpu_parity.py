@@ -31,6 +31,11 @@ SMALL = [
     ("fast_decay", 200, 2, [0, 200], 3, None, 2.5),
     # sequences of 1 to 33 tokens, several inside one chunk and one segment
     ("short_sequences", 100, 2, [0, 3, 10, 11, 40, 64, 65, 98, 100], 5, None, 1.0),
+    # long compose scans (39 and 24 maps) with slow gates, so that products of
+    # many transitions stay significant; the varlen case has structurally zero
+    # transitions in the middle of the scan
+    ("forty_segments_slow", 1280, 2, [0, 1280], 40, None, 0.01),
+    ("varlen_25_segments_slow", 1000, 2, [0, 333, 334, 700, 1000], 25, None, 0.01),
 ]
 
 
@@ -104,6 +109,33 @@ def test_determinism_three_launches(gs):
     for o in outs[1:]:
         for key in o:
             assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_determinism_long_compose():
+    """A 39-map compose scan over slow gates: repeated launches agree bit for
+    bit."""
+    T, H, cu, S = 1280, 2, [0, 500, 1280], 40
+    print(f"case long compose determinism: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=14, cu_seqlens=cu, gate_scale=0.01)
+    outs = [pu.run_gpu(x, cu, S)[1] for _ in range(3)]
+    for o in outs[1:]:
+        for key in o:
+            assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_compose_head_range():
+    """A compose launch over one head leaves the other heads' carry-ins
+    untouched and gives that head the all-heads result."""
+    T, H, cu, S = 640, 3, [0, 640], 30
+    print(f"case compose head range: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=15, cu_seqlens=cu, gate_scale=0.01)
+    plan, ref_out = pu.run_gpu(x, cu, S)
+    pd = plan.device_blob("cuda:0")
+    carry = torch.full_like(ref_out["carry_in"], -7.0)
+    kda.compose_summaries(plan, pd, ref_out["transitions"], ref_out["updates"], carry, heads=(1, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(carry[:, 1], ref_out["carry_in"][:, 1])
+    assert bool((carry[:, 0] == -7.0).all()) and bool((carry[:, 2] == -7.0).all())
 
 
 @pytest.mark.parametrize("groups", [2, 3, 4])
