@@ -66,6 +66,14 @@ def _seq_starts(cu_seqlens, T):
     return starts
 
 
+def _start_state(cu_seqlens, t, h0, shape):
+    """The state a sequence starting at token t begins from: zero, or h0[n]."""
+    if h0 is None:
+        return np.zeros(shape)
+    n = [int(c) for c in cu_seqlens].index(t)
+    return np.array(h0[n], dtype=np.float64)
+
+
 def recurrence(q, k, v, g, beta, cu_seqlens, h0=None):
     """Monolithic recurrence over every packed sequence.
 
@@ -88,13 +96,15 @@ def recurrence(q, k, v, g, beta, cu_seqlens, h0=None):
     return o, final
 
 
-def segment_updates(k, v, g, beta, cu_seqlens, bounds):
+def segment_updates(k, v, g, beta, cu_seqlens, bounds, h0=None):
     """B_r: the state at the end of segment r when the segment starts from zero.
 
     [cuLA#136] Summary names the pair preceding_state_update /
     preceding_transition; the update is the affine map's constant term, i.e.
-    the segment run from a zero state, with the state reset to zero at every
-    sequence start inside the segment.  Returns [R, H, K, V].
+    the segment run from a zero state, with the state reset at every sequence
+    start inside the segment to that sequence's initial state (zero, or
+    ``h0[n]`` when given: the reset is an affine map whose constant term is the
+    initial state).  Returns [R, H, K, V].
     """
     T, H, K = k.shape
     V = v.shape[2]
@@ -106,7 +116,7 @@ def segment_updates(k, v, g, beta, cu_seqlens, bounds):
         S = np.zeros((H, K, V))
         for t in range(int(bounds[r]), int(bounds[r + 1])):
             if starts[t]:
-                S = np.zeros((H, K, V))
+                S = _start_state(cu_seqlens, t, h0, (H, K, V))
             S, _ = kda_step(S, zeros_q, k[t], v[t], g[t], beta[t])
         B[r] = S
     return B
@@ -166,8 +176,9 @@ def compose(A, B):
     return C, cur
 
 
-def segmented_forward(q, k, v, g, beta, cu_seqlens, bounds, C):
-    """Re-run each segment from its carry-in C_r (reset at sequence starts).
+def segmented_forward(q, k, v, g, beta, cu_seqlens, bounds, C, h0=None):
+    """Re-run each segment from its carry-in C_r (reset at sequence starts to
+    zero, or to ``h0[n]`` when given).
 
     This is the segmented execution the pages' context-parallel forward
     performs once every rank has its predecessors' summaries ([cuLA#136]
@@ -184,7 +195,7 @@ def segmented_forward(q, k, v, g, beta, cu_seqlens, bounds, C):
         S = np.array(C[r], dtype=np.float64)
         for t in range(int(bounds[r]), int(bounds[r + 1])):
             if starts[t]:
-                S = np.zeros((H, K, V))
+                S = _start_state(cu_seqlens, t, h0, (H, K, V))
             S, o[t] = kda_step(S, q[t], k[t], v[t], g[t], beta[t])
             if t in ends:
                 final[ends[t]] = S

@@ -230,3 +230,77 @@ def test_transition_contracts():
     A = ko.segment_transitions(k, g, beta, [0, T], [0, 1, T])
     for h in range(H):
         assert np.linalg.norm(A[1, h], 2) <= 1.0 + 1e-12
+
+
+# ------------------------------------------------------ initial states h0
+
+def test_h0_enters_through_the_dense_maps():
+    """With h0, each sequence's o_t and final state gain exactly the image of
+    h0[n] under the product of the dense per-token maps since the sequence
+    start (the recurrence is affine in the state)."""
+    rng = np.random.default_rng(21)
+    T, H, K, V = 14, 2, 5, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, K, V, g_scale=0.3)
+    cu = [0, 6, T]
+    h0 = rng.standard_normal((2, H, K, V))
+    o1, f1 = ko.recurrence(q, k, v, g, beta, cu, h0=h0)
+    o0, f0 = ko.recurrence(q, k, v, g, beta, cu)
+    for n in range(2):
+        for h in range(H):
+            M = np.eye(K)
+            for t in range(cu[n], cu[n + 1]):
+                M = _dense_map(k[t, h], g[t, h], beta[t, h]) @ M
+                np.testing.assert_allclose(o1[t, h] - o0[t, h], (M @ h0[n, h]).T @ q[t, h],
+                                           rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(f1[n, h] - f0[n, h], M @ h0[n, h], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_segmented_plus_composed_equals_monolithic_with_h0(seed):
+    q, k, v, g, beta, cu, bounds = _random_case(seed)
+    N, H, K, V = len(cu) - 1, k.shape[1], k.shape[2], v.shape[2]
+    h0 = np.random.default_rng(100 + seed).standard_normal((N, H, K, V))
+    o, final = ko.recurrence(q, k, v, g, beta, cu, h0=h0)
+    A = ko.segment_transitions(k, g, beta, cu, bounds)
+    B = ko.segment_updates(k, v, g, beta, cu, bounds, h0=h0)
+    C, last = ko.compose(A, B)
+    o2, final2 = ko.segmented_forward(q, k, v, g, beta, cu, bounds, C, h0=h0)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(final2, final, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(last, final[-1], rtol=1e-12, atol=1e-12)
+    starts = set(int(x) for x in cu[:-1])
+    for r in range(1, len(bounds) - 1):
+        b = int(bounds[r])
+        if b in starts:
+            continue
+        cu_prefix = np.array([int(x) for x in cu if x < b] + [b])
+        _, state = ko.recurrence(q[:b], k[:b], v[:b], g[:b], beta[:b], cu_prefix, h0=h0)
+        np.testing.assert_allclose(C[r], state[-1], rtol=1e-12, atol=1e-12)
+
+
+def test_h0_pure_decay_update_closed_form():
+    """beta = 0: a segment that holds a sequence start ends at that sequence's
+    h0 decayed by the gates since the start; one without is zero."""
+    rng = np.random.default_rng(22)
+    T, H, K, V = 16, 2, 4, 3
+    _, k, v, g, _ = _rand_inputs(rng, T, H, K, V, g_scale=0.2)
+    beta = np.zeros((T, H))
+    cu = [0, 7, T]
+    h0 = rng.standard_normal((2, H, K, V))
+    B = ko.segment_updates(k, v, g, beta, cu, [0, 5, 10, T], h0=h0)
+    np.testing.assert_allclose(B[0], np.exp(g[0:5].sum(0))[:, :, None] * h0[0], rtol=1e-13)
+    np.testing.assert_allclose(B[1], np.exp(g[7:10].sum(0))[:, :, None] * h0[1], rtol=1e-13)
+    assert not B[2].any()
+
+
+def test_linearity_in_v_and_h0():
+    q, k, v, g, beta, cu, bounds = _random_case(6)
+    N, H, K, V = len(cu) - 1, k.shape[1], k.shape[2], v.shape[2]
+    h0 = np.random.default_rng(23).standard_normal((N, H, K, V))
+    o, f = ko.recurrence(q, k, v, g, beta, cu, h0=h0)
+    o2, f2 = ko.recurrence(q, k, 2 * v, g, beta, cu, h0=2 * h0)
+    np.testing.assert_array_equal(o2, 2 * o)
+    np.testing.assert_array_equal(f2, 2 * f)
+    B = ko.segment_updates(k, v, g, beta, cu, bounds, h0=h0)
+    B2 = ko.segment_updates(k, 2 * v, g, beta, cu, bounds, h0=2 * h0)
+    np.testing.assert_array_equal(B2, 2 * B)
