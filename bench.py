@@ -224,6 +224,8 @@ def main():
     ap.add_argument("--groups", type=int, default=1,
                     help="head groups per step; each group's compose overlaps other groups' work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--initial-state", action="store_true",
+                    help="give every sequence a (seeded, random) initial state")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -258,10 +260,13 @@ def main():
     plan = kda.Plan(cu, w.segments)
     pd = plan.device_blob(dev)
     out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev)
+    h0 = None
+    if args.initial_state:
+        h0 = synth.initial_states(plan.N, w.H, w.K, w.V, seed=w.seed + 1000).to(dev)
 
     def step(ev=None):
         kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], out=out, groups=args.groups,
-                    events=ev)
+                    events=ev, initial_state=h0)
 
     for _ in range(args.warmup):
         step()
@@ -335,7 +340,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "segments": w.segments, "sequences": plan.N, "seed": w.seed,
-                   "head_groups": groups},
+                   "head_groups": groups, "initial_state": bool(args.initial_state)},
         "roofline": roof,
         # summed launch durations per step; with head groups the compose
         # launches overlap the other two on a second stream

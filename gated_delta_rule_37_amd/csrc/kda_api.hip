@@ -29,6 +29,9 @@ int check_heads(int32_t H, int32_t head_begin, int32_t head_count) {
   return KDA_OK;
 }
 
+// An optional tensor: null, or 16-byte aligned.
+int check_optional(const void* p) { return p == nullptr || aligned16(p) ? KDA_OK : KDA_ERR_MISALIGNED; }
+
 int check_tensors(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs) {
     if (p == nullptr) return KDA_ERR_INVALID_ARG;
@@ -60,7 +63,8 @@ extern "C" size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H) {
 
 extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                                      const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                                     const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                                     const uint16_t* beta, const float* initial_state,
+                                     int32_t H, int32_t K, int32_t V,
                                      int32_t head_begin, int32_t head_count,
                                      float* transitions, float* updates, void* chunk_cache,
                                      hipStream_t stream) {
@@ -69,6 +73,8 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   st = check_tensors({k, v, g, beta, transitions, updates, chunk_cache});
+  if (st != KDA_OK) return st;
+  st = check_optional(initial_state);
   if (st != KDA_OK) return st;
   kda::ChunkParams p{};
   p.plan = plan_dev;
@@ -85,6 +91,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.transitions = transitions;
   p.updates = updates;
   p.carry = nullptr;
+  p.init_state = initial_state;
   p.chunk_cache = static_cast<uint16_t*>(chunk_cache);
   (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, head_count, 1), dim3(kda::kSummaryThreads), 0, stream, p);
@@ -120,7 +127,8 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
 
 extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q,
                                const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                               const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                               const uint16_t* beta, const float* initial_state,
+                               int32_t H, int32_t K, int32_t V,
                                int32_t head_begin, int32_t head_count,
                                const float* carry_in, float* o, float* final_state,
                                const void* chunk_cache, hipStream_t stream) {
@@ -129,6 +137,8 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   st = check_tensors({q, k, v, g, beta, carry_in, o, final_state, chunk_cache});
+  if (st != KDA_OK) return st;
+  st = check_optional(initial_state);
   if (st != KDA_OK) return st;
   kda::ChunkParams p{};
   p.plan = plan_dev;
@@ -145,6 +155,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.transitions = nullptr;
   p.updates = nullptr;
   p.carry = carry_in;
+  p.init_state = initial_state;
   p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(chunk_cache));
   (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, head_count, 1), dim3(kda::kCarryThreads), 0, stream, p);

@@ -31,6 +31,7 @@ struct ChunkParams {
   float* transitions;
   float* updates;
   const float* carry;
+  const float* init_state;  // per-sequence initial states [N, H, K, V], or null (zero)
   uint16_t* chunk_cache;  // T diag(beta) per chunk of the fragments that end a segment
 };
 

@@ -597,14 +597,15 @@ struct alignas(16) PipeSmem {
 //     S_new = Diag(e^{G_C}) S + K^^T U = Diag(e^{G_C - a}) (R + Kc^T U)
 // and fac = e^{a_next + G_C - a} re-anchors it for the next chunk
 // (e^{G_C - a} after the last one, which leaves S itself).  Modes:
-//   kModeFwd    from zero or from the carry-in: o and, at a sequence end,
-//               the final state
-//   kModeSumS   from zero, no o: B_r
+//   kModeFwd    from the carry-in, the sequence's initial state or zero (init):
+//               o and, at a sequence end, the final state
+//   kModeSumS   from the sequence's initial state or zero (init), no o: B_r
 //   kModeSumPhi from the identity with V = 0, no o: A_r
+// init points at the starting state's [K, V] matrix for this head, or is null.
 template <int MODE>
 __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, const int ow, const int32_t flags,
                                            const int32_t seg, const int32_t seq, const int32_t beg,
-                                           const int32_t end, const bool from_carry) {
+                                           const int32_t end, const float* init) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
   const int h = p.h0 + blockIdx.y;
@@ -628,8 +629,8 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         R[dt][i] = (own && dt == ow && i == 4 * (ln_s >> 3) + (ln_s & 3)) ? 1.f : 0.f;
-  } else if (from_carry) {
-    const float* src = p.carry + (static_cast<size_t>(seg) * H + h) * KD * VD + col;
+  } else if (init != nullptr) {
+    const float* src = init + col;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -1086,6 +1087,18 @@ __device__ __forceinline__ void pipe_idle(const int32_t beg, const int32_t end) 
   for (int i = 0; i < 2 * nc + 3; ++i) block_sync();
 }
 
+// The state a fragment starts from, for this head: the carry-in C_r where it
+// continues a sequence across its segment's start (carry launch; the
+// summaries launch runs B_r from zero there), else it starts a sequence and
+// begins at that sequence's initial state, if any.
+__device__ __forceinline__ const float* start_state(const ChunkParams& p, const int32_t flags, const int32_t seg,
+                                                    const int32_t seq, const bool carry_launch) {
+  const size_t h = static_cast<size_t>(p.h0) + blockIdx.y;
+  if ((flags & kFragCarried) != 0)
+    return carry_launch ? p.carry + (static_cast<size_t>(seg) * p.H + h) * KD * VD : nullptr;
+  return p.init_state != nullptr ? p.init_state + (static_cast<size_t>(seq) * p.H + h) * KD * VD : nullptr;
+}
+
 // Summaries launch: one workgroup per fragment that ends its segment and
 // head.  Waves 0-3 own the update B_r (the fragment from a zero state),
 // waves 4-7 the transition A_r (from the identity with V = 0) when the
@@ -1105,10 +1118,10 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < NOWN) {
-    pipe_owner<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, false);
+    pipe_owner<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, start_state(p, flags, seg, seq, false));
   } else if (wave < 2 * NOWN) {
     if (work.phi) {
-      pipe_owner<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, false);
+      pipe_owner<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, nullptr);
     } else {
       f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * p.H + h) * KD * KD);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -1135,7 +1148,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave < NOWN) pipe_owner<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, (flags & kFragCarried) != 0);
+  if (wave < NOWN) pipe_owner<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, start_state(p, flags, seg, seq, true));
   else if (wave < 2 * NOWN) pipe_ophelper<kModeFwd>(p, sm, wave - NOWN, beg, end);
   else pipe_thelper<false>(p, sm, wave - 2 * NOWN, flags, seg, beg, end);
 }

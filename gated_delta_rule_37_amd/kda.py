@@ -83,11 +83,11 @@ def lib() -> ctypes.CDLL:
     L.kda_summary_bytes.restype = sz
     L.kda_chunk_cache_bytes.argtypes = [p, i32]
     L.kda_chunk_cache_bytes.restype = sz
-    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p]
+    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p]
     L.kda_segment_summaries.restype = ctypes.c_int
     L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p]
+    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p]
     L.kda_apply_carry.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -199,11 +199,20 @@ def _cache_ptr(plan: Plan, H: int, chunk_cache) -> int:
     return _ptr(chunk_cache, torch.uint8, (n,), "chunk_cache")
 
 
+def _init_ptr(plan: Plan, H: int, K: int, V: int, initial_state):
+    """Address of the per-sequence initial states [N, H, K, V], or None (zero)."""
+    if initial_state is None:
+        return None
+    return _ptr(initial_state, torch.float32, (plan.N, H, K, V), "initial_state")
+
+
 def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transitions, updates,
-                      chunk_cache, stream=None, heads=None):
+                      chunk_cache, stream=None, heads=None, initial_state=None):
     """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment,
-    for the heads ``heads = (begin, count)`` (default: all)."""
+    for the heads ``heads = (begin, count)`` (default: all).  Sequences start
+    from ``initial_state`` [N, H, K, V] when given, else from zero."""
     H, K, V, ins = _inputs(plan, None, k, v, g, beta)
+    ins.append(_init_ptr(plan, H, K, V, initial_state))
     outs = [
         _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
         _ptr(updates, torch.float32, (plan.S, H, K, V), "updates"),
@@ -230,9 +239,11 @@ def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, 
 
 
 def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
-                chunk_cache, stream=None, heads=None):
-    """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r."""
+                chunk_cache, stream=None, heads=None, initial_state=None):
+    """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r
+    (a fragment that starts a sequence from ``initial_state``, else zero)."""
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
+    ins.append(_init_ptr(plan, H, K, V, initial_state))
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
     oo = _ptr(o, torch.float32, (plan.T, H, V), "o")
     ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
@@ -282,8 +293,11 @@ def _side_stream(device) -> torch.cuda.Stream:
     return s
 
 
-def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, events=None):
+def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, events=None,
+            initial_state=None):
     """The whole segmented forward: summaries, compose, carry.  Returns ``out``.
+    Sequence n starts from ``initial_state[n]`` ([N, H, K, V] FP32) when given,
+    else from zero.
 
     With ``groups`` > 1 the heads are cut into that many groups.  Summaries and
     carry launches of every group run in order on ``stream``; each group's
@@ -315,12 +329,13 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
 
     if len(runs) == 1:
         timed("summaries", main, lambda: segment_summaries(
-            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main))
+            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main,
+            initial_state=initial_state))
         timed("compose", main, lambda: compose_summaries(
             plan, pd, out["transitions"], out["updates"], out["carry_in"], main))
         timed("carry", main, lambda: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["chunk_cache"], main))
+            out["chunk_cache"], main, initial_state=initial_state))
         return out
 
     side = _side_stream(q.device)
@@ -328,7 +343,7 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
     for hr in runs:
         timed("summaries", main, lambda hr=hr: segment_summaries(
             plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main,
-            heads=hr))
+            heads=hr, initial_state=initial_state))
         ev = torch.cuda.Event()
         ev.record(main)
         done_s.append(ev)
@@ -343,7 +358,7 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
         main.wait_event(evc)
         timed("carry", main, lambda hr=hr: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["chunk_cache"], main, heads=hr))
+            out["chunk_cache"], main, heads=hr, initial_state=initial_state))
     # every launch on the side stream precedes the last carry launch on main,
     # so work issued later on main is ordered after all of it
     return out

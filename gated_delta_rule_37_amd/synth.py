@@ -117,6 +117,14 @@ def workload_inputs(w: Workload):
                        max_len=w.max_len, gate_scale=w.gate_scale)
 
 
+def initial_states(N: int, H: int, K: int, V: int, seed: int, scale: float = 0.5) -> torch.Tensor:
+    """Per-sequence initial states [N, H, K, V], FP32, scale * N(0, 1) drawn from
+    ``torch.Generator('cpu').manual_seed(seed)`` (no workload specifies one;
+    these exercise the optional initial-state input)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return (scale * torch.randn(N, H, K, V, generator=gen, dtype=torch.float32)).contiguous()
+
+
 def bits(t: torch.Tensor):
     """The raw 16-bit patterns of a bf16 tensor as a numpy uint16 array."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")

@@ -46,8 +46,13 @@
  *       q, k, g : [T, H, K] bf16        v : [T, H, V] bf16
  *       beta    : [T, H]    bf16
  *       o       : [T, H, V] fp32        final_state : [N, H, K, V] fp32
+ *       initial_state : [N, H, K, V] fp32, or NULL (every sequence starts at 0)
  *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
  *       chunk_cache : kda_chunk_cache_bytes(plan, H) bytes of device memory
+ *   - Initial states: sequence n starts from initial_state[n] (the reading
+ *     that a sequence start resets the state to the sequence's own initial
+ *     state, zero when none is given).  Pass the same initial_state, or NULL
+ *     to both, to kda_segment_summaries and kda_apply_carry.
  *   - Head range: each device call works on the heads [head_begin,
  *     head_begin + head_count) of tensors that hold H heads, and touches no
  *     other head's data (outputs included).  Heads are independent, so the
@@ -159,7 +164,8 @@ size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
  *
  * Writes:
  *   updates[r]      = B_r, the state at the end of segment r run from zero
- *                     (reset at each sequence start inside it);
+ *                     (reset at each sequence start inside it to that
+ *                     sequence's initial state);
  *   transitions[r]  = A_r, the product of the per-token maps of segment r,
  *                     latest on the left, when segment r carries in and no
  *                     sequence starts inside it; otherwise exactly 0 (the
@@ -173,7 +179,8 @@ size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
  */
 int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
                           const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                          const uint16_t* beta, int32_t H, int32_t K, int32_t V,
+                          const uint16_t* beta, const float* initial_state,
+                          int32_t H, int32_t K, int32_t V,
                           int32_t head_begin, int32_t head_count,
                           float* transitions, float* updates, void* chunk_cache,
                           hipStream_t stream);
@@ -194,7 +201,8 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
 /*
  * kda_apply_carry -- the forward with the carry applied: every fragment (a
  * run of one sequence's tokens inside one segment) starts from its
- * segment's carry-in C_r when it continues a sequence, else from zero, and
+ * segment's carry-in C_r when it continues a sequence, else from the
+ * sequence's initial state (zero when initial_state is NULL), and
  * writes its rows of o and, when it ends a sequence, that sequence's
  * final_state.  Every row of o and every final state is written here.
  * #136 Summary (the forward that consumes
@@ -205,7 +213,7 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
  */
 int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const uint16_t* g, const uint16_t* beta,
+                    const uint16_t* g, const uint16_t* beta, const float* initial_state,
                     int32_t H, int32_t K, int32_t V,
                     int32_t head_begin, int32_t head_count, const float* carry_in,
                     float* o, float* final_state, const void* chunk_cache,

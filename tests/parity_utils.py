@@ -30,10 +30,11 @@ def to_device(x, dev="cuda:0"):
     return {n: x[n].to(dev) for n in NAMES}
 
 
-def run_gpu(x, cu, S, bounds=None, dev="cuda:0"):
+def run_gpu(x, cu, S, bounds=None, dev="cuda:0", h0=None):
     plan = kda.Plan(cu, S, bounds)
     d = to_device(x, dev)
-    out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"])
+    init = None if h0 is None else h0.to(dev)
+    out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=init)
     torch.cuda.synchronize()
     out.pop("chunk_cache")   # an internal cache between the two passes, not an output
     return plan, out
@@ -50,14 +51,20 @@ def oracle_inputs(x, heads=None):
     return res
 
 
-def run_oracle(x, cu, plan, heads=None, want_o=True):
+def run_oracle(x, cu, plan, heads=None, want_o=True, h0=None):
+    """fp64 reference; ``h0`` is the FP32 initial-state tensor the GPU got (or None)."""
     f = oracle_inputs(x, heads)
     bounds = plan.blob[4:4 + plan.S + 1].tolist()
+    init = None
+    if h0 is not None:
+        init = h0.double().numpy()
+        if heads is not None:
+            init = init[:, heads]
     ref = {}
     if want_o:
-        ref["o"], ref["final"] = ko.recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], cu)
+        ref["o"], ref["final"] = ko.recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], cu, h0=init)
     ref["A"] = ko.segment_transitions(f["k"], f["g"], f["beta"], cu, bounds)
-    ref["B"] = ko.segment_updates(f["k"], f["v"], f["g"], f["beta"], cu, bounds)
+    ref["B"] = ko.segment_updates(f["k"], f["v"], f["g"], f["beta"], cu, bounds, h0=init)
     ref["C"], _ = ko.compose(ref["A"], ref["B"])
     return ref
 

@@ -107,9 +107,9 @@ _FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereference
 
 
 def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, k=_FAKE, upd=_FAKE, cache=_FAKE,
-                    h0=0, hn=None):
+                    h0=0, hn=None, init=None):
     L = kda.lib()
-    return L.kda_segment_summaries(plan.handle, plan_dev, k, _FAKE, _FAKE, _FAKE,
+    return L.kda_segment_summaries(plan.handle, plan_dev, k, _FAKE, _FAKE, _FAKE, init,
                                    H, K, V, h0, H if hn is None else hn, _FAKE, upd, cache, None)
 
 
@@ -124,7 +124,7 @@ def test_head_ranges_validate_before_launch():
         assert _call_summaries(plan, k=bad, h0=h0, hn=hn) == -1, (h0, hn)
         assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 128, 128, h0, hn,
                                        bad, None) == -1, (h0, hn)
-        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
                                  h0, hn, bad, _FAKE, _FAKE, _FAKE, None) == -1, (h0, hn)
     # a valid range reaches the pointer checks
     assert _call_summaries(plan, k=bad, h0=1, hn=1) == -5
@@ -154,17 +154,22 @@ def test_device_calls_validate_before_launch():
     assert _call_summaries(plan, cache=0) == -1
     assert _call_summaries(plan, cache=_FAKE + 8) == -5
     L = kda.lib()
-    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128, 0, 2,
+    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128, 0, 2,
                                    _FAKE, _FAKE, _FAKE, None) == -1
+    # the optional initial states: misaligned is refused (NULL is valid and
+    # means zero, so it is not tried here with fake buffers)
+    assert _call_summaries(plan, init=_FAKE + 4) == -5
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE + 8, 2, 128,
+                             128, 0, 2, _FAKE, _FAKE, _FAKE, _FAKE, None) == -5
     assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, 0, 2, _FAKE,
                                    None) == -4
     assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, 0, 2, _FAKE,
                                    None) == -1
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
                              0, 2, _FAKE + 4, _FAKE, _FAKE, _FAKE, None) == -5
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
                              0, 2, _FAKE, 0, _FAKE, _FAKE, None) == -1
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, 128, 128,
+    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
                              0, 2, _FAKE, _FAKE, _FAKE, 0, None) == -1
     assert L.kda_last_hip_error() == 0
 

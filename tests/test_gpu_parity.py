@@ -48,6 +48,46 @@ def test_small_cases(name, T, H, cu, S, bounds, gs):
     pu.compare(pu.gpu_numpy(out), ref, name)
 
 
+H0_CASES = [
+    # name, T, H, cu_seqlens, segments, gate scale: sequences that start at
+    # token 0, at a segment boundary and inside segments
+    ("h0_single_sequence", 200, 2, [0, 200], 3, 0.05),
+    ("h0_varlen_mid_segment_starts", 300, 2, [0, 37, 150, 151, 300], 4, 0.05),
+    ("h0_short_sequences", 100, 2, [0, 3, 10, 11, 40, 64, 65, 98, 100], 5, 1.0),
+    ("h0_long_compose", 1000, 2, [0, 333, 334, 700, 1000], 25, 0.01),
+]
+
+
+@pytest.mark.parametrize("name,T,H,cu,S,gs", H0_CASES, ids=[c[0] for c in H0_CASES])
+def test_initial_states(name, T, H, cu, S, gs):
+    print(f"case {name}: T={T} H={H} S={S} cu={cu}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=len(name) + T, cu_seqlens=cu, gate_scale=gs)
+    h0 = synth.initial_states(len(cu) - 1, H, 128, 128, seed=T + S)
+    plan, out = pu.run_gpu(x, cu, S, h0=h0)
+    ref = pu.run_oracle(x, cu, plan, h0=h0)
+    pu.compare(pu.gpu_numpy(out), ref, name)
+
+
+def test_zero_initial_states_equal_none_and_scale_with_v():
+    """A zero initial state gives bitwise the results of none; doubling v and
+    the initial states together doubles o, the final states, B and C bit for
+    bit and leaves A alone."""
+    T, H, cu, S = 300, 2, [0, 120, 121, 300], 4
+    x = synth.make_inputs(T, H, 128, 128, seed=16, cu_seqlens=cu, gate_scale=0.05)
+    _, base = pu.run_gpu(x, cu, S)
+    _, zero = pu.run_gpu(x, cu, S, h0=torch.zeros(3, H, 128, 128))
+    for key in base:
+        assert torch.equal(zero[key], base[key]), key
+    h0 = synth.initial_states(3, H, 128, 128, seed=17)
+    _, out1 = pu.run_gpu(x, cu, S, h0=h0)
+    x2 = dict(x)
+    x2["v"] = (x["v"].float() * 2).to(torch.bfloat16)
+    _, out2 = pu.run_gpu(x2, cu, S, h0=2 * h0)
+    for key in ("o", "final_state", "updates", "carry_in"):
+        assert torch.equal(out2[key], 2 * out1[key]), key
+    assert torch.equal(out2["transitions"], out1["transitions"])
+
+
 def test_pure_decay_beta_zero():
     T, H, cu, S = 160, 2, [0, 160], 3
     x = synth.make_inputs(T, H, 128, 128, seed=5, cu_seqlens=cu, gate_scale=0.01)

@@ -41,3 +41,19 @@ def test_workload_sampled_heads(name, heads):
         assert np.abs(ref["A"][1:]).max() > 1e-7
         assert np.abs(ref["C"][1:]).max() > 1e-2
     assert errs["o_abs"] <= pu.O_ATOL
+
+
+def test_workload_with_initial_states():
+    """The varlen workload at full size with an initial state for every
+    sequence (sampled heads, every token)."""
+    name, heads = "varlen32k_h32_s8", [9]
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w)
+    cu = x["cu_seqlens"].tolist()
+    h0 = synth.initial_states(len(cu) - 1, w.H, 128, 128, seed=31)
+    print(f"workload {name} with initial states: N={len(cu) - 1} heads={heads}", flush=True)
+    plan, out = pu.run_gpu(x, cu, w.segments, h0=h0)
+    got = pu.gpu_numpy(out, heads)
+    del out
+    torch.cuda.empty_cache()
+    pu.compare(got, pu.run_oracle(x, cu, plan, heads, h0=h0), name + "+h0")
