@@ -60,10 +60,11 @@ BYTES = {
 STATE_BYTES = K * V * 4
 
 
-def chunk_kernel_work(blob, H):
+def chunk_kernel_work(blob, H, o_bytes=4):
     """Algorithmic MACs, executed bf16 MFMA MACs and HBM bytes of the two chunk
     launches, from the plan blob: {"summaries": ..., "carry": ...}
-    (kda_chunk_kernel, then kda_carry_kernel)."""
+    (kda_chunk_kernel, then kda_carry_kernel).  ``o_bytes`` is the size of one
+    element of o (4 for FP32, 2 for the BF16 output)."""
     T, N, S, F = (int(x) for x in blob[:4])
     o = 4
     o += S + 1          # seg_bounds
@@ -97,7 +98,7 @@ def chunk_kernel_work(blob, H):
         # carry: o and the final state of every fragment, from C_r or zero
         work["carry"]["macs"] += MACS["fwd_cached" if seg_last else "fwd"] * L * H
         work["carry"]["mfma_macs"] += MFMA_MACS["fwd_cached" if seg_last else "fwd"] * L * H
-        work["carry"]["bytes"] += BYTES["fwd"] * L * H + STATE_BYTES * H * (carried + seq_end)
+        work["carry"]["bytes"] += (BYTES["fwd"] - (4 - o_bytes) * V) * L * H + STATE_BYTES * H * (carried + seq_end)
     return work
 
 
@@ -140,13 +141,16 @@ def cpu_baseline(x, w, heads=8, tokens=16384):
     }
 
 
-def traffic_from_profile(kernel):
+def traffic_from_profile(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed PMC summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and this workload (default options);
+    else None."""
     path = TRAFFIC_JSON
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec.get("workload") != workload:
+        return None
     digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if rec.get("kernel_source_sha256") != digest:
         return None
@@ -226,6 +230,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--initial-state", action="store_true",
                     help="give every sequence a (seeded, random) initial state")
+    ap.add_argument("--o-bf16", action="store_true", help="store o as BF16 (rounded FP32 result)")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -259,7 +264,7 @@ def main():
     cu = x["cu_seqlens"].tolist()
     plan = kda.Plan(cu, w.segments)
     pd = plan.device_blob(dev)
-    out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev)
+    out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev, torch.bfloat16 if args.o_bf16 else torch.float32)
     h0 = None
     if args.initial_state:
         h0 = synth.initial_states(plan.N, w.H, w.K, w.V, seed=w.seed + 1000).to(dev)
@@ -289,7 +294,7 @@ def main():
     pass1_ms, compose_ms, pass2_ms = per_step["summaries"], per_step["compose"], per_step["carry"]
 
     blob = plan.blob
-    cw = chunk_kernel_work(blob, w.H)
+    cw = chunk_kernel_work(blob, w.H, 2 if args.o_bf16 else 4)
     # one launch covers 1/groups of the heads: its work is the step's / groups
     # (groups of equal size; the bench workload's 32 heads split evenly)
     launches = {"kda_chunk_kernel": (cw["summaries"], launch_ms["summaries"]),
@@ -308,8 +313,10 @@ def main():
             achieved = wk["bytes"] / (ms * 1e-3) / 1e9
             r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-        # the committed counters were taken with one launch per step
-        r["traffic"] = traffic_from_profile(name) if groups == 1 else None
+        # the committed counters were taken with one launch per step, FP32 o
+        # and no initial states
+        default_opts = groups == 1 and not args.o_bf16 and not args.initial_state
+        r["traffic"] = traffic_from_profile(name, w.name) if default_opts else None
         r["kernel"] = name
         r["launch_ms_avg"] = round(ms, 4)
         r["launches_per_step"] = groups
@@ -340,7 +347,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "segments": w.segments, "sequences": plan.N, "seed": w.seed,
-                   "head_groups": groups, "initial_state": bool(args.initial_state)},
+                   "head_groups": groups, "initial_state": bool(args.initial_state),
+                   "o": "bf16" if args.o_bf16 else "fp32"},
         "roofline": roof,
         # summed launch durations per step; with head groups the compose
         # launches overlap the other two on a second stream

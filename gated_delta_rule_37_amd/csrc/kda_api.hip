@@ -130,7 +130,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
                                const uint16_t* beta, const float* initial_state,
                                int32_t H, int32_t K, int32_t V,
                                int32_t head_begin, int32_t head_count,
-                               const float* carry_in, float* o, float* final_state,
+                               const float* carry_in, void* o, int32_t o_format, float* final_state,
                                const void* chunk_cache, hipStream_t stream) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
@@ -140,6 +140,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   if (st != KDA_OK) return st;
   st = check_optional(initial_state);
   if (st != KDA_OK) return st;
+  if (o_format != KDA_O_FP32 && o_format != KDA_O_BF16) return KDA_ERR_INVALID_ARG;
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -150,7 +151,8 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.v = v;
   p.g = g;
   p.beta = beta;
-  p.o = o;
+  p.o = static_cast<float*>(o);
+  p.o_bf16 = o_format == KDA_O_BF16 ? 1 : 0;
   p.final_state = final_state;
   p.transitions = nullptr;
   p.updates = nullptr;

@@ -26,7 +26,8 @@ struct ChunkParams {
   const uint16_t* v;
   const uint16_t* g;
   const uint16_t* beta;
-  float* o;
+  float* o;              // [T, H, V], FP32, or BF16 bits when o_bf16 is set
+  int32_t o_bf16;
   float* final_state;
   float* transitions;
   float* updates;

@@ -770,15 +770,33 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     if (fwd) {
       mfma_result_fence(O);
       // rows past the fragment's end fall outside the buffer and are dropped
-      const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
-                                                         (nn - 1) * o_row + 4 * VD, kBufDword3);
-      const int o_voff = 4 * lh * o_row + 4 * col;
+      if (p.o_bf16) {
+        // BF16 o: the FP32 result rounded to nearest even
+        const int ob_row = o_row / 2;
+        const auto rso = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<uint16_t*>(p.o) + (static_cast<size_t>(c0) * H + h) * VD, 0,
+            (nn - 1) * ob_row + 2 * VD, kBufDword3);
+        const int o_voff = 4 * lh * ob_row + 2 * col;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ov = O[4 * r + e];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+          for (int e = 0; e < 4; ++e) {
+            const bf16 ob = static_cast<bf16>(O[4 * r + e]);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, ob), rso, o_voff,
+                                                  (8 * r + e) * ob_row, 0);
+          }
+        }
+      } else {
+        const auto rso = __builtin_amdgcn_make_buffer_rsrc(p.o + (static_cast<size_t>(c0) * H + h) * VD, 0,
+                                                           (nn - 1) * o_row + 4 * VD, kBufDword3);
+        const int o_voff = 4 * lh * o_row + 4 * col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ov = O[4 * r + e];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+          }
         }
       }
     }

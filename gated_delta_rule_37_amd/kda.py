@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.kda_segment_summaries.restype = ctypes.c_int
     L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p]
+    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
     L.kda_apply_carry.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -245,21 +245,28 @@ def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, 
     H, K, V, ins = _inputs(plan, q, k, v, g, beta)
     ins.append(_init_ptr(plan, H, K, V, initial_state))
     c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
-    oo = _ptr(o, torch.float32, (plan.T, H, V), "o")
+    if o.dtype not in O_FORMATS:
+        raise TypeError(f"o: expected one of {list(O_FORMATS)}, got {o.dtype}")
+    oo = _ptr(o, o.dtype, (plan.T, H, V), "o")
     ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
     cc = _cache_ptr(plan, H, chunk_cache)
     pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), c, oo, ff, cc,
-                               _stream(q, stream))
+    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), c, oo,
+                               O_FORMATS[o.dtype], ff, cc, _stream(q, stream))
     _check(st, "kda_apply_carry")
 
 
-def alloc_outputs(plan: Plan, H: int, K: int, V: int, device):
+# storage formats of o accepted by kda_apply_carry (kda_o_format)
+O_FORMATS = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def alloc_outputs(plan: Plan, H: int, K: int, V: int, device, o_dtype=torch.float32):
     """Fresh output buffers (o, final_state, transitions, updates, carry_in) and
-    the chunk cache shared by the summaries and carry passes."""
+    the chunk cache shared by the summaries and carry passes.  ``o_dtype`` is
+    float32, or bfloat16 for the rounded BF16 output."""
     f32 = dict(dtype=torch.float32, device=device)
     return dict(
-        o=torch.empty(plan.T, H, V, **f32),
+        o=torch.empty(plan.T, H, V, dtype=o_dtype, device=device),
         final_state=torch.empty(plan.N, H, K, V, **f32),
         transitions=torch.empty(plan.S, H, K, K, **f32),
         updates=torch.empty(plan.S, H, K, V, **f32),
@@ -294,10 +301,11 @@ def _side_stream(device) -> torch.cuda.Stream:
 
 
 def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, events=None,
-            initial_state=None):
+            initial_state=None, o_dtype=torch.float32):
     """The whole segmented forward: summaries, compose, carry.  Returns ``out``.
     Sequence n starts from ``initial_state[n]`` ([N, H, K, V] FP32) when given,
-    else from zero.
+    else from zero.  ``o_dtype`` (used when ``out`` is None) is float32 or
+    bfloat16.
 
     With ``groups`` > 1 the heads are cut into that many groups.  Summaries and
     carry launches of every group run in order on ``stream``; each group's
@@ -311,7 +319,7 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
     T, H, K = q.shape
     V = v.shape[2]
     if out is None:
-        out = alloc_outputs(plan, H, K, V, q.device)
+        out = alloc_outputs(plan, H, K, V, q.device, o_dtype)
     pd = plan.device_blob(q.device)
     main = torch.cuda.current_stream(q.device) if stream is None else stream
     runs = head_groups(H, groups)

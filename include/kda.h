@@ -45,7 +45,8 @@
  *     (other K, V return KDA_ERR_UNSUPPORTED).
  *       q, k, g : [T, H, K] bf16        v : [T, H, V] bf16
  *       beta    : [T, H]    bf16
- *       o       : [T, H, V] fp32        final_state : [N, H, K, V] fp32
+ *       o       : [T, H, V] fp32 (or bf16, see kda_o_format)
+ *       final_state : [N, H, K, V] fp32
  *       initial_state : [N, H, K, V] fp32, or NULL (every sequence starts at 0)
  *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
  *       chunk_cache : kda_chunk_cache_bytes(plan, H) bytes of device memory
@@ -92,6 +93,15 @@ typedef enum kda_status {
   KDA_ERR_HIP = -6,            /* a HIP launch failed; see kda_last_hip_error() */
   KDA_ERR_NO_MEMORY = -7       /* host allocation for the plan failed */
 } kda_status;
+
+/* Storage format of o (kda_apply_carry).  The recurrence runs in FP32 either
+ * way; KDA_O_BF16 stores each element rounded to the nearest bfloat16 (ties
+ * to even), which halves the output bytes.  The pages fix BF16 inputs and an
+ * FP32 state ([#110] Supported configuration) but not o's storage. */
+typedef enum kda_o_format {
+  KDA_O_FP32 = 0,
+  KDA_O_BF16 = 1
+} kda_o_format;
 
 /* Opaque host-side plan; immutable once built. */
 typedef struct kda_plan kda_plan;
@@ -208,6 +218,8 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
  * #136 Summary (the forward that consumes
  * preceding_state_update / preceding_transition), #110 Motivation (rank 1
  * consumes only the V-state it needs).
+ *   o            [T, H, V] in the format o_format names (kda_o_format; other
+ *                values give KDA_ERR_INVALID_ARG): FP32, or BF16 bits.
  *   chunk_cache  the buffer kda_segment_summaries filled for the same plan,
  *                H and inputs (read only).
  */
@@ -216,7 +228,7 @@ int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
                     const uint16_t* g, const uint16_t* beta, const float* initial_state,
                     int32_t H, int32_t K, int32_t V,
                     int32_t head_begin, int32_t head_count, const float* carry_in,
-                    float* o, float* final_state, const void* chunk_cache,
+                    void* o, int32_t o_format, float* final_state, const void* chunk_cache,
                     hipStream_t stream);
 
 /* Human-readable name of a kda_status value. */

@@ -125,7 +125,7 @@ def test_head_ranges_validate_before_launch():
         assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 128, 128, h0, hn,
                                        bad, None) == -1, (h0, hn)
         assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                                 h0, hn, bad, _FAKE, _FAKE, _FAKE, None) == -1, (h0, hn)
+                                 h0, hn, bad, _FAKE, 0, _FAKE, _FAKE, None) == -1, (h0, hn)
     # a valid range reaches the pointer checks
     assert _call_summaries(plan, k=bad, h0=1, hn=1) == -5
 
@@ -160,17 +160,21 @@ def test_device_calls_validate_before_launch():
     # means zero, so it is not tried here with fake buffers)
     assert _call_summaries(plan, init=_FAKE + 4) == -5
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE + 8, 2, 128,
-                             128, 0, 2, _FAKE, _FAKE, _FAKE, _FAKE, None) == -5
+                             128, 0, 2, _FAKE, _FAKE, 0, _FAKE, _FAKE, None) == -5
     assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, 0, 2, _FAKE,
                                    None) == -4
     assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, 0, 2, _FAKE,
                                    None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE + 4, _FAKE, _FAKE, _FAKE, None) == -5
+                             0, 2, _FAKE + 4, _FAKE, 0, _FAKE, _FAKE, None) == -5
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE, 0, _FAKE, _FAKE, None) == -1
+                             0, 2, _FAKE, 0, 0, _FAKE, _FAKE, None) == -1
     assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE, _FAKE, _FAKE, 0, None) == -1
+                             0, 2, _FAKE, _FAKE, 0, _FAKE, 0, None) == -1
+    # an unknown o format is refused before launch
+    for fmt in (-1, 2, 7):
+        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128,
+                                 128, 0, 2, _FAKE, _FAKE, fmt, _FAKE, _FAKE, None) == -1, fmt
     assert L.kda_last_hip_error() == 0
 
 

@@ -88,6 +88,39 @@ def test_zero_initial_states_equal_none_and_scale_with_v():
     assert torch.equal(out2["transitions"], out1["transitions"])
 
 
+BF16_O_CASES = [
+    ("bf16o_varlen", 300, 2, [0, 37, 150, 151, 300], 4, 0.05, False),
+    ("bf16o_initial_states", 200, 2, [0, 90, 200], 3, 0.3, True),
+]
+
+
+@pytest.mark.parametrize("name,T,H,cu,S,gs,with_h0", BF16_O_CASES, ids=[c[0] for c in BF16_O_CASES])
+def test_bf16_output(name, T, H, cu, S, gs, with_h0):
+    """o stored as BF16 is the FP32 run's o rounded to nearest even, bit for
+    bit, and every other output is unchanged.  Against the oracle its error
+    bound is the FP32 one plus the rounding, 2e-3 + 2^-8 |o_ref| per element
+    (a bfloat16 half-ulp is at most 2^-9 |o|, doubled for margin)."""
+    print(f"case {name}: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=len(name) + T, cu_seqlens=cu, gate_scale=gs)
+    h0 = synth.initial_states(len(cu) - 1, H, 128, 128, seed=T) if with_h0 else None
+    plan = kda.Plan(cu, S)
+    d = pu.to_device(x)
+    init = None if h0 is None else h0.to("cuda:0")
+    o32 = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=init)
+    o16 = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=init,
+                      o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16["o"].dtype == torch.bfloat16
+    assert torch.equal(o16["o"], o32["o"].to(torch.bfloat16))
+    for key in ("final_state", "transitions", "updates", "carry_in"):
+        assert torch.equal(o16[key], o32[key]), key
+    ref = pu.run_oracle(x, cu, plan, h0=h0)
+    err = np.abs(o16["o"].double().cpu().numpy() - ref["o"])
+    bound = pu.O_ATOL + 2.0 ** -8 * np.abs(ref["o"])
+    print(f"[{name}] bf16 o: max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}", flush=True)
+    assert (err <= bound).all()
+
+
 def test_pure_decay_beta_zero():
     T, H, cu, S = 160, 2, [0, 160], 3
     x = synth.make_inputs(T, H, 128, 128, seed=5, cu_seqlens=cu, gate_scale=0.01)

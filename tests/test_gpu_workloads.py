@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_37_amd import synth
+from gated_delta_rule_37_amd import kda, synth
 import parity_utils as pu
 
 pytestmark = pytest.mark.gpu
@@ -57,3 +57,18 @@ def test_workload_with_initial_states():
     del out
     torch.cuda.empty_cache()
     pu.compare(got, pu.run_oracle(x, cu, plan, heads, h0=h0), name + "+h0")
+
+
+def test_bench_workload_bf16_output():
+    """At the bench workload's full size, the BF16 o is the FP32 run's o
+    rounded to nearest even, bit for bit (every element)."""
+    w = synth.WORKLOADS["t65536_h32_s64"]
+    x = synth.workload_inputs(w)
+    cu = x["cu_seqlens"].tolist()
+    print(f"workload {w.name} bf16 o", flush=True)
+    plan = kda.Plan(cu, w.segments)
+    d = pu.to_device(x)
+    o32 = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"])["o"]
+    o16 = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.bfloat16)["o"]
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
