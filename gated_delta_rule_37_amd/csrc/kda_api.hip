@@ -42,6 +42,17 @@ int check_tensors(std::initializer_list<const void*> ptrs) {
   return KDA_OK;
 }
 
+// Grid of a chunk kernel: F * hn workgroups numbered linearly (head fastest),
+// laid out as x = hn * a, y = ceil(F / a) with the smallest a that keeps y
+// within 65535.  x must stay within 2^31 - 1 work-items.
+int chunk_grid(int32_t F, int32_t hn, int threads, dim3* grid) {
+  const int64_t a = (static_cast<int64_t>(F) + 65534) / 65535;
+  const int64_t x = static_cast<int64_t>(hn) * (a > 0 ? a : 1);
+  if (x * threads > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  *grid = dim3(static_cast<uint32_t>(x), static_cast<uint32_t>((F + x / hn - 1) / (x / hn)), 1);
+  return KDA_OK;
+}
+
 int finish_launch() {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -81,6 +92,7 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.L = plan->layout;
   p.H = H;
   p.h0 = head_begin;
+  p.hn = head_count;
   p.q = nullptr;
   p.k = k;
   p.v = v;
@@ -94,7 +106,10 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.init_state = initial_state;
   p.chunk_cache = static_cast<uint16_t*>(chunk_cache);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_chunk_kernel, dim3(plan->F, head_count, 1), dim3(kda::kSummaryThreads), 0, stream, p);
+  dim3 grid;
+  st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(kda::kda_chunk_kernel, grid, dim3(kda::kSummaryThreads), 0, stream, p);
   return finish_launch();
 }
 
@@ -146,6 +161,7 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.L = plan->layout;
   p.H = H;
   p.h0 = head_begin;
+  p.hn = head_count;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -160,6 +176,9 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.init_state = initial_state;
   p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(chunk_cache));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_carry_kernel, dim3(plan->F, head_count, 1), dim3(kda::kCarryThreads), 0, stream, p);
+  dim3 grid;
+  st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(kda::kda_carry_kernel, grid, dim3(kda::kCarryThreads), 0, stream, p);
   return finish_launch();
 }

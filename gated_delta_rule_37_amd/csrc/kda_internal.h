@@ -20,10 +20,10 @@ constexpr int32_t kMaxTokens = (1 << 30);
 // Word offsets of the arrays inside the plan blob (see kda_plan_blob()).
 struct BlobLayout {
   int32_t seg_bounds, seg_first_seq, seg_last_seq, seg_carry_in, seg_transition_live,
-      seg_frag_ptr, frag_seq, frag_begin, frag_end, frag_seg, frag_flags, seq_end_seg;
+      seg_frag_ptr, frag_seq, frag_begin, frag_end, frag_seg, frag_flags, seq_end_seg, frag_order;
 };
 
-inline BlobLayout blob_layout(int32_t S, int32_t F) {
+inline BlobLayout blob_layout(int32_t S, int32_t F, int32_t N) {
   BlobLayout L;
   int32_t o = 4;
   L.seg_bounds = o;          o += S + 1;
@@ -37,7 +37,8 @@ inline BlobLayout blob_layout(int32_t S, int32_t F) {
   L.frag_end = o;            o += F;
   L.frag_seg = o;            o += F;
   L.frag_flags = o;          o += F;
-  L.seq_end_seg = o;
+  L.seq_end_seg = o;         o += N;
+  L.frag_order = o;
   return L;
 }
 

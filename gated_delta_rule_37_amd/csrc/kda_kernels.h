@@ -20,7 +20,8 @@ struct ChunkParams {
   const int32_t* plan;   // device copy of the plan blob
   BlobLayout L;
   int32_t H;             // heads in the tensors (their stride)
-  int32_t h0;            // first head of this launch (grid y covers the rest)
+  int32_t h0;            // heads [h0, h0 + hn) are this launch's
+  int32_t hn;
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;

@@ -527,15 +527,29 @@ __device__ __forceinline__ void t_merge(const float* an, const float* tt, const 
   tbl[ti * TS + 16 + cp] = static_cast<bf16>(0.f);
 }
 
+// Chunk-kernel workgroups are numbered linearly, x fastest: id = rank * hn +
+// head.  The heads of one fragment are adjacent and the fragments come in the
+// plan's launch order (longest first).  The host spreads the ids over x and y
+// only when y alone would exceed its limit; ids past the end do nothing.
+__device__ __forceinline__ uint64_t block_linear() {
+  return static_cast<uint64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+}
+__device__ __forceinline__ int block_head(const ChunkParams& p) {
+  return p.h0 + static_cast<int>(block_linear() % static_cast<uint64_t>(p.hn));
+}
+__device__ __forceinline__ int64_t block_rank(const ChunkParams& p) {
+  return static_cast<int64_t>(block_linear() / static_cast<uint64_t>(p.hn));
+}
+
 // Chunk cache transfer of T diag(beta) (4 KB per chunk and head): the 256
 // lanes of four waves (index 0..255 = 64 wave + lane) each move 16 bytes,
 // lane i taking half i/128 (hi, lo), row (i/4) % 32 and quarter i % 4.
-__device__ __forceinline__ size_t cache_elem(const ChunkParams& p, const int32_t seg, const int32_t beg,
+__device__ __forceinline__ size_t cache_elem(const ChunkParams& p, const int h, const int32_t seg, const int32_t beg,
                                              const int it, const int i) {
   const int which = i >> 7;
   const int row = (i >> 2) & 31;
   const int q = i & 3;
-  return (static_cast<size_t>(chunk_cache_slot(seg, beg, it)) * p.H + p.h0 + blockIdx.y) * (kChunkCacheBytes / 2) +
+  return (static_cast<size_t>(chunk_cache_slot(seg, beg, it)) * p.H + h) * (kChunkCacheBytes / 2) +
          which * (CH * CH) + row * CH + 8 * q;
 }
 __device__ __forceinline__ int cache_lds(const int i) { return ((i >> 2) & 31) * TS + 8 * (i & 3); }
@@ -603,12 +617,12 @@ struct alignas(16) PipeSmem {
 //   kModeSumPhi from the identity with V = 0, no o: A_r
 // init points at the starting state's [K, V] matrix for this head, or is null.
 template <int MODE>
-__device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, const int ow, const int32_t flags,
+__device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, const int h, const int ow,
+                                           const int32_t flags,
                                            const int32_t seg, const int32_t seq, const int32_t beg,
                                            const int32_t end, const float* init) {
   constexpr bool fwd = MODE == kModeFwd;
   constexpr bool use_v = MODE != kModeSumPhi;
-  const int h = p.h0 + blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
   const int lh = lane >> 5;
@@ -849,10 +863,9 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 // stay in registers until part 2 (step 2m-2), when the owners are done with
 // chunk m-2's.
 template <int MODE>
-__device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm, const int oh, const int32_t beg,
+__device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm, const int h, const int oh, const int32_t beg,
                                               const int32_t end) {
   constexpr bool fwd = MODE == kModeFwd;
-  const int h = p.h0 + blockIdx.y;
   const int H = p.H;
   const int lane = threadIdx.x & 63;
   const int tk = lane & 15;                    // tokens tk and 16 + tk
@@ -1033,7 +1046,8 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
 // stores them in part 2: one block on each of th 0-2 where T diag(beta) comes
 // from the cache, all three on th 3 where th 0-2 build it.
 template <bool FILL>
-__device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int th, const int32_t flags,
+__device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int h, const int th,
+                                             const int32_t flags,
                                              const int32_t seg, const int32_t beg, const int32_t end) {
   const int lane = threadIdx.x & 63;
   const int nc = (end - beg + CH - 1) / CH;
@@ -1041,7 +1055,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
   const int ci = 64 * th + lane;   // this lane's 16 bytes of a cached chunk
   auto to_cache = [&](const int m) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)]);
-    *reinterpret_cast<u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, m, ci)) = v;
+    *reinterpret_cast<u32x4*>(p.chunk_cache + cache_elem(p, h, seg, beg, m, ci)) = v;
   };
   block_sync();   // steps -3, -2: the operands of chunk 0 are being built
   block_sync();
@@ -1057,7 +1071,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
       const int lane_s = opaque(lane);
       if (FILL && m > 0) to_cache(m - 1);
       if (cached) {
-        tbv = *reinterpret_cast<const u32x4*>(p.chunk_cache + cache_elem(p, seg, beg, m, ci));
+        tbv = *reinterpret_cast<const u32x4*>(p.chunk_cache + cache_elem(p, h, seg, beg, m, ci));
       } else if (th < 2) {
         a_diag_solve(sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.beta[b], sm.an, sm.tt, sm.tn, th, lane_s);
       } else if (th == 2) {
@@ -1109,9 +1123,10 @@ __device__ __forceinline__ void pipe_idle(const int32_t beg, const int32_t end) 
 // continues a sequence across its segment's start (carry launch; the
 // summaries launch runs B_r from zero there), else it starts a sequence and
 // begins at that sequence's initial state, if any.
-__device__ __forceinline__ const float* start_state(const ChunkParams& p, const int32_t flags, const int32_t seg,
+__device__ __forceinline__ const float* start_state(const ChunkParams& p, const int h_, const int32_t flags,
+                                                    const int32_t seg,
                                                     const int32_t seq, const bool carry_launch) {
-  const size_t h = static_cast<size_t>(p.h0) + blockIdx.y;
+  const size_t h = static_cast<size_t>(h_);
   if ((flags & kFragCarried) != 0)
     return carry_launch ? p.carry + (static_cast<size_t>(seg) * p.H + h) * KD * VD : nullptr;
   return p.init_state != nullptr ? p.init_state + (static_cast<size_t>(seq) * p.H + h) * KD * VD : nullptr;
@@ -1124,8 +1139,10 @@ __device__ __forceinline__ const float* start_state(const ChunkParams& p, const 
 // are the operand helpers and 12-15 the T helpers, shared by both states.
 __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkParams p) {
   __shared__ PipeSmem sm;
-  const int f = blockIdx.x;
-  const int h = p.h0 + blockIdx.y;
+  const int64_t rank = block_rank(p);
+  if (rank >= p.plan[3]) return;   // padding of the grid (header word 3 is F)
+  const int f = p.plan[p.L.frag_order + static_cast<int>(rank)];
+  const int h = block_head(p);
   const int tid = threadIdx.x;
   const int32_t flags = p.plan[p.L.frag_flags + f];
   const int32_t seg = p.plan[p.L.frag_seg + f];
@@ -1136,10 +1153,10 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < NOWN) {
-    pipe_owner<kModeSumS>(p, sm, wave, flags, seg, seq, beg, end, start_state(p, flags, seg, seq, false));
+    pipe_owner<kModeSumS>(p, sm, h, wave, flags, seg, seq, beg, end, start_state(p, h, flags, seg, seq, false));
   } else if (wave < 2 * NOWN) {
     if (work.phi) {
-      pipe_owner<kModeSumPhi>(p, sm, wave - NOWN, flags, seg, seq, beg, end, nullptr);
+      pipe_owner<kModeSumPhi>(p, sm, h, wave - NOWN, flags, seg, seq, beg, end, nullptr);
     } else {
       f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * p.H + h) * KD * KD);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -1147,18 +1164,21 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
       pipe_idle(beg, end);
     }
   } else if (wave < 3 * NOWN) {
-    pipe_ophelper<kModeSumS>(p, sm, wave - 2 * NOWN, beg, end);
+    pipe_ophelper<kModeSumS>(p, sm, h, wave - 2 * NOWN, beg, end);
   } else {
-    pipe_thelper<true>(p, sm, wave - 3 * NOWN, flags, seg, beg, end);
+    pipe_thelper<true>(p, sm, h, wave - 3 * NOWN, flags, seg, beg, end);
   }
 }
 
 // Carry launch: every fragment runs with the forward body (o and, where a
 // sequence ends, the final state), from its segment's carry-in C_r when it
-// continues a sequence, else from zero.
+// continues a sequence, else from its sequence's initial state (or zero).
 __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams p) {
   __shared__ PipeSmem sm;
-  const int f = blockIdx.x;
+  const int64_t rank = block_rank(p);
+  if (rank >= p.plan[3]) return;   // padding of the grid (header word 3 is F)
+  const int f = p.plan[p.L.frag_order + static_cast<int>(rank)];
+  const int h = block_head(p);
   const int tid = threadIdx.x;
   const int32_t flags = p.plan[p.L.frag_flags + f];
   const int32_t seg = p.plan[p.L.frag_seg + f];
@@ -1166,9 +1186,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave < NOWN) pipe_owner<kModeFwd>(p, sm, wave, flags, seg, seq, beg, end, start_state(p, flags, seg, seq, true));
-  else if (wave < 2 * NOWN) pipe_ophelper<kModeFwd>(p, sm, wave - NOWN, beg, end);
-  else pipe_thelper<false>(p, sm, wave - 2 * NOWN, flags, seg, beg, end);
+  if (wave < NOWN) pipe_owner<kModeFwd>(p, sm, h, wave, flags, seg, seq, beg, end, start_state(p, h, flags, seg, seq, true));
+  else if (wave < 2 * NOWN) pipe_ophelper<kModeFwd>(p, sm, h, wave - NOWN, beg, end);
+  else pipe_thelper<false>(p, sm, h, wave - 2 * NOWN, flags, seg, beg, end);
 }
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of

@@ -88,9 +88,16 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
     plan->F = F;
     std::vector<int32_t> end_seg(num_seqs);
     for (int32_t n = 0; n < num_seqs; ++n) end_seg[n] = locate(b, cu[n + 1] - 1);
+    // launch order: longest fragments first (ties by index), so that the long
+    // sequential chains are not the last to start
+    std::vector<int32_t> order(F);
+    for (int32_t f = 0; f < F; ++f) order[f] = f;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return f_end[x] - f_beg[x] > f_end[y] - f_beg[y];
+    });
 
     std::vector<int32_t>& blob = plan->blob;
-    blob.reserve(4 + (S + 1) * 2 + S * 4 + F * 5 + num_seqs);
+    blob.reserve(4 + (S + 1) * 2 + S * 4 + F * 6 + num_seqs);
     blob.insert(blob.end(), {T, num_seqs, S, F});
     auto append = [&blob](const std::vector<int32_t>& a) { blob.insert(blob.end(), a.begin(), a.end()); };
     append(b);
@@ -105,7 +112,8 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
     append(f_seg);
     append(f_flags);
     append(end_seg);
-    plan->layout = kda::blob_layout(S, F);
+    append(order);
+    plan->layout = kda::blob_layout(S, F, num_seqs);
   } catch (const std::bad_alloc&) {
     delete plan;
     return KDA_ERR_NO_MEMORY;

@@ -132,10 +132,13 @@ int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_s
  *   seg_bounds[S+1] seg_first_seq[S] seg_last_seq[S] seg_carry_in[S]
  *   seg_transition_live[S] seg_frag_ptr[S+1]
  *   frag_seq[F] frag_begin[F] frag_end[F] frag_seg[F] frag_flags[F]
- *   seq_end_seg[N]
+ *   seq_end_seg[N] frag_order[F]
  * A fragment is the part of one sequence inside one segment.  frag_flags bit
  * 1: first fragment of a segment that continues a sequence (it carries in);
  * bit 2: ends at its segment's end; bit 4: ends at its sequence's end.
+ * frag_order lists the fragments longest first (ties by index): the device
+ * calls start them in that order, so that the longest sequential chains do
+ * not start last (it changes no result).
  * `*blob` stays valid until kda_plan_destroy.
  */
 int kda_plan_blob(const kda_plan* plan, const int32_t** blob, size_t* n_int32);

@@ -21,9 +21,12 @@ The plan is serialised as one int32 vector (the "blob"):
   seg_bounds[S+1], seg_first_seq[S], seg_last_seq[S], seg_carry_in[S],
   seg_transition_live[S], seg_frag_ptr[S+1],
   frag_seq[F], frag_begin[F], frag_end[F], frag_seg[F], frag_flags[F],
-  seq_end_seg[N]
+  seq_end_seg[N], frag_order[F]
 frag_flags bits: 1 = first fragment of a carrying segment, 2 = ends at its
-segment's end, 4 = ends at its sequence's end.
+segment's end, 4 = ends at its sequence's end.  frag_order lists the fragments
+longest first (ties by index): the order in which they are worth starting, so
+that the long sequential ones do not start last (a scheduling choice, not part
+of the method).
 """
 from __future__ import annotations
 
@@ -103,18 +106,19 @@ def build_plan(cu_seqlens, num_segments, custom_bounds=None):
     F = len(f_seq)
     # the segment holding the sequence's last token (bounds partition [0, T) like cu_seqlens)
     seq_end_seg = [_seq_of_token(bounds, cu[n + 1] - 1) for n in range(N)]
+    frag_order = sorted(range(F), key=lambda f: (-(f_end[f] - f_beg[f]), f))
 
     plan = dict(
         T=T, N=N, S=S, F=F,
         seg_bounds=bounds, seg_first_seq=seg_first, seg_last_seq=seg_last,
         seg_carry_in=carry, seg_transition_live=live, seg_frag_ptr=frag_ptr,
         frag_seq=f_seq, frag_begin=f_beg, frag_end=f_end, frag_seg=f_seg,
-        frag_flags=f_flags, seq_end_seg=seq_end_seg,
+        frag_flags=f_flags, seq_end_seg=seq_end_seg, frag_order=frag_order,
     )
     blob = [T, N, S, F]
     for key in ("seg_bounds", "seg_first_seq", "seg_last_seq", "seg_carry_in",
                 "seg_transition_live", "seg_frag_ptr", "frag_seq", "frag_begin",
-                "frag_end", "frag_seg", "frag_flags", "seq_end_seg"):
+                "frag_end", "frag_seg", "frag_flags", "seq_end_seg", "frag_order"):
         blob.extend(plan[key])
     plan["blob"] = np.asarray(blob, dtype=np.int32)
     return plan

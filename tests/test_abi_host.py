@@ -43,7 +43,7 @@ def test_status_strings():
 @pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
 def test_plan_blob_matches_golden(case):
     plan = kda.Plan(case["cu_seqlens"], case["segments"], case["custom_bounds"])
-    assert plan.blob.tolist() == case["blob"]
+    assert plan.blob.tolist() == case["blob"] + case["frag_order"]
 
 
 @pytest.mark.parametrize("seed", range(40))

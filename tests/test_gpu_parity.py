@@ -10,6 +10,7 @@ import torch
 
 from gated_delta_rule_37_amd import kda, synth
 import parity_utils as pu
+from oracle import kda_oracle as ko
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +120,28 @@ def test_bf16_output(name, T, H, cu, S, gs, with_h0):
     bound = pu.O_ATOL + 2.0 ** -8 * np.abs(ref["o"])
     print(f"[{name}] bf16 o: max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}", flush=True)
     assert (err <= bound).all()
+
+
+def test_more_fragments_than_one_grid_dimension():
+    """70000 one-token sequences make 70000 fragments, more than the 65535
+    workgroups one grid dimension takes, so the launch folds the fragment
+    ranks over two dimensions (and pads the last row)."""
+    N = 70000
+    cu = list(range(N + 1))
+    x = synth.make_inputs(N, 1, 128, 128, seed=18, cu_seqlens=cu)
+    print(f"case {N} one-token sequences, one head", flush=True)
+    plan, out = pu.run_gpu(x, cu, 2)
+    assert plan.F == N
+    # every o row, and the final states of every 97th sequence (all of them
+    # would be 70000 state matrices on each side)
+    f = pu.oracle_inputs(x)
+    o_ref, fin_ref = ko.recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], cu)
+    o_err = float(np.abs(out["o"].double().cpu().numpy() - o_ref).max())
+    pick = list(range(0, N, 97))
+    fin = out["final_state"][pick].double().cpu().numpy()
+    rel = pu.state_errors(fin, fin_ref[pick])
+    print(f"[many fragments] o_abs={o_err:.3e}, final_rel={rel:.3e}", flush=True)
+    assert o_err <= pu.O_ATOL and rel <= pu.STATE_RTOL
 
 
 def test_pure_decay_beta_zero():

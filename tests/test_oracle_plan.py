@@ -18,7 +18,7 @@ def _cases():
 @pytest.mark.parametrize("case", _cases()["cases"], ids=lambda c: c["name"])
 def test_plan_matches_hand_derived_blob(case):
     plan = po.build_plan(case["cu_seqlens"], case["segments"], case["custom_bounds"])
-    assert plan["blob"].tolist() == case["blob"]
+    assert plan["blob"].tolist() == case["blob"] + case["frag_order"]
 
 
 @pytest.mark.parametrize("case", _cases()["invalid"])
