@@ -251,6 +251,24 @@ def test_head_groups_match_single_launch(groups):
     pu.compare(pu.gpu_numpy(out), pu.run_oracle(x, cu, plan), f"groups={groups}")
 
 
+def test_head_groups_with_initial_states_and_bf16_output():
+    """Head groups, initial states and the BF16 o together give bitwise the
+    single-launch results."""
+    T, H, cu, S = 300, 4, [0, 110, 300], 4
+    print(f"case head groups + h0 + bf16 o: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=19, cu_seqlens=cu, gate_scale=0.2)
+    h0 = synth.initial_states(2, H, 128, 128, seed=20).to("cuda:0")
+    plan = kda.Plan(cu, S)
+    d = pu.to_device(x)
+    one = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=h0,
+                      o_dtype=torch.bfloat16)
+    grp = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=h0,
+                      o_dtype=torch.bfloat16, groups=3)
+    torch.cuda.synchronize()
+    for key in ("o", "final_state", "transitions", "updates", "carry_in"):
+        assert torch.equal(grp[key], one[key]), key
+
+
 def test_head_range_touches_only_its_heads():
     """Each device call with a head range writes those heads' rows of its
     outputs and nothing else (the other heads keep a sentinel)."""
