@@ -890,14 +890,27 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
       rk[j] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0);
       rg[j] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
       if (fwd) rq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
-      rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
+      if (fwd) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0);
     }
     const int nb = (oh == 0 && nn > 0) ? (nn - 1) * H * 2 + 2 : 0;
     const auto rsb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.beta + static_cast<size_t>(min(cs, end - 1)) * H + h), 0, nb, kBufDword3);
     rb = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rsb, lane < CH ? lane * H * 2 : nb, 0, 0));
   };
+  // The summaries launch loads v in part 2, right after storing the previous
+  // chunk's v to LDS, and pins k's unpacked values before the next loads:
+  // both loads then land in registers that are already free, with no copies
+  // at the loop's back edge (which would wait for them one step early).
+  auto fetch_v = [&](int cs) {
+    const int nn = min(CH, end - cs);
+    const size_t base = (static_cast<size_t>(min(cs, end - 1)) * H + h) * KD;
+    const int nrec = nn > 0 ? (nn - 1) * row_bytes + KD * 2 : 0;
+    const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + base), 0, nrec, kBufDword3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(rsv, in_voff + 16 * j * row_bytes, 0, 0);
+  };
   fetch(beg);
+  if (!fwd) fetch_v(beg);
 
   // fac = 2^t for this lane's eight channels (t in log2 units), written by
   // the lanes with tk = 0.  Where 2^t would leave the FP32 normal range (the
@@ -957,7 +970,11 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
           G[j][2 * w] = __uint_as_float(rg[j][w] << 16) * kLog2e;
           G[j][2 * w + 1] = __uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e;
         }
-        vkeep[j] = rv[j];
+        if (fwd) vkeep[j] = rv[j];
+        if (!fwd) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(kf[j][c]));
+        }
       }
       if (oh == 0 && lane < CH) sm.beta[b][lane] = __uint_as_float(rb << 16);
       __builtin_amdgcn_sched_barrier(0);
@@ -1024,8 +1041,9 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
       const int off = (tk + 16 * j) * NS + c8;
       st4(&sm.kc_h[b][off], sw_rows(fwd && j, kch[j]));
       st4(&sm.kc_l[b][off], sw_rows(fwd && j, kcl[j]));
-      st4(&sm.vv[b][off], sw_rows(fwd && j, vkeep[j]));
+      st4(&sm.vv[b][off], sw_rows(fwd && j, fwd ? vkeep[j] : rv[j]));
     }
+    if (!fwd) fetch_v(beg + (m + 1) * CH);
     block_sync();
   }
   // step 2nc-3: R *= e^{G_C - a} after the last chunk turns R back into S
