@@ -37,6 +37,12 @@ SMALL = [
     # transitions in the middle of the scan
     ("forty_segments_slow", 1280, 2, [0, 1280], 40, None, 0.01),
     ("varlen_25_segments_slow", 1000, 2, [0, 333, 334, 700, 1000], 25, None, 0.01),
+    # degenerate sizes: one token; two one-token segments; sequences that end
+    # exactly on 32-token chunk boundaries; more heads than any workload
+    ("single_token", 1, 1, [0, 1], 1, None, 1.0),
+    ("two_one_token_segments", 2, 1, [0, 2], 2, None, 1.0),
+    ("chunk_aligned_sequences", 128, 2, [0, 32, 96, 128], 4, None, 0.5),
+    ("sixty_four_heads", 70, 64, [0, 30, 70], 3, None, 0.5),
 ]
 
 
