@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <initializer_list>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -29,16 +30,60 @@ int check_heads(int32_t H, int32_t head_begin, int32_t head_count) {
   return KDA_OK;
 }
 
-// An optional tensor: null, or 16-byte aligned.
-int check_optional(const void* p) { return p == nullptr || aligned16(p) ? KDA_OK : KDA_ERR_MISALIGNED; }
+// A device buffer of the call: its address, the bytes the caller has there
+// and the bytes the call needs.  `optional` buffers may be null (then the
+// size is not checked).
+struct Buf {
+  const void* ptr;
+  size_t have;
+  size_t need;
+  bool optional;
+};
 
-int check_tensors(std::initializer_list<const void*> ptrs) {
-  for (const void* p : ptrs) {
-    if (p == nullptr) return KDA_ERR_INVALID_ARG;
+// Null pointers first, then alignment, then sizes, so that each error is
+// reported the same way whichever buffer has it.
+int check_buffers(std::initializer_list<Buf> bufs) {
+  for (const Buf& b : bufs) {
+    if (b.ptr == nullptr && !b.optional) return KDA_ERR_INVALID_ARG;
   }
-  for (const void* p : ptrs) {
-    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  for (const Buf& b : bufs) {
+    if (b.ptr != nullptr && !aligned16(b.ptr)) return KDA_ERR_MISALIGNED;
   }
+  for (const Buf& b : bufs) {
+    if (b.ptr != nullptr && b.have < b.need) return KDA_ERR_BUFFER_TOO_SMALL;
+  }
+  return KDA_OK;
+}
+
+// Byte sizes of the tensors of a plan, for H heads of K = V = 128.
+struct Sizes {
+  size_t plan_dev, qkg, v, beta, state_n, trans, state_s, o32, o16;
+};
+Sizes sizes_of(const kda_plan* plan, int32_t H) {
+  const size_t T = static_cast<size_t>(plan->T), N = static_cast<size_t>(plan->N),
+               S = static_cast<size_t>(plan->S), h = static_cast<size_t>(H), K = 128, V = 128;
+  Sizes z;
+  z.plan_dev = plan->blob.size() * sizeof(int32_t);
+  z.qkg = T * h * K * 2;
+  z.v = T * h * V * 2;
+  z.beta = T * h * 2;
+  z.state_n = N * h * K * V * 4;
+  z.trans = S * h * K * K * 4;
+  z.state_s = S * h * K * V * 4;
+  z.o32 = T * h * V * 4;
+  z.o16 = T * h * V * 2;
+  return z;
+}
+
+size_t workspace_need(const kda_plan* plan, int32_t H) {
+  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
+  return slots * static_cast<size_t>(H) * kda::kChunkCacheBytes;
+}
+
+int check_workspace(const void* ws, size_t have, const kda_plan* plan, int32_t H) {
+  if (ws == nullptr) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return KDA_ERR_MISALIGNED;
+  if (have < workspace_need(plan, H)) return KDA_ERR_WORKSPACE_TOO_SMALL;
   return KDA_OK;
 }
 
@@ -62,31 +107,82 @@ int finish_launch() {
   return KDA_OK;
 }
 
-}  // namespace
+// ---------------------------------------------------------------- checks
 
-extern "C" int kda_last_hip_error(void) { return g_last_hip_error; }
-
-extern "C" size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H) {
-  if (plan == nullptr || H <= 0) return 0;
-  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
-  return slots * static_cast<size_t>(H) * kda::kChunkCacheBytes;
-}
-
-extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                                     const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                                     const uint16_t* beta, const float* initial_state,
-                                     int32_t H, int32_t K, int32_t V,
-                                     int32_t head_begin, int32_t head_count,
-                                     float* transitions, float* updates, void* chunk_cache,
-                                     hipStream_t stream) {
+int check_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                    const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
+                    const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
+                    const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                    int32_t V, int32_t head_begin, int32_t head_count, const float* transitions,
+                    size_t transitions_bytes, const float* updates, size_t updates_bytes,
+                    const void* workspace, size_t workspace_bytes) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
   st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
-  st = check_tensors({k, v, g, beta, transitions, updates, chunk_cache});
+  const Sizes z = sizes_of(plan, H);
+  st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
+                      {k, k_bytes, z.qkg, false},
+                      {v, v_bytes, z.v, false},
+                      {g, g_bytes, z.qkg, false},
+                      {beta, beta_bytes, z.beta, false},
+                      {initial_state, initial_state_bytes, z.state_n, true},
+                      {transitions, transitions_bytes, z.trans, false},
+                      {updates, updates_bytes, z.state_s, false}});
   if (st != KDA_OK) return st;
-  st = check_optional(initial_state);
+  return check_workspace(workspace, workspace_bytes, plan, H);
+}
+
+int check_compose(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                  const float* transitions, size_t transitions_bytes, const float* updates,
+                  size_t updates_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                  int32_t head_count, const float* carry_in, size_t carry_in_bytes) {
+  int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
+  if (st != KDA_OK) return st;
+  const Sizes z = sizes_of(plan, H);
+  return check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
+                        {transitions, transitions_bytes, z.trans, false},
+                        {updates, updates_bytes, z.state_s, false},
+                        {carry_in, carry_in_bytes, z.state_s, false}});
+}
+
+int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
+                size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
+                const void* workspace, size_t workspace_bytes) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
+  if (st != KDA_OK) return st;
+  if (o_format != KDA_O_FP32 && o_format != KDA_O_BF16) return KDA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(plan, H);
+  st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
+                      {q, q_bytes, z.qkg, false},
+                      {k, k_bytes, z.qkg, false},
+                      {v, v_bytes, z.v, false},
+                      {g, g_bytes, z.qkg, false},
+                      {beta, beta_bytes, z.beta, false},
+                      {initial_state, initial_state_bytes, z.state_n, true},
+                      {carry_in, carry_in_bytes, z.state_s, false},
+                      {o, o_bytes, o_format == KDA_O_BF16 ? z.o16 : z.o32, false},
+                      {final_state, final_state_bytes, z.state_n, false}});
+  if (st != KDA_OK) return st;
+  return check_workspace(workspace, workspace_bytes, plan, H);
+}
+
+// --------------------------------------------------------------- launches
+// Each takes arguments that have passed the checks above.
+
+int launch_summaries(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* k,
+                     const uint16_t* v, const uint16_t* g, const uint16_t* beta,
+                     const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
+                     float* transitions, float* updates, void* workspace, hipStream_t stream) {
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -104,25 +200,18 @@ extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_d
   p.updates = updates;
   p.carry = nullptr;
   p.init_state = initial_state;
-  p.chunk_cache = static_cast<uint16_t*>(chunk_cache);
-  (void)hipGetLastError();
+  p.chunk_cache = static_cast<uint16_t*>(workspace);
   dim3 grid;
-  st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
+  const int st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
   if (st != KDA_OK) return st;
+  (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_chunk_kernel, grid, dim3(kda::kSummaryThreads), 0, stream, p);
   return finish_launch();
 }
 
-extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                                     const float* transitions, const float* updates, int32_t H,
-                                     int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
-                                     float* carry_in, hipStream_t stream) {
-  int st = check_dims(plan, plan_dev, H, K, V);
-  if (st != KDA_OK) return st;
-  st = check_heads(H, head_begin, head_count);
-  if (st != KDA_OK) return st;
-  st = check_tensors({transitions, updates, carry_in});
-  if (st != KDA_OK) return st;
+int launch_compose(const kda_plan* plan, const int32_t* plan_dev, const float* transitions,
+                   const float* updates, int32_t H, int32_t head_begin, int32_t head_count,
+                   float* carry_in, hipStream_t stream) {
   kda::ComposeParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -140,22 +229,11 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
   return finish_launch();
 }
 
-extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q,
-                               const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                               const uint16_t* beta, const float* initial_state,
-                               int32_t H, int32_t K, int32_t V,
-                               int32_t head_begin, int32_t head_count,
-                               const float* carry_in, void* o, int32_t o_format, float* final_state,
-                               const void* chunk_cache, hipStream_t stream) {
-  int st = check_dims(plan, plan_dev, H, K, V);
-  if (st != KDA_OK) return st;
-  st = check_heads(H, head_begin, head_count);
-  if (st != KDA_OK) return st;
-  st = check_tensors({q, k, v, g, beta, carry_in, o, final_state, chunk_cache});
-  if (st != KDA_OK) return st;
-  st = check_optional(initial_state);
-  if (st != KDA_OK) return st;
-  if (o_format != KDA_O_FP32 && o_format != KDA_O_BF16) return KDA_ERR_INVALID_ARG;
+int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, const uint16_t* g, const uint16_t* beta,
+                 const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
+                 const float* carry_in, void* o, int32_t o_format, float* final_state,
+                 const void* workspace, hipStream_t stream) {
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -174,11 +252,101 @@ extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, co
   p.updates = nullptr;
   p.carry = carry_in;
   p.init_state = initial_state;
-  p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(chunk_cache));
-  (void)hipGetLastError();
+  p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(workspace));
   dim3 grid;
-  st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
+  const int st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
   if (st != KDA_OK) return st;
+  (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_carry_kernel, grid, dim3(kda::kCarryThreads), 0, stream, p);
   return finish_launch();
+}
+
+}  // namespace
+
+extern "C" int kda_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V) {
+  if (plan == nullptr || H <= 0 || K != 128 || V != 128) return 0;
+  return workspace_need(plan, H);
+}
+
+extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                                     const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
+                                     const uint16_t* g, size_t g_bytes, const uint16_t* beta,
+                                     size_t beta_bytes, const float* initial_state,
+                                     size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
+                                     int32_t head_begin, int32_t head_count, float* transitions,
+                                     size_t transitions_bytes, float* updates, size_t updates_bytes,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_summaries(plan, plan_dev, plan_dev_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                                 beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin,
+                                 head_count, transitions, transitions_bytes, updates, updates_bytes,
+                                 workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  return launch_summaries(plan, plan_dev, k, v, g, beta, initial_state, H, head_begin, head_count,
+                          transitions, updates, workspace, stream);
+}
+
+extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                                     const float* transitions, size_t transitions_bytes,
+                                     const float* updates, size_t updates_bytes, int32_t H, int32_t K,
+                                     int32_t V, int32_t head_begin, int32_t head_count, float* carry_in,
+                                     size_t carry_in_bytes, hipStream_t stream) {
+  const int st = check_compose(plan, plan_dev, plan_dev_bytes, transitions, transitions_bytes, updates,
+                               updates_bytes, H, K, V, head_begin, head_count, carry_in, carry_in_bytes);
+  if (st != KDA_OK) return st;
+  return launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry_in, stream);
+}
+
+extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                               const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                               const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                               const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                               size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
+                               int32_t head_begin, int32_t head_count, const float* carry_in,
+                               size_t carry_in_bytes, void* o, size_t o_bytes, int32_t o_format,
+                               float* final_state, size_t final_state_bytes, const void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_carry(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
+                             beta, beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin,
+                             head_count, carry_in, carry_in_bytes, o, o_bytes, o_format, final_state,
+                             final_state_bytes, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  return launch_carry(plan, plan_dev, q, k, v, g, beta, initial_state, H, head_begin, head_count, carry_in,
+                      o, o_format, final_state, workspace, stream);
+}
+
+extern "C" int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                           const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                           const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                           const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                           size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
+                           int32_t head_begin, int32_t head_count, float* transitions,
+                           size_t transitions_bytes, float* updates, size_t updates_bytes,
+                           float* carry_in, size_t carry_in_bytes, void* o, size_t o_bytes,
+                           int32_t o_format, float* final_state, size_t final_state_bytes,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_summaries(plan, plan_dev, plan_dev_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                           beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
+                           transitions, transitions_bytes, updates, updates_bytes, workspace,
+                           workspace_bytes);
+  if (st != KDA_OK) return st;
+  st = check_compose(plan, plan_dev, plan_dev_bytes, transitions, transitions_bytes, updates, updates_bytes,
+                     H, K, V, head_begin, head_count, carry_in, carry_in_bytes);
+  if (st != KDA_OK) return st;
+  st = check_carry(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                   beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count, carry_in,
+                   carry_in_bytes, o, o_bytes, o_format, final_state, final_state_bytes, workspace,
+                   workspace_bytes);
+  if (st != KDA_OK) return st;
+  dim3 unused;
+  st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &unused);
+  if (st != KDA_OK) return st;
+  st = launch_summaries(plan, plan_dev, k, v, g, beta, initial_state, H, head_begin, head_count, transitions,
+                        updates, workspace, stream);
+  if (st != KDA_OK) return st;
+  st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry_in, stream);
+  if (st != KDA_OK) return st;
+  return launch_carry(plan, plan_dev, q, k, v, g, beta, initial_state, H, head_begin, head_count, carry_in, o,
+                      o_format, final_state, workspace, stream);
 }

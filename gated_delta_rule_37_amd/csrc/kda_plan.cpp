@@ -157,6 +157,8 @@ extern "C" const char* kda_status_string(int status) {
     case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
     case KDA_ERR_NO_MEMORY: return "KDA_ERR_NO_MEMORY";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_BUFFER_TOO_SMALL: return "KDA_ERR_BUFFER_TOO_SMALL";
     default: return "KDA_ERR_UNKNOWN";
   }
 }

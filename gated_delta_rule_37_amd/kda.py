@@ -11,8 +11,12 @@ Entry points mirror the C names:
 * :func:`segment_summaries` (``kda_segment_summaries``)
 * :func:`compose_summaries` (``kda_compose_summaries``)
 * :func:`apply_carry` (``kda_apply_carry``)
+* :func:`forward_call` (``kda_forward``): the three device calls in one C call
 * :func:`forward` runs the three device calls in order (optionally per head
   group, with the compose launches on a second stream) on fresh output buffers.
+
+Every device tensor is passed as its address and its size in bytes, so the
+library can refuse an undersized buffer before it launches anything.
 """
 from __future__ import annotations
 
@@ -34,13 +38,15 @@ STATUS = {
     -5: "KDA_ERR_MISALIGNED",
     -6: "KDA_ERR_HIP",
     -7: "KDA_ERR_NO_MEMORY",
+    -8: "KDA_ERR_WORKSPACE_TOO_SMALL",
+    -9: "KDA_ERR_BUFFER_TOO_SMALL",
 }
 
 # Every symbol include/kda.h declares.
 SYMBOLS = (
     "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
-    "kda_summary_bytes", "kda_chunk_cache_bytes", "kda_segment_summaries", "kda_compose_summaries",
-    "kda_apply_carry", "kda_status_string", "kda_last_hip_error",
+    "kda_summary_bytes", "kda_workspace_bytes", "kda_segment_summaries", "kda_compose_summaries",
+    "kda_apply_carry", "kda_forward", "kda_status_string", "kda_last_hip_error",
 )
 
 
@@ -81,14 +87,18 @@ def lib() -> ctypes.CDLL:
     L.kda_plan_destroy.restype = None
     L.kda_summary_bytes.argtypes = [p, i32, i32, i32]
     L.kda_summary_bytes.restype = sz
-    L.kda_chunk_cache_bytes.argtypes = [p, i32]
-    L.kda_chunk_cache_bytes.restype = sz
-    L.kda_segment_summaries.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p]
+    L.kda_workspace_bytes.argtypes = [p, i32, i32, i32]
+    L.kda_workspace_bytes.restype = sz
+    buf = [p, sz]            # a device pointer and its size in bytes
+    dims = [i32] * 5         # H, K, V, head_begin, head_count
+    L.kda_segment_summaries.argtypes = [p, *buf, *buf * 4, *buf, *dims, *buf, *buf, *buf, p]
     L.kda_segment_summaries.restype = ctypes.c_int
-    L.kda_compose_summaries.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p]
+    L.kda_compose_summaries.argtypes = [p, *buf, *buf, *buf, *dims, *buf, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
+    L.kda_apply_carry.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, i32, *buf, *buf, p]
     L.kda_apply_carry.restype = ctypes.c_int
+    L.kda_forward.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, *buf, p]
+    L.kda_forward.restype = ctypes.c_int
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_last_hip_error.argtypes = []
@@ -143,8 +153,8 @@ class Plan:
     def summary_bytes(self, H: int, K: int = 128, V: int = 128) -> int:
         return int(lib().kda_summary_bytes(self._h, H, K, V))
 
-    def chunk_cache_bytes(self, H: int) -> int:
-        return int(lib().kda_chunk_cache_bytes(self._h, H))
+    def workspace_bytes(self, H: int, K: int = 128, V: int = 128) -> int:
+        return int(lib().kda_workspace_bytes(self._h, H, K, V))
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -158,16 +168,20 @@ class Plan:
             pass
 
 
-def _ptr(t: torch.Tensor, dtype, shape, name: str) -> int:
+def _buf(t: torch.Tensor, dtype, shape, name: str):
+    """(address, size in bytes) of a device tensor, after checking its dtype,
+    shape and layout; None stands for an absent optional tensor."""
+    if t is None:
+        return (None, 0)
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be a device tensor")
-    return t.data_ptr()
+    return (t.data_ptr(), t.numel() * t.element_size())
 
 
 def _stream(t: torch.Tensor, stream):
@@ -176,17 +190,24 @@ def _stream(t: torch.Tensor, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _inputs(plan: Plan, q, k, v, g, beta):
-    """Shapes and device addresses of (q,) k, v, g, beta; q may be None."""
+def _inputs(plan: Plan, q, k, v, g, beta, initial_state):
+    """H, K, V and the flat (pointer, bytes) list of (q,) k, v, g, beta and the
+    initial states; q and initial_state may be None."""
     T, H, K = k.shape
     V = v.shape[2]
     if T != plan.T:
         raise ValueError(f"inputs hold {T} tokens, the plan {plan.T}")
-    ptrs = [] if q is None else [_ptr(q, torch.bfloat16, (T, H, K), "q")]
-    return H, K, V, ptrs + [
-        _ptr(k, torch.bfloat16, (T, H, K), "k"), _ptr(v, torch.bfloat16, (T, H, V), "v"),
-        _ptr(g, torch.bfloat16, (T, H, K), "g"), _ptr(beta, torch.bfloat16, (T, H), "beta"),
+    bufs = [] if q is None else [_buf(q, torch.bfloat16, (T, H, K), "q")]
+    bufs += [
+        _buf(k, torch.bfloat16, (T, H, K), "k"), _buf(v, torch.bfloat16, (T, H, V), "v"),
+        _buf(g, torch.bfloat16, (T, H, K), "g"), _buf(beta, torch.bfloat16, (T, H), "beta"),
+        _buf(initial_state, torch.float32, (plan.N, H, K, V), "initial_state"),
     ]
+    return H, K, V, _flat(bufs)
+
+
+def _flat(bufs):
+    return [x for b in bufs for x in b]
 
 
 def _heads(H: int, heads):
@@ -194,33 +215,27 @@ def _heads(H: int, heads):
     return (0, H) if heads is None else (int(heads[0]), int(heads[1]))
 
 
-def _cache_ptr(plan: Plan, H: int, chunk_cache) -> int:
-    n = plan.chunk_cache_bytes(H)
-    return _ptr(chunk_cache, torch.uint8, (n,), "chunk_cache")
+def _workspace(plan: Plan, H: int, workspace):
+    return _buf(workspace, torch.uint8, (plan.workspace_bytes(H),), "workspace")
 
 
-def _init_ptr(plan: Plan, H: int, K: int, V: int, initial_state):
-    """Address of the per-sequence initial states [N, H, K, V], or None (zero)."""
-    if initial_state is None:
-        return None
-    return _ptr(initial_state, torch.float32, (plan.N, H, K, V), "initial_state")
+def _plan_dev(plan: Plan, plan_dev):
+    return _buf(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
 
 
 def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transitions, updates,
-                      chunk_cache, stream=None, heads=None, initial_state=None):
+                      workspace, stream=None, heads=None, initial_state=None):
     """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment,
     for the heads ``heads = (begin, count)`` (default: all).  Sequences start
     from ``initial_state`` [N, H, K, V] when given, else from zero."""
-    H, K, V, ins = _inputs(plan, None, k, v, g, beta)
-    ins.append(_init_ptr(plan, H, K, V, initial_state))
-    outs = [
-        _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
-        _ptr(updates, torch.float32, (plan.S, H, K, V), "updates"),
-        _cache_ptr(plan, H, chunk_cache),
-    ]
-    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_segment_summaries(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), *outs,
-                                     _stream(k, stream))
+    H, K, V, ins = _inputs(plan, None, k, v, g, beta, initial_state)
+    outs = _flat([
+        _buf(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
+        _buf(updates, torch.float32, (plan.S, H, K, V), "updates"),
+        _workspace(plan, H, workspace),
+    ])
+    st = lib().kda_segment_summaries(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V,
+                                     *_heads(H, heads), *outs, _stream(k, stream))
     _check(st, "kda_segment_summaries")
 
 
@@ -229,31 +244,52 @@ def compose_summaries(plan: Plan, plan_dev: torch.Tensor, transitions, updates, 
     """``kda_compose_summaries``: ordered FP32 scan of the summaries."""
     S, H, K, _ = transitions.shape
     V = updates.shape[3]
-    a = _ptr(transitions, torch.float32, (plan.S, H, K, K), "transitions")
-    b = _ptr(updates, torch.float32, (plan.S, H, K, V), "updates")
-    c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
-    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_compose_summaries(plan.handle, pd, a, b, H, K, V, *_heads(H, heads), c,
-                                     _stream(transitions, stream))
+    bufs = _flat([
+        _buf(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
+        _buf(updates, torch.float32, (plan.S, H, K, V), "updates"),
+    ])
+    c = _buf(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
+    st = lib().kda_compose_summaries(plan.handle, *_plan_dev(plan, plan_dev), *bufs, H, K, V,
+                                     *_heads(H, heads), *c, _stream(transitions, stream))
     _check(st, "kda_compose_summaries")
 
 
-def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
-                chunk_cache, stream=None, heads=None, initial_state=None):
-    """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r
-    (a fragment that starts a sequence from ``initial_state``, else zero)."""
-    H, K, V, ins = _inputs(plan, q, k, v, g, beta)
-    ins.append(_init_ptr(plan, H, K, V, initial_state))
-    c = _ptr(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
+def _o_buf(plan: Plan, o, H, V):
     if o.dtype not in O_FORMATS:
         raise TypeError(f"o: expected one of {list(O_FORMATS)}, got {o.dtype}")
-    oo = _ptr(o, o.dtype, (plan.T, H, V), "o")
-    ff = _ptr(final_state, torch.float32, (plan.N, H, K, V), "final_state")
-    cc = _cache_ptr(plan, H, chunk_cache)
-    pd = _ptr(plan_dev, torch.int32, (len(plan.blob),), "plan_dev")
-    st = lib().kda_apply_carry(plan.handle, pd, *ins, H, K, V, *_heads(H, heads), c, oo,
-                               O_FORMATS[o.dtype], ff, cc, _stream(q, stream))
+    return _buf(o, o.dtype, (plan.T, H, V), "o"), O_FORMATS[o.dtype]
+
+
+def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
+                workspace, stream=None, heads=None, initial_state=None):
+    """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r
+    (a fragment that starts a sequence from ``initial_state``, else zero)."""
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    c = _buf(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
+    ob, fmt = _o_buf(plan, o, H, V)
+    ff = _buf(final_state, torch.float32, (plan.N, H, K, V), "final_state")
+    ws = _workspace(plan, H, workspace)
+    st = lib().kda_apply_carry(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V, *_heads(H, heads),
+                               *c, *ob, fmt, *ff, *ws, _stream(q, stream))
     _check(st, "kda_apply_carry")
+
+
+def forward_call(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stream=None, heads=None,
+                 initial_state=None):
+    """``kda_forward``: summaries, compose and carry in one C call, into the
+    buffers of ``out`` (as :func:`alloc_outputs` makes them)."""
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    summ = _flat([
+        _buf(out["transitions"], torch.float32, (plan.S, H, K, K), "transitions"),
+        _buf(out["updates"], torch.float32, (plan.S, H, K, V), "updates"),
+        _buf(out["carry_in"], torch.float32, (plan.S, H, K, V), "carry_in"),
+    ])
+    ob, fmt = _o_buf(plan, out["o"], H, V)
+    ff = _buf(out["final_state"], torch.float32, (plan.N, H, K, V), "final_state")
+    ws = _workspace(plan, H, out["workspace"])
+    st = lib().kda_forward(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V, *_heads(H, heads),
+                           *summ, *ob, fmt, *ff, *ws, _stream(q, stream))
+    _check(st, "kda_forward")
 
 
 # storage formats of o accepted by kda_apply_carry (kda_o_format)
@@ -262,7 +298,7 @@ O_FORMATS = {torch.float32: 0, torch.bfloat16: 1}
 
 def alloc_outputs(plan: Plan, H: int, K: int, V: int, device, o_dtype=torch.float32):
     """Fresh output buffers (o, final_state, transitions, updates, carry_in) and
-    the chunk cache shared by the summaries and carry passes.  ``o_dtype`` is
+    the workspace shared by the summaries and carry passes.  ``o_dtype`` is
     float32, or bfloat16 for the rounded BF16 output."""
     f32 = dict(dtype=torch.float32, device=device)
     return dict(
@@ -271,7 +307,7 @@ def alloc_outputs(plan: Plan, H: int, K: int, V: int, device, o_dtype=torch.floa
         transitions=torch.empty(plan.S, H, K, K, **f32),
         updates=torch.empty(plan.S, H, K, V, **f32),
         carry_in=torch.empty(plan.S, H, K, V, **f32),
-        chunk_cache=torch.empty(plan.chunk_cache_bytes(H), dtype=torch.uint8, device=device),
+        workspace=torch.empty(plan.workspace_bytes(H, K, V), dtype=torch.uint8, device=device),
     )
 
 
@@ -337,20 +373,20 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
 
     if len(runs) == 1:
         timed("summaries", main, lambda: segment_summaries(
-            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main,
+            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["workspace"], main,
             initial_state=initial_state))
         timed("compose", main, lambda: compose_summaries(
             plan, pd, out["transitions"], out["updates"], out["carry_in"], main))
         timed("carry", main, lambda: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["chunk_cache"], main, initial_state=initial_state))
+            out["workspace"], main, initial_state=initial_state))
         return out
 
     side = _side_stream(q.device)
     done_s, done_c = [], []
     for hr in runs:
         timed("summaries", main, lambda hr=hr: segment_summaries(
-            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["chunk_cache"], main,
+            plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["workspace"], main,
             heads=hr, initial_state=initial_state))
         ev = torch.cuda.Event()
         ev.record(main)
@@ -366,7 +402,7 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
         main.wait_event(evc)
         timed("carry", main, lambda hr=hr: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["chunk_cache"], main, heads=hr, initial_state=initial_state))
+            out["workspace"], main, heads=hr, initial_state=initial_state))
     # every launch on the side stream precedes the last carry launch on main,
     # so work issued later on main is ordered after all of it
     return out

@@ -28,8 +28,8 @@
  *     kda_segment_summaries    (device)
  *     kda_compose_summaries    (device)
  *     kda_apply_carry          (device)
- * After the three device calls, o and final_state hold the monolithic
- * recurrence's results.
+ * (or kda_forward, which enqueues the three device calls at once).  After
+ * them, o and final_state hold the monolithic recurrence's results.
  *
  * Conventions shared by every entry point:
  *   - Return value: KDA_OK (0) or a negative kda_status.  Every check runs on
@@ -49,7 +49,7 @@
  *       final_state : [N, H, K, V] fp32
  *       initial_state : [N, H, K, V] fp32, or NULL (every sequence starts at 0)
  *       transitions : [S, H, K, K] fp32 updates / carry_in : [S, H, K, V] fp32
- *       chunk_cache : kda_chunk_cache_bytes(plan, H) bytes of device memory
+ *       workspace : kda_workspace_bytes(plan, H, K, V) bytes of device memory
  *   - Initial states: sequence n starts from initial_state[n] (the reading
  *     that a sequence start resets the state to the sequence's own initial
  *     state, zero when none is given).  Pass the same initial_state, or NULL
@@ -88,16 +88,19 @@ typedef enum kda_status {
   KDA_ERR_INVALID_ARG = -1,    /* null pointer, non-positive size, plan_dev missing */
   KDA_ERR_BAD_CU_SEQLENS = -2, /* cu_seqlens not 0 = c_0 < c_1 < ... (empty sequence) */
   KDA_ERR_BAD_SEGMENTS = -3,   /* num_segments outside [1, T] or bad custom bounds */
-  KDA_ERR_UNSUPPORTED = -4,    /* K or V other than 128, H out of range, T too large */
+  KDA_ERR_UNSUPPORTED = -4,    /* K or V other than 128, H > 65535, T > 2^30 */
   KDA_ERR_MISALIGNED = -5,     /* a tensor pointer is not 16-byte aligned */
   KDA_ERR_HIP = -6,            /* a HIP launch failed; see kda_last_hip_error() */
-  KDA_ERR_NO_MEMORY = -7       /* host allocation for the plan failed */
+  KDA_ERR_NO_MEMORY = -7,      /* host allocation for the plan failed */
+  KDA_ERR_WORKSPACE_TOO_SMALL = -8, /* workspace_bytes < kda_workspace_bytes(plan, H, K, V) */
+  KDA_ERR_BUFFER_TOO_SMALL = -9     /* another device buffer is smaller than its shape */
 } kda_status;
 
-/* Storage format of o (kda_apply_carry).  The recurrence runs in FP32 either
- * way; KDA_O_BF16 stores each element rounded to the nearest bfloat16 (ties
- * to even), which halves the output bytes.  The pages fix BF16 inputs and an
- * FP32 state ([#110] Supported configuration) but not o's storage. */
+/* Storage format of o (kda_apply_carry, kda_forward).  The recurrence runs in
+ * FP32 either way; KDA_O_BF16 stores each element rounded to the nearest
+ * bfloat16 (ties to even), which halves the output bytes.  The pages fix BF16
+ * inputs and an FP32 state ([#110] Supported configuration) but not o's
+ * storage. */
 typedef enum kda_o_format {
   KDA_O_FP32 = 0,
   KDA_O_BF16 = 1
@@ -119,7 +122,7 @@ typedef struct kda_plan kda_plan;
  *   out           receives the plan (owned by the caller; free with
  *                 kda_plan_destroy).  Untouched on error.
  * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_BAD_CU_SEQLENS, KDA_ERR_BAD_SEGMENTS,
- * KDA_ERR_UNSUPPORTED (T >= 2^31 / 256), KDA_ERR_NO_MEMORY.
+ * KDA_ERR_UNSUPPORTED (T > 2^30 tokens), KDA_ERR_NO_MEMORY.
  */
 int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_segments,
                       const int32_t* custom_bounds, kda_plan** out);
@@ -127,7 +130,7 @@ int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_s
 /*
  * kda_plan_blob -- the plan's canonical int32 serialisation.  The device
  * entry points read a device copy of exactly these n_int32 words
- * (`plan_dev`).  Layout:
+ * (`plan_dev`, n_int32 * 4 bytes).  Layout:
  *   header [T, N, S, F]
  *   seg_bounds[S+1] seg_first_seq[S] seg_last_seq[S] seg_carry_in[S]
  *   seg_transition_live[S] seg_frag_ptr[S+1]
@@ -158,17 +161,46 @@ void kda_plan_destroy(kda_plan* plan);
 size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 
 /*
- * kda_chunk_cache_bytes -- bytes of the chunk cache that kda_segment_summaries
- * fills and kda_apply_carry reads: the per-chunk factor T diag(beta) of the
- * UT form of the recurrence (T = (I + A)^{-1}, A_ij = beta_i k_i^T
- * Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token chunk) of every
- * fragment that ends its segment, so that the carry pass does not rebuild
- * it.  This is an implementation cache, not part of the method: its contents
- * are opaque, and what kda_segment_summaries writes for a head is valid for
+ * kda_workspace_bytes -- bytes of the caller-owned device workspace that
+ * kda_segment_summaries fills and kda_apply_carry reads (#136 Summary by
+ * CodeRabbit: a reusable workspace; #136 Latest cuDNN compatibility:
+ * workspace requirements are validated up front).
+ * It holds, for every fragment that ends its segment, the per-chunk factor
+ * T diag(beta) of the UT form of the recurrence (T = (I + A)^{-1},
+ * A_ij = beta_i k_i^T Diag(exp(G_i - G_j)) k_j for j < i inside a 32-token
+ * chunk), so that the carry pass does not rebuild it.  Its contents are
+ * opaque: what kda_segment_summaries writes for a head is valid for
  * kda_apply_carry on the same plan, H, head and inputs.
- * Size: (ceil(T / 32) + S) * H * 4096.  Returns 0 for a NULL plan or H <= 0.
+ * Size: (ceil(T / 32) + S) * H * 4096 bytes.  Returns 0 for a NULL plan,
+ * H <= 0, or K, V other than 128.
  */
-size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
+size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
+
+/*
+ * Device calls: arguments shared by kda_segment_summaries,
+ * kda_compose_summaries, kda_apply_carry and kda_forward.
+ *   plan, plan_dev  the host plan and the caller's device copy of its blob.
+ *   H, K, V         heads held by every tensor; K = V = 128.
+ *   head_begin, head_count  the heads this call works on (see above).
+ *   X, X_bytes      every device buffer X comes with the number of bytes
+ *                   the caller allocated at X.  The call needs, for the
+ *                   plan's T, N, S and the H heads of the layout:
+ *                     plan_dev        n_int32 * 4
+ *                     q, k, g         T * H * K * 2      v   T * H * V * 2
+ *                     beta            T * H * 2
+ *                     initial_state   N * H * K * V * 4  (when not NULL)
+ *                     transitions     S * H * K * K * 4
+ *                     updates, carry_in  S * H * K * V * 4
+ *                     o               T * H * V * 4 (FP32) or * 2 (BF16)
+ *                     final_state     N * H * K * V * 4
+ *                     workspace       kda_workspace_bytes(plan, H, K, V)
+ *                   A smaller workspace gives KDA_ERR_WORKSPACE_TOO_SMALL,
+ *                   any other smaller buffer KDA_ERR_BUFFER_TOO_SMALL; in
+ *                   both cases nothing is enqueued.
+ *   stream          the HIP stream every launch of the call is enqueued on.
+ * Check order: plan and dimensions, head range, null pointers, alignment,
+ * sizes.
+ */
 
 /*
  * kda_segment_summaries -- the affine summary of every segment.
@@ -183,20 +215,18 @@ size_t kda_chunk_cache_bytes(const kda_plan* plan, int32_t H);
  *                     latest on the left, when segment r carries in and no
  *                     sequence starts inside it; otherwise exactly 0 (the
  *                     reset's linear part);
- *   chunk_cache     the chunk factors of every fragment that ends its
- *                   segment (kda_chunk_cache_bytes).
+ *   workspace       the chunk factors of every fragment that ends its
+ *                   segment (kda_workspace_bytes).
  * It reads no q and writes no o or final state: kda_apply_carry does.
- *   plan_dev     device copy of kda_plan_blob(plan).
- *   chunk_cache  device buffer of kda_chunk_cache_bytes(plan, H) bytes,
- *                16-byte aligned, owned by the caller.
  */
-int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                          const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                          const uint16_t* beta, const float* initial_state,
-                          int32_t H, int32_t K, int32_t V,
-                          int32_t head_begin, int32_t head_count,
-                          float* transitions, float* updates, void* chunk_cache,
-                          hipStream_t stream);
+int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                          const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
+                          const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
+                          const float* initial_state, size_t initial_state_bytes,
+                          int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                          float* transitions, size_t transitions_bytes,
+                          float* updates, size_t updates_bytes,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_compose_summaries -- ordered FP32 scan C_0 = 0, C_{r+1} = A_r C_r + B_r.
@@ -205,11 +235,11 @@ int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev,
  * carry_in[r] is the state entering segment r (all r in [0, S)).  Where the
  * plan says A_r is structurally zero the product is skipped (C_{r+1} = B_r).
  */
-int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
-                          const float* transitions, const float* updates,
-                          int32_t H, int32_t K, int32_t V,
-                          int32_t head_begin, int32_t head_count, float* carry_in,
-                          hipStream_t stream);
+int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                          const float* transitions, size_t transitions_bytes,
+                          const float* updates, size_t updates_bytes,
+                          int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                          float* carry_in, size_t carry_in_bytes, hipStream_t stream);
 
 /*
  * kda_apply_carry -- the forward with the carry applied: every fragment (a
@@ -223,16 +253,40 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev,
  * consumes only the V-state it needs).
  *   o            [T, H, V] in the format o_format names (kda_o_format; other
  *                values give KDA_ERR_INVALID_ARG): FP32, or BF16 bits.
- *   chunk_cache  the buffer kda_segment_summaries filled for the same plan,
+ *   workspace    the buffer kda_segment_summaries filled for the same plan,
  *                H and inputs (read only).
  */
-int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev,
-                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const uint16_t* g, const uint16_t* beta, const float* initial_state,
-                    int32_t H, int32_t K, int32_t V,
-                    int32_t head_begin, int32_t head_count, const float* carry_in,
-                    void* o, int32_t o_format, float* final_state, const void* chunk_cache,
-                    hipStream_t stream);
+int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                    const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                    const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                    const uint16_t* beta, size_t beta_bytes,
+                    const float* initial_state, size_t initial_state_bytes,
+                    int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                    const float* carry_in, size_t carry_in_bytes,
+                    void* o, size_t o_bytes, int32_t o_format,
+                    float* final_state, size_t final_state_bytes,
+                    const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_forward -- one whole forward pass: kda_segment_summaries,
+ * kda_compose_summaries and kda_apply_carry over the same heads, enqueued in
+ * that order on `stream` (#136 Sequence Diagram: plan, summaries, composition,
+ * then the forward that consumes them).  Every argument means what it means
+ * for those calls; all of them are checked before the first launch, so an
+ * error enqueues nothing.  Results are bitwise those of the three calls.
+ */
+int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                const uint16_t* beta, size_t beta_bytes,
+                const float* initial_state, size_t initial_state_bytes,
+                int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                float* transitions, size_t transitions_bytes,
+                float* updates, size_t updates_bytes,
+                float* carry_in, size_t carry_in_bytes,
+                void* o, size_t o_bytes, int32_t o_format,
+                float* final_state, size_t final_state_bytes,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a kda_status value. */
 const char* kda_status_string(int status);

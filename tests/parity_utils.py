@@ -36,7 +36,7 @@ def run_gpu(x, cu, S, bounds=None, dev="cuda:0", h0=None):
     init = None if h0 is None else h0.to(dev)
     out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=init)
     torch.cuda.synchronize()
-    out.pop("chunk_cache")   # an internal cache between the two passes, not an output
+    out.pop("workspace")   # an internal cache between the two passes, not an output
     return plan, out
 
 

@@ -91,43 +91,78 @@ def test_summary_workspace_64_segments_32_heads_is_256_mib():
     assert plan.summary_bytes(32, 128, 128) == 256 * 1024 * 1024
 
 
-def test_chunk_cache_bytes():
+def test_workspace_bytes():
     # (ceil(T / 32) + S) slots of 4096 bytes per head
-    assert kda.Plan([0, 65536], 64).chunk_cache_bytes(32) == (2048 + 64) * 32 * 4096
-    assert kda.Plan([0, 100], 3).chunk_cache_bytes(2) == (4 + 3) * 2 * 4096
-    assert kda.Plan([0, 1], 1).chunk_cache_bytes(1) == 2 * 4096
+    assert kda.Plan([0, 65536], 64).workspace_bytes(32) == (2048 + 64) * 32 * 4096
+    assert kda.Plan([0, 100], 3).workspace_bytes(2) == (4 + 3) * 2 * 4096
+    assert kda.Plan([0, 1], 1).workspace_bytes(1) == 2 * 4096
     L = kda.lib()
-    assert L.kda_chunk_cache_bytes(None, 4) == 0
-    assert kda.Plan([0, 100], 3).chunk_cache_bytes(0) == 0
+    assert L.kda_workspace_bytes(None, 4, 128, 128) == 0
+    assert kda.Plan([0, 100], 3).workspace_bytes(0) == 0
+    assert kda.Plan([0, 100], 3).workspace_bytes(2, 64, 128) == 0
 
 
 # ------------------------------------------------ device entry points: host checks
+# No call below ever has every argument valid: each one fails a host check,
+# so nothing is launched (the fake addresses are never dereferenced).
 
-_FAKE = 1 << 20   # a 16-byte-aligned non-null address that is never dereferenced
+_FAKE = 1 << 20   # a 16-byte-aligned non-null address
+_BIG = 1 << 40    # a size larger than any buffer a call needs
 
 
-def _call_summaries(plan, plan_dev=_FAKE, H=2, K=128, V=128, k=_FAKE, upd=_FAKE, cache=_FAKE,
-                    h0=0, hn=None, init=None):
+class Call:
+    """One device call with fake buffers of ample size; keyword overrides
+    replace a buffer's address (``<name>``), its size (``<name>_bytes``) or a
+    scalar argument."""
+
+    SUMMARIES = ("plan_dev", "k", "v", "g", "beta", "init", "dims", "transitions", "updates", "workspace")
+    COMPOSE = ("plan_dev", "transitions", "updates", "dims", "carry")
+    CARRY = ("plan_dev", "q", "k", "v", "g", "beta", "init", "dims", "carry", "o", "fmt", "final",
+             "workspace")
+    FORWARD = ("plan_dev", "q", "k", "v", "g", "beta", "init", "dims", "transitions", "updates", "carry",
+               "o", "fmt", "final", "workspace")
+
+    def __init__(self, fn, order):
+        self.fn, self.order = fn, order
+
+    def __call__(self, plan, H=2, K=128, V=128, h0=0, hn=None, fmt=0, **kw):
+        args = [None if plan is None else plan.handle]
+        for name in self.order:
+            if name == "dims":
+                args += [H, K, V, h0, H if hn is None else hn]
+            elif name == "fmt":
+                args.append(fmt)
+            else:
+                default = None if name == "init" else _FAKE
+                args += [kw.get(name, default), kw.get(name + "_bytes", _BIG)]
+        args.append(None)   # stream
+        return self.fn(*args)
+
+
+def _calls():
     L = kda.lib()
-    return L.kda_segment_summaries(plan.handle, plan_dev, k, _FAKE, _FAKE, _FAKE, init,
-                                   H, K, V, h0, H if hn is None else hn, _FAKE, upd, cache, None)
+    return dict(summaries=Call(L.kda_segment_summaries, Call.SUMMARIES),
+                compose=Call(L.kda_compose_summaries, Call.COMPOSE),
+                carry=Call(L.kda_apply_carry, Call.CARRY),
+                forward=Call(L.kda_forward, Call.FORWARD))
+
+
+def _first_output(call):
+    return "carry" if "transitions" not in call.order else "transitions"
 
 
 def test_head_ranges_validate_before_launch():
     plan = kda.Plan([0, 100], 2)
-    L = kda.lib()
     # every call below also has a misaligned pointer (checked after the head
     # range), so a range check that let one through returns -5 and still
     # launches nothing
     bad = _FAKE + 4
-    for h0, hn in ((0, 0), (-1, 2), (1, 2), (0, 3), (2, 1), (0, -1)):
-        assert _call_summaries(plan, k=bad, h0=h0, hn=hn) == -1, (h0, hn)
-        assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 128, 128, h0, hn,
-                                       bad, None) == -1, (h0, hn)
-        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                                 h0, hn, bad, _FAKE, 0, _FAKE, _FAKE, None) == -1, (h0, hn)
-    # a valid range reaches the pointer checks
-    assert _call_summaries(plan, k=bad, h0=1, hn=1) == -5
+    for name, call in _calls().items():
+        out = _first_output(call)
+        for h0, hn in ((0, 0), (-1, 2), (1, 2), (0, 3), (2, 1), (0, -1)):
+            assert call(plan, h0=h0, hn=hn, **{out: bad}) == -1, (name, h0, hn)
+        # a valid range reaches the pointer checks
+        assert call(plan, h0=1, hn=1, **{out: bad}) == -5, name
 
 
 def test_head_groups_cover_every_head_once():
@@ -142,40 +177,81 @@ def test_head_groups_cover_every_head_once():
 
 def test_device_calls_validate_before_launch():
     plan = kda.Plan([0, 100], 2)
-    assert _call_summaries(plan, K=64) == -4
-    assert _call_summaries(plan, V=256) == -4
-    assert _call_summaries(plan, H=0) == -1
-    assert _call_summaries(plan, H=70000) == -4
-    assert _call_summaries(plan, plan_dev=0) == -1
-    assert _call_summaries(plan, k=0) == -1
-    assert _call_summaries(plan, k=_FAKE + 2) == -5
-    assert _call_summaries(plan, upd=_FAKE + 8) == -5
-    assert _call_summaries(plan, plan_dev=_FAKE + 4) == -5
-    assert _call_summaries(plan, cache=0) == -1
-    assert _call_summaries(plan, cache=_FAKE + 8) == -5
+    c = _calls()
+    for name, call in c.items():
+        # each of these fails one check, before any size check
+        assert call(plan, K=64) == -4, name
+        assert call(plan, V=256) == -4, name
+        assert call(plan, H=0) == -1, name
+        assert call(plan, H=70000) == -4, name
+        assert call(plan, plan_dev=0) == -1, name
+        assert call(plan, plan_dev=_FAKE + 4) == -5, name
+        assert call(None) == -1, name
+    for name in ("summaries", "carry", "forward"):
+        assert c[name](plan, k=0) == -1, name
+        assert c[name](plan, k=_FAKE + 2) == -5, name
+        assert c[name](plan, workspace=0) == -1, name
+        assert c[name](plan, workspace=_FAKE + 8) == -5, name
+        # the optional initial states: misaligned is refused (NULL is valid and
+        # means zero)
+        assert c[name](plan, init=_FAKE + 4) == -5, name
+    for name in ("summaries", "compose", "forward"):
+        assert c[name](plan, updates=_FAKE + 8) == -5, name
+        assert c[name](plan, transitions=0) == -1, name
+    for name in ("compose", "carry", "forward"):
+        assert c[name](plan, carry=_FAKE + 4) == -5, name
+        assert c[name](plan, carry=0) == -1, name
+    for name in ("carry", "forward"):
+        assert c[name](plan, o=0) == -1, name
+        assert c[name](plan, final=0) == -1, name
+        # an unknown o format is refused before launch
+        for fmt in (-1, 2, 7):
+            assert c[name](plan, fmt=fmt) == -1, (name, fmt)
+    assert kda.lib().kda_last_hip_error() == 0
+
+
+def _needs(plan, H):
+    """Bytes each buffer of a call needs (K = V = 128), by argument name."""
+    T, N, S = plan.T, plan.N, plan.S
+    return dict(plan_dev=4 * len(plan.blob), q=T * H * 256, k=T * H * 256, v=T * H * 256,
+                g=T * H * 256, beta=T * H * 2, init=N * H * 65536, transitions=S * H * 65536,
+                updates=S * H * 65536, carry=S * H * 65536, o=T * H * 512, final=N * H * 65536,
+                workspace=plan.workspace_bytes(H))
+
+
+@pytest.mark.parametrize("cu,S,H", [([0, 100], 2, 2), ([0, 37, 150, 151, 300], 4, 3), ([0, 1], 1, 1)])
+def test_undersized_buffers_are_refused(cu, S, H):
+    """Every buffer of every call at exactly the bytes its shape needs except
+    one, which is one byte short: the call returns KDA_ERR_WORKSPACE_TOO_SMALL
+    for the workspace and KDA_ERR_BUFFER_TOO_SMALL for any other buffer, and
+    launches nothing.  A given initial state is checked like the others."""
+    plan = kda.Plan(cu, S)
+    need = _needs(plan, H)
+    for name, call in _calls().items():
+        exact = {b + "_bytes": need[b] for b in call.order if b in need}
+        for buf in call.order:
+            if buf not in need:
+                continue
+            args = dict(exact, init=_FAKE)
+            args[buf + "_bytes"] = need[buf] - 1
+            want = -8 if buf == "workspace" else -9
+            assert call(plan, H=H, **args) == want, (name, buf)
+        if "o" in call.order:
+            # BF16 o needs half the FP32 bytes
+            args = dict(exact, o_bytes=need["o"] // 2 - 1)
+            assert call(plan, H=H, fmt=1, **args) == -9, name
+    assert kda.lib().kda_last_hip_error() == 0
+
+
+def test_unsupported_token_count_boundary():
+    """2^30 tokens is the largest plan accepted; one more is KDA_ERR_UNSUPPORTED."""
     L = kda.lib()
-    assert L.kda_segment_summaries(None, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128, 0, 2,
-                                   _FAKE, _FAKE, _FAKE, None) == -1
-    # the optional initial states: misaligned is refused (NULL is valid and
-    # means zero, so it is not tried here with fake buffers)
-    assert _call_summaries(plan, init=_FAKE + 4) == -5
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE + 8, 2, 128,
-                             128, 0, 2, _FAKE, _FAKE, 0, _FAKE, _FAKE, None) == -5
-    assert L.kda_compose_summaries(plan.handle, _FAKE, _FAKE, _FAKE, 2, 96, 128, 0, 2, _FAKE,
-                                   None) == -4
-    assert L.kda_compose_summaries(plan.handle, _FAKE, 0, _FAKE, 2, 128, 128, 0, 2, _FAKE,
-                                   None) == -1
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE + 4, _FAKE, 0, _FAKE, _FAKE, None) == -5
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE, 0, 0, _FAKE, _FAKE, None) == -1
-    assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128, 128,
-                             0, 2, _FAKE, _FAKE, 0, _FAKE, 0, None) == -1
-    # an unknown o format is refused before launch
-    for fmt in (-1, 2, 7):
-        assert L.kda_apply_carry(plan.handle, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, None, 2, 128,
-                                 128, 0, 2, _FAKE, _FAKE, fmt, _FAKE, _FAKE, None) == -1, fmt
-    assert L.kda_last_hip_error() == 0
+    out = ctypes.c_void_p()
+    over = (ctypes.c_int32 * 2)(0, (1 << 30) + 1)
+    assert L.kda_plan_segments(over, 1, 1, None, ctypes.byref(out)) == -4
+    at = (ctypes.c_int32 * 2)(0, 1 << 30)
+    assert L.kda_plan_segments(at, 1, 1, None, ctypes.byref(out)) == 0
+    L.kda_plan_destroy(out)
 
 
 def test_plan_info_and_null_handling():

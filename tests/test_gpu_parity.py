@@ -251,7 +251,7 @@ def test_head_groups_match_single_launch(groups):
     d = pu.to_device(x)
     out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], groups=groups)
     torch.cuda.synchronize()
-    out.pop("chunk_cache")
+    out.pop("workspace")
     for key in ref_out:
         assert torch.equal(out[key], ref_out[key]), key
     pu.compare(pu.gpu_numpy(out), pu.run_oracle(x, cu, plan), f"groups={groups}")
@@ -289,10 +289,10 @@ def test_head_range_touches_only_its_heads():
     pd = plan.device_blob("cuda:0")
     hr = (1, 1)
     kda.segment_summaries(plan, pd, d["k"], d["v"], d["g"], d["beta"], out["transitions"],
-                          out["updates"], out["chunk_cache"], heads=hr)
+                          out["updates"], out["workspace"], heads=hr)
     kda.compose_summaries(plan, pd, out["transitions"], out["updates"], out["carry_in"], heads=hr)
     kda.apply_carry(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out["carry_in"], out["o"],
-                    out["final_state"], out["chunk_cache"], heads=hr)
+                    out["final_state"], out["workspace"], heads=hr)
     torch.cuda.synchronize()
     for key in ("o", "final_state", "transitions", "updates", "carry_in"):
         t = out[key]
@@ -300,3 +300,23 @@ def test_head_range_touches_only_its_heads():
         assert not bool((t[:, 1] == -7.0).any()), key
     got = pu.gpu_numpy(out, heads=[1])
     pu.compare(got, pu.run_oracle(x, cu, plan, heads=[1]), "head 1 only")
+
+
+def test_forward_call_matches_three_calls():
+    """kda_forward (one C call) gives bitwise the results of the three device
+    calls issued one by one, with and without initial states, FP32 and BF16 o."""
+    T, H, cu, S = 300, 3, [0, 37, 150, 151, 300], 4
+    print(f"case kda_forward: T={T} H={H} S={S}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=21, cu_seqlens=cu, gate_scale=0.2)
+    plan = kda.Plan(cu, S)
+    d = pu.to_device(x)
+    pd = plan.device_blob("cuda:0")
+    for h0 in (None, synth.initial_states(len(cu) - 1, H, 128, 128, seed=22).to("cuda:0")):
+        for o_dtype in (torch.float32, torch.bfloat16):
+            ref = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=h0,
+                              o_dtype=o_dtype)
+            out = kda.alloc_outputs(plan, H, 128, 128, "cuda:0", o_dtype)
+            kda.forward_call(plan, pd, d["q"], d["k"], d["v"], d["g"], d["beta"], out, initial_state=h0)
+            torch.cuda.synchronize()
+            for key in ("o", "final_state", "transitions", "updates", "carry_in"):
+                assert torch.equal(out[key], ref[key]), (key, h0 is None, o_dtype)
