@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -261,9 +262,47 @@ int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* 
   return finish_launch();
 }
 
+// ------------------------------------------------- allocation-free variant
+// The workspace of kda_forward_noalloc: a fixed device array, one copy per
+// GPU, kept until the process ends.  Host code never uses its name as an
+// address (on the host it is only a stand-in); each device's address comes
+// from hipGetSymbolAddress with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device), or a KDA status.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return KDA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      g_last_hip_error = static_cast<int>(e);
+      return KDA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" int kda_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" size_t kda_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 extern "C" size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V) {
   if (plan == nullptr || H <= 0 || K != 128 || V != 128) return 0;
@@ -349,4 +388,31 @@ extern "C" int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t
   if (st != KDA_OK) return st;
   return launch_carry(plan, plan_dev, q, k, v, g, beta, initial_state, H, head_begin, head_count, carry_in, o,
                       o_format, final_state, workspace, stream);
+}
+
+extern "C" int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                                   const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                                   const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                                   const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                                   size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
+                                   int32_t head_begin, int32_t head_count, float* transitions,
+                                   size_t transitions_bytes, float* updates, size_t updates_bytes,
+                                   float* carry_in, size_t carry_in_bytes, void* o, size_t o_bytes,
+                                   int32_t o_format, float* final_state, size_t final_state_bytes,
+                                   hipStream_t stream) {
+  // The size check comes first, so that an oversized call is refused without
+  // touching the device; the checks of kda_forward then see a workspace of
+  // exactly the size needed.
+  if (plan != nullptr && H > 0 && workspace_need(plan, H) > kScratchBytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != KDA_OK) return st;
+  // every chunk-cache slot the carry launch reads is written by the summaries
+  // launch of the same call, so the array needs no clearing between calls
+  return kda_forward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                     beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
+                     transitions, transitions_bytes, updates, updates_bytes, carry_in, carry_in_bytes, o,
+                     o_bytes, o_format, final_state, final_state_bytes, ws, kScratchBytes, stream);
 }

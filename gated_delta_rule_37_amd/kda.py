@@ -12,6 +12,8 @@ Entry points mirror the C names:
 * :func:`compose_summaries` (``kda_compose_summaries``)
 * :func:`apply_carry` (``kda_apply_carry``)
 * :func:`forward_call` (``kda_forward``): the three device calls in one C call
+* :func:`forward_noalloc` (``kda_forward_noalloc``): the same without a
+  caller workspace (the library's fixed per-GPU array instead)
 * :func:`forward` runs the three device calls in order (optionally per head
   group, with the compose launches on a second stream) on fresh output buffers.
 
@@ -46,7 +48,8 @@ STATUS = {
 SYMBOLS = (
     "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
     "kda_summary_bytes", "kda_workspace_bytes", "kda_segment_summaries", "kda_compose_summaries",
-    "kda_apply_carry", "kda_forward", "kda_status_string", "kda_last_hip_error",
+    "kda_apply_carry", "kda_forward", "kda_forward_noalloc", "kda_noalloc_max_workspace_bytes",
+    "kda_status_string", "kda_last_hip_error",
 )
 
 
@@ -99,6 +102,10 @@ def lib() -> ctypes.CDLL:
     L.kda_apply_carry.restype = ctypes.c_int
     L.kda_forward.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, *buf, p]
     L.kda_forward.restype = ctypes.c_int
+    L.kda_forward_noalloc.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, p]
+    L.kda_forward_noalloc.restype = ctypes.c_int
+    L.kda_noalloc_max_workspace_bytes.argtypes = []
+    L.kda_noalloc_max_workspace_bytes.restype = sz
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_last_hip_error.argtypes = []
@@ -290,6 +297,27 @@ def forward_call(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stre
     st = lib().kda_forward(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V, *_heads(H, heads),
                            *summ, *ob, fmt, *ff, *ws, _stream(q, stream))
     _check(st, "kda_forward")
+
+
+def forward_noalloc(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stream=None, heads=None,
+                    initial_state=None):
+    """``kda_forward_noalloc``: :func:`forward_call` with the library's fixed
+    workspace array (``out`` needs no "workspace" entry)."""
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    summ = _flat([
+        _buf(out["transitions"], torch.float32, (plan.S, H, K, K), "transitions"),
+        _buf(out["updates"], torch.float32, (plan.S, H, K, V), "updates"),
+        _buf(out["carry_in"], torch.float32, (plan.S, H, K, V), "carry_in"),
+    ])
+    ob, fmt = _o_buf(plan, out["o"], H, V)
+    ff = _buf(out["final_state"], torch.float32, (plan.N, H, K, V), "final_state")
+    st = lib().kda_forward_noalloc(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V, *_heads(H, heads),
+                                   *summ, *ob, fmt, *ff, _stream(q, stream))
+    _check(st, "kda_forward_noalloc")
+
+
+def noalloc_max_workspace_bytes() -> int:
+    return int(lib().kda_noalloc_max_workspace_bytes())
 
 
 # storage formats of o accepted by kda_apply_carry (kda_o_format)

@@ -37,7 +37,8 @@
  *     no output is touched.  There is no fallback path of any kind.
  *   - Device pointers are plain device addresses owned by the caller; the
  *     library never allocates or frees device memory and keeps no global
- *     state.  Distinct plans may be used from distinct threads.
+ *     state, apart from the fixed per-GPU workspace array of
+ *     kda_forward_noalloc.  Distinct plans may be used from distinct threads.
  *   - BF16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *   - Tensors are dense and contiguous; every tensor pointer must be 16-byte
  *     aligned (KDA_ERR_MISALIGNED otherwise).
@@ -287,6 +288,36 @@ int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_b
                 void* o, size_t o_bytes, int32_t o_format,
                 float* final_state, size_t final_state_bytes,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_forward_noalloc -- kda_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same checks and the same kernels, with the
+ * workspace taken from a fixed array inside the library instead of an
+ * argument.  Each GPU the library runs on holds one such array of
+ * kda_noalloc_max_workspace_bytes() bytes (64 MiB) until the process ends;
+ * the first call on a device looks its address up (hipGetSymbolAddress), and
+ * no call allocates or frees anything.  A plan and head count whose
+ * kda_workspace_bytes exceeds that size return KDA_ERR_WORKSPACE_TOO_SMALL
+ * before anything else is checked or enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race on it and must not be made.
+ * Results are bitwise those of kda_forward.
+ */
+int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                        const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                        const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                        const uint16_t* beta, size_t beta_bytes,
+                        const float* initial_state, size_t initial_state_bytes,
+                        int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                        float* transitions, size_t transitions_bytes,
+                        float* updates, size_t updates_bytes,
+                        float* carry_in, size_t carry_in_bytes,
+                        void* o, size_t o_bytes, int32_t o_format,
+                        float* final_state, size_t final_state_bytes, hipStream_t stream);
+
+/* Bytes of the fixed workspace array kda_forward_noalloc uses on each GPU. */
+size_t kda_noalloc_max_workspace_bytes(void);
 
 /* Human-readable name of a kda_status value. */
 const char* kda_status_string(int status);
