@@ -55,6 +55,15 @@ constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
 constexpr int XS = 20;    // row stride (fp32) of the 16 x 16 off-diagonal product
 constexpr float kLog2e = 1.4426950408889634f;
+// Largest in-chunk factor exponent (log2 units) of the anchored chunk form.
+// A fragment with a chunk where some channel's decay between a token and the
+// anchor (or from the chunk start to the anchor) exceeds it is run again
+// token by token (see pipe_owner).
+constexpr float kFactorMax = 96.f;
+// Floor of the per-token log2 decay in the token-by-token re-run: 2^-300
+// times any finite FP32 value is below the smallest FP32 denormal, so the
+// floor changes no FP32 product.
+constexpr float kGateFloor = -300.f;
 // Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access;
 // accesses at or past num_records read zero and drop writes.
 constexpr int kBufDword3 = 0x00020000;
@@ -601,7 +610,26 @@ struct alignas(16) PipeSmem {
   float beta[2][CH];
   alignas(16) int16_t fexp[2][KD];            // power-of-two part of fac (0: none)
   int32_t fsplit[2][NOWN];                    // per operand helper: some fac split
+  alignas(16) int32_t rerun[NOWN];            // per operand helper: some chunk beyond the anchored form
 };
+
+// Whether the fragment is run again token by token: the OR of the operand
+// helpers' flags, uniform over the wave.  The helpers write them in step
+// 2nc-3; every wave reads them after its last pipeline barrier.
+__device__ __forceinline__ bool fragment_rerun(const PipeSmem& sm) {
+  const u32x4 f = *reinterpret_cast<const u32x4*>(&sm.rerun[0]);
+  return __builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) != 0;
+}
+
+// In the token-by-token re-run the operand buffers of parity b hold FP32
+// rows of 32 tokens: k in kr_h (tokens 0..15) and kr_l (16..31), q in
+// qr_h / qr_l and the per-token decay 2^l in kc_h / kc_l, each [16][128].
+__device__ __forceinline__ float* tok_rows(bf16* lo_half, bf16* hi_half, const int t) {
+  return reinterpret_cast<float*>(t < 16 ? lo_half : hi_half) + (t & 15) * KD;
+}
+typedef const volatile __attribute__((address_space(3))) f32x4 lds_f32x4;
+// a 16-byte LDS read the compiler neither merges with nor hoists over another
+__device__ __forceinline__ f32x4 ld4v(const float* p) { return *(lds_f32x4*)(const_cast<float*>(p)); }
 
 // Owner wave ow: the state columns [32ow, 32ow + 32) as four 32 x 32 FP32
 // accumulator tiles R[dt] (rows 32dt + 8r + 4(l/32) + e in lane l, register
@@ -631,27 +659,31 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
   const int o_row = H * VD * 4;   // one token of o (bytes)
 
   f32x16 R[4];
+  // the starting state (unanchored): identity, the given state or zero
+  auto load_start = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
-  if (MODE == kModeSumPhi) {
-    // the diagonal element of column col sits in tile col/32, register
-    // 4((col%32)/8) + col%4, of the lanes with l/32 = (col/4)%2
-    const int ln_s = opaque(lane) & 31;
-    const bool own = ((ln_s >> 2) & 1) == (lane >> 5);
+    for (int dt = 0; dt < 4; ++dt) R[dt] = zero16();
+    if (MODE == kModeSumPhi) {
+      // the diagonal element of column col sits in tile col/32, register
+      // 4((col%32)/8) + col%4, of the lanes with l/32 = (col/4)%2
+      const int ln_s = opaque(lane) & 31;
+      const bool own = ((ln_s >> 2) & 1) == (lane >> 5);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        R[dt][i] = (own && dt == ow && i == 4 * (ln_s >> 3) + (ln_s & 3)) ? 1.f : 0.f;
-  } else if (init != nullptr) {
-    const float* src = init + col;
+        for (int i = 0; i < 16; ++i)
+          R[dt][i] = (own && dt == ow && i == 4 * (ln_s >> 3) + (ln_s & 3)) ? 1.f : 0.f;
+    } else if (init != nullptr) {
+      const float* src = init + col;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
-  }
+          for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = src[(32 * dt + 8 * r + 4 * lh + e) * VD];
+    }
+  };
+  load_start();
   f32x16 Y = zero16(), O = zero16();
 
   // A operands of k-step kk (channels 16kk .. 16kk+15, k-slot order)
@@ -818,6 +850,76 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     rescale_exp((n + 1) & 1, lh);
   };
 
+  // Block n of the re-run, one token at a time in FP32:
+  //     R <- 2^l o R;  u = beta (v - R^T k);  R <- R + k u^T;  o = R^T q,
+  // with R the state itself.  A lane holds 64 rows of its column; the other
+  // 64 are in lane l ^ 32, so each dot product over the rows is the lane's
+  // part plus its partner's (summed in the same order in both lanes).
+  auto token_steps = [&](const int n) __attribute__((always_inline)) {
+    const int b = n & 1;
+    const int c0 = beg + n * CH;
+    const int nn = min(CH, end - c0);
+    const int lane_r = opaque(lane);
+    const int lhr = lane_r >> 5;
+    const int colr = 32 * ow + (lane_r & 31);
+    auto halves = [](const float x) {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    };
+    for (int t = 0; t < nn; ++t) {
+      const float* kt = tok_rows(sm.kr_h[b], sm.kr_l[b], t);
+      const float* dct = tok_rows(sm.kc_h[b], sm.kc_l[b], t);
+      float part[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        part[dt] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 32 * dt + 8 * r + 4 * lhr;
+          const f32x4 dv = ld4v(dct + row);
+          const f32x4 kv = ld4v(kt + row);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            R[dt][4 * r + e] *= dv[e];
+            part[dt] = __builtin_fmaf(kv[e], R[dt][4 * r + e], part[dt]);
+          }
+        }
+      }
+      const float kS = halves((part[0] + part[1]) + (part[2] + part[3]));
+      float vt = 0.f;
+      if (use_v) vt = bf2f(__builtin_bit_cast(uint16_t, sm.vv[b][t * NS + ((fwd && t >= 16) ? (colr ^ 4) : colr)]));
+      const float u = sm.beta[b][t] * (vt - kS);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 kv = ld4v(kt + 32 * dt + 8 * r + 4 * lhr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[dt][4 * r + e] = __builtin_fmaf(kv[e], u, R[dt][4 * r + e]);
+        }
+      }
+      if (fwd) {
+        const float* qt = tok_rows(sm.qr_h[b], sm.qr_l[b], t);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          part[dt] = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4 qv = ld4v(qt + 32 * dt + 8 * r + 4 * lhr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[dt] = __builtin_fmaf(qv[e], R[dt][4 * r + e], part[dt]);
+          }
+        }
+        const float ov = halves((part[0] + part[1]) + (part[2] + part[3]));
+        if (lhr == 0) {
+          const size_t oi = (static_cast<size_t>(c0 + t) * H + h) * VD + colr;
+          if (p.o_bf16) reinterpret_cast<bf16*>(p.o)[oi] = static_cast<bf16>(ov);
+          else p.o[oi] = ov;
+        }
+      }
+    }
+  };
+
   block_sync();   // steps -3 .. -1: the helpers fill the pipeline
   block_sync();
   block_sync();
@@ -837,6 +939,19 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     block_sync();
     finish(n);
     block_sync();
+  }
+  if (fragment_rerun(sm)) {
+    // Some chunk's in-chunk factors left the range the anchored form keeps
+    // finite and accurate, so its results for this fragment are discarded:
+    // the fragment runs again from its starting state, one token at a time
+    // in FP32.  The operand helpers stage each 32-token block as FP32 rows
+    // (two barriers per block, in every wave).
+    load_start();
+    for (int n = 0; n < nc; ++n) {
+      block_sync();
+      token_steps(n);
+      block_sync();
+    }
   }
   const int lane_e = opaque(lane);
   const int lh_e = lane_e >> 5;
@@ -947,6 +1062,7 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
   float dprev[8];   // (G_C - a) of the previous chunk, log2 units
 #pragma unroll
   for (int c = 0; c < 8; ++c) dprev[c] = 0.f;
+  bool rerun_w = false;   // some chunk is beyond the anchored form (this wave's channels)
 
   for (int m = 0; m < nc; ++m) {
     const int b = m & 1;
@@ -1001,8 +1117,18 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
         for (int c = 0; c < 8; ++c) t[c] = a[c] + dprev[c];
         store_fac(b, t);
       }
+      // The anchored form keeps every in-chunk factor 2^(G_i - a) within
+      // 2^+-kFactorMax when the anchor's decay a and the anchor-to-end decay
+      // G_C - a both stay above -kFactorMax (g <= 0: the extremes are token
+      // 0, at most -a, and token 31).  Beyond that on any channel of any
+      // chunk the fragment's results are discarded and it runs again.
+      float dmin = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) dprev[c] = gc[c] - a[c];
+      for (int c = 0; c < 8; ++c) {
+        dprev[c] = gc[c] - a[c];
+        dmin = fminf(dmin, fminf(a[c], dprev[c]));
+      }
+      rerun_w |= __builtin_amdgcn_ballot_w64(!(dmin >= -kFactorMax)) != 0;
 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -1048,9 +1174,47 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
   }
   // step 2nc-3: R *= e^{G_C - a} after the last chunk turns R back into S
   store_fac(nc & 1, dprev);
+  if (lane == 0) sm.rerun[oh] = rerun_w ? 1 : 0;
   block_sync();
   block_sync();   // steps 2nc-2, 2nc-1
   block_sync();
+  if (fragment_rerun(sm)) {
+    // The token-by-token re-run: block m's k, q and per-token decay as FP32
+    // rows, v and beta as in the pipeline, then the owners' turn.
+    for (int m = 0; m < nc; ++m) {
+      const int b = m & 1;
+      fetch(beg + m * CH);
+      if (!fwd) fetch_v(beg + m * CH);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float kx[8], dx[8], qx[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kx[2 * w] = __uint_as_float(rk[j][w] << 16);
+          kx[2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
+          dx[2 * w] = __builtin_amdgcn_exp2f(fmaxf(__uint_as_float(rg[j][w] << 16) * kLog2e, kGateFloor));
+          dx[2 * w + 1] = __builtin_amdgcn_exp2f(fmaxf(__uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e, kGateFloor));
+          qx[2 * w] = __uint_as_float(rq[j][w] << 16);
+          qx[2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
+        }
+        float* kd = tok_rows(sm.kr_h[b], sm.kr_l[b], tk + 16 * j) + c8;
+        float* dd = tok_rows(sm.kc_h[b], sm.kc_l[b], tk + 16 * j) + c8;
+        st4(kd, f32x4{kx[0], kx[1], kx[2], kx[3]});
+        st4(kd + 4, f32x4{kx[4], kx[5], kx[6], kx[7]});
+        st4(dd, f32x4{dx[0], dx[1], dx[2], dx[3]});
+        st4(dd + 4, f32x4{dx[4], dx[5], dx[6], dx[7]});
+        if (fwd) {
+          float* qd = tok_rows(sm.qr_h[b], sm.qr_l[b], tk + 16 * j) + c8;
+          st4(qd, f32x4{qx[0], qx[1], qx[2], qx[3]});
+          st4(qd + 4, f32x4{qx[4], qx[5], qx[6], qx[7]});
+        }
+        st4(&sm.vv[b][(tk + 16 * j) * NS + c8], sw_rows(fwd && j, rv[j]));
+      }
+      if (oh == 0 && lane < CH) sm.beta[b][lane] = __uint_as_float(rb << 16);
+      block_sync();
+      block_sync();
+    }
+  }
 }
 
 // T helper th (0..3) of the pipeline.  Part 1 of chunk m (step 2m-1) computes
@@ -1129,12 +1293,19 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
   }
   if (FILL) to_cache(nc - 1);
   block_sync();   // step 2nc-1
+  if (fragment_rerun(sm)) {
+    for (int m = 0; m < 2 * nc; ++m) block_sync();   // the re-run's barriers
+  }
 }
 
-// Helper wave with nothing to compute: keeps the barrier count of a fragment.
-__device__ __forceinline__ void pipe_idle(const int32_t beg, const int32_t end) {
+// Helper wave with nothing to compute: keeps the barrier count of a fragment
+// (including the re-run's, when some chunk is beyond the anchored form).
+__device__ __forceinline__ void pipe_idle(const PipeSmem& sm, const int32_t beg, const int32_t end) {
   const int nc = (end - beg + CH - 1) / CH;
   for (int i = 0; i < 2 * nc + 3; ++i) block_sync();
+  if (fragment_rerun(sm)) {
+    for (int m = 0; m < 2 * nc; ++m) block_sync();
+  }
 }
 
 // The state a fragment starts from, for this head: the carry-in C_r where it
@@ -1179,7 +1350,7 @@ __global__ void __launch_bounds__(kSummaryThreads, 1) kda_chunk_kernel(ChunkPara
       f32x4* dst = reinterpret_cast<f32x4*>(p.transitions + (static_cast<size_t>(seg) * p.H + h) * KD * KD);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       for (int i = tid - NOWN * 64; i < KD * KD / 4; i += NOWN * 64) dst[i] = z;
-      pipe_idle(beg, end);
+      pipe_idle(sm, beg, end);
     }
   } else if (wave < 3 * NOWN) {
     pipe_ophelper<kModeSumS>(p, sm, h, wave - 2 * NOWN, beg, end);

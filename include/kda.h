@@ -65,12 +65,15 @@
  *     KDA_ERR_INVALID_ARG.
  *   - Device calls are asynchronous on `stream`; launch failures are reported
  *     as KDA_ERR_HIP (kda_last_hip_error() gives the hipError_t).
- *   - Supported gate domain: g <= 0 and finite, with the decay mass of any 16
- *     consecutive tokens of one 32-token chunk below about 60 nats per
- *     channel.  The in-chunk exponential factors and the chunk-anchored copy
- *     of the state then stay inside the FP32 normal range; the re-anchoring
- *     between two chunks, which spans up to 32 tokens, is applied in two
- *     factors where one would underflow.
+ *   - Gate domain: every g <= 0, finite or -inf (exp(-inf) = 0 forgets the
+ *     channel).  The chunked (anchored) form is exact only while every
+ *     in-chunk decay factor of a 32-token chunk stays within 2^+-96: per
+ *     channel, the decay from the chunk's start to its anchor (token 15) and
+ *     from the anchor to the chunk's end both below 96 log2 units (66.5
+ *     nats).  Each launch checks that on the device; a fragment with any
+ *     chunk beyond it is run again from its starting state one token at a
+ *     time in FP32 (the same launch, no host involvement; slower but exact
+ *     for any such input).  g > 0 or NaN is outside the method's domain.
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -3,23 +3,23 @@
 HIP path does not import it, and it imports nothing from the HIP path).
 
 Per head, state S (K x V), one fragment of tokens processed in 32-token
-chunks.  All exponent arithmetic is in log2 units; g is first floored at
--300 (log2 units; exp2(-300) times any FP32 value is below the smallest FP32
-denormal, so the floor changes no FP32 result).
+chunks.  All exponent arithmetic is in log2 units.
 
 In a chunk with per-channel log-decays l_0 .. l_31:
-    G'_i = l_1 + ... + l_i  (G'_0 = 0)   in-chunk prefix without the first token
-    x_i  = G'_i - G'_15                  factor exponents around the anchor token 15
-    a    = l_0 + G'_15                   the anchor's decay from the chunk start
-    d    = x_31                          decay from the anchor to the chunk end
-The fast (anchored) form holds the state as R = 2^a o S and uses
+    G_i = l_0 + ... + l_i                in-chunk prefix
+    a   = G_15                           the anchor's decay from the chunk start
+    x_i = G_i - a                        factor exponents around the anchor
+    d   = x_31                           decay from the anchor to the chunk end
+The anchored form holds the state as R = 2^a o S and uses
     Kr = k 2^x,  Kc = k 2^-x,  Qr = q 2^x,
     A  = beta o (Kr Kc^T) strictly lower,  T = (I + A)^-1,  P = Qr Kc^T (j <= i)
     Y  = Kr R,  U = T diag(beta) (V - Y),  O = Qr R + P U,  R <- R + Kc^T U
-and re-anchors with R <- 2^(a_next + d) o R.  Its factors stay inside
-2^[-XF, XF] when max_d max(x_0, -x_31) <= XF.  A chunk beyond that is
-"extreme": its anchor and its leftover are taken as 0 (R = S on entry and
-exit), and its tokens run one by one in FP32:
+and re-anchors with R <- 2^(a_next + d) o R.  With g <= 0 its factors stay
+inside 2^[-XF, XF] when a >= -XF and d >= -XF on every channel (|x_0| <= -a).
+A chunk beyond that is "extreme"; a fragment with any extreme chunk is run
+again from its starting state with every token one by one in FP32 (its
+anchored results discarded), the log2 decay floored at -300 (2^-300 times
+any FP32 value is below the smallest FP32 denormal):
     R <- 2^l o R;  u = beta (v - R^T k);  R <- R + k u^T;  o = R^T q.
 """
 from __future__ import annotations
@@ -62,13 +62,13 @@ def exp2(x):
 
 
 def chunk_factors(l):
-    """Per-chunk exponents from the floored log2 decays l [32, K]."""
+    """Per-chunk exponents from the log2 decays l [32, K]."""
     l = l.astype(np.float32)
-    Gp = np.cumsum(np.concatenate([np.zeros((1, l.shape[1]), np.float32), l[1:]], 0), 0, dtype=np.float32)
-    x = (Gp - Gp[15]).astype(np.float32)
-    a = (l[0] + Gp[15]).astype(np.float32)
+    G = np.cumsum(l, 0, dtype=np.float32)
+    a = G[15]
+    x = (G - a).astype(np.float32)
     d = x[31]
-    extreme = bool(np.any(x[0] > XF) or np.any(-x[31] > XF))
+    extreme = not bool(np.all(np.minimum(a, d) >= -XF))
     return x, a, d, extreme
 
 
@@ -85,9 +85,9 @@ def run_fragment(k, v, q, g, beta, S0, robust=True, want_o=True):
     """One fragment (tokens of one sequence inside one segment) from S0.
 
     k, q, g: [L, K]; v: [L, V]; beta: [L] (float32 values of the BF16 inputs);
-    S0: [K, V].  ``robust=False`` forces the anchored form on every chunk (to
-    show what it does beyond its range).  Returns (o [L, V], S_end, number of
-    extreme chunks)."""
+    S0: [K, V].  ``robust=False`` keeps the anchored form's results even with
+    extreme chunks (to show what it does beyond its range).  Returns
+    (o [L, V], S_end, number of extreme chunks)."""
     L, K = k.shape
     V = v.shape[1]
     nc = (L + CH - 1) // CH
@@ -97,40 +97,41 @@ def run_fragment(k, v, q, g, beta, S0, robust=True, want_o=True):
         return np.concatenate([a, np.zeros((pad,) + a.shape[1:], a.dtype)], 0).astype(np.float32)
 
     k, v, q, beta = padded(k), padded(v), padded(q), padded(beta)
-    lg = np.maximum(padded(g) * f32(LOG2E), f32(GFLOOR)).astype(np.float32)
-    facts = [chunk_factors(lg[m * CH:(m + 1) * CH]) for m in range(nc)]
-    ext = [robust and f[3] for f in facts]
-    A_ = [f32(0) * facts[m][1] if ext[m] else facts[m][1] for m in range(nc)]
-    D_ = [f32(0) * facts[m][2] if ext[m] else facts[m][2] for m in range(nc)]
-
+    lg = (padded(g) * f32(LOG2E)).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        facts = [chunk_factors(lg[m * CH:(m + 1) * CH]) for m in range(nc)]
+    n_ext = sum(f[3] for f in facts)
     o = np.zeros((nc * CH, V), np.float32)
+    if robust and n_ext:
+        R = S0.astype(np.float32).copy()
+        for t in range(L):
+            R = (R * exp2(np.maximum(lg[t], f32(GFLOOR)))[:, None]).astype(np.float32)
+            u = (beta[t] * (v[t] - k[t] @ R)).astype(np.float32)
+            R = (R + np.outer(k[t], u)).astype(np.float32)
+            o[t] = q[t] @ R
+        return o[:L], R, n_ext
+
+    A_ = [f[1] for f in facts]
+    D_ = [f[2] for f in facts]
     R = rescale(S0.astype(np.float32), A_[0])
     tri_s = np.tril(np.ones((CH, CH), bool), -1)
     tri_i = np.tril(np.ones((CH, CH), bool), 0)
     for m in range(nc):
         sl = slice(m * CH, (m + 1) * CH)
         km, vm, qm, bm = k[sl], v[sl], q[sl], beta[sl]
-        if ext[m]:
-            for i in range(CH):
-                t = m * CH + i
-                R = (R * exp2(lg[t])[:, None]).astype(np.float32)
-                u = (bm[i] * (vm[i] - km[i] @ R)).astype(np.float32)
-                R = (R + np.outer(km[i], u)).astype(np.float32)
-                o[t] = qm[i] @ R
-        else:
-            x = facts[m][0]
-            Kr = (km * exp2(x)).astype(np.float32)
-            Kc = (km * exp2(-x)).astype(np.float32)
-            Qr = (qm * exp2(x)).astype(np.float32)
-            Amat = np.where(tri_s, bm[:, None] * smm(Kr, Kc.T), 0).astype(np.float32)
-            T = np.linalg.inv((np.eye(CH) + Amat).astype(np.float64)).astype(np.float32)
-            Tb = (T * bm[None, :]).astype(np.float32)
-            Y = smm(Kr, R)
-            U = smm(Tb, (vm - Y).astype(np.float32))
-            if want_o:
-                P = np.where(tri_i, smm(Qr, Kc.T), 0).astype(np.float32)
-                o[sl] = smm(Qr, R) + smm(P, U)
-            R = (R + smm(Kc.T, U)).astype(np.float32)
+        x = facts[m][0]
+        Kr = (km * exp2(x)).astype(np.float32)
+        Kc = (km * exp2(-x)).astype(np.float32)
+        Qr = (qm * exp2(x)).astype(np.float32)
+        Amat = np.where(tri_s, bm[:, None] * smm(Kr, Kc.T), 0).astype(np.float32)
+        T = np.linalg.inv((np.eye(CH) + Amat).astype(np.float64)).astype(np.float32)
+        Tb = (T * bm[None, :]).astype(np.float32)
+        Y = smm(Kr, R)
+        U = smm(Tb, (vm - Y).astype(np.float32))
+        if want_o:
+            P = np.where(tri_i, smm(Qr, Kc.T), 0).astype(np.float32)
+            o[sl] = smm(Qr, R) + smm(P, U)
+        R = (R + smm(Kc.T, U)).astype(np.float32)
         nxt = A_[m + 1] if m + 1 < nc else np.zeros_like(A_[0])
         R = rescale(R, (nxt + D_[m]).astype(np.float32))
-    return o[:L], R, sum(ext)
+    return o[:L], R, n_ext
