@@ -10,83 +10,17 @@
 #include "kda.h"
 #include "kda_internal.h"
 #include "kda_kernels.h"
+#include "kda_validate.h"
 
 namespace {
 
+using kda::check_carry;
+using kda::check_compose;
+using kda::check_dims;
+using kda::check_summaries;
+using kda::workspace_need;
+
 thread_local int g_last_hip_error = 0;
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V) {
-  if (plan == nullptr || plan_dev == nullptr) return KDA_ERR_INVALID_ARG;
-  if (H <= 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
-  if (K != 128 || V != 128) return KDA_ERR_UNSUPPORTED;
-  if (H > 65535) return KDA_ERR_UNSUPPORTED;
-  if (!aligned16(plan_dev)) return KDA_ERR_MISALIGNED;
-  return KDA_OK;
-}
-
-int check_heads(int32_t H, int32_t head_begin, int32_t head_count) {
-  if (head_begin < 0 || head_count <= 0 || head_count > H - head_begin) return KDA_ERR_INVALID_ARG;
-  return KDA_OK;
-}
-
-// A device buffer of the call: its address, the bytes the caller has there
-// and the bytes the call needs.  `optional` buffers may be null (then the
-// size is not checked).
-struct Buf {
-  const void* ptr;
-  size_t have;
-  size_t need;
-  bool optional;
-};
-
-// Null pointers first, then alignment, then sizes, so that each error is
-// reported the same way whichever buffer has it.
-int check_buffers(std::initializer_list<Buf> bufs) {
-  for (const Buf& b : bufs) {
-    if (b.ptr == nullptr && !b.optional) return KDA_ERR_INVALID_ARG;
-  }
-  for (const Buf& b : bufs) {
-    if (b.ptr != nullptr && !aligned16(b.ptr)) return KDA_ERR_MISALIGNED;
-  }
-  for (const Buf& b : bufs) {
-    if (b.ptr != nullptr && b.have < b.need) return KDA_ERR_BUFFER_TOO_SMALL;
-  }
-  return KDA_OK;
-}
-
-// Byte sizes of the tensors of a plan, for H heads of K = V = 128.
-struct Sizes {
-  size_t plan_dev, qkg, v, beta, state_n, trans, state_s, o32, o16;
-};
-Sizes sizes_of(const kda_plan* plan, int32_t H) {
-  const size_t T = static_cast<size_t>(plan->T), N = static_cast<size_t>(plan->N),
-               S = static_cast<size_t>(plan->S), h = static_cast<size_t>(H), K = 128, V = 128;
-  Sizes z;
-  z.plan_dev = plan->blob.size() * sizeof(int32_t);
-  z.qkg = T * h * K * 2;
-  z.v = T * h * V * 2;
-  z.beta = T * h * 2;
-  z.state_n = N * h * K * V * 4;
-  z.trans = S * h * K * K * 4;
-  z.state_s = S * h * K * V * 4;
-  z.o32 = T * h * V * 4;
-  z.o16 = T * h * V * 2;
-  return z;
-}
-
-size_t workspace_need(const kda_plan* plan, int32_t H) {
-  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
-  return slots * static_cast<size_t>(H) * kda::kChunkCacheBytes;
-}
-
-int check_workspace(const void* ws, size_t have, const kda_plan* plan, int32_t H) {
-  if (ws == nullptr) return KDA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return KDA_ERR_MISALIGNED;
-  if (have < workspace_need(plan, H)) return KDA_ERR_WORKSPACE_TOO_SMALL;
-  return KDA_OK;
-}
 
 // Grid of a chunk kernel: F * hn workgroups numbered linearly (head fastest),
 // laid out as x = hn * a, y = ceil(F / a) with the smallest a that keeps y
@@ -106,75 +40,6 @@ int finish_launch() {
     return KDA_ERR_HIP;
   }
   return KDA_OK;
-}
-
-// ---------------------------------------------------------------- checks
-
-int check_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
-                    const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
-                    const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
-                    const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
-                    int32_t V, int32_t head_begin, int32_t head_count, const float* transitions,
-                    size_t transitions_bytes, const float* updates, size_t updates_bytes,
-                    const void* workspace, size_t workspace_bytes) {
-  int st = check_dims(plan, plan_dev, H, K, V);
-  if (st != KDA_OK) return st;
-  st = check_heads(H, head_begin, head_count);
-  if (st != KDA_OK) return st;
-  const Sizes z = sizes_of(plan, H);
-  st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
-                      {k, k_bytes, z.qkg, false},
-                      {v, v_bytes, z.v, false},
-                      {g, g_bytes, z.qkg, false},
-                      {beta, beta_bytes, z.beta, false},
-                      {initial_state, initial_state_bytes, z.state_n, true},
-                      {transitions, transitions_bytes, z.trans, false},
-                      {updates, updates_bytes, z.state_s, false}});
-  if (st != KDA_OK) return st;
-  return check_workspace(workspace, workspace_bytes, plan, H);
-}
-
-int check_compose(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
-                  const float* transitions, size_t transitions_bytes, const float* updates,
-                  size_t updates_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
-                  int32_t head_count, const float* carry_in, size_t carry_in_bytes) {
-  int st = check_dims(plan, plan_dev, H, K, V);
-  if (st != KDA_OK) return st;
-  st = check_heads(H, head_begin, head_count);
-  if (st != KDA_OK) return st;
-  const Sizes z = sizes_of(plan, H);
-  return check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
-                        {transitions, transitions_bytes, z.trans, false},
-                        {updates, updates_bytes, z.state_s, false},
-                        {carry_in, carry_in_bytes, z.state_s, false}});
-}
-
-int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
-                const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
-                const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                const uint16_t* beta, size_t beta_bytes, const float* initial_state,
-                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
-                int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
-                size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
-                const void* workspace, size_t workspace_bytes) {
-  int st = check_dims(plan, plan_dev, H, K, V);
-  if (st != KDA_OK) return st;
-  st = check_heads(H, head_begin, head_count);
-  if (st != KDA_OK) return st;
-  if (o_format != KDA_O_FP32 && o_format != KDA_O_BF16) return KDA_ERR_INVALID_ARG;
-  const Sizes z = sizes_of(plan, H);
-  st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
-                      {q, q_bytes, z.qkg, false},
-                      {k, k_bytes, z.qkg, false},
-                      {v, v_bytes, z.v, false},
-                      {g, g_bytes, z.qkg, false},
-                      {beta, beta_bytes, z.beta, false},
-                      {initial_state, initial_state_bytes, z.state_n, true},
-                      {carry_in, carry_in_bytes, z.state_s, false},
-                      {o, o_bytes, o_format == KDA_O_BF16 ? z.o16 : z.o32, false},
-                      {final_state, final_state_bytes, z.state_n, false}});
-  if (st != KDA_OK) return st;
-  return check_workspace(workspace, workspace_bytes, plan, H);
 }
 
 // --------------------------------------------------------------- launches

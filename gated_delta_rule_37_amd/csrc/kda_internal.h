@@ -13,6 +13,10 @@ constexpr int32_t kFragCarried = 1;  // first fragment of a segment that continu
 constexpr int32_t kFragSegLast = 2;  // ends at its segment's end (its state is B_r)
 constexpr int32_t kFragSeqEnd = 4;   // ends at its sequence's end (owns final_state)
 
+// Bytes of one chunk-cache slot per head: T diag(beta) of a 32-token chunk
+// as bf16 hi and lo parts (2 x 32 x 32 x 2).
+constexpr int kChunkCacheBytes = 4096;
+
 // Largest supported packed token count: a chunk-count times 64 times the head
 // count stays far inside 32-bit grid arithmetic.
 constexpr int32_t kMaxTokens = (1 << 30);

@@ -42,8 +42,7 @@ struct ChunkParams {
 // ceil(e_r / 32) + r for the segment end e_r, the next segment's first is at
 // least floor(e_r / 32) + r + 1, so segments never share one); a slot holds,
 // per head, T diag(beta) as
-// [hi | lo] x [32 rows] x [32 columns in k-slot order] bf16 = 4096 bytes.
-constexpr int kChunkCacheBytes = 4096;
+// [hi | lo] x [32 rows] x [32 columns in k-slot order] bf16 = kChunkCacheBytes.
 __host__ __device__ inline int64_t chunk_cache_slot(int32_t seg, int32_t frag_begin, int32_t it) {
   return static_cast<int64_t>(frag_begin / 32) + seg + it;
 }

@@ -1,0 +1,44 @@
+// Host-side argument validation of the C ABI's device calls (kda_validate.cpp).
+// Each check returns KDA_OK or the kda_status the entry point returns; the
+// checks run in the order the header of the C ABI states.
+#ifndef KDA_VALIDATE_H_
+#define KDA_VALIDATE_H_
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+// Bytes of the workspace (the chunk cache) a plan needs for H heads.
+size_t workspace_need(const kda_plan* plan, int32_t H);
+
+// Plan, plan_dev and dimensions (K = V = 128, 0 < H <= 65535).
+int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V);
+
+int check_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                    const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
+                    const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
+                    const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                    int32_t V, int32_t head_begin, int32_t head_count, const float* transitions,
+                    size_t transitions_bytes, const float* updates, size_t updates_bytes,
+                    const void* workspace, size_t workspace_bytes);
+
+int check_compose(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                  const float* transitions, size_t transitions_bytes, const float* updates,
+                  size_t updates_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                  int32_t head_count, const float* carry_in, size_t carry_in_bytes);
+
+int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
+                size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
+                const void* workspace, size_t workspace_bytes);
+
+}  // namespace kda
+
+#endif  // KDA_VALIDATE_H_

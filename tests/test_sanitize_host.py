@@ -1,0 +1,129 @@
+"""The host code of the library under AddressSanitizer and UndefinedBehavior
+Sanitizer (CPU only): the planner (kda_plan.cpp) and the device calls'
+argument validation (kda_validate.cpp) are built with g++
+-fsanitize=address,undefined together with ``tests/sanitize/host_driver.cpp``,
+and driven with the plan fuzz cases, the invalid inputs and the buffer-size
+cases.  Any sanitizer report aborts the driver (nonzero exit); plan blobs must
+equal the plan oracle's, statuses the documented codes."""
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import plan_oracle as po
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_37_amd", "csrc")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "plan_cases.json")
+STATUS = {"INVALID_ARG": -1, "BAD_CU_SEQLENS": -2, "BAD_SEGMENTS": -3, "UNSUPPORTED": -4}
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path_factory.mktemp("sanitize") / "host_driver")
+    cmd = [gxx, "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+           "-I" + CSRC, "-I/opt/rocm/include", os.path.join(CSRC, "kda_plan.cpp"),
+           os.path.join(CSRC, "kda_validate.cpp"), os.path.join(ROOT, "tests", "sanitize", "host_driver.cpp"),
+           "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.fail("sanitizer build failed:\n" + res.stderr[-3000:])
+    return exe
+
+
+def _run(exe, lines):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:exitcode=23",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1:exitcode=24")
+    res = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, env=env,
+                         timeout=300)
+    assert res.returncode == 0, res.stderr[-4000:]
+    assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr, res.stderr[-4000:]
+    return res.stdout.strip().splitlines()
+
+
+def _plan_line(cu, S, bounds=None):
+    parts = [len(cu) - 1, S] + list(cu) + (list(bounds) if bounds else [])
+    return "plan " + " ".join(str(int(x)) for x in parts)
+
+
+def test_plans_under_sanitizers(driver):
+    rng = np.random.default_rng(2024)
+    cases = []
+    for seed in range(60):
+        N = int(rng.integers(1, 40))
+        cu = [0] + np.cumsum(rng.integers(1, 300, size=N)).astype(int).tolist()
+        T = cu[-1]
+        S = int(rng.integers(1, min(T, 80) + 1))
+        bounds = None
+        if seed % 3 == 0 and S > 1:
+            bounds = [0] + sorted(rng.choice(np.arange(1, T), size=S - 1, replace=False).tolist()) + [T]
+        cases.append((cu, S, bounds))
+    # edge sizes: one token, one segment per token, sequences of one token
+    cases += [([0, 1], 1, None), ([0, 7], 7, None), (list(range(9)), 3, None), (list(range(9)), 8, None)]
+    out = _run(driver, [_plan_line(*c) for c in cases])
+    assert len(out) == len(cases)
+    for (cu, S, bounds), line in zip(cases, out):
+        words = [int(w) for w in line.split()]
+        assert words[0] == 0, (cu, S, bounds)
+        np.testing.assert_array_equal(words[1:], po.build_plan(cu, S, bounds)["blob"])
+
+
+def test_invalid_plans_under_sanitizers(driver):
+    invalid = json.load(open(GOLDEN))["invalid"]
+    lines, want = [], []
+    for c in invalid:
+        if c["cu_seqlens"] is None or c["custom_bounds"] is not None and len(c["custom_bounds"]) != c["segments"] + 1:
+            continue   # the driver reads exactly S + 1 bounds; null inputs are covered by the ctypes tests
+        lines.append(_plan_line(c["cu_seqlens"], c["segments"], c["custom_bounds"]))
+        want.append(STATUS[c["kind"]])
+    lines.append(_plan_line([0, (1 << 30) + 1], 1))
+    want.append(STATUS["UNSUPPORTED"])
+    out = _run(driver, lines)
+    assert [int(line.split()[0]) for line in out] == want
+
+
+def _needs(cu, S, H):
+    T, N = cu[-1], len(cu) - 1
+    blob_words = len(po.build_plan(cu, S)["blob"])
+    ws = ((T + 31) // 32 + S) * H * 4096
+    return [4 * blob_words, T * H * 256, T * H * 256, T * H * 256, T * H * 256, T * H * 2, N * H * 65536,
+            S * H * 65536, S * H * 65536, S * H * 65536, T * H * 512, N * H * 65536, ws]
+
+
+@pytest.mark.parametrize("cu,S,H", [([0, 100], 2, 2), ([0, 37, 150, 151, 300], 4, 3), ([0, 1], 1, 1),
+                                    ([0, 65536], 64, 32)])
+def test_validation_under_sanitizers(driver, cu, S, H):
+    """Every buffer at exactly its size: all three checks pass (KDA_OK);
+    each buffer one byte short: the documented error in the calls that take
+    it; BF16 o needs half the bytes."""
+    need = _needs(cu, S, H)
+    head = ["check", len(cu) - 1, S] + cu + [H]
+    lines = [" ".join(map(str, head + need + [0]))]
+    want = [(0, 0, 0)]
+    for i in range(13):
+        short = list(need)
+        short[i] -= 1
+        lines.append(" ".join(map(str, head + short + [0])))
+        code = -8 if i == 12 else -9
+        # which of (summaries, compose, carry) take buffer i
+        takes = {0: (1, 1, 1), 1: (0, 0, 1), 2: (1, 0, 1), 3: (1, 0, 1), 4: (1, 0, 1), 5: (1, 0, 1),
+                 6: (1, 0, 1), 7: (1, 1, 0), 8: (1, 1, 0), 9: (0, 1, 1), 10: (0, 0, 1), 11: (0, 0, 1),
+                 12: (1, 0, 1)}[i]
+        want.append(tuple(code if t else 0 for t in takes))
+    bf = list(need)
+    bf[10] = need[10] // 2
+    lines.append(" ".join(map(str, head + bf + [1])))
+    want.append((0, 0, 0))
+    bf[10] -= 1
+    lines.append(" ".join(map(str, head + bf + [1])))
+    want.append((0, 0, -9))
+    out = _run(driver, lines)
+    got = [tuple(int(w) for w in line.split()) for line in out]
+    assert got == want
