@@ -49,7 +49,6 @@ constexpr int NOWN = 4;               // waves per role: owners (32 columns each
 // summaries kernel: owners of S (waves 0-3) and of the transition (4-7), helpers 8-11
 static_assert(4 * NOWN * 64 == kSummaryThreads, "summaries kernel wave roles");
 static_assert(3 * NOWN * 64 == kCarryThreads, "carry kernel: owners, operand helpers, T helpers");
-constexpr int NTC = kComposeThreads;  // compose kernel: 4 waves of 64
 constexpr int NS = 152;   // row stride (bf16) of token-major [32][128] tiles (conflict-free row and transposed reads)
 constexpr int TS = 40;    // row stride (bf16) of channel-major [128][32] tiles
 constexpr int FS = 36;    // row stride (fp32) of the 32 x 32 triangular-solve tiles
@@ -139,44 +138,11 @@ __device__ __forceinline__ void mfma_result_fence(f32x16& t) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(t));
 }
 
-// Two 16 x 16 accumulator tiles t0 (rows 0..15) and t1 (rows 16..31) hold, in
-// lane l and register e, rows 4(l/16) + e of column l%16.  A B operand of the
-// 16x16x32 MFMA needs rows 8(l/16) + 0..7 of one column per lane.  A 32-lane
-// swap of (t0, t1) followed by a 16-lane swap regroups them (checked on gfx950:
-// permlane32_swap(x, y) -> (x_lo|y_lo, x_hi|y_hi); permlane16_swap(x, y) ->
-// (x0 y0 x2 y2, x1 y1 x3 y3) by 16-lane rows).
-__device__ __forceinline__ void tiles16_to_b(const f32x4& t0, const f32x4& t1, float out[8]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[e]), __float_as_uint(t1[e]), false, false);
-    const auto q = __builtin_amdgcn_permlane16_swap(p[0], p[1], false, false);
-    out[e] = __uint_as_float(q[0]);
-    out[4 + e] = __uint_as_float(q[1]);
-  }
-}
-
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
-}
-
-// A 32 x 32 accumulator tile holds, in lane l and register 4r+e, the element
-// (row 8r + 4(l/32) + e, column l%32).  A B operand of the 32x32x16 MFMA needs
-// rows 16s + 8(l/32) + 0..7 of one column per lane.  Swapping the upper half of
-// register group 2s with the lower half of group 2s+1 across the two 32-lane
-// halves regroups them: out[0..3] = rows 16s + 8h + 0..3, out[4..7] = the next
-// four.
-__device__ __forceinline__ void tile_rows_to_b(const f32x16& t, int s, float out[8]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t x = __float_as_uint(t[4 * (2 * s) + e]);
-    const uint32_t y = __float_as_uint(t[4 * (2 * s + 1) + e]);
-    const auto p = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-    out[e] = __uint_as_float(p[0]);
-    out[4 + e] = __uint_as_float(p[1]);
-  }
 }
 
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1380,15 +1346,40 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   else pipe_thelper<false>(p, sm, h, wave - 2 * NOWN, flags, seg, beg, end);
 }
 
-// Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r for one head and one block of
-// 32 state columns.  Wave w computes rows [32w, 32w + 32); the current carry
-// is shared through LDS as split B operands.  A_r and B_r do not depend on
-// the carry, so each step's operands are loaded one step ahead.  Blocks are
-// numbered so that the column blocks of one head run on one XCD (workgroups
-// are dealt to the eight XCDs in turn) and share its L2 copy of A_r.
-__global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
-  __shared__ bf16x8 cbh[8][64];
-  __shared__ bf16x8 cbl[8][64];
+// Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r on FP32 matrix cores, for one
+// head and one block of 16 state columns (the columns of C never mix, so each
+// block scans on its own).  Wave w computes rows [16w, 16w + 16) as one
+// 16 x 16 tile (v_mfma_f32_16x16x4_f32; lane l, register i holds row
+// 16w + 4(l/16) + i, column l%16).  The k slots are permuted so that each
+// operand is contiguous: MFMA s, k slot j = l/16 stands for k = 32j + s, so a
+// lane's A operand over the whole product is A_r[16w + l%16][32j .. 32j + 31]
+// and its B operand C_r[32j .. 32j + 31][col].
+//
+// The scan is bound by moving A_r (64 KB per step and workgroup), not by the
+// products.  Read in the operand layout, each 16-byte load of a wave would
+// touch 64 rows' cache lines; instead the workgroup loads A_r with whole rows
+// per wave instruction, kComposeRing steps ahead into a ring of register
+// buffers (the step loop is unrolled over the ring, so no buffer is copied),
+// and stores it one step ahead into a double-buffered LDS tile with padded
+// rows, from which the operands are read without bank conflicts.  The carry
+// goes through a second, transposed LDS tile.  Every step has exactly one
+// barrier, so both tiles alternate by step parity.  The column blocks of a head
+// are numbered onto one XCD (workgroups are dealt to the eight XCDs in turn),
+// where they share its L2 copy of A_r.
+constexpr int kAtStride = KD + 4;   // floats per row of the A_r tile
+constexpr int kCtStride = KD + 4;   // floats per column of the transposed carry tile
+constexpr int kComposeRing = 4;     // operand ring: A_r is loaded kComposeRing - 1 steps before its store to LDS
+constexpr int kComposeWaves = kComposeThreads / 64;
+constexpr int kAPieces = KD * KD / 4 / kComposeThreads;   // 16-byte pieces of A_r per lane
+static_assert(kComposeWaves * 16 == KD, "compose: one 16-row tile per wave");
+
+struct alignas(16) ComposeSmem {
+  float at[2][KD * kAtStride];                  // A_r, row-major, by step parity
+  float ct[2][kComposeColumns * kCtStride];     // C_r[:, block] transposed, by step parity
+};
+
+__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(ComposeParams p) {
+  __shared__ ComposeSmem sm;
   const int H = p.H;
   const int xcd = blockIdx.x % 8;
   const int kq = blockIdx.x / 8;
@@ -1399,27 +1390,30 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int ln = lane & 31;
-  const int lh = lane >> 5;
-  const int col = 32 * cb + ln;
+  const int lc = lane & 15;    // column within the block (and row within the tile for A)
+  const int lj = lane >> 4;    // k slot: k = 32 lj + s
+  const int col = kComposeColumns * cb + lc;
+  const int row0 = 16 * wave;
 
-  // this lane's operands of step r: B_r (accumulator layout) and, when the
-  // transition is live, its row 32w + l%32 of A_r in k-step order
-  auto load_step = [&](const int r, const bool live, f32x4 (&a)[KD / 16][2], f32x16& bv) {
+  // A_r, coalesced: piece u of lane tid is 16-byte piece u * 512 + tid of the
+  // row-major matrix, i.e. row 16u + tid / 32, floats 4 (tid % 32) ..
+  auto load_a = [&](const int r, f32x4 (&a)[kAPieces]) {
+    const float* src = p.transitions + (static_cast<size_t>(r) * H + h) * KD * KD;
+#pragma unroll
+    for (int u = 0; u < kAPieces; ++u) a[u] = *reinterpret_cast<const f32x4*>(&src[4 * (u * kComposeThreads + tid)]);
+  };
+  auto store_a = [&](const int buf, const f32x4 (&a)[kAPieces]) {
+#pragma unroll
+    for (int u = 0; u < kAPieces; ++u) {
+      const int pc = u * kComposeThreads + tid;
+      st4(&sm.at[buf][(pc >> 5) * kAtStride + 4 * (pc & 31)], a[u]);
+    }
+  };
+  // this lane's rows of B_r, in the accumulator layout
+  auto load_b = [&](const int r, f32x4& bv) {
     const float* bsrc = p.updates + (static_cast<size_t>(r) * H + h) * KD * VD;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[4 * q + e] = bsrc[(32 * wave + 8 * q + 4 * lh + e) * VD + col];
-    }
-    if (live) {
-      const float* arow = p.transitions + ((static_cast<size_t>(r) * H + h) * KD + 32 * wave + ln) * KD;
-#pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        a[kk][0] = *reinterpret_cast<const f32x4*>(&arow[16 * kk + 8 * lh]);
-        a[kk][1] = *reinterpret_cast<const f32x4*>(&arow[16 * kk + 8 * lh + 4]);
-      }
-    }
+    for (int i = 0; i < 4; ++i) bv[i] = bsrc[(row0 + 4 * lj + i) * VD + col];
   };
 
   // transition flags of steps [lbase, lbase + 64) as a wave-wide bit mask.
@@ -1437,67 +1431,69 @@ __global__ void __launch_bounds__(NTC, 1) kda_compose_kernel(ComposeParams p) {
     return ((lmask >> (r - lbase)) & 1ull) != 0;
   };
 
-  f32x16 cur = zero16();
-  f32x4 a_n[KD / 16][2];
-  f32x16 b_n = zero16();
-  bool live_n = false;
-  if (p.S > 1) {
-    live_n = live_at(0);
-    load_step(0, live_n, a_n, b_n);
+  // ring slot t % kComposeRing holds step t's operands: its A_r from the
+  // load until the store to LDS one step before its use, its B_r and flag
+  // until its use
+  f32x4 a_ring[kComposeRing][kAPieces];
+  f32x4 b_ring[kComposeRing];
+  bool lv[kComposeRing];
+#pragma unroll
+  for (int d = 0; d < kComposeRing; ++d) {
+    lv[d] = false;
+    b_ring[d] = zero4();
+    if (d < p.S - 1) {
+      lv[d] = live_at(d);
+      load_b(d, b_ring[d]);
+      if (lv[d]) load_a(d, a_ring[d]);
+    }
   }
-  for (int r = 0; r < p.S; ++r) {
-    float* cdst = p.carry + (static_cast<size_t>(r) * H + h) * KD * VD;
+  if (lv[0]) store_a(0, a_ring[0]);
+  f32x4 cur = zero4();
+  for (int r0 = 0;; r0 += kComposeRing) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int ph = 0; ph < kComposeRing; ++ph) {
+      const int r = r0 + ph;            // r % kComposeRing == ph
+      float* cdst = p.carry + (static_cast<size_t>(r) * H + h) * KD * VD;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cdst[(32 * wave + 8 * q + 4 * lh + e) * VD + col] = cur[4 * q + e];
-    }
-    if (r == p.S - 1) break;
-    // take step r's operands, then issue step r+1's loads
-    f32x4 a_c[KD / 16][2];
-#pragma unroll
-    for (int kk = 0; kk < KD / 16; ++kk) {
-      a_c[kk][0] = a_n[kk][0];
-      a_c[kk][1] = a_n[kk][1];
-    }
-    f32x16 nxt = b_n;
-    const bool live = live_n;
-    if (r + 1 < p.S - 1) {
-      live_n = live_at(r + 1);
-      load_step(r + 1, live_n, a_n, b_n);
-    }
-    if (live) {
-      // A_r's rows, split (independent of the carry, so before the barrier)
-      bf16x8 ah[KD / 16], al[KD / 16];
-#pragma unroll
-      for (int kk = 0; kk < KD / 16; ++kk) {
-        const float xv[8] = {a_c[kk][0][0], a_c[kk][0][1], a_c[kk][0][2], a_c[kk][0][3],
-                             a_c[kk][1][0], a_c[kk][1][1], a_c[kk][1][2], a_c[kk][1][3]};
-        split8<true>(xv, ah[kk], al[kk]);
+      for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
+      if (r == p.S - 1) return;
+      const int buf = r & 1;
+      const bool live = lv[ph];
+      f32x4 nxt = b_ring[ph];
+      if (live) {
+        mfma_result_fence(cur);
+        // the carry, transposed into LDS: column lc, rows row0 + 4lj + 0..3
+        st4(&sm.ct[buf][lc * kCtStride + row0 + 4 * lj], cur);
       }
-      mfma_result_fence(cur);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float x[8];
-        tile_rows_to_b(cur, s, x);
-        split8<true>(x, cbh[2 * wave + s][lane], cbl[2 * wave + s][lane]);
-      }
+      // A_r reached LDS in step r-1 (or before the loop) and the carry just
+      // now; the barrier also ends step r-1's reads of the other parity's
+      // tiles, which step r refills below.  Every step takes it, also one
+      // whose transition is structurally zero, so that the parity stays safe.
       __syncthreads();
-      // two accumulation chains (even and odd k-steps) halve the dependent
-      // MFMA sequence
-      f32x16 acc1 = zero16();
+      if (live) {
+        f32x4 bop[8], aop[8];
 #pragma unroll
-      for (int kk = 0; kk < KD / 16; kk += 2) {
-        nxt = mfma3(ah[kk], al[kk], cbh[kk][lane], cbl[kk][lane], nxt);
-        acc1 = mfma3(ah[kk + 1], al[kk + 1], cbh[kk + 1][lane], cbl[kk + 1][lane], acc1);
+        for (int q = 0; q < 8; ++q) {
+          bop[q] = ld4(&sm.ct[buf][lc * kCtStride + 32 * lj + 4 * q]);
+          aop[q] = ld4(&sm.at[buf][(row0 + lc) * kAtStride + 32 * lj + 4 * q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nxt = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], nxt, 0, 0, 0);
       }
-      mfma_result_fence(nxt);
-      mfma_result_fence(acc1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) nxt[i] += acc1[i];
-      __syncthreads();
+      // step r+1's A_r into the other tile
+      const int p1 = (ph + 1) % kComposeRing;
+      if (r + 1 < p.S - 1 && lv[p1]) store_a(buf ^ 1, a_ring[p1]);
+      // step r + kComposeRing's operands into the slots step r has used up
+      const int rn = r + kComposeRing;
+      if (rn < p.S - 1) {
+        lv[ph] = live_at(rn);
+        load_b(rn, b_ring[ph]);
+        if (lv[ph]) load_a(rn, a_ring[ph]);
+      }
+      cur = nxt;
     }
-    cur = nxt;
   }
 }
 

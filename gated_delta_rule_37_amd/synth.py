@@ -42,6 +42,7 @@ class Workload:
     min_len: int = 512
     max_len: int = 8192
     gate_scale: float = 1.0
+    beta_scale: float = 1.0
     notes: str = field(default="", compare=False)
 
 
@@ -62,6 +63,10 @@ STRESS = {
                                  gate_scale=0.01),
     "t65536_h32_s64_slow": Workload("t65536_h32_s64_slow", 65536, 32, 128, 128, 64,
                                     seed=104, gate_scale=0.01),
+    # long memory: slow gates and weak writes (beta x 0.01), so every 1024-token
+    # transition stays O(1) and the 63-step composition carries real products
+    "t65536_h32_s64_longmem": Workload("t65536_h32_s64_longmem", 65536, 32, 128, 128, 64,
+                                       seed=105, gate_scale=0.001, beta_scale=0.01),
 }
 
 
@@ -81,7 +86,7 @@ def draw_lengths(gen: torch.Generator, total: int, lo: int, hi: int) -> list[int
 
 def make_inputs(T: int, H: int, K: int, V: int, seed: int, *, cu_seqlens=None,
                 varlen: bool = False, min_len: int = 512, max_len: int = 8192,
-                gate_scale: float = 1.0):
+                gate_scale: float = 1.0, beta_scale: float = 1.0):
     """Return a dict of CPU tensors: q, k, g [T,H,K], v [T,H,V], beta [T,H] (bf16)
     and cu_seqlens (int32, [N+1])."""
     gen = torch.Generator("cpu").manual_seed(int(seed))
@@ -104,7 +109,7 @@ def make_inputs(T: int, H: int, K: int, V: int, seed: int, *, cu_seqlens=None,
     q = xq / xq.norm(dim=-1, keepdim=True)
     k = xk / xk.norm(dim=-1, keepdim=True)
     g = -torch.nn.functional.softplus(xg) * gate_scale
-    beta = torch.sigmoid(xb)
+    beta = torch.sigmoid(xb) * beta_scale
     return dict(
         q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), v=xv.to(torch.bfloat16),
         g=g.to(torch.bfloat16), beta=beta.to(torch.bfloat16), cu_seqlens=cu_seqlens,
@@ -114,7 +119,7 @@ def make_inputs(T: int, H: int, K: int, V: int, seed: int, *, cu_seqlens=None,
 def workload_inputs(w: Workload):
     """Inputs of a named workload (see ``WORKLOADS``)."""
     return make_inputs(w.T, w.H, w.K, w.V, w.seed, varlen=w.varlen, min_len=w.min_len,
-                       max_len=w.max_len, gate_scale=w.gate_scale)
+                       max_len=w.max_len, gate_scale=w.gate_scale, beta_scale=w.beta_scale)
 
 
 def initial_states(N: int, H: int, K: int, V: int, seed: int, scale: float = 0.5) -> torch.Tensor:

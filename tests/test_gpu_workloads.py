@@ -19,6 +19,7 @@ CASES = [
     ("t65536_h32_s64", [17]),
     ("t4096_h8_s4_slow", [2]),
     ("t65536_h32_s64_slow", [30]),
+    ("t65536_h32_s64_longmem", [12]),
 ]
 
 
@@ -48,6 +49,11 @@ def test_workload_sampled_heads(name, heads):
         # carries are large, so the composition is exercised for real
         assert np.abs(ref["A"][1:]).max() > 1e-7
         assert np.abs(ref["C"][1:]).max() > 1e-2
+    if w.beta_scale < 1.0:
+        # long memory: every transition is O(1), so each of the 63 compose
+        # steps moves the carry by a full product (checked to the relative
+        # tolerance on every A_r by compare())
+        assert min(np.abs(ref["A"][r]).max() for r in range(1, w.segments)) > 0.1
     assert errs["o_abs"] <= pu.O_ATOL
 
 
