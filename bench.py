@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3      # dense FP32 matrix cores
+HOST_CORE_SHARE = 16          # host cores one GPU's share of the box gives a job
 
 # Algorithmic multiply-adds per token-head of the chunked method at chunk C=32,
 # K = V = 128 (triangular products counted exactly, FP32-grade):
@@ -103,41 +105,68 @@ def chunk_kernel_work(blob, H, o_bytes=4):
 
 
 def compose_work(S, H, live_count):
+    """The ordered scan: one K x K by K x V product per live transition, on
+    FP32 matrix cores; reads A_r (live ones) and B_r, writes every C_r."""
     macs = live_count * H * K * K * V
     bytes_ = (S - 1) * H * (K * V * 4) + live_count * H * K * K * 4 + S * H * K * V * 4
-    return {"macs": macs, "mfma_macs": 3 * macs, "bytes": bytes_}
+    return {"macs": macs, "bytes": bytes_}
 
 
-def cpu_baseline(x, w, heads=8, tokens=16384):
-    """The fp64 oracle on a bounded sample: `heads` heads x the first `tokens`
-    tokens, with the workload's segment length; full method (recurrence,
-    updates, transitions, composition)."""
-    import numpy as np
+_CPU_SAMPLE = {}
+
+
+def _oracle_head(h):
+    """The fp64 oracle over one head of the CPU sample (a pool worker)."""
     from threadpoolctl import threadpool_limits
+
+    from oracle import kda_oracle as ko
+
+    f, cu, bounds = _CPU_SAMPLE["f"], _CPU_SAMPLE["cu"], _CPU_SAMPLE["bounds"]
+    one = {n: a[:, h:h + 1] for n, a in f.items()}
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ko.recurrence(one["q"], one["k"], one["v"], one["g"], one["beta"], cu)
+        A = ko.segment_transitions(one["k"], one["g"], one["beta"], cu, bounds)
+        B = ko.segment_updates(one["k"], one["v"], one["g"], one["beta"], cu, bounds)
+        ko.compose(A, B)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(x, w, tokens=65536):
+    """The fp64 oracle timed on the host's cores: one process per core (at most
+    the one-GPU share of the box), each running the whole method (monolithic o
+    and final state, transitions, updates, composition) on one head of a
+    bounded sample, the first ``tokens`` tokens with the workload's segment
+    length; scaled to tokens/s over all H heads.  Must run before the process
+    touches the GPU (the pool forks)."""
+    import multiprocessing as mp
 
     from gated_delta_rule_37_amd import synth
     from oracle import kda_oracle as ko
 
-    seg_len = w.T // w.segments
+    cores = min(len(os.sched_getaffinity(0)), HOST_CORE_SHARE)
+    heads = min(cores, w.H)
     tokens = min(tokens, w.T)
-    f = {n: ko.decode_bf16(synth.bits(x[n][:tokens, :heads])) for n in ("q", "k", "v", "g", "beta")}
-    cu = [0, tokens]
-    bounds = list(range(0, tokens, seg_len)) + [tokens]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        ko.recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], cu)
-        A = ko.segment_transitions(f["k"], f["g"], f["beta"], cu, bounds)
-        B = ko.segment_updates(f["k"], f["v"], f["g"], f["beta"], cu, bounds)
-        ko.compose(A, B)
-        dt = time.perf_counter() - t0
+    seg_len = w.T // w.segments
+    cu_full = x["cu_seqlens"].tolist()
+    cu = [c for c in cu_full if c < tokens] + [tokens]
+    _CPU_SAMPLE["f"] = {n: ko.decode_bf16(synth.bits(x[n][:tokens, :heads]))
+                        for n in ("q", "k", "v", "g", "beta")}
+    _CPU_SAMPLE["cu"] = cu
+    _CPU_SAMPLE["bounds"] = list(range(0, tokens, seg_len)) + [tokens]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(heads) as pool:
+        per_head = pool.map(_oracle_head, range(heads))
+    wall = time.perf_counter() - t0
     return {
-        "value": round(tokens * heads / w.H / dt, 3),
+        "value": round(tokens * heads / w.H / wall, 3),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": heads,
         "kind": "oracle",
-        "sample": f"heads 0..{heads - 1} of {w.H}, tokens [0, {tokens}) of {w.name}, "
-                  f"{len(bounds) - 1} segments of {seg_len}; monolithic o+final, "
-                  f"transitions, updates, composition; fp64 numpy, 1 thread; {dt:.1f} s",
+        "sample": f"heads 0..{heads - 1} of {w.H} (one per process, BLAS 1 thread), tokens [0, {tokens}) "
+                  f"of {w.name}, {len(_CPU_SAMPLE['bounds']) - 1} segments of {seg_len}; monolithic o + "
+                  f"final, transitions, updates, composition; fp64 numpy; wall {wall:.1f} s "
+                  f"(per head {min(per_head):.1f}-{max(per_head):.1f} s); scaled to all {w.H} heads",
     }
 
 
@@ -231,8 +260,12 @@ def main():
     ap.add_argument("--initial-state", action="store_true",
                     help="give every sequence a (seeded, random) initial state")
     ap.add_argument("--o-bf16", action="store_true", help="store o as BF16 (rounded FP32 result)")
-    ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens of the CPU oracle's sample (one head per host core)")
+    ap.add_argument("--no-pages-timing", action="store_true",
+                    help="skip the pages' timing method (20 warmups, 60 iterations, 5 repeats)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="one JSON line per workload (pages' timing method; no CPU leg)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (PMC calibration)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
@@ -257,13 +290,62 @@ def main():
 
     from gated_delta_rule_37_amd import kda, synth
 
+    if args.all_workloads:
+        # one line per workload, the pages' timing method only (no CPU leg)
+        for name in list(synth.WORKLOADS) + list(synth.STRESS):
+            w = synth.WORKLOADS.get(name) or synth.STRESS[name]
+            res = measure(args, w, synth.workload_inputs(w), torch, kda, synth)
+            print(json.dumps(res), flush=True)
+        return
+
     w = synth.WORKLOADS.get(args.workload) or synth.STRESS[args.workload]
     x = synth.workload_inputs(w)
+    # the CPU leg runs first: its process pool forks, which must happen before
+    # this process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x, w, args.cpu_tokens)
+    res = measure(args, w, x, torch, kda, synth)
+    res["cpu_baseline"] = cpu
+    print(json.dumps(res), flush=True)
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def pages_timing(step, torch, repeats=5, warmup=20, iters=60):
+    """The pages' GPU timing method: 20 warmups and 60 timed iterations per
+    repeat, 5 repeats, the median of each repeat's per-launch medians (HIP
+    events on each launch's stream).  Returns ms per launch kind and their sum
+    per step."""
+    meds = {}
+    for _ in range(repeats):
+        for _ in range(warmup):
+            step()
+        ev = {}
+        for _ in range(iters):
+            step(ev)
+        torch.cuda.synchronize()
+        per = {kind: [a.elapsed_time(b) for a, b in pairs] for kind, pairs in ev.items()}
+        n = len(per["summaries"]) // iters   # launches of a kind per step (head groups)
+        for kind, times in per.items():
+            # sum the launches of one step, then the median over steps
+            step_sums = [sum(times[i * n:(i + 1) * n]) for i in range(iters)]
+            meds.setdefault(kind, []).append(_median(step_sums))
+    out = {kind: round(_median(v), 4) for kind, v in meds.items()}
+    out["step_launch_sum"] = round(sum(out[k] for k in ("summaries", "compose", "carry")), 4)
+    out["method"] = f"{repeats} repeats x ({warmup} warmups + {iters} timed), median of per-repeat medians"
+    return out
+
+
+def measure(args, w, x, torch, kda, synth):
+    """Time the whole forward on one workload (inputs resident on the GPU):
+    the driver's K timed steps, then the pages' method; return the JSON line."""
     dev = torch.device("cuda:0")
     d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
     cu = x["cu_seqlens"].tolist()
     plan = kda.Plan(cu, w.segments)
-    pd = plan.device_blob(dev)
     out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev, torch.bfloat16 if args.o_bf16 else torch.float32)
     h0 = None
     if args.initial_state:
@@ -284,6 +366,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pages = pages_timing(step, torch) if not args.no_pages_timing else None
 
     # per launch: each kind has steps * groups launches, each over one head group
     n_launch = {kind: len(pairs) for kind, pairs in events.items()}
@@ -321,6 +404,12 @@ def main():
         r["launch_ms_avg"] = round(ms, 4)
         r["launches_per_step"] = groups
         r["bounds_ms"] = {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)}
+        # the method's own FP32-grade multiply-adds (each split-bf16 product
+        # above executes about three bf16 ones) against the FP32 matrix peak
+        fp32 = wk["macs"] * 2 / (ms * 1e-3) / 1e12
+        r["fp32grade"] = {"achieved": round(fp32, 2), "unit": "TFLOP/s",
+                          "fp32_mfma_peak": PEAK_FP32_TFLOPS,
+                          "ratio_to_fp32_mfma_peak": round(fp32 / PEAK_FP32_TFLOPS, 4)}
         return r
 
     # the dominant kernel of the step is the longer of the two chunk launches
@@ -331,8 +420,10 @@ def main():
     S = plan.S
     live = int(sum(blob[4 + (S + 1) + 3 * S: 4 + (S + 1) + 4 * S]))
     comp = compose_work(S, w.H, live)
+    t_c_mfma = comp["macs"] * 2 / (PEAK_FP32_TFLOPS * 1e12) * 1e3
+    t_c_hbm = comp["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
 
-    res = {
+    return {
         "metric": "KDA fwd tokens/s at H=32,K=V=128 (segmented+compose)",
         "value": round(w.T / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
@@ -343,10 +434,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 state (split-bf16 MFMA)",
+        "dtype": "bf16 in, fp32 state (split-bf16 MFMA chunks, fp32 MFMA compose)",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "segments": w.segments, "sequences": plan.N, "seed": w.seed,
+                   "gate_scale": w.gate_scale, "beta_scale": w.beta_scale,
                    "head_groups": groups, "initial_state": bool(args.initial_state),
                    "o": "bf16" if args.o_bf16 else "fp32"},
         "roofline": roof,
@@ -355,19 +447,17 @@ def main():
         "kernels_ms": {"segment_summaries": round(pass1_ms, 4),
                        "compose_summaries": round(compose_ms, 4),
                        "apply_carry": round(pass2_ms, 4)},
+        "pages_method_ms": pages,
         "compose_roofline": {
-            "achieved_tflops_bf16": round(comp["mfma_macs"] * 2 / (compose_ms * 1e-3) / 1e12, 2),
+            "bound": "mfma" if t_c_mfma >= t_c_hbm else "hbm",
+            "bound_ms_fp32_mfma": round(t_c_mfma, 4),
+            "bound_ms_hbm": round(t_c_hbm, 4),
+            "achieved_tflops_fp32": round(comp["macs"] * 2 / (compose_ms * 1e-3) / 1e12, 2),
             "achieved_gbs": round(comp["bytes"] / (compose_ms * 1e-3) / 1e9, 1),
-            "bound_ms_hbm": round(comp["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
-            "bound_ms_mfma": round(comp["mfma_macs"] * 2 / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 4),
+            "frac": round(max(t_c_mfma, t_c_hbm) / compose_ms, 4),
         },
         "other_chunk_roofline": other,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_heads, args.cpu_tokens)
-    else:
-        res["cpu_baseline"] = None
-    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":
