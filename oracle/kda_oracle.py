@@ -25,6 +25,7 @@ __all__ = [
     "compose",
     "compose_pair",
     "segmented_forward",
+    "safe_gate",
 ]
 
 
@@ -37,6 +38,20 @@ def decode_bf16(bits) -> np.ndarray:
     """
     b = np.ascontiguousarray(np.asarray(bits).view(np.uint16)).astype(np.uint32)
     return (b << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def safe_gate(g, lower_bound=None):
+    """The optional safe gate: the log-decays the recurrence runs on.
+
+    [cuLA#136] Summary by CodeRabbit names "optional safe-gate parameters" and
+    defines nothing more.  The reading taken here is a lower bound on each
+    per-step, per-channel log-decay: g <- max(g, lower_bound) elementwise
+    (a decay factor exp(g) never below exp(lower_bound)); ``None`` leaves g
+    as given.
+    """
+    if lower_bound is None:
+        return g
+    return np.maximum(g, float(lower_bound))
 
 
 def kda_step(S, q_t, k_t, v_t, g_t, beta_t):

@@ -304,3 +304,31 @@ def test_linearity_in_v_and_h0():
     B = ko.segment_updates(k, v, g, beta, cu, bounds, h0=h0)
     B2 = ko.segment_updates(k, 2 * v, g, beta, cu, bounds, h0=2 * h0)
     np.testing.assert_array_equal(B2, 2 * B)
+
+
+def test_safe_gate_pins():
+    """The safe gate (a lower bound on g): a bound at or below every g changes
+    nothing, a bound of 0 is exactly the recurrence with g = 0, and a bound in
+    between replaces exactly the elements below it."""
+    rng = np.random.default_rng(77)
+    T, H, K, V = 20, 2, 8, 8
+    q, k, v = (rng.standard_normal((T, H, d)) for d in (K, K, V))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    g = -rng.exponential(1.0, (T, H, K))
+    beta = rng.uniform(0, 1, (T, H))
+    cu = [0, 7, T]
+    base = ko.recurrence(q, k, v, g, beta, cu)
+    low = ko.safe_gate(g, g.min() - 1.0)
+    np.testing.assert_array_equal(low, g)
+    for got, want in zip(ko.recurrence(q, k, v, low, beta, cu), base):
+        np.testing.assert_array_equal(got, want)
+    zero = ko.safe_gate(g, 0.0)
+    np.testing.assert_array_equal(zero, np.zeros_like(g))
+    for got, want in zip(ko.recurrence(q, k, v, zero, beta, cu), ko.recurrence(q, k, v, np.zeros_like(g), beta, cu)):
+        np.testing.assert_array_equal(got, want)
+    mid = ko.safe_gate(g, -0.5)
+    below = g < -0.5
+    assert below.any() and (~below).any()
+    np.testing.assert_array_equal(mid[below], -0.5)
+    np.testing.assert_array_equal(mid[~below], g[~below])
+    assert ko.safe_gate(g, None) is g
