@@ -3,6 +3,7 @@
 // enqueued; an error returns a negative kda_status and enqueues nothing.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <initializer_list>
 #include <mutex>
@@ -45,8 +46,14 @@ int finish_launch() {
 // --------------------------------------------------------------- launches
 // Each takes arguments that have passed the checks above.
 
+// The safe gate's lower bound as the kernels take it (log2 units).
+void set_gate(kda::ChunkParams& p, float gate_lower_bound) {
+  p.gate_floor_on = gate_lower_bound > -INFINITY ? 1 : 0;
+  p.gate_floor = gate_lower_bound * 1.4426950408889634f;
+}
+
 int launch_summaries(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* k,
-                     const uint16_t* v, const uint16_t* g, const uint16_t* beta,
+                     const uint16_t* v, const uint16_t* g, const uint16_t* beta, float gate_lower_bound,
                      const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
                      float* transitions, float* updates, void* workspace, hipStream_t stream) {
   kda::ChunkParams p{};
@@ -66,6 +73,7 @@ int launch_summaries(const kda_plan* plan, const int32_t* plan_dev, const uint16
   p.updates = updates;
   p.carry = nullptr;
   p.init_state = initial_state;
+  set_gate(p, gate_lower_bound);
   p.chunk_cache = static_cast<uint16_t*>(workspace);
   dim3 grid;
   const int st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
@@ -96,7 +104,7 @@ int launch_compose(const kda_plan* plan, const int32_t* plan_dev, const float* t
 }
 
 int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q, const uint16_t* k,
-                 const uint16_t* v, const uint16_t* g, const uint16_t* beta,
+                 const uint16_t* v, const uint16_t* g, const uint16_t* beta, float gate_lower_bound,
                  const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
                  const float* carry_in, void* o, int32_t o_format, float* final_state,
                  const void* workspace, hipStream_t stream) {
@@ -118,6 +126,7 @@ int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* 
   p.updates = nullptr;
   p.carry = carry_in;
   p.init_state = initial_state;
+  set_gate(p, gate_lower_bound);
   p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(workspace));
   dim3 grid;
   const int st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
@@ -177,18 +186,18 @@ extern "C" size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K
 extern "C" int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                                      const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
                                      const uint16_t* g, size_t g_bytes, const uint16_t* beta,
-                                     size_t beta_bytes, const float* initial_state,
+                                     size_t beta_bytes, float gate_lower_bound, const float* initial_state,
                                      size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
                                      int32_t head_begin, int32_t head_count, float* transitions,
                                      size_t transitions_bytes, float* updates, size_t updates_bytes,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int st = check_summaries(plan, plan_dev, plan_dev_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
-                                 beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin,
-                                 head_count, transitions, transitions_bytes, updates, updates_bytes,
+                                 beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V,
+                                 head_begin, head_count, transitions, transitions_bytes, updates, updates_bytes,
                                  workspace, workspace_bytes);
   if (st != KDA_OK) return st;
-  return launch_summaries(plan, plan_dev, k, v, g, beta, initial_state, H, head_begin, head_count,
-                          transitions, updates, workspace, stream);
+  return launch_summaries(plan, plan_dev, k, v, g, beta, gate_lower_bound, initial_state, H, head_begin,
+                          head_count, transitions, updates, workspace, stream);
 }
 
 extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
@@ -205,25 +214,27 @@ extern "C" int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_d
 extern "C" int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                                const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                                const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                               const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                               const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
+                               const float* initial_state,
                                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
                                int32_t head_begin, int32_t head_count, const float* carry_in,
                                size_t carry_in_bytes, void* o, size_t o_bytes, int32_t o_format,
                                float* final_state, size_t final_state_bytes, const void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
   const int st = check_carry(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
-                             beta, beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin,
-                             head_count, carry_in, carry_in_bytes, o, o_bytes, o_format, final_state,
-                             final_state_bytes, workspace, workspace_bytes);
+                             beta, beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V,
+                             head_begin, head_count, carry_in, carry_in_bytes, o, o_bytes, o_format,
+                             final_state, final_state_bytes, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
-  return launch_carry(plan, plan_dev, q, k, v, g, beta, initial_state, H, head_begin, head_count, carry_in,
-                      o, o_format, final_state, workspace, stream);
+  return launch_carry(plan, plan_dev, q, k, v, g, beta, gate_lower_bound, initial_state, H, head_begin,
+                      head_count, carry_in, o, o_format, final_state, workspace, stream);
 }
 
 extern "C" int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                            const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                            const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                           const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                           const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
+                           const float* initial_state,
                            size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
                            int32_t head_begin, int32_t head_count, float* transitions,
                            size_t transitions_bytes, float* updates, size_t updates_bytes,
@@ -231,7 +242,8 @@ extern "C" int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t
                            int32_t o_format, float* final_state, size_t final_state_bytes,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_summaries(plan, plan_dev, plan_dev_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
-                           beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
+                           beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V,
+                           head_begin, head_count,
                            transitions, transitions_bytes, updates, updates_bytes, workspace,
                            workspace_bytes);
   if (st != KDA_OK) return st;
@@ -239,26 +251,28 @@ extern "C" int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t
                      H, K, V, head_begin, head_count, carry_in, carry_in_bytes);
   if (st != KDA_OK) return st;
   st = check_carry(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
-                   beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count, carry_in,
+                   beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V, head_begin,
+                   head_count, carry_in,
                    carry_in_bytes, o, o_bytes, o_format, final_state, final_state_bytes, workspace,
                    workspace_bytes);
   if (st != KDA_OK) return st;
   dim3 unused;
   st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &unused);
   if (st != KDA_OK) return st;
-  st = launch_summaries(plan, plan_dev, k, v, g, beta, initial_state, H, head_begin, head_count, transitions,
-                        updates, workspace, stream);
+  st = launch_summaries(plan, plan_dev, k, v, g, beta, gate_lower_bound, initial_state, H, head_begin,
+                        head_count, transitions, updates, workspace, stream);
   if (st != KDA_OK) return st;
   st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry_in, stream);
   if (st != KDA_OK) return st;
-  return launch_carry(plan, plan_dev, q, k, v, g, beta, initial_state, H, head_begin, head_count, carry_in, o,
-                      o_format, final_state, workspace, stream);
+  return launch_carry(plan, plan_dev, q, k, v, g, beta, gate_lower_bound, initial_state, H, head_begin,
+                      head_count, carry_in, o, o_format, final_state, workspace, stream);
 }
 
 extern "C" int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                                    const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                                    const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                                   const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                                   const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
+                                   const float* initial_state,
                                    size_t initial_state_bytes, int32_t H, int32_t K, int32_t V,
                                    int32_t head_begin, int32_t head_count, float* transitions,
                                    size_t transitions_bytes, float* updates, size_t updates_bytes,
@@ -277,7 +291,7 @@ extern "C" int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev
   // every chunk-cache slot the carry launch reads is written by the summaries
   // launch of the same call, so the array needs no clearing between calls
   return kda_forward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
-                     beta_bytes, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
+                     beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
                      transitions, transitions_bytes, updates, updates_bytes, carry_in, carry_in_bytes, o,
                      o_bytes, o_format, final_state, final_state_bytes, ws, kScratchBytes, stream);
 }

@@ -30,6 +30,8 @@ struct ChunkParams {
   const uint16_t* beta;
   float* o;              // [T, H, V], FP32, or BF16 bits when o_bf16 is set
   int32_t o_bf16;
+  int32_t gate_floor_on;  // the optional gate lower bound is set
+  float gate_floor;       // that bound in log2 units (-inf when not set)
   float* final_state;
   float* transitions;
   float* updates;

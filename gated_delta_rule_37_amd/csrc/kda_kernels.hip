@@ -1058,6 +1058,13 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
           for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(kf[j][c]));
         }
       }
+      if (p.gate_floor_on) {
+        // the optional safe gate: every log-decay at least the lower bound
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) G[j][c] = fmaxf(G[j][c], p.gate_floor);
+      }
       if (oh == 0 && lane < CH) sm.beta[b][lane] = __uint_as_float(rb << 16);
       __builtin_amdgcn_sched_barrier(0);
       fetch(beg + (m + 1) * CH);
@@ -1158,8 +1165,11 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
         for (int w = 0; w < 4; ++w) {
           kx[2 * w] = __uint_as_float(rk[j][w] << 16);
           kx[2 * w + 1] = __uint_as_float(rk[j][w] & 0xffff0000u);
-          dx[2 * w] = __builtin_amdgcn_exp2f(fmaxf(__uint_as_float(rg[j][w] << 16) * kLog2e, kGateFloor));
-          dx[2 * w + 1] = __builtin_amdgcn_exp2f(fmaxf(__uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e, kGateFloor));
+          // (gate_floor is -inf when the safe gate is off)
+          dx[2 * w] = __builtin_amdgcn_exp2f(
+              fmaxf(fmaxf(__uint_as_float(rg[j][w] << 16) * kLog2e, p.gate_floor), kGateFloor));
+          dx[2 * w + 1] = __builtin_amdgcn_exp2f(
+              fmaxf(fmaxf(__uint_as_float(rg[j][w] & 0xffff0000u) * kLog2e, p.gate_floor), kGateFloor));
           qx[2 * w] = __uint_as_float(rq[j][w] << 16);
           qx[2 * w + 1] = __uint_as_float(rq[j][w] & 0xffff0000u);
         }

@@ -88,16 +88,23 @@ size_t workspace_need(const kda_plan* plan, int32_t H) {
   return slots * static_cast<size_t>(H) * kChunkCacheBytes;
 }
 
+int check_gate_bound(float gate_lower_bound) {
+  // NaN fails both comparisons
+  return (gate_lower_bound <= 0.f) ? KDA_OK : KDA_ERR_INVALID_ARG;
+}
+
 int check_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                     const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
                     const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
-                    const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                    float gate_lower_bound, const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
                     int32_t V, int32_t head_begin, int32_t head_count, const float* transitions,
                     size_t transitions_bytes, const float* updates, size_t updates_bytes,
                     const void* workspace, size_t workspace_bytes) {
   int st = check_dims(plan, plan_dev, H, K, V);
   if (st != KDA_OK) return st;
   st = check_heads(H, head_begin, head_count);
+  if (st != KDA_OK) return st;
+  st = check_gate_bound(gate_lower_bound);
   if (st != KDA_OK) return st;
   const Sizes z = sizes_of(plan, H);
   st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
@@ -130,9 +137,9 @@ int check_compose(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev
 int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                 const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                 const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                const uint16_t* beta, size_t beta_bytes, const float* initial_state,
-                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
-                int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
+                const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
+                const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                int32_t V, int32_t head_begin, int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
                 size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
                 const void* workspace, size_t workspace_bytes) {
   int st = check_dims(plan, plan_dev, H, K, V);
@@ -140,6 +147,8 @@ int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_b
   st = check_heads(H, head_begin, head_count);
   if (st != KDA_OK) return st;
   if (o_format != KDA_O_FP32 && o_format != KDA_O_BF16) return KDA_ERR_INVALID_ARG;
+  st = check_gate_bound(gate_lower_bound);
+  if (st != KDA_OK) return st;
   const Sizes z = sizes_of(plan, H);
   st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
                       {q, q_bytes, z.qkg, false},

@@ -17,10 +17,13 @@ size_t workspace_need(const kda_plan* plan, int32_t H);
 // Plan, plan_dev and dimensions (K = V = 128, 0 < H <= 65535).
 int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V);
 
+// The optional safe-gate lower bound: <= 0 or -inf (not NaN).
+int check_gate_bound(float gate_lower_bound);
+
 int check_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                     const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
                     const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
-                    const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                    float gate_lower_bound, const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
                     int32_t V, int32_t head_begin, int32_t head_count, const float* transitions,
                     size_t transitions_bytes, const float* updates, size_t updates_bytes,
                     const void* workspace, size_t workspace_bytes);
@@ -33,9 +36,9 @@ int check_compose(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev
 int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                 const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                 const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                const uint16_t* beta, size_t beta_bytes, const float* initial_state,
-                size_t initial_state_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
-                int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
+                const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
+                const float* initial_state, size_t initial_state_bytes, int32_t H, int32_t K,
+                int32_t V, int32_t head_begin, int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
                 size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
                 const void* workspace, size_t workspace_bytes);
 

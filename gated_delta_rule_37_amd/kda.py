@@ -94,15 +94,16 @@ def lib() -> ctypes.CDLL:
     L.kda_workspace_bytes.restype = sz
     buf = [p, sz]            # a device pointer and its size in bytes
     dims = [i32] * 5         # H, K, V, head_begin, head_count
-    L.kda_segment_summaries.argtypes = [p, *buf, *buf * 4, *buf, *dims, *buf, *buf, *buf, p]
+    f32 = ctypes.c_float     # the safe gate's lower bound
+    L.kda_segment_summaries.argtypes = [p, *buf, *buf * 4, f32, *buf, *dims, *buf, *buf, *buf, p]
     L.kda_segment_summaries.restype = ctypes.c_int
     L.kda_compose_summaries.argtypes = [p, *buf, *buf, *buf, *dims, *buf, p]
     L.kda_compose_summaries.restype = ctypes.c_int
-    L.kda_apply_carry.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, i32, *buf, *buf, p]
+    L.kda_apply_carry.argtypes = [p, *buf, *buf * 5, f32, *buf, *dims, *buf, *buf, i32, *buf, *buf, p]
     L.kda_apply_carry.restype = ctypes.c_int
-    L.kda_forward.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, *buf, p]
+    L.kda_forward.argtypes = [p, *buf, *buf * 5, f32, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, *buf, p]
     L.kda_forward.restype = ctypes.c_int
-    L.kda_forward_noalloc.argtypes = [p, *buf, *buf * 5, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, p]
+    L.kda_forward_noalloc.argtypes = [p, *buf, *buf * 5, f32, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, p]
     L.kda_forward_noalloc.restype = ctypes.c_int
     L.kda_noalloc_max_workspace_bytes.argtypes = []
     L.kda_noalloc_max_workspace_bytes.restype = sz
@@ -197,9 +198,10 @@ def _stream(t: torch.Tensor, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _inputs(plan: Plan, q, k, v, g, beta, initial_state):
-    """H, K, V and the flat (pointer, bytes) list of (q,) k, v, g, beta and the
-    initial states; q and initial_state may be None."""
+def _inputs(plan: Plan, q, k, v, g, beta, initial_state, gate_lower_bound=None):
+    """H, K, V and the flat argument list of (q,) k, v, g, beta (pointer, bytes
+    each), the safe gate's lower bound and the initial states (q and
+    initial_state may be None; no bound is -inf)."""
     T, H, K = k.shape
     V = v.shape[2]
     if T != plan.T:
@@ -208,9 +210,10 @@ def _inputs(plan: Plan, q, k, v, g, beta, initial_state):
     bufs += [
         _buf(k, torch.bfloat16, (T, H, K), "k"), _buf(v, torch.bfloat16, (T, H, V), "v"),
         _buf(g, torch.bfloat16, (T, H, K), "g"), _buf(beta, torch.bfloat16, (T, H), "beta"),
-        _buf(initial_state, torch.float32, (plan.N, H, K, V), "initial_state"),
     ]
-    return H, K, V, _flat(bufs)
+    bound = float("-inf") if gate_lower_bound is None else float(gate_lower_bound)
+    init = _buf(initial_state, torch.float32, (plan.N, H, K, V), "initial_state")
+    return H, K, V, _flat(bufs) + [bound] + list(init)
 
 
 def _flat(bufs):
@@ -231,11 +234,11 @@ def _plan_dev(plan: Plan, plan_dev):
 
 
 def segment_summaries(plan: Plan, plan_dev: torch.Tensor, k, v, g, beta, transitions, updates,
-                      workspace, stream=None, heads=None, initial_state=None):
+                      workspace, stream=None, heads=None, initial_state=None, gate_lower_bound=None):
     """``kda_segment_summaries``: the affine summary (A_r, B_r) of every segment,
     for the heads ``heads = (begin, count)`` (default: all).  Sequences start
     from ``initial_state`` [N, H, K, V] when given, else from zero."""
-    H, K, V, ins = _inputs(plan, None, k, v, g, beta, initial_state)
+    H, K, V, ins = _inputs(plan, None, k, v, g, beta, initial_state, gate_lower_bound)
     outs = _flat([
         _buf(transitions, torch.float32, (plan.S, H, K, K), "transitions"),
         _buf(updates, torch.float32, (plan.S, H, K, V), "updates"),
@@ -268,10 +271,10 @@ def _o_buf(plan: Plan, o, H, V):
 
 
 def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, o, final_state,
-                workspace, stream=None, heads=None, initial_state=None):
+                workspace, stream=None, heads=None, initial_state=None, gate_lower_bound=None):
     """``kda_apply_carry``: o and the final states, each segment from its carry-in C_r
     (a fragment that starts a sequence from ``initial_state``, else zero)."""
-    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state, gate_lower_bound)
     c = _buf(carry_in, torch.float32, (plan.S, H, K, V), "carry_in")
     ob, fmt = _o_buf(plan, o, H, V)
     ff = _buf(final_state, torch.float32, (plan.N, H, K, V), "final_state")
@@ -282,10 +285,10 @@ def apply_carry(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, carry_in, 
 
 
 def forward_call(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stream=None, heads=None,
-                 initial_state=None):
+                 initial_state=None, gate_lower_bound=None):
     """``kda_forward``: summaries, compose and carry in one C call, into the
     buffers of ``out`` (as :func:`alloc_outputs` makes them)."""
-    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state, gate_lower_bound)
     summ = _flat([
         _buf(out["transitions"], torch.float32, (plan.S, H, K, K), "transitions"),
         _buf(out["updates"], torch.float32, (plan.S, H, K, V), "updates"),
@@ -300,10 +303,10 @@ def forward_call(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stre
 
 
 def forward_noalloc(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, stream=None, heads=None,
-                    initial_state=None):
+                    initial_state=None, gate_lower_bound=None):
     """``kda_forward_noalloc``: :func:`forward_call` with the library's fixed
     workspace array (``out`` needs no "workspace" entry)."""
-    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state)
+    H, K, V, ins = _inputs(plan, q, k, v, g, beta, initial_state, gate_lower_bound)
     summ = _flat([
         _buf(out["transitions"], torch.float32, (plan.S, H, K, K), "transitions"),
         _buf(out["updates"], torch.float32, (plan.S, H, K, V), "updates"),
@@ -365,7 +368,7 @@ def _side_stream(device) -> torch.cuda.Stream:
 
 
 def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, events=None,
-            initial_state=None, o_dtype=torch.float32):
+            initial_state=None, o_dtype=torch.float32, gate_lower_bound=None):
     """The whole segmented forward: summaries, compose, carry.  Returns ``out``.
     Sequence n starts from ``initial_state[n]`` ([N, H, K, V] FP32) when given,
     else from zero.  ``o_dtype`` (used when ``out`` is None) is float32 or
@@ -402,12 +405,12 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
     if len(runs) == 1:
         timed("summaries", main, lambda: segment_summaries(
             plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["workspace"], main,
-            initial_state=initial_state))
+            initial_state=initial_state, gate_lower_bound=gate_lower_bound))
         timed("compose", main, lambda: compose_summaries(
             plan, pd, out["transitions"], out["updates"], out["carry_in"], main))
         timed("carry", main, lambda: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["workspace"], main, initial_state=initial_state))
+            out["workspace"], main, initial_state=initial_state, gate_lower_bound=gate_lower_bound))
         return out
 
     side = _side_stream(q.device)
@@ -415,7 +418,7 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
     for hr in runs:
         timed("summaries", main, lambda hr=hr: segment_summaries(
             plan, pd, k, v, g, beta, out["transitions"], out["updates"], out["workspace"], main,
-            heads=hr, initial_state=initial_state))
+            heads=hr, initial_state=initial_state, gate_lower_bound=gate_lower_bound))
         ev = torch.cuda.Event()
         ev.record(main)
         done_s.append(ev)
@@ -430,7 +433,8 @@ def forward(plan: Plan, q, k, v, g, beta, out=None, stream=None, groups=1, event
         main.wait_event(evc)
         timed("carry", main, lambda hr=hr: apply_carry(
             plan, pd, q, k, v, g, beta, out["carry_in"], out["o"], out["final_state"],
-            out["workspace"], main, heads=hr, initial_state=initial_state))
+            out["workspace"], main, heads=hr, initial_state=initial_state,
+            gate_lower_bound=gate_lower_bound))
     # every launch on the side stream precedes the last carry launch on main,
     # so work issued later on main is ordered after all of it
     return out

@@ -201,9 +201,16 @@ size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V
  *                   A smaller workspace gives KDA_ERR_WORKSPACE_TOO_SMALL,
  *                   any other smaller buffer KDA_ERR_BUFFER_TOO_SMALL; in
  *                   both cases nothing is enqueued.
+ *   gate_lower_bound  the optional safe gate (#136 Summary by CodeRabbit:
+ *                   optional safe-gate parameters): the recurrence runs on
+ *                   max(g, gate_lower_bound) per element, in nats.  -INFINITY
+ *                   leaves g as given; a bound >= -4.4 keeps every chunk in
+ *                   the anchored form's range (no fragment is re-run).  NaN or
+ *                   a bound > 0 gives KDA_ERR_INVALID_ARG.  Pass the same bound
+ *                   to kda_segment_summaries and kda_apply_carry.
  *   stream          the HIP stream every launch of the call is enqueued on.
- * Check order: plan and dimensions, head range, null pointers, alignment,
- * sizes.
+ * Check order: plan and dimensions, head range, o_format and gate bound,
+ * null pointers, alignment, sizes.
  */
 
 /*
@@ -226,6 +233,7 @@ size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V
 int kda_segment_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                           const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
                           const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
+                          float gate_lower_bound,
                           const float* initial_state, size_t initial_state_bytes,
                           int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
                           float* transitions, size_t transitions_bytes,
@@ -263,7 +271,7 @@ int kda_compose_summaries(const kda_plan* plan, const int32_t* plan_dev, size_t 
 int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                     const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                     const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                    const uint16_t* beta, size_t beta_bytes,
+                    const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
                     const float* initial_state, size_t initial_state_bytes,
                     int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
                     const float* carry_in, size_t carry_in_bytes,
@@ -282,7 +290,7 @@ int kda_apply_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_d
 int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                 const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                 const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                const uint16_t* beta, size_t beta_bytes,
+                const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
                 const float* initial_state, size_t initial_state_bytes,
                 int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
                 float* transitions, size_t transitions_bytes,
@@ -310,7 +318,7 @@ int kda_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_b
 int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                         const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
                         const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                        const uint16_t* beta, size_t beta_bytes,
+                        const uint16_t* beta, size_t beta_bytes, float gate_lower_bound,
                         const float* initial_state, size_t initial_state_bytes,
                         int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
                         float* transitions, size_t transitions_bytes,

@@ -3,12 +3,12 @@
 // and -fsanitize=address,undefined, and runs the cases it reads from stdin,
 // one per line:
 //   plan N S c_0 .. c_N [b_0 .. b_S]   -> "status w_0 w_1 ..." (the plan blob)
-//   check N S c_0 .. c_N H sizes...     -> "summaries compose carry" statuses
+//   check N S c_0 .. c_N H sizes... fmt bound -> "summaries compose carry" statuses
 // `check` builds the balanced plan and calls the three validation functions
 // with fake, never dereferenced, 16-byte-aligned addresses and the given byte
 // counts (in the order of kda_forward's buffers: plan_dev q k v g beta
 // initial_state transitions updates carry_in o final_state workspace, then
-// o_format); nothing is launched.
+// o_format and the safe gate's lower bound); nothing is launched.
 #include <cstdint>
 #include <iostream>
 #include <sstream>
@@ -54,6 +54,9 @@ void run_check(std::istringstream& in) {
   for (auto& x : z) in >> x;
   int32_t fmt;
   in >> fmt;
+  std::string bound_text;
+  in >> bound_text;
+  const float bound = std::stof(bound_text);
   kda_plan* plan = nullptr;
   if (kda_plan_segments(cu.data(), N, S, nullptr, &plan) != KDA_OK) {
     std::cout << "noplan\n";
@@ -63,10 +66,10 @@ void run_check(std::istringstream& in) {
   auto f32 = [](int i) { return static_cast<const float*>(fake(i)); };
   const int32_t* pd = static_cast<const int32_t*>(fake(0));
   const int s1 = kda::check_summaries(plan, pd, z[0], u16(2), z[2], u16(3), z[3], u16(4), z[4], u16(5), z[5],
-                                      f32(6), z[6], H, 128, 128, 0, H, f32(7), z[7], f32(8), z[8], fake(12), z[12]);
+                                      bound, f32(6), z[6], H, 128, 128, 0, H, f32(7), z[7], f32(8), z[8], fake(12), z[12]);
   const int s2 = kda::check_compose(plan, pd, z[0], f32(7), z[7], f32(8), z[8], H, 128, 128, 0, H, f32(9), z[9]);
   const int s3 = kda::check_carry(plan, pd, z[0], u16(1), z[1], u16(2), z[2], u16(3), z[3], u16(4), z[4], u16(5),
-                                  z[5], f32(6), z[6], H, 128, 128, 0, H, f32(9), z[9], fake(10), z[10], fmt,
+                                  z[5], bound, f32(6), z[6], H, 128, 128, 0, H, f32(9), z[9], fake(10), z[10], fmt,
                                   f32(11), z[11], fake(12), z[12]);
   std::cout << s1 << ' ' << s2 << ' ' << s3 << '\n';
   kda_plan_destroy(plan);

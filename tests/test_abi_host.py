@@ -115,23 +115,28 @@ class Call:
     replace a buffer's address (``<name>``), its size (``<name>_bytes``) or a
     scalar argument."""
 
-    SUMMARIES = ("plan_dev", "k", "v", "g", "beta", "init", "dims", "transitions", "updates", "workspace")
+    SUMMARIES = ("plan_dev", "k", "v", "g", "beta", "gate", "init", "dims", "transitions", "updates",
+                 "workspace")
     COMPOSE = ("plan_dev", "transitions", "updates", "dims", "carry")
-    CARRY = ("plan_dev", "q", "k", "v", "g", "beta", "init", "dims", "carry", "o", "fmt", "final",
+    CARRY = ("plan_dev", "q", "k", "v", "g", "beta", "gate", "init", "dims", "carry", "o", "fmt", "final",
              "workspace")
-    FORWARD = ("plan_dev", "q", "k", "v", "g", "beta", "init", "dims", "transitions", "updates", "carry",
-               "o", "fmt", "final", "workspace")
+    FORWARD = ("plan_dev", "q", "k", "v", "g", "beta", "gate", "init", "dims", "transitions", "updates",
+               "carry", "o", "fmt", "final", "workspace")
+    NOALLOC = ("plan_dev", "q", "k", "v", "g", "beta", "gate", "init", "dims", "transitions", "updates",
+               "carry", "o", "fmt", "final")
 
     def __init__(self, fn, order):
         self.fn, self.order = fn, order
 
-    def __call__(self, plan, H=2, K=128, V=128, h0=0, hn=None, fmt=0, **kw):
+    def __call__(self, plan, H=2, K=128, V=128, h0=0, hn=None, fmt=0, gate=float("-inf"), **kw):
         args = [None if plan is None else plan.handle]
         for name in self.order:
             if name == "dims":
                 args += [H, K, V, h0, H if hn is None else hn]
             elif name == "fmt":
                 args.append(fmt)
+            elif name == "gate":
+                args.append(gate)
             else:
                 default = None if name == "init" else _FAKE
                 args += [kw.get(name, default), kw.get(name + "_bytes", _BIG)]
@@ -207,6 +212,13 @@ def test_device_calls_validate_before_launch():
         # an unknown o format is refused before launch
         for fmt in (-1, 2, 7):
             assert c[name](plan, fmt=fmt) == -1, (name, fmt)
+    # the safe gate's bound: NaN or > 0 is refused (checked before the
+    # buffers: a misaligned buffer would otherwise give -5)
+    for name in ("summaries", "carry", "forward"):
+        for bad in (float("nan"), 0.5, float("inf")):
+            assert c[name](plan, gate=bad, k=_FAKE + 4) == -1, (name, bad)
+        for ok in (float("-inf"), 0.0, -3.0):
+            assert c[name](plan, gate=ok, k=_FAKE + 4) == -5, (name, ok)
     assert kda.lib().kda_last_hip_error() == 0
 
 

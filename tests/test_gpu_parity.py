@@ -395,3 +395,35 @@ def test_determinism_token_by_token_rerun():
     for o in outs[1:]:
         for key in o:
             assert torch.equal(o[key], outs[0][key]), key
+
+
+SAFE_GATE = [
+    # name, T, H, cu_seqlens, segments, gate scale, bound (nats)
+    ("bound_-0.5", 300, 2, [0, 37, 150, 151, 300], 4, 1.0, -0.5),
+    # gate x8 re-runs fragments without a bound; with -4.4 every chunk stays
+    # in the anchored form's range
+    ("bound_-4.4_gate_x8", 260, 2, [0, 90, 260], 3, 8.0, -4.4),
+    ("bound_0", 130, 1, [0, 130], 2, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,T,H,cu,S,gs,bound", SAFE_GATE, ids=[c[0] for c in SAFE_GATE])
+def test_safe_gate(name, T, H, cu, S, gs, bound):
+    """The safe gate: the recurrence runs on max(g, bound), against the
+    oracle's safe_gate of the same inputs."""
+    print(f"case {name}: T={T} H={H} S={S} bound={bound}", flush=True)
+    x = synth.make_inputs(T, H, 128, 128, seed=len(name) + T, cu_seqlens=cu, gate_scale=gs)
+    h0 = synth.initial_states(len(cu) - 1, H, 128, 128, seed=T + 1)
+    plan, out = pu.run_gpu(x, cu, S, h0=h0, gate_lower_bound=bound)
+    pu.compare(pu.gpu_numpy(out), pu.run_oracle(x, cu, plan, h0=h0, gate_lower_bound=bound), name)
+
+
+def test_safe_gate_below_every_g_changes_nothing():
+    """A bound below every g gives bitwise the results of no bound."""
+    T, H, cu, S = 200, 2, [0, 120, 200], 3
+    x = synth.make_inputs(T, H, 128, 128, seed=26, cu_seqlens=cu, gate_scale=0.5)
+    low = float(x["g"].float().min()) - 1.0
+    _, a = pu.run_gpu(x, cu, S)
+    _, b = pu.run_gpu(x, cu, S, gate_lower_bound=low)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key

@@ -105,12 +105,12 @@ def test_validation_under_sanitizers(driver, cu, S, H):
     it; BF16 o needs half the bytes."""
     need = _needs(cu, S, H)
     head = ["check", len(cu) - 1, S] + cu + [H]
-    lines = [" ".join(map(str, head + need + [0]))]
+    lines = [" ".join(map(str, head + need + [0, "-inf"]))]
     want = [(0, 0, 0)]
     for i in range(13):
         short = list(need)
         short[i] -= 1
-        lines.append(" ".join(map(str, head + short + [0])))
+        lines.append(" ".join(map(str, head + short + [0, "-inf"])))
         code = -8 if i == 12 else -9
         # which of (summaries, compose, carry) take buffer i
         takes = {0: (1, 1, 1), 1: (0, 0, 1), 2: (1, 0, 1), 3: (1, 0, 1), 4: (1, 0, 1), 5: (1, 0, 1),
@@ -119,11 +119,15 @@ def test_validation_under_sanitizers(driver, cu, S, H):
         want.append(tuple(code if t else 0 for t in takes))
     bf = list(need)
     bf[10] = need[10] // 2
-    lines.append(" ".join(map(str, head + bf + [1])))
+    lines.append(" ".join(map(str, head + bf + [1, "-inf"])))
     want.append((0, 0, 0))
     bf[10] -= 1
-    lines.append(" ".join(map(str, head + bf + [1])))
+    lines.append(" ".join(map(str, head + bf + [1, "-inf"])))
     want.append((0, 0, -9))
+    # the safe gate's bound: finite <= 0 passes, NaN and > 0 are refused
+    for bound, code in (("-4.4", 0), ("0", 0), ("nan", -1), ("0.25", -1)):
+        lines.append(" ".join(map(str, head + need + [0, bound])))
+        want.append((code, 0, code))
     out = _run(driver, lines)
     got = [tuple(int(w) for w in line.split()) for line in out]
     assert got == want

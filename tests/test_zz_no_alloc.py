@@ -48,5 +48,6 @@ def test_noalloc_refuses_workspace_beyond_fixed_array():
     plan = kda.Plan([0, 65536], 64)
     assert plan.workspace_bytes(32) > cap
     L = kda.lib()
-    args = [plan.handle, 16, 0] + [16, 0] * 6 + [32, 128, 128, 0, 32] + [16, 0] * 4 + [0] + [16, 0] + [None]
+    args = ([plan.handle, 16, 0] + [16, 0] * 5 + [float("-inf")] + [16, 0] + [32, 128, 128, 0, 32]
+            + [16, 0] * 4 + [0] + [16, 0] + [None])
     assert L.kda_forward_noalloc(*args) == -8
