@@ -30,7 +30,10 @@ fp64 throughout.
 Modules
 -------
 ``kda_oracle``  recurrence, segment summaries, ordered composition, segmented
-                reconstruction.
+                reconstruction, the optional safe gate; the backward:
+                gradients of q, k, v, g, beta and the initial states by a
+                reverse pass, the following summaries of each segment, their
+                reverse composition and the segmented reverse pass.
 ``plan_oracle`` the contiguous segment plan over packed sequences.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``

@@ -26,6 +26,10 @@ __all__ = [
     "compose_pair",
     "segmented_forward",
     "safe_gate",
+    "backward",
+    "backward_summaries",
+    "compose_backward",
+    "segmented_backward",
 ]
 
 
@@ -215,3 +219,156 @@ def segmented_forward(q, k, v, g, beta, cu_seqlens, bounds, C, h0=None):
             if t in ends:
                 final[ends[t]] = S
     return o, final
+
+
+# ----------------------------------------------------------------- backward
+#
+# The pages validate the forward and the gradients of q, k, v, g and beta
+# together ([cuLA#110] Correctness; [cuLA#136] Sequence Diagram: the backward
+# gathers the following ranks' summaries).  The loss is the pairing of the
+# forward's outputs with given cotangents,
+#     L = sum_t <o_t, do_t> + sum_n <final_n, dfinal_n>,
+# and the gradients are those of the recurrence as the forward defines it
+# (one token: decay, erase, write, read).
+
+
+def _step_parts(S_prev, k_t, v_t, g_t, beta_t):
+    """The intermediate values of one token (all heads): decayed state
+    S~ = Diag(exp g) S_prev, p = S~^T k, u = beta (v - p), S = S~ + k u^T."""
+    St = np.exp(g_t)[:, :, None] * S_prev
+    p = np.einsum("hk,hkv->hv", k_t, St)
+    u = beta_t[:, None] * (v_t - p)
+    S = St + k_t[:, :, None] * u[:, None, :]
+    return St, p, u, S
+
+
+def _token_backward(dS, S_prev, q_t, k_t, v_t, g_t, beta_t, do_t):
+    """Reverse one token.  dS is dL/dS_t from the later tokens; returns
+    (dL/dS_{t-1}, dq_t, dk_t, dv_t, dg_t, dbeta_t), each the chain rule through
+    o_t = S_t^T q_t, S_t = S~ + k u^T, u = beta (v - S~^T k), S~ = e^g o S_prev."""
+    St, p, u, S = _step_parts(S_prev, k_t, v_t, g_t, beta_t)
+    dS = dS + q_t[:, :, None] * do_t[:, None, :]                  # o_t = S_t^T q_t
+    dq = np.einsum("hkv,hv->hk", S, do_t)
+    du = np.einsum("hkv,hk->hv", dS, k_t)                          # S_t = S~ + k u^T
+    dk = np.einsum("hkv,hv->hk", dS, u)
+    dbeta = np.sum(du * (v_t - p), axis=-1)                        # u = beta (v - p)
+    dv = beta_t[:, None] * du
+    dp = -beta_t[:, None] * du
+    dSt = dS + k_t[:, :, None] * dp[:, None, :]                    # p = S~^T k
+    dk = dk + np.einsum("hkv,hv->hk", St, dp)
+    dg = np.sum(dSt * St, axis=-1)                                 # S~ = e^g o S_prev
+    dS_prev = np.exp(g_t)[:, :, None] * dSt
+    return dS_prev, dq, dk, dv, dg, dbeta
+
+
+def backward(q, k, v, g, beta, cu_seqlens, do, dfinal=None, h0=None):
+    """Gradients of L = sum <o, do> + sum <final, dfinal> for the monolithic
+    recurrence: one reverse pass per sequence over its forward states.
+
+    do: [T, H, V]; dfinal: [N, H, K, V] or None (zero); h0 as in recurrence.
+    Returns (dq, dk, dv, dg, dbeta, dh0) with the shapes of q, k, v, g, beta
+    and [N, H, K, V]."""
+    T, H, K = k.shape
+    V = v.shape[2]
+    N = len(cu_seqlens) - 1
+    dq, dk, dg = (np.zeros((T, H, K)) for _ in range(3))
+    dv = np.zeros((T, H, V))
+    dbeta = np.zeros((T, H))
+    dh0 = np.zeros((N, H, K, V))
+    for n in range(N):
+        bos, eos = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
+        S = np.zeros((H, K, V)) if h0 is None else np.array(h0[n], dtype=np.float64)
+        prev = []
+        for t in range(bos, eos):
+            prev.append(S)
+            S = _step_parts(S, k[t], v[t], g[t], beta[t])[3]
+        dS = np.zeros((H, K, V)) if dfinal is None else np.array(dfinal[n], dtype=np.float64)
+        for t in range(eos - 1, bos - 1, -1):
+            dS, dq[t], dk[t], dv[t], dg[t], dbeta[t] = _token_backward(
+                dS, prev[t - bos], q[t], k[t], v[t], g[t], beta[t], do[t])
+        dh0[n] = dS
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def backward_summaries(q, k, v, g, beta, cu_seqlens, bounds, do, dfinal=None, h0=None, C=None):
+    """The following summaries of the backward ([cuLA#136] Sequence Diagram:
+    the backward gathers the following ranks' summaries).  A segment maps the
+    gradient at its end, D (dL/dS at its last token, from the later tokens),
+    to the gradient at its start affinely: dL/dS_in = A_r^T D + E_r, with A_r
+    the segment's transition (forward) and E_r the gradient at its start from
+    its own outputs alone (D = 0).  E_r is taken over the segment's first
+    fragment, which starts from the carry-in C_r (the forward's state there;
+    zero for C=None); a sequence start inside the segment resets the state,
+    so gradients there do not reach S_in.  Returns E [R, H, K, V]."""
+    T, H, K = k.shape
+    V = v.shape[2]
+    starts = _seq_starts(cu_seqlens, T)
+    ends = {int(cu_seqlens[n + 1]) - 1: n for n in range(len(cu_seqlens) - 1)}
+    R = len(bounds) - 1
+    E = np.zeros((R, H, K, V))
+    for r in range(R):
+        b0, b1 = int(bounds[r]), int(bounds[r + 1])
+        if starts[b0]:
+            continue
+        # the first fragment: tokens b0 .. up to (not incl.) the next sequence start
+        f1 = b0 + 1
+        while f1 < b1 and not starts[f1]:
+            f1 += 1
+        S = np.zeros((H, K, V)) if C is None else np.array(C[r], dtype=np.float64)
+        prev = []
+        for t in range(b0, f1):
+            prev.append(S)
+            S = _step_parts(S, k[t], v[t], g[t], beta[t])[3]
+        dS = np.zeros((H, K, V))
+        if f1 - 1 in ends and dfinal is not None:
+            dS = np.array(dfinal[ends[f1 - 1]], dtype=np.float64)
+        for t in range(f1 - 1, b0 - 1, -1):
+            dS = _token_backward(dS, prev[t - b0], q[t], k[t], v[t], g[t], beta[t], do[t])[0]
+        E[r] = dS
+    return E
+
+
+def compose_backward(A, E):
+    """Reverse ordered scan of the backward summaries: D_{R-1} = 0 and
+    D_{r-1} = A_r^T D_r + E_r, the gradient at the end of segment r-1 from
+    every later token.  Returns D [R, H, K, V]."""
+    R = A.shape[0]
+    D = np.zeros_like(E)
+    for r in range(R - 1, 0, -1):
+        D[r - 1] = np.swapaxes(A[r], -1, -2) @ D[r] + E[r]
+    return D
+
+
+def segmented_backward(q, k, v, g, beta, cu_seqlens, bounds, do, D, C, dfinal=None, h0=None):
+    """Each segment's backward from D_r at its end and its forward from the
+    carry-in C_r (sequence starts reset to zero or h0[n]); the gradients that
+    reach a sequence's start go to dh0.  Returns what backward() returns."""
+    T, H, K = k.shape
+    V = v.shape[2]
+    N = len(cu_seqlens) - 1
+    starts = _seq_starts(cu_seqlens, T)
+    ends = {int(cu_seqlens[n + 1]) - 1: n for n in range(N)}
+    first = {int(cu_seqlens[n]): n for n in range(N)}
+    dq, dk, dg = (np.zeros((T, H, K)) for _ in range(3))
+    dv = np.zeros((T, H, V))
+    dbeta = np.zeros((T, H))
+    dh0 = np.zeros((N, H, K, V))
+    for r in range(len(bounds) - 1):
+        b0, b1 = int(bounds[r]), int(bounds[r + 1])
+        S = np.array(C[r], dtype=np.float64)
+        prev = []
+        for t in range(b0, b1):
+            if starts[t]:
+                S = _start_state(cu_seqlens, t, h0, (H, K, V))
+            prev.append(S)
+            S = _step_parts(S, k[t], v[t], g[t], beta[t])[3]
+        dS = np.array(D[r], dtype=np.float64)
+        for t in range(b1 - 1, b0 - 1, -1):
+            if t in ends and dfinal is not None:
+                dS = dS + dfinal[ends[t]]
+            dS, dq[t], dk[t], dv[t], dg[t], dbeta[t] = _token_backward(
+                dS, prev[t - b0], q[t], k[t], v[t], g[t], beta[t], do[t])
+            if starts[t]:
+                dh0[first[t]] = dS
+                dS = np.zeros((H, K, V))
+    return dq, dk, dv, dg, dbeta, dh0
