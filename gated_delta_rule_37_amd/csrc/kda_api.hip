@@ -15,6 +15,8 @@
 
 namespace {
 
+using kda::backward_workspace_need;
+using kda::check_backward;
 using kda::check_carry;
 using kda::check_compose;
 using kda::check_dims;
@@ -294,4 +296,56 @@ extern "C" int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev
                      beta_bytes, gate_lower_bound, initial_state, initial_state_bytes, H, K, V, head_begin, head_count,
                      transitions, transitions_bytes, updates, updates_bytes, carry_in, carry_in_bytes, o,
                      o_bytes, o_format, final_state, final_state_bytes, ws, kScratchBytes, stream);
+}
+
+extern "C" size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V) {
+  if (plan == nullptr || H <= 0 || K != 128 || V != 128) return 0;
+  return backward_workspace_need(plan, H);
+}
+
+extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                            const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                            const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                            const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                            size_t initial_state_bytes, const float* d_o, size_t d_o_bytes,
+                            const float* d_final, size_t d_final_bytes, int32_t H, int32_t K, int32_t V,
+                            int32_t head_begin, int32_t head_count, float* dq, size_t dq_bytes, float* dk,
+                            size_t dk_bytes, float* dv, size_t dv_bytes, float* dg, size_t dg_bytes,
+                            float* dbeta, size_t dbeta_bytes, float* d_initial_state,
+                            size_t d_initial_state_bytes, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const int st = check_backward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
+                                beta, beta_bytes, initial_state, initial_state_bytes, d_o, d_o_bytes, d_final,
+                                d_final_bytes, H, K, V, head_begin, head_count, dq, dq_bytes, dk, dk_bytes, dv,
+                                dv_bytes, dg, dg_bytes, dbeta, dbeta_bytes, d_initial_state,
+                                d_initial_state_bytes, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  const int64_t blocks = static_cast<int64_t>(plan->N) * head_count;
+  if (blocks > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  kda::BwdParams p{};
+  p.plan = plan_dev;
+  p.L = plan->layout;
+  p.H = H;
+  p.h0 = head_begin;
+  p.hn = head_count;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.h0s = initial_state;
+  p.d_o = d_o;
+  p.dfinal = d_final;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dg = dg;
+  p.dbeta = dbeta;
+  p.dh0 = d_initial_state;
+  p.ws = static_cast<float*>(workspace);
+  p.ckpt_floats = (static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->N)) * H * 128 * 128;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kda::kda_backward_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kda::kBwdThreads), 0,
+                     stream, p);
+  return finish_launch();
 }

@@ -62,7 +62,34 @@ struct ComposeParams {
   float* carry;
 };
 
+// Backward (kda_backward): one workgroup per (sequence, head).
+constexpr int kBwdThreads = 256;
+struct BwdParams {
+  const int32_t* plan;
+  BlobLayout L;
+  int32_t H;              // heads in the tensors
+  int32_t h0;             // heads [h0, h0 + hn) are this launch's
+  int32_t hn;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* h0s;       // initial states [N, H, K, V] or null (zero)
+  const float* d_o;       // dL/do [T, H, V]
+  const float* dfinal;    // dL/dfinal [N, H, K, V] or null (zero)
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;             // dL/dh0 [N, H, K, V] or null (not wanted)
+  float* ws;              // checkpoints, then the per-workgroup chunk buffers
+  size_t ckpt_floats;     // floats of the checkpoint part
+};
+
 __global__ void kda_chunk_kernel(ChunkParams p);
+__global__ void kda_backward_kernel(BwdParams p);
 __global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_compose_kernel(ComposeParams p);
 

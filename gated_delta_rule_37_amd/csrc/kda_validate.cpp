@@ -83,6 +83,13 @@ int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t
   return KDA_OK;
 }
 
+size_t backward_workspace_need(const kda_plan* plan, int32_t H) {
+  const size_t mat = size_t(128) * 128 * sizeof(float);
+  const size_t ckpt = (static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->N)) * H * mat;
+  const size_t cbuf = static_cast<size_t>(plan->N) * H * 32 * mat;
+  return ckpt + cbuf;
+}
+
 size_t workspace_need(const kda_plan* plan, int32_t H) {
   const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
   return slots * static_cast<size_t>(H) * kChunkCacheBytes;
@@ -162,6 +169,44 @@ int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_b
                       {final_state, final_state_bytes, z.state_n, false}});
   if (st != KDA_OK) return st;
   return check_workspace(workspace, workspace_bytes, plan, H);
+}
+
+int check_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                   const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                   const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                   const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                   size_t initial_state_bytes, const float* d_o, size_t d_o_bytes, const float* d_final,
+                   size_t d_final_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                   int32_t head_count, const float* dq, size_t dq_bytes, const float* dk, size_t dk_bytes,
+                   const float* dv, size_t dv_bytes, const float* dg, size_t dg_bytes, const float* dbeta,
+                   size_t dbeta_bytes, const float* d_initial_state, size_t d_initial_state_bytes,
+                   const void* workspace, size_t workspace_bytes) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  st = check_heads(H, head_begin, head_count);
+  if (st != KDA_OK) return st;
+  const Sizes z = sizes_of(plan, H);
+  const size_t f32_tk = z.qkg * 2;   // [T, H, 128] fp32
+  st = check_buffers({{plan_dev, plan_dev_bytes, z.plan_dev, false},
+                      {q, q_bytes, z.qkg, false},
+                      {k, k_bytes, z.qkg, false},
+                      {v, v_bytes, z.v, false},
+                      {g, g_bytes, z.qkg, false},
+                      {beta, beta_bytes, z.beta, false},
+                      {initial_state, initial_state_bytes, z.state_n, true},
+                      {d_o, d_o_bytes, f32_tk, false},
+                      {d_final, d_final_bytes, z.state_n, true},
+                      {dq, dq_bytes, f32_tk, false},
+                      {dk, dk_bytes, f32_tk, false},
+                      {dv, dv_bytes, f32_tk, false},
+                      {dg, dg_bytes, f32_tk, false},
+                      {dbeta, dbeta_bytes, z.beta * 2, false},
+                      {d_initial_state, d_initial_state_bytes, z.state_n, true}});
+  if (st != KDA_OK) return st;
+  if (workspace == nullptr) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+  if (workspace_bytes < backward_workspace_need(plan, H)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  return KDA_OK;
 }
 
 }  // namespace kda

@@ -14,6 +14,10 @@ namespace kda {
 // Bytes of the workspace (the chunk cache) a plan needs for H heads.
 size_t workspace_need(const kda_plan* plan, int32_t H);
 
+// Bytes of the backward's workspace for H heads: a state checkpoint per
+// 32-token chunk of every sequence, plus 32 states per (sequence, head).
+size_t backward_workspace_need(const kda_plan* plan, int32_t H);
+
 // Plan, plan_dev and dimensions (K = V = 128, 0 < H <= 65535).
 int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t K, int32_t V);
 
@@ -41,6 +45,17 @@ int check_carry(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_b
                 int32_t V, int32_t head_begin, int32_t head_count, const float* carry_in, size_t carry_in_bytes, const void* o,
                 size_t o_bytes, int32_t o_format, const float* final_state, size_t final_state_bytes,
                 const void* workspace, size_t workspace_bytes);
+
+int check_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                   const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                   const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                   const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                   size_t initial_state_bytes, const float* d_o, size_t d_o_bytes, const float* d_final,
+                   size_t d_final_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                   int32_t head_count, const float* dq, size_t dq_bytes, const float* dk, size_t dk_bytes,
+                   const float* dv, size_t dv_bytes, const float* dg, size_t dg_bytes, const float* dbeta,
+                   size_t dbeta_bytes, const float* d_initial_state, size_t d_initial_state_bytes,
+                   const void* workspace, size_t workspace_bytes);
 
 }  // namespace kda
 

@@ -14,6 +14,7 @@ Entry points mirror the C names:
 * :func:`forward_call` (``kda_forward``): the three device calls in one C call
 * :func:`forward_noalloc` (``kda_forward_noalloc``): the same without a
   caller workspace (the library's fixed per-GPU array instead)
+* :func:`backward` (``kda_backward``): gradients of q, k, v, g, beta, h0
 * :func:`forward` runs the three device calls in order (optionally per head
   group, with the compose launches on a second stream) on fresh output buffers.
 
@@ -49,7 +50,7 @@ SYMBOLS = (
     "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
     "kda_summary_bytes", "kda_workspace_bytes", "kda_segment_summaries", "kda_compose_summaries",
     "kda_apply_carry", "kda_forward", "kda_forward_noalloc", "kda_noalloc_max_workspace_bytes",
-    "kda_status_string", "kda_last_hip_error",
+    "kda_backward", "kda_backward_workspace_bytes", "kda_status_string", "kda_last_hip_error",
 )
 
 
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
     L.kda_forward.restype = ctypes.c_int
     L.kda_forward_noalloc.argtypes = [p, *buf, *buf * 5, f32, *buf, *dims, *buf, *buf, *buf, *buf, i32, *buf, p]
     L.kda_forward_noalloc.restype = ctypes.c_int
+    L.kda_backward.argtypes = [p, *buf, *buf * 5, *buf, *buf, *buf, *dims, *buf * 6, *buf, p]
+    L.kda_backward.restype = ctypes.c_int
+    L.kda_backward_workspace_bytes.argtypes = [p, i32, i32, i32]
+    L.kda_backward_workspace_bytes.restype = sz
     L.kda_noalloc_max_workspace_bytes.argtypes = []
     L.kda_noalloc_max_workspace_bytes.restype = sz
     L.kda_status_string.argtypes = [ctypes.c_int]
@@ -317,6 +322,40 @@ def forward_noalloc(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, s
     st = lib().kda_forward_noalloc(plan.handle, *_plan_dev(plan, plan_dev), *ins, H, K, V, *_heads(H, heads),
                                    *summ, *ob, fmt, *ff, _stream(q, stream))
     _check(st, "kda_forward_noalloc")
+
+
+def backward(plan: Plan, q, k, v, g, beta, d_o, d_final=None, initial_state=None, want_dh0=False,
+             stream=None, heads=None):
+    """``kda_backward``: gradients of L = sum <o, d_o> + sum <final, d_final>.
+    Returns dict(dq, dk, dv, dg, dbeta, dh0) (fp32; dh0 None unless wanted)."""
+    T, H, K = k.shape
+    V = v.shape[2]
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty(T, H, K, **f32), dk=torch.empty(T, H, K, **f32),
+               dv=torch.empty(T, H, V, **f32), dg=torch.empty(T, H, K, **f32),
+               dbeta=torch.empty(T, H, **f32),
+               dh0=torch.empty(plan.N, H, K, V, **f32) if want_dh0 else None)
+    ins = _flat([
+        _buf(q, torch.bfloat16, (T, H, K), "q"), _buf(k, torch.bfloat16, (T, H, K), "k"),
+        _buf(v, torch.bfloat16, (T, H, V), "v"), _buf(g, torch.bfloat16, (T, H, K), "g"),
+        _buf(beta, torch.bfloat16, (T, H), "beta"),
+        _buf(initial_state, torch.float32, (plan.N, H, K, V), "initial_state"),
+        _buf(d_o, torch.float32, (T, H, V), "d_o"),
+        _buf(d_final, torch.float32, (plan.N, H, K, V), "d_final"),
+    ])
+    grads = _flat([
+        _buf(out["dq"], torch.float32, None, "dq"), _buf(out["dk"], torch.float32, None, "dk"),
+        _buf(out["dv"], torch.float32, None, "dv"), _buf(out["dg"], torch.float32, None, "dg"),
+        _buf(out["dbeta"], torch.float32, None, "dbeta"), _buf(out["dh0"], torch.float32, None, "dh0"),
+    ])
+    ws_bytes = int(lib().kda_backward_workspace_bytes(plan.handle, H, K, V))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib().kda_backward(plan.handle, *_plan_dev(plan, plan.device_blob(dev)), *ins, H, K, V,
+                            *_heads(H, heads), *grads, *_buf(ws, torch.uint8, None, "workspace"),
+                            _stream(q, stream))
+    _check(st, "kda_backward")
+    return out
 
 
 def noalloc_max_workspace_bytes() -> int:

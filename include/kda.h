@@ -330,6 +330,39 @@ int kda_forward_noalloc(const kda_plan* plan, const int32_t* plan_dev, size_t pl
 /* Bytes of the fixed workspace array kda_forward_noalloc uses on each GPU. */
 size_t kda_noalloc_max_workspace_bytes(void);
 
+/*
+ * kda_backward -- gradients of the recurrence (#110 Correctness: output and
+ * Q/K/V/g/beta gradients; #136 Sequence Diagram: the backward of the CP
+ * forward).  For the loss
+ *     L = sum_t <o_t, d_o_t> + sum_n <final_n, d_final_n>
+ * of the forward over the same plan, inputs and initial states, it writes
+ *   dq, dk, dg  [T, H, K] fp32    dv [T, H, V] fp32    dbeta [T, H] fp32
+ *   d_initial_state [N, H, K, V] fp32 (optional: NULL when not wanted)
+ * d_o [T, H, V] fp32 is required, d_final [N, H, K, V] fp32 optional (NULL =
+ * zero).  g is the log-decay as given (no safe gate).  Every sequence and
+ * head is reversed in FP32, one token at a time from state checkpoints taken
+ * every 32 tokens; workspace: kda_backward_workspace_bytes(plan, H, K, V)
+ * bytes, caller-owned, contents not needed afterwards.  Arguments, sizes and
+ * errors as for the forward's device calls (each buffer with its byte count).
+ */
+int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                 const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                 const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                 const uint16_t* beta, size_t beta_bytes,
+                 const float* initial_state, size_t initial_state_bytes,
+                 const float* d_o, size_t d_o_bytes, const float* d_final, size_t d_final_bytes,
+                 int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                 float* dq, size_t dq_bytes, float* dk, size_t dk_bytes,
+                 float* dv, size_t dv_bytes, float* dg, size_t dg_bytes,
+                 float* dbeta, size_t dbeta_bytes,
+                 float* d_initial_state, size_t d_initial_state_bytes,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of kda_backward's workspace: (ceil(T/32) + N) * H state checkpoints
+ * plus 32 states per (sequence, head), 64 KiB each.  0 for a NULL plan,
+ * H <= 0 or K, V other than 128. */
+size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
+
 /* Human-readable name of a kda_status value. */
 const char* kda_status_string(int status);
 

@@ -278,3 +278,40 @@ def test_plan_info_and_null_handling():
     out = ctypes.c_void_p()
     assert L.kda_plan_segments(None, 1, 1, None, ctypes.byref(out)) == -1
     L.kda_plan_destroy(None)
+
+
+def test_backward_validates_before_launch():
+    """kda_backward refuses bad arguments with the documented codes (fake,
+    never dereferenced buffers; every call below fails a check)."""
+    L = kda.lib()
+    plan = kda.Plan([0, 70, 100], 2)
+    H = 2
+    T, N = 100, 2
+    need = dict(plan_dev=4 * len(plan.blob), q=T * H * 256, k=T * H * 256, v=T * H * 256, g=T * H * 256,
+                beta=T * H * 2, init=N * H * 65536, do=T * H * 512, dfinal=N * H * 65536, dq=T * H * 512,
+                dk=T * H * 512, dv=T * H * 512, dg=T * H * 512, dbeta=T * H * 4, dh0=N * H * 65536,
+                ws=L.kda_backward_workspace_bytes(plan.handle, H, 128, 128))
+    assert need["ws"] == ((100 + 31) // 32 + 2) * H * 65536 + 2 * H * 32 * 65536
+    order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "dq", "dk", "dv", "dg", "dbeta",
+             "dh0", "ws")
+
+    def call(H=H, K=128, **over):
+        args = [plan.handle]
+        for name in order:
+            if name == "dq":
+                args += [H, K, 128, 0, H]
+            args += [over.get(name, _FAKE), over.get(name + "_bytes", need[name])]
+        args.append(None)
+        return L.kda_backward(*args)
+
+    assert call(K=64) == -4
+    assert call(do=0) == -1
+    assert call(dq=_FAKE + 4) == -5
+    assert call(ws=0) == -1
+    for name in order:
+        short = {name + "_bytes": need[name] - 1, "q": _FAKE + 4} if name == "q" else {name + "_bytes": need[name] - 1}
+        if name == "q":
+            continue
+        want = -8 if name == "ws" else -9
+        assert call(**short) == want, name
+    assert L.kda_last_hip_error() == 0
