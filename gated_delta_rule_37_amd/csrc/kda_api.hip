@@ -314,14 +314,31 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
                             float* dbeta, size_t dbeta_bytes, float* d_initial_state,
                             size_t d_initial_state_bytes, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  const int st = check_backward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
+  int st = check_backward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
                                 beta, beta_bytes, initial_state, initial_state_bytes, d_o, d_o_bytes, d_final,
                                 d_final_bytes, H, K, V, head_begin, head_count, dq, dq_bytes, dk, dk_bytes, dv,
                                 dv_bytes, dg, dg_bytes, dbeta, dbeta_bytes, d_initial_state,
                                 d_initial_state_bytes, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
-  const int64_t blocks = static_cast<int64_t>(plan->N) * head_count;
-  if (blocks > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  dim3 unused;
+  st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &unused);
+  if (st != KDA_OK) return st;
+  const int64_t seg_blocks = static_cast<int64_t>(plan->S) * head_count;
+  const int64_t items = static_cast<int64_t>(plan->F) * head_count;
+  if (seg_blocks > 2147483647LL || items > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  const kda::BwdLayout W = kda::backward_layout(plan, H);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* transitions = reinterpret_cast<float*>(ws + W.transitions);
+  float* updates = reinterpret_cast<float*>(ws + W.updates);
+  float* carry = reinterpret_cast<float*>(ws + W.carry);
+  float* esum = reinterpret_cast<float*>(ws + W.esum);
+  float* dcarry = reinterpret_cast<float*>(ws + W.dcarry);
+  // the forward's summaries and carry-ins, without the safe gate
+  st = launch_summaries(plan, plan_dev, k, v, g, beta, -INFINITY, initial_state, H, head_begin, head_count,
+                        transitions, updates, ws + W.cache, stream);
+  if (st != KDA_OK) return st;
+  st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream);
+  if (st != KDA_OK) return st;
   kda::BwdParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -336,16 +353,39 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.h0s = initial_state;
   p.d_o = d_o;
   p.dfinal = d_final;
+  p.carry = carry;
+  p.esum = esum;
+  p.dcarry = dcarry;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
   p.dg = dg;
   p.dbeta = dbeta;
   p.dh0 = d_initial_state;
-  p.ws = static_cast<float*>(workspace);
-  p.ckpt_floats = (static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->N)) * H * 128 * 128;
+  p.ckpt = reinterpret_cast<float*>(ws + W.ckpt);
+  p.scratch = reinterpret_cast<float*>(ws + W.scratch);
+  // E_r, then D_r = the reverse scan of (A^T, E), then every fragment
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_backward_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kda::kBwdThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL(kda::kda_backward_summary_kernel, dim3(static_cast<uint32_t>(seg_blocks)),
+                     dim3(kda::kBwdThreads), 0, stream, p);
+  st = finish_launch();
+  if (st != KDA_OK) return st;
+  kda::ComposeParams c{};
+  c.plan = plan_dev;
+  c.L = plan->layout;
+  c.H = H;
+  c.h0 = head_begin;
+  c.hn = head_count;
+  c.S = plan->S;
+  c.transitions = transitions;
+  c.updates = esum;
+  c.carry = dcarry;
+  const int cblocks = ((head_count + 7) / 8) * 8 * kda::kComposeColumnBlocks;
+  hipLaunchKernelGGL(kda::kda_compose_reverse_kernel, dim3(cblocks), dim3(kda::kComposeThreads), 0, stream, c);
+  st = finish_launch();
+  if (st != KDA_OK) return st;
+  const int64_t grid = items < kda::kBwdGrid ? items : kda::kBwdGrid;
+  hipLaunchKernelGGL(kda::kda_backward_fragment_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),
+                     0, stream, p);
   return finish_launch();
 }

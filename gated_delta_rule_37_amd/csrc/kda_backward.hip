@@ -4,7 +4,7 @@
 // inclusionAI/cuLA pull request #110 "feat(cp): add opt-in NVSHMEM CP state
 // handoff" (Correctness: output and Q/K/V/g/beta gradients are validated) and
 // pull request #136 "feat(kda): add cuDNN concatenated-summary Kimi CP"
-// (Sequence Diagram: the backward pass of the context-parallel KDA).
+// (Sequence Diagram: the backward gathers the following ranks' summaries).
 //
 // Per token, with S~ = Diag(e^g) S_{t-1}, p = S~^T k, u = beta (v - p),
 // S_t = S~ + k u^T and o_t = S_t^T q, the reverse step from dS = dL/dS_t is
@@ -12,12 +12,25 @@
 //     dq   = S_t do,  du = dS^T k,  dv = beta du,  dbeta = <du, v - p>
 //     dp   = -beta du,  dk = dS u + S~ dp
 //     dS~  = dS + k dp^T,  dg = rowsum(dS~ o S~),  dS_{t-1} = Diag(e^g) dS~.
-// One workgroup runs one (sequence, head) in FP32, token by token: a forward
-// sweep keeps the state at the start of every 32-token chunk, and the reverse
-// sweep recomputes each chunk's per-token states from its checkpoint into a
-// per-workgroup buffer before walking its tokens backwards.  The state and its
-// cotangent live in LDS as 128 x 128 FP32 tiles; products over rows use one
-// thread per column, products over columns one thread per row.
+// The cotangent recursion does not involve the state, so a segment maps the
+// cotangent at its end, D, to the one at its start affinely: A_r^T D + E_r.
+// The segments therefore run in parallel, as in the forward:
+//   kda_backward_summary_kernel   E_r: the first fragment of every carried
+//                                 segment reversed from its own outputs only;
+//   (reverse compose)             D_{r-1} = A_r^T D_r + E_r;
+//   kda_backward_fragment_kernel  every (fragment, head): forward from its
+//                                 carry-in C_r (or initial state), reverse
+//                                 from D_r (and dfinal at a sequence end).
+//
+// Layout: a 1024-thread workgroup holds a 128 x 128 state in registers,
+// thread (c, grp) = (tid % 128, tid / 128) owning column c of rows
+// [16 grp, 16 grp + 16).  Sums over rows (p, du) go through one LDS exchange
+// of eight partials; sums over columns (dq, dk, dg) are reduced within each
+// wave by a transposing butterfly (lane-swap and DPP moves) and across the
+// two waves of a row group through LDS.  The fragment kernel keeps the state
+// every 32 tokens in global memory (level 1), recomputes a chunk's states
+// every 4 tokens into its workgroup's scratch (level 2), and each 4-token
+// group's per-token states in registers before walking it backwards.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -28,195 +41,554 @@
 namespace kda {
 namespace {
 
-constexpr int BD = 128;          // key = value dimension
-constexpr int BS = BD + 1;       // LDS row stride (floats): row and column walks are conflict-free
-constexpr int BCH = 32;          // tokens per checkpointed chunk
+constexpr int BD = 128;               // key = value dimension
+constexpr int NT = kBwdThreads;       // 1024
+constexpr int NGRP = NT / BD;         // row groups: 8
+constexpr int NR = BD / NGRP;         // rows per thread: 16
+constexpr int GT = 4;                 // tokens per register group
+constexpr int CK = kBwdCheckpointTokens;   // tokens per level-1 checkpoint: 32
+constexpr int GPC = CK / GT;          // groups per checkpoint chunk: 8
+constexpr size_t MAT = static_cast<size_t>(BD) * BD;
 constexpr float kLog2eB = 1.4426950408889634f;
+static_assert(NR == 16 && NT == 1024, "backward layout: 16 rows per thread, 16 waves");
 
-struct alignas(16) BwdSmem {
-  float S[BD * BS];       // S_{t-1} (the forward sweep: the running state)
-  float dS[BD * BS];      // dL/dS_t
-  float q[BD], k[BD], dec[BD], v[BD], dov[BD];
-  float p[BD], u[BD], du[BD], dp[BD];
-  float part[2][BD];      // partial sums of the two halves
-  float part2[2][BD];
-  float part3[2][BD];
-  float beta;
-  float red[4];
+// One group of up to four tokens' vectors.
+struct alignas(16) TokGroup {
+  float k[GT][BD];
+  float dec[GT][BD];   // e^g
+  float kd[GT][BD];    // k e^g
+  float q[GT][BD];
+  float v[GT][BD];
+  float dov[GT][BD];
+  float beta[GT];
 };
 
-__device__ __forceinline__ float bfv(const uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+struct alignas(16) BwdSmem {
+  TokGroup tg[2];                 // by group parity
+  float colpart[2][NGRP][BD];     // row-sum partials, by exchange parity
+  float rowpart[4][2][BD];        // column sums of the two waves of a row group
+  float red[2];                   // dbeta: the sums of waves 0 and 1
+};
 
-// Sequence n's token range from the plan blob: its fragments are consecutive
-// (frag_seq does not decrease), the first begins it and the last ends it.
-__device__ __forceinline__ void seq_bounds(const BwdParams& p, const int n, int32_t& bos, int32_t& eos) {
-  const int32_t F = p.plan[3];
-  const int32_t* fs = p.plan + p.L.frag_seq;
-  int lo = 0, hi = F;   // first f with frag_seq[f] >= n
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (fs[mid] < n) lo = mid + 1;
-    else hi = mid;
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4 l4(const float* src) { return *reinterpret_cast<const f4*>(src); }
+
+__device__ __forceinline__ float bfv(const uint32_t b) { return __uint_as_float(b << 16); }
+
+// Raw buffer resources: a uniform base and byte count in scalar registers,
+// 32-bit per-lane offsets; accesses at or past the count read zero and drop
+// writes (buffer word 3 of gfx9 raw, unswizzled 32-bit access).
+constexpr int kBufWord3 = 0x00020000;
+using Rsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ Rsrc rsrc(const void* base, const uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+
+// A group's loads, in registers between their issue and their store to LDS.
+// Waves 0-1 load k and g, waves 2-3 q and v (4 bf16 of each per lane), waves
+// 4-5 d_o (4 floats), lanes 0-3 of wave 6 beta; bits 5-6 of tid select the
+// token m of the group, and a token past the group's n reads zero.
+struct Fetch {
+  u2 a, b;
+  f4 f;
+  uint32_t beta;
+};
+
+__device__ __forceinline__ void fetch_group(const BwdParams& p, const int h, const int t0, const int n, const int tid,
+                                            const int wave, Fetch& x) {
+  const int H = p.H;
+  const size_t tok0 = static_cast<size_t>(t0) * H + h;
+  const int m = (tid >> 5) & 3;
+  if (wave < 4) {
+    const uint32_t row = static_cast<uint32_t>(H) * BD * 2;
+    const uint32_t nrec = (n - 1) * row + BD * 2;
+    const bool kg = wave < 2;
+    const Rsrc ra = rsrc((kg ? p.k : p.q) + tok0 * BD, nrec);
+    const Rsrc rb = rsrc((kg ? p.g : p.v) + tok0 * BD, nrec);
+    const int off = m * row + 8 * (tid & 31);
+    x.a = __builtin_amdgcn_raw_buffer_load_b64(ra, off, 0, 0);
+    x.b = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+  } else if (wave < 6) {
+    const uint32_t row = static_cast<uint32_t>(H) * BD * 4;
+    const Rsrc rd = rsrc(p.d_o + tok0 * BD, (n - 1) * row + BD * 4);
+    x.f = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rd, m * row + 16 * (tid & 31), 0, 0));
+  } else if (wave == 6) {
+    const uint32_t nb = (n - 1) * H * 2 + 2;
+    const int lane = tid & 63;
+    x.beta = __builtin_amdgcn_raw_buffer_load_b16(rsrc(p.beta + tok0, nb), lane < GT ? lane * H * 2 : nb, 0, 0);
   }
-  int lo2 = lo, hi2 = F;   // first f with frag_seq[f] > n
-  while (lo2 < hi2) {
-    const int mid = (lo2 + hi2) >> 1;
-    if (fs[mid] <= n) lo2 = mid + 1;
-    else hi2 = mid;
+}
+
+__device__ __forceinline__ void store_group(TokGroup& tg, const int n, const int tid, const int wave, const Fetch& x) {
+  const int m = (tid >> 5) & 3;
+  if (wave < 4) {
+    if (m >= n) return;
+    const int e = 4 * (tid & 31);
+    const uint32_t wa[4] = {x.a[0] & 0xffffu, x.a[0] >> 16, x.a[1] & 0xffffu, x.a[1] >> 16};
+    const uint32_t wb[4] = {x.b[0] & 0xffffu, x.b[0] >> 16, x.b[1] & 0xffffu, x.b[1] >> 16};
+    if (wave < 2) {
+      f4 kk, dc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kk[j] = bfv(wa[j]);
+        dc[j] = __builtin_amdgcn_exp2f(bfv(wb[j]) * kLog2eB);
+      }
+      *reinterpret_cast<f4*>(&tg.k[m][e]) = kk;
+      *reinterpret_cast<f4*>(&tg.dec[m][e]) = dc;
+      *reinterpret_cast<f4*>(&tg.kd[m][e]) = kk * dc;
+    } else {
+      f4 qq, vv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qq[j] = bfv(wa[j]);
+        vv[j] = bfv(wb[j]);
+      }
+      *reinterpret_cast<f4*>(&tg.q[m][e]) = qq;
+      *reinterpret_cast<f4*>(&tg.v[m][e]) = vv;
+    }
+  } else if (wave < 6) {
+    if (m < n) *reinterpret_cast<f4*>(&tg.dov[m][4 * (tid & 31)]) = x.f;
+  } else if (wave == 6) {
+    const int lane = tid & 63;
+    if (lane < n) tg.beta[lane] = bfv(x.beta);
   }
-  bos = p.plan[p.L.frag_begin + lo];
-  eos = p.plan[p.L.frag_end + lo2 - 1];
+}
+
+// Keeps the scheduler from hoisting the LDS row loads of later 4-row slices
+// (with 16 waves per CU the load latency is hidden by the other waves; the
+// registers are not).
+__device__ __forceinline__ void slice_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(const float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Transposing butterfly: val(i) gives this lane's term of value i (16
+// values, summed over the wave's 64 lanes).  Returns the full sum of value
+// ridx(lane) = 8 b5 + 4 b4 + 2 b2 + b3 (b = the lane's bits); the four lanes
+// that differ in bits 0-1 return the same value.  Each stage pairs lanes that
+// still hold the same values and keeps half of them: lane bit 5 (rows of 32
+// swapped), bit 4 (rows of 16 swapped), bit 2 (mirror within 8 lanes, which
+// also flips bits 0-1), bit 3 (rotation by 8 within 16); then all-reduces
+// over bits 0 and 1.  The flips generate all 64 lanes, each counted once.
+// Values i and i + 8 are made together and folded at once.
+__device__ __forceinline__ int ridx(const int lane) {
+  return 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
+}
+
+template <typename Val>
+__device__ __forceinline__ float wave_rows_reduce(Val&& val, const int lane) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float lo = val(j), hi = val(j + 8);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + 4]), false, false);
+    x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b2 = (lane & 4) != 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float a = x[j] + dpp<0x141>(x[j]);          // row_half_mirror
+    const float b = x[j + 2] + dpp<0x141>(x[j + 2]);
+    x[j] = b2 ? b : a;
+  }
+  const float a = x[0] + dpp<0x128>(x[0]);            // row_ror:8
+  const float b = x[1] + dpp<0x128>(x[1]);
+  float y = (lane & 8) ? b : a;
+  y += dpp<0xB1>(y);                                  // quad_perm [1,0,3,2]
+  y += dpp<0x4E>(y);                                  // quad_perm [2,3,0,1]
+  return y;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// The thread's 16 elements of a [128][128] FP32 state at a uniform base:
+// rows 16 grp + i, column c, i.e. byte offset voff + 512 i with
+// voff = 4 (2048 grp + c).
+__device__ __forceinline__ void load_state(const float* src, const int voff, float (&s)[NR]) {
+  if (src == nullptr) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) s[i] = 0.f;
+    return;
+  }
+  const Rsrc r = rsrc(src, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) s[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, i * 512, 0));
+}
+__device__ __forceinline__ void add_state(const float* src, const int voff, float (&s)[NR]) {
+  const Rsrc r = rsrc(src, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) s[i] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, i * 512, 0));
+}
+__device__ __forceinline__ void store_state(float* dst, const int voff, const float (&s)[NR]) {
+  const Rsrc r = rsrc(dst, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[i]), r, voff, i * 512, 0);
+}
+// Checkpoints in the workgroup's own order: thread tid's 16 elements are
+// contiguous at byte 64 tid (four 16-byte accesses).
+__device__ __forceinline__ void put_ckpt(float* dst, const int tid, const float (&s)[NR]) {
+  const Rsrc r = rsrc(dst, MAT * 4);
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(u4, f4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]}), r, 4 * NR * tid, 16 * j, 0);
+}
+__device__ __forceinline__ void get_ckpt(const float* src, const int tid, float (&s)[NR]) {
+  const Rsrc r = rsrc(src, MAT * 4);
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 t = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * NR * tid, 16 * j, 0));
+    s[4 * j] = t[0];
+    s[4 * j + 1] = t[1];
+    s[4 * j + 2] = t[2];
+    s[4 * j + 3] = t[3];
+  }
+}
+
+// Per-thread context shared by both kernels.
+struct Ctx {
+  BwdSmem& sm;
+  int tid, c, grp, lane, wave;   // grp and wave are wave-uniform
+  int voff;  // byte offset of the thread's first state element, 4 (NR BD grp + c)
+  int par;   // colpart parity
+  int gb;    // token-group buffer parity
+
+  __device__ Ctx(BwdSmem& s, const int t)
+      : sm(s), tid(t), c(t & (BD - 1)), grp(__builtin_amdgcn_readfirstlane(t >> 7)), lane(t & 63),
+        wave(__builtin_amdgcn_readfirstlane(t >> 6)), voff(4 * (NR * BD * (t >> 7) + (t & (BD - 1)))), par(0),
+        gb(0) {}
+
+  // sum over all 128 rows of the column partials (one per row group)
+  __device__ __forceinline__ float col_sum(const float part) {
+    float* cp = &sm.colpart[par][0][0];
+    cp[grp * BD + c] = part;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) s += cp[g * BD + c];
+    par ^= 1;
+    return s;
+  }
+};
+
+// One forward step of token m of the group: p and u of column c from
+// S = S_{t-1}; with upd (uniform), S <- S_t.  Row vectors are read from LDS
+// four at a time (broadcast reads), not held.
+__device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, const int m, const float u,
+                                            float (&s)[NR]) {
+  const int r0 = NR * x.grp;
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
+    const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[4 * j + e] = fmaf(dc[e], s[4 * j + e], kk[e] * u);
+    slice_fence();
+  }
+}
+
+__device__ __forceinline__ void fwd_step(Ctx& x, const TokGroup& tg, const int m, float (&s)[NR], float& u,
+                                         float& pp, const bool upd) {
+  const int r0 = NR * x.grp;
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 kd = l4(&tg.kd[m][r0 + 4 * j]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part = fmaf(kd[e], s[4 * j + e], part);
+    slice_fence();
+  }
+  pp = x.col_sum(part);
+  u = tg.beta[m] * (tg.v[m][x.c] - pp);
+  if (upd) update_only(x, tg, m, u, s);
+}
+
+// dS += q do^T for this thread's elements; returns its partial of du = dS^T k.
+__device__ __forceinline__ float add_qdo(const Ctx& x, const TokGroup& tg, const int m, const float doc,
+                                        float (&ds)[NR]) {
+  const int r0 = NR * x.grp;
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 qq = l4(&tg.q[m][r0 + 4 * j]);
+    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ds[4 * j + e] = fmaf(qq[e], doc, ds[4 * j + e]);
+      part = fmaf(ds[4 * j + e], kk[e], part);
+    }
+    slice_fence();
+  }
+  return part;
+}
+
+// dS_{t-1} = Diag(e^g) (dS + k dp^T)
+__device__ __forceinline__ void cotangent_step(const Ctx& x, const TokGroup& tg, const int m, const float dp,
+                                               float (&ds)[NR]) {
+  const int r0 = NR * x.grp;
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
+    const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ds[4 * j + e] = dc[e] * fmaf(kk[e], dp, ds[4 * j + e]);
+    slice_fence();
+  }
+}
+
+// The cotangent-only reverse step (no gradients written): dS <- dS_{t-1}.
+__device__ __forceinline__ void rev_cotangent(Ctx& x, const TokGroup& tg, const int m, float (&ds)[NR]) {
+  const float du = x.col_sum(add_qdo(x, tg, m, tg.dov[m][x.c], ds));
+  cotangent_step(x, tg, m, -tg.beta[m] * du, ds);
+}
+
+// The full reverse step of token m (global index t) from S_{t-1} = st, with
+// u and p of column c from the forward step: writes the token's gradients.
+__device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
+                                         const int t, const float (&st)[NR], float (&ds)[NR], const float u,
+                                         const float pp) {
+  const int H = p.H;
+  const size_t tk = static_cast<size_t>(t) * H + h;
+  const int r0 = NR * x.grp;
+  const float doc = tg.dov[m][x.c];
+  const float beta = tg.beta[m];
+  const float du = x.col_sum(add_qdo(x, tg, m, doc, ds));
+  const float dp = -beta * du;
+  if (x.wave < 2) {   // row group 0 (tid < 128, a wave-uniform test): dv, and the terms of dbeta
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.c, 0, 0);
+    const float s = wave_sum(du * (tg.v[m][x.c] - pp));
+    if (x.lane == 0) x.sm.red[x.wave] = s;
+  }
+  // column sums of four row quantities; lanes with bits 0-1 clear publish
+  const int half = x.wave & 1;
+  const bool pub = (x.lane & 3) == 0;
+  const int row = NR * x.grp + ridx(x.lane);
+  const float* krow = &tg.k[m][r0];
+  const float* drow = &tg.dec[m][r0];
+  const float q0 = wave_rows_reduce(                                         // S_t do
+      [&](const int i) { return fmaf(drow[i], st[i], krow[i] * u) * doc; }, x.lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const float q1 = wave_rows_reduce([&](const int i) { return ds[i] * u; }, x.lane);        // dS u
+  __builtin_amdgcn_sched_barrier(0);
+  const float q2 = wave_rows_reduce([&](const int i) { return st[i] * dp; }, x.lane);       // S dp
+  __builtin_amdgcn_sched_barrier(0);
+  const float q3 = wave_rows_reduce([&](const int i) { return ds[i] * st[i]; }, x.lane);    // dS o S
+  if (pub) {
+    x.sm.rowpart[0][half][row] = q0;
+    x.sm.rowpart[1][half][row] = q1;
+    x.sm.rowpart[2][half][row] = q2;
+    x.sm.rowpart[3][half][row] = q3;
+  }
+  cotangent_step(x, tg, m, dp, ds);
+  __syncthreads();
+  if (x.wave < 2) {
+    const int r = x.tid;
+    const float x1 = x.sm.rowpart[0][0][r] + x.sm.rowpart[0][1][r];
+    const float x2 = x.sm.rowpart[1][0][r] + x.sm.rowpart[1][1][r];
+    const float x3 = x.sm.rowpart[2][0][r] + x.sm.rowpart[2][1][r];
+    const float x4 = x.sm.rowpart[3][0][r] + x.sm.rowpart[3][1][r];
+    const float dr = tg.dec[m][r], kr = tg.k[m][r];
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x1), rsrc(p.dq + tk * BD, BD * 4), 4 * r, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x3, x2)), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0,
+                                          0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * fmaf(kr, x3, x4)), rsrc(p.dg + tk * BD, BD * 4), 4 * r,
+                                          0, 0);
+    if (r == 0) p.dbeta[tk] = x.sm.red[0] + x.sm.red[1];
+  }
 }
 
 }  // namespace
 
-__global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_kernel(BwdParams p) {
+// E_r for every segment r and head: the cotangent at the start of segment r
+// due to the outputs of its first fragment (and that fragment's dfinal when
+// it ends a sequence) when nothing after the segment contributes.  Zero for a
+// segment that does not continue a sequence.  One workgroup per (r, head).
+__global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_summary_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
-  const int bid = blockIdx.x;
-  const int n = bid / p.hn;
-  const int h = p.h0 + bid % p.hn;
-  const int tid = threadIdx.x;
-  const int c = tid & (BD - 1);   // column (column walks) or row (row walks)
-  const int half = tid >> 7;      // which 64 rows (column walks) or columns (row walks)
+  const int r = blockIdx.x / p.hn;
+  const int h = p.h0 + blockIdx.x % p.hn;
   const int H = p.H;
-  int32_t bos, eos;
-  seq_bounds(p, n, bos, eos);
-  const int L = eos - bos;
-  const int nchunks = (L + BCH - 1) / BCH;
-  const size_t mat = static_cast<size_t>(BD) * BD;
-  float* ckpt = p.ws + (static_cast<size_t>(bos / BCH + n) * H + h) * mat;   // chunk j: + j * H * mat
-  float* cbuf = p.ws + p.ckpt_floats + (static_cast<size_t>(n) * H + h) * BCH * mat;
-
-  // state tiles <-> global [128][128] (each thread 64 rows of one column)
-  auto tile_to_global = [&](const float* t, float* g) {
-    for (int r = 64 * half; r < 64 * half + 64; ++r) g[r * BD + c] = t[r * BS + c];
-  };
-  auto global_to_tile = [&](const float* g, float* t) {
-    for (int r = 64 * half; r < 64 * half + 64; ++r) t[r * BS + c] = g == nullptr ? 0.f : g[r * BD + c];
-  };
-  // token t's vectors into LDS (threads 0..127: one element of each)
-  auto load_token = [&](const int t, const bool grads) {
-    if (tid < BD) {
-      const size_t ik = (static_cast<size_t>(t) * H + h) * BD + tid;
-      sm.k[tid] = bfv(p.k[ik]);
-      sm.dec[tid] = __builtin_amdgcn_exp2f(bfv(p.g[ik]) * kLog2eB);
-      sm.v[tid] = bfv(p.v[ik]);
-      if (grads) {
-        sm.q[tid] = bfv(p.q[ik]);
-        sm.dov[tid] = p.d_o[ik];
-      }
-      if (tid == 0) sm.beta = bfv(p.beta[static_cast<size_t>(t) * H + h]);
+  const int tid = threadIdx.x;
+  Ctx x(sm, tid);
+  float ds[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) ds[i] = 0.f;
+  if (p.plan[p.L.seg_carry_in + r] != 0) {
+    const int f = p.plan[p.L.seg_frag_ptr + r];
+    const int32_t flags = p.plan[p.L.frag_flags + f];
+    const int32_t seq = p.plan[p.L.frag_seq + f];
+    const int32_t beg = p.plan[p.L.frag_begin + f];
+    const int32_t end = p.plan[p.L.frag_end + f];
+    if ((flags & kFragSeqEnd) && p.dfinal != nullptr)
+      load_state(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+    const int ng = (end - beg + GT - 1) / GT;
+    {
+      Fetch f0;
+      fetch_group(p, h, beg + GT * (ng - 1), min(GT, end - beg - GT * (ng - 1)), tid, x.wave, f0);
+      store_group(sm.tg[0], min(GT, end - beg - GT * (ng - 1)), tid, x.wave, f0);
     }
-  };
-  // p = S~^T k and u = beta (v - p), S~ = Diag(dec) S (column walk)
-  auto compute_pu = [&]() {
-    float acc = 0.f;
-    for (int r = 64 * half; r < 64 * half + 64; ++r) acc += sm.k[r] * sm.dec[r] * sm.S[r * BS + c];
-    sm.part[half][c] = acc;
-    __syncthreads();
-    if (tid < BD) {
-      const float pp = sm.part[0][tid] + sm.part[1][tid];
-      sm.p[tid] = pp;
-      sm.u[tid] = sm.beta * (sm.v[tid] - pp);
-    }
-    __syncthreads();
-  };
-  // S <- S~ + k u^T (the forward update)
-  auto update_S = [&]() {
-    for (int r = 64 * half; r < 64 * half + 64; ++r)
-      sm.S[r * BS + c] = sm.dec[r] * sm.S[r * BS + c] + sm.k[r] * sm.u[c];
-  };
-
-  // ---- forward sweep: the state at the start of every chunk
-  global_to_tile(p.h0s == nullptr ? nullptr : p.h0s + (static_cast<size_t>(n) * H + h) * mat, sm.S);
-  __syncthreads();
-  for (int j = 0; j < nchunks; ++j) {
-    tile_to_global(sm.S, ckpt + static_cast<size_t>(j) * H * mat);
-    const int t1 = min(bos + (j + 1) * BCH, eos);
-    for (int t = bos + j * BCH; t < t1; ++t) {
-      load_token(t, false);
+    for (int gi = ng - 1; gi >= 0; --gi) {
+      Fetch fx;
       __syncthreads();
-      compute_pu();
-      update_S();
-      __syncthreads();
+      const TokGroup& tg = sm.tg[x.gb];
+      const int n = min(GT, end - beg - GT * gi);
+      if (gi > 0) fetch_group(p, h, beg + GT * (gi - 1), GT, tid, x.wave, fx);
+#pragma unroll
+      for (int m = GT - 1; m >= 0; --m)
+        if (m < n) rev_cotangent(x, tg, m, ds);
+      if (gi > 0) store_group(sm.tg[x.gb ^ 1], GT, tid, x.wave, fx);
+      x.gb ^= 1;
     }
   }
+  store_state(p.esum + (static_cast<size_t>(r) * H + h) * MAT, x.voff, ds);
+}
 
-  // ---- reverse sweep
-  global_to_tile(p.dfinal == nullptr ? nullptr : p.dfinal + (static_cast<size_t>(n) * H + h) * mat, sm.dS);
-  __syncthreads();
-  for (int j = nchunks - 1; j >= 0; --j) {
-    const int t0 = bos + j * BCH;
-    const int t1 = min(t0 + BCH, eos);
-    // the chunk's per-token states S_{t-1}, from its checkpoint
-    global_to_tile(ckpt + static_cast<size_t>(j) * H * mat, sm.S);
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-      tile_to_global(sm.S, cbuf + static_cast<size_t>(t - t0) * mat);
-      load_token(t, false);
+// Every (fragment, head) item: the forward from the fragment's start state
+// (carry-in C_r for a carried fragment, else the initial state or zero) with
+// level-1 checkpoints, then per 32-token chunk from the last: the level-2
+// recompute, and per 4-token group from the last: the register recompute
+// and the reverse steps.  The cotangent starts from D_r (when the fragment
+// ends its segment) plus dfinal (when it ends its sequence); a fragment
+// that starts its sequence writes what reaches that start to dh0.
+// Persistent: workgroup b takes items b, b + grid, ... in the plan's
+// longest-first order, with its own level-2 scratch.
+__global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
+  __shared__ BwdSmem sm;
+  const int H = p.H;
+  const int F = p.plan[3];
+  const int items = F * p.hn;
+  const int tid = threadIdx.x;
+  Ctx x(sm, tid);
+  float* lvl2 = p.scratch + static_cast<size_t>(blockIdx.x) * GPC * MAT;
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int f = p.plan[p.L.frag_order + item / p.hn];
+    const int h = p.h0 + item % p.hn;
+    const int32_t flags = p.plan[p.L.frag_flags + f];
+    const int32_t seg = p.plan[p.L.frag_seg + f];
+    const int32_t seq = p.plan[p.L.frag_seq + f];
+    const int32_t beg = p.plan[p.L.frag_begin + f];
+    const int32_t end = p.plan[p.L.frag_end + f];
+    const int len = end - beg;
+    const int ng = (len + GT - 1) / GT;           // 4-token groups
+    const int nch = (len + CK - 1) / CK;          // 32-token chunks
+    const int top = ng - GPC * (nch - 1);         // groups of the last chunk
+    float* ck = p.ckpt + (static_cast<size_t>(beg / CK + f) * H + h) * MAT;   // chunk j at + j H MAT
+    auto gtokens = [&](const int g) { return min(GT, len - GT * g); };
+
+    // One token group: wait for its vectors, prefetch group gn's (gn < 0:
+    // none), run body(tg, n), then store the prefetch into the other buffer.
+    auto group = [&](const int g, const int gn, auto&& body) {
+      Fetch fx;
       __syncthreads();
-      compute_pu();
-      update_S();
-      __syncthreads();
+      const TokGroup& tg = sm.tg[x.gb];
+      if (gn >= 0) fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
+      body(tg, gtokens(g));
+      if (gn >= 0) store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
+      x.gb ^= 1;
+    };
+
+    // run: the running state of the level-1 and level-2 passes, and each
+    // reversed group's first state
+    float run[NR];
+    {
+      const float* s0 = nullptr;
+      if (flags & kFragCarried) s0 = p.carry + (static_cast<size_t>(seg) * H + h) * MAT;
+      else if (p.h0s != nullptr) s0 = p.h0s + (static_cast<size_t>(seq) * H + h) * MAT;
+      load_state(s0, x.voff, run);
     }
-    for (int t = t1 - 1; t >= t0; --t) {
-      global_to_tile(cbuf + static_cast<size_t>(t - t0) * mat, sm.S);
-      load_token(t, true);
-      __syncthreads();
-      compute_pu();
-      // dS += q do^T
-      for (int r = 64 * half; r < 64 * half + 64; ++r) sm.dS[r * BS + c] += sm.q[r] * sm.dov[c];
-      __syncthreads();
-      // du = dS^T k (column walk)
-      {
-        float acc = 0.f;
-        for (int r = 64 * half; r < 64 * half + 64; ++r) acc += sm.dS[r * BS + c] * sm.k[r];
-        sm.part[half][c] = acc;
-      }
-      __syncthreads();
-      if (tid < BD) {
-        const float d = sm.part[0][tid] + sm.part[1][tid];
-        sm.du[tid] = d;
-        sm.dp[tid] = -sm.beta * d;
-        p.dv[(static_cast<size_t>(t) * H + h) * BD + tid] = sm.beta * d;
-        // dbeta = <du, v - p>: a wave sum, then the two waves' sums
-        float x = d * (sm.v[tid] - sm.p[tid]);
-        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-        if ((tid & 63) == 0) sm.red[tid >> 6] = x;
-      }
-      __syncthreads();
-      if (tid == 0) p.dbeta[static_cast<size_t>(t) * H + h] = sm.red[0] + sm.red[1];
-      // row walk: thread row c, columns [64 half, 64 half + 64)
-      //   dq = S_t do, dk = dS u + S~ dp, dg = rowsum((dS + k dp^T) o S~)
-      {
-        const int r = c;
-        const float dr = sm.dec[r], kr = sm.k[r];
-        float aq = 0.f, ak = 0.f, ag = 0.f;
-        for (int cc = 64 * half; cc < 64 * half + 64; ++cc) {
-          const float st = dr * sm.S[r * BS + cc];          // S~
-          const float ds = sm.dS[r * BS + cc];
-          aq += (st + kr * sm.u[cc]) * sm.dov[cc];
-          ak += ds * sm.u[cc] + st * sm.dp[cc];
-          ag += (ds + kr * sm.dp[cc]) * st;
+    __syncthreads();   // the previous item's reads of both token buffers are done
+    {
+      Fetch f0;
+      fetch_group(p, h, beg, gtokens(0), tid, x.wave, f0);
+      store_group(sm.tg[x.gb], gtokens(0), tid, x.wave, f0);
+    }
+
+    // level 1: the state at every chunk start, forward through the fragment
+    for (int g = 0; g < ng; ++g) {
+      group(g, g + 1 < ng ? g + 1 : GPC * (nch - 1), [&](const TokGroup& tg, const int n) {
+        if (g % GPC == 0) put_ckpt(ck + static_cast<size_t>(g / GPC) * H * MAT, tid, run);
+#pragma unroll
+        for (int m = 0; m < GT; ++m) {
+          float u, pp;
+          if (m < n) fwd_step(x, tg, m, run, u, pp, true);
         }
-        sm.part[half][r] = aq;
-        sm.part2[half][r] = ak;
-        sm.part3[half][r] = ag;
-      }
-      __syncthreads();
-      if (tid < BD) {
-        const size_t ik = (static_cast<size_t>(t) * H + h) * BD + tid;
-        p.dq[ik] = sm.part[0][tid] + sm.part[1][tid];
-        p.dk[ik] = sm.part2[0][tid] + sm.part2[1][tid];
-        p.dg[ik] = sm.part3[0][tid] + sm.part3[1][tid];
-      }
-      // dS_{t-1} = Diag(dec) (dS + k dp^T)
-      for (int r = 64 * half; r < 64 * half + 64; ++r)
-        sm.dS[r * BS + c] = sm.dec[r] * (sm.dS[r * BS + c] + sm.k[r] * sm.dp[c]);
-      __syncthreads();
+      });
     }
+
+    // the cotangent at the fragment's end
+    float ds[NR];
+    if (flags & kFragSegLast) {
+      load_state(p.dcarry + (static_cast<size_t>(seg) * H + h) * MAT, x.voff, ds);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) ds[i] = 0.f;
+    }
+    if ((flags & kFragSeqEnd) && p.dfinal != nullptr)
+      add_state(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+
+    for (int j = nch - 1; j >= 0; --j) {
+      const int g0 = GPC * j;
+      const int g1 = g0 + (j == nch - 1 ? top : GPC);   // the chunk's groups [g0, g1)
+      // level 2: the chunk's state every 4 tokens into the scratch
+      get_ckpt(ck + static_cast<size_t>(j) * H * MAT, tid, run);
+      for (int g = g0; g < g1; ++g) {
+        group(g, g + 1 < g1 ? g + 1 : g1 - 1, [&](const TokGroup& tg, const int n) {
+          put_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
+          if (g + 1 < g1) {
+#pragma unroll
+            for (int m = 0; m < GT; ++m) {
+              float u, pp;
+              if (m < n) fwd_step(x, tg, m, run, u, pp, true);
+            }
+          }
+        });
+      }
+      // the groups backwards.  One forward pass from the group's first state
+      // (run, from the scratch) gives every token's u and p and the state
+      // before the last token; the state before token m < n - 1 is rebuilt
+      // from run by m update-only steps (u is known: no exchange).
+      for (int g = g1 - 1; g >= g0; --g) {
+        group(g, g > g0 ? g - 1 : (j > 0 ? g0 - GPC : -1), [&](const TokGroup& tg, const int n) {
+          float uu[GT], pv[GT], w[NR];
+          get_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
+#pragma unroll
+          for (int i = 0; i < NR; ++i) w[i] = run[i];
+#pragma unroll
+          for (int m = 0; m < GT; ++m)
+            if (m < n) fwd_step(x, tg, m, w, uu[m], pv[m], m + 1 < n);
+          const int t0 = beg + GT * g;
+#pragma unroll
+          for (int m = GT - 1; m >= 0; --m) {
+            if (m < n) {
+              if (m + 1 < n) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i) w[i] = run[i];
+#pragma unroll
+                for (int q = 0; q < m; ++q) update_only(x, tg, q, uu[q], w);
+              }
+              rev_step(x, p, h, tg, m, t0 + m, w, ds, uu[m], pv[m]);
+            }
+          }
+        });
+      }
+    }
+    if (!(flags & kFragCarried) && p.dh0 != nullptr)
+      store_state(p.dh0 + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
   }
-  if (p.dh0 != nullptr) tile_to_global(sm.dS, p.dh0 + (static_cast<size_t>(n) * H + h) * mat);
 }
 
 }  // namespace kda

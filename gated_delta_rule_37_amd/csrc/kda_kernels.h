@@ -62,8 +62,7 @@ struct ComposeParams {
   float* carry;
 };
 
-// Backward (kda_backward): one workgroup per (sequence, head).
-constexpr int kBwdThreads = 256;
+// Backward (kda_backward); its geometry constants are in kda_internal.h.
 struct BwdParams {
   const int32_t* plan;
   BlobLayout L;
@@ -78,20 +77,25 @@ struct BwdParams {
   const float* h0s;       // initial states [N, H, K, V] or null (zero)
   const float* d_o;       // dL/do [T, H, V]
   const float* dfinal;    // dL/dfinal [N, H, K, V] or null (zero)
+  const float* carry;     // the forward's carry-in C_r [S, H, K, V]
+  float* esum;            // E_r [S, H, K, V] (written by the summary launch)
+  const float* dcarry;    // D_r [S, H, K, V] (the reverse compose of E)
   float* dq;
   float* dk;
   float* dv;
   float* dg;
   float* dbeta;
   float* dh0;             // dL/dh0 [N, H, K, V] or null (not wanted)
-  float* ws;              // checkpoints, then the per-workgroup chunk buffers
-  size_t ckpt_floats;     // floats of the checkpoint part
+  float* ckpt;            // level-1 checkpoints: slot floor(begin/32) + f + j per head
+  float* scratch;         // per-workgroup level-2 states
 };
 
 __global__ void kda_chunk_kernel(ChunkParams p);
-__global__ void kda_backward_kernel(BwdParams p);
+__global__ void kda_backward_summary_kernel(BwdParams p);
+__global__ void kda_backward_fragment_kernel(BwdParams p);
 __global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_compose_kernel(ComposeParams p);
+__global__ void kda_compose_reverse_kernel(ComposeParams p);
 
 }  // namespace kda
 

@@ -1388,8 +1388,11 @@ struct alignas(16) ComposeSmem {
   float ct[2][kComposeColumns * kCtStride];     // C_r[:, block] transposed, by step parity
 };
 
-__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(ComposeParams p) {
-  __shared__ ComposeSmem sm;
+// REV: the backward's reverse scan D_{S-1} = 0, D_{r-1} = A_r^T D_r + E_r (the
+// same kernel with step s standing for segment S-1-s; A_r^T is read from the
+// row-major tile column-wise, with scalar LDS reads).
+template <bool REV>
+__device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem& sm) {
   const int H = p.H;
   const int xcd = blockIdx.x % 8;
   const int kq = blockIdx.x / 8;
@@ -1407,8 +1410,10 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
 
   // A_r, coalesced: piece u of lane tid is 16-byte piece u * 512 + tid of the
   // row-major matrix, i.e. row 16u + tid / 32, floats 4 (tid % 32) ..
+  const int S = p.S;
+  auto seg_of = [&](const int r) { return REV ? S - 1 - r : r; };
   auto load_a = [&](const int r, f32x4 (&a)[kAPieces]) {
-    const float* src = p.transitions + (static_cast<size_t>(r) * H + h) * KD * KD;
+    const float* src = p.transitions + (static_cast<size_t>(seg_of(r)) * H + h) * KD * KD;
 #pragma unroll
     for (int u = 0; u < kAPieces; ++u) a[u] = *reinterpret_cast<const f32x4*>(&src[4 * (u * kComposeThreads + tid)]);
   };
@@ -1421,7 +1426,7 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
   };
   // this lane's rows of B_r, in the accumulator layout
   auto load_b = [&](const int r, f32x4& bv) {
-    const float* bsrc = p.updates + (static_cast<size_t>(r) * H + h) * KD * VD;
+    const float* bsrc = p.updates + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bv[i] = bsrc[(row0 + 4 * lj + i) * VD + col];
   };
@@ -1435,7 +1440,9 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
     if (r - lbase >= 64) {
       lbase = r & ~63;
       const int idx = lbase + lane;
-      const bool f = idx < p.S - 1 && p.plan[p.L.seg_transition_live + idx] != 0;
+      // forward: A_idx is applied for idx < S-1; reverse: A_{S-1-idx}^T for
+      // 1 <= idx < S-1 (D_{S-1} is zero, so A_{S-1} is never read)
+      const bool f = idx < S - 1 && (!REV || idx >= 1) && p.plan[p.L.seg_transition_live + seg_of(idx)] != 0;
       lmask = __builtin_amdgcn_ballot_w64(f);
     }
     return ((lmask >> (r - lbase)) & 1ull) != 0;
@@ -1463,7 +1470,7 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
 #pragma unroll
     for (int ph = 0; ph < kComposeRing; ++ph) {
       const int r = r0 + ph;            // r % kComposeRing == ph
-      float* cdst = p.carry + (static_cast<size_t>(r) * H + h) * KD * VD;
+      float* cdst = p.carry + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
       if (r == p.S - 1) return;
@@ -1485,7 +1492,12 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           bop[q] = ld4(&sm.ct[buf][lc * kCtStride + 32 * lj + 4 * q]);
-          aop[q] = ld4(&sm.at[buf][(row0 + lc) * kAtStride + 32 * lj + 4 * q]);
+          if (REV) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) aop[q][e] = sm.at[buf][(32 * lj + 4 * q + e) * kAtStride + row0 + lc];
+          } else {
+            aop[q] = ld4(&sm.at[buf][(row0 + lc) * kAtStride + 32 * lj + 4 * q]);
+          }
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -1505,6 +1517,16 @@ __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(Compose
       cur = nxt;
     }
   }
+}
+
+__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(ComposeParams p) {
+  __shared__ ComposeSmem sm;
+  compose_scan<false>(p, sm);
+}
+
+__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_reverse_kernel(ComposeParams p) {
+  __shared__ ComposeSmem sm;
+  compose_scan<true>(p, sm);
 }
 
 }  // namespace kda

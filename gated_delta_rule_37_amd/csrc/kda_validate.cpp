@@ -83,12 +83,34 @@ int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t
   return KDA_OK;
 }
 
-size_t backward_workspace_need(const kda_plan* plan, int32_t H) {
+BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
   const size_t mat = size_t(128) * 128 * sizeof(float);
-  const size_t ckpt = (static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->N)) * H * mat;
-  const size_t cbuf = static_cast<size_t>(plan->N) * H * 32 * mat;
-  return ckpt + cbuf;
+  const size_t seg_states = static_cast<size_t>(plan->S) * H * mat;
+  auto aligned = [](size_t x) { return (x + 255) & ~size_t(255); };
+  BwdLayout L{};
+  size_t o = 0;
+  L.cache = o;
+  o += aligned(workspace_need(plan, H));
+  L.transitions = o;
+  o += seg_states;
+  L.updates = o;
+  o += seg_states;
+  L.carry = o;
+  o += seg_states;
+  L.esum = o;
+  o += seg_states;
+  L.dcarry = o;
+  o += seg_states;
+  L.ckpt = o;
+  o += (static_cast<size_t>(plan->T / kBwdCheckpointTokens) + static_cast<size_t>(plan->F)) * H * mat;
+  L.scratch = o;
+  const size_t items = static_cast<size_t>(plan->F) * H;
+  o += (items < static_cast<size_t>(kBwdGrid) ? items : kBwdGrid) * kBwdScratchStates * mat;
+  L.total = o;
+  return L;
 }
+
+size_t backward_workspace_need(const kda_plan* plan, int32_t H) { return backward_layout(plan, H).total; }
 
 size_t workspace_need(const kda_plan* plan, int32_t H) {
   const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);

@@ -14,8 +14,16 @@ namespace kda {
 // Bytes of the workspace (the chunk cache) a plan needs for H heads.
 size_t workspace_need(const kda_plan* plan, int32_t H);
 
-// Bytes of the backward's workspace for H heads: a state checkpoint per
-// 32-token chunk of every sequence, plus 32 states per (sequence, head).
+// Byte offsets of the parts of the backward's workspace for H heads (each
+// 256-byte aligned): the forward's chunk cache, the forward's transitions,
+// updates and carry-ins recomputed, the backward summaries E and their
+// reverse compose D (each S x H states), the level-1 checkpoints
+// ((floor(T/32) + F) x H states) and the fragment launch's scratch
+// (min(F H, kBwdGrid) x kBwdScratchStates states).
+struct BwdLayout {
+  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, scratch, total;
+};
+BwdLayout backward_layout(const kda_plan* plan, int32_t H);
 size_t backward_workspace_need(const kda_plan* plan, int32_t H);
 
 // Plan, plan_dev and dimensions (K = V = 128, 0 < H <= 65535).

@@ -339,11 +339,16 @@ size_t kda_noalloc_max_workspace_bytes(void);
  *   dq, dk, dg  [T, H, K] fp32    dv [T, H, V] fp32    dbeta [T, H] fp32
  *   d_initial_state [N, H, K, V] fp32 (optional: NULL when not wanted)
  * d_o [T, H, V] fp32 is required, d_final [N, H, K, V] fp32 optional (NULL =
- * zero).  g is the log-decay as given (no safe gate).  Every sequence and
- * head is reversed in FP32, one token at a time from state checkpoints taken
- * every 32 tokens; workspace: kda_backward_workspace_bytes(plan, H, K, V)
- * bytes, caller-owned, contents not needed afterwards.  Arguments, sizes and
- * errors as for the forward's device calls (each buffer with its byte count).
+ * zero).  g is the log-decay as given (no safe gate).  The segments of the
+ * plan run in parallel, as in the forward (#136: the backward gathers the
+ * following summaries): the call recomputes the forward's transitions and
+ * carry-ins, forms each carried segment's backward summary E_r (the
+ * cotangent at its start due to its first fragment's own outputs), scans
+ * D_{r-1} = A_r^T D_r + E_r in reverse, and reverses every (fragment, head)
+ * in FP32 one token at a time from its carry-in and D_r.  Workspace:
+ * kda_backward_workspace_bytes(plan, H, K, V) bytes, caller-owned, contents
+ * not needed afterwards.  Arguments, sizes and errors as for the forward's
+ * device calls (each buffer with its byte count).
  */
 int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                  const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
@@ -358,8 +363,11 @@ int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_
                  float* d_initial_state, size_t d_initial_state_bytes,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of kda_backward's workspace: (ceil(T/32) + N) * H state checkpoints
- * plus 32 states per (sequence, head), 64 KiB each.  0 for a NULL plan,
+/* Bytes of kda_backward's workspace for H heads (each part 256-byte
+ * aligned): kda_workspace_bytes(plan, H); five arrays of S * H states
+ * (transitions, updates, carry-ins, backward summaries and their reverse
+ * compose); (floor(T/32) + F) * H state checkpoints; min(F * H, 256) * 8
+ * states of per-workgroup scratch; a state is 64 KiB.  0 for a NULL plan,
  * H <= 0 or K, V other than 128. */
 size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 

@@ -291,7 +291,13 @@ def test_backward_validates_before_launch():
                 beta=T * H * 2, init=N * H * 65536, do=T * H * 512, dfinal=N * H * 65536, dq=T * H * 512,
                 dk=T * H * 512, dv=T * H * 512, dg=T * H * 512, dbeta=T * H * 4, dh0=N * H * 65536,
                 ws=L.kda_backward_workspace_bytes(plan.handle, H, 128, 128))
-    assert need["ws"] == ((100 + 31) // 32 + 2) * H * 65536 + 2 * H * 32 * 65536
+    # the forward's chunk cache (256-byte aligned), five S x H state arrays
+    # (transitions, updates, carry-ins, backward summaries and their compose),
+    # (floor(T/32) + F) x H checkpoints, min(F H, 256) x 8 scratch states
+    S, F = 2, plan.F
+    cache = ((T + 31) // 32 + S) * H * 4096
+    cache = (cache + 255) // 256 * 256
+    assert need["ws"] == cache + 5 * S * H * 65536 + (T // 32 + F) * H * 65536 + min(F * H, 256) * 8 * 65536
     order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "dq", "dk", "dv", "dg", "dbeta",
              "dh0", "ws")
 

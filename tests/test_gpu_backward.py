@@ -1,6 +1,8 @@
 """GPU parity of the backward (kda_backward through the C-ABI) against the
 fp64 oracle's backward on the same bytes: gradients of q, k, v, g, beta and
-the initial states for L = sum <o, d_o> + sum <final, d_final>.
+the initial states for L = sum <o, d_o> + sum <final, d_final>, with one
+segment and with several (segments run in parallel through the backward
+summaries and their reverse compose; the result must not depend on S).
 
 Tolerance (written here): every gradient tensor, per head,
 max |grad_gpu - grad_ref| <= 1e-4 * max |grad_ref| -- the relative bound the
@@ -19,25 +21,33 @@ pytestmark = pytest.mark.gpu
 GRAD_RTOL = 1e-4
 
 CASES = [
-    # name, T, H, cu_seqlens, gate scale, initial states + d_final
-    ("one_sequence_ragged", 70, 2, [0, 70], 1.0, False),
-    ("varlen_h0_dfinal", 300, 2, [0, 37, 150, 151, 300], 0.3, True),
-    ("chunk_aligned", 64, 1, [0, 32, 64], 1.0, True),
-    ("short_sequences", 40, 2, [0, 1, 2, 9, 40], 0.5, True),
-    ("fast_gates", 96, 1, [0, 96], 4.0, True),
+    # name, T, H, cu_seqlens, segments, gate scale, initial states + d_final
+    ("one_sequence_ragged", 70, 2, [0, 70], 1, 1.0, False),
+    ("varlen_h0_dfinal", 300, 2, [0, 37, 150, 151, 300], 1, 0.3, True),
+    ("chunk_aligned", 64, 1, [0, 32, 64], 1, 1.0, True),
+    ("short_sequences", 40, 2, [0, 1, 2, 9, 40], 1, 0.5, True),
+    ("fast_gates", 96, 1, [0, 96], 1, 4.0, True),
+    # several segments: carried segments, the backward summaries E_r and
+    # their reverse compose D_r (the pages' following summaries)
+    ("one_sequence_5_segments", 300, 2, [0, 300], 5, 0.3, True),
+    ("varlen_4_segments", 300, 2, [0, 37, 150, 151, 300], 4, 0.3, True),
+    ("one_sequence_16_segments", 1000, 1, [0, 1000], 16, 0.1, False),
+    ("varlen_7_segments_h0", 777, 3, [0, 5, 300, 301, 640, 777], 7, 0.2, True),
+    ("segments_longer_than_sequences", 200, 1, [0, 10, 20, 30, 200], 3, 1.0, True),
+    ("fast_gates_segments", 256, 2, [0, 256], 4, 4.0, True),
 ]
 
 
-@pytest.mark.parametrize("name,T,H,cu,gs,with_h0", CASES, ids=[c[0] for c in CASES])
-def test_backward_parity(name, T, H, cu, gs, with_h0):
-    print(f"case {name}: T={T} H={H} cu={cu}", flush=True)
+@pytest.mark.parametrize("name,T,H,cu,S,gs,with_h0", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(name, T, H, cu, S, gs, with_h0):
+    print(f"case {name}: T={T} H={H} cu={cu} S={S}", flush=True)
     x = synth.make_inputs(T, H, 128, 128, seed=len(name) + T, cu_seqlens=cu, gate_scale=gs)
     N = len(cu) - 1
     gen = torch.Generator().manual_seed(T + 3)
     d_o = torch.randn(T, H, 128, generator=gen)
     d_final = torch.randn(N, H, 128, 128, generator=gen) if with_h0 else None
     h0 = synth.initial_states(N, H, 128, 128, seed=T + 5) if with_h0 else None
-    plan = kda.Plan(cu, 1)
+    plan = kda.Plan(cu, S)
     d = pu.to_device(x)
     got = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o.cuda(),
                        d_final=None if d_final is None else d_final.cuda(),
@@ -70,7 +80,7 @@ def test_backward_deterministic():
     T, H, cu = 150, 2, [0, 60, 150]
     x = synth.make_inputs(T, H, 128, 128, seed=31, cu_seqlens=cu)
     d_o = torch.randn(T, H, 128, generator=torch.Generator().manual_seed(32)).cuda()
-    plan = kda.Plan(cu, 1)
+    plan = kda.Plan(cu, 3)
     d = pu.to_device(x)
     outs = [kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o) for _ in range(3)]
     torch.cuda.synchronize()
