@@ -296,22 +296,20 @@ __device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, co
     const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[4 * j + e] = fmaf(dc[e], s[4 * j + e], kk[e] * u);
-    slice_fence();
   }
 }
 
 __device__ __forceinline__ void fwd_step(Ctx& x, const TokGroup& tg, const int m, float (&s)[NR], float& u,
                                          float& pp, const bool upd) {
   const int r0 = NR * x.grp;
-  float part = 0.f;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};   // four partial sums: a short dependent chain
 #pragma unroll
   for (int j = 0; j < NR / 4; ++j) {
     const f4 kd = l4(&tg.kd[m][r0 + 4 * j]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part = fmaf(kd[e], s[4 * j + e], part);
-    slice_fence();
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(kd[e], s[4 * j + e], acc[e]);
   }
-  pp = x.col_sum(part);
+  pp = x.col_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
   u = tg.beta[m] * (tg.v[m][x.c] - pp);
   if (upd) update_only(x, tg, m, u, s);
 }
@@ -320,7 +318,7 @@ __device__ __forceinline__ void fwd_step(Ctx& x, const TokGroup& tg, const int m
 __device__ __forceinline__ float add_qdo(const Ctx& x, const TokGroup& tg, const int m, const float doc,
                                         float (&ds)[NR]) {
   const int r0 = NR * x.grp;
-  float part = 0.f;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NR / 4; ++j) {
     const f4 qq = l4(&tg.q[m][r0 + 4 * j]);
@@ -328,11 +326,10 @@ __device__ __forceinline__ float add_qdo(const Ctx& x, const TokGroup& tg, const
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ds[4 * j + e] = fmaf(qq[e], doc, ds[4 * j + e]);
-      part = fmaf(ds[4 * j + e], kk[e], part);
+      acc[e] = fmaf(ds[4 * j + e], kk[e], acc[e]);
     }
-    slice_fence();
   }
-  return part;
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // dS_{t-1} = Diag(e^g) (dS + k dp^T)
@@ -345,7 +342,6 @@ __device__ __forceinline__ void cotangent_step(const Ctx& x, const TokGroup& tg,
     const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) ds[4 * j + e] = dc[e] * fmaf(kk[e], dp, ds[4 * j + e]);
-    slice_fence();
   }
 }
 
@@ -380,11 +376,8 @@ __device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h
   const float* drow = &tg.dec[m][r0];
   const float q0 = wave_rows_reduce(                                         // S_t do
       [&](const int i) { return fmaf(drow[i], st[i], krow[i] * u) * doc; }, x.lane);
-  __builtin_amdgcn_sched_barrier(0);
   const float q1 = wave_rows_reduce([&](const int i) { return ds[i] * u; }, x.lane);        // dS u
-  __builtin_amdgcn_sched_barrier(0);
   const float q2 = wave_rows_reduce([&](const int i) { return st[i] * dp; }, x.lane);       // S dp
-  __builtin_amdgcn_sched_barrier(0);
   const float q3 = wave_rows_reduce([&](const int i) { return ds[i] * st[i]; }, x.lane);    // dS o S
   if (pub) {
     x.sm.rowpart[0][half][row] = q0;
@@ -416,7 +409,7 @@ __device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h
 // due to the outputs of its first fragment (and that fragment's dfinal when
 // it ends a sequence) when nothing after the segment contributes.  Zero for a
 // segment that does not continue a sequence.  One workgroup per (r, head).
-__global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_summary_kernel(BwdParams p) {
+__global__ void __launch_bounds__(kBwdThreads, 8) kda_backward_summary_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
   const int r = blockIdx.x / p.hn;
   const int h = p.h0 + blockIdx.x % p.hn;
