@@ -271,6 +271,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
                     help="fetch.csv write.csv copy_fetch.csv copy_write.csv from rocprofv3 --pmc runs")
     ap.add_argument("--copy-bytes-used", type=int, default=1 << 30)
+    ap.add_argument("--backward-steps", type=int, default=3,
+                    help="timed calls of the backward (kda_backward) on the same workload; 0: none")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.copy_bytes_used)
@@ -305,6 +307,8 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(x, w, args.cpu_tokens)
     res = measure(args, w, x, torch, kda, synth)
     res["cpu_baseline"] = cpu
+    if args.backward_steps > 0:
+        res["backward"] = measure_backward(args, w, x, torch, kda)
     print(json.dumps(res), flush=True)
 
 
@@ -457,6 +461,51 @@ def measure(args, w, x, torch, kda, synth):
             "frac": round(max(t_c_mfma, t_c_hbm) / compose_ms, 4),
         },
         "other_chunk_roofline": other,
+    }
+
+
+# Algorithmic FP32 flops of the backward per (token, head): the forward
+# quantities it needs (p = S~^T k: 2KV, S_t = S~ + k u^T: 3KV) and the
+# reverse step (dS += q do^T: 2KV, du: 2KV, dq: 2KV, dk: 4KV, dS~: 2KV,
+# dg: 2KV, dS_{t-1}: KV) -- 20 K V; recomputation is not counted.
+BWD_FLOPS_PER_TOKEN_HEAD = 20 * 128 * 128
+
+
+def measure_backward(args, w, x, torch, kda):
+    """Time kda_backward (the gradients of q, k, v, g, beta for a seeded
+    d_o) on the same workload: one untimed call, then args.backward_steps
+    calls between events on the calling stream.  The roofline is the ALU
+    bound of the whole call (five launches; the fragment launch dominates,
+    its own duration is in the committed kernel trace)."""
+    dev = torch.device("cuda:0")
+    d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    plan = kda.Plan(x["cu_seqlens"].tolist(), w.segments)
+    gen = torch.Generator().manual_seed(w.seed + 2000)
+    d_o = torch.randn(w.T, w.H, w.V, generator=gen).to(dev)
+
+    def call():
+        return kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o)
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.backward_steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.backward_steps
+    flops = BWD_FLOPS_PER_TOKEN_HEAD * w.T * w.H
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "ms_per_call": round(ms, 3),
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "calls": args.backward_steps,
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "flops_per_token_head": BWD_FLOPS_PER_TOKEN_HEAD,
+                     "peak_without_packed_fp32": PEAK_FP32_TFLOPS / 2,
+                     "frac_without_packed_fp32": round(achieved / (PEAK_FP32_TFLOPS / 2), 4)},
     }
 
 
