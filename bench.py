@@ -271,6 +271,9 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
                     help="fetch.csv write.csv copy_fetch.csv copy_write.csv from rocprofv3 --pmc runs")
     ap.add_argument("--copy-bytes-used", type=int, default=1 << 30)
+    ap.add_argument("--pieces", default="auto",
+                    help="piece length in tokens (a multiple of 32), 0 for none, or 'auto': pieces only "
+                         "where segments x heads leave compute units idle (kda.auto_piece_tokens)")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="timed calls of the backward (kda_backward) on the same workload; 0: none")
     args = ap.parse_args()
@@ -343,13 +346,21 @@ def pages_timing(step, torch, repeats=5, warmup=20, iters=60):
     return out
 
 
+def piece_tokens(args, kda, cu, w):
+    """The plan's piece length: --pieces, or the binding's rule for 'auto'."""
+    if args.pieces == "auto":
+        return kda.auto_piece_tokens(cu, w.segments, w.H)
+    return int(args.pieces)
+
+
 def measure(args, w, x, torch, kda, synth):
     """Time the whole forward on one workload (inputs resident on the GPU):
     the driver's K timed steps, then the pages' method; return the JSON line."""
     dev = torch.device("cuda:0")
     d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
     cu = x["cu_seqlens"].tolist()
-    plan = kda.Plan(cu, w.segments)
+    pieces = piece_tokens(args, kda, cu, w)
+    plan = kda.Plan(cu, w.segments, None, pieces)
     out = kda.alloc_outputs(plan, w.H, w.K, w.V, dev, torch.bfloat16 if args.o_bf16 else torch.float32)
     h0 = None
     if args.initial_state:
@@ -422,7 +433,7 @@ def measure(args, w, x, torch, kda, synth):
     other = roofline("kda_carry_kernel" if dominant == "kda_chunk_kernel" else "kda_chunk_kernel")
 
     S = plan.S
-    live = int(sum(blob[4 + (S + 1) + 3 * S: 4 + (S + 1) + 4 * S]))
+    live = int(plan.segment_live.sum())
     comp = compose_work(S, w.H, live)
     t_c_mfma = comp["macs"] * 2 / (PEAK_FP32_TFLOPS * 1e12) * 1e3
     t_c_hbm = comp["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
@@ -443,6 +454,7 @@ def measure(args, w, x, torch, kda, synth):
         "config": {"workload": w.name, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "segments": w.segments, "sequences": plan.N, "seed": w.seed,
                    "gate_scale": w.gate_scale, "beta_scale": w.beta_scale,
+                   "piece_tokens": pieces, "pieces": plan.P,
                    "head_groups": groups, "initial_state": bool(args.initial_state),
                    "o": "bf16" if args.o_bf16 else "fp32"},
         "roofline": roof,
@@ -479,7 +491,8 @@ def measure_backward(args, w, x, torch, kda):
     its own duration is in the committed kernel trace)."""
     dev = torch.device("cuda:0")
     d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
-    plan = kda.Plan(x["cu_seqlens"].tolist(), w.segments)
+    cu = x["cu_seqlens"].tolist()
+    plan = kda.Plan(cu, w.segments, None, piece_tokens(args, kda, cu, w))
     gen = torch.Generator().manual_seed(w.seed + 2000)
     d_o = torch.randn(w.T, w.H, w.V, generator=gen).to(dev)
 

@@ -22,6 +22,7 @@ using kda::check_compose;
 using kda::check_dims;
 using kda::check_summaries;
 using kda::workspace_need;
+using kda::PieceLayout;
 
 thread_local int g_last_hip_error = 0;
 
@@ -54,10 +55,41 @@ void set_gate(kda::ChunkParams& p, float gate_lower_bound) {
   p.gate_floor = gate_lower_bound * 1.4426950408889634f;
 }
 
+// A scan launch (the compose kernel in one of its modes): grid of
+// (chain, head) units padded to a multiple of 8, times the column blocks.
+int launch_scan(void (*kernel)(kda::ComposeParams), const kda::ComposeParams& c, int chains, int column_blocks,
+                hipStream_t stream) {
+  const int64_t units = static_cast<int64_t>(chains) * c.hn;
+  const int64_t blocks = ((units + 7) / 8) * 8 * column_blocks;
+  if (blocks > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kda::kComposeThreads), 0, stream, c);
+  return finish_launch();
+}
+
+kda::ComposeParams scan_params(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t head_begin,
+                               int32_t head_count) {
+  kda::ComposeParams c{};
+  c.plan = plan_dev;
+  c.L = plan->layout;
+  c.H = H;
+  c.h0 = head_begin;
+  c.hn = head_count;
+  c.chains = plan->S;
+  return c;
+}
+
+// Summaries into `transitions` / `updates`: per segment, or per piece with
+// fold = false (the backward's own arrays).  With pieces and fold = true the
+// pieces' summaries go to the workspace and are folded into the segments'.
 int launch_summaries(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* k,
                      const uint16_t* v, const uint16_t* g, const uint16_t* beta, float gate_lower_bound,
                      const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
-                     float* transitions, float* updates, void* workspace, hipStream_t stream) {
+                     float* transitions, float* updates, void* workspace, hipStream_t stream, bool fold = true) {
+  const bool via_pieces = plan->pieces && fold;
+  const kda::PieceLayout PL = kda::piece_layout(plan, H);
+  float* piece_a = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + PL.transitions);
+  float* piece_b = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + PL.updates);
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -71,45 +103,63 @@ int launch_summaries(const kda_plan* plan, const int32_t* plan_dev, const uint16
   p.beta = beta;
   p.o = nullptr;
   p.final_state = nullptr;
-  p.transitions = transitions;
-  p.updates = updates;
+  p.transitions = via_pieces ? piece_a : transitions;
+  p.updates = via_pieces ? piece_b : updates;
   p.carry = nullptr;
   p.init_state = initial_state;
   set_gate(p, gate_lower_bound);
   p.chunk_cache = static_cast<uint16_t*>(workspace);
   dim3 grid;
-  const int st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
+  int st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &grid);
   if (st != KDA_OK) return st;
   (void)hipGetLastError();
   hipLaunchKernelGGL(kda::kda_chunk_kernel, grid, dim3(kda::kSummaryThreads), 0, stream, p);
-  return finish_launch();
+  st = finish_launch();
+  if (st != KDA_OK || !via_pieces) return st;
+  // each segment's (A_r, B_r) from its pieces'
+  kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);
+  c.live_off = plan->layout.seg_transition_live;
+  c.transitions = piece_a;
+  c.updates = piece_b;
+  c.out_a = transitions;
+  c.out_b = updates;
+  return launch_scan(kda::kda_fold_pieces_kernel, c, plan->S, 2 * kda::kComposeColumnBlocks, stream);
 }
 
+// The ordered scan over the segments (pieces = false) or, for the backward,
+// over the pieces.
 int launch_compose(const kda_plan* plan, const int32_t* plan_dev, const float* transitions,
                    const float* updates, int32_t H, int32_t head_begin, int32_t head_count,
-                   float* carry_in, hipStream_t stream) {
-  kda::ComposeParams p{};
-  p.plan = plan_dev;
-  p.L = plan->layout;
-  p.H = H;
-  p.h0 = head_begin;
-  p.hn = head_count;
-  p.S = plan->S;
-  p.transitions = transitions;
-  p.updates = updates;
-  p.carry = carry_in;
-  (void)hipGetLastError();
-  // one workgroup per (head, column block), heads padded to a multiple of 8
-  const int blocks = ((head_count + 7) / 8) * 8 * kda::kComposeColumnBlocks;
-  hipLaunchKernelGGL(kda::kda_compose_kernel, dim3(blocks), dim3(kda::kComposeThreads), 0, stream, p);
-  return finish_launch();
+                   float* carry_in, hipStream_t stream, bool pieces = false) {
+  kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);
+  c.S = pieces ? plan->P : plan->S;
+  c.live_off = pieces ? plan->layout.seg_transition_live : plan->layout.useg_transition_live;
+  c.transitions = transitions;
+  c.updates = updates;
+  c.carry = carry_in;
+  return launch_scan(kda::kda_compose_kernel, c, 1, kda::kComposeColumnBlocks, stream);
 }
 
 int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* q, const uint16_t* k,
                  const uint16_t* v, const uint16_t* g, const uint16_t* beta, float gate_lower_bound,
                  const float* initial_state, int32_t H, int32_t head_begin, int32_t head_count,
                  const float* carry_in, void* o, int32_t o_format, float* final_state,
-                 const void* workspace, hipStream_t stream) {
+                 const void* workspace, hipStream_t stream, bool piece_level = false) {
+  const float* carry = carry_in;
+  if (plan->pieces && !piece_level) {
+    // every piece's carry-in, from its segment's
+    const kda::PieceLayout PL = kda::piece_layout(plan, H);
+    const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+    kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);
+    c.live_off = plan->layout.seg_transition_live;
+    c.transitions = reinterpret_cast<const float*>(ws + PL.transitions);
+    c.updates = reinterpret_cast<const float*>(ws + PL.updates);
+    c.carry = const_cast<float*>(reinterpret_cast<const float*>(ws + PL.carry));
+    c.init = carry_in;
+    const int st = launch_scan(kda::kda_piece_carry_kernel, c, plan->S, kda::kComposeColumnBlocks, stream);
+    if (st != KDA_OK) return st;
+    carry = c.carry;
+  }
   kda::ChunkParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -126,7 +176,7 @@ int launch_carry(const kda_plan* plan, const int32_t* plan_dev, const uint16_t* 
   p.final_state = final_state;
   p.transitions = nullptr;
   p.updates = nullptr;
-  p.carry = carry_in;
+  p.carry = carry;
   p.init_state = initial_state;
   set_gate(p, gate_lower_bound);
   p.chunk_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(workspace));
@@ -323,7 +373,7 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   dim3 unused;
   st = chunk_grid(plan->F, head_count, kda::kSummaryThreads, &unused);
   if (st != KDA_OK) return st;
-  const int64_t seg_blocks = static_cast<int64_t>(plan->S) * head_count;
+  const int64_t seg_blocks = static_cast<int64_t>(plan->P) * head_count;   // the backward works on pieces
   const int64_t items = static_cast<int64_t>(plan->F) * head_count;
   if (seg_blocks > 2147483647LL || items > 2147483647LL) return KDA_ERR_UNSUPPORTED;
   const kda::BwdLayout W = kda::backward_layout(plan, H);
@@ -335,9 +385,10 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   float* dcarry = reinterpret_cast<float*>(ws + W.dcarry);
   // the forward's summaries and carry-ins, without the safe gate
   st = launch_summaries(plan, plan_dev, k, v, g, beta, -INFINITY, initial_state, H, head_begin, head_count,
-                        transitions, updates, ws + W.cache, stream);
+                        transitions, updates, ws + W.cache, stream, /*fold=*/false);
   if (st != KDA_OK) return st;
-  st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream);
+  st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream,
+                      /*pieces=*/true);
   if (st != KDA_OK) return st;
   kda::BwdParams p{};
   p.plan = plan_dev;
@@ -370,19 +421,13 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
                      dim3(kda::kBwdThreads), 0, stream, p);
   st = finish_launch();
   if (st != KDA_OK) return st;
-  kda::ComposeParams c{};
-  c.plan = plan_dev;
-  c.L = plan->layout;
-  c.H = H;
-  c.h0 = head_begin;
-  c.hn = head_count;
-  c.S = plan->S;
+  kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);
+  c.S = plan->P;
+  c.live_off = plan->layout.seg_transition_live;
   c.transitions = transitions;
   c.updates = esum;
   c.carry = dcarry;
-  const int cblocks = ((head_count + 7) / 8) * 8 * kda::kComposeColumnBlocks;
-  hipLaunchKernelGGL(kda::kda_compose_reverse_kernel, dim3(cblocks), dim3(kda::kComposeThreads), 0, stream, c);
-  st = finish_launch();
+  st = launch_scan(kda::kda_compose_reverse_kernel, c, 1, kda::kComposeColumnBlocks, stream);
   if (st != KDA_OK) return st;
   const int64_t grid = items < kda::kBwdGrid ? items : kda::kBwdGrid;
   hipLaunchKernelGGL(kda::kda_backward_fragment_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),

@@ -30,34 +30,51 @@ constexpr int kBwdScratchStates = kBwdCheckpointTokens / 4;
 constexpr int32_t kMaxTokens = (1 << 30);
 
 // Word offsets of the arrays inside the plan blob (see kda_plan_blob()).
+// The seg_* arrays describe the pieces (the segments themselves when the plan
+// has no pieces); the useg_* offsets the segment-level arrays, which alias
+// the piece-level ones when there are no pieces (useg_piece_ptr is then -1).
 struct BlobLayout {
   int32_t seg_bounds, seg_first_seq, seg_last_seq, seg_carry_in, seg_transition_live,
       seg_frag_ptr, frag_seq, frag_begin, frag_end, frag_seg, frag_flags, seq_end_seg, frag_order;
+  int32_t useg_bounds, useg_carry_in, useg_transition_live, useg_piece_ptr;
 };
 
-inline BlobLayout blob_layout(int32_t S, int32_t F, int32_t N) {
+inline BlobLayout blob_layout(int32_t P, int32_t F, int32_t N, int32_t S, bool pieces) {
   BlobLayout L;
   int32_t o = 4;
-  L.seg_bounds = o;          o += S + 1;
-  L.seg_first_seq = o;       o += S;
-  L.seg_last_seq = o;        o += S;
-  L.seg_carry_in = o;        o += S;
-  L.seg_transition_live = o; o += S;
-  L.seg_frag_ptr = o;        o += S + 1;
+  L.seg_bounds = o;          o += P + 1;
+  L.seg_first_seq = o;       o += P;
+  L.seg_last_seq = o;        o += P;
+  L.seg_carry_in = o;        o += P;
+  L.seg_transition_live = o; o += P;
+  L.seg_frag_ptr = o;        o += P + 1;
   L.frag_seq = o;            o += F;
   L.frag_begin = o;          o += F;
   L.frag_end = o;            o += F;
   L.frag_seg = o;            o += F;
   L.frag_flags = o;          o += F;
   L.seq_end_seg = o;         o += N;
-  L.frag_order = o;
+  L.frag_order = o;          o += F;
+  if (pieces) {
+    o += 1;                  // S
+    L.useg_bounds = o;          o += S + 1;
+    L.useg_carry_in = o;        o += S;
+    L.useg_transition_live = o; o += S;
+    L.useg_piece_ptr = o;
+  } else {
+    L.useg_bounds = L.seg_bounds;
+    L.useg_carry_in = L.seg_carry_in;
+    L.useg_transition_live = L.seg_transition_live;
+    L.useg_piece_ptr = -1;
+  }
   return L;
 }
 
 }  // namespace kda
 
 struct kda_plan {
-  int32_t T = 0, N = 0, S = 0, F = 0;
+  int32_t T = 0, N = 0, S = 0, P = 0, F = 0;   // S segments, P pieces (P = S: no pieces)
+  bool pieces = false;
   kda::BlobLayout layout{};
   std::vector<int32_t> blob;
 };

@@ -56,10 +56,15 @@ struct ComposeParams {
   int32_t H;    // heads in the tensors
   int32_t h0;   // heads [h0, h0 + hn) are composed by this launch
   int32_t hn;
-  int32_t S;
+  int32_t S;          // steps of the one chain (compose, reverse): segments or pieces
+  int32_t live_off;   // plan word offset of the transition flags of those steps
+  int32_t chains;     // fold, piece carry: one chain per segment
   const float* transitions;
   const float* updates;
-  float* carry;
+  float* carry;       // compose, reverse, piece carry: every step's value
+  const float* init;  // piece carry: the segments' carry-ins
+  float* out_a;       // fold: the segments' transitions
+  float* out_b;       // fold: the segments' updates
 };
 
 // Backward (kda_backward); its geometry constants are in kda_internal.h.
@@ -96,6 +101,8 @@ __global__ void kda_backward_fragment_kernel(BwdParams p);
 __global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_compose_kernel(ComposeParams p);
 __global__ void kda_compose_reverse_kernel(ComposeParams p);
+__global__ void kda_fold_pieces_kernel(ComposeParams p);
+__global__ void kda_piece_carry_kernel(ComposeParams p);
 
 }  // namespace kda
 

@@ -1388,30 +1388,54 @@ struct alignas(16) ComposeSmem {
   float ct[2][kComposeColumns * kCtStride];     // C_r[:, block] transposed, by step parity
 };
 
-// REV: the backward's reverse scan D_{S-1} = 0, D_{r-1} = A_r^T D_r + E_r (the
-// same kernel with step s standing for segment S-1-s; A_r^T is read from the
-// row-major tile column-wise, with scalar LDS reads).
-template <bool REV>
+// The same scan serves four uses (MODE):
+//  kScanCompose  the forward's C_0 = 0, C_{r+1} = A_r C_r + B_r over the
+//                segments (or, for the backward, over the pieces);
+//  kScanReverse  the backward's D_{S-1} = 0, D_{r-1} = A_r^T D_r + E_r: step s
+//                stands for segment S-1-s, and A_r^T is read from the
+//                row-major tile column-wise, with scalar LDS reads;
+//  kScanFold     per segment, its pieces' summaries folded into the
+//                segment's own: X <- A'_i X (+ B'_i) from X = [I | 0] over
+//                the pieces in order, one chain per (segment, head) and 16
+//                column blocks (8 of A_r, 8 of B_r); only the end is written;
+//  kScanPieces   per segment, every piece's carry-in: X = C_r (zero for a
+//                segment that does not continue a sequence), written at each
+//                piece, then X <- A'_i X + B'_i.
+// A transition that is structurally zero (its flag clear) is skipped.
+enum ScanMode { kScanCompose = 0, kScanReverse = 1, kScanFold = 2, kScanPieces = 3 };
+
+template <int MODE>
 __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem& sm) {
+  constexpr bool REV = MODE == kScanReverse;
+  constexpr bool CHAINS = MODE == kScanFold || MODE == kScanPieces;
+  constexpr int NCB = MODE == kScanFold ? 2 * kComposeColumnBlocks : kComposeColumnBlocks;
   const int H = p.H;
   const int xcd = blockIdx.x % 8;
   const int kq = blockIdx.x / 8;
-  const int cb = kq % kComposeColumnBlocks;
-  const int hl = xcd + 8 * (kq / kComposeColumnBlocks);
-  if (hl >= p.hn) return;
-  const int h = p.h0 + hl;
+  const int cb = kq % NCB;
+  const int unit = xcd + 8 * (kq / NCB);   // (chain, head), its column blocks on one XCD
+  if (unit >= (CHAINS ? p.chains : 1) * p.hn) return;
+  const int chain = CHAINS ? unit / p.hn : 0;
+  const int h = p.h0 + unit % p.hn;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lc = lane & 15;    // column within the block (and row within the tile for A)
   const int lj = lane >> 4;    // k slot: k = 32 lj + s
-  const int col = kComposeColumns * cb + lc;
+  const bool bpart = MODE == kScanFold && cb >= kComposeColumnBlocks;   // a column block of B_r
+  const int col = kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + lc;
   const int row0 = 16 * wave;
 
+  // the chain: steps over the segments, or over one segment's pieces
+  int base = 0, S = p.S;
+  if (CHAINS) {
+    base = p.plan[p.L.useg_piece_ptr + chain];
+    const int len = p.plan[p.L.useg_piece_ptr + chain + 1] - base;
+    S = MODE == kScanFold ? len + 1 : len;   // a fold applies every piece, then writes
+  }
+  auto seg_of = [&](const int r) { return REV ? S - 1 - r : base + r; };
   // A_r, coalesced: piece u of lane tid is 16-byte piece u * 512 + tid of the
   // row-major matrix, i.e. row 16u + tid / 32, floats 4 (tid % 32) ..
-  const int S = p.S;
-  auto seg_of = [&](const int r) { return REV ? S - 1 - r : r; };
   auto load_a = [&](const int r, f32x4 (&a)[kAPieces]) {
     const float* src = p.transitions + (static_cast<size_t>(seg_of(r)) * H + h) * KD * KD;
 #pragma unroll
@@ -1424,11 +1448,19 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       st4(&sm.at[buf][(pc >> 5) * kAtStride + 4 * (pc & 31)], a[u]);
     }
   };
-  // this lane's rows of B_r, in the accumulator layout
+  // this lane's rows of B_r, in the accumulator layout (none for a fold's
+  // column block of A_r)
   auto load_b = [&](const int r, f32x4& bv) {
+    if (MODE == kScanFold && !bpart) return;
     const float* bsrc = p.updates + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bv[i] = bsrc[(row0 + 4 * lj + i) * VD + col];
+  };
+  // where step r's value goes: the carry of that segment or piece, or for a
+  // fold (last step only) the segment's transition or update
+  auto dest = [&](const int r) -> float* {
+    if (MODE == kScanFold) return (bpart ? p.out_b : p.out_a) + (static_cast<size_t>(chain) * H + h) * KD * VD;
+    return p.carry + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
   };
 
   // transition flags of steps [lbase, lbase + 64) as a wave-wide bit mask.
@@ -1442,7 +1474,7 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       const int idx = lbase + lane;
       // forward: A_idx is applied for idx < S-1; reverse: A_{S-1-idx}^T for
       // 1 <= idx < S-1 (D_{S-1} is zero, so A_{S-1} is never read)
-      const bool f = idx < S - 1 && (!REV || idx >= 1) && p.plan[p.L.seg_transition_live + seg_of(idx)] != 0;
+      const bool f = idx < S - 1 && (!REV || idx >= 1) && p.plan[p.live_off + seg_of(idx)] != 0;
       lmask = __builtin_amdgcn_ballot_w64(f);
     }
     return ((lmask >> (r - lbase)) & 1ull) != 0;
@@ -1458,7 +1490,7 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
   for (int d = 0; d < kComposeRing; ++d) {
     lv[d] = false;
     b_ring[d] = zero4();
-    if (d < p.S - 1) {
+    if (d < S - 1) {
       lv[d] = live_at(d);
       load_b(d, b_ring[d]);
       if (lv[d]) load_a(d, a_ring[d]);
@@ -1466,14 +1498,24 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
   }
   if (lv[0]) store_a(0, a_ring[0]);
   f32x4 cur = zero4();
+  if (MODE == kScanFold && !bpart) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = row0 + 4 * lj + i == col ? 1.f : 0.f;   // the identity
+  } else if (MODE == kScanPieces && p.plan[p.L.useg_carry_in + chain] != 0) {
+    const float* csrc = p.init + (static_cast<size_t>(chain) * H + h) * KD * VD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = csrc[(row0 + 4 * lj + i) * VD + col];
+  }
   for (int r0 = 0;; r0 += kComposeRing) {
 #pragma unroll
     for (int ph = 0; ph < kComposeRing; ++ph) {
       const int r = r0 + ph;            // r % kComposeRing == ph
-      float* cdst = p.carry + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
+      if (MODE != kScanFold || r == S - 1) {
+        float* cdst = dest(r);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
-      if (r == p.S - 1) return;
+        for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
+      }
+      if (r == S - 1) return;
       const int buf = r & 1;
       const bool live = lv[ph];
       f32x4 nxt = b_ring[ph];
@@ -1506,10 +1548,10 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       }
       // step r+1's A_r into the other tile
       const int p1 = (ph + 1) % kComposeRing;
-      if (r + 1 < p.S - 1 && lv[p1]) store_a(buf ^ 1, a_ring[p1]);
+      if (r + 1 < S - 1 && lv[p1]) store_a(buf ^ 1, a_ring[p1]);
       // step r + kComposeRing's operands into the slots step r has used up
       const int rn = r + kComposeRing;
-      if (rn < p.S - 1) {
+      if (rn < S - 1) {
         lv[ph] = live_at(rn);
         load_b(rn, b_ring[ph]);
         if (lv[ph]) load_a(rn, a_ring[ph]);
@@ -1521,12 +1563,22 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
 
 __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(ComposeParams p) {
   __shared__ ComposeSmem sm;
-  compose_scan<false>(p, sm);
+  compose_scan<kScanCompose>(p, sm);
 }
 
 __global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_reverse_kernel(ComposeParams p) {
   __shared__ ComposeSmem sm;
-  compose_scan<true>(p, sm);
+  compose_scan<kScanReverse>(p, sm);
+}
+
+__global__ void __launch_bounds__(kComposeThreads, 1) kda_fold_pieces_kernel(ComposeParams p) {
+  __shared__ ComposeSmem sm;
+  compose_scan<kScanFold>(p, sm);
+}
+
+__global__ void __launch_bounds__(kComposeThreads, 1) kda_piece_carry_kernel(ComposeParams p) {
+  __shared__ ComposeSmem sm;
+  compose_scan<kScanPieces>(p, sm);
 }
 
 }  // namespace kda

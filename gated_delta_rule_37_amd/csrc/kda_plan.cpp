@@ -24,9 +24,8 @@ int32_t locate(const std::vector<int32_t>& bounds, int32_t t) {
 
 }  // namespace
 
-extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
-                                 int32_t num_segments, const int32_t* custom_bounds,
-                                 kda_plan** out) {
+extern "C" int kda_plan_segments_pieces(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_segments,
+                                        const int32_t* custom_bounds, int32_t piece_tokens, kda_plan** out) {
   if (cu_seqlens == nullptr || out == nullptr) return KDA_ERR_INVALID_ARG;
   if (num_seqs < 1) return KDA_ERR_BAD_CU_SEQLENS;
   if (cu_seqlens[0] != 0) return KDA_ERR_BAD_CU_SEQLENS;
@@ -39,6 +38,7 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
   if (T > kda::kMaxTokens) return KDA_ERR_UNSUPPORTED;
   const int32_t S = num_segments;
   if (S < 1 || S > T) return KDA_ERR_BAD_SEGMENTS;
+  if (piece_tokens < 0 || piece_tokens % 32 != 0) return KDA_ERR_BAD_SEGMENTS;
 
   std::vector<int32_t> cu(cu_seqlens, cu_seqlens + num_seqs + 1);
   std::vector<int32_t> b(S + 1);
@@ -57,24 +57,53 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
   kda_plan* plan = new (std::nothrow) kda_plan;
   if (plan == nullptr) return KDA_ERR_NO_MEMORY;
   try {
+    // Pieces: each segment cut every piece_tokens tokens from its start (the
+    // last piece shorter); without pieces the pieces are the segments.
+    std::vector<int32_t> pb, piece_ptr(S + 1);
+    for (int32_t r = 0; r < S; ++r) {
+      piece_ptr[r] = static_cast<int32_t>(pb.size());
+      pb.push_back(b[r]);
+      if (piece_tokens > 0) {
+        for (int64_t x = static_cast<int64_t>(b[r]) + piece_tokens; x < b[r + 1]; x += piece_tokens)
+          pb.push_back(static_cast<int32_t>(x));
+      }
+    }
+    piece_ptr[S] = static_cast<int32_t>(pb.size());
+    pb.push_back(T);
+    const int32_t P = static_cast<int32_t>(pb.size()) - 1;
+    const bool pieces = P > S;
+
     plan->T = T;
     plan->N = num_seqs;
     plan->S = S;
-    std::vector<int32_t> first(S), last(S), carry(S), live(S), frag_ptr(S + 1);
+    plan->P = P;
+    plan->pieces = pieces;
+    // carry-in and live flags of a list of bounds (segments or pieces)
+    auto flags_of = [&](const std::vector<int32_t>& bb, int32_t R, std::vector<int32_t>& first,
+                        std::vector<int32_t>& last, std::vector<int32_t>& carry, std::vector<int32_t>& live) {
+      first.resize(R);
+      last.resize(R);
+      carry.resize(R);
+      live.resize(R);
+      for (int32_t r = 0; r < R; ++r) {
+        first[r] = locate(cu, bb[r]);
+        last[r] = locate(cu, bb[r + 1] - 1);
+        const bool starts_here = cu[first[r]] == bb[r];
+        carry[r] = (r > 0 && !starts_here) ? 1 : 0;
+        live[r] = (carry[r] && first[r] == last[r]) ? 1 : 0;
+      }
+    };
+    std::vector<int32_t> first, last, carry, live, frag_ptr(P + 1);
+    flags_of(pb, P, first, last, carry, live);
     std::vector<int32_t> f_seq, f_beg, f_end, f_seg, f_flags;
     frag_ptr[0] = 0;
-    for (int32_t r = 0; r < S; ++r) {
-      first[r] = locate(cu, b[r]);
-      last[r] = locate(cu, b[r + 1] - 1);
-      const bool starts_here = cu[first[r]] == b[r];
-      carry[r] = (r > 0 && !starts_here) ? 1 : 0;
-      live[r] = (carry[r] && first[r] == last[r]) ? 1 : 0;
+    for (int32_t r = 0; r < P; ++r) {
       for (int32_t n = first[r]; n <= last[r]; ++n) {
-        const int32_t lo = std::max(b[r], cu[n]);
-        const int32_t hi = std::min(b[r + 1], cu[n + 1]);
+        const int32_t lo = std::max(pb[r], cu[n]);
+        const int32_t hi = std::min(pb[r + 1], cu[n + 1]);
         int32_t flags = 0;
-        if (lo == b[r] && carry[r]) flags |= kda::kFragCarried;
-        if (hi == b[r + 1]) flags |= kda::kFragSegLast;
+        if (lo == pb[r] && carry[r]) flags |= kda::kFragCarried;
+        if (hi == pb[r + 1]) flags |= kda::kFragSegLast;
         if (hi == cu[n + 1]) flags |= kda::kFragSeqEnd;
         f_seq.push_back(n);
         f_beg.push_back(lo);
@@ -87,7 +116,7 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
     const int32_t F = static_cast<int32_t>(f_seq.size());
     plan->F = F;
     std::vector<int32_t> end_seg(num_seqs);
-    for (int32_t n = 0; n < num_seqs; ++n) end_seg[n] = locate(b, cu[n + 1] - 1);
+    for (int32_t n = 0; n < num_seqs; ++n) end_seg[n] = locate(pb, cu[n + 1] - 1);
     // launch order: longest fragments first (ties by index), so that the long
     // sequential chains are not the last to start
     std::vector<int32_t> order(F);
@@ -97,10 +126,10 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
     });
 
     std::vector<int32_t>& blob = plan->blob;
-    blob.reserve(4 + (S + 1) * 2 + S * 4 + F * 6 + num_seqs);
-    blob.insert(blob.end(), {T, num_seqs, S, F});
+    blob.reserve(4 + (P + 1) * 2 + P * 4 + F * 6 + num_seqs + (pieces ? 3 * S + 3 : 0));
+    blob.insert(blob.end(), {T, num_seqs, P, F});
     auto append = [&blob](const std::vector<int32_t>& a) { blob.insert(blob.end(), a.begin(), a.end()); };
-    append(b);
+    append(pb);
     append(first);
     append(last);
     append(carry);
@@ -113,13 +142,27 @@ extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs,
     append(f_flags);
     append(end_seg);
     append(order);
-    plan->layout = kda::blob_layout(S, F, num_seqs);
+    if (pieces) {
+      std::vector<int32_t> ufirst, ulast, ucarry, ulive;
+      flags_of(b, S, ufirst, ulast, ucarry, ulive);
+      blob.push_back(S);
+      append(b);
+      append(ucarry);
+      append(ulive);
+      append(piece_ptr);
+    }
+    plan->layout = kda::blob_layout(P, F, num_seqs, S, pieces);
   } catch (const std::bad_alloc&) {
     delete plan;
     return KDA_ERR_NO_MEMORY;
   }
   *out = plan;
   return KDA_OK;
+}
+
+extern "C" int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_segments,
+                                 const int32_t* custom_bounds, kda_plan** out) {
+  return kda_plan_segments_pieces(cu_seqlens, num_seqs, num_segments, custom_bounds, 0, out);
 }
 
 extern "C" int kda_plan_blob(const kda_plan* plan, const int32_t** blob, size_t* n_int32) {
@@ -136,6 +179,12 @@ extern "C" int kda_plan_info(const kda_plan* plan, int32_t* T, int32_t* N, int32
   if (N) *N = plan->N;
   if (S) *S = plan->S;
   if (F) *F = plan->F;
+  return KDA_OK;
+}
+
+extern "C" int kda_plan_pieces(const kda_plan* plan, int32_t* P) {
+  if (plan == nullptr || P == nullptr) return KDA_ERR_INVALID_ARG;
+  *P = plan->P;
   return KDA_OK;
 }
 

@@ -85,7 +85,7 @@ int check_dims(const kda_plan* plan, const int32_t* plan_dev, int32_t H, int32_t
 
 BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
   const size_t mat = size_t(128) * 128 * sizeof(float);
-  const size_t seg_states = static_cast<size_t>(plan->S) * H * mat;
+  const size_t seg_states = static_cast<size_t>(plan->P) * H * mat;   // the backward works on pieces
   auto aligned = [](size_t x) { return (x + 255) & ~size_t(255); };
   BwdLayout L{};
   size_t o = 0;
@@ -112,10 +112,19 @@ BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
 
 size_t backward_workspace_need(const kda_plan* plan, int32_t H) { return backward_layout(plan, H).total; }
 
-size_t workspace_need(const kda_plan* plan, int32_t H) {
-  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->S);
-  return slots * static_cast<size_t>(H) * kChunkCacheBytes;
+PieceLayout piece_layout(const kda_plan* plan, int32_t H) {
+  const size_t slots = static_cast<size_t>((plan->T + 31) / 32) + static_cast<size_t>(plan->P);
+  const size_t cache = (slots * static_cast<size_t>(H) * kChunkCacheBytes + 255) & ~size_t(255);
+  const size_t states = plan->pieces ? static_cast<size_t>(plan->P) * H * 128 * 128 * sizeof(float) : 0;
+  PieceLayout L{};
+  L.transitions = cache;
+  L.updates = cache + states;
+  L.carry = cache + 2 * states;
+  L.total = cache + 3 * states;
+  return L;
 }
+
+size_t workspace_need(const kda_plan* plan, int32_t H) { return piece_layout(plan, H).total; }
 
 int check_gate_bound(float gate_lower_bound) {
   // NaN fails both comparisons

@@ -11,13 +11,19 @@
 
 namespace kda {
 
-// Bytes of the workspace (the chunk cache) a plan needs for H heads.
+// The forward's workspace for H heads: the chunk cache (256-byte aligned),
+// then, for a plan with pieces, the pieces' transitions, updates and
+// carry-ins (P x H states each).
+struct PieceLayout {
+  size_t transitions, updates, carry, total;
+};
+PieceLayout piece_layout(const kda_plan* plan, int32_t H);
 size_t workspace_need(const kda_plan* plan, int32_t H);
 
 // Byte offsets of the parts of the backward's workspace for H heads (each
-// 256-byte aligned): the forward's chunk cache, the forward's transitions,
+// 256-byte aligned): the forward's workspace, the forward's transitions,
 // updates and carry-ins recomputed, the backward summaries E and their
-// reverse compose D (each S x H states), the level-1 checkpoints
+// reverse compose D (each P x H states, per piece), the level-1 checkpoints
 // ((floor(T/32) + F) x H states) and the fragment launch's scratch
 // (min(F H, kBwdGrid) x kBwdScratchStates states).
 struct BwdLayout {

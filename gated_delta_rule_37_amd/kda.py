@@ -47,7 +47,8 @@ STATUS = {
 
 # Every symbol include/kda.h declares.
 SYMBOLS = (
-    "kda_plan_segments", "kda_plan_blob", "kda_plan_info", "kda_plan_destroy",
+    "kda_plan_segments", "kda_plan_segments_pieces", "kda_plan_pieces", "kda_plan_blob", "kda_plan_info",
+    "kda_plan_destroy",
     "kda_summary_bytes", "kda_workspace_bytes", "kda_segment_summaries", "kda_compose_summaries",
     "kda_apply_carry", "kda_forward", "kda_forward_noalloc", "kda_noalloc_max_workspace_bytes",
     "kda_backward", "kda_backward_workspace_bytes", "kda_status_string", "kda_last_hip_error",
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
     i32, p, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     L.kda_plan_segments.argtypes = [p, i32, i32, p, ctypes.POINTER(p)]
     L.kda_plan_segments.restype = ctypes.c_int
+    L.kda_plan_segments_pieces.argtypes = [p, i32, i32, p, i32, ctypes.POINTER(p)]
+    L.kda_plan_segments_pieces.restype = ctypes.c_int
+    L.kda_plan_pieces.argtypes = [p, p]
+    L.kda_plan_pieces.restype = ctypes.c_int
     L.kda_plan_blob.argtypes = [p, ctypes.POINTER(p), ctypes.POINTER(sz)]
     L.kda_plan_blob.restype = ctypes.c_int
     L.kda_plan_info.argtypes = [p, p, p, p, p]
@@ -126,9 +131,13 @@ def _check(status: int, where: str):
 
 
 class Plan:
-    """Host-side segment plan (``kda_plan_segments``); reusable across calls."""
+    """Host-side segment plan (``kda_plan_segments_pieces``); reusable across
+    calls.  ``piece_tokens`` > 0 (a multiple of 32) cuts every segment into
+    pieces of that many tokens that run in parallel; the calls' results stay
+    per segment.  ``S`` is the segment count, ``P`` the piece count (= S
+    without pieces), ``bounds`` the segment bounds."""
 
-    def __init__(self, cu_seqlens, num_segments: int, custom_bounds=None):
+    def __init__(self, cu_seqlens, num_segments: int, custom_bounds=None, piece_tokens: int = 0):
         L = lib()
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         self._cu = cu
@@ -137,17 +146,30 @@ class Plan:
             bounds = np.ascontiguousarray(np.asarray(custom_bounds, dtype=np.int32))
         self._bounds = bounds
         handle = ctypes.c_void_p()
-        st = L.kda_plan_segments(
+        st = L.kda_plan_segments_pieces(
             cu.ctypes.data, int(len(cu) - 1), int(num_segments),
-            None if bounds is None else bounds.ctypes.data, ctypes.byref(handle))
-        _check(st, "kda_plan_segments")
+            None if bounds is None else bounds.ctypes.data, int(piece_tokens), ctypes.byref(handle))
+        _check(st, "kda_plan_segments_pieces")
         self._h = handle
         ptr = ctypes.c_void_p()
         n = ctypes.c_size_t()
         _check(L.kda_plan_blob(self._h, ctypes.byref(ptr), ctypes.byref(n)), "kda_plan_blob")
         arr = (ctypes.c_int32 * n.value).from_address(ptr.value)
         self.blob = np.array(arr, dtype=np.int32, copy=True)
-        self.T, self.N, self.S, self.F = (int(x) for x in self.blob[:4])
+        self.T, self.N, self.P, self.F = (int(x) for x in self.blob[:4])
+        S = ctypes.c_int32()
+        _check(L.kda_plan_info(self._h, None, None, ctypes.byref(S), None), "kda_plan_info")
+        self.S = S.value
+        self.pieces = self.P > self.S
+        if self.pieces:
+            # the segment-level block after the piece-level arrays: [S, bounds[S+1], ...]
+            o = 4 + 6 * self.P + 2 + 6 * self.F + self.N
+            assert int(self.blob[o]) == self.S
+            self.bounds = self.blob[o + 1:o + 2 + self.S].copy()
+            self.segment_live = self.blob[o + 2 + 2 * self.S:o + 2 + 3 * self.S].copy()
+        else:
+            self.bounds = self.blob[4:4 + self.S + 1].copy()
+            self.segment_live = self.blob[4 + self.S + 1 + 3 * self.S:4 + self.S + 1 + 4 * self.S].copy()
         self._dev = {}
 
     @property
@@ -364,6 +386,24 @@ def noalloc_max_workspace_bytes() -> int:
 
 # storage formats of o accepted by kda_apply_carry (kda_o_format)
 O_FORMATS = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def auto_piece_tokens(cu_seqlens, num_segments: int, H: int, custom_bounds=None, target_items: int = 256,
+                      min_piece: int = 128) -> int:
+    """A piece length for ``Plan(..., piece_tokens=...)``: 0 (no pieces) when the
+    plain plan already gives the GPU's 256 compute units a (fragment, head)
+    item each; else the multiple of 32, at least ``min_piece``, that makes
+    about ``target_items`` pieces times heads (0 if no segment is longer).
+    Measured on the three small workloads (65536 tokens and more need none):
+    about one item per compute unit, with pieces of at least 128 tokens, is
+    where the shorter chunk chains stop paying for the longer scans."""
+    plain = Plan(cu_seqlens, num_segments, custom_bounds)
+    if plain.F * H >= 256:
+        return 0
+    b = plain.bounds
+    longest = int(np.max(b[1:] - b[:-1]))
+    L = max(int(min_piece), 32 * -(-(plain.T * H) // (int(target_items) * 32)))
+    return L if L < longest else 0
 
 
 def alloc_outputs(plan: Plan, H: int, K: int, V: int, device, o_dtype=torch.float32):

@@ -132,6 +132,24 @@ int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_s
                       const int32_t* custom_bounds, kda_plan** out);
 
 /*
+ * kda_plan_segments_pieces -- the same plan, with every segment cut into
+ * pieces of piece_tokens tokens from its start (the last one shorter) that
+ * the device calls run in parallel.  This fills the GPU where segments x
+ * heads are few (#136 Walkthrough: balanced contiguous shards); every call's
+ * results stay per segment (kda_segment_summaries folds the pieces'
+ * summaries into the segment's, kda_apply_carry scans the pieces' carry-ins
+ * from the segment's), and kda_workspace_bytes grows by 3 * P * H states of
+ * 64 KiB for the pieces' summaries and carry-ins.  piece_tokens = 0 is
+ * kda_plan_segments; otherwise it must be a multiple of 32
+ * (KDA_ERR_BAD_SEGMENTS).  Other arguments and errors as kda_plan_segments.
+ */
+int kda_plan_segments_pieces(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_segments,
+                             const int32_t* custom_bounds, int32_t piece_tokens, kda_plan** out);
+
+/* The plan's piece count P (S when it has no pieces). */
+int kda_plan_pieces(const kda_plan* plan, int32_t* P);
+
+/*
  * kda_plan_blob -- the plan's canonical int32 serialisation.  The device
  * entry points read a device copy of exactly these n_int32 words
  * (`plan_dev`, n_int32 * 4 bytes).  Layout:
@@ -145,7 +163,11 @@ int kda_plan_segments(const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_s
  * bit 2: ends at its segment's end; bit 4: ends at its sequence's end.
  * frag_order lists the fragments longest first (ties by index): the device
  * calls start them in that order, so that the longest sequential chains do
- * not start last (it changes no result).
+ * not start last (it changes no result).  In a plan with pieces (P > S) the
+ * seg_* arrays above describe the P pieces (the header holds P in place of
+ * S) and the blob ends with the segments' own block:
+ *   S, useg_bounds[S+1], useg_carry_in[S], useg_transition_live[S],
+ *   useg_piece_ptr[S+1] (segment r owns pieces [ptr[r], ptr[r+1])).
  * `*blob` stays valid until kda_plan_destroy.
  */
 int kda_plan_blob(const kda_plan* plan, const int32_t** blob, size_t* n_int32);

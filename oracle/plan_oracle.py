@@ -27,6 +27,15 @@ segment's end, 4 = ends at its sequence's end.  frag_order lists the fragments
 longest first (ties by index): the order in which they are worth starting, so
 that the long sequential ones do not start last (a scheduling choice, not part
 of the method).
+
+Pieces (a one-GPU scheduling choice, not on the pages): with piece_tokens > 0
+(a multiple of 32) every segment is cut every piece_tokens tokens from its
+start, the last piece shorter.  The arrays above then describe the P pieces
+(header [T, N, P, F]), and when P > S the blob ends with the segments' own
+block: S, seg_bounds[S+1], seg_carry_in[S], seg_transition_live[S],
+piece_ptr[S+1] (segment r owns pieces [piece_ptr[r], piece_ptr[r+1])).
+Without pieces (or when no segment is longer than piece_tokens) the blob is
+exactly the plain one.
 """
 from __future__ import annotations
 
@@ -53,7 +62,18 @@ def _seq_of_token(cu, t):
     raise AssertionError("token outside every sequence")
 
 
-def build_plan(cu_seqlens, num_segments, custom_bounds=None):
+def _flags(cu, bounds):
+    """Per span of ``bounds``: first and last sequence, carry-in, live."""
+    starts = set(cu[:-1])
+    R = len(bounds) - 1
+    first = [_seq_of_token(cu, bounds[r]) for r in range(R)]
+    last = [_seq_of_token(cu, bounds[r + 1] - 1) for r in range(R)]
+    carry = [1 if (r > 0 and bounds[r] not in starts) else 0 for r in range(R)]
+    live = [1 if (carry[r] and first[r] == last[r]) else 0 for r in range(R)]
+    return first, last, carry, live
+
+
+def build_plan(cu_seqlens, num_segments, custom_bounds=None, piece_tokens=0):
     """Return the plan as a dict of python lists plus the int32 blob."""
     cu = [int(x) for x in cu_seqlens]
     if len(cu) < 2:
@@ -78,15 +98,29 @@ def build_plan(cu_seqlens, num_segments, custom_bounds=None):
             if bounds[r + 1] <= bounds[r]:
                 raise PlanError("BAD_SEGMENTS", "custom bounds must be strictly increasing")
 
-    starts = set(cu[:-1])
-    seg_first = [_seq_of_token(cu, bounds[r]) for r in range(S)]
-    seg_last = [_seq_of_token(cu, bounds[r + 1] - 1) for r in range(S)]
-    carry = [1 if (r > 0 and bounds[r] not in starts) else 0 for r in range(S)]
-    live = [1 if (carry[r] and seg_first[r] == seg_last[r]) else 0 for r in range(S)]
+    piece_tokens = int(piece_tokens)
+    if piece_tokens < 0 or piece_tokens % 32:
+        raise PlanError("BAD_SEGMENTS", "piece_tokens must be a non-negative multiple of 32")
+    seg_bounds = bounds
+    pbounds, piece_ptr = [], []
+    for r in range(S):
+        piece_ptr.append(len(pbounds))
+        x = seg_bounds[r]
+        while x < seg_bounds[r + 1]:
+            pbounds.append(x)
+            if piece_tokens == 0:
+                break
+            x += piece_tokens
+    piece_ptr.append(len(pbounds))
+    pbounds.append(T)
+    P = len(pbounds) - 1
+    pieces = P > S
+    bounds = pbounds           # everything below is per piece
+    seg_first, seg_last, carry, live = _flags(cu, bounds)
 
     frag_ptr = [0]
     f_seq, f_beg, f_end, f_seg, f_flags = [], [], [], [], []
-    for r in range(S):
+    for r in range(P):
         for n in range(seg_first[r], seg_last[r] + 1):
             b = max(bounds[r], cu[n])
             e = min(bounds[r + 1], cu[n + 1])
@@ -109,16 +143,26 @@ def build_plan(cu_seqlens, num_segments, custom_bounds=None):
     frag_order = sorted(range(F), key=lambda f: (-(f_end[f] - f_beg[f]), f))
 
     plan = dict(
-        T=T, N=N, S=S, F=F,
+        T=T, N=N, S=P, F=F,
         seg_bounds=bounds, seg_first_seq=seg_first, seg_last_seq=seg_last,
         seg_carry_in=carry, seg_transition_live=live, seg_frag_ptr=frag_ptr,
         frag_seq=f_seq, frag_begin=f_beg, frag_end=f_end, frag_seg=f_seg,
         frag_flags=f_flags, seq_end_seg=seq_end_seg, frag_order=frag_order,
     )
-    blob = [T, N, S, F]
+    blob = [T, N, P, F]
     for key in ("seg_bounds", "seg_first_seq", "seg_last_seq", "seg_carry_in",
                 "seg_transition_live", "seg_frag_ptr", "frag_seq", "frag_begin",
                 "frag_end", "frag_seg", "frag_flags", "seq_end_seg", "frag_order"):
         blob.extend(plan[key])
+    plan["segments"] = S
+    plan["segment_bounds"] = seg_bounds
+    plan["piece_ptr"] = piece_ptr
+    if pieces:
+        _, _, ucarry, ulive = _flags(cu, seg_bounds)
+        blob.append(S)
+        blob.extend(seg_bounds)
+        blob.extend(ucarry)
+        blob.extend(ulive)
+        blob.extend(piece_ptr)
     plan["blob"] = np.asarray(blob, dtype=np.int32)
     return plan

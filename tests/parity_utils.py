@@ -30,12 +30,12 @@ def to_device(x, dev="cuda:0"):
     return {n: x[n].to(dev) for n in NAMES}
 
 
-def run_gpu(x, cu, S, bounds=None, dev="cuda:0", h0=None, gate_lower_bound=None):
-    plan = kda.Plan(cu, S, bounds)
+def run_gpu(x, cu, S, bounds=None, dev="cuda:0", h0=None, gate_lower_bound=None, piece_tokens=0, groups=1):
+    plan = kda.Plan(cu, S, bounds, piece_tokens)
     d = to_device(x, dev)
     init = None if h0 is None else h0.to(dev)
     out = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=init,
-                      gate_lower_bound=gate_lower_bound)
+                      gate_lower_bound=gate_lower_bound, groups=groups)
     torch.cuda.synchronize()
     out.pop("workspace")   # an internal cache between the two passes, not an output
     return plan, out
@@ -57,7 +57,7 @@ def run_oracle(x, cu, plan, heads=None, want_o=True, h0=None, gate_lower_bound=N
     None); ``gate_lower_bound`` the safe gate's bound (or None)."""
     f = oracle_inputs(x, heads)
     f["g"] = ko.safe_gate(f["g"], gate_lower_bound)
-    bounds = plan.blob[4:4 + plan.S + 1].tolist()
+    bounds = plan.bounds.tolist()
     init = None
     if h0 is not None:
         init = h0.double().numpy()

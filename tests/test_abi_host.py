@@ -321,3 +321,56 @@ def test_backward_validates_before_launch():
         want = -8 if name == "ws" else -9
         assert call(**short) == want, name
     assert L.kda_last_hip_error() == 0
+
+
+PIECES_GOLDEN = os.path.join(ROOT, "tests", "golden", "plan_pieces_cases.json")
+
+
+@pytest.mark.parametrize("case", json.load(open(PIECES_GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_pieces_plan_blob_matches_golden(case):
+    plan = kda.Plan(case["cu_seqlens"], case["segments"], case["custom_bounds"], case["piece_tokens"])
+    assert plan.blob.tolist() == case["blob"]
+    assert plan.S == case["segments"] and plan.P > plan.S and plan.pieces
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_pieces_plan_blob_matches_oracle_random(seed):
+    rng = np.random.default_rng(3000 + seed)
+    N = int(rng.integers(1, 20))
+    lens = rng.integers(1, 400, size=N)
+    cu = [0] + np.cumsum(lens).astype(int).tolist()
+    T = cu[-1]
+    S = int(rng.integers(1, min(T, 12) + 1))
+    bounds = None
+    if seed % 3 == 0 and S > 1:
+        cuts = sorted(rng.choice(np.arange(1, T), size=S - 1, replace=False).tolist())
+        bounds = [0] + cuts + [T]
+    L = 32 * int(rng.integers(1, 8))
+    want = po.build_plan(cu, S, bounds, L)["blob"]
+    plan = kda.Plan(cu, S, bounds, L)
+    np.testing.assert_array_equal(plan.blob, want)
+    P = ctypes.c_int32()
+    assert kda.lib().kda_plan_pieces(plan.handle, ctypes.byref(P)) == 0
+    assert P.value == plan.P == int(want[2])
+    assert plan.bounds.tolist() == (bounds if bounds is not None else [(r * T) // S for r in range(S + 1)])
+
+
+def test_pieces_plan_refuses_bad_piece_length():
+    L = kda.lib()
+    out = ctypes.c_void_p()
+    cu = (ctypes.c_int32 * 2)(0, 100)
+    for bad in (-32, 16, 33):
+        assert L.kda_plan_segments_pieces(cu, 1, 2, None, bad, ctypes.byref(out)) == -3
+    assert L.kda_plan_pieces(None, None) == -1
+
+
+def test_pieces_plan_workspace_grows_by_piece_states():
+    """kda_workspace_bytes: the chunk cache over pieces, then 3 P H states."""
+    plain = kda.Plan([0, 1000], 2)
+    cut = kda.Plan([0, 1000], 2, None, 128)
+    H = 3
+    cache = lambda P: (((1000 + 31) // 32 + P) * H * 4096 + 255) // 256 * 256
+    assert plain.workspace_bytes(H) == ((1000 + 31) // 32 + 2) * H * 4096
+    assert cut.P == 8
+    assert cut.workspace_bytes(H) == cache(8) + 3 * 8 * H * 65536
+    assert cut.summary_bytes(H) == plain.summary_bytes(H)   # results stay per segment

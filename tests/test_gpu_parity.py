@@ -158,7 +158,7 @@ def test_pure_decay_beta_zero():
     got = pu.gpu_numpy(out)
     assert not got["o"].any() and not got["B"].any() and not got["final"].any()
     g = pu.oracle_inputs(x)["g"]
-    b = plan.blob[4:4 + S + 1]
+    b = plan.bounds
     for r in range(1, S):
         for h in range(H):
             want = np.diag(np.exp(g[b[r]:b[r + 1], h].sum(0)))

@@ -70,3 +70,49 @@ def test_plan_invariants_random(seed):
     else:
         plan = po.build_plan(cu, S)
     _check_invariants(cu, plan)
+
+
+PIECES_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "plan_pieces_cases.json")
+
+
+@pytest.mark.parametrize("case", json.load(open(PIECES_GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_pieces_plan_matches_hand_derived_blob(case):
+    plan = po.build_plan(case["cu_seqlens"], case["segments"], case["custom_bounds"], case["piece_tokens"])
+    assert plan["blob"].tolist() == case["blob"]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_pieces_plan_invariants_random(seed):
+    """Pieces partition every segment at multiples of piece_tokens from its
+    start; the per-piece arrays obey the segment invariants; piece_ptr maps
+    segments to their pieces; larger pieces than any segment give the plain
+    plan's blob."""
+    rng = np.random.default_rng(500 + seed)
+    N = int(rng.integers(1, 6))
+    lens = rng.integers(1, 120, size=N)
+    cu = [0] + list(np.cumsum(lens).astype(int))
+    T = cu[-1]
+    S = int(rng.integers(1, min(T, 6) + 1))
+    L = 32 * int(rng.integers(1, 4))
+    plan = po.build_plan(cu, S, None, L)
+    _check_invariants(cu, plan)
+    segb, ptr = plan["segment_bounds"], plan["piece_ptr"]
+    pb = plan["seg_bounds"]
+    assert ptr[0] == 0 and ptr[-1] == plan["S"]
+    for r in range(S):
+        want = list(range(segb[r], segb[r + 1], L))
+        assert pb[ptr[r]:ptr[r + 1]] == want
+    plain = po.build_plan(cu, S)
+    if plan["S"] == S:
+        assert plan["blob"].tolist() == plain["blob"].tolist()
+    else:
+        assert len(plan["blob"]) > len(plain["blob"])
+    big = po.build_plan(cu, S, None, 32 * ((T + 31) // 32))
+    assert big["blob"].tolist() == plain["blob"].tolist()
+
+
+@pytest.mark.parametrize("bad", [-32, 16, 33])
+def test_pieces_plan_rejects_bad_piece_length(bad):
+    with pytest.raises(po.PlanError) as e:
+        po.build_plan([0, 100], 2, None, bad)
+    assert e.value.kind == "BAD_SEGMENTS"
