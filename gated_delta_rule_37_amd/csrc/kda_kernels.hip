@@ -1541,10 +1541,15 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
             aop[q] = ld4(&sm.at[buf][(row0 + lc) * kAtStride + 32 * lj + 4 * q]);
           }
         }
+        // four independent accumulator chains (k slot e of every MFMA group),
+        // summed at the end: the MFMAs issue back to back instead of each
+        // waiting for the previous one's result
+        f32x4 acc[4] = {nxt, zero4(), zero4(), zero4()};
 #pragma unroll
         for (int q = 0; q < 8; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nxt = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], nxt, 0, 0, 0);
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], acc[e], 0, 0, 0);
+        nxt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
       // step r+1's A_r into the other tile
       const int p1 = (ph + 1) % kComposeRing;
