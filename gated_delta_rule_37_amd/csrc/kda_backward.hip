@@ -66,8 +66,8 @@ struct alignas(16) TokGroup {
 struct alignas(16) BwdSmem {
   TokGroup tg[2];                 // by group parity
   float colpart[2][NGRP][BD];     // row-sum partials, by exchange parity
-  float rowpart[4][2][BD];        // column sums of the two waves of a row group
-  float red[2];                   // dbeta: the sums of waves 0 and 1
+  float rowpart[3][2][BD];        // column sums of the two waves of a row group
+  float red[4];                   // dbeta's and u.do's sums of waves 0 and 1
 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -363,27 +363,32 @@ __device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h
   const float beta = tg.beta[m];
   const float du = x.col_sum(add_qdo(x, tg, m, doc, ds));
   const float dp = -beta * du;
-  if (x.wave < 2) {   // row group 0 (tid < 128, a wave-uniform test): dv, and the terms of dbeta
+  if (x.wave < 2) {   // row group 0 (tid < 128, a wave-uniform test): dv, dbeta's and u.do's terms
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.c, 0, 0);
-    const float s = wave_sum(du * (tg.v[m][x.c] - pp));
-    if (x.lane == 0) x.sm.red[x.wave] = s;
+    const float sb = wave_sum(du * (tg.v[m][x.c] - pp));
+    const float su = wave_sum(u * doc);
+    if (x.lane == 0) {
+      x.sm.red[x.wave] = sb;
+      x.sm.red[2 + x.wave] = su;
+    }
   }
-  // column sums of four row quantities; lanes with bits 0-1 clear publish
+  // column sums of three row quantities (S = S_{t-1}, e = e^g of the row):
+  //   dq_r = e_r sum_c S do + k_r (u . do)
+  //   dk_r = sum_c (dS u + e_r S dp)
+  //   dg_r = e_r sum_c S (dS + k_r dp)
+  // lanes with bits 0-1 clear publish
   const int half = x.wave & 1;
   const bool pub = (x.lane & 3) == 0;
   const int row = NR * x.grp + ridx(x.lane);
   const float* krow = &tg.k[m][r0];
   const float* drow = &tg.dec[m][r0];
-  const float q0 = wave_rows_reduce(                                         // S_t do
-      [&](const int i) { return fmaf(drow[i], st[i], krow[i] * u) * doc; }, x.lane);
-  const float q1 = wave_rows_reduce([&](const int i) { return ds[i] * u; }, x.lane);        // dS u
-  const float q2 = wave_rows_reduce([&](const int i) { return st[i] * dp; }, x.lane);       // S dp
-  const float q3 = wave_rows_reduce([&](const int i) { return ds[i] * st[i]; }, x.lane);    // dS o S
+  const float q0 = wave_rows_reduce([&](const int i) { return st[i] * doc; }, x.lane);
+  const float q1 = wave_rows_reduce([&](const int i) { return fmaf(ds[i], u, drow[i] * (st[i] * dp)); }, x.lane);
+  const float q2 = wave_rows_reduce([&](const int i) { return st[i] * fmaf(krow[i], dp, ds[i]); }, x.lane);
   if (pub) {
     x.sm.rowpart[0][half][row] = q0;
     x.sm.rowpart[1][half][row] = q1;
     x.sm.rowpart[2][half][row] = q2;
-    x.sm.rowpart[3][half][row] = q3;
   }
   cotangent_step(x, tg, m, dp, ds);
   __syncthreads();
@@ -392,13 +397,12 @@ __device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h
     const float x1 = x.sm.rowpart[0][0][r] + x.sm.rowpart[0][1][r];
     const float x2 = x.sm.rowpart[1][0][r] + x.sm.rowpart[1][1][r];
     const float x3 = x.sm.rowpart[2][0][r] + x.sm.rowpart[2][1][r];
-    const float x4 = x.sm.rowpart[3][0][r] + x.sm.rowpart[3][1][r];
     const float dr = tg.dec[m][r], kr = tg.k[m][r];
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x1), rsrc(p.dq + tk * BD, BD * 4), 4 * r, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x3, x2)), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0,
-                                          0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * fmaf(kr, x3, x4)), rsrc(p.dg + tk * BD, BD * 4), 4 * r,
-                                          0, 0);
+    const float ud = x.sm.red[2] + x.sm.red[3];
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x1, kr * ud)), rsrc(p.dq + tk * BD, BD * 4),
+                                          4 * r, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x2), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * x3), rsrc(p.dg + tk * BD, BD * 4), 4 * r, 0, 0);
     if (r == 0) p.dbeta[tk] = x.sm.red[0] + x.sm.red[1];
   }
 }

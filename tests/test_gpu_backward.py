@@ -87,3 +87,39 @@ def test_backward_deterministic():
     for o in outs[1:]:
         for key in ("dq", "dk", "dv", "dg", "dbeta"):
             assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_bench_workload_last_segments_sampled_head():
+    """The backward at the bench workload's full size (65536 tokens x 32
+    heads, 64 segments) as bench.py runs it.  One head's gradients over the
+    last two segments (2048 tokens) depend on the forward state at their start
+    and on nothing after them, so the oracle's backward of those tokens from
+    that state (its forward over the first 63488 tokens) gives them exactly;
+    segment 62's gradients include the cotangent D_62 = E_63 that the GPU
+    forms through the backward summaries and the reverse compose."""
+    w = synth.WORKLOADS["t65536_h32_s64"]
+    x = synth.workload_inputs(w)
+    cu = x["cu_seqlens"].tolist()
+    assert cu == [0, w.T]
+    plan = kda.Plan(cu, w.segments)
+    d = pu.to_device(x)
+    d_o = torch.randn(w.T, w.H, w.V, generator=torch.Generator().manual_seed(w.seed + 2000))
+    got = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o.cuda())
+    torch.cuda.synchronize()
+    h = 9
+    b = int(plan.bounds[w.segments - 2])
+    f = pu.oracle_inputs(x, [h])
+    _, c_in = ko.recurrence(f["q"][:b], f["k"][:b], f["v"][:b], f["g"][:b], f["beta"][:b], [0, b])
+    win = slice(b, w.T)
+    ref = ko.backward(f["q"][win], f["k"][win], f["v"][win], f["g"][win], f["beta"][win], [0, w.T - b],
+                      d_o[win, h:h + 1].double().numpy(), h0=c_in)
+    errs = {}
+    for key, want in zip(("dq", "dk", "dv", "dg", "dbeta"), ref):
+        have = got[key][win, h:h + 1].double().cpu().numpy()
+        assert np.isfinite(have).all(), key
+        scale = np.abs(want).max()
+        errs[key] = np.abs(have - want).max() / scale
+    print("[bench workload, head 9, last 2048 tokens] " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for key, e in errs.items():
+        assert e <= GRAD_RTOL, (key, e)
