@@ -29,8 +29,9 @@
 // wave by a transposing butterfly (lane-swap and DPP moves) and across the
 // two waves of a row group through LDS.  The fragment kernel keeps the state
 // every 32 tokens in global memory (level 1), recomputes a chunk's states
-// every 4 tokens into its workgroup's scratch (level 2), and each 4-token
-// group's per-token states in registers before walking it backwards.
+// every 4 tokens into its workgroup's scratch and its tokens' u and p into
+// LDS (level 2), and each 4-token group's per-token states in registers
+// (update-only steps) before walking it backwards.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -86,15 +87,12 @@ __device__ __forceinline__ Rsrc rsrc(const void* base, const uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
 }
 
-// A group's loads, in registers between their issue and their store to LDS.
-// Waves 0-1 load k and g, waves 2-3 q and v (4 bf16 of each per lane), waves
-// 4-5 d_o (4 floats), lanes 0-3 of wave 6 beta; bits 5-6 of tid select the
-// token m of the group, and a token past the group's n reads zero.
-struct Fetch {
-  u2 a, b;
-  f4 f;
-  uint32_t beta;
-};
+// A group's loads, in registers between their issue and their store to LDS
+// (four dwords, whatever the role).  Waves 0-1 load k and g, waves 2-3 q and v
+// (4 bf16 of each per lane), waves 4-5 d_o (4 floats), lanes 0-3 of wave 6
+// beta; bits 5-6 of tid select the token m of the group, and a token past the
+// group's n reads zero.
+using Fetch = u4;
 
 __device__ __forceinline__ void fetch_group(const BwdParams& p, const int h, const int t0, const int n, const int tid,
                                             const int wave, Fetch& x) {
@@ -108,16 +106,17 @@ __device__ __forceinline__ void fetch_group(const BwdParams& p, const int h, con
     const Rsrc ra = rsrc((kg ? p.k : p.q) + tok0 * BD, nrec);
     const Rsrc rb = rsrc((kg ? p.g : p.v) + tok0 * BD, nrec);
     const int off = m * row + 8 * (tid & 31);
-    x.a = __builtin_amdgcn_raw_buffer_load_b64(ra, off, 0, 0);
-    x.b = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(ra, off, 0, 0);
+    const u2 b = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+    x = u4{a[0], a[1], b[0], b[1]};
   } else if (wave < 6) {
     const uint32_t row = static_cast<uint32_t>(H) * BD * 4;
     const Rsrc rd = rsrc(p.d_o + tok0 * BD, (n - 1) * row + BD * 4);
-    x.f = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rd, m * row + 16 * (tid & 31), 0, 0));
+    x = __builtin_amdgcn_raw_buffer_load_b128(rd, m * row + 16 * (tid & 31), 0, 0);
   } else if (wave == 6) {
     const uint32_t nb = (n - 1) * H * 2 + 2;
     const int lane = tid & 63;
-    x.beta = __builtin_amdgcn_raw_buffer_load_b16(rsrc(p.beta + tok0, nb), lane < GT ? lane * H * 2 : nb, 0, 0);
+    x[0] = __builtin_amdgcn_raw_buffer_load_b16(rsrc(p.beta + tok0, nb), lane < GT ? lane * H * 2 : nb, 0, 0);
   }
 }
 
@@ -126,8 +125,8 @@ __device__ __forceinline__ void store_group(TokGroup& tg, const int n, const int
   if (wave < 4) {
     if (m >= n) return;
     const int e = 4 * (tid & 31);
-    const uint32_t wa[4] = {x.a[0] & 0xffffu, x.a[0] >> 16, x.a[1] & 0xffffu, x.a[1] >> 16};
-    const uint32_t wb[4] = {x.b[0] & 0xffffu, x.b[0] >> 16, x.b[1] & 0xffffu, x.b[1] >> 16};
+    const uint32_t wa[4] = {x[0] & 0xffffu, x[0] >> 16, x[1] & 0xffffu, x[1] >> 16};
+    const uint32_t wb[4] = {x[2] & 0xffffu, x[2] >> 16, x[3] & 0xffffu, x[3] >> 16};
     if (wave < 2) {
       f4 kk, dc;
 #pragma unroll
@@ -149,16 +148,16 @@ __device__ __forceinline__ void store_group(TokGroup& tg, const int n, const int
       *reinterpret_cast<f4*>(&tg.v[m][e]) = vv;
     }
   } else if (wave < 6) {
-    if (m < n) *reinterpret_cast<f4*>(&tg.dov[m][4 * (tid & 31)]) = x.f;
+    if (m < n) *reinterpret_cast<f4*>(&tg.dov[m][4 * (tid & 31)]) = __builtin_bit_cast(f4, x);
   } else if (wave == 6) {
     const int lane = tid & 63;
-    if (lane < n) tg.beta[lane] = bfv(x.beta);
+    if (lane < n) tg.beta[lane] = bfv(x[0]);
   }
 }
 
-// Keeps the scheduler from hoisting the LDS row loads of later 4-row slices
-// (with 16 waves per CU the load latency is hidden by the other waves; the
-// registers are not).
+// Keeps the scheduler from hoisting the LDS row loads of later steps above
+// this point (with 16 waves per CU the load latency is hidden by the other
+// waves; the registers are not).
 __device__ __forceinline__ void slice_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int CTRL>
@@ -464,6 +463,7 @@ __global__ void __launch_bounds__(kBwdThreads, 8) kda_backward_summary_kernel(Bw
 // longest-first order, with its own level-2 scratch.
 __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
+  __shared__ float up[GPC][GT][2][BD];   // u and p of a 32-token chunk's tokens, by group
   const int H = p.H;
   const int F = p.plan[3];
   const int items = F * p.hn;
@@ -540,34 +540,41 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
     for (int j = nch - 1; j >= 0; --j) {
       const int g0 = GPC * j;
       const int g1 = g0 + (j == nch - 1 ? top : GPC);   // the chunk's groups [g0, g1)
-      // level 2: the chunk's state every 4 tokens into the scratch
+      // level 2: the chunk's state every 4 tokens into the scratch, and every
+      // token's u and p (column c) into LDS
       get_ckpt(ck + static_cast<size_t>(j) * H * MAT, tid, run);
       for (int g = g0; g < g1; ++g) {
         group(g, g + 1 < g1 ? g + 1 : g1 - 1, [&](const TokGroup& tg, const int n) {
           put_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
-          if (g + 1 < g1) {
 #pragma unroll
-            for (int m = 0; m < GT; ++m) {
-              float u, pp;
-              if (m < n) fwd_step(x, tg, m, run, u, pp, true);
+          for (int m = 0; m < GT; ++m) {
+            float u, pp;
+            if (m < n) {
+              // (the state after the chunk's last group is not needed, but
+              // its tokens' u and p are, so every step updates)
+              fwd_step(x, tg, m, run, u, pp, true);
+              if (x.wave < 2) {
+                up[g - g0][m][0][x.c] = u;
+                up[g - g0][m][1][x.c] = pp;
+              }
             }
           }
         });
       }
-      // the groups backwards.  One forward pass from the group's first state
-      // (run, from the scratch) gives every token's u and p and the state
-      // before the last token; the state before token m < n - 1 is rebuilt
-      // from run by m update-only steps (u is known: no exchange).
+      // the groups backwards: the state before token m is rebuilt from the
+      // group's first state (run, from the scratch) by m update-only steps
+      // (u is known: no exchange, no barrier)
       for (int g = g1 - 1; g >= g0; --g) {
         group(g, g > g0 ? g - 1 : (j > 0 ? g0 - GPC : -1), [&](const TokGroup& tg, const int n) {
-          float uu[GT], pv[GT], w[NR];
+          float w[NR];
           get_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
+          const int t0 = beg + GT * g;
+          const float(&upg)[GT][2][BD] = up[g - g0];
 #pragma unroll
           for (int i = 0; i < NR; ++i) w[i] = run[i];
 #pragma unroll
-          for (int m = 0; m < GT; ++m)
-            if (m < n) fwd_step(x, tg, m, w, uu[m], pv[m], m + 1 < n);
-          const int t0 = beg + GT * g;
+          for (int m = 0; m + 1 < GT; ++m)
+            if (m + 1 < n) update_only(x, tg, m, upg[m][0][x.c], w);
 #pragma unroll
           for (int m = GT - 1; m >= 0; --m) {
             if (m < n) {
@@ -575,9 +582,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
 #pragma unroll
                 for (int i = 0; i < NR; ++i) w[i] = run[i];
 #pragma unroll
-                for (int q = 0; q < m; ++q) update_only(x, tg, q, uu[q], w);
+                for (int q = 0; q < m; ++q) update_only(x, tg, q, upg[q][0][x.c], w);
               }
-              rev_step(x, p, h, tg, m, t0 + m, w, ds, uu[m], pv[m]);
+              rev_step(x, p, h, tg, m, t0 + m, w, ds, upg[m][0][x.c], upg[m][1][x.c]);
             }
           }
         });
