@@ -67,8 +67,8 @@ struct alignas(16) TokGroup {
 struct alignas(16) BwdSmem {
   TokGroup tg[2];                 // by group parity
   float colpart[2][NGRP][BD];     // row-sum partials, by exchange parity
-  float rowpart[3][2][BD];        // column sums of the two waves of a row group
-  float red[4];                   // dbeta's and u.do's sums of waves 0 and 1
+  float rowpart[2][3][2][BD];     // column sums of the two waves of a row group, by token parity
+  float red[2][4];                // dbeta's and u.do's sums of waves 0 and 1, by token parity
 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -351,24 +351,32 @@ __device__ __forceinline__ void rev_cotangent(Ctx& x, const TokGroup& tg, const 
 }
 
 // The full reverse step of token m (global index t) from S_{t-1} = st, with
-// u and p of column c from the forward step: writes the token's gradients.
-__device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
+// u and p of column c from the forward pass, in two parts around a pending
+// tail: rev_begin adds q do^T and sums du over the rows (its exchange is the
+// step's only barrier); rev_rest writes dv, publishes the column sums of the
+// row quantities into rowpart[b] and red[b] and steps the cotangent back.
+// rev_tail (waves 0 and 1, one row each) turns a published token's sums into
+// its dq, dk, dg and dbeta after a later barrier: the next token's exchange,
+// or the barrier that ends a group.  Consecutive tokens alternate b.
+__device__ __forceinline__ float rev_begin(Ctx& x, const TokGroup& tg, const int m, float (&ds)[NR]) {
+  return x.col_sum(add_qdo(x, tg, m, tg.dov[m][x.c], ds));
+}
+
+__device__ __forceinline__ void rev_rest(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
                                          const int t, const float (&st)[NR], float (&ds)[NR], const float u,
-                                         const float pp) {
-  const int H = p.H;
-  const size_t tk = static_cast<size_t>(t) * H + h;
+                                         const float pp, const float du, const int b) {
+  const size_t tk = static_cast<size_t>(t) * p.H + h;
   const int r0 = NR * x.grp;
   const float doc = tg.dov[m][x.c];
   const float beta = tg.beta[m];
-  const float du = x.col_sum(add_qdo(x, tg, m, doc, ds));
   const float dp = -beta * du;
   if (x.wave < 2) {   // row group 0 (tid < 128, a wave-uniform test): dv, dbeta's and u.do's terms
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.c, 0, 0);
     const float sb = wave_sum(du * (tg.v[m][x.c] - pp));
     const float su = wave_sum(u * doc);
     if (x.lane == 0) {
-      x.sm.red[x.wave] = sb;
-      x.sm.red[2 + x.wave] = su;
+      x.sm.red[b][x.wave] = sb;
+      x.sm.red[b][2 + x.wave] = su;
     }
   }
   // column sums of three row quantities (S = S_{t-1}, e = e^g of the row):
@@ -385,25 +393,28 @@ __device__ __forceinline__ void rev_step(Ctx& x, const BwdParams& p, const int h
   const float q1 = wave_rows_reduce([&](const int i) { return fmaf(ds[i], u, drow[i] * (st[i] * dp)); }, x.lane);
   const float q2 = wave_rows_reduce([&](const int i) { return st[i] * fmaf(krow[i], dp, ds[i]); }, x.lane);
   if (pub) {
-    x.sm.rowpart[0][half][row] = q0;
-    x.sm.rowpart[1][half][row] = q1;
-    x.sm.rowpart[2][half][row] = q2;
+    x.sm.rowpart[b][0][half][row] = q0;
+    x.sm.rowpart[b][1][half][row] = q1;
+    x.sm.rowpart[b][2][half][row] = q2;
   }
   cotangent_step(x, tg, m, dp, ds);
-  __syncthreads();
-  if (x.wave < 2) {
-    const int r = x.tid;
-    const float x1 = x.sm.rowpart[0][0][r] + x.sm.rowpart[0][1][r];
-    const float x2 = x.sm.rowpart[1][0][r] + x.sm.rowpart[1][1][r];
-    const float x3 = x.sm.rowpart[2][0][r] + x.sm.rowpart[2][1][r];
-    const float dr = tg.dec[m][r], kr = tg.k[m][r];
-    const float ud = x.sm.red[2] + x.sm.red[3];
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x1, kr * ud)), rsrc(p.dq + tk * BD, BD * 4),
-                                          4 * r, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x2), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * x3), rsrc(p.dg + tk * BD, BD * 4), 4 * r, 0, 0);
-    if (r == 0) p.dbeta[tk] = x.sm.red[0] + x.sm.red[1];
-  }
+}
+
+__device__ __forceinline__ void rev_tail(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
+                                         const int t, const int b) {
+  if (x.wave >= 2) return;
+  const size_t tk = static_cast<size_t>(t) * p.H + h;
+  const int r = x.tid;
+  const float x1 = x.sm.rowpart[b][0][0][r] + x.sm.rowpart[b][0][1][r];
+  const float x2 = x.sm.rowpart[b][1][0][r] + x.sm.rowpart[b][1][1][r];
+  const float x3 = x.sm.rowpart[b][2][0][r] + x.sm.rowpart[b][2][1][r];
+  const float dr = tg.dec[m][r], kr = tg.k[m][r];
+  const float ud = x.sm.red[b][2] + x.sm.red[b][3];
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x1, kr * ud)), rsrc(p.dq + tk * BD, BD * 4), 4 * r,
+                                        0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x2), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * x3), rsrc(p.dg + tk * BD, BD * 4), 4 * r, 0, 0);
+  if (r == 0) p.dbeta[tk] = x.sm.red[b][0] + x.sm.red[b][1];
 }
 
 }  // namespace
@@ -584,9 +595,13 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
 #pragma unroll
                 for (int q = 0; q < m; ++q) update_only(x, tg, q, upg[q][0][x.c], w);
               }
-              rev_step(x, p, h, tg, m, t0 + m, w, ds, upg[m][0][x.c], upg[m][1][x.c]);
+              const float du = rev_begin(x, tg, m, ds);
+              if (m + 1 < n) rev_tail(x, p, h, tg, m + 1, t0 + m + 1, (m + 1) & 1);   // published before the barrier above
+              rev_rest(x, p, h, tg, m, t0 + m, w, ds, upg[m][0][x.c], upg[m][1][x.c], du, m & 1);
             }
           }
+          __syncthreads();
+          rev_tail(x, p, h, tg, 0, t0, 0);
         });
       }
     }
