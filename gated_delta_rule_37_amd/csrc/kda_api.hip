@@ -417,8 +417,15 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.scratch = reinterpret_cast<float*>(ws + W.scratch);
   // E_r, then D_r = the reverse scan of (A^T, E), then every fragment
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kda::kda_backward_summary_kernel, dim3(static_cast<uint32_t>(seg_blocks)),
-                     dim3(kda::kBwdThreads), 0, stream, p);
+  // many (piece, head) items: small workgroups, several per CU; few: large
+  // ones, each item's chain shorter
+  if (seg_blocks >= 1024) {
+    hipLaunchKernelGGL(kda::kda_backward_summary_narrow_kernel, dim3(static_cast<uint32_t>(seg_blocks)),
+                       dim3(kda::kBwdSummaryThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(kda::kda_backward_summary_kernel, dim3(static_cast<uint32_t>(seg_blocks)),
+                       dim3(kda::kBwdThreads), 0, stream, p);
+  }
   st = finish_launch();
   if (st != KDA_OK) return st;
   kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);

@@ -344,12 +344,6 @@ __device__ __forceinline__ void cotangent_step(const Ctx& x, const TokGroup& tg,
   }
 }
 
-// The cotangent-only reverse step (no gradients written): dS <- dS_{t-1}.
-__device__ __forceinline__ void rev_cotangent(Ctx& x, const TokGroup& tg, const int m, float (&ds)[NR]) {
-  const float du = x.col_sum(add_qdo(x, tg, m, tg.dov[m][x.c], ds));
-  cotangent_step(x, tg, m, -tg.beta[m] * du, ds);
-}
-
 // The full reverse step of token m (global index t) from S_{t-1} = st, with
 // u and p of column c from the forward pass, in two parts around a pending
 // tail: rev_begin adds q do^T and sums du over the rows (its exchange is the
@@ -423,44 +417,175 @@ __device__ __forceinline__ void rev_tail(Ctx& x, const BwdParams& p, const int h
 // due to the outputs of its first fragment (and that fragment's dfinal when
 // it ends a sequence) when nothing after the segment contributes.  Zero for a
 // segment that does not continue a sequence.  One workgroup per (r, head).
-__global__ void __launch_bounds__(kBwdThreads, 8) kda_backward_summary_kernel(BwdParams p) {
-  __shared__ BwdSmem sm;
+//
+// The cotangent-only step is short and its one exchange per token sets the
+// pace.  With many (segment, head) items the launch uses small workgroups
+// (256 threads, 64 rows of one column per thread), several per CU, whose
+// chains overlap; with few, 1024-thread workgroups (16 rows per thread),
+// whose chain per token is four times shorter.
+namespace {
+template <int ER>
+struct alignas(16) ESmem {
+  static constexpr int EG = BD / ER;
+  float k[2][GT][BD];       // token vectors by group parity
+  float dec[2][GT][BD];
+  float q[2][GT][BD];
+  float dov[2][GT][BD];
+  float beta[2][GT];
+  float colpart[2][EG][BD];
+};
+
+// Waves 0-1 load k and g (4 bf16 each), waves 2-3 q (4 bf16) and d_o (4
+// floats), lanes 0-3 of wave 0 also beta; bits 5-6 of tid select the token.
+struct EFetch {
+  u4 a;
+  f4 f;
+  uint32_t beta;
+};
+
+__device__ __forceinline__ void efetch(const BwdParams& p, const int h, const int t0, const int n, const int tid,
+                                       const int wave, EFetch& x) {
+  if (wave >= 4) return;
+  const int H = p.H;
+  const size_t tok0 = static_cast<size_t>(t0) * H + h;
+  const int m = (tid >> 5) & 3;
+  const uint32_t row = static_cast<uint32_t>(H) * BD * 2;
+  const uint32_t nrec = (n - 1) * row + BD * 2;
+  const int off = m * row + 8 * (tid & 31);
+  if (wave < 2) {
+    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rsrc(p.k + tok0 * BD, nrec), off, 0, 0);
+    const u2 b = __builtin_amdgcn_raw_buffer_load_b64(rsrc(p.g + tok0 * BD, nrec), off, 0, 0);
+    x.a = u4{a[0], a[1], b[0], b[1]};
+    if (wave == 0) {
+      const uint32_t nb = (n - 1) * H * 2 + 2;
+      const int lane = tid & 63;
+      x.beta = __builtin_amdgcn_raw_buffer_load_b16(rsrc(p.beta + tok0, nb), lane < GT ? lane * H * 2 : nb, 0, 0);
+    }
+  } else {
+    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rsrc(p.q + tok0 * BD, nrec), off, 0, 0);
+    x.a = u4{a[0], a[1], 0u, 0u};
+    const uint32_t rowf = static_cast<uint32_t>(H) * BD * 4;
+    x.f = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(p.d_o + tok0 * BD, (n - 1) * rowf + BD * 4),
+                                                                        m * rowf + 16 * (tid & 31), 0, 0));
+  }
+}
+
+template <int ER>
+__device__ __forceinline__ void estore(ESmem<ER>& sm, const int b, const int n, const int tid, const int wave,
+                                       const EFetch& x) {
+  if (wave >= 4) return;
+  const int m = (tid >> 5) & 3;
+  const int e = 4 * (tid & 31);
+  if (wave == 0 && (tid & 63) < n) sm.beta[b][tid & 63] = bfv(x.beta);
+  if (m >= n) return;
+  const uint32_t wa[4] = {x.a[0] & 0xffffu, x.a[0] >> 16, x.a[1] & 0xffffu, x.a[1] >> 16};
+  if (wave < 2) {
+    const uint32_t wb[4] = {x.a[2] & 0xffffu, x.a[2] >> 16, x.a[3] & 0xffffu, x.a[3] >> 16};
+    f4 kk, dc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kk[j] = bfv(wa[j]);
+      dc[j] = __builtin_amdgcn_exp2f(bfv(wb[j]) * kLog2eB);
+    }
+    *reinterpret_cast<f4*>(&sm.k[b][m][e]) = kk;
+    *reinterpret_cast<f4*>(&sm.dec[b][m][e]) = dc;
+  } else {
+    f4 qq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qq[j] = bfv(wa[j]);
+    *reinterpret_cast<f4*>(&sm.q[b][m][e]) = qq;
+    *reinterpret_cast<f4*>(&sm.dov[b][m][e]) = x.f;
+  }
+}
+
+template <int ER>
+__device__ __forceinline__ void backward_summary(const BwdParams& p) {
+  constexpr int EG = BD / ER;
+  __shared__ ESmem<ER> sm;
   const int r = blockIdx.x / p.hn;
   const int h = p.h0 + blockIdx.x % p.hn;
   const int H = p.H;
   const int tid = threadIdx.x;
-  Ctx x(sm, tid);
-  float ds[NR];
+  const int c = tid & (BD - 1);
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = ER * grp;
+  const int voff = 4 * (ER * BD * grp + c);   // row r0 + i at + 512 i
+  float ds[ER];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) ds[i] = 0.f;
+  for (int i = 0; i < ER; ++i) ds[i] = 0.f;
   if (p.plan[p.L.seg_carry_in + r] != 0) {
     const int f = p.plan[p.L.seg_frag_ptr + r];
     const int32_t flags = p.plan[p.L.frag_flags + f];
     const int32_t seq = p.plan[p.L.frag_seq + f];
     const int32_t beg = p.plan[p.L.frag_begin + f];
     const int32_t end = p.plan[p.L.frag_end + f];
-    if ((flags & kFragSeqEnd) && p.dfinal != nullptr)
-      load_state(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+    if ((flags & kFragSeqEnd) && p.dfinal != nullptr) {
+      const Rsrc rd = rsrc(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, MAT * 4);
+#pragma unroll
+      for (int i = 0; i < ER; ++i) ds[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, voff, i * 512, 0));
+    }
     const int ng = (end - beg + GT - 1) / GT;
+    int gb = 0, par = 0;
     {
-      Fetch f0;
-      fetch_group(p, h, beg + GT * (ng - 1), min(GT, end - beg - GT * (ng - 1)), tid, x.wave, f0);
-      store_group(sm.tg[0], min(GT, end - beg - GT * (ng - 1)), tid, x.wave, f0);
+      EFetch f0;
+      const int n0 = min(GT, end - beg - GT * (ng - 1));
+      efetch(p, h, beg + GT * (ng - 1), n0, tid, wave, f0);
+      estore(sm, 0, n0, tid, wave, f0);
     }
     for (int gi = ng - 1; gi >= 0; --gi) {
-      Fetch fx;
+      EFetch fx;
       __syncthreads();
-      const TokGroup& tg = sm.tg[x.gb];
       const int n = min(GT, end - beg - GT * gi);
-      if (gi > 0) fetch_group(p, h, beg + GT * (gi - 1), GT, tid, x.wave, fx);
+      if (gi > 0) efetch(p, h, beg + GT * (gi - 1), GT, tid, wave, fx);
 #pragma unroll
-      for (int m = GT - 1; m >= 0; --m)
-        if (m < n) rev_cotangent(x, tg, m, ds);
-      if (gi > 0) store_group(sm.tg[x.gb ^ 1], GT, tid, x.wave, fx);
-      x.gb ^= 1;
+      for (int m = GT - 1; m >= 0; --m) {
+        if (m < n) {
+          // dS += q do^T, du = dS^T k (rows), dS <- Diag(e^g) (dS + k dp^T)
+          const float doc = sm.dov[gb][m][c];
+          f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < ER / 4; ++j) {
+            const f4 qq = l4(&sm.q[gb][m][r0 + 4 * j]);
+            const f4 kk = l4(&sm.k[gb][m][r0 + 4 * j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ds[4 * j + e] = fmaf(qq[e], doc, ds[4 * j + e]);
+              acc[e] = fmaf(ds[4 * j + e], kk[e], acc[e]);
+            }
+          }
+          sm.colpart[par][grp][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+          __syncthreads();
+          float du = 0.f;
+#pragma unroll
+          for (int g2 = 0; g2 < EG; ++g2) du += sm.colpart[par][g2][c];
+          par ^= 1;
+          const float dp = -sm.beta[gb][m] * du;
+#pragma unroll
+          for (int j = 0; j < ER / 4; ++j) {
+            const f4 kk = l4(&sm.k[gb][m][r0 + 4 * j]);
+            const f4 dc = l4(&sm.dec[gb][m][r0 + 4 * j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds[4 * j + e] = dc[e] * fmaf(kk[e], dp, ds[4 * j + e]);
+          }
+        }
+      }
+      if (gi > 0) estore(sm, gb ^ 1, GT, tid, wave, fx);
+      gb ^= 1;
     }
   }
-  store_state(p.esum + (static_cast<size_t>(r) * H + h) * MAT, x.voff, ds);
+  const Rsrc re = rsrc(p.esum + (static_cast<size_t>(r) * H + h) * MAT, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < ER; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ds[i]), re, voff, i * 512, 0);
+}
+}  // namespace
+
+__global__ void __launch_bounds__(kBwdThreads, 8) kda_backward_summary_kernel(BwdParams p) {
+  backward_summary<BD * BD / kBwdThreads>(p);
+}
+
+__global__ void __launch_bounds__(kBwdSummaryThreads) kda_backward_summary_narrow_kernel(BwdParams p) {
+  backward_summary<BD * BD / kBwdSummaryThreads>(p);
 }
 
 // Every (fragment, head) item: the forward from the fragment's start state

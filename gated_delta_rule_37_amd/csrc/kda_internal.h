@@ -20,7 +20,8 @@ constexpr int kChunkCacheBytes = 4096;
 // Backward geometry: 1024-thread workgroups, a persistent fragment launch of
 // at most kBwdGrid workgroups with kBwdScratchStates 64 KiB states of scratch
 // each, and level-1 state checkpoints every kBwdCheckpointTokens tokens.
-constexpr int kBwdThreads = 1024;
+constexpr int kBwdThreads = 1024;          // the fragment launch
+constexpr int kBwdSummaryThreads = 256;    // the backward-summary launch
 constexpr int kBwdGrid = 256;
 constexpr int kBwdCheckpointTokens = 32;
 constexpr int kBwdScratchStates = kBwdCheckpointTokens / 4;
