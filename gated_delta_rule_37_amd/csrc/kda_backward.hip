@@ -14,7 +14,8 @@
 //     dS~  = dS + k dp^T,  dg = rowsum(dS~ o S~),  dS_{t-1} = Diag(e^g) dS~.
 // The cotangent recursion does not involve the state, so a segment maps the
 // cotangent at its end, D, to the one at its start affinely: A_r^T D + E_r.
-// The segments therefore run in parallel, as in the forward:
+// The segments (the pieces of a plan with pieces) therefore run in parallel,
+// as in the forward:
 //   kda_backward_summary_kernel   E_r: the first fragment of every carried
 //                                 segment reversed from its own outputs only;
 //   (reverse compose)             D_{r-1} = A_r^T D_r + E_r;

@@ -12,11 +12,11 @@ import parity_utils as pu
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("t1024_h4_s2", [0, 3]),
-    ("t4096_h8_s4", [0, 7]),
-    ("t8192_h16_s4", [11]),
-    ("varlen32k_h32_s8", [5]),
-    ("t65536_h32_s64", [17]),
+    ("t1024_h4_s2", [0, 1, 2, 3]),
+    ("t4096_h8_s4", [0, 3, 7]),
+    ("t8192_h16_s4", [0, 11, 15]),
+    ("varlen32k_h32_s8", [5, 31]),
+    ("t65536_h32_s64", [0, 31]),
     ("t4096_h8_s4_slow", [2]),
     ("t65536_h32_s64_slow", [30]),
     ("t65536_h32_s64_longmem", [12]),
