@@ -29,10 +29,10 @@
 // of eight partials; sums over columns (dq, dk, dg) are reduced within each
 // wave by a transposing butterfly (lane-swap and DPP moves) and across the
 // two waves of a row group through LDS.  The fragment kernel keeps the state
-// every 32 tokens in global memory (level 1), recomputes a chunk's states
-// every 4 tokens into its workgroup's scratch and its tokens' u and p into
-// LDS (level 2), and each 4-token group's per-token states in registers
-// (update-only steps) before walking it backwards.
+// every 32 tokens and every token's u and p in global memory (level 1),
+// recomputes a chunk's states every 4 tokens into its workgroup's scratch by
+// update-only steps (level 2; u known, no exchange), and each 4-token group's
+// per-token states in registers the same way before walking it backwards.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -600,7 +600,8 @@ __global__ void __launch_bounds__(kBwdSummaryThreads) kda_backward_summary_narro
 // longest-first order, with its own level-2 scratch.
 __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
-  __shared__ float up[GPC][GT][2][BD];   // u and p of a 32-token chunk's tokens, by group
+  // u and p of a 32-token chunk's tokens, by chunk parity and group
+  __shared__ float up[2][GPC][GT][2][BD];
   const int H = p.H;
   const int F = p.plan[3];
   const int items = F * p.hn;
@@ -625,13 +626,32 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
 
     // One token group: wait for its vectors, prefetch group gn's (gn < 0:
     // none), run body(tg, n), then store the prefetch into the other buffer.
-    auto group = [&](const int g, const int gn, auto&& body) {
+    // u and p of every token, written by level 1 (a thread per column of
+    // waves 0 and 1), read back a group ahead into LDS
+    const size_t up_token = static_cast<size_t>(H) * 2 * BD;   // floats between tokens
+    auto up_base = [&](const int t) { return p.upbuf + (static_cast<size_t>(t) * H + h) * 2 * BD; };
+    // One token group: wait for its vectors, prefetch group gn's (gn < 0:
+    // none; with gn_up also its tokens' u and p, one float per thread), run
+    // body(tg, n), then store the prefetch for the next group.
+    auto group = [&](const int g, const int gn, const bool gn_up, auto&& body) {
       Fetch fx;
+      float fu = 0.f;
+      const int um = tid >> 8, uk = (tid >> 7) & 1;   // the float this thread fetches: token um, u or p
       __syncthreads();
       const TokGroup& tg = sm.tg[x.gb];
-      if (gn >= 0) fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
+      if (gn >= 0) {
+        fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
+        if (gn_up) {
+          const uint32_t bytes = (gtokens(gn) - 1) * up_token * 4 + 2 * BD * 4;
+          fu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rsrc(up_base(beg + GT * gn), bytes), static_cast<int>(um * up_token * 4) + 4 * (uk * BD + x.c), 0, 0));
+        }
+      }
       body(tg, gtokens(g));
-      if (gn >= 0) store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
+      if (gn >= 0) {
+        store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
+        if (gn_up) up[(gn / GPC) & 1][gn % GPC][um][uk][x.c] = fu;
+      }
       x.gb ^= 1;
     };
 
@@ -651,14 +671,30 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
       store_group(sm.tg[x.gb], gtokens(0), tid, x.wave, f0);
     }
 
-    // level 1: the state at every chunk start, forward through the fragment
+    // level 1: the state at every chunk start and every token's u and p,
+    // forward through the fragment.  The last chunk's u and p also go
+    // straight to LDS, where its level 2 reads them next (its first group may
+    // be level 1's last, whose values a prefetch could not yet see).
+    const int glast = GPC * (nch - 1);   // the last chunk's first group
     for (int g = 0; g < ng; ++g) {
-      group(g, g + 1 < ng ? g + 1 : GPC * (nch - 1), [&](const TokGroup& tg, const int n) {
+      group(g, g + 1 < ng ? g + 1 : glast, false, [&](const TokGroup& tg, const int n) {
         if (g % GPC == 0) put_ckpt(ck + static_cast<size_t>(g / GPC) * H * MAT, tid, run);
+        const Rsrc ru = rsrc(up_base(beg + GT * g), (n - 1) * up_token * 4 + 2 * BD * 4);
 #pragma unroll
         for (int m = 0; m < GT; ++m) {
           float u, pp;
-          if (m < n) fwd_step(x, tg, m, run, u, pp, true);
+          if (m < n) {
+            fwd_step(x, tg, m, run, u, pp, true);
+            if (x.wave < 2) {
+              const int o = static_cast<int>(m * up_token * 4) + 4 * x.c;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), ru, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pp), ru, o + 4 * BD, 0, 0);
+              if (g >= glast) {
+                up[(nch - 1) & 1][g - glast][m][0][x.c] = u;
+                up[(nch - 1) & 1][g - glast][m][1][x.c] = pp;
+              }
+            }
+          }
         }
       });
     }
@@ -677,24 +713,17 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
     for (int j = nch - 1; j >= 0; --j) {
       const int g0 = GPC * j;
       const int g1 = g0 + (j == nch - 1 ? top : GPC);   // the chunk's groups [g0, g1)
-      // level 2: the chunk's state every 4 tokens into the scratch, and every
-      // token's u and p (column c) into LDS
+      // level 2: the chunk's state every 4 tokens into the scratch, by
+      // update-only steps with the u that level 1 kept (no exchange)
+      const auto& upj = up[j & 1];
       get_ckpt(ck + static_cast<size_t>(j) * H * MAT, tid, run);
       for (int g = g0; g < g1; ++g) {
-        group(g, g + 1 < g1 ? g + 1 : g1 - 1, [&](const TokGroup& tg, const int n) {
+        group(g, g + 1 < g1 ? g + 1 : g1 - 1, g + 1 < g1, [&](const TokGroup& tg, const int n) {
           put_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
+          if (g + 1 < g1) {   // the state after the chunk's last group is not needed
 #pragma unroll
-          for (int m = 0; m < GT; ++m) {
-            float u, pp;
-            if (m < n) {
-              // (the state after the chunk's last group is not needed, but
-              // its tokens' u and p are, so every step updates)
-              fwd_step(x, tg, m, run, u, pp, true);
-              if (x.wave < 2) {
-                up[g - g0][m][0][x.c] = u;
-                up[g - g0][m][1][x.c] = pp;
-              }
-            }
+            for (int m = 0; m < GT; ++m)
+              if (m < n) update_only(x, tg, m, upj[g - g0][m][0][x.c], run);
           }
         });
       }
@@ -702,11 +731,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
       // group's first state (run, from the scratch) by m update-only steps
       // (u is known: no exchange, no barrier)
       for (int g = g1 - 1; g >= g0; --g) {
-        group(g, g > g0 ? g - 1 : (j > 0 ? g0 - GPC : -1), [&](const TokGroup& tg, const int n) {
+        group(g, g > g0 ? g - 1 : (j > 0 ? g0 - GPC : -1), g == g0 && j > 0, [&](const TokGroup& tg, const int n) {
           float w[NR];
           get_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
           const int t0 = beg + GT * g;
-          const float(&upg)[GT][2][BD] = up[g - g0];
+          const float(&upg)[GT][2][BD] = upj[g - g0];
 #pragma unroll
           for (int i = 0; i < NR; ++i) w[i] = run[i];
 #pragma unroll

@@ -24,10 +24,11 @@ size_t workspace_need(const kda_plan* plan, int32_t H);
 // 256-byte aligned): the forward's workspace, the forward's transitions,
 // updates and carry-ins recomputed, the backward summaries E and their
 // reverse compose D (each P x H states, per piece), the level-1 checkpoints
-// ((floor(T/32) + F) x H states) and the fragment launch's scratch
-// (min(F H, kBwdGrid) x kBwdScratchStates states).
+// ((floor(T/32) + F) x H states), the fragment launch's scratch
+// (min(F H, kBwdGrid) x kBwdScratchStates states) and every token's u and p
+// (T x H x 2 x 128 floats).
 struct BwdLayout {
-  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, scratch, total;
+  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, scratch, up, total;
 };
 BwdLayout backward_layout(const kda_plan* plan, int32_t H);
 size_t backward_workspace_need(const kda_plan* plan, int32_t H);
