@@ -13,10 +13,10 @@ pytestmark = pytest.mark.gpu
 KEYS = ("o", "final_state", "transitions", "updates", "carry_in")
 
 
-def _run_both(T, H, cu, S, seed, gs, with_h0):
-    print(f"case noalloc: T={T} H={H} S={S} cu={cu} h0={with_h0}", flush=True)
+def _run_both(T, H, cu, S, seed, gs, with_h0, piece_tokens=0):
+    print(f"case noalloc: T={T} H={H} S={S} cu={cu} h0={with_h0} pieces={piece_tokens}", flush=True)
     x = synth.make_inputs(T, H, 128, 128, seed=seed, cu_seqlens=cu, gate_scale=gs)
-    plan = kda.Plan(cu, S)
+    plan = kda.Plan(cu, S, None, piece_tokens)
     d = pu.to_device(x)
     pd = plan.device_blob("cuda:0")
     h0 = synth.initial_states(len(cu) - 1, H, 128, 128, seed=seed + 1) if with_h0 else None
@@ -38,6 +38,12 @@ def _run_both(T, H, cu, S, seed, gs, with_h0):
 def test_noalloc_matches_forward_two_calls_second_smaller():
     _run_both(600, 4, [0, 37, 600], 6, seed=41, gs=0.3, with_h0=False)
     _run_both(200, 2, [0, 90, 200], 3, seed=42, gs=0.05, with_h0=True)
+
+
+def test_noalloc_with_pieces_matches_forward():
+    """A plan with pieces: the pieces' summaries and carry-ins live in the
+    fixed array too, behind the chunk cache."""
+    _run_both(700, 2, [0, 300, 700], 2, seed=43, gs=0.2, with_h0=True, piece_tokens=128)
 
 
 def test_noalloc_refuses_workspace_beyond_fixed_array():
