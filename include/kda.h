@@ -197,8 +197,10 @@ size_t kda_summary_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
  * chunk), so that the carry pass does not rebuild it.  Its contents are
  * opaque: what kda_segment_summaries writes for a head is valid for
  * kda_apply_carry on the same plan, H, head and inputs.
- * Size: (ceil(T / 32) + S) * H * 4096 bytes.  Returns 0 for a NULL plan,
- * H <= 0, or K, V other than 128.
+ * Size: (ceil(T / 32) + P) * H * 4096 bytes (P = S without pieces); with
+ * pieces (kda_plan_segments_pieces) rounded up to 256 bytes and followed by
+ * the pieces' transitions, updates and carry-ins, 3 * P * H * 65536 bytes.
+ * Returns 0 for a NULL plan, H <= 0, or K, V other than 128.
  */
 size_t kda_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 
