@@ -86,3 +86,39 @@ def test_bench_workload_bf16_output():
     o16 = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.bfloat16)["o"]
     torch.cuda.synchronize()
     assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("name,pieces", [("t65536_h32_s64", False), ("t8192_h16_s4", True)])
+def test_full_size_forward_bitwise_deterministic(name, pieces):
+    """Three launches of the whole forward at full size, in bench.py's
+    configuration, give bitwise the same outputs (every MFMA result that a
+    later instruction reads must have landed: a missing hazard wait shows up
+    here as launch-to-launch differences)."""
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w)
+    cu = x["cu_seqlens"].tolist()
+    L = kda.auto_piece_tokens(cu, w.segments, w.H) if pieces else 0
+    plan = kda.Plan(cu, w.segments, None, L)
+    d = pu.to_device(x)
+    first = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"])
+    for _ in range(2):
+        again = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"])
+        torch.cuda.synchronize()
+        for key in ("o", "final_state", "transitions", "updates", "carry_in"):
+            assert torch.equal(again[key], first[key]), key
+        del again
+
+
+def test_full_size_backward_bitwise_deterministic():
+    """Two backward calls on the bench workload give bitwise the same
+    gradients."""
+    w = synth.WORKLOADS["t65536_h32_s64"]
+    x = synth.workload_inputs(w)
+    plan = kda.Plan([0, w.T], w.segments)
+    d = pu.to_device(x)
+    d_o = torch.randn(w.T, w.H, w.V, generator=torch.Generator().manual_seed(7)).cuda()
+    a = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o)
+    b = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.equal(a[key], b[key]), key
