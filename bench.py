@@ -299,8 +299,13 @@ def main():
         # one line per workload, the pages' timing method only (no CPU leg)
         for name in list(synth.WORKLOADS) + list(synth.STRESS):
             w = synth.WORKLOADS.get(name) or synth.STRESS[name]
-            res = measure(args, w, synth.workload_inputs(w), torch, kda, synth)
+            x = synth.workload_inputs(w)
+            res = measure(args, w, x, torch, kda, synth)
+            if args.backward_steps > 0:
+                res["backward"] = measure_backward(args, w, x, torch, kda)
             print(json.dumps(res), flush=True)
+            del x, res
+            torch.cuda.empty_cache()
         return
 
     w = synth.WORKLOADS.get(args.workload) or synth.STRESS[args.workload]

@@ -347,17 +347,19 @@ def forward_noalloc(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, s
 
 
 def backward(plan: Plan, q, k, v, g, beta, d_o, d_final=None, initial_state=None, want_dh0=False,
-             stream=None, heads=None):
+             stream=None, heads=None, sentinel=None):
     """``kda_backward``: gradients of L = sum <o, d_o> + sum <final, d_final>.
-    Returns dict(dq, dk, dv, dg, dbeta, dh0) (fp32; dh0 None unless wanted)."""
+    Returns dict(dq, dk, dv, dg, dbeta, dh0) (fp32; dh0 None unless wanted).
+    ``heads`` = (begin, count) restricts the call to those heads; the output
+    buffers are filled with ``sentinel`` first when it is given."""
     T, H, K = k.shape
     V = v.shape[2]
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dq=torch.empty(T, H, K, **f32), dk=torch.empty(T, H, K, **f32),
-               dv=torch.empty(T, H, V, **f32), dg=torch.empty(T, H, K, **f32),
-               dbeta=torch.empty(T, H, **f32),
-               dh0=torch.empty(plan.N, H, K, V, **f32) if want_dh0 else None)
+    make = (lambda *shape: torch.empty(*shape, **f32)) if sentinel is None else (
+        lambda *shape: torch.full(shape, float(sentinel), **f32))
+    out = dict(dq=make(T, H, K), dk=make(T, H, K), dv=make(T, H, V), dg=make(T, H, K), dbeta=make(T, H),
+               dh0=make(plan.N, H, K, V) if want_dh0 else None)
     ins = _flat([
         _buf(q, torch.bfloat16, (T, H, K), "q"), _buf(k, torch.bfloat16, (T, H, K), "k"),
         _buf(v, torch.bfloat16, (T, H, V), "v"), _buf(g, torch.bfloat16, (T, H, K), "g"),

@@ -126,3 +126,28 @@ def test_bench_workload_last_segments_sampled_head():
           flush=True)
     for key, e in errs.items():
         assert e <= GRAD_RTOL, (key, e)
+
+
+def test_backward_head_range_touches_only_its_heads():
+    """kda_backward over heads [1, 3) of 4: those heads' gradients equal the
+    all-heads call's bit for bit, and the other heads' gradient buffers keep
+    a sentinel."""
+    T, H, cu = 260, 4, [0, 100, 260]
+    x = synth.make_inputs(T, H, 128, 128, seed=61, cu_seqlens=cu, gate_scale=0.3)
+    N = len(cu) - 1
+    gen = torch.Generator().manual_seed(62)
+    d_o = torch.randn(T, H, 128, generator=gen).cuda()
+    d_final = torch.randn(N, H, 128, 128, generator=gen).cuda()
+    h0 = synth.initial_states(N, H, 128, 128, seed=63).cuda()
+    plan = kda.Plan(cu, 3)
+    d = pu.to_device(x)
+    full = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d_final=d_final,
+                        initial_state=h0, want_dh0=True)
+    part = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d_final=d_final,
+                        initial_state=h0, want_dh0=True, heads=(1, 2), sentinel=-5.0)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        a, b = full[key], part[key]
+        hs = (slice(None), slice(1, 3))
+        assert torch.equal(a[hs], b[hs]), key
+        assert (b[:, 0] == -5.0).all() and (b[:, 3] == -5.0).all(), key
