@@ -1356,234 +1356,4 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
   else pipe_thelper<false>(p, sm, h, wave - 2 * NOWN, flags, seg, beg, end);
 }
 
-// Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r on FP32 matrix cores, for one
-// head and one block of 16 state columns (the columns of C never mix, so each
-// block scans on its own).  Wave w computes rows [16w, 16w + 16) as one
-// 16 x 16 tile (v_mfma_f32_16x16x4_f32; lane l, register i holds row
-// 16w + 4(l/16) + i, column l%16).  The k slots are permuted so that each
-// operand is contiguous: MFMA s, k slot j = l/16 stands for k = 32j + s, so a
-// lane's A operand over the whole product is A_r[16w + l%16][32j .. 32j + 31]
-// and its B operand C_r[32j .. 32j + 31][col].
-//
-// The scan is bound by moving A_r (64 KB per step and workgroup), not by the
-// products.  Read in the operand layout, each 16-byte load of a wave would
-// touch 64 rows' cache lines; instead the workgroup loads A_r with whole rows
-// per wave instruction, kComposeRing steps ahead into a ring of register
-// buffers (the step loop is unrolled over the ring, so no buffer is copied),
-// and stores it one step ahead into a double-buffered LDS tile with padded
-// rows, from which the operands are read without bank conflicts.  The carry
-// goes through a second, transposed LDS tile.  Every step has exactly one
-// barrier, so both tiles alternate by step parity.  The column blocks of a head
-// are numbered onto one XCD (workgroups are dealt to the eight XCDs in turn),
-// where they share its L2 copy of A_r.
-constexpr int kAtStride = KD + 4;   // floats per row of the A_r tile
-constexpr int kCtStride = KD + 4;   // floats per column of the transposed carry tile
-constexpr int kComposeRing = 4;     // operand ring: A_r is loaded kComposeRing - 1 steps before its store to LDS
-constexpr int kComposeWaves = kComposeThreads / 64;
-constexpr int kAPieces = KD * KD / 4 / kComposeThreads;   // 16-byte pieces of A_r per lane
-static_assert(kComposeWaves * 16 == KD, "compose: one 16-row tile per wave");
-
-struct alignas(16) ComposeSmem {
-  float at[2][KD * kAtStride];                  // A_r, row-major, by step parity
-  float ct[2][kComposeColumns * kCtStride];     // C_r[:, block] transposed, by step parity
-};
-
-// The same scan serves four uses (MODE):
-//  kScanCompose  the forward's C_0 = 0, C_{r+1} = A_r C_r + B_r over the
-//                segments (or, for the backward, over the pieces);
-//  kScanReverse  the backward's D_{S-1} = 0, D_{r-1} = A_r^T D_r + E_r: step s
-//                stands for segment S-1-s, and A_r^T is read from the
-//                row-major tile column-wise, with scalar LDS reads;
-//  kScanFold     per segment, its pieces' summaries folded into the
-//                segment's own: X <- A'_i X (+ B'_i) from X = [I | 0] over
-//                the pieces in order, one chain per (segment, head) and 16
-//                column blocks (8 of A_r, 8 of B_r); only the end is written;
-//  kScanPieces   per segment, every piece's carry-in: X = C_r (zero for a
-//                segment that does not continue a sequence), written at each
-//                piece, then X <- A'_i X + B'_i.
-// A transition that is structurally zero (its flag clear) is skipped.
-enum ScanMode { kScanCompose = 0, kScanReverse = 1, kScanFold = 2, kScanPieces = 3 };
-
-template <int MODE>
-__device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem& sm) {
-  constexpr bool REV = MODE == kScanReverse;
-  constexpr bool CHAINS = MODE == kScanFold || MODE == kScanPieces;
-  constexpr int NCB = MODE == kScanFold ? 2 * kComposeColumnBlocks : kComposeColumnBlocks;
-  const int H = p.H;
-  const int xcd = blockIdx.x % 8;
-  const int kq = blockIdx.x / 8;
-  const int cb = kq % NCB;
-  const int unit = xcd + 8 * (kq / NCB);   // (chain, head), its column blocks on one XCD
-  if (unit >= (CHAINS ? p.chains : 1) * p.hn) return;
-  const int chain = CHAINS ? unit / p.hn : 0;
-  const int h = p.h0 + unit % p.hn;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int lc = lane & 15;    // column within the block (and row within the tile for A)
-  const int lj = lane >> 4;    // k slot: k = 32 lj + s
-  const bool bpart = MODE == kScanFold && cb >= kComposeColumnBlocks;   // a column block of B_r
-  const int col = kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + lc;
-  const int row0 = 16 * wave;
-
-  // the chain: steps over the segments, or over one segment's pieces
-  int base = 0, S = p.S;
-  if (CHAINS) {
-    base = p.plan[p.L.useg_piece_ptr + chain];
-    const int len = p.plan[p.L.useg_piece_ptr + chain + 1] - base;
-    S = MODE == kScanFold ? len + 1 : len;   // a fold applies every piece, then writes
-  }
-  auto seg_of = [&](const int r) { return REV ? S - 1 - r : base + r; };
-  // A_r, coalesced: piece u of lane tid is 16-byte piece u * 512 + tid of the
-  // row-major matrix, i.e. row 16u + tid / 32, floats 4 (tid % 32) ..
-  auto load_a = [&](const int r, f32x4 (&a)[kAPieces]) {
-    const float* src = p.transitions + (static_cast<size_t>(seg_of(r)) * H + h) * KD * KD;
-#pragma unroll
-    for (int u = 0; u < kAPieces; ++u) a[u] = *reinterpret_cast<const f32x4*>(&src[4 * (u * kComposeThreads + tid)]);
-  };
-  auto store_a = [&](const int buf, const f32x4 (&a)[kAPieces]) {
-#pragma unroll
-    for (int u = 0; u < kAPieces; ++u) {
-      const int pc = u * kComposeThreads + tid;
-      st4(&sm.at[buf][(pc >> 5) * kAtStride + 4 * (pc & 31)], a[u]);
-    }
-  };
-  // this lane's rows of B_r, in the accumulator layout (none for a fold's
-  // column block of A_r)
-  auto load_b = [&](const int r, f32x4& bv) {
-    if (MODE == kScanFold && !bpart) return;
-    const float* bsrc = p.updates + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = bsrc[(row0 + 4 * lj + i) * VD + col];
-  };
-  // where step r's value goes: the carry of that segment or piece, or for a
-  // fold (last step only) the segment's transition or update
-  auto dest = [&](const int r) -> float* {
-    if (MODE == kScanFold) return (bpart ? p.out_b : p.out_a) + (static_cast<size_t>(chain) * H + h) * KD * VD;
-    return p.carry + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
-  };
-
-  // transition flags of steps [lbase, lbase + 64) as a wave-wide bit mask.
-  // (A plan read inside the loop would be a vector load whose wait also
-  // drains the prefetches and the carry stores in flight.)
-  uint64_t lmask = 0;
-  int lbase = -64;
-  auto live_at = [&](const int r) {
-    if (r - lbase >= 64) {
-      lbase = r & ~63;
-      const int idx = lbase + lane;
-      // forward: A_idx is applied for idx < S-1; reverse: A_{S-1-idx}^T for
-      // 1 <= idx < S-1 (D_{S-1} is zero, so A_{S-1} is never read)
-      const bool f = idx < S - 1 && (!REV || idx >= 1) && p.plan[p.live_off + seg_of(idx)] != 0;
-      lmask = __builtin_amdgcn_ballot_w64(f);
-    }
-    return ((lmask >> (r - lbase)) & 1ull) != 0;
-  };
-
-  // ring slot t % kComposeRing holds step t's operands: its A_r from the
-  // load until the store to LDS one step before its use, its B_r and flag
-  // until its use
-  f32x4 a_ring[kComposeRing][kAPieces];
-  f32x4 b_ring[kComposeRing];
-  bool lv[kComposeRing];
-#pragma unroll
-  for (int d = 0; d < kComposeRing; ++d) {
-    lv[d] = false;
-    b_ring[d] = zero4();
-    if (d < S - 1) {
-      lv[d] = live_at(d);
-      load_b(d, b_ring[d]);
-      if (lv[d]) load_a(d, a_ring[d]);
-    }
-  }
-  if (lv[0]) store_a(0, a_ring[0]);
-  f32x4 cur = zero4();
-  if (MODE == kScanFold && !bpart) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = row0 + 4 * lj + i == col ? 1.f : 0.f;   // the identity
-  } else if (MODE == kScanPieces && p.plan[p.L.useg_carry_in + chain] != 0) {
-    const float* csrc = p.init + (static_cast<size_t>(chain) * H + h) * KD * VD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = csrc[(row0 + 4 * lj + i) * VD + col];
-  }
-  for (int r0 = 0;; r0 += kComposeRing) {
-#pragma unroll
-    for (int ph = 0; ph < kComposeRing; ++ph) {
-      const int r = r0 + ph;            // r % kComposeRing == ph
-      if (MODE != kScanFold || r == S - 1) {
-        float* cdst = dest(r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
-      }
-      if (r == S - 1) return;
-      const int buf = r & 1;
-      const bool live = lv[ph];
-      f32x4 nxt = b_ring[ph];
-      if (live) {
-        mfma_result_fence(cur);
-        // the carry, transposed into LDS: column lc, rows row0 + 4lj + 0..3
-        st4(&sm.ct[buf][lc * kCtStride + row0 + 4 * lj], cur);
-      }
-      // A_r reached LDS in step r-1 (or before the loop) and the carry just
-      // now; the barrier also ends step r-1's reads of the other parity's
-      // tiles, which step r refills below.  Every step takes it, also one
-      // whose transition is structurally zero, so that the parity stays safe.
-      __syncthreads();
-      if (live) {
-        f32x4 bop[8], aop[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          bop[q] = ld4(&sm.ct[buf][lc * kCtStride + 32 * lj + 4 * q]);
-          if (REV) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) aop[q][e] = sm.at[buf][(32 * lj + 4 * q + e) * kAtStride + row0 + lc];
-          } else {
-            aop[q] = ld4(&sm.at[buf][(row0 + lc) * kAtStride + 32 * lj + 4 * q]);
-          }
-        }
-        // four independent accumulator chains (k slot e of every MFMA group),
-        // summed at the end: the MFMAs issue back to back instead of each
-        // waiting for the previous one's result
-        f32x4 acc[4] = {nxt, zero4(), zero4(), zero4()};
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], acc[e], 0, 0, 0);
-        nxt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      }
-      // step r+1's A_r into the other tile
-      const int p1 = (ph + 1) % kComposeRing;
-      if (r + 1 < S - 1 && lv[p1]) store_a(buf ^ 1, a_ring[p1]);
-      // step r + kComposeRing's operands into the slots step r has used up
-      const int rn = r + kComposeRing;
-      if (rn < S - 1) {
-        lv[ph] = live_at(rn);
-        load_b(rn, b_ring[ph]);
-        if (lv[ph]) load_a(rn, a_ring[ph]);
-      }
-      cur = nxt;
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_kernel(ComposeParams p) {
-  __shared__ ComposeSmem sm;
-  compose_scan<kScanCompose>(p, sm);
-}
-
-__global__ void __launch_bounds__(kComposeThreads, 1) kda_compose_reverse_kernel(ComposeParams p) {
-  __shared__ ComposeSmem sm;
-  compose_scan<kScanReverse>(p, sm);
-}
-
-__global__ void __launch_bounds__(kComposeThreads, 1) kda_fold_pieces_kernel(ComposeParams p) {
-  __shared__ ComposeSmem sm;
-  compose_scan<kScanFold>(p, sm);
-}
-
-__global__ void __launch_bounds__(kComposeThreads, 1) kda_piece_carry_kernel(ComposeParams p) {
-  __shared__ ComposeSmem sm;
-  compose_scan<kScanPieces>(p, sm);
-}
-
 }  // namespace kda
