@@ -21,6 +21,8 @@ namespace {
 
 constexpr int KD = 128;   // key dimension
 constexpr int VD = 128;   // value dimension
+// Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access.
+constexpr int kBufDword3 = 0x00020000;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -48,16 +50,21 @@ __device__ __forceinline__ f32x4 zero4() {
 //
 // Moving A_r (64 KB per step and workgroup) costs more than the products.
 // Each wave loads only the part of A_r its own tile multiplies (its 16 rows,
-// two whole rows per wave instruction), kComposeRing steps ahead into a ring
-// of register buffers (the step loop is unrolled over the ring, so no buffer
-// is copied), and turns it into the operand layout through an LDS region of
-// its own with padded rows.  No other wave touches that region, so the
-// wave stores step r+1's A and reads its operand back in the middle of step
-// r's products, off the scan's chain: the chain per step is the carry's
-// transposed store, one barrier, the carry's operand reads and the products.
-// The carry tile alternates by step parity.  The column blocks of a head are
-// numbered onto one XCD (workgroups are dealt to the eight XCDs in turn),
-// where they share its L2 copy of A_r.
+// two whole rows per wave instruction), kComposeRing steps ahead into a
+// ring of register buffers (the step loop is unrolled over the ring, so no
+// buffer is copied), and turns it into the operand layout through an LDS
+// region of its own with padded rows.  No other wave touches that region,
+// so the wave stores step r+1's A and reads its operand back in the middle
+// of step r's products, off the scan's chain: the chain per step is the
+// carry's transposed store, one barrier, the carry's operand reads and the
+// products.  The carry tile alternates by step parity.  The column blocks of
+// a head are numbered onto one XCD (workgroups are dealt to the eight XCDs
+// in turn), where they share its L2 copy of A_r.
+//
+// Global accesses go through buffer resources built in scalar registers
+// from each step's matrices, with lane offsets fixed for the whole scan: no
+// per-lane address is computed into a register that a load in flight still
+// owns (the compiler would make such a write wait for that load).
 constexpr int kAtStride = KD + 4;   // floats per row of a wave's A_r region
 constexpr int kCtStride = KD + 4;   // floats per column of the transposed carry tile
 constexpr int kComposeRing = 3;     // operand ring: A_r is loaded kComposeRing - 1 steps before its store to LDS
@@ -135,10 +142,14 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
   const int b_off = (row0 + (lane >> 2)) * VD + kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + 4 * (lane & 3);
   auto load_a = [&](const int r, f32x4 (&a)[kAPieces + 1]) {
     const size_t m = static_cast<size_t>(seg_of(r)) * H + h;
-    const float* src = p.transitions + m * KD * KD + a_off;
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.transitions + m * KD * KD), 0,
+                                                      KD * KD * 4, kBufDword3);
+    const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.updates + m * KD * VD), 0,
+                                                      KD * VD * 4, kBufDword3);
 #pragma unroll
-    for (int u = 0; u < kAPieces; ++u) a[u] = *reinterpret_cast<const f32x4*>(&src[u * a_step]);
-    a[kAPieces] = ld4(p.updates + m * KD * VD + b_off);
+    for (int u = 0; u < kAPieces; ++u)
+      a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * (a_off + u * a_step), 0, 0));
+    a[kAPieces] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, 4 * b_off, 0, 0));
   };
   // into the wave's region.  Forward: row-major 16 x kAtStride.  Reverse:
   // k-major, 16 floats per k, with a 16-float skew per 32 k so that the
@@ -169,6 +180,8 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       }
     }
   };
+  // this lane's four entries of a carry, as byte offsets in its matrix
+  const int c_off = 4 * ((row0 + 4 * lj) * VD + col);
   // where step r's value goes: the carry of that segment or piece, or for a
   // fold (last step only) the segment's transition or update
   auto dest = [&](const int r) -> float* {
@@ -240,9 +253,9 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       {
         // a fold writes its one destination at every step; the last write,
         // step S-1's, stays
-        float* cdst = dest(r);
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(dest(r), 0, KD * VD * 4, kBufDword3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur[i]), rc, c_off + 4 * i * VD, 0, 0);
       }
       if (r == S - 1) return;
       const int buf = r & 1;
