@@ -44,9 +44,10 @@ __device__ __forceinline__ f32x4 zero4() {
 // block scans on its own).  Wave w computes rows [16w, 16w + 16) as one
 // 16 x 16 tile (v_mfma_f32_16x16x4_f32; lane l, register i holds row
 // 16w + 4(l/16) + i, column l%16).  The k slots are permuted so that each
-// operand is contiguous: MFMA s, k slot j = l/16 stands for k = 32j + s, so a
-// lane's A operand over the whole product is A_r[16w + l%16][32j .. 32j + 31]
-// and its B operand C_r[32j .. 32j + 31][col].
+// operand is contiguous: MFMA s = 4q + e, k slot j = l/16 stands for
+// k = 32j + 4(q xor (j & 1)) + e, so a lane's A operand over the whole
+// product is A_r[16w + l%16][32j .. 32j + 31] and its B operand
+// C_r[32j .. 32j + 31][col], in 16-byte blocks.
 //
 // Moving A_r (64 KB per step and workgroup) costs more than the products.
 // Each wave loads only the part of A_r its own tile multiplies (its 16 rows,
@@ -65,8 +66,14 @@ __device__ __forceinline__ f32x4 zero4() {
 // from each step's matrices, with lane offsets fixed for the whole scan: no
 // per-lane address is computed into a register that a load in flight still
 // owns (the compiler would make such a write wait for that load).
-constexpr int kAtStride = KD + 4;   // floats per row of a wave's A_r region
-constexpr int kCtStride = KD + 4;   // floats per column of the transposed carry tile
+// Row strides of the LDS tiles.  A stride of 34 16-byte units (34 = 2 mod
+// 16) with the k-block order of kblk below makes every 16-byte access of the
+// scan conflict-free: the A stores, the operand reads and the transposed
+// carry stores.  (A 16-byte LDS access is served in four 16-lane passes:
+// lanes {0-3, 12-15, 20-27}, {4-11, 16-19, 28-31} and the same + 32; the
+// 16 lanes of a pass must touch 16 different 4-bank units.)
+constexpr int kAtStride = KD + 8;   // floats per row of a wave's A_r region
+constexpr int kCtStride = KD + 8;   // floats per column of the transposed carry tile
 constexpr int kComposeRing = 3;     // operand ring: A_r is loaded kComposeRing - 1 steps before its store to LDS
 constexpr int kComposeWaves = kComposeThreads / 64;
 constexpr int kAPieces = KD * KD / 4 / kComposeThreads;   // 16-byte pieces of A_r per lane
@@ -115,7 +122,11 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lc = lane & 15;    // column within the block (and row within the tile for A)
-  const int lj = lane >> 4;    // k slot: k = 32 lj + s
+  const int lj = lane >> 4;    // k slot
+  // MFMA 4q + e, k slot lj, stands for k = kblk(q) + e: the slots of lanes
+  // 16-31 and 48-63 take their 4-k blocks in another order than those of
+  // lanes 0-15 and 32-47 (any order serves, as long as A and C agree)
+  auto kblk = [&](const int q) { return 32 * lj + 4 * (q ^ (lj & 1)); };
   const bool bpart = MODE == kScanFold && cb >= kComposeColumnBlocks;   // a column block of B_r
   const int col = kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + lc;
   const int row0 = 16 * wave;
@@ -174,9 +185,9 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
     for (int q = q0; q < q1; ++q) {
       if (REV) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) aop[q][e] = region[(32 * lj + 4 * q + e) * 16 + 16 * lj + lc];
+        for (int e = 0; e < 4; ++e) aop[q][e] = region[(kblk(q) + e) * 16 + 16 * lj + lc];
       } else {
-        aop[q] = ld4(&region[lc * kAtStride + 32 * lj + 4 * q]);
+        aop[q] = ld4(&region[lc * kAtStride + kblk(q)]);
       }
     }
   };
@@ -276,7 +287,7 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
       __syncthreads();
       f32x4 bop[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) bop[q] = ld4(&sm.ct[buf][lc * kCtStride + 32 * lj + 4 * q]);
+      for (int q = 0; q < 8; ++q) bop[q] = ld4(&sm.ct[buf][lc * kCtStride + kblk(q)]);
       // four independent accumulator chains (k slot e of every MFMA group),
       // summed at the end: the MFMAs issue back to back instead of each
       // waiting for the previous one's result.  Step r+1's A goes through the
