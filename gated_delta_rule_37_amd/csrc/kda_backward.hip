@@ -581,7 +581,7 @@ __device__ __forceinline__ void backward_summary(const BwdParams& p) {
 }
 }  // namespace
 
-__global__ void __launch_bounds__(kBwdThreads, 8) kda_backward_summary_kernel(BwdParams p) {
+__global__ void __launch_bounds__(kBwdThreads, 4) kda_backward_summary_kernel(BwdParams p) {
   backward_summary<BD * BD / kBwdThreads>(p);
 }
 
