@@ -41,68 +41,68 @@ __device__ __forceinline__ f32x4 zero4() {
 
 // Ordered scan C_0 = 0, C_{r+1} = A_r C_r + B_r on FP32 matrix cores, for one
 // head and one block of 16 state columns (the columns of C never mix, so each
-// block scans on its own).  Wave w computes rows [16w, 16w + 16) as one
-// 16 x 16 tile (v_mfma_f32_16x16x4_f32; lane l, register i holds row
-// 16w + 4(l/16) + i, column l%16).  The k slots are permuted so that each
-// operand is contiguous: MFMA s = 4q + e, k slot j = l/16 stands for
-// k = 32j + 4(q xor (j & 1)) + e, so a lane's A operand over the whole
-// product is A_r[16w + l%16][32j .. 32j + 31] and its B operand
-// C_r[32j .. 32j + 31][col], in 16-byte blocks.
+// block scans on its own).  Sixteen waves: wave w computes the partial
+// product of row tile t = w % 8 (rows [16t, 16t + 16)) over the k half
+// h = w / 8 (k in [64h, 64h + 64)), one 16 x 16 tile (v_mfma_f32_16x16x4_f32;
+// lane l, register i holds row 16t + 4(l/16) + i, column l%16), 16 MFMAs a
+// step.  Two waves per row tile give each SIMD four waves, whose LDS
+// traffic, barrier waits and chain tails overlap each other's products.
+// The k slots are permuted: MFMA 4q + e, k slot j = l/16 stands for
+// k = 64h + 16j + 4(q xor (j & 1)) + e, so each lane's operands are 16-byte
+// blocks.
 //
-// Moving A_r (64 KB per step and workgroup) costs more than the products.
-// Each wave loads only the part of A_r its own tile multiplies (its 16 rows,
-// two whole rows per wave instruction), kComposeRing steps ahead into a
-// ring of register buffers (the step loop is unrolled over the ring, so no
-// buffer is copied), and turns it into the operand layout through an LDS
-// region of its own with padded rows.  No other wave touches that region,
-// so the wave stores step r+1's A and reads its operand back in the middle
-// of step r's products, off the scan's chain: the chain per step is the
-// carry's transposed store, one barrier, the carry's operand reads and the
-// products.  The carry tile alternates by step parity.  The column blocks of
-// a head are numbered onto one XCD (workgroups are dealt to the eight XCDs
-// in turn), where they share its L2 copy of A_r.
+// A step's carry is held as the two waves' partial sums: each wave stores
+// its partial, transposed, into its half's copy of the carry tile; after the
+// step's one barrier the waves read the sum of both copies as their B
+// operand, and both waves of a row tile store the full carry (the same
+// values) to global memory.  A transition that is structurally zero is
+// dropped by a select (the k-half-0 wave keeps B_r, the other zero).
 //
-// Global accesses go through buffer resources built in scalar registers
-// from each step's matrices, with lane offsets fixed for the whole scan: no
-// per-lane address is computed into a register that a load in flight still
-// owns (the compiler would make such a write wait for that load).
-// Row strides of the LDS tiles.  A stride of 34 16-byte units (34 = 2 mod
-// 16) with the k-block order of kblk below makes every 16-byte access of the
-// scan conflict-free: the A stores, the operand reads and the transposed
-// carry stores.  (A 16-byte LDS access is served in four 16-lane passes:
-// lanes {0-3, 12-15, 20-27}, {4-11, 16-19, 28-31} and the same + 32; the
-// 16 lanes of a pass must touch 16 different 4-bank units.)
-constexpr int kAtStride = KD + 8;   // floats per row of a wave's A_r region
-constexpr int kCtStride = KD + 8;   // floats per column of the transposed carry tile
-constexpr int kComposeRing = 3;     // operand ring: A_r is loaded kComposeRing - 1 steps before its store to LDS
+// Each wave loads only the block of A_r its products use (its 16 rows by
+// its 64 k; the reverse scan's wave the block of A_r^T, i.e. 64 rows by 16
+// columns of A_r), kComposeRing steps ahead into a ring of register
+// buffers (the step loop is unrolled over the ring, so no buffer is
+// copied), and turns it into the operand layout through an LDS region no
+// other wave touches: it stores step r+1's block and reads it back in the
+// middle of step r's products, off the scan's chain.  The forward region
+// has 64-float rows whose 16-byte slots are XOR-swizzled by the row, which
+// with the k order above makes its stores and operand reads conflict-free
+// (a 16-byte LDS access is served in four 16-lane passes: lanes
+// {0-3, 12-15, 20-27}, {4-11, 16-19, 28-31} and the same + 32; the 16 lanes
+// of a pass must touch 16 different 4-bank units).  Global accesses go
+// through buffer resources built in scalar registers with fixed lane
+// offsets, and every step issues the same accesses whatever its flags, so
+// the compiler's wait counts are exact.  The column blocks of a head are
+// numbered onto one XCD (workgroups are dealt to the eight XCDs in turn),
+// where they share its L2 copy of A_r.
+constexpr int kCtStride = KD + 8;   // floats per column of a carry-tile copy (34 16-byte units)
+constexpr int kComposeRing = 2;     // operand ring: a block is loaded kComposeRing - 1 steps before its store to LDS
 constexpr int kComposeWaves = kComposeThreads / 64;
-constexpr int kAPieces = KD * KD / 4 / kComposeThreads;   // 16-byte pieces of A_r per lane
-constexpr int kARegion = 16 * kAtStride;                 // floats per wave's A_r region
-constexpr int kBtStride = kComposeColumns + 4;           // floats per row of a wave's B_r rows
-static_assert(kComposeWaves * 16 == KD, "compose: one 16-row tile per wave");
-static_assert(kAPieces == 8, "compose: a wave's 16 rows (or columns) of A_r are 8 pieces per lane");
-static_assert(KD * 16 + 4 * 16 <= kARegion, "compose: the reverse layout fits a wave's region");
+constexpr int kKHalf = KD / 2;                                 // k per wave
+constexpr int kAPieces = 16 * kKHalf / 4 / 64;                 // 16-byte pieces of a wave's A block per lane
+constexpr int kARegion = 16 * kKHalf + 4 * 16;                 // floats per wave's region (reverse: skewed)
+constexpr int kBtStride = kComposeColumns + 4;                 // floats per row of a wave's B_r rows
+static_assert(kComposeWaves == 16 && kAPieces == 4, "compose: 8 row tiles x 2 k halves, 4 pieces per lane");
 
 struct alignas(16) ComposeSmem {
-  float at[kComposeWaves][kARegion];            // each wave's part of A_r
-  float ct[2][kComposeColumns * kCtStride];     // C_r[:, block] transposed, by step parity
-  float bt[kComposeWaves][16 * kBtStride];       // each wave's 16 rows of B_r[:, block]
+  float at[kComposeWaves][kARegion];                     // each wave's block of A_r
+  float ct[2][2][kComposeColumns * kCtStride];           // partial carries, by step parity and k half
+  float bt[kComposeWaves / 2][16 * kBtStride];           // each row tile's 16 rows of B_r[:, block]
 };
 
 // The same scan serves four uses (MODE):
 //  kScanCompose  the forward's C_0 = 0, C_{r+1} = A_r C_r + B_r over the
 //                segments (or, for the backward, over the pieces);
 //  kScanReverse  the backward's D_{S-1} = 0, D_{r-1} = A_r^T D_r + E_r: step s
-//                stands for segment S-1-s, and a wave's operand is the block
-//                of 16 columns of A_r (its rows of A_r^T);
+//                stands for segment S-1-s;
 //  kScanFold     per segment, its pieces' summaries folded into the
 //                segment's own: X <- A'_i X (+ B'_i) from X = [I | 0] over
 //                the pieces in order, one chain per (segment, head) and 16
-//                column blocks (8 of A_r, 8 of B_r); only the end is written;
+//                column blocks (8 of A_r, 8 of B_r); only the end is kept;
 //  kScanPieces   per segment, every piece's carry-in: X = C_r (zero for a
 //                segment that does not continue a sequence), written at each
 //                piece, then X <- A'_i X + B'_i.
-// A transition that is structurally zero (its flag clear) is skipped.
+// A transition that is structurally zero (its flag clear) is dropped.
 enum ScanMode { kScanCompose = 0, kScanReverse = 1, kScanFold = 2, kScanPieces = 3 };
 
 template <int MODE>
@@ -121,15 +121,16 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int tile = wave & 7;   // row tile
+  const int kh = wave >> 3;    // k half
   const int lc = lane & 15;    // column within the block (and row within the tile for A)
   const int lj = lane >> 4;    // k slot
-  // MFMA 4q + e, k slot lj, stands for k = kblk(q) + e: the slots of lanes
-  // 16-31 and 48-63 take their 4-k blocks in another order than those of
-  // lanes 0-15 and 32-47 (any order serves, as long as A and C agree)
-  auto kblk = [&](const int q) { return 32 * lj + 4 * (q ^ (lj & 1)); };
+  // MFMA 4q + e, k slot lj, stands for k = 64 kh + kblk(q) + e
+  auto kblk = [&](const int q) { return 16 * lj + 4 * (q ^ (lj & 1)); };
   const bool bpart = MODE == kScanFold && cb >= kComposeColumnBlocks;   // a column block of B_r
-  const int col = kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + lc;
-  const int row0 = 16 * wave;
+  const int col0 = kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb);
+  const int col = col0 + lc;
+  const int row0 = 16 * tile;
   float* const region = sm.at[wave];
 
   // the chain: steps over the segments, or over one segment's pieces
@@ -140,18 +141,16 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
     S = MODE == kScanFold ? len + 1 : len;   // a fold applies every piece, then writes
   }
   auto seg_of = [&](const int r) { return REV ? S - 1 - r : base + r; };
-  // this wave's part of A_r, coalesced.  Forward: piece u is row
-  // 16w + 2u + lane/32, floats 4(lane % 32) .. (two whole rows per wave
-  // instruction).  Reverse: piece u is row 16u + lane/4, floats
-  // 16w + 4(lane % 4) .. (sixteen 64-byte row pieces per instruction).
-  const int a_off = REV ? (lane >> 2) * KD + row0 + 4 * (lane & 3) : (row0 + (lane >> 5)) * KD + 4 * (lane & 31);
-  constexpr int a_step = REV ? 16 * KD : 2 * KD;
-  // B_r: the wave's 16 rows of the column block, one 16-byte piece per lane
-  // (row 16w + lane/4, columns 4(lane % 4) ..), staged through the wave's
-  // own rows of bt like A_r (a fold's column block of A_r loads it too and
-  // adds zero instead)
-  const int b_off = (row0 + (lane >> 2)) * VD + kComposeColumns * (bpart ? cb - kComposeColumnBlocks : cb) + 4 * (lane & 3);
-  auto load_a = [&](const int r, f32x4 (&a)[kAPieces + 1]) {
+  // Piece u < 4 of a step's slot, as a byte offset in A_r: forward, row
+  // 16t + 4u + lane/16, floats 64kh + 4(lane % 16) .. (four 256-byte row
+  // pieces per wave instruction); reverse, row 64kh + 16u + lane/4, floats
+  // 16t + 4(lane % 4) .. (sixteen 64-byte row pieces).  Piece 4: B_r[16t +
+  // lane/4][col0 + 4(lane % 4) ..], the row tile's rows of the column block.
+  const int a_off = 4 * (REV ? (kKHalf * kh + (lane >> 2)) * KD + row0 + 4 * (lane & 3)
+                             : (row0 + (lane >> 4)) * KD + kKHalf * kh + 4 * (lane & 15));
+  constexpr int a_step = 4 * (REV ? 16 * KD : 4 * KD);
+  const int b_off = 4 * ((row0 + (lane >> 2)) * VD + col0 + 4 * (lane & 3));
+  auto load_step = [&](const int r, f32x4 (&a)[kAPieces + 1]) {
     const size_t m = static_cast<size_t>(seg_of(r)) * H + h;
     const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.transitions + m * KD * KD), 0,
                                                       KD * KD * 4, kBufDword3);
@@ -159,42 +158,53 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
                                                       KD * VD * 4, kBufDword3);
 #pragma unroll
     for (int u = 0; u < kAPieces; ++u)
-      a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * (a_off + u * a_step), 0, 0));
-    a[kAPieces] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, 4 * b_off, 0, 0));
+      a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + u * a_step, 0, 0));
+    a[kAPieces] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off, 0, 0));
   };
-  // into the wave's region.  Forward: row-major 16 x kAtStride.  Reverse:
-  // k-major, 16 floats per k, with a 16-float skew per 32 k so that the
-  // lanes' scalar reads of one k slot fall into distinct banks.
-  const int st_off = REV ? (lane >> 2) * 16 + 4 * (lane & 3) : (lane >> 5) * kAtStride + 4 * (lane & 31);
-  auto store_a = [&](const f32x4 (&a)[kAPieces + 1]) {
+  // The wave's block into its region, and its operand back.  Forward: row
+  // i of the tile at 64 i, its 16-byte slot s holding k-block s xor
+  // (2i % 16).  Reverse: k-major, 16 floats per k, with a 16-float skew per
+  // 16 k (the lanes' scalar reads of one k slot then fall into distinct
+  // banks).
+  auto store_at = [&](const f32x4 (&a)[kAPieces + 1]) {
 #pragma unroll
     for (int u = 0; u < kAPieces; ++u) {
-      const int o = REV ? u * 256 + (u >> 1) * 16 : u * 2 * kAtStride;
-      st4(&region[st_off + o], a[u]);
+      if (REV) {
+        const int kl = 16 * u + (lane >> 2);
+        st4(&region[kl * 16 + 16 * u + 4 * (lane & 3)], a[u]);
+      } else {
+        const int i = 4 * u + (lane >> 4);
+        st4(&region[64 * i + 4 * ((lane & 15) ^ ((2 * i) & 15))], a[u]);
+      }
     }
-    st4(&sm.bt[wave][(lane >> 2) * kBtStride + 4 * (lane & 3)], a[kAPieces]);
   };
-  auto read_b = [&]() {
-    f32x4 bv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = sm.bt[wave][(4 * lj + i) * kBtStride + lc];
-    return bv;
-  };
-  auto read_a = [&](f32x4 (&aop)[8], const int q0, const int q1) {
+  auto read_at = [&](f32x4 (&aop)[kAPieces], const int q0, const int q1) {
 #pragma unroll
     for (int q = q0; q < q1; ++q) {
       if (REV) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) aop[q][e] = region[(kblk(q) + e) * 16 + 16 * lj + lc];
+        for (int e = 0; e < 4; ++e) {
+          const int kl = kblk(q) + e;
+          aop[q][e] = region[kl * 16 + 16 * (kl >> 4) + lc];
+        }
       } else {
-        aop[q] = ld4(&region[lc * kAtStride + kblk(q)]);
+        aop[q] = ld4(&region[64 * lc + 4 * ((kblk(q) >> 2) ^ ((2 * lc) & 15))]);
       }
     }
+  };
+  // B_r through the row tile's rows of bt into the accumulator layout (both
+  // waves of the tile store the same values)
+  auto store_b = [&](const f32x4& b) { st4(&sm.bt[tile][(lane >> 2) * kBtStride + 4 * (lane & 3)], b); };
+  auto read_b = [&]() {
+    f32x4 bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = sm.bt[tile][(4 * lj + i) * kBtStride + lc];
+    return bv;
   };
   // this lane's four entries of a carry, as byte offsets in its matrix
   const int c_off = 4 * ((row0 + 4 * lj) * VD + col);
   // where step r's value goes: the carry of that segment or piece, or for a
-  // fold (last step only) the segment's transition or update
+  // fold the segment's transition or update
   auto dest = [&](const int r) -> float* {
     if (MODE == kScanFold) return (bpart ? p.out_b : p.out_a) + (static_cast<size_t>(chain) * H + h) * KD * VD;
     return p.carry + (static_cast<size_t>(seg_of(r)) * H + h) * KD * VD;
@@ -217,104 +227,103 @@ __device__ __forceinline__ void compose_scan(const ComposeParams& p, ComposeSmem
     return ((lmask >> (r - lbase)) & 1ull) != 0;
   };
 
-  // ring slot t % kComposeRing holds step t's A_r and B_r pieces from the
-  // load until their store to LDS during step t-1 (every loaded register
-  // has that one consumer), and its flag until its use.  aop and bcur hold
-  // the operands of the step whose products run next: each half of aop is
-  // read back for step t+1 as soon as step t's products have consumed it.
-  //
-  // Every step issues the same global accesses whatever its flags (four
-  // carry stores, then B and A of step t + kComposeRing, clamped to the
-  // last step), so the compiler's wait counts are exact and each wait lets
-  // the later steps' loads stay in flight; with loads under conditions it
-  // has to wait for all but the newest few.
-  f32x4 a_ring[kComposeRing][kAPieces + 1];
-  f32x4 aop[8];
-  f32x4 bcur;
-  bool lv[kComposeRing];
-  f32x4 cur = zero4();
-  if (MODE == kScanFold && !bpart) {
+  // this wave's partial of the running value (the k-half-1 wave starts at 0)
+  f32x4 part = zero4();
+  if (kh == 0) {
+    if (MODE == kScanFold && !bpart) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = row0 + 4 * lj + i == col ? 1.f : 0.f;   // the identity
-  } else if (MODE == kScanPieces && p.plan[p.L.useg_carry_in + chain] != 0) {
-    const float* csrc = p.init + (static_cast<size_t>(chain) * H + h) * KD * VD;
+      for (int i = 0; i < 4; ++i) part[i] = row0 + 4 * lj + i == col ? 1.f : 0.f;   // the identity
+    } else if (MODE == kScanPieces && p.plan[p.L.useg_carry_in + chain] != 0) {
+      const float* csrc = p.init + (static_cast<size_t>(chain) * H + h) * KD * VD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = csrc[(row0 + 4 * lj + i) * VD + col];
+      for (int i = 0; i < 4; ++i) part[i] = csrc[(row0 + 4 * lj + i) * VD + col];
+    }
   }
   if (S < 2) {   // no step applies a transition: the start is the one value
-    if (S == 1) {
+    if (S == 1 && kh == 0) {
       float* cdst = dest(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = cur[i];
+      for (int i = 0; i < 4; ++i) cdst[(row0 + 4 * lj + i) * VD + col] = part[i];
     }
     return;
   }
+
+  // ring slot t % kComposeRing holds step t's pieces from the load until
+  // their store to LDS during step t-1, and lv its flag until its use; aop
+  // and bcur hold the operands of the step whose products run next
+  f32x4 ring[kComposeRing][kAPieces + 1];
+  f32x4 aop[kAPieces];
+  f32x4 bcur;
+  bool lv[kComposeRing];
 #pragma unroll
   for (int d = 0; d < kComposeRing; ++d) {
     lv[d] = live_at(d);
-    load_a(d < S - 1 ? d : S - 2, a_ring[d]);
+    load_step(d < S - 1 ? d : S - 2, ring[d]);
   }
-  store_a(a_ring[0]);
-  read_a(aop, 0, 8);
+  store_at(ring[0]);
+  store_b(ring[0][kAPieces]);
+  read_at(aop, 0, kAPieces);
   bcur = read_b();
+  const int ct_own = lc * kCtStride + row0 + 4 * lj;   // this lane's entries in a carry-tile copy
   for (int r0 = 0;; r0 += kComposeRing) {
 #pragma unroll
     for (int ph = 0; ph < kComposeRing; ++ph) {
       const int r = r0 + ph;            // r % kComposeRing == ph
-      {
-        // a fold writes its one destination at every step; the last write,
-        // step S-1's, stays
-        const auto rc = __builtin_amdgcn_make_buffer_rsrc(dest(r), 0, KD * VD * 4, kBufDword3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur[i]), rc, c_off + 4 * i * VD, 0, 0);
-      }
-      if (r == S - 1) return;
       const int buf = r & 1;
       const int p1 = (ph + 1) % kComposeRing;
       const bool live = lv[ph];
-      // step r + kComposeRing's operands into the slot whose A and B went to
-      // LDS during step r-1: issued first, they have the whole step to land
+      // step r + kComposeRing's pieces into the slot step r-1 has used up,
+      // issued first so that they have the whole step to land (the last
+      // steps load the last transition again, unused)
       {
         const int rn = r + kComposeRing;
-        const int rc = rn < S - 1 ? rn : S - 2;
         lv[ph] = live_at(rn);
-        load_a(rc, a_ring[ph]);
+        load_step(rn < S - 1 ? rn : S - 2, ring[ph]);
       }
-      // the carry, transposed into LDS: column lc, rows row0 + 4lj + 0..3
-      st4(&sm.ct[buf][lc * kCtStride + row0 + 4 * lj], cur);
-      // the carry reached LDS; the barrier also ends step r-1's reads of the
-      // other parity's tile, which step r+1 refills
+      // this wave's partial of C_r, transposed into its half's copy
+      st4(&sm.ct[buf][kh][ct_own], part);
+      // both partials reached LDS; the barrier also ends step r-1's reads of
+      // the other parity's copies, which step r+1 refills
       __syncthreads();
-      f32x4 bop[8];
+      {
+        // C_r in full, stored by both waves of the row tile
+        const f32x4 other = ld4(&sm.ct[buf][kh ^ 1][ct_own]);
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(dest(r), 0, KD * VD * 4, kBufDword3);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) bop[q] = ld4(&sm.ct[buf][lc * kCtStride + kblk(q)]);
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part[i] + other[i]), rc, c_off + 4 * i * VD, 0, 0);
+      }
+      if (r == S - 1) return;
+      f32x4 bop[kAPieces];
+#pragma unroll
+      for (int q = 0; q < kAPieces; ++q) {
+        const int o = lc * kCtStride + kKHalf * kh + kblk(q);
+        bop[q] = ld4(&sm.ct[buf][0][o]) + ld4(&sm.ct[buf][1][o]);
+      }
       // four independent accumulator chains (k slot e of every MFMA group),
-      // summed at the end: the MFMAs issue back to back instead of each
-      // waiting for the previous one's result.  Step r+1's A goes through the
-      // wave's region between the two halves of the products.
-      // (a fold's column block of A_r adds no B)
-      const f32x4 b0 = MODE == kScanFold && !bpart ? zero4() : bcur;
+      // summed at the end; step r+1's operands go through LDS between the
+      // two halves of the products
+      const f32x4 b0 = kh == 0 && !(MODE == kScanFold && !bpart) ? bcur : zero4();
       f32x4 acc[4] = {b0, zero4(), zero4(), zero4()};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < kAPieces / 2; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], acc[e], 0, 0, 0);
-      store_a(a_ring[p1]);
-      read_a(aop, 0, 4);
+      store_at(ring[p1]);
+      store_b(ring[p1][kAPieces]);
+      read_at(aop, 0, kAPieces / 2);
 #pragma unroll
-      for (int q = 4; q < 8; ++q)
+      for (int q = kAPieces / 2; q < kAPieces; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[q][e], bop[q][e], acc[e], 0, 0, 0);
-      read_a(aop, 4, 8);
+      read_at(aop, kAPieces / 2, kAPieces);
       bcur = read_b();
       // the products run whatever the flag (the loop has no branch for the
       // compiler to merge wait counts over); a transition that is
       // structurally zero is dropped here, whatever its buffer holds
       const f32x4 prod = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      f32x4 nxt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nxt[i] = live ? prod[i] : b0[i];
-      cur = nxt;
+      for (int i = 0; i < 4; ++i) part[i] = live ? prod[i] : b0[i];
     }
   }
 }

@@ -13,7 +13,7 @@ namespace kda {
 
 constexpr int kSummaryThreads = 1024;  // kda_chunk_kernel (summaries launch): 16 waves
 constexpr int kCarryThreads = 768;    // kda_carry_kernel (carry launch): 12 waves
-constexpr int kComposeThreads = 512;  // kda_compose_kernel workgroup size: 8 waves
+constexpr int kComposeThreads = 1024;  // kda_compose_kernel workgroup size: 16 waves
 constexpr int kComposeColumns = 16;      // state columns per compose workgroup
 constexpr int kComposeColumnBlocks = 128 / kComposeColumns;
 
