@@ -66,6 +66,10 @@ constexpr float kGateFloor = -300.f;
 // Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access;
 // accesses at or past num_records read zero and drop writes.
 constexpr int kBufDword3 = 0x00020000;
+// Cache policy of the o stores: non-temporal (nt).  o is written once per
+// launch and read by nothing in it; streaming it past the caches leaves
+// them to the inputs and the chunk cache (the carry launch ~1% faster).
+constexpr int kStreamAux = 2;
 
 enum Mode { kModeFwd = 0, kModeSumS = 1, kModeSumPhi = 2 };
 
@@ -795,7 +799,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
           for (int e = 0; e < 4; ++e) {
             const bf16 ob = static_cast<bf16>(O[4 * r + e]);
             __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, ob), rso, o_voff,
-                                                  (8 * r + e) * ob_row, 0);
+                                                  (8 * r + e) * ob_row, kStreamAux);
           }
         }
       } else {
@@ -807,7 +811,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float ov = O[4 * r + e];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ov), rso, o_voff, (8 * r + e) * o_row, kStreamAux);
           }
         }
       }
