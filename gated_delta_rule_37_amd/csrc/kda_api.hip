@@ -414,7 +414,6 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.dbeta = dbeta;
   p.dh0 = d_initial_state;
   p.ckpt = reinterpret_cast<float*>(ws + W.ckpt);
-  p.scratch = reinterpret_cast<float*>(ws + W.scratch);
   p.upbuf = reinterpret_cast<float*>(ws + W.up);
   // E_r, then D_r = the reverse scan of (A^T, E), then every fragment
   (void)hipGetLastError();

@@ -29,10 +29,14 @@
 // of eight partials; sums over columns (dq, dk, dg) are reduced within each
 // wave by a transposing butterfly (lane-swap and DPP moves) and across the
 // two waves of a row group through LDS.  The fragment kernel keeps the state
-// every 32 tokens and every token's u and p in global memory (level 1),
-// recomputes a chunk's states every 4 tokens into its workgroup's scratch by
-// update-only steps (level 2; u known, no exchange), and each 4-token group's
-// per-token states in registers the same way before walking it backwards.
+// every 16 tokens and every token's u and p in global memory (level 1); in
+// the reverse it recomputes each 4-token group's first state from its
+// chunk's checkpoint by update-only steps (u known, no exchange; the chunk's
+// k, e^g and u held in LDS), and the group's per-token states in registers
+// the same way before walking it backwards.  Recomputing costs three
+// update-only steps per token; storing states every 4 tokens instead would
+// write 64 KiB per group and workgroup, which the memory system cannot take
+// at the rate 256 workgroups would produce it.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,8 +52,8 @@ constexpr int NT = kBwdThreads;       // 1024
 constexpr int NGRP = NT / BD;         // row groups: 8
 constexpr int NR = BD / NGRP;         // rows per thread: 16
 constexpr int GT = 4;                 // tokens per register group
-constexpr int CK = kBwdCheckpointTokens;   // tokens per level-1 checkpoint: 32
-constexpr int GPC = CK / GT;          // groups per checkpoint chunk: 8
+constexpr int CK = kBwdCheckpointTokens;   // tokens per checkpoint chunk: 16
+constexpr int GPC = CK / GT;          // groups per checkpoint chunk: 4
 constexpr size_t MAT = static_cast<size_t>(BD) * BD;
 constexpr float kLog2eB = 1.4426950408889634f;
 static_assert(NR == 16 && NT == 1024, "backward layout: 16 rows per thread, 16 waves");
@@ -69,7 +73,7 @@ struct alignas(16) BwdSmem {
   TokGroup tg[2];                 // by group parity
   float colpart[2][NGRP][BD];     // row-sum partials, by exchange parity
   float rowpart[2][3][2][BD];     // column sums of the two waves of a row group, by token parity
-  float red[2][4];                // dbeta's and u.do's sums of waves 0 and 1, by token parity
+  float red[2][4];                // dbeta's and u.do's sums of waves 2 and 3, by token parity
 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -161,6 +165,14 @@ __device__ __forceinline__ void store_group(TokGroup& tg, const int n, const int
 // waves; the registers are not).
 __device__ __forceinline__ void slice_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum.  Called right
+// after a state is loaded into registers that a loop then updates: the wait
+// counter is in order and shared by loads and stores, and a loop whose
+// registers may still hold a pending load from before it waits for every
+// memory access of the wave (the loop's own prefetches and stores included)
+// at their first use in each iteration.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(const float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -208,10 +220,18 @@ __device__ __forceinline__ float wave_rows_reduce(Val&& val, const int lane) {
   return y;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+// Sums of two values over the wave's 64 lanes, by lane-swap and DPP moves
+// only: lanes 0-31 return the sum of a, lanes 32-63 that of b.
+__device__ __forceinline__ float wave_sum2(const float a, const float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  y = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // rows 0-1 and 2-3 summed
+  y += dpp<0xB1>(y);                                   // quad_perm [1,0,3,2]
+  y += dpp<0x4E>(y);                                   // quad_perm [2,3,0,1]
+  y += dpp<0x141>(y);                                  // row_half_mirror
+  y += dpp<0x140>(y);                                  // row_mirror
+  return y;
 }
 
 // The thread's 16 elements of a [128][128] FP32 state at a uniform base:
@@ -284,21 +304,26 @@ struct Ctx {
   }
 };
 
-// One forward step of token m of the group: p and u of column c from
-// S = S_{t-1}; with upd (uniform), S <- S_t.  Row vectors are read from LDS
-// four at a time (broadcast reads), not held.
-__device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, const int m, const float u,
+// S <- Diag(e^g) S + k u^T for this thread's elements, from a token's k and
+// e^g rows in LDS, read four at a time (broadcast reads), not held.
+__device__ __forceinline__ void update_rows(const Ctx& x, const float* krow, const float* drow, const float u,
                                             float (&s)[NR]) {
   const int r0 = NR * x.grp;
 #pragma unroll
   for (int j = 0; j < NR / 4; ++j) {
-    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
-    const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
+    const f4 kk = l4(&krow[r0 + 4 * j]);
+    const f4 dc = l4(&drow[r0 + 4 * j]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[4 * j + e] = fmaf(dc[e], s[4 * j + e], kk[e] * u);
   }
 }
+__device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, const int m, const float u,
+                                            float (&s)[NR]) {
+  update_rows(x, tg.k[m], tg.dec[m], u, s);
+}
 
+// One forward step of token m of the group: p and u of column c from
+// S = S_{t-1}; with upd (uniform), S <- S_t.
 __device__ __forceinline__ void fwd_step(Ctx& x, const TokGroup& tg, const int m, float (&s)[NR], float& u,
                                          float& pp, const bool upd) {
   const int r0 = NR * x.grp;
@@ -365,14 +390,12 @@ __device__ __forceinline__ void rev_rest(Ctx& x, const BwdParams& p, const int h
   const float doc = tg.dov[m][x.c];
   const float beta = tg.beta[m];
   const float dp = -beta * du;
-  if (x.wave < 2) {   // row group 0 (tid < 128, a wave-uniform test): dv, dbeta's and u.do's terms
+  // row group 1 (waves 2 and 3, on the other two SIMDs than row group 0's,
+  // which runs rev_tail): dv, dbeta's and u.do's terms
+  if (x.grp == 1) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.c, 0, 0);
-    const float sb = wave_sum(du * (tg.v[m][x.c] - pp));
-    const float su = wave_sum(u * doc);
-    if (x.lane == 0) {
-      x.sm.red[b][x.wave] = sb;
-      x.sm.red[b][2 + x.wave] = su;
-    }
+    const float s2 = wave_sum2(du * (tg.v[m][x.c] - pp), u * doc);
+    if ((x.lane & 31) == 0) x.sm.red[b][2 * (x.lane >> 5) + (x.wave & 1)] = s2;
   }
   // column sums of three row quantities (S = S_{t-1}, e = e^g of the row):
   //   dq_r = e_r sum_c S do + k_r (u . do)
@@ -591,23 +614,23 @@ __global__ void __launch_bounds__(kBwdSummaryThreads) kda_backward_summary_narro
 
 // Every (fragment, head) item: the forward from the fragment's start state
 // (carry-in C_r for a carried fragment, else the initial state or zero) with
-// level-1 checkpoints, then per 32-token chunk from the last: the level-2
-// recompute, and per 4-token group from the last: the register recompute
-// and the reverse steps.  The cotangent starts from D_r (when the fragment
-// ends its segment) plus dfinal (when it ends its sequence); a fragment
-// that starts its sequence writes what reaches that start to dh0.
-// Persistent: workgroup b takes items b, b + grid, ... in the plan's
-// longest-first order, with its own level-2 scratch.
+// checkpoints every 16 tokens, then per 4-token group from the last: the
+// recompute of its states and the reverse steps.  The cotangent starts from
+// D_r (when the fragment ends its segment) plus dfinal (when it ends its
+// sequence); a fragment that starts its sequence writes what reaches that
+// start to dh0.  Persistent: workgroup b takes items b, b + grid, ... in
+// the plan's longest-first order.
 __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
-  // u and p of a 32-token chunk's tokens, by chunk parity and group
-  __shared__ float up[2][GPC][GT][2][BD];
+  // one 16-token chunk's u and p (by token), k and e^g rows
+  __shared__ float upc[CK][2][BD];
+  __shared__ float ckk[CK][BD];
+  __shared__ float ckd[CK][BD];
   const int H = p.H;
   const int F = p.plan[3];
   const int items = F * p.hn;
   const int tid = threadIdx.x;
   Ctx x(sm, tid);
-  float* lvl2 = p.scratch + static_cast<size_t>(blockIdx.x) * GPC * MAT;
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int f = p.plan[p.L.frag_order + item / p.hn];
@@ -619,52 +642,64 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
     const int32_t end = p.plan[p.L.frag_end + f];
     const int len = end - beg;
     const int ng = (len + GT - 1) / GT;           // 4-token groups
-    const int nch = (len + CK - 1) / CK;          // 32-token chunks
+    const int nch = (len + CK - 1) / CK;          // 16-token chunks
     const int top = ng - GPC * (nch - 1);         // groups of the last chunk
     float* ck = p.ckpt + (static_cast<size_t>(beg / CK + f) * H + h) * MAT;   // chunk j at + j H MAT
     auto gtokens = [&](const int g) { return min(GT, len - GT * g); };
 
-    // One token group: wait for its vectors, prefetch group gn's (gn < 0:
-    // none), run body(tg, n), then store the prefetch into the other buffer.
     // u and p of every token, written by level 1 (a thread per column of
-    // waves 0 and 1), read back a group ahead into LDS
+    // waves 0 and 1): [u | p] per token and head
     const size_t up_token = static_cast<size_t>(H) * 2 * BD;   // floats between tokens
     auto up_base = [&](const int t) { return p.upbuf + (static_cast<size_t>(t) * H + h) * 2 * BD; };
     // One token group: wait for its vectors, prefetch group gn's (gn < 0:
-    // none; with gn_up also its tokens' u and p, one float per thread), run
-    // body(tg, n), then store the prefetch for the next group.
-    auto group = [&](const int g, const int gn, const bool gn_up, auto&& body) {
+    // none), run body(tg, n), then store the prefetch for the next group.
+    auto group = [&](const int g, const int gn, auto&& body) {
       Fetch fx;
-      float fu = 0.f;
-      const int um = tid >> 8, uk = (tid >> 7) & 1;   // the float this thread fetches: token um, u or p
       __syncthreads();
       const TokGroup& tg = sm.tg[x.gb];
-      if (gn >= 0) {
-        fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
-        if (gn_up) {
-          const uint32_t bytes = (gtokens(gn) - 1) * up_token * 4 + 2 * BD * 4;
-          fu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rsrc(up_base(beg + GT * gn), bytes), static_cast<int>(um * up_token * 4) + 4 * (uk * BD + x.c), 0, 0));
-        }
-      }
+      if (gn >= 0) fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
       body(tg, gtokens(g));
-      if (gn >= 0) {
-        store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
-        if (gn_up) up[(gn / GPC) & 1][gn % GPC][um][uk][x.c] = fu;
-      }
+      if (gn >= 0) store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
       x.gb ^= 1;
     };
+    // Chunk j's k and e^g rows (threads 0-511 k, 512-1023 g: token
+    // (tid / 32) % 16, four values each) and, with with_up, its tokens' u and
+    // p (64 threads per token, 16 bytes each) into LDS.  Called after every
+    // read of the previous chunk's rows: the next group's barrier publishes
+    // them.
+    auto load_chunk = [&](const int j, const bool with_up) {
+      const int t0 = beg + CK * j;
+      const int n = min(CK, len - CK * j);
+      const int m = (tid >> 5) & (CK - 1);
+      const bool isg = tid >= NT / 2;
+      const uint32_t row = static_cast<uint32_t>(H) * BD * 2;
+      const size_t tok0 = static_cast<size_t>(t0) * H + h;
+      const u2 kg = __builtin_amdgcn_raw_buffer_load_b64(rsrc((isg ? p.g : p.k) + tok0 * BD, (n - 1) * row + BD * 2),
+                                                         m * row + 8 * (tid & 31), 0, 0);
+      u4 uv = {0u, 0u, 0u, 0u};
+      const int mu = tid >> 6;
+      if (with_up)
+        uv = __builtin_amdgcn_raw_buffer_load_b128(rsrc(up_base(t0), (n - 1) * up_token * 4 + 2 * BD * 4),
+                                                   static_cast<int>(mu * up_token * 4) + 16 * (tid & 63), 0, 0);
+      const uint32_t w[4] = {kg[0] & 0xffffu, kg[0] >> 16, kg[1] & 0xffffu, kg[1] >> 16};
+      f4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = isg ? __builtin_amdgcn_exp2f(bfv(w[e]) * kLog2eB) : bfv(w[e]);
+      *reinterpret_cast<f4*>(isg ? &ckd[m][4 * (tid & 31)] : &ckk[m][4 * (tid & 31)]) = r;
+      if (with_up) *reinterpret_cast<f4*>(&upc[mu][0][0] + 4 * (tid & 63)) = __builtin_bit_cast(f4, uv);
+    };
 
-    // run: the running state of the level-1 and level-2 passes, and each
-    // reversed group's first state
+    // run: the running state of level 1, then each reversed group's first
+    // state
     float run[NR];
     {
       const float* s0 = nullptr;
       if (flags & kFragCarried) s0 = p.carry + (static_cast<size_t>(seg) * H + h) * MAT;
       else if (p.h0s != nullptr) s0 = p.h0s + (static_cast<size_t>(seq) * H + h) * MAT;
       load_state(s0, x.voff, run);
+      wait_vmem();
     }
-    __syncthreads();   // the previous item's reads of both token buffers are done
+    __syncthreads();   // the previous item's reads of both token buffers and the chunk rows are done
     {
       Fetch f0;
       fetch_group(p, h, beg, gtokens(0), tid, x.wave, f0);
@@ -673,11 +708,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
 
     // level 1: the state at every chunk start and every token's u and p,
     // forward through the fragment.  The last chunk's u and p also go
-    // straight to LDS, where its level 2 reads them next (its first group may
-    // be level 1's last, whose values a prefetch could not yet see).
+    // straight to LDS, where the reverse reads them first (its last tokens'
+    // stores may not yet be visible to other threads' loads).
     const int glast = GPC * (nch - 1);   // the last chunk's first group
     for (int g = 0; g < ng; ++g) {
-      group(g, g + 1 < ng ? g + 1 : glast, false, [&](const TokGroup& tg, const int n) {
+      group(g, g + 1 < ng ? g + 1 : ng - 1, [&](const TokGroup& tg, const int n) {
         if (g % GPC == 0) put_ckpt(ck + static_cast<size_t>(g / GPC) * H * MAT, tid, run);
         const Rsrc ru = rsrc(up_base(beg + GT * g), (n - 1) * up_token * 4 + 2 * BD * 4);
 #pragma unroll
@@ -690,14 +725,15 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), ru, o, 0, 0);
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pp), ru, o + 4 * BD, 0, 0);
               if (g >= glast) {
-                up[(nch - 1) & 1][g - glast][m][0][x.c] = u;
-                up[(nch - 1) & 1][g - glast][m][1][x.c] = pp;
+                upc[GT * (g - glast) + m][0][x.c] = u;
+                upc[GT * (g - glast) + m][1][x.c] = pp;
               }
             }
           }
         }
       });
     }
+    load_chunk(nch - 1, false);
 
     // the cotangent at the fragment's end
     float ds[NR];
@@ -709,33 +745,23 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
     }
     if ((flags & kFragSeqEnd) && p.dfinal != nullptr)
       add_state(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+    wait_vmem();
 
+    // the groups backwards, chunk by chunk.  A group's first state is
+    // recomputed from its chunk's checkpoint by update-only steps with the
+    // u that level 1 kept (no exchange), and the state before its token m
+    // from that by m more; the chunk's rows stay in LDS for this.
     for (int j = nch - 1; j >= 0; --j) {
       const int g0 = GPC * j;
       const int g1 = g0 + (j == nch - 1 ? top : GPC);   // the chunk's groups [g0, g1)
-      // level 2: the chunk's state every 4 tokens into the scratch, by
-      // update-only steps with the u that level 1 kept (no exchange)
-      const auto& upj = up[j & 1];
-      get_ckpt(ck + static_cast<size_t>(j) * H * MAT, tid, run);
-      for (int g = g0; g < g1; ++g) {
-        group(g, g + 1 < g1 ? g + 1 : g1 - 1, g + 1 < g1, [&](const TokGroup& tg, const int n) {
-          put_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
-          if (g + 1 < g1) {   // the state after the chunk's last group is not needed
-#pragma unroll
-            for (int m = 0; m < GT; ++m)
-              if (m < n) update_only(x, tg, m, upj[g - g0][m][0][x.c], run);
-          }
-        });
-      }
-      // the groups backwards: the state before token m is rebuilt from the
-      // group's first state (run, from the scratch) by m update-only steps
-      // (u is known: no exchange, no barrier)
+      const float* ckj = ck + static_cast<size_t>(j) * H * MAT;
       for (int g = g1 - 1; g >= g0; --g) {
-        group(g, g > g0 ? g - 1 : (j > 0 ? g0 - GPC : -1), g == g0 && j > 0, [&](const TokGroup& tg, const int n) {
+        group(g, g - 1, [&](const TokGroup& tg, const int n) {
           float w[NR];
-          get_ckpt(lvl2 + static_cast<size_t>(g - g0) * MAT, tid, run);
+          get_ckpt(ckj, tid, run);
+          for (int q = 0; q < GT * (g - g0); ++q) update_rows(x, ckk[q], ckd[q], upc[q][0][x.c], run);
           const int t0 = beg + GT * g;
-          const float(&upg)[GT][2][BD] = upj[g - g0];
+          const float(&upg)[GT][2][BD] = *reinterpret_cast<const float(*)[GT][2][BD]>(&upc[GT * (g - g0)][0][0]);
 #pragma unroll
           for (int i = 0; i < NR; ++i) w[i] = run[i];
 #pragma unroll
@@ -759,6 +785,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
           rev_tail(x, p, h, tg, 0, t0, 0);
         });
       }
+      if (j > 0) load_chunk(j - 1, true);   // every read of chunk j's rows ended at the barrier above
     }
     if (!(flags & kFragCarried) && p.dh0 != nullptr)
       store_state(p.dh0 + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);

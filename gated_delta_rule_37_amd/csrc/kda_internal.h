@@ -18,13 +18,12 @@ constexpr int32_t kFragSeqEnd = 4;   // ends at its sequence's end (owns final_s
 constexpr int kChunkCacheBytes = 4096;
 
 // Backward geometry: 1024-thread workgroups, a persistent fragment launch of
-// at most kBwdGrid workgroups with kBwdScratchStates 64 KiB states of scratch
-// each, and level-1 state checkpoints every kBwdCheckpointTokens tokens.
+// at most kBwdGrid workgroups, and state checkpoints every
+// kBwdCheckpointTokens tokens.
 constexpr int kBwdThreads = 1024;          // the fragment launch
 constexpr int kBwdSummaryThreads = 256;    // the backward-summary launch
 constexpr int kBwdGrid = 256;
-constexpr int kBwdCheckpointTokens = 32;
-constexpr int kBwdScratchStates = kBwdCheckpointTokens / 4;
+constexpr int kBwdCheckpointTokens = 16;
 
 // Largest supported packed token count: a chunk-count times 64 times the head
 // count stays far inside 32-bit grid arithmetic.

@@ -91,8 +91,7 @@ struct BwdParams {
   float* dg;
   float* dbeta;
   float* dh0;             // dL/dh0 [N, H, K, V] or null (not wanted)
-  float* ckpt;            // level-1 checkpoints: slot floor(begin/32) + f + j per head
-  float* scratch;         // per-workgroup level-2 states
+  float* ckpt;            // state checkpoints: slot floor(begin/16) + f + j per head
   float* upbuf;           // u and p of every token [T, H, 2, V] (the fragment launch's level 1)
 };
 

@@ -103,9 +103,6 @@ BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
   o += seg_states;
   L.ckpt = o;
   o += (static_cast<size_t>(plan->T / kBwdCheckpointTokens) + static_cast<size_t>(plan->F)) * H * mat;
-  L.scratch = o;
-  const size_t items = static_cast<size_t>(plan->F) * H;
-  o += (items < static_cast<size_t>(kBwdGrid) ? items : kBwdGrid) * kBwdScratchStates * mat;
   L.up = o;
   o += static_cast<size_t>(plan->T) * H * 2 * 128 * sizeof(float);
   L.total = o;

@@ -23,12 +23,11 @@ size_t workspace_need(const kda_plan* plan, int32_t H);
 // Byte offsets of the parts of the backward's workspace for H heads (each
 // 256-byte aligned): the forward's workspace, the forward's transitions,
 // updates and carry-ins recomputed, the backward summaries E and their
-// reverse compose D (each P x H states, per piece), the level-1 checkpoints
-// ((floor(T/32) + F) x H states), the fragment launch's scratch
-// (min(F H, kBwdGrid) x kBwdScratchStates states) and every token's u and p
+// reverse compose D (each P x H states, per piece), the state checkpoints
+// ((floor(T/16) + F) x H states) and every token's u and p
 // (T x H x 2 x 128 floats).
 struct BwdLayout {
-  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, scratch, up, total;
+  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, up, total;
 };
 BwdLayout backward_layout(const kda_plan* plan, int32_t H);
 size_t backward_workspace_need(const kda_plan* plan, int32_t H);

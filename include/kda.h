@@ -390,9 +390,8 @@ int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_
 /* Bytes of kda_backward's workspace for H heads (each part 256-byte
  * aligned): kda_workspace_bytes(plan, H); five arrays of S * H states
  * (transitions, updates, carry-ins, backward summaries and their reverse
- * compose, per piece); (floor(T/32) + F) * H state checkpoints;
- * min(F * H, 256) * 8 states of per-workgroup scratch (a state is 64 KiB);
- * T * H * 1 KiB for every token's u and p.  0 for a NULL plan, H <= 0 or
+ * compose, per piece); (floor(T/16) + F) * H state checkpoints (a state is
+ * 64 KiB); T * H * 1 KiB for every token's u and p.  0 for a NULL plan, H <= 0 or
  * K, V other than 128. */
 size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 

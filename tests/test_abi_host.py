@@ -293,13 +293,12 @@ def test_backward_validates_before_launch():
                 ws=L.kda_backward_workspace_bytes(plan.handle, H, 128, 128))
     # the forward's chunk cache (256-byte aligned), five S x H state arrays
     # (transitions, updates, carry-ins, backward summaries and their compose),
-    # (floor(T/32) + F) x H checkpoints, min(F H, 256) x 8 scratch states,
-    # every token's u and p (1 KiB per token and head)
+    # (floor(T/16) + F) x H checkpoints, every token's u and p (1 KiB per
+    # token and head)
     S, F = 2, plan.F
     cache = ((T + 31) // 32 + S) * H * 4096
     cache = (cache + 255) // 256 * 256
-    assert need["ws"] == (cache + 5 * S * H * 65536 + (T // 32 + F) * H * 65536 + min(F * H, 256) * 8 * 65536
-                          + T * H * 1024)
+    assert need["ws"] == cache + 5 * S * H * 65536 + (T // 16 + F) * H * 65536 + T * H * 1024
     order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "dq", "dk", "dv", "dg", "dbeta",
              "dh0", "ws")
 

@@ -35,9 +35,12 @@ CASES = [
     ("varlen_7_segments_h0", 777, 3, [0, 5, 300, 301, 640, 777], 7, 0.2, True),
     ("segments_longer_than_sequences", 200, 1, [0, 10, 20, 30, 200], 3, 1.0, True),
     ("fast_gates_segments", 256, 2, [0, 256], 4, 4.0, True),
-    # fragments of 33 and 67 tokens: a last 32-token chunk of one token, whose
-    # level-2 group is level 1's last
+    # fragments of 33 and 67 tokens: a last 16-token checkpoint chunk of one
+    # and of three tokens (its u and p reach the reverse from level 1 through
+    # LDS)
     ("chunk_plus_one_fragments", 100, 2, [0, 33, 100], 1, 0.5, True),
+    # fragments of 17, 48 (three whole chunks), 16 and 4 tokens
+    ("checkpoint_chunk_edges", 85, 2, [0, 17, 65, 81, 85], 1, 0.5, True),
 ]
 
 
