@@ -437,6 +437,10 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   st = launch_scan(kda::kda_compose_reverse_kernel, c, 1, kda::kComposeColumnBlocks, stream);
   if (st != KDA_OK) return st;
   const int64_t grid = items < kda::kBwdGrid ? items : kda::kBwdGrid;
+  hipLaunchKernelGGL(kda::kda_backward_forward_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),
+                     0, stream, p);
+  st = finish_launch();
+  if (st != KDA_OK) return st;
   hipLaunchKernelGGL(kda::kda_backward_fragment_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),
                      0, stream, p);
   return finish_launch();

@@ -58,11 +58,14 @@ constexpr size_t MAT = static_cast<size_t>(BD) * BD;
 constexpr float kLog2eB = 1.4426950408889634f;
 static_assert(NR == 16 && NT == 1024, "backward layout: 16 rows per thread, 16 waves");
 
-// One group of up to four tokens' vectors.
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// One group of up to four tokens' vectors (the reverse launch).
 struct alignas(16) TokGroup {
   float k[GT][BD];
   float dec[GT][BD];   // e^g
-  float kd[GT][BD];    // k e^g
   float q[GT][BD];
   float v[GT][BD];
   float dov[GT][BD];
@@ -76,9 +79,30 @@ struct alignas(16) BwdSmem {
   float red[2][4];                // dbeta's and u.do's sums of waves 2 and 3, by token parity
 };
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+// The forward launch's LDS: two 16-token chunks' k, e^g, v and beta (by
+// chunk parity); the current 4-token group's derived rows, with
+// Gam_t = e^{g_0 + ... + g_t} (per channel, from the group's first token):
+// gk_t = k_t Gam_t, kh_t = k_t e^{g_{t+1} + ... + g_{n-1}}, gamn = Gam_{n-1}
+// and ap[(t-1)t/2 + j] = sum_r k_t k_j e^{g_{j+1} + ... + g_t} (j < t); and
+// the exchange of four row-sum partials per row group.
+struct alignas(16) FwdChunk {
+  float k[CK][BD];
+  float dec[CK][BD];
+  float v[CK][BD];
+  float beta[CK];
+};
+struct alignas(16) FwdGroup {
+  float gk[GT][BD];
+  float kh[GT][BD];
+  float gamn[BD];
+  float ap[8];
+};
+struct alignas(16) FwdSmem {
+  FwdChunk ch[2];
+  FwdGroup fg;
+  f4 colpart4[NGRP][BD];
+};
+
 __device__ __forceinline__ f4 l4(const float* src) { return *reinterpret_cast<const f4*>(src); }
 
 __device__ __forceinline__ float bfv(const uint32_t b) { return __uint_as_float(b << 16); }
@@ -141,7 +165,6 @@ __device__ __forceinline__ void store_group(TokGroup& tg, const int n, const int
       }
       *reinterpret_cast<f4*>(&tg.k[m][e]) = kk;
       *reinterpret_cast<f4*>(&tg.dec[m][e]) = dc;
-      *reinterpret_cast<f4*>(&tg.kd[m][e]) = kk * dc;
     } else {
       f4 qq, vv;
 #pragma unroll
@@ -278,15 +301,16 @@ __device__ __forceinline__ void get_ckpt(const float* src, const int tid, float 
   }
 }
 
-// Per-thread context shared by both kernels.
-struct Ctx {
-  BwdSmem& sm;
+// Per-thread context of a 1024-thread launch over its LDS.
+template <typename Smem>
+struct CtxT {
+  Smem& sm;
   int tid, c, grp, lane, wave;   // grp and wave are wave-uniform
   int voff;  // byte offset of the thread's first state element, 4 (NR BD grp + c)
   int par;   // colpart parity
   int gb;    // token-group buffer parity
 
-  __device__ Ctx(BwdSmem& s, const int t)
+  __device__ CtxT(Smem& s, const int t)
       : sm(s), tid(t), c(t & (BD - 1)), grp(__builtin_amdgcn_readfirstlane(t >> 7)), lane(t & 63),
         wave(__builtin_amdgcn_readfirstlane(t >> 6)), voff(4 * (NR * BD * (t >> 7) + (t & (BD - 1)))), par(0),
         gb(0) {}
@@ -303,6 +327,8 @@ struct Ctx {
     return s;
   }
 };
+using Ctx = CtxT<BwdSmem>;
+using FwdCtx = CtxT<FwdSmem>;
 
 // S <- Diag(e^g) S + k u^T for this thread's elements, from a token's k and
 // e^g rows in LDS, read four at a time (broadcast reads), not held.
@@ -322,21 +348,147 @@ __device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, co
   update_rows(x, tg.k[m], tg.dec[m], u, s);
 }
 
-// One forward step of token m of the group: p and u of column c from
-// S = S_{t-1}; with upd (uniform), S <- S_t.
-__device__ __forceinline__ void fwd_step(Ctx& x, const TokGroup& tg, const int m, float (&s)[NR], float& u,
-                                         float& pp, const bool upd) {
+// The derived rows of the group of n tokens at token t0 of chunk cb: waves
+// 0-1 one row each, wave 2 the six ap sums (two rows per lane, reduced by
+// the butterfly).  Tokens t >= n count as k = 0, e^g = 1.
+__device__ __forceinline__ void derive_rows(const FwdCtx& x, const FwdChunk& cb, const int t0, const int n) {
+  FwdGroup& fg = x.sm.fg;
+  if (x.wave < 2) {
+    const int r = x.tid;
+    float kv[GT], dv[GT];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+      kv[t] = t < n ? cb.k[t0 + t][r] : 0.f;
+      dv[t] = t < n ? cb.dec[t0 + t][r] : 1.f;
+    }
+    float gam = 1.f;
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+      gam *= dv[t];
+      fg.gk[t][r] = kv[t] * gam;
+    }
+    fg.gamn[r] = gam;
+    float suf = 1.f;
+#pragma unroll
+    for (int t = GT - 1; t >= 0; --t) {
+      fg.kh[t][r] = kv[t] * suf;
+      suf *= dv[t];
+    }
+  } else if (x.wave == 2) {
+    float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 2 * x.lane + hh;
+      float kv[GT], dv[GT];
+#pragma unroll
+      for (int t = 0; t < GT; ++t) {
+        kv[t] = t < n ? cb.k[t0 + t][r] : 0.f;
+        dv[t] = t < n ? cb.dec[t0 + t][r] : 1.f;
+      }
+#pragma unroll
+      for (int t = 1; t < GT; ++t) {
+        float d = 1.f;
+#pragma unroll
+        for (int j = t - 1; j >= 0; --j) {
+          d *= dv[j + 1];
+          acc[(t - 1) * t / 2 + j] = fmaf(kv[t] * kv[j], d, acc[(t - 1) * t / 2 + j]);
+        }
+      }
+    }
+    const float y = wave_rows_reduce([&](const int i) { return i < 6 ? acc[i] : 0.f; }, x.lane);
+    const int i = ridx(x.lane);
+    if ((x.lane & 3) == 0 && i < 6) fg.ap[i] = y;
+  }
+}
+
+// The forward over the group (n tokens at token t0 of chunk cb) from S (its
+// first state) to its last state, with every token's u and p of column c:
+// one exchange for the four sums a_t = sum_r gk_t S
+// (p_t = a_t + sum_{j<t} ap_tj u_j, u_t = beta_t (v_t - p_t)), then
+// S <- Diag(gamn) S + sum_t kh_t u_t^T.  emit(t, u_t, p_t) for t < n;
+// tokens t >= n get u = 0.
+template <typename Emit>
+__device__ __forceinline__ void fwd_group(FwdCtx& x, const FwdChunk& cb, const int t0, const int n, float (&s)[NR],
+                                          Emit&& emit) {
+  const FwdGroup& fg = x.sm.fg;
   const int r0 = NR * x.grp;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};   // four partial sums: a short dependent chain
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NR / 4; ++j) {
-    const f4 kd = l4(&tg.kd[m][r0 + 4 * j]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(kd[e], s[4 * j + e], acc[e]);
+    for (int t = 0; t < GT; ++t) {
+      const f4 kk = l4(&fg.gk[t][r0 + 4 * j]);
+      acc[t] = fmaf(kk[0], s[4 * j], fmaf(kk[1], s[4 * j + 1], fmaf(kk[2], s[4 * j + 2], fmaf(kk[3], s[4 * j + 3], acc[t]))));
+    }
   }
-  pp = x.col_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  u = tg.beta[m] * (tg.v[m][x.c] - pp);
-  if (upd) update_only(x, tg, m, u, s);
+  x.sm.colpart4[x.grp][x.c] = acc;
+  __syncthreads();
+  f4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < NGRP; ++g) a += x.sm.colpart4[g][x.c];
+  float u[GT];
+#pragma unroll
+  for (int t = 0; t < GT; ++t) {
+    float pt = a[t];
+#pragma unroll
+    for (int j = 0; j < t; ++j) pt = fmaf(fg.ap[(t - 1) * t / 2 + j], u[j], pt);
+    u[t] = t < n ? cb.beta[t0 + t] * (cb.v[t0 + t][x.c] - pt) : 0.f;
+    if (t < n) emit(t, u[t], pt);
+  }
+#pragma unroll
+  for (int j = 0; j < NR / 4; ++j) {
+    const f4 gn = l4(&fg.gamn[r0 + 4 * j]);
+    const f4 h0 = l4(&fg.kh[0][r0 + 4 * j]);
+    const f4 h1 = l4(&fg.kh[1][r0 + 4 * j]);
+    const f4 h2 = l4(&fg.kh[2][r0 + 4 * j]);
+    const f4 h3 = l4(&fg.kh[3][r0 + 4 * j]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      s[4 * j + e] = fmaf(gn[e], s[4 * j + e], fmaf(h0[e], u[0], fmaf(h1[e], u[1], fmaf(h2[e], u[2], h3[e] * u[3]))));
+  }
+}
+
+// A chunk's loads for the forward launch, in registers between their issue
+// and their store to LDS: threads 0-511 k, 512-1023 g (token (tid / 32) % 16,
+// four bf16 at 4 (tid % 32)); every thread v (token tid / 64, two bf16 at
+// 2 (tid % 64)); threads 0-15 beta of token tid.  Tokens past the chunk's n
+// read zero.  Every thread issues the same three loads.
+__device__ __forceinline__ void fetch_chunk(const BwdParams& p, const int h, const int t0, const int n, const int tid,
+                                            u4& x) {
+  const uint32_t row = static_cast<uint32_t>(p.H) * BD * 2;
+  const size_t tok0 = static_cast<size_t>(t0) * p.H + h;
+  const uint32_t nrec = (n - 1) * row + BD * 2;
+  const int m = (tid >> 5) & (CK - 1);
+  const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rsrc((tid >= NT / 2 ? p.g : p.k) + tok0 * BD, nrec),
+                                                    m * row + 8 * (tid & 31), 0, 0);
+  const uint32_t vv = __builtin_amdgcn_raw_buffer_load_b32(rsrc(p.v + tok0 * BD, nrec), (tid >> 6) * row + 4 * (tid & 63),
+                                                           0, 0);
+  const uint32_t nb = (n - 1) * p.H * 2 + 2;
+  const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(rsrc(p.beta + tok0, nb), tid < CK ? tid * p.H * 2 : nb, 0, 0);
+  x = u4{a[0], a[1], vv, bb};
+}
+
+__device__ __forceinline__ void store_chunk(FwdChunk& cb, const int n, const int tid, const u4& x) {
+  const int m = (tid >> 5) & (CK - 1);
+  if (m < n) {
+    const uint32_t w[4] = {x[0] & 0xffffu, x[0] >> 16, x[1] & 0xffffu, x[1] >> 16};
+    f4 r;
+    if (tid >= NT / 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_exp2f(bfv(w[e]) * kLog2eB);
+      *reinterpret_cast<f4*>(&cb.dec[m][4 * (tid & 31)]) = r;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = bfv(w[e]);
+      *reinterpret_cast<f4*>(&cb.k[m][4 * (tid & 31)]) = r;
+    }
+  }
+  const int mv = tid >> 6;
+  if (mv < n) {
+    cb.v[mv][2 * (tid & 63)] = bfv(x[2] & 0xffffu);
+    cb.v[mv][2 * (tid & 63) + 1] = bfv(x[2] >> 16);
+  }
+  if (tid < n) cb.beta[tid] = bfv(x[3]);
 }
 
 // dS += q do^T for this thread's elements; returns its partial of du = dS^T k.
@@ -612,155 +764,177 @@ __global__ void __launch_bounds__(kBwdSummaryThreads) kda_backward_summary_narro
   backward_summary<BD * BD / kBwdSummaryThreads>(p);
 }
 
-// Every (fragment, head) item: the forward from the fragment's start state
-// (carry-in C_r for a carried fragment, else the initial state or zero) with
-// checkpoints every 16 tokens, then per 4-token group from the last: the
-// recompute of its states and the reverse steps.  The cotangent starts from
-// D_r (when the fragment ends its segment) plus dfinal (when it ends its
+// Per (fragment, head) item: the item's fields, its checkpoint and u/p
+// addressing, and the group prefetch (shared by the two fragment launches).
+struct Item {
+  int32_t flags, seg, seq, beg, len, ng, nch, top, h;
+  float* ck;   // checkpoint of chunk j at ck + j H MAT
+  __device__ Item(const BwdParams& p, const int item) {
+    const int f = p.plan[p.L.frag_order + item / p.hn];
+    h = p.h0 + item % p.hn;
+    flags = p.plan[p.L.frag_flags + f];
+    seg = p.plan[p.L.frag_seg + f];
+    seq = p.plan[p.L.frag_seq + f];
+    beg = p.plan[p.L.frag_begin + f];
+    len = p.plan[p.L.frag_end + f] - beg;
+    ng = (len + GT - 1) / GT;          // 4-token groups
+    nch = (len + CK - 1) / CK;         // 16-token chunks
+    top = ng - GPC * (nch - 1);        // groups of the last chunk
+    ck = p.ckpt + (static_cast<size_t>(beg / CK + f) * p.H + h) * MAT;
+  }
+  __device__ int gtokens(const int g) const { return min(GT, len - GT * g); }
+  // [u | p] of token t (1 KiB per token and head)
+  __device__ float* up_base(const BwdParams& p, const int t) const {
+    return p.upbuf + (static_cast<size_t>(t) * p.H + h) * 2 * BD;
+  }
+};
+
+// One token group: wait for its vectors, prefetch group gn's (gn < 0: none),
+// run body(tg, n), then store the prefetch for the next group.
+template <typename Body>
+__device__ __forceinline__ void token_group(Ctx& x, const BwdParams& p, const Item& it, const int g, const int gn,
+                                            Body&& body) {
+  Fetch fx;
+  __syncthreads();
+  if (gn >= 0) fetch_group(p, it.h, it.beg + GT * gn, it.gtokens(gn), x.tid, x.wave, fx);
+  body(x.sm.tg[x.gb], it.gtokens(g));
+  if (gn >= 0) store_group(x.sm.tg[x.gb ^ 1], it.gtokens(gn), x.tid, x.wave, fx);
+  x.gb ^= 1;
+}
+
+// Every (fragment, head) item, forward from the fragment's start state
+// (carry-in C_r for a carried fragment, else the initial state or zero): the
+// state at the start of every 16-token chunk (put_ckpt order) and every
+// token's u and p, for the reverse launch.  Four tokens per exchange; a
+// chunk's inputs are loaded during the chunk before it, so the launch waits
+// for global memory once per chunk (the wait counter is in order: a wait
+// for a load also waits for every store issued before it).  Persistent:
+// workgroup b takes items b, b + grid, ... in the plan's longest-first order.
+__global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_forward_kernel(BwdParams p) {
+  __shared__ FwdSmem sm;
+  const int items = p.plan[3] * p.hn;
+  FwdCtx x(sm, threadIdx.x);
+  const size_t up_token = static_cast<size_t>(p.H) * 2 * BD;   // floats between tokens
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const Item it(p, item);
+    auto ctokens = [&](const int j) { return min(CK, it.len - CK * j); };
+    float run[NR];
+    {
+      const float* s0 = nullptr;
+      if (it.flags & kFragCarried) s0 = p.carry + (static_cast<size_t>(it.seg) * p.H + it.h) * MAT;
+      else if (p.h0s != nullptr) s0 = p.h0s + (static_cast<size_t>(it.seq) * p.H + it.h) * MAT;
+      load_state(s0, x.voff, run);
+    }
+    __syncthreads();   // the previous item's reads of both chunk buffers are done
+    {
+      u4 f0;
+      fetch_chunk(p, it.h, it.beg, ctokens(0), x.tid, f0);
+      store_chunk(sm.ch[0], ctokens(0), x.tid, f0);
+    }
+    wait_vmem();
+    for (int j = 0; j < it.nch; ++j) {
+      const int nj = ctokens(j);
+      const FwdChunk& cb = sm.ch[j & 1];
+      u4 fx;
+      __syncthreads();   // chunk j's rows are in LDS; chunk j - 1's reads of the other buffer are done
+      if (j + 1 < it.nch) fetch_chunk(p, it.h, it.beg + CK * (j + 1), ctokens(j + 1), x.tid, fx);
+      put_ckpt(it.ck + static_cast<size_t>(j) * p.H * MAT, x.tid, run);
+      for (int gl = 0; GT * gl < nj; ++gl) {
+        const int n = min(GT, nj - GT * gl);
+        if (gl > 0) __syncthreads();   // every read of the previous group's derived rows is done
+        derive_rows(x, cb, GT * gl, n);
+        __syncthreads();
+        const int t0 = it.beg + CK * j + GT * gl;
+        const Rsrc ru = rsrc(it.up_base(p, t0), (n - 1) * up_token * 4 + 2 * BD * 4);
+        fwd_group(x, cb, GT * gl, n, run, [&](const int m, const float u, const float pp) {
+          if (x.wave < 2) {
+            const int o = static_cast<int>(m * up_token * 4) + 4 * x.c;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), ru, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pp), ru, o + 4 * BD, 0, 0);
+          }
+        });
+      }
+      if (j + 1 < it.nch) store_chunk(sm.ch[(j + 1) & 1], ctokens(j + 1), x.tid, fx);
+    }
+  }
+}
+
+// Every (fragment, head) item, backwards from its end: the cotangent starts
+// from D_r (when the fragment ends its segment) plus dfinal (when it ends its
 // sequence); a fragment that starts its sequence writes what reaches that
-// start to dh0.  Persistent: workgroup b takes items b, b + grid, ... in
-// the plan's longest-first order.
+// start to dh0.  Per 4-token group from the last: its first state is
+// recomputed from its chunk's checkpoint by update-only steps with the u
+// that the forward launch kept (no exchange; the chunk's k, e^g and u held
+// in LDS), the state before its token m from that by m more, then the
+// reverse steps.  Persistent, in the forward launch's item order.
 __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
   __shared__ BwdSmem sm;
   // one 16-token chunk's u and p (by token), k and e^g rows
   __shared__ float upc[CK][2][BD];
   __shared__ float ckk[CK][BD];
   __shared__ float ckd[CK][BD];
-  const int H = p.H;
-  const int F = p.plan[3];
-  const int items = F * p.hn;
+  const int items = p.plan[3] * p.hn;
   const int tid = threadIdx.x;
   Ctx x(sm, tid);
+  const size_t up_token = static_cast<size_t>(p.H) * 2 * BD;   // floats between tokens
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int f = p.plan[p.L.frag_order + item / p.hn];
-    const int h = p.h0 + item % p.hn;
-    const int32_t flags = p.plan[p.L.frag_flags + f];
-    const int32_t seg = p.plan[p.L.frag_seg + f];
-    const int32_t seq = p.plan[p.L.frag_seq + f];
-    const int32_t beg = p.plan[p.L.frag_begin + f];
-    const int32_t end = p.plan[p.L.frag_end + f];
-    const int len = end - beg;
-    const int ng = (len + GT - 1) / GT;           // 4-token groups
-    const int nch = (len + CK - 1) / CK;          // 16-token chunks
-    const int top = ng - GPC * (nch - 1);         // groups of the last chunk
-    float* ck = p.ckpt + (static_cast<size_t>(beg / CK + f) * H + h) * MAT;   // chunk j at + j H MAT
-    auto gtokens = [&](const int g) { return min(GT, len - GT * g); };
-
-    // u and p of every token, written by level 1 (a thread per column of
-    // waves 0 and 1): [u | p] per token and head
-    const size_t up_token = static_cast<size_t>(H) * 2 * BD;   // floats between tokens
-    auto up_base = [&](const int t) { return p.upbuf + (static_cast<size_t>(t) * H + h) * 2 * BD; };
-    // One token group: wait for its vectors, prefetch group gn's (gn < 0:
-    // none), run body(tg, n), then store the prefetch for the next group.
-    auto group = [&](const int g, const int gn, auto&& body) {
-      Fetch fx;
-      __syncthreads();
-      const TokGroup& tg = sm.tg[x.gb];
-      if (gn >= 0) fetch_group(p, h, beg + GT * gn, gtokens(gn), tid, x.wave, fx);
-      body(tg, gtokens(g));
-      if (gn >= 0) store_group(sm.tg[x.gb ^ 1], gtokens(gn), tid, x.wave, fx);
-      x.gb ^= 1;
-    };
+    const Item it(p, item);
+    const int h = it.h;
     // Chunk j's k and e^g rows (threads 0-511 k, 512-1023 g: token
-    // (tid / 32) % 16, four values each) and, with with_up, its tokens' u and
-    // p (64 threads per token, 16 bytes each) into LDS.  Called after every
-    // read of the previous chunk's rows: the next group's barrier publishes
-    // them.
-    auto load_chunk = [&](const int j, const bool with_up) {
-      const int t0 = beg + CK * j;
-      const int n = min(CK, len - CK * j);
+    // (tid / 32) % 16, four values each) and its tokens' u and p (64 threads
+    // per token, 16 bytes each) into LDS.  Called after every read of the
+    // previous chunk's rows: the next group's barrier publishes them.
+    auto load_chunk = [&](const int j) {
+      const int t0 = it.beg + CK * j;
+      const int n = min(CK, it.len - CK * j);
       const int m = (tid >> 5) & (CK - 1);
       const bool isg = tid >= NT / 2;
-      const uint32_t row = static_cast<uint32_t>(H) * BD * 2;
-      const size_t tok0 = static_cast<size_t>(t0) * H + h;
+      const uint32_t row = static_cast<uint32_t>(p.H) * BD * 2;
+      const size_t tok0 = static_cast<size_t>(t0) * p.H + h;
       const u2 kg = __builtin_amdgcn_raw_buffer_load_b64(rsrc((isg ? p.g : p.k) + tok0 * BD, (n - 1) * row + BD * 2),
                                                          m * row + 8 * (tid & 31), 0, 0);
-      u4 uv = {0u, 0u, 0u, 0u};
       const int mu = tid >> 6;
-      if (with_up)
-        uv = __builtin_amdgcn_raw_buffer_load_b128(rsrc(up_base(t0), (n - 1) * up_token * 4 + 2 * BD * 4),
-                                                   static_cast<int>(mu * up_token * 4) + 16 * (tid & 63), 0, 0);
+      const u4 uv = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc(it.up_base(p, t0), (n - 1) * up_token * 4 + 2 * BD * 4), static_cast<int>(mu * up_token * 4) + 16 * (tid & 63),
+          0, 0);
       const uint32_t w[4] = {kg[0] & 0xffffu, kg[0] >> 16, kg[1] & 0xffffu, kg[1] >> 16};
       f4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = isg ? __builtin_amdgcn_exp2f(bfv(w[e]) * kLog2eB) : bfv(w[e]);
       *reinterpret_cast<f4*>(isg ? &ckd[m][4 * (tid & 31)] : &ckk[m][4 * (tid & 31)]) = r;
-      if (with_up) *reinterpret_cast<f4*>(&upc[mu][0][0] + 4 * (tid & 63)) = __builtin_bit_cast(f4, uv);
+      *reinterpret_cast<f4*>(&upc[mu][0][0] + 4 * (tid & 63)) = __builtin_bit_cast(f4, uv);
     };
 
-    // run: the running state of level 1, then each reversed group's first
-    // state
-    float run[NR];
-    {
-      const float* s0 = nullptr;
-      if (flags & kFragCarried) s0 = p.carry + (static_cast<size_t>(seg) * H + h) * MAT;
-      else if (p.h0s != nullptr) s0 = p.h0s + (static_cast<size_t>(seq) * H + h) * MAT;
-      load_state(s0, x.voff, run);
-      wait_vmem();
-    }
-    __syncthreads();   // the previous item's reads of both token buffers and the chunk rows are done
-    {
-      Fetch f0;
-      fetch_group(p, h, beg, gtokens(0), tid, x.wave, f0);
-      store_group(sm.tg[x.gb], gtokens(0), tid, x.wave, f0);
-    }
-
-    // level 1: the state at every chunk start and every token's u and p,
-    // forward through the fragment.  The last chunk's u and p also go
-    // straight to LDS, where the reverse reads them first (its last tokens'
-    // stores may not yet be visible to other threads' loads).
-    const int glast = GPC * (nch - 1);   // the last chunk's first group
-    for (int g = 0; g < ng; ++g) {
-      group(g, g + 1 < ng ? g + 1 : ng - 1, [&](const TokGroup& tg, const int n) {
-        if (g % GPC == 0) put_ckpt(ck + static_cast<size_t>(g / GPC) * H * MAT, tid, run);
-        const Rsrc ru = rsrc(up_base(beg + GT * g), (n - 1) * up_token * 4 + 2 * BD * 4);
-#pragma unroll
-        for (int m = 0; m < GT; ++m) {
-          float u, pp;
-          if (m < n) {
-            fwd_step(x, tg, m, run, u, pp, true);
-            if (x.wave < 2) {
-              const int o = static_cast<int>(m * up_token * 4) + 4 * x.c;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), ru, o, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pp), ru, o + 4 * BD, 0, 0);
-              if (g >= glast) {
-                upc[GT * (g - glast) + m][0][x.c] = u;
-                upc[GT * (g - glast) + m][1][x.c] = pp;
-              }
-            }
-          }
-        }
-      });
-    }
-    load_chunk(nch - 1, false);
-
-    // the cotangent at the fragment's end
-    float ds[NR];
-    if (flags & kFragSegLast) {
-      load_state(p.dcarry + (static_cast<size_t>(seg) * H + h) * MAT, x.voff, ds);
+    float ds[NR];   // the cotangent at the fragment's end
+    if (it.flags & kFragSegLast) {
+      load_state(p.dcarry + (static_cast<size_t>(it.seg) * p.H + h) * MAT, x.voff, ds);
     } else {
 #pragma unroll
       for (int i = 0; i < NR; ++i) ds[i] = 0.f;
     }
-    if ((flags & kFragSeqEnd) && p.dfinal != nullptr)
-      add_state(p.dfinal + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+    if ((it.flags & kFragSeqEnd) && p.dfinal != nullptr)
+      add_state(p.dfinal + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
     wait_vmem();
+    __syncthreads();   // the previous item's reads of both token buffers and the chunk rows are done
+    {
+      Fetch f0;
+      fetch_group(p, h, it.beg + GT * (it.ng - 1), it.gtokens(it.ng - 1), tid, x.wave, f0);
+      store_group(sm.tg[x.gb], it.gtokens(it.ng - 1), tid, x.wave, f0);
+    }
+    load_chunk(it.nch - 1);
 
-    // the groups backwards, chunk by chunk.  A group's first state is
-    // recomputed from its chunk's checkpoint by update-only steps with the
-    // u that level 1 kept (no exchange), and the state before its token m
-    // from that by m more; the chunk's rows stay in LDS for this.
-    for (int j = nch - 1; j >= 0; --j) {
+    float run[NR];
+    for (int j = it.nch - 1; j >= 0; --j) {
       const int g0 = GPC * j;
-      const int g1 = g0 + (j == nch - 1 ? top : GPC);   // the chunk's groups [g0, g1)
-      const float* ckj = ck + static_cast<size_t>(j) * H * MAT;
+      const int g1 = g0 + (j == it.nch - 1 ? it.top : GPC);   // the chunk's groups [g0, g1)
+      const float* ckj = it.ck + static_cast<size_t>(j) * p.H * MAT;
       for (int g = g1 - 1; g >= g0; --g) {
-        group(g, g - 1, [&](const TokGroup& tg, const int n) {
+        token_group(x, p, it, g, g - 1, [&](const TokGroup& tg, const int n) {
           float w[NR];
           get_ckpt(ckj, tid, run);
           for (int q = 0; q < GT * (g - g0); ++q) update_rows(x, ckk[q], ckd[q], upc[q][0][x.c], run);
-          const int t0 = beg + GT * g;
+          const int t0 = it.beg + GT * g;
           const float(&upg)[GT][2][BD] = *reinterpret_cast<const float(*)[GT][2][BD]>(&upc[GT * (g - g0)][0][0]);
 #pragma unroll
           for (int i = 0; i < NR; ++i) w[i] = run[i];
@@ -785,10 +959,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
           rev_tail(x, p, h, tg, 0, t0, 0);
         });
       }
-      if (j > 0) load_chunk(j - 1, true);   // every read of chunk j's rows ended at the barrier above
+      if (j > 0) load_chunk(j - 1);   // every read of chunk j's rows ended at the barrier above
     }
-    if (!(flags & kFragCarried) && p.dh0 != nullptr)
-      store_state(p.dh0 + (static_cast<size_t>(seq) * H + h) * MAT, x.voff, ds);
+    if (!(it.flags & kFragCarried) && p.dh0 != nullptr)
+      store_state(p.dh0 + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
   }
 }
 

@@ -98,7 +98,8 @@ struct BwdParams {
 __global__ void kda_chunk_kernel(ChunkParams p);
 __global__ void kda_backward_summary_kernel(BwdParams p);         // kBwdThreads threads
 __global__ void kda_backward_summary_narrow_kernel(BwdParams p);  // kBwdSummaryThreads threads
-__global__ void kda_backward_fragment_kernel(BwdParams p);
+__global__ void kda_backward_forward_kernel(BwdParams p);         // kBwdThreads threads
+__global__ void kda_backward_fragment_kernel(BwdParams p);        // kBwdThreads threads
 __global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_compose_kernel(ComposeParams p);
 __global__ void kda_compose_reverse_kernel(ComposeParams p);
