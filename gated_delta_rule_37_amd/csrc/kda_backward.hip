@@ -72,11 +72,19 @@ struct alignas(16) TokGroup {
   float beta[GT];
 };
 
-struct alignas(16) BwdSmem {
-  TokGroup tg[2];                 // by group parity
-  float colpart[2][NGRP][BD];     // row-sum partials, by exchange parity
-  float rowpart[2][3][2][BD];     // column sums of the two waves of a row group, by token parity
-  float red[2][4];                // dbeta's and u.do's sums of waves 2 and 3, by token parity
+// The reverse launch's LDS: two token groups (by group parity), the du
+// exchange (one partial per 32-row block, by exchange parity), the row sums
+// (one partial per 32-column block, by token parity), dbeta's and u.do's
+// column sums (one partial per 32-column block, by token parity), and one
+// 16-token chunk's u and p (by token), k and e^g rows for the recompute.
+struct alignas(16) RevSmem {
+  TokGroup tg[2];
+  float colpart[2][4][BD];
+  float rowpart[2][3][4][BD];
+  float red[2][2][4];
+  float upc[CK][2][BD];
+  float ckk[CK][BD];
+  float ckd[CK][BD];
 };
 
 // The forward launch's LDS: two 16-token chunks' k, e^g, v and beta (by
@@ -243,20 +251,6 @@ __device__ __forceinline__ float wave_rows_reduce(Val&& val, const int lane) {
   return y;
 }
 
-// Sums of two values over the wave's 64 lanes, by lane-swap and DPP moves
-// only: lanes 0-31 return the sum of a, lanes 32-63 that of b.
-__device__ __forceinline__ float wave_sum2(const float a, const float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  y = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // rows 0-1 and 2-3 summed
-  y += dpp<0xB1>(y);                                   // quad_perm [1,0,3,2]
-  y += dpp<0x4E>(y);                                   // quad_perm [2,3,0,1]
-  y += dpp<0x141>(y);                                  // row_half_mirror
-  y += dpp<0x140>(y);                                  // row_mirror
-  return y;
-}
-
 // The thread's 16 elements of a [128][128] FP32 state at a uniform base:
 // rows 16 grp + i, column c, i.e. byte offset voff + 512 i with
 // voff = 4 (2048 grp + c).
@@ -270,83 +264,22 @@ __device__ __forceinline__ void load_state(const float* src, const int voff, flo
 #pragma unroll
   for (int i = 0; i < NR; ++i) s[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, i * 512, 0));
 }
-__device__ __forceinline__ void add_state(const float* src, const int voff, float (&s)[NR]) {
-  const Rsrc r = rsrc(src, MAT * 4);
-#pragma unroll
-  for (int i = 0; i < NR; ++i) s[i] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, i * 512, 0));
-}
 __device__ __forceinline__ void store_state(float* dst, const int voff, const float (&s)[NR]) {
   const Rsrc r = rsrc(dst, MAT * 4);
 #pragma unroll
   for (int i = 0; i < NR; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[i]), r, voff, i * 512, 0);
 }
-// Checkpoints in the workgroup's own order: thread tid's 16 elements are
-// contiguous at byte 64 tid (four 16-byte accesses).
-__device__ __forceinline__ void put_ckpt(float* dst, const int tid, const float (&s)[NR]) {
-  const Rsrc r = rsrc(dst, MAT * 4);
-#pragma unroll
-  for (int j = 0; j < NR / 4; ++j)
-    __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(u4, f4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]}), r, 4 * NR * tid, 16 * j, 0);
-}
-__device__ __forceinline__ void get_ckpt(const float* src, const int tid, float (&s)[NR]) {
-  const Rsrc r = rsrc(src, MAT * 4);
-#pragma unroll
-  for (int j = 0; j < NR / 4; ++j) {
-    const f4 t = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * NR * tid, 16 * j, 0));
-    s[4 * j] = t[0];
-    s[4 * j + 1] = t[1];
-    s[4 * j + 2] = t[2];
-    s[4 * j + 3] = t[3];
-  }
-}
-
-// Per-thread context of a 1024-thread launch over its LDS.
-template <typename Smem>
-struct CtxT {
-  Smem& sm;
+// Per-thread context of the forward launch: thread (c, grp) = (tid % 128,
+// tid / 128) holds column c of rows [16 grp, 16 grp + 16) of the state.
+struct FwdCtx {
+  FwdSmem& sm;
   int tid, c, grp, lane, wave;   // grp and wave are wave-uniform
   int voff;  // byte offset of the thread's first state element, 4 (NR BD grp + c)
-  int par;   // colpart parity
-  int gb;    // token-group buffer parity
 
-  __device__ CtxT(Smem& s, const int t)
+  __device__ FwdCtx(FwdSmem& s, const int t)
       : sm(s), tid(t), c(t & (BD - 1)), grp(__builtin_amdgcn_readfirstlane(t >> 7)), lane(t & 63),
-        wave(__builtin_amdgcn_readfirstlane(t >> 6)), voff(4 * (NR * BD * (t >> 7) + (t & (BD - 1)))), par(0),
-        gb(0) {}
-
-  // sum over all 128 rows of the column partials (one per row group)
-  __device__ __forceinline__ float col_sum(const float part) {
-    float* cp = &sm.colpart[par][0][0];
-    cp[grp * BD + c] = part;
-    __syncthreads();
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < NGRP; ++g) s += cp[g * BD + c];
-    par ^= 1;
-    return s;
-  }
+        wave(__builtin_amdgcn_readfirstlane(t >> 6)), voff(4 * (NR * BD * (t >> 7) + (t & (BD - 1)))) {}
 };
-using Ctx = CtxT<BwdSmem>;
-using FwdCtx = CtxT<FwdSmem>;
-
-// S <- Diag(e^g) S + k u^T for this thread's elements, from a token's k and
-// e^g rows in LDS, read four at a time (broadcast reads), not held.
-__device__ __forceinline__ void update_rows(const Ctx& x, const float* krow, const float* drow, const float u,
-                                            float (&s)[NR]) {
-  const int r0 = NR * x.grp;
-#pragma unroll
-  for (int j = 0; j < NR / 4; ++j) {
-    const f4 kk = l4(&krow[r0 + 4 * j]);
-    const f4 dc = l4(&drow[r0 + 4 * j]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[4 * j + e] = fmaf(dc[e], s[4 * j + e], kk[e] * u);
-  }
-}
-__device__ __forceinline__ void update_only(const Ctx& x, const TokGroup& tg, const int m, const float u,
-                                            float (&s)[NR]) {
-  update_rows(x, tg.k[m], tg.dec[m], u, s);
-}
 
 // The derived rows of the group of n tokens at token t0 of chunk cb: waves
 // 0-1 one row each, wave 2 the six ap sums (two rows per lane, reduced by
@@ -491,100 +424,214 @@ __device__ __forceinline__ void store_chunk(FwdChunk& cb, const int n, const int
   if (tid < n) cb.beta[tid] = bfv(x[3]);
 }
 
-// dS += q do^T for this thread's elements; returns its partial of du = dS^T k.
-__device__ __forceinline__ float add_qdo(const Ctx& x, const TokGroup& tg, const int m, const float doc,
-                                        float (&ds)[NR]) {
-  const int r0 = NR * x.grp;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+// The reverse launch's layout: wave w owns the 32 x 32 block of rows from
+// 32 (w / 4) and columns from 32 (w % 4); lane l of it the 4 x 4 block of
+// rows R0 + i, R0 = 32 (w / 4) + 4 (l / 8), and columns C0 + j,
+// C0 = 32 (w % 4) + 4 (l % 8), as s[4 i + j].  A sum over rows (du) is taken
+// over the thread's four rows, the wave's eight row quads (lane swaps and a
+// DPP move) and the four row blocks (LDS); a sum over columns (the rows of
+// dq, dk, dg) over the thread's four columns, the wave's eight column quads
+// (DPP moves) and the four column blocks (LDS).  Compared with a column of
+// 16 rows per thread, three of every four additions of the per-token row
+// sums happen inside the thread.
+struct R4 {
+  RevSmem& sm;
+  int tid, lane, wave, rb, cb, R0, C0, voff;   // wave, rb and cb are wave-uniform
+  int par;   // du exchange parity
+  int gb;    // token-group buffer parity
+  __device__ R4(RevSmem& s, const int t)
+      : sm(s), tid(t), lane(t & 63), wave(__builtin_amdgcn_readfirstlane(t >> 6)), rb(wave >> 2), cb(wave & 3),
+        R0(32 * rb + 4 * ((t & 63) >> 3)), C0(32 * cb + 4 * (t & 7)), voff(4 * (BD * R0 + C0)), par(0), gb(0) {}
+};
+
+// The thread's 16 elements of a row-major [128][128] FP32 state: row R0 + i
+// at byte voff + 512 i, four columns per 16-byte access.
+__device__ __forceinline__ void load4(const float* src, const int voff, float (&s)[16]) {
+  if (src == nullptr) {
 #pragma unroll
-  for (int j = 0; j < NR / 4; ++j) {
-    const f4 qq = l4(&tg.q[m][r0 + 4 * j]);
-    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    return;
+  }
+  const Rsrc r = rsrc(src, MAT * 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ds[4 * j + e] = fmaf(qq[e], doc, ds[4 * j + e]);
-      acc[e] = fmaf(ds[4 * j + e], kk[e], acc[e]);
+  for (int i = 0; i < 4; ++i) {
+    const f4 t = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 512 * i, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * i + j] = t[j];
+  }
+}
+__device__ __forceinline__ void add4(const float* src, const int voff, float (&s)[16]) {
+  const Rsrc r = rsrc(src, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f4 t = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 512 * i, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * i + j] += t[j];
+  }
+}
+__device__ __forceinline__ void store4(float* dst, const int voff, const float (&s)[16]) {
+  const Rsrc r = rsrc(dst, MAT * 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(u4, f4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]}), r, voff, 512 * i, 0);
+}
+
+// S <- Diag(e^g) S + k u^T for the thread's block, from a token's k and e^g
+// rows and its u (by column) in LDS.
+__device__ __forceinline__ void update4(const R4& x, const float* krow, const float* drow, const float* urow,
+                                        float (&s)[16]) {
+  const f4 kk = l4(krow + x.R0), dc = l4(drow + x.R0), uu = l4(urow + x.C0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * i + j] = fmaf(dc[i], s[4 * i + j], kk[i] * uu[j]);
+}
+
+// Sum over the wave's eight row quads (lane bits 3-5) of four per-column
+// values v[j]: returns that of j = 2 b5 + b4 (b = the lane's bits; lanes
+// that differ in bit 3 agree).  Rows of 32 swapped (bit 5), rows of 16
+// swapped (bit 4), rotation by 8 within 16 (bit 3).
+__device__ __forceinline__ float sum_row_quads(const f4 v) {
+  const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
+  const float a = __uint_as_float(r0[0]) + __uint_as_float(r0[1]);
+  const float b = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float c = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+  return c + dpp<0x128>(c);   // row_ror:8
+}
+
+// Sum over the wave's eight column quads (lane bits 0-2) of four per-row
+// values w[i]: returns that of i = 2 b2 + b1 (lanes that differ in bit 0
+// agree).  Mirror within 8 lanes (pairs bit 2, also flips bits 0-1), then
+// quad permutations for bits 1 and 0; the flips cover the eight lanes once.
+__device__ __forceinline__ float sum_col_quads(const f4 w, const int lane) {
+  const float a0 = w[0] + dpp<0x141>(w[0]);   // row_half_mirror
+  const float a2 = w[2] + dpp<0x141>(w[2]);
+  const float b0 = w[1] + dpp<0x141>(w[1]);
+  const float b2 = w[3] + dpp<0x141>(w[3]);
+  const bool hi2 = (lane & 4) != 0;
+  const float a = hi2 ? a2 : a0;
+  const float b = hi2 ? b2 : b0;
+  const float ca = a + dpp<0x4E>(a);          // quad_perm [2,3,0,1]
+  const float cb = b + dpp<0x4E>(b);
+  const float c = (lane & 2) ? cb : ca;
+  return c + dpp<0xB1>(c);                    // quad_perm [1,0,3,2]
+}
+
+// Sum of one value over the wave's eight column quads (every lane).
+__device__ __forceinline__ float sum_col_quads1(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v + dpp<0x141>(v);
+}
+
+// The reverse step of token m (global index t) from S_{t-1} = st, with u and
+// p of the thread's columns from the forward launch, in two parts around a
+// pending tail: rev_begin adds q do^T and sums du over the rows (its exchange
+// is the step's only barrier); rev_rest writes dv, publishes the row sums
+// into rowpart[b] and red[b] and steps the cotangent back.  rev_tail (waves
+// 0 and 1, one row each) turns a published token's sums into its dq, dk, dg
+// and dbeta after a later barrier: the next token's exchange, or the barrier
+// that ends a group.  Consecutive tokens alternate b.
+__device__ __forceinline__ f4 rev_begin(R4& x, const TokGroup& tg, const int m, float (&ds)[16]) {
+  const f4 qq = l4(&tg.q[m][x.R0]), kk = l4(&tg.k[m][x.R0]), dd = l4(&tg.dov[m][x.C0]);
+  f4 pc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ds[4 * i + j] = fmaf(qq[i], dd[j], ds[4 * i + j]);
+      pc[j] = fmaf(ds[4 * i + j], kk[i], pc[j]);
+    }
+  const float v = sum_row_quads(pc);
+  float* cp = &x.sm.colpart[x.par][0][0];
+  if ((x.lane & 8) == 0) cp[x.rb * BD + x.C0 + 2 * ((x.lane >> 5) & 1) + ((x.lane >> 4) & 1)] = v;
+  __syncthreads();
+  const f4 du = (l4(cp + x.C0) + l4(cp + BD + x.C0)) + (l4(cp + 2 * BD + x.C0) + l4(cp + 3 * BD + x.C0));
+  x.par ^= 1;
+  return du;
+}
+
+__device__ __forceinline__ void rev_rest(R4& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
+                                         const int t, const float (&st)[16], float (&ds)[16], const f4 uu,
+                                         const f4 pp, const f4 du, const int b) {
+  const size_t tk = static_cast<size_t>(t) * p.H + h;
+  const float beta = tg.beta[m];
+  const f4 dd = l4(&tg.dov[m][x.C0]);
+  const f4 dp = -beta * du;
+  if (x.rb == 1) {   // waves 4-7, one per column block: dv, dbeta's and u.do's terms
+    if (x.lane < 8)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.C0,
+                                             0, 0);
+    const f4 vv = l4(&tg.v[m][x.C0]);
+    float sb = 0.f, su = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sb = fmaf(du[j], vv[j] - pp[j], sb);
+      su = fmaf(uu[j], dd[j], su);
+    }
+    sb = sum_col_quads1(sb);
+    su = sum_col_quads1(su);
+    if (x.lane == 0) {
+      x.sm.red[b][0][x.cb] = sb;
+      x.sm.red[b][1][x.cb] = su;
     }
   }
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-// dS_{t-1} = Diag(e^g) (dS + k dp^T)
-__device__ __forceinline__ void cotangent_step(const Ctx& x, const TokGroup& tg, const int m, const float dp,
-                                               float (&ds)[NR]) {
-  const int r0 = NR * x.grp;
+  // per row over the thread's columns: W = S do, X = S dp, Y = <S, dS>, Z = dS u;
+  // the rows of dq, dk and dg need W, Z + e X and Y + k X
+  const f4 kk = l4(&tg.k[m][x.R0]), ee = l4(&tg.dec[m][x.R0]);
+  f4 w, q1, q2;
 #pragma unroll
-  for (int j = 0; j < NR / 4; ++j) {
-    const f4 kk = l4(&tg.k[m][r0 + 4 * j]);
-    const f4 dc = l4(&tg.dec[m][r0 + 4 * j]);
+  for (int i = 0; i < 4; ++i) {
+    float W = 0.f, X = 0.f, Y = 0.f, Z = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ds[4 * j + e] = dc[e] * fmaf(kk[e], dp, ds[4 * j + e]);
+    for (int j = 0; j < 4; ++j) {
+      W = fmaf(st[4 * i + j], dd[j], W);
+      X = fmaf(st[4 * i + j], dp[j], X);
+      Y = fmaf(st[4 * i + j], ds[4 * i + j], Y);
+      Z = fmaf(ds[4 * i + j], uu[j], Z);
+    }
+    w[i] = W;
+    q1[i] = fmaf(ee[i], X, Z);
+    q2[i] = fmaf(kk[i], X, Y);
   }
+  const float r0 = sum_col_quads(w, x.lane);
+  const float r1 = sum_col_quads(q1, x.lane);
+  const float r2 = sum_col_quads(q2, x.lane);
+  if ((x.lane & 1) == 0) {
+    const int row = x.R0 + 2 * ((x.lane >> 2) & 1) + ((x.lane >> 1) & 1);
+    x.sm.rowpart[b][0][x.cb][row] = r0;
+    x.sm.rowpart[b][1][x.cb][row] = r1;
+    x.sm.rowpart[b][2][x.cb][row] = r2;
+  }
+  // dS_{t-1} = Diag(e^g) (dS + k dp^T)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ds[4 * i + j] = ee[i] * fmaf(kk[i], dp[j], ds[4 * i + j]);
 }
 
-// The full reverse step of token m (global index t) from S_{t-1} = st, with
-// u and p of column c from the forward pass, in two parts around a pending
-// tail: rev_begin adds q do^T and sums du over the rows (its exchange is the
-// step's only barrier); rev_rest writes dv, publishes the column sums of the
-// row quantities into rowpart[b] and red[b] and steps the cotangent back.
-// rev_tail (waves 0 and 1, one row each) turns a published token's sums into
-// its dq, dk, dg and dbeta after a later barrier: the next token's exchange,
-// or the barrier that ends a group.  Consecutive tokens alternate b.
-__device__ __forceinline__ float rev_begin(Ctx& x, const TokGroup& tg, const int m, float (&ds)[NR]) {
-  return x.col_sum(add_qdo(x, tg, m, tg.dov[m][x.c], ds));
-}
-
-__device__ __forceinline__ void rev_rest(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
-                                         const int t, const float (&st)[NR], float (&ds)[NR], const float u,
-                                         const float pp, const float du, const int b) {
-  const size_t tk = static_cast<size_t>(t) * p.H + h;
-  const int r0 = NR * x.grp;
-  const float doc = tg.dov[m][x.c];
-  const float beta = tg.beta[m];
-  const float dp = -beta * du;
-  // row group 1 (waves 2 and 3, on the other two SIMDs than row group 0's,
-  // which runs rev_tail): dv, dbeta's and u.do's terms
-  if (x.grp == 1) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(beta * du), rsrc(p.dv + tk * BD, BD * 4), 4 * x.c, 0, 0);
-    const float s2 = wave_sum2(du * (tg.v[m][x.c] - pp), u * doc);
-    if ((x.lane & 31) == 0) x.sm.red[b][2 * (x.lane >> 5) + (x.wave & 1)] = s2;
-  }
-  // column sums of three row quantities (S = S_{t-1}, e = e^g of the row):
-  //   dq_r = e_r sum_c S do + k_r (u . do)
-  //   dk_r = sum_c (dS u + e_r S dp)
-  //   dg_r = e_r sum_c S (dS + k_r dp)
-  // lanes with bits 0-1 clear publish
-  const int half = x.wave & 1;
-  const bool pub = (x.lane & 3) == 0;
-  const int row = NR * x.grp + ridx(x.lane);
-  const float* krow = &tg.k[m][r0];
-  const float* drow = &tg.dec[m][r0];
-  const float q0 = wave_rows_reduce([&](const int i) { return st[i] * doc; }, x.lane);
-  const float q1 = wave_rows_reduce([&](const int i) { return fmaf(ds[i], u, drow[i] * (st[i] * dp)); }, x.lane);
-  const float q2 = wave_rows_reduce([&](const int i) { return st[i] * fmaf(krow[i], dp, ds[i]); }, x.lane);
-  if (pub) {
-    x.sm.rowpart[b][0][half][row] = q0;
-    x.sm.rowpart[b][1][half][row] = q1;
-    x.sm.rowpart[b][2][half][row] = q2;
-  }
-  cotangent_step(x, tg, m, dp, ds);
-}
-
-__device__ __forceinline__ void rev_tail(Ctx& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
+// dq = e^g (S_{t-1} do) + k (u . do), dk = dS u + e^g (S_{t-1} dp),
+// dg = e^g rowsum(S_{t-1} o (dS + k dp^T)), dbeta = <du, v - p>.
+__device__ __forceinline__ void rev_tail(const R4& x, const BwdParams& p, const int h, const TokGroup& tg, const int m,
                                          const int t, const int b) {
   if (x.wave >= 2) return;
   const size_t tk = static_cast<size_t>(t) * p.H + h;
   const int r = x.tid;
-  const float x1 = x.sm.rowpart[b][0][0][r] + x.sm.rowpart[b][0][1][r];
-  const float x2 = x.sm.rowpart[b][1][0][r] + x.sm.rowpart[b][1][1][r];
-  const float x3 = x.sm.rowpart[b][2][0][r] + x.sm.rowpart[b][2][1][r];
+  const auto& rp = x.sm.rowpart[b];
+  const float x1 = (rp[0][0][r] + rp[0][1][r]) + (rp[0][2][r] + rp[0][3][r]);
+  const float x2 = (rp[1][0][r] + rp[1][1][r]) + (rp[1][2][r] + rp[1][3][r]);
+  const float x3 = (rp[2][0][r] + rp[2][1][r]) + (rp[2][2][r] + rp[2][3][r]);
+  const auto& rd = x.sm.red[b];
+  const float ud = (rd[1][0] + rd[1][1]) + (rd[1][2] + rd[1][3]);
   const float dr = tg.dec[m][r], kr = tg.k[m][r];
-  const float ud = x.sm.red[b][2] + x.sm.red[b][3];
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dr, x1, kr * ud)), rsrc(p.dq + tk * BD, BD * 4), 4 * r,
                                         0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x2), rsrc(p.dk + tk * BD, BD * 4), 4 * r, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr * x3), rsrc(p.dg + tk * BD, BD * 4), 4 * r, 0, 0);
-  if (r == 0) p.dbeta[tk] = x.sm.red[b][0] + x.sm.red[b][1];
+  if (r == 0) p.dbeta[tk] = (rd[0][0] + rd[0][1]) + (rd[0][2] + rd[0][3]);
 }
 
 }  // namespace
@@ -792,7 +839,7 @@ struct Item {
 // One token group: wait for its vectors, prefetch group gn's (gn < 0: none),
 // run body(tg, n), then store the prefetch for the next group.
 template <typename Body>
-__device__ __forceinline__ void token_group(Ctx& x, const BwdParams& p, const Item& it, const int g, const int gn,
+__device__ __forceinline__ void token_group(R4& x, const BwdParams& p, const Item& it, const int g, const int gn,
                                             Body&& body) {
   Fetch fx;
   __syncthreads();
@@ -804,7 +851,7 @@ __device__ __forceinline__ void token_group(Ctx& x, const BwdParams& p, const It
 
 // Every (fragment, head) item, forward from the fragment's start state
 // (carry-in C_r for a carried fragment, else the initial state or zero): the
-// state at the start of every 16-token chunk (put_ckpt order) and every
+// state at the start of every 16-token chunk (row-major) and every
 // token's u and p, for the reverse launch.  Four tokens per exchange; a
 // chunk's inputs are loaded during the chunk before it, so the launch waits
 // for global memory once per chunk (the wait counter is in order: a wait
@@ -838,7 +885,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_forward_kernel(Bw
       u4 fx;
       __syncthreads();   // chunk j's rows are in LDS; chunk j - 1's reads of the other buffer are done
       if (j + 1 < it.nch) fetch_chunk(p, it.h, it.beg + CK * (j + 1), ctokens(j + 1), x.tid, fx);
-      put_ckpt(it.ck + static_cast<size_t>(j) * p.H * MAT, x.tid, run);
+      store_state(it.ck + static_cast<size_t>(j) * p.H * MAT, x.voff, run);
       for (int gl = 0; GT * gl < nj; ++gl) {
         const int n = min(GT, nj - GT * gl);
         if (gl > 0) __syncthreads();   // every read of the previous group's derived rows is done
@@ -868,14 +915,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_forward_kernel(Bw
 // in LDS), the state before its token m from that by m more, then the
 // reverse steps.  Persistent, in the forward launch's item order.
 __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(BwdParams p) {
-  __shared__ BwdSmem sm;
-  // one 16-token chunk's u and p (by token), k and e^g rows
-  __shared__ float upc[CK][2][BD];
-  __shared__ float ckk[CK][BD];
-  __shared__ float ckd[CK][BD];
+  __shared__ RevSmem sm;
   const int items = p.plan[3] * p.hn;
   const int tid = threadIdx.x;
-  Ctx x(sm, tid);
+  R4 x(sm, tid);
   const size_t up_token = static_cast<size_t>(p.H) * 2 * BD;   // floats between tokens
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -902,19 +945,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
       f4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = isg ? __builtin_amdgcn_exp2f(bfv(w[e]) * kLog2eB) : bfv(w[e]);
-      *reinterpret_cast<f4*>(isg ? &ckd[m][4 * (tid & 31)] : &ckk[m][4 * (tid & 31)]) = r;
-      *reinterpret_cast<f4*>(&upc[mu][0][0] + 4 * (tid & 63)) = __builtin_bit_cast(f4, uv);
+      *reinterpret_cast<f4*>(isg ? &sm.ckd[m][4 * (tid & 31)] : &sm.ckk[m][4 * (tid & 31)]) = r;
+      *reinterpret_cast<f4*>(&sm.upc[mu][0][0] + 4 * (tid & 63)) = __builtin_bit_cast(f4, uv);
     };
 
-    float ds[NR];   // the cotangent at the fragment's end
+    float ds[16];   // the cotangent at the fragment's end
     if (it.flags & kFragSegLast) {
-      load_state(p.dcarry + (static_cast<size_t>(it.seg) * p.H + h) * MAT, x.voff, ds);
+      load4(p.dcarry + (static_cast<size_t>(it.seg) * p.H + h) * MAT, x.voff, ds);
     } else {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) ds[i] = 0.f;
+      for (int e = 0; e < 16; ++e) ds[e] = 0.f;
     }
     if ((it.flags & kFragSeqEnd) && p.dfinal != nullptr)
-      add_state(p.dfinal + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
+      add4(p.dfinal + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
     wait_vmem();
     __syncthreads();   // the previous item's reads of both token buffers and the chunk rows are done
     {
@@ -924,35 +967,36 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
     }
     load_chunk(it.nch - 1);
 
-    float run[NR];
+    float run[16];
     for (int j = it.nch - 1; j >= 0; --j) {
       const int g0 = GPC * j;
       const int g1 = g0 + (j == it.nch - 1 ? it.top : GPC);   // the chunk's groups [g0, g1)
       const float* ckj = it.ck + static_cast<size_t>(j) * p.H * MAT;
       for (int g = g1 - 1; g >= g0; --g) {
         token_group(x, p, it, g, g - 1, [&](const TokGroup& tg, const int n) {
-          float w[NR];
-          get_ckpt(ckj, tid, run);
-          for (int q = 0; q < GT * (g - g0); ++q) update_rows(x, ckk[q], ckd[q], upc[q][0][x.c], run);
+          float w[16];
+          load4(ckj, x.voff, run);
+          for (int q = 0; q < GT * (g - g0); ++q) update4(x, sm.ckk[q], sm.ckd[q], sm.upc[q][0], run);
           const int t0 = it.beg + GT * g;
-          const float(&upg)[GT][2][BD] = *reinterpret_cast<const float(*)[GT][2][BD]>(&upc[GT * (g - g0)][0][0]);
+          const int q0 = GT * (g - g0);   // the group's first token in the chunk
 #pragma unroll
-          for (int i = 0; i < NR; ++i) w[i] = run[i];
+          for (int e = 0; e < 16; ++e) w[e] = run[e];
 #pragma unroll
           for (int m = 0; m + 1 < GT; ++m)
-            if (m + 1 < n) update_only(x, tg, m, upg[m][0][x.c], w);
+            if (m + 1 < n) update4(x, tg.k[m], tg.dec[m], sm.upc[q0 + m][0], w);
 #pragma unroll
           for (int m = GT - 1; m >= 0; --m) {
             if (m < n) {
               if (m + 1 < n) {
 #pragma unroll
-                for (int i = 0; i < NR; ++i) w[i] = run[i];
+                for (int e = 0; e < 16; ++e) w[e] = run[e];
 #pragma unroll
-                for (int q = 0; q < m; ++q) update_only(x, tg, q, upg[q][0][x.c], w);
+                for (int q = 0; q < m; ++q) update4(x, tg.k[q], tg.dec[q], sm.upc[q0 + q][0], w);
               }
-              const float du = rev_begin(x, tg, m, ds);
+              const f4 du = rev_begin(x, tg, m, ds);
               if (m + 1 < n) rev_tail(x, p, h, tg, m + 1, t0 + m + 1, (m + 1) & 1);   // published before the barrier above
-              rev_rest(x, p, h, tg, m, t0 + m, w, ds, upg[m][0][x.c], upg[m][1][x.c], du, m & 1);
+              rev_rest(x, p, h, tg, m, t0 + m, w, ds, l4(&sm.upc[q0 + m][0][x.C0]), l4(&sm.upc[q0 + m][1][x.C0]), du,
+                       m & 1);
             }
           }
           __syncthreads();
@@ -962,7 +1006,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
       if (j > 0) load_chunk(j - 1);   // every read of chunk j's rows ended at the barrier above
     }
     if (!(it.flags & kFragCarried) && p.dh0 != nullptr)
-      store_state(p.dh0 + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
+      store4(p.dh0 + (static_cast<size_t>(it.seq) * p.H + h) * MAT, x.voff, ds);
   }
 }
 
