@@ -114,3 +114,108 @@ def chunk_backward(q, k, v, g, beta, do, S0, dS_end, C=32):
         dS, dq[a:b], dk[a:b], dv[a:b], dg[a:b], dbeta[a:b] = _chunk(
             states[c], dS, q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], do[a:b])
     return dq, dk, dv, dg, dbeta, dS
+
+
+# ---------------------------------------------------------------------------
+# The same backward in the anchored three-pass form the matrix-core kernels
+# take.  Per chunk of C tokens (a ragged last chunk padded with zero tokens,
+# g = 0: G is flat past the end), with a = G_15 the chunk's anchor and
+# Gc = G_{C-1}:
+#     Kr = k e^{G-a},  Kc = k e^{a-G},  Qr = q e^{G-a}
+#     A' = strict_lower(Kr Kc^T),  T = (I + diag(beta) A')^-1,  Tb = T diag(beta)
+#     P  = lower_incl(Qr Kc^T)
+# pass 1 (forward): R_c = e^{a_c} o S_c (the state entering chunk c, rows
+#     scaled by its anchor), R_{c+1} = fac_c o (R_c + Kc^T Tb (V - Kr R_c)),
+#     fac_c = e^{a_{c+1} + Gc_c - a_c};
+# pass 2 (reverse): D_c = fac_c o Delta_{c+1} (the cotangent of the state
+#     leaving chunk c, rows scaled by e^{Gc - a}; Delta_n is the fragment
+#     end's cotangent and fac_{n-1} = e^{Gc - a} there),
+#     dU = P^T dO + Kc D_c,  dR = Tb^T dU,
+#     Delta_c = D_c + Qr^T dO - Kr^T dR,  dS_start = e^{a_0} o Delta_0;
+# pass 3 (every chunk on its own, from R_c and D_c):
+#     W = Kr R,  X = diag(beta)(V - W),  U = T X,  dU = P^T dO + Kc D
+#     dX = T^T dU,  dR = diag(beta) dX = dv,  dA = strict_lower(-dX U^T)
+#     dbeta = rowsum(dX o (V - W)) + rowsum(dA o A'),  dA' = diag(beta) dA
+#     dP = lower_incl(dO U^T)
+#     dq   = (dO R^T + dP Kc) o e^{G-a}
+#     dk_d = (-dR R^T + dA' Kc) o e^{G-a}
+#     dk_i = (dP^T Qr + dA'^T Kr) o e^{a-G}
+#     dk_h = (U D^T) o e^{a-G}
+#     dk = dk_d + dk_i + dk_h,  dG = q o dq + k o (dk_d - dk_i - dk_h)
+#     dG_{C-1} += colsum(k o dk_h) + rowsum(D o R),  dg = reverse cumsum of dG
+# ---------------------------------------------------------------------------
+def _anchored_operands(q, k, g, C):
+    G = np.cumsum(g, axis=0)
+    a = G[min(15, C - 1)]
+    Gc = G[-1]
+    Kr, Kc, Qr = k * np.exp(G - a), k * np.exp(a - G), q * np.exp(G - a)
+    Ap = (Kr @ Kc.T) * np.tril(np.ones((C, C)), -1)
+    P = (Qr @ Kc.T) * np.tril(np.ones((C, C)))
+    return G, a, Gc, Kr, Kc, Qr, Ap, P
+
+
+def _pad(x, C):
+    out = np.zeros((C,) + x.shape[1:])
+    out[:x.shape[0]] = x
+    return out
+
+
+def anchored_backward(q, k, v, g, beta, do, S0, dS_end, C=32):
+    """Gradients of one head's fragment by the three passes above; returns
+    (dq, dk, dv, dg, dbeta, dS0) and the per-chunk R_c and D_c."""
+    L, K = k.shape
+    nc = (L + C - 1) // C
+    ch = []
+    for c in range(nc):
+        s = slice(c * C, min(L, (c + 1) * C))
+        ch.append(dict(q=_pad(q[s], C), k=_pad(k[s], C), v=_pad(v[s], C), g=_pad(g[s], C),
+                       beta=_pad(beta[s], C), do=_pad(do[s], C), n=s.stop - s.start))
+    for x in ch:
+        x["G"], x["a"], x["Gc"], x["Kr"], x["Kc"], x["Qr"], x["Ap"], x["P"] = _anchored_operands(x["q"], x["k"], x["g"], C)
+        x["T"] = np.linalg.inv(np.eye(C) + x["beta"][:, None] * x["Ap"])
+        x["Tb"] = x["T"] * x["beta"][None, :]
+    fac = [np.exp(ch[c + 1]["a"] + ch[c]["Gc"] - ch[c]["a"]) for c in range(nc - 1)]
+    fac.append(np.exp(ch[-1]["Gc"] - ch[-1]["a"]))
+    # pass 1
+    R = [np.exp(ch[0]["a"])[:, None] * S0]
+    for c in range(nc - 1):
+        x = ch[c]
+        U = x["Tb"] @ (x["v"] - x["Kr"] @ R[c])
+        R.append(fac[c][:, None] * (R[c] + x["Kc"].T @ U))
+    # pass 2
+    D = [None] * nc
+    delta = np.array(dS_end, dtype=np.float64)
+    for c in range(nc - 1, -1, -1):
+        x = ch[c]
+        D[c] = fac[c][:, None] * delta
+        dU = x["P"].T @ x["do"] + x["Kc"] @ D[c]
+        dR = x["Tb"].T @ dU
+        delta = D[c] + x["Qr"].T @ x["do"] - x["Kr"].T @ dR
+    dS0 = np.exp(ch[0]["a"])[:, None] * delta
+    # pass 3
+    outs = {n: [] for n in ("dq", "dk", "dv", "dg", "dbeta")}
+    for c in range(nc):
+        x = ch[c]
+        Rc, Dc = R[c], D[c]
+        eGa, eaG = np.exp(x["G"] - x["a"]), np.exp(x["a"] - x["G"])
+        Rv = x["v"] - x["Kr"] @ Rc
+        U = x["T"] @ (x["beta"][:, None] * Rv)
+        dU = x["P"].T @ x["do"] + x["Kc"] @ Dc
+        dX = x["T"].T @ dU
+        dR = x["beta"][:, None] * dX
+        dA = -(dX @ U.T) * np.tril(np.ones((C, C)), -1)
+        dbeta = np.sum(dX * Rv, axis=1) + np.sum(dA * x["Ap"], axis=1)
+        dAp = x["beta"][:, None] * dA
+        dP = (x["do"] @ U.T) * np.tril(np.ones((C, C)))
+        dq = (x["do"] @ Rc.T + dP @ x["Kc"]) * eGa
+        dk_d = (-dR @ Rc.T + dAp @ x["Kc"]) * eGa
+        dk_i = (dP.T @ x["Qr"] + dAp.T @ x["Kr"]) * eaG
+        dk_h = (U @ Dc.T) * eaG
+        dG = x["q"] * dq + x["k"] * (dk_d - dk_i - dk_h)
+        dG[-1] += np.sum(x["k"] * dk_h, axis=0) + np.sum(Dc * Rc, axis=1)
+        dg = np.cumsum(dG[::-1], axis=0)[::-1]
+        n = x["n"]
+        for name, val in (("dq", dq), ("dk", dk_d + dk_i + dk_h), ("dv", dR), ("dg", dg), ("dbeta", dbeta)):
+            outs[name].append(val[:n])
+    res = tuple(np.concatenate(outs[nm], axis=0) for nm in ("dq", "dk", "dv", "dg", "dbeta"))
+    return res + (dS0,), R, D

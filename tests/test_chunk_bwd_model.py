@@ -73,3 +73,36 @@ def test_chunk_backward_chunking_invariance():
     a = cbm.chunk_backward(*x, C=48)
     b = cbm.chunk_backward(*x, C=3)
     _check(a, b)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 32, 33, 70, 96, 131])
+def test_anchored_three_pass_matches_oracle(T):
+    """The anchored three-pass form (forward anchored states R_c, reverse
+    anchored cotangents D_c, then every chunk's gradients on their own) gives
+    the oracle's gradients, ragged last chunks and one-token fragments
+    included."""
+    x = _inputs(T, 16, 12, seed=700 + T)
+    got, R, D = cbm.anchored_backward(*x, C=32)
+    _check(got, _oracle(*x))
+
+
+def test_anchored_three_pass_beta_zero_and_strong_gates():
+    """beta = 0 tokens and gates three times the pages' scale (in-chunk decay
+    well inside the anchored range in fp64)."""
+    q, k, v, g, beta, do, S0, dS = _inputs(80, 16, 16, seed=21, gate_scale=3.0)
+    beta[[0, 5, 31, 32, 79]] = 0.0
+    got, _, _ = cbm.anchored_backward(q, k, v, g, beta, do, S0, dS, C=32)
+    _check(got, _oracle(q, k, v, g, beta, do, S0, dS), rtol=1e-8)
+
+
+def test_anchored_three_pass_zero_start_and_end():
+    """No start state and no end cotangent (a fragment that starts its
+    sequence and ends where nothing follows): dS0 still picks up every
+    output's cotangent."""
+    q, k, v, g, beta, do, S0, dS = _inputs(64, 8, 8, seed=4)
+    S0[:] = 0.0
+    dS[:] = 0.0
+    got, _, _ = cbm.anchored_backward(q, k, v, g, beta, do, S0, dS, C=32)
+    ref = _oracle(q, k, v, g, beta, do, S0, dS)
+    _check(got, ref)
+    assert np.abs(ref[5]).max() > 1e-3
