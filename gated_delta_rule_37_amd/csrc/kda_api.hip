@@ -390,6 +390,38 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream,
                       /*pieces=*/true);
   if (st != KDA_OK) return st;
+  // the checkpoint launch: every fragment forward from its carry-in (or its
+  // initial state, or zero), the anchored state entering every 32-token chunk
+  // and its T diag(beta); fragments that leave the anchored form's range are
+  // flagged for the token-by-token path
+  const size_t slots = kda::backward_chunk_slots(plan);
+  if (static_cast<int64_t>(slots) * head_count > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  {
+    kda::ChunkParams c{};
+    c.plan = plan_dev;
+    c.L = plan->layout;
+    c.H = H;
+    c.h0 = head_begin;
+    c.hn = head_count;
+    c.k = k;
+    c.v = v;
+    c.g = g;
+    c.beta = beta;
+    c.carry = carry;
+    c.init_state = initial_state;
+    set_gate(c, -INFINITY);
+    c.chunk_cache = reinterpret_cast<uint16_t*>(ws + W.tcache);
+    c.ckpt = reinterpret_cast<float*>(ws + W.ck32);
+    c.item_flag = reinterpret_cast<int32_t*>(ws + W.iflag);
+    c.slot_map = reinterpret_cast<int32_t*>(ws + W.smap);
+    dim3 grid;
+    st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
+    if (st != KDA_OK) return st;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kda::kda_ckpt_kernel, grid, dim3(kda::kCarryThreads), 0, stream, c);
+    st = finish_launch();
+    if (st != KDA_OK) return st;
+  }
   kda::BwdParams p{};
   p.plan = plan_dev;
   p.L = plan->layout;
@@ -415,8 +447,16 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.dh0 = d_initial_state;
   p.ckpt = reinterpret_cast<float*>(ws + W.ckpt);
   p.upbuf = reinterpret_cast<float*>(ws + W.up);
-  // E_r, then D_r = the reverse scan of (A^T, E), then every fragment
+  p.ck32 = reinterpret_cast<const float*>(ws + W.ck32);
+  p.dcot = reinterpret_cast<float*>(ws + W.dcot);
+  p.tcache = reinterpret_cast<const uint16_t*>(ws + W.tcache);
+  p.iflag = reinterpret_cast<const int32_t*>(ws + W.iflag);
+  p.smap = reinterpret_cast<int32_t*>(ws + W.smap);
+  // E_r: the chunked chain over each carried segment's first fragment, then
+  // the token-by-token summaries of the flagged ones
   (void)hipGetLastError();
+  hipLaunchKernelGGL(kda::kda_bwd_chain_e_kernel, dim3(static_cast<uint32_t>(seg_blocks)),
+                     dim3(kda::kChainThreads), 0, stream, p);
   // many (piece, head) items: small workgroups, several per CU; few: large
   // ones, each item's chain shorter
   if (seg_blocks >= 1024) {
@@ -428,6 +468,7 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   }
   st = finish_launch();
   if (st != KDA_OK) return st;
+  // D_r = the reverse scan of (A^T, E)
   kda::ComposeParams c = scan_params(plan, plan_dev, H, head_begin, head_count);
   c.S = plan->P;
   c.live_off = plan->layout.seg_transition_live;
@@ -436,12 +477,18 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   c.carry = dcarry;
   st = launch_scan(kda::kda_compose_reverse_kernel, c, 1, kda::kComposeColumnBlocks, stream);
   if (st != KDA_OK) return st;
+  // the token-by-token path for the flagged fragments (the others' workgroups
+  // skip them)
   const int64_t grid = items < kda::kBwdGrid ? items : kda::kBwdGrid;
   hipLaunchKernelGGL(kda::kda_backward_forward_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),
                      0, stream, p);
-  st = finish_launch();
-  if (st != KDA_OK) return st;
   hipLaunchKernelGGL(kda::kda_backward_fragment_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kda::kBwdThreads),
                      0, stream, p);
+  // the chunked path: every fragment's cotangent chain, then every chunk's
+  // gradients
+  hipLaunchKernelGGL(kda::kda_bwd_chain_kernel, dim3(static_cast<uint32_t>(items)), dim3(kda::kChainThreads), 0,
+                     stream, p);
+  hipLaunchKernelGGL(kda::kda_bwd_grad_kernel, dim3(static_cast<uint32_t>(slots * head_count)),
+                     dim3(kda::kGradThreads), 0, stream, p);
   return finish_launch();
 }

@@ -734,10 +734,14 @@ __device__ __forceinline__ void backward_summary(const BwdParams& p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = ER * grp;
   const int voff = 4 * (ER * BD * grp + c);   // row r0 + i at + 512 i
+  // the chunked launch took every segment except the carried ones whose
+  // first fragment is on this path
+  if (p.plan[p.L.seg_carry_in + r] == 0) return;
+  if (p.iflag[static_cast<size_t>(p.plan[p.L.seg_frag_ptr + r]) * p.hn + (h - p.h0)] == 0) return;
   float ds[ER];
 #pragma unroll
   for (int i = 0; i < ER; ++i) ds[i] = 0.f;
-  if (p.plan[p.L.seg_carry_in + r] != 0) {
+  {
     const int f = p.plan[p.L.seg_frag_ptr + r];
     const int32_t flags = p.plan[p.L.frag_flags + f];
     const int32_t seq = p.plan[p.L.frag_seq + f];
@@ -815,10 +819,12 @@ __global__ void __launch_bounds__(kBwdSummaryThreads) kda_backward_summary_narro
 // addressing, and the group prefetch (shared by the two fragment launches).
 struct Item {
   int32_t flags, seg, seq, beg, len, ng, nch, top, h;
+  bool chunked;   // on the chunked path (not this one)
   float* ck;   // checkpoint of chunk j at ck + j H MAT
   __device__ Item(const BwdParams& p, const int item) {
     const int f = p.plan[p.L.frag_order + item / p.hn];
     h = p.h0 + item % p.hn;
+    chunked = p.iflag[static_cast<size_t>(f) * p.hn + item % p.hn] == 0;
     flags = p.plan[p.L.frag_flags + f];
     seg = p.plan[p.L.frag_seg + f];
     seq = p.plan[p.L.frag_seq + f];
@@ -864,6 +870,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_forward_kernel(Bw
   const size_t up_token = static_cast<size_t>(p.H) * 2 * BD;   // floats between tokens
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const Item it(p, item);
+    if (it.chunked) continue;
     auto ctokens = [&](const int j) { return min(CK, it.len - CK * j); };
     float run[NR];
     {
@@ -923,6 +930,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) kda_backward_fragment_kernel(B
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const Item it(p, item);
+    if (it.chunked) continue;
     const int h = it.h;
     // Chunk j's k and e^g rows (threads 0-511 k, 512-1023 g: token
     // (tid / 32) % 16, four values each) and its tokens' u and p (64 threads

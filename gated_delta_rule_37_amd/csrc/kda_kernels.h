@@ -16,6 +16,8 @@ constexpr int kCarryThreads = 768;    // kda_carry_kernel (carry launch): 12 wav
 constexpr int kComposeThreads = 1024;  // kda_compose_kernel workgroup size: 16 waves
 constexpr int kComposeColumns = 16;      // state columns per compose workgroup
 constexpr int kComposeColumnBlocks = 128 / kComposeColumns;
+constexpr int kChainThreads = 768;     // kda_bwd_chain_kernel: 12 waves
+constexpr int kGradThreads = 1024;     // kda_bwd_grad_kernel: 16 waves
 
 struct ChunkParams {
   const int32_t* plan;   // device copy of the plan blob
@@ -38,6 +40,13 @@ struct ChunkParams {
   const float* carry;
   const float* init_state;  // per-sequence initial states [N, H, K, V], or null (zero)
   uint16_t* chunk_cache;  // T diag(beta) per chunk of the fragments that end a segment
+  // checkpoint launch (the chunked backward): the state entering every chunk,
+  // rows scaled by the chunk's anchor, at slot floor(begin / 32) + f + chunk;
+  // and per (fragment, head) item 1 where the fragment left the anchored
+  // form's range (its checkpoints are not valid), else 0
+  float* ckpt;
+  int32_t* item_flag;
+  int32_t* slot_map;   // per chunk slot: the fragment whose chunk it holds, -1 where none
 };
 
 // Chunk cache: slot of chunk `it` of the fragment that ends segment r and
@@ -93,6 +102,15 @@ struct BwdParams {
   float* dh0;             // dL/dh0 [N, H, K, V] or null (not wanted)
   float* ckpt;            // state checkpoints: slot floor(begin/16) + f + j per head
   float* upbuf;           // u and p of every token [T, H, 2, V] (the fragment launch's level 1)
+  // chunked path, per chunk slot floor(begin/32) + f + c and head: the
+  // anchored state entering the chunk, the anchored cotangent of the state
+  // leaving it, T diag(beta); per (fragment, head) the path flag (1: the
+  // token-by-token path), per slot its fragment (-1: none)
+  const float* ck32;
+  float* dcot;
+  const uint16_t* tcache;
+  const int32_t* iflag;
+  int32_t* smap;
 };
 
 __global__ void kda_chunk_kernel(ChunkParams p);
@@ -101,6 +119,10 @@ __global__ void kda_backward_summary_narrow_kernel(BwdParams p);  // kBwdSummary
 __global__ void kda_backward_forward_kernel(BwdParams p);         // kBwdThreads threads
 __global__ void kda_backward_fragment_kernel(BwdParams p);        // kBwdThreads threads
 __global__ void kda_carry_kernel(ChunkParams p);
+__global__ void kda_ckpt_kernel(ChunkParams p);   // kCarryThreads threads
+__global__ void kda_bwd_chain_e_kernel(BwdParams p);   // kChainThreads threads, one per (piece, head)
+__global__ void kda_bwd_chain_kernel(BwdParams p);     // kChainThreads threads, one per (fragment, head)
+__global__ void kda_bwd_grad_kernel(BwdParams p);      // kGradThreads threads, one per (chunk slot, head)
 __global__ void kda_compose_kernel(ComposeParams p);
 __global__ void kda_compose_reverse_kernel(ComposeParams p);
 __global__ void kda_fold_pieces_kernel(ComposeParams p);

@@ -105,8 +105,23 @@ BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
   o += (static_cast<size_t>(plan->T / kBwdCheckpointTokens) + static_cast<size_t>(plan->F)) * H * mat;
   L.up = o;
   o += static_cast<size_t>(plan->T) * H * 2 * 128 * sizeof(float);
+  const size_t slots = backward_chunk_slots(plan);
+  L.ck32 = o;
+  o += slots * H * mat;
+  L.dcot = o;
+  o += slots * H * mat;
+  L.tcache = o;
+  o += slots * H * kChunkCacheBytes;
+  L.iflag = o;
+  o += aligned(static_cast<size_t>(plan->F) * H * sizeof(int32_t));
+  L.smap = o;
+  o += aligned(slots * sizeof(int32_t));
   L.total = o;
   return L;
+}
+
+size_t backward_chunk_slots(const kda_plan* plan) {
+  return (static_cast<size_t>(plan->T) + 31) / 32 + static_cast<size_t>(plan->F);
 }
 
 size_t backward_workspace_need(const kda_plan* plan, int32_t H) { return backward_layout(plan, H).total; }

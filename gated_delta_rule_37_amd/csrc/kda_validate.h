@@ -25,10 +25,17 @@ size_t workspace_need(const kda_plan* plan, int32_t H);
 // updates and carry-ins recomputed, the backward summaries E and their
 // reverse compose D (each P x H states, per piece), the state checkpoints
 // ((floor(T/16) + F) x H states) and every token's u and p
-// (T x H x 2 x 128 floats).
+// (T x H x 2 x 128 floats) of the token-by-token path; for the chunked path
+// the anchored states and cotangents of every 32-token chunk
+// ((ceil(T/32) + F) x H states each), every chunk's T diag(beta)
+// ((ceil(T/32) + F) x H x 4 KB), the fragments' path flags (F x H int32) and
+// the chunk-slot-to-fragment map (ceil(T/32) + F int32).
 struct BwdLayout {
-  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, up, total;
+  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, up, ck32, dcot, tcache, iflag, smap, total;
 };
+// Chunk slots of the chunked backward: chunk c of fragment f at
+// floor(begin_f / 32) + f + c, below ceil(T / 32) + F.
+size_t backward_chunk_slots(const kda_plan* plan);
 BwdLayout backward_layout(const kda_plan* plan, int32_t H);
 size_t backward_workspace_need(const kda_plan* plan, int32_t H);
 

@@ -293,12 +293,18 @@ def test_backward_validates_before_launch():
                 ws=L.kda_backward_workspace_bytes(plan.handle, H, 128, 128))
     # the forward's chunk cache (256-byte aligned), five S x H state arrays
     # (transitions, updates, carry-ins, backward summaries and their compose),
-    # (floor(T/16) + F) x H checkpoints, every token's u and p (1 KiB per
-    # token and head)
+    # (floor(T/16) + F) x H checkpoints and every token's u and p (1 KiB per
+    # token and head) for the token-by-token path; for the chunked path, per
+    # chunk slot (ceil(T/32) + F of them) and head an anchored state, an
+    # anchored cotangent and a 4 KiB T diag(beta), then F x H path flags and
+    # the slot map (int32, each 256-byte aligned)
     S, F = 2, plan.F
     cache = ((T + 31) // 32 + S) * H * 4096
     cache = (cache + 255) // 256 * 256
-    assert need["ws"] == cache + 5 * S * H * 65536 + (T // 16 + F) * H * 65536 + T * H * 1024
+    slots = (T + 31) // 32 + F
+    al = lambda x: (x + 255) // 256 * 256
+    assert need["ws"] == (cache + 5 * S * H * 65536 + (T // 16 + F) * H * 65536 + T * H * 1024
+                          + 2 * slots * H * 65536 + slots * H * 4096 + al(F * H * 4) + al(slots * 4))
     order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "dq", "dk", "dv", "dg", "dbeta",
              "dh0", "ws")
 
