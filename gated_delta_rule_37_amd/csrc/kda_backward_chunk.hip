@@ -330,15 +330,10 @@ __device__ __forceinline__ void put_fac(ChainSmem& sm, const int b, const int ob
   if (lane == 0) sm.fsplit[b][ob] = sp ? 1 : 0;
 }
 
-__device__ __forceinline__ void rescale4(f32x16 (&D)[4], const ChainSmem& sm, const int b, const int lh) {
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 f = ld4(&sm.fac[b][32 * dt + 8 * r + 4 * lh]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) D[dt][4 * r + e] *= f[e];
-    }
+// The power-of-two part of fac, on the rare chunks where some channel has it
+// (rows 32dt .. 32dt+31 are builder dt's channels, so its flag covers tile
+// dt); the normal part is applied separately.  The two factors commute.
+__device__ __forceinline__ void rescale_exp4(f32x16 (&D)[4], const ChainSmem& sm, const int b, const int lh) {
   const u32x4 fl = *reinterpret_cast<const u32x4*>(&sm.fsplit[b][0]);
   if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
 #pragma unroll
@@ -364,13 +359,17 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) Dl[dt] = zero16();
   // the cotangent at the fragment's end (row 32dt + 8r + 4lh + e, column col)
+  const int voff = 4 * (4 * lh * VD + col);
   auto add_end = [&](const float* src) {
+    const auto rs = res(src, MATF * 4);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Dl[dt][4 * r + e] += src[(32 * dt + 8 * r + 4 * lh + e) * VD + col];
+        for (int e = 0; e < 4; ++e)
+          Dl[dt][4 * r + e] += __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 4 * (32 * dt + 8 * r + e) * VD, 0));
   };
   if (end1 != nullptr) add_end(end1);
   if (end2 != nullptr) add_end(end2);
@@ -382,28 +381,36 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
   for (int m = 0; m < nc; ++m) {
     const int b = m & 1;
     const int c = nc - 1 - m;
-    // ---- step 2m+2
-    rescale4(Dl, sm, b, lh);
-    if (!E) {
-      const auto rs = res(p.dcot + (static_cast<size_t>(ck0 + c) * H + h) * MATF, MATF * 4);
-      const int voff = 4 * (4 * lh * VD + col);
+    // ---- step 2m+2: per 32-row tile, D = fac o Delta (stored), then its
+    // two k-steps of Kc D
+    rescale_exp4(Dl, sm, b, lh);
+    const auto rsd = res(p.dcot + (static_cast<size_t>(ck0 + c) * H + h) * MATF, MATF * 4);
+    f32x16 Y = zero16();
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 fv = ld4(&sm.fac[b][32 * dt + 8 * r + 4 * lh]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Dl[dt][4 * r + e] *= fv[e];
+      }
+      if (!E) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Dl[dt][4 * r + e]), rs, voff,
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Dl[dt][4 * r + e]), rsd, voff,
                                                   4 * (32 * dt + 8 * r + e) * VD, 0);
-    }
-    f32x16 Y = zero16();
+      }
 #pragma unroll
-    for (int kk = 0; kk < KD / 16; ++kk) {
-      float xv[8];
-      tile_kslots(Dl[kk >> 1], kk & 1, xv);
-      bf16x8 bh, bl;
-      split8(xv, bh, bl);
-      Y = mfma3(rowfrag(sm.kc_h[b], kk, pro), rowfrag(sm.kc_l[b], kk, pro), bh, bl, Y);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kk = 2 * dt + s2;
+        float xv[8];
+        tile_kslots(Dl[dt], s2, xv);
+        bf16x8 bh, bl;
+        split8(xv, bh, bl);
+        Y = mfma3(rowfrag(sm.kc_h[b], kk, pro), rowfrag(sm.kc_l[b], kk, pro), bh, bl, Y);
+      }
     }
     bf16x8 doh[2], dol[2];
 #pragma unroll
@@ -439,14 +446,25 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
     __syncthreads();
   }
   // the start of the fragment: dS = e^{a_0} o Delta_0
-  rescale4(Dl, sm, nc & 1, lh);
+  rescale_exp4(Dl, sm, nc & 1, lh);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 fv = ld4(&sm.fac[nc & 1][32 * dt + 8 * r + 4 * lh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Dl[dt][4 * r + e] *= fv[e];
+    }
   if (out != nullptr) {
+    const auto rs = res(out, MATF * 4);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[(32 * dt + 8 * r + 4 * lh + e) * VD + col] = Dl[dt][4 * r + e];
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Dl[dt][4 * r + e]), rs, voff,
+                                                4 * (32 * dt + 8 * r + e) * VD, 0);
   }
 }
 
@@ -565,42 +583,61 @@ __device__ __forceinline__ void chain_run(const BwdParams& p, const int f, const
 
 // ===========================================================================
 // Pass 3: one chunk's gradients from its R_c and D_c.  Sixteen waves in
-// phases, each ending with a barrier:
-//   0  waves 0-3 build Kr, Kc, Qr, dO and G - a; beta
-//   1  waves 0-3: W = Kr R and Kc D for value block w;  wave 4: A';  wave 5: P^T
-//   2  waves 0, 1: the diagonal blocks of T;  then waves 0-3: T and T^T
-//   3  waves 0-3 (value block w): U^T = X^T T^T -> U plane, dU = Kc D + P^T dO,
-//      dX = T^T dU, dX^T -> dX plane, dv, rowsum(dX o (V - W))
-//   4  wave 0: dP;  wave 1: dA, dA', dbeta
-//   5  waves 0-3 (channel block w): dq, dk, dg
+// phases, each ending with a barrier.  The state fragments each phase
+// multiplies are loaded a phase ahead, by waves that have nothing else to
+// do, so that their latency overlaps the phase before:
+//   0  waves 8-11 build Kr, Kc, Qr, dO and G - a; beta.  Waves 0-3 load the
+//      column fragments of R (value block w), waves 4-7 those of D.
+//   1  waves 0-3: W = Kr R;  waves 4-7: Kc D;  wave 8: A';  wave 9: P^T
+//   2  waves 8, 9: the diagonal blocks of T;  then waves 8-11: T and T^T
+//   3  waves 0-3: U^T = X^T T^T -> U plane;  waves 4-7: dU = Kc D + P^T dO,
+//      dX = T^T dU and dX^T -> dX plane, dv
+//   4  waves 0-3: rowsum(dX o (V - W)), and the row fragments of R (channel
+//      block w);  waves 4-7: those of D;  wave 8: dP;  wave 9: dA, dA';
+//      waves 12-15: rowsum(D o R)
+//   5  waves 0-3 (channel block w): dO R^T + dP Kc, -dR R^T + dA' Kc;
+//      waves 4-7: U D^T + dP^T Qr + dA'^T Kr, through LDS to waves 0-3;
+//      wave 12: dbeta
+//   6  waves 0-3: dq, dk, dg
 // ===========================================================================
+constexpr int XWS = 33;   // row stride (fp32) of the phase-5 exchange tiles
+
 struct alignas(16) GradSmem {
   bf16 kr_h[CH * NB], kr_l[CH * NB];
   bf16 kc_h[CH * NB], kc_l[CH * NB];
   bf16 qr_h[CH * NB], qr_l[CH * NB];
   bf16 do_h[CH * NB], do_l[CH * NB];
   bf16 u_h[CH * NB], u_l[CH * NB];
+  bf16 dx_h[CH * NB], dx_l[CH * NB];
+  // 32 x 32 matrices, columns in k-slot order: T[i][kpos(j)], T^T, P^T
+  // (phases 1-3), then dP, dP^T, dA', dA'^T (phases 4-5)
   union {
     struct {
-      bf16 h[CH * NB], l[CH * NB];   // dX, token-major
-    } dx;
+      bf16 t_h[CH * TB], t_l[CH * TB], tt_h[CH * TB], tt_l[CH * TB], pt_h[CH * TB], pt_l[CH * TB];
+    } a;
     struct {
+      bf16 dp_h[CH * TB], dp_l[CH * TB], dpt_h[CH * TB], dpt_l[CH * TB];
+      bf16 da_h[CH * TB], da_l[CH * TB], dat_h[CH * TB], dat_l[CH * TB];
+    } b;
+  } m;
+  // A' and the solve scratch (phases 1-4), then the exchange (phase 5)
+  union {
+    struct {
+      float ap[CH * AS];    // A' (strictly lower)
       float t00[16 * FS];   // t00[c][i] = T00[i][c]
       float t11[16 * FS];   // t11[c][i] = T11[i][c]
       float xm[16 * FS];    // xm[c][i] = (A10 T00)[i][c]
-    } sv;
-  };
-  bf16 t_h[CH * TB], t_l[CH * TB];       // T[i][kpos(j)]
-  bf16 tt_h[CH * TB], tt_l[CH * TB];     // T^T[j][kpos(i)]
-  bf16 pt_h[CH * TB], pt_l[CH * TB];     // P^T[j][kpos(i)]
-  bf16 dp_h[CH * TB], dp_l[CH * TB];     // dP[i][kpos(j)]
-  bf16 dpt_h[CH * TB], dpt_l[CH * TB];   // dP^T[j][kpos(i)]
-  bf16 da_h[CH * TB], da_l[CH * TB];     // dA'[i][kpos(j)]
-  bf16 dat_h[CH * TB], dat_l[CH * TB];   // dA'^T[j][kpos(i)]
-  float ap[CH * AS];                     // A' (strictly lower)
+    } s;
+    struct {
+      float xw[4][CH * XWS];   // (dk_i + dk_h)[token][channel] per channel block
+      float kh[4][CH];         // colsum(k o dk_h) per channel block
+    } x;
+  } e;
   float gl[CH * GS];                     // G - a (log2 units)
   float beta[CH];
   float red[4][CH];                      // rowsum(dX o (V - W)) per value block
+  float red2[CH];                        // rowsum(dA o A')
+  float rs[KD];                          // rowsum(D o R)
 };
 
 // Rows 8r + 4(l/32) + e (r, e = 0..3) of a [tokens][H][128] FP32 tensor at
@@ -618,6 +655,461 @@ __device__ __forceinline__ void store_rows(float* base, const int H, const int n
                                             0);
 }
 
+// Column fragments of a state (value column col, all 128 channels in the
+// k-slot order of the eight k-steps): x[8kk + j] = S[16kk + 4(l/32) + j'][col],
+// j' = j (j < 4) or 8 + j - 4.
+__device__ __forceinline__ void load_colfrags(const float* S, const int col, const int lane, float (&x)[64]) {
+  const auto rs = res(S, MATF * 4);
+  const int voff = 4 * (4 * (lane >> 5) * VD + col);
+#pragma unroll
+  for (int kk = 0; kk < KD / 16; ++kk)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[8 * kk + j] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 4 * (16 * kk + (j < 4 ? j : 8 + j - 4)) * VD, 0));
+}
+// Row fragments of a state (channel row, all 128 values in k-slot order):
+// x[8ks + j] = S[row][16ks + 4(l/32) + j'].
+__device__ __forceinline__ void load_rowfrags(const float* S, const int row, const int lane, float (&x)[64]) {
+  const auto rs = res(S, MATF * 4);
+  const int roff = 4 * (row * VD + 4 * (lane >> 5));
+#pragma unroll
+  for (int ks = 0; ks < VD / 16; ++ks) {
+    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, roff, 64 * ks, 0));
+    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, roff, 64 * ks + 32, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * ks + e] = a[e];
+      x[8 * ks + 4 + e] = b[e];
+    }
+  }
+}
+// acc += A B over the 128 channels (or values) with A's rows from a
+// token-major plane pair and B from eight k-steps of fragments in registers.
+__device__ __forceinline__ f32x16 prod_frags(const bf16* ah, const bf16* al, const float (&x)[64], const int pro,
+                                             f32x16 acc) {
+#pragma unroll
+  for (int kk = 0; kk < KD / 16; ++kk) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = x[8 * kk + j];
+    bf16x8 bh, bl;
+    split8<true>(v, bh, bl);
+    acc = mfma3(rowfrag(ah, kk, pro), rowfrag(al, kk, pro), bh, bl, acc);
+  }
+  return acc;
+}
+// The tile rows (tokens 8r + 4(l/32) + e, k-slot order of k-steps 0, 1) of
+// column c0 + l % 32 of a split token-major plane, as FP32.
+__device__ __forceinline__ void plane_col(const bf16* ph, const bf16* pl, const int c0, const int trb, float (&x)[16]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const bf16x8 h = colfrag(ph, s, c0, trb);
+    const bf16x8 l = colfrag(pl, s, c0, trb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[8 * s + j] = static_cast<float>(h[j]) + static_cast<float>(l[j]);
+  }
+}
+
+// One chunk of the gradient launch: its fields, shared by the wave roles.
+struct GradCtx {
+  int H, h, c0, n, lane, lh, wave, w4, pro, trb, tbo;
+  uint32_t rowb;   // one token of a bf16 [T, H, 128] tensor
+  const float* Rg;
+  const float* Dg;
+};
+
+// Waves 0-3 (w = value block in phases 0-4, channel block in 5-6).
+__device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+  const int lane = x.lane, lh = x.lh, w = x.w4;
+  float fr[64], vv[16];
+  const int colv = 32 * w + (lane & 31);
+  // ---- phase 0: R's column fragments and V at the W tile's rows
+  load_colfrags(x.Rg, colv, lane, fr);
+  {
+    const auto rv = res(p.v + (static_cast<size_t>(x.c0) * x.H + x.h) * VD, (x.n - 1) * x.rowb + VD * 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[4 * r + e] = __uint_as_float(
+            static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(
+                rv, static_cast<int>(4 * lh * x.rowb + 2 * colv), static_cast<int>((8 * r + e) * x.rowb), 0)))
+            << 16);
+  }
+  __syncthreads();
+  // ---- phase 1: W = Kr R
+  f32x16 W = prod_frags(sm.kr_h, sm.kr_l, fr, x.pro, zero16());
+  __syncthreads();
+  __syncthreads();   // phase 2: the solve
+  __syncthreads();
+  // ---- phase 3: V - W, X = diag(beta)(V - W), U^T = X^T T^T -> U plane
+  mfma_result_fence(W);
+  f32x16 X;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      W[4 * r + e] = vv[4 * r + e] - W[4 * r + e];
+      X[4 * r + e] = sm.beta[8 * r + 4 * lh + e] * W[4 * r + e];
+    }
+  {
+    bf16x8 xh[2], xl[2];
+    tile_kslots_split(X, xh, xl);
+    f32x16 UT = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      UT = mfma3(xh[s], xl[s], smallrow(sm.m.a.t_h, s, x.tbo), smallrow(sm.m.a.t_l, s, x.tbo), UT);
+    mfma_result_fence(UT);
+    store_plane_t(UT, sm.u_h, sm.u_l, 32 * w, lane);
+  }
+  __syncthreads();
+  // ---- phase 4: rowsum(dX o (V - W)) over value block w (dX read back from
+  // its plane); R's row fragments for channel block w
+  {
+    float dxv[16];
+    plane_col(sm.dx_h, sm.dx_l, 32 * w, x.trb, dxv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float s32 = sum32(dxv[4 * r + e] * W[4 * r + e]);
+        if ((lane & 31) == 0) sm.red[w][8 * r + 4 * lh + e] = s32;
+      }
+  }
+  load_rowfrags(x.Rg, 32 * w + (lane & 31), lane, fr);
+  __syncthreads();
+  // ---- phase 5: dO R^T + dP Kc and -dR R^T + dA' Kc for channel block w
+  f32x16 vq = prod_frags(sm.do_h, sm.do_l, fr, x.pro, zero16());
+  f32x16 vd = prod_frags(sm.dx_h, sm.dx_l, fr, x.pro, zero16());
+  mfma_result_fence(vd);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vd[4 * r + e] *= -sm.beta[8 * r + 4 * lh + e];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const bf16x8 kch = colfrag(sm.kc_h, s, 32 * w, x.trb), kcl = colfrag(sm.kc_l, s, 32 * w, x.trb);
+    vq = mfma3(smallrow(sm.m.b.dp_h, s, x.tbo), smallrow(sm.m.b.dp_l, s, x.tbo), kch, kcl, vq);
+    vd = mfma3(smallrow(sm.m.b.da_h, s, x.tbo), smallrow(sm.m.b.da_l, s, x.tbo), kch, kcl, vd);
+  }
+  mfma_result_fence(vq);
+  mfma_result_fence(vd);
+  __syncthreads();
+  // ---- phase 6: dq, dk, dg
+  const int col = 32 * w + (lane & 31);
+  float kr[16], qr[16];
+  plane_col(sm.kr_h, sm.kr_l, 32 * w, x.trb, kr);
+  plane_col(sm.qr_h, sm.qr_l, 32 * w, x.trb, qr);
+  f32x16 dk, dG;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 8 * r + 4 * lh + e;
+      const int q = 4 * r + e;
+      const float xg = sm.gl[i * GS + col];
+      const float ega = __builtin_amdgcn_exp2f(xg);
+      const float eag = __builtin_amdgcn_exp2f(-xg);
+      vq[q] *= ega;
+      vd[q] *= ega;
+      const float w1 = sm.e.x.xw[w][i * XWS + (lane & 31)];
+      dk[q] = vd[q] + w1;
+      // q = Qr e^{a-G}, k = Kr e^{a-G}
+      dG[q] = qr[q] * eag * vq[q] + kr[q] * eag * (vd[q] - w1);
+    }
+  // the chunk-end term, on token 31 (lane half 1, register 15)
+  if (lh == 1) dG[15] += sm.e.x.kh[w][lane & 31] + sm.rs[col];
+  // dg_t = sum of dG over tokens t .. 31 of the chunk (dG is the gradient of
+  // the prefix G in natural units: every factor above is a product)
+  float gs[4], ps[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gs[r] = (dG[4 * r] + dG[4 * r + 1]) + (dG[4 * r + 2] + dG[4 * r + 3]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ps[r] = __shfl_xor(gs[r], 32);
+  f32x16 dg;
+  float after = 0.f;   // sum of the groups after group (r, lh)
+#pragma unroll
+  for (int r = 3; r >= 0; --r) {
+    float run = after + (lh == 0 ? ps[r] : 0.f);
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      run += dG[4 * r + e];
+      dg[4 * r + e] = run;
+    }
+    after += gs[r] + ps[r];
+  }
+  const size_t ob = (static_cast<size_t>(x.c0) * x.H + x.h) * KD;
+  store_rows(p.dq + ob, x.H, x.n, col, lane, vq);
+  store_rows(p.dk + ob, x.H, x.n, col, lane, dk);
+  store_rows(p.dg + ob, x.H, x.n, col, lane, dg);
+}
+
+// Waves 4-7 (w = value block in phases 0-3, channel block in 4-5).
+__device__ __forceinline__ void grad_role_b(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+  const int lane = x.lane, lh = x.lh, w = x.w4;
+  float fr[64];
+  // ---- phase 0: D's column fragments
+  load_colfrags(x.Dg, 32 * w + (lane & 31), lane, fr);
+  __syncthreads();
+  // ---- phase 1: Kc D
+  f32x16 Y = prod_frags(sm.kc_h, sm.kc_l, fr, x.pro, zero16());
+  __syncthreads();
+  __syncthreads();   // phase 2: the solve
+  __syncthreads();
+  // ---- phase 3: dU = Kc D + P^T dO, dX = T^T dU, dX^T = dU^T T -> dX plane, dv
+  {
+    const int col = 32 * w + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      Y = mfma3(smallrow(sm.m.a.pt_h, s, x.tbo), smallrow(sm.m.a.pt_l, s, x.tbo), colfrag(sm.do_h, s, 32 * w, x.trb),
+                colfrag(sm.do_l, s, 32 * w, x.trb), Y);
+    mfma_result_fence(Y);
+    bf16x8 uh[2], ul[2];
+    tile_kslots_split(Y, uh, ul);
+    f32x16 dX = zero16(), dXT = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      dX = mfma3(smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), uh[s], ul[s], dX);
+      dXT = mfma3(uh[s], ul[s], smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), dXT);
+    }
+    mfma_result_fence(dX);
+    mfma_result_fence(dXT);
+    store_plane_t(dXT, sm.dx_h, sm.dx_l, 32 * w, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dX[4 * r + e] *= sm.beta[8 * r + 4 * lh + e];
+    store_rows(p.dv + (static_cast<size_t>(x.c0) * x.H + x.h) * VD, x.H, x.n, col, lane, dX);
+  }
+  __syncthreads();
+  // ---- phase 4: D's row fragments for channel block w
+  load_rowfrags(x.Dg, 32 * w + (lane & 31), lane, fr);
+  __syncthreads();
+  // ---- phase 5: (U D^T + dP^T Qr + dA'^T Kr) e^{a-G} to the exchange, with
+  // colsum(k o U D^T e^{a-G})
+  const int col = 32 * w + (lane & 31);
+  f32x16 Dkh = prod_frags(sm.u_h, sm.u_l, fr, x.pro, zero16());
+  f32x16 Dki = zero16();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    Dki = mfma3(smallrow(sm.m.b.dpt_h, s, x.tbo), smallrow(sm.m.b.dpt_l, s, x.tbo), colfrag(sm.qr_h, s, 32 * w, x.trb),
+                colfrag(sm.qr_l, s, 32 * w, x.trb), Dki);
+    Dki = mfma3(smallrow(sm.m.b.dat_h, s, x.tbo), smallrow(sm.m.b.dat_l, s, x.tbo), colfrag(sm.kr_h, s, 32 * w, x.trb),
+                colfrag(sm.kr_l, s, 32 * w, x.trb), Dki);
+  }
+  float kr[16];
+  plane_col(sm.kr_h, sm.kr_l, 32 * w, x.trb, kr);
+  mfma_result_fence(Dkh);
+  mfma_result_fence(Dki);
+  float ks = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 8 * r + 4 * lh + e;
+      const float eag = __builtin_amdgcn_exp2f(-sm.gl[i * GS + col]);
+      const float vh = Dkh[4 * r + e] * eag;
+      sm.e.x.xw[w][i * XWS + (lane & 31)] = vh + Dki[4 * r + e] * eag;
+      ks = fmaf(kr[4 * r + e] * eag, vh, ks);   // k = Kr e^{a-G}
+    }
+  ks += __shfl_xor(ks, 32);
+  if (lh == 0) sm.e.x.kh[w][lane & 31] = ks;
+  __syncthreads();
+}
+
+// Waves 8-11: the operands, A', P^T, the solve for T, dP and dA.
+__device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+  const int lane = x.lane, lh = x.lh, wave = x.wave, w = x.w4;
+  // ---- phase 0: Kr, Kc, Qr, dO planes and G - a; beta
+  {
+    ChunkIn in;
+    fetch_chunk(p, x.h, x.c0, x.n, w, lane, in);
+    if (wave == 8 && lane < CH) {
+      const auto rb = res(p.beta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 2 + 2);
+      sm.beta[lane] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(
+                          __builtin_amdgcn_raw_buffer_load_b16(rb, lane * x.H * 2, 0, 0)))
+                      << 16);
+    }
+    float a[8], gc[8];
+    build_chunk(in, Planes{sm.kr_h, sm.kr_l, sm.kc_h, sm.kc_l, sm.qr_h, sm.qr_l, sm.do_h, sm.do_l}, sm.gl, w, lane,
+                a, gc);
+  }
+  __syncthreads();
+  // ---- phase 1: A' = Kr Kc^T (strictly lower, FP32) or P = Qr Kc^T -> P^T
+  if (wave == 8 || wave == 9) {
+    f32x16 acc = zero16();
+    const bf16* xh = wave == 8 ? sm.kr_h : sm.qr_h;
+    const bf16* xl = wave == 8 ? sm.kr_l : sm.qr_l;
+#pragma unroll
+    for (int kk = 0; kk < KD / 16; ++kk)
+      acc = mfma3(rowfrag(xh, kk, x.pro), rowfrag(xl, kk, x.pro), rowfrag(sm.kc_h, kk, x.pro),
+                  rowfrag(sm.kc_l, kk, x.pro), acc);
+    mfma_result_fence(acc);
+    const int j = lane & 31;
+    if (wave == 8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * r + 4 * lh + e;
+          sm.e.s.ap[i * AS + j] = j < i ? acc[4 * r + e] : 0.f;
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
+      store_t(acc, sm.m.a.pt_h, sm.m.a.pt_l, lane);
+    }
+  }
+  __syncthreads();
+  // ---- phase 2: T = (I + diag(beta) A')^-1 by 16 x 16 blocks; column c of
+  // diagonal block wave - 8 by forward substitution
+  if (wave == 8 || wave == 9) {
+    const int cc = lane & 15;
+    const int o = 16 * (wave - 8);
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xs[i] = (i == cc) ? 1.f : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 15; ++jj)
+#pragma unroll
+      for (int i = jj + 1; i < 16; ++i) xs[i] -= sm.beta[o + i] * sm.e.s.ap[(o + i) * AS + o + jj] * xs[jj];
+    float* dst = wave == 8 ? sm.e.s.t00 : sm.e.s.t11;
+    if (lane < 16) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        st4(&dst[cc * FS + 4 * q4], f32x4{xs[4 * q4], xs[4 * q4 + 1], xs[4 * q4 + 2], xs[4 * q4 + 3]});
+    }
+  }
+  __syncthreads();
+  {
+    // X = A10 T00 (column tc), then T10 = -T11 X; T and T^T as split bf16
+    const int ti = lane & 15;
+    const int tc = 4 * w + (lane >> 4);
+    float xsum = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) xsum += sm.e.s.ap[(16 + ti) * AS + mm] * sm.e.s.t00[tc * FS + mm];
+    xsum *= sm.beta[16 + ti];
+    sm.e.s.xm[tc * FS + ti] = xsum;
+    wave_lds_order();
+    float t10 = 0.f;
+#pragma unroll
+    for (int kq = 0; kq < 16; ++kq) t10 -= sm.e.s.t11[kq * FS + ti] * sm.e.s.xm[tc * FS + kq];
+    const float t00 = sm.e.s.t00[tc * FS + ti];
+    const float t11 = sm.e.s.t11[tc * FS + ti];
+    const int pc = kpos(tc);
+    const int pi = kpos(ti);
+    bf16* th = sm.m.a.t_h;
+    bf16* tl = sm.m.a.t_l;
+    bf16* uh = sm.m.a.tt_h;
+    bf16* ul = sm.m.a.tt_l;
+    bf16 hh, ll;
+    const bf16 z = static_cast<bf16>(0.f);
+    split(t00, hh, ll);
+    th[ti * TB + pc] = hh;
+    tl[ti * TB + pc] = ll;
+    uh[tc * TB + pi] = hh;
+    ul[tc * TB + pi] = ll;
+    split(t11, hh, ll);
+    th[(16 + ti) * TB + 16 + pc] = hh;
+    tl[(16 + ti) * TB + 16 + pc] = ll;
+    uh[(16 + tc) * TB + 16 + pi] = hh;
+    ul[(16 + tc) * TB + 16 + pi] = ll;
+    split(t10, hh, ll);
+    th[(16 + ti) * TB + pc] = hh;
+    tl[(16 + ti) * TB + pc] = ll;
+    uh[tc * TB + 16 + pi] = hh;
+    ul[tc * TB + 16 + pi] = ll;
+    th[ti * TB + 16 + pc] = z;
+    tl[ti * TB + 16 + pc] = z;
+    uh[(16 + tc) * TB + pi] = z;
+    ul[(16 + tc) * TB + pi] = z;
+  }
+  __syncthreads();
+  __syncthreads();   // phase 3
+  // ---- phase 4: dP = lower_incl(dO U^T);  dA = strict_lower(-dX U^T),
+  // rowsum(dA o A'), dA' = diag(beta) dA
+  if (wave == 8 || wave == 9) {
+    f32x16 acc = zero16();
+    const bf16* xh = wave == 8 ? sm.do_h : sm.dx_h;
+    const bf16* xl = wave == 8 ? sm.do_l : sm.dx_l;
+#pragma unroll
+    for (int kk = 0; kk < VD / 16; ++kk)
+      acc = mfma3(rowfrag(xh, kk, x.pro), rowfrag(xl, kk, x.pro), rowfrag(sm.u_h, kk, x.pro), rowfrag(sm.u_l, kk, x.pro),
+                  acc);
+    mfma_result_fence(acc);
+    const int j = lane & 31;
+    if (wave == 8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
+      store_n(acc, sm.m.b.dp_h, sm.m.b.dp_l, lane);
+      store_t(acc, sm.m.b.dpt_h, sm.m.b.dpt_l, lane);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * r + 4 * lh + e;
+          const float da = j < i ? -acc[4 * r + e] : 0.f;
+          const float s32 = sum32(da * sm.e.s.ap[i * AS + j]);
+          if (j == 0) sm.red2[i] = s32;
+          acc[4 * r + e] = sm.beta[i] * da;
+        }
+      store_n(acc, sm.m.b.da_h, sm.m.b.da_l, lane);
+      store_t(acc, sm.m.b.dat_h, sm.m.b.dat_l, lane);
+    }
+  }
+  __syncthreads();
+  __syncthreads();   // phase 5
+}
+
+// Waves 12-15: rowsum(D o R) (phase 4), dbeta (phase 5).
+__device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+  const int lane = x.lane, lh = x.lh, w = x.w4;
+  for (int i = 0; i < 5; ++i) __syncthreads();   // phases 0-3
+  {
+    // channels of block w: row 32w + l % 32, the lane's half of the values,
+    // in two passes of 32
+    const int row = 32 * w + (lane & 31);
+    const auto rr = res(x.Rg, MATF * 4);
+    const auto rd = res(x.Dg, MATF * 4);
+    const int roff = 4 * (row * VD + 4 * lh);
+    float s = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 a[8], b[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = 256 * half + 64 * q;
+        a[2 * q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff, o, 0));
+        a[2 * q + 1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff, o + 32, 0));
+        b[2 * q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, roff, o, 0));
+        b[2 * q + 1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, roff, o + 32, 0));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(a[q][e], b[q][e], s);
+    }
+    s += __shfl_xor(s, 32);
+    if (lh == 0) sm.rs[row] = s;
+  }
+  __syncthreads();
+  // ---- phase 5: dbeta
+  if (x.wave == 12 && lane < CH) {
+    const float db = sm.red2[lane] + ((sm.red[0][lane] + sm.red[1][lane]) + (sm.red[2][lane] + sm.red[3][lane]));
+    const auto rb = res(p.dbeta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 4 + 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(db), rb, lane * x.H * 4, 0, 0);
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ void grad_chunk(const BwdParams& p) {
   __shared__ GradSmem sm;
   const int hn = p.hn;
@@ -626,386 +1118,28 @@ __device__ __forceinline__ void grad_chunk(const BwdParams& p) {
   const int f = p.smap[slot];
   if (f < 0) return;
   if (p.iflag[static_cast<size_t>(f) * hn + hi] != 0) return;
-  const int H = p.H;
-  const int h = p.h0 + hi;
+  GradCtx x;
+  x.H = p.H;
+  x.h = p.h0 + hi;
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
-  const int c = static_cast<int>(slot - (beg / CH + f));
-  const int c0 = beg + CH * c;
-  const int n = min(CH, end - c0);
-  const float* Rg = p.ck32 + (static_cast<size_t>(slot) * H + h) * MATF;
-  const float* Dg = p.dcot + (static_cast<size_t>(slot) * H + h) * MATF;
+  x.c0 = beg + CH * static_cast<int>(slot - (beg / CH + f));
+  x.n = min(CH, end - x.c0);
+  x.Rg = p.ck32 + (static_cast<size_t>(slot) * x.H + x.h) * MATF;
+  x.Dg = p.dcot + (static_cast<size_t>(slot) * x.H + x.h) * MATF;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int lh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pro = (lane & 31) * NB + 4 * lh;
-  const int trb = tr_base(lane);
-  const int tbo = (lane & 31) * TB + 8 * lh;
-  const uint32_t rowb = static_cast<uint32_t>(H) * 128 * 2;   // one token of a bf16 [T, H, 128] tensor
-  const uint32_t rowf = static_cast<uint32_t>(H) * 128 * 4;
-
-  // ---- phase 0
-  if (wave < 4) {
-    ChunkIn x;
-    fetch_chunk(p, h, c0, n, wave, lane, x);
-    float a[8], gc[8];
-    build_chunk(x, Planes{sm.kr_h, sm.kr_l, sm.kc_h, sm.kc_l, sm.qr_h, sm.qr_l, sm.do_h, sm.do_l}, sm.gl, wave, lane,
-                a, gc);
-    if (wave == 0 && lane < CH) {
-      const auto rb = res(p.beta + static_cast<size_t>(c0) * H + h, (n - 1) * H * 2 + 2);
-      sm.beta[lane] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(
-                          __builtin_amdgcn_raw_buffer_load_b16(rb, lane * H * 2, 0, 0)))
-                      << 16);
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 1
-  f32x16 W = zero16(), Y = zero16();
-  float vv[16];
-  if (wave < 4) {
-    const int vb = wave;
-    const int col = 32 * vb + (lane & 31);
-    // V at the tile's rows (issued now, used in phase 3)
-    {
-      const auto rv = res(p.v + (static_cast<size_t>(c0) * H + h) * VD, (n - 1) * rowb + VD * 2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vv[4 * r + e] = __uint_as_float(
-              static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(
-                  rv, static_cast<int>(4 * lh * rowb + 2 * col), static_cast<int>((8 * r + e) * rowb), 0)))
-              << 16);
-    }
-    const auto rr = res(Rg, MATF * 4);
-    const auto rd = res(Dg, MATF * 4);
-    const int voff = 4 * (4 * lh * VD + col);
-#pragma unroll 2
-    for (int kk = 0; kk < KD / 16; ++kk) {
-      float xr[8], xd[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int chn = 16 * kk + (j < 4 ? j : 8 + j - 4);
-        xr[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, voff, 4 * chn * VD, 0));
-        xd[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, voff, 4 * chn * VD, 0));
-      }
-      bf16x8 rh, rl, dh, dl;
-      split8<true>(xr, rh, rl);
-      split8<true>(xd, dh, dl);
-      W = mfma3(rowfrag(sm.kr_h, kk, pro), rowfrag(sm.kr_l, kk, pro), rh, rl, W);
-      Y = mfma3(rowfrag(sm.kc_h, kk, pro), rowfrag(sm.kc_l, kk, pro), dh, dl, Y);
-    }
-  } else if (wave == 4 || wave == 5) {
-    // A' = Kr Kc^T (strictly lower, FP32) or P = Qr Kc^T -> P^T
-    f32x16 acc = zero16();
-    const bf16* xh = wave == 4 ? sm.kr_h : sm.qr_h;
-    const bf16* xl = wave == 4 ? sm.kr_l : sm.qr_l;
-#pragma unroll
-    for (int kk = 0; kk < KD / 16; ++kk)
-      acc = mfma3(rowfrag(xh, kk, pro), rowfrag(xl, kk, pro), rowfrag(sm.kc_h, kk, pro), rowfrag(sm.kc_l, kk, pro),
-                  acc);
-    mfma_result_fence(acc);
-    const int j = lane & 31;
-    if (wave == 4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * r + 4 * lh + e;
-          sm.ap[i * AS + j] = j < i ? acc[4 * r + e] : 0.f;
-        }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
-      store_t(acc, sm.pt_h, sm.pt_l, lane);
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: T = (I + diag(beta) A')^-1 by 16 x 16 blocks
-  if (wave < 2) {
-    // column c of the diagonal block wave: forward substitution
-    const int cc = lane & 15;
-    const int o = 16 * wave;
-    float xs[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xs[i] = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 15; ++jj)
-#pragma unroll
-      for (int i = jj + 1; i < 16; ++i) xs[i] -= sm.beta[o + i] * sm.ap[(o + i) * AS + o + jj] * xs[jj];
-    float* dst = wave == 0 ? sm.sv.t00 : sm.sv.t11;
-    if (lane < 16) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        st4(&dst[cc * FS + 4 * q4], f32x4{xs[4 * q4], xs[4 * q4 + 1], xs[4 * q4 + 2], xs[4 * q4 + 3]});
-    }
-  }
-  __syncthreads();
-  if (wave < 4) {
-    const int ti = lane & 15;
-    const int tc = 4 * wave + (lane >> 4);
-    // X = A10 T00 (column tc), then T10 = -T11 X
-    float xsum = 0.f;
-#pragma unroll
-    for (int mm = 0; mm < 16; ++mm) xsum += sm.ap[(16 + ti) * AS + mm] * sm.sv.t00[tc * FS + mm];
-    xsum *= sm.beta[16 + ti];
-    sm.sv.xm[tc * FS + ti] = xsum;
-    wave_lds_order();
-    float t10 = 0.f;
-#pragma unroll
-    for (int kq = 0; kq < 16; ++kq) t10 -= sm.sv.t11[kq * FS + ti] * sm.sv.xm[tc * FS + kq];
-    const float t00 = sm.sv.t00[tc * FS + ti];
-    const float t11 = sm.sv.t11[tc * FS + ti];
-    const int pc = kpos(tc);
-    const int pi = kpos(ti);
-    bf16 hh, ll;
-    const bf16 z = static_cast<bf16>(0.f);
-    split(t00, hh, ll);
-    sm.t_h[ti * TB + pc] = hh;
-    sm.t_l[ti * TB + pc] = ll;
-    sm.tt_h[tc * TB + pi] = hh;
-    sm.tt_l[tc * TB + pi] = ll;
-    split(t11, hh, ll);
-    sm.t_h[(16 + ti) * TB + 16 + pc] = hh;
-    sm.t_l[(16 + ti) * TB + 16 + pc] = ll;
-    sm.tt_h[(16 + tc) * TB + 16 + pi] = hh;
-    sm.tt_l[(16 + tc) * TB + 16 + pi] = ll;
-    split(t10, hh, ll);
-    sm.t_h[(16 + ti) * TB + pc] = hh;
-    sm.t_l[(16 + ti) * TB + pc] = ll;
-    sm.tt_h[tc * TB + 16 + pi] = hh;
-    sm.tt_l[tc * TB + 16 + pi] = ll;
-    sm.t_h[ti * TB + 16 + pc] = z;
-    sm.t_l[ti * TB + 16 + pc] = z;
-    sm.tt_h[(16 + tc) * TB + pi] = z;
-    sm.tt_l[(16 + tc) * TB + pi] = z;
-  }
-  __syncthreads();
-
-  // ---- phase 3 (value block vb = wave)
-  if (wave < 4) {
-    const int vb = wave;
-    const int col = 32 * vb + (lane & 31);
-    mfma_result_fence(W);
-    mfma_result_fence(Y);
-    f32x16 Rv, X;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * r + 4 * lh + e;
-        Rv[4 * r + e] = vv[4 * r + e] - W[4 * r + e];
-        X[4 * r + e] = sm.beta[i] * Rv[4 * r + e];
-      }
-    // U^T = X^T T^T (rows: values, columns: tokens)
-    bf16x8 xh[2], xl[2];
-    tile_kslots_split(X, xh, xl);
-    f32x16 UT = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) UT = mfma3(xh[s], xl[s], smallrow(sm.t_h, s, tbo), smallrow(sm.t_l, s, tbo), UT);
-    // dU = Kc D + P^T dO
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      Y = mfma3(smallrow(sm.pt_h, s, tbo), smallrow(sm.pt_l, s, tbo), colfrag(sm.do_h, s, 32 * vb, trb),
-                colfrag(sm.do_l, s, 32 * vb, trb), Y);
-    mfma_result_fence(UT);
-    store_plane_t(UT, sm.u_h, sm.u_l, 32 * vb, lane);
-    mfma_result_fence(Y);
-    bf16x8 uh[2], ul[2];
-    tile_kslots_split(Y, uh, ul);
-    // dX = T^T dU (rows: tokens) and dX^T = dU^T T (rows: values)
-    f32x16 dX = zero16(), dXT = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      dX = mfma3(smallrow(sm.tt_h, s, tbo), smallrow(sm.tt_l, s, tbo), uh[s], ul[s], dX);
-      dXT = mfma3(uh[s], ul[s], smallrow(sm.tt_h, s, tbo), smallrow(sm.tt_l, s, tbo), dXT);
-    }
-    mfma_result_fence(dX);
-    mfma_result_fence(dXT);
-    store_plane_t(dXT, sm.dx.h, sm.dx.l, 32 * vb, lane);
-    f32x16 dv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * r + 4 * lh + e;
-        dv[4 * r + e] = sm.beta[i] * dX[4 * r + e];
-        const float s32 = sum32(dX[4 * r + e] * Rv[4 * r + e]);
-        if ((lane & 31) == 0) sm.red[vb][i] = s32;
-      }
-    store_rows(p.dv + (static_cast<size_t>(c0) * H + h) * VD, H, n, col, lane, dv);
-  }
-  __syncthreads();
-
-  // ---- phase 4
-  if (wave < 2) {
-    f32x16 acc = zero16();
-    const bf16* xh = wave == 0 ? sm.do_h : sm.dx.h;
-    const bf16* xl = wave == 0 ? sm.do_l : sm.dx.l;
-#pragma unroll
-    for (int kk = 0; kk < VD / 16; ++kk)
-      acc = mfma3(rowfrag(xh, kk, pro), rowfrag(xl, kk, pro), rowfrag(sm.u_h, kk, pro), rowfrag(sm.u_l, kk, pro), acc);
-    mfma_result_fence(acc);
-    const int j = lane & 31;
-    if (wave == 0) {
-      // dP = lower_incl(dO U^T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
-      store_n(acc, sm.dp_h, sm.dp_l, lane);
-      store_t(acc, sm.dpt_h, sm.dpt_l, lane);
-    } else {
-      // dA = strict_lower(-dX U^T); dbeta; dA' = diag(beta) dA
-      float db[16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * r + 4 * lh + e;
-          const float da = j < i ? -acc[4 * r + e] : 0.f;
-          db[4 * r + e] = sum32(da * sm.ap[i * AS + j]);
-          acc[4 * r + e] = sm.beta[i] * da;
-        }
-      if ((lane & 31) == 0) {
-        const auto rb = res(p.dbeta + static_cast<size_t>(c0) * H + h, (n - 1) * H * 4 + 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * r + 4 * lh + e;
-            const float tot = db[4 * r + e] + ((sm.red[0][i] + sm.red[1][i]) + (sm.red[2][i] + sm.red[3][i]));
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(tot), rb, i * H * 4, 0, 0);
-          }
-      }
-      store_n(acc, sm.da_h, sm.da_l, lane);
-      store_t(acc, sm.dat_h, sm.dat_l, lane);
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 5 (channel block ct = wave)
-  if (wave < 4) {
-    const int ct = wave;
-    const int col = 32 * ct + (lane & 31);
-    // k and q at the tile's rows, for dG
-    float kq[16], qq[16];
-    {
-      const size_t b0 = (static_cast<size_t>(c0) * H + h) * KD;
-      const auto rk = res(p.k + b0, (n - 1) * rowb + KD * 2);
-      const auto rq = res(p.q + b0, (n - 1) * rowb + KD * 2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int vo = static_cast<int>(4 * lh * rowb + 2 * col);
-          const int so = static_cast<int>((8 * r + e) * rowb);
-          kq[4 * r + e] = __uint_as_float(
-              static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rk, vo, so, 0))) << 16);
-          qq[4 * r + e] = __uint_as_float(
-              static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rq, vo, so, 0))) << 16);
-        }
-    }
-    f32x16 Zq = zero16(), Dkd = zero16(), Dki = zero16(), Dkh = zero16();
-    float rs = 0.f;   // this lane's half of rowsum(D o R) for channel col
-    const auto rr = res(Rg, MATF * 4);
-    const auto rd = res(Dg, MATF * 4);
-    const int roff = 4 * (col * VD + 4 * lh);
-#pragma unroll 2
-    for (int ks = 0; ks < VD / 16; ++ks) {
-      const f32x4 r0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff, 64 * ks, 0));
-      const f32x4 r1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff, 64 * ks + 32, 0));
-      const f32x4 d0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, roff, 64 * ks, 0));
-      const f32x4 d1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, roff, 64 * ks + 32, 0));
-      float xr[8], xd[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xr[e] = r0[e];
-        xr[4 + e] = r1[e];
-        xd[e] = d0[e];
-        xd[4 + e] = d1[e];
-        rs = fmaf(r0[e], d0[e], rs);
-        rs = fmaf(r1[e], d1[e], rs);
-      }
-      bf16x8 rh, rl, dh, dl;
-      split8<true>(xr, rh, rl);
-      split8<true>(xd, dh, dl);
-      Zq = mfma3(rowfrag(sm.do_h, ks, pro), rowfrag(sm.do_l, ks, pro), rh, rl, Zq);
-      Dkd = mfma3(rowfrag(sm.dx.h, ks, pro), rowfrag(sm.dx.l, ks, pro), rh, rl, Dkd);
-      Dkh = mfma3(rowfrag(sm.u_h, ks, pro), rowfrag(sm.u_l, ks, pro), dh, dl, Dkh);
-    }
-    mfma_result_fence(Dkd);
-    // -dR R^T = -diag(beta) (dX R^T)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Dkd[4 * r + e] *= -sm.beta[8 * r + 4 * lh + e];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 kch = colfrag(sm.kc_h, s, 32 * ct, trb), kcl = colfrag(sm.kc_l, s, 32 * ct, trb);
-      Zq = mfma3(smallrow(sm.dp_h, s, tbo), smallrow(sm.dp_l, s, tbo), kch, kcl, Zq);
-      Dkd = mfma3(smallrow(sm.da_h, s, tbo), smallrow(sm.da_l, s, tbo), kch, kcl, Dkd);
-      Dki = mfma3(smallrow(sm.dpt_h, s, tbo), smallrow(sm.dpt_l, s, tbo), colfrag(sm.qr_h, s, 32 * ct, trb),
-                  colfrag(sm.qr_l, s, 32 * ct, trb), Dki);
-      Dki = mfma3(smallrow(sm.dat_h, s, tbo), smallrow(sm.dat_l, s, tbo), colfrag(sm.kr_h, s, 32 * ct, trb),
-                  colfrag(sm.kr_l, s, 32 * ct, trb), Dki);
-    }
-    mfma_result_fence(Zq, Dkd, Dki, Dkh);
-    f32x16 dq, dk, dG;
-    float ksum = 0.f;   // colsum(k o dk_h) over this lane's tokens
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * r + 4 * lh + e;
-        const float xg = sm.gl[i * GS + col];
-        const float ega = __builtin_amdgcn_exp2f(xg);
-        const float eag = __builtin_amdgcn_exp2f(-xg);
-        const int q = 4 * r + e;
-        const float vq = Zq[q] * ega;
-        const float vd = Dkd[q] * ega;
-        const float vi = Dki[q] * eag;
-        const float vh = Dkh[q] * eag;
-        dq[q] = vq;
-        dk[q] = vd + vi + vh;
-        dG[q] = qq[q] * vq + kq[q] * (vd - vi - vh);
-        ksum = fmaf(kq[q], vh, ksum);
-      }
-    // the chunk-end term, on token 31 (lane half 1, register 15)
-    const float tot = (ksum + rs) + __shfl_xor(ksum + rs, 32);
-    if (lh == 1) dG[15] += tot;
-    // dg_t = sum of dG over tokens t .. 31 of the chunk (dG is the gradient
-    // of the prefix G in natural units: every factor above is a product)
-    float gs[4], ps[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) gs[r] = (dG[4 * r] + dG[4 * r + 1]) + (dG[4 * r + 2] + dG[4 * r + 3]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ps[r] = __shfl_xor(gs[r], 32);
-    f32x16 dg;
-    float after = 0.f;   // sum of the groups after group (r, lh)
-#pragma unroll
-    for (int r = 3; r >= 0; --r) {
-      const float own_after = after + (lh == 0 ? ps[r] : 0.f);
-      float run = own_after;
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        run += dG[4 * r + e];
-        dg[4 * r + e] = run;
-      }
-      after += gs[r] + ps[r];
-    }
-    const size_t ob = (static_cast<size_t>(c0) * H + h) * KD;
-    store_rows(p.dq + ob, H, n, col, lane, dq);
-    store_rows(p.dk + ob, H, n, col, lane, dk);
-    store_rows(p.dg + ob, H, n, col, lane, dg);
-  }
+  x.lane = tid & 63;
+  x.lh = x.lane >> 5;
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  x.w4 = x.wave & 3;
+  x.pro = (x.lane & 31) * NB + 4 * x.lh;
+  x.trb = tr_base(x.lane);
+  x.tbo = (x.lane & 31) * TB + 8 * x.lh;
+  x.rowb = static_cast<uint32_t>(x.H) * 128 * 2;
+  if (x.wave < 4) grad_role_a(p, sm, x);
+  else if (x.wave < 8) grad_role_b(p, sm, x);
+  else if (x.wave < 12) grad_role_c(p, sm, x);
+  else grad_role_d(p, sm, x);
 }
 
 }  // namespace

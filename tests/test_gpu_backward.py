@@ -82,6 +82,42 @@ def test_backward_parity(name, T, H, cu, S, gs, with_h0):
         assert e <= GRAD_RTOL, (key, e)
 
 
+def test_backward_mixed_paths():
+    """One call in which some (fragment, head) items leave the anchored chunk
+    form's range and take the token-by-token kernels while the others take
+    the chunked ones: head 1's gates over sequence 1 (tokens 100..229) are
+    eight times the pages' scale, so its two fragments there (one starting
+    its sequence, one carried into the next segment, whose backward summary
+    E_r then comes from the token-by-token launch) are flagged, while head 0
+    and every other fragment stay chunked.  Both heads are checked against
+    the oracle, with initial states and d_final."""
+    T, H, cu, S = 300, 2, [0, 100, 230, 300], 3
+    x = synth.make_inputs(T, H, 128, 128, seed=71, cu_seqlens=cu, gate_scale=1.0)
+    strong = synth.make_inputs(T, H, 128, 128, seed=72, cu_seqlens=cu, gate_scale=8.0)
+    x["g"][100:230, 1] = strong["g"][100:230, 1]
+    N = len(cu) - 1
+    gen = torch.Generator().manual_seed(73)
+    d_o = torch.randn(T, H, 128, generator=gen)
+    d_final = torch.randn(N, H, 128, 128, generator=gen)
+    h0 = synth.initial_states(N, H, 128, 128, seed=74)
+    plan = kda.Plan(cu, S)
+    d = pu.to_device(x)
+    got = kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o.cuda(), d_final=d_final.cuda(),
+                       initial_state=h0.cuda(), want_dh0=True)
+    torch.cuda.synchronize()
+    f = pu.oracle_inputs(x)
+    ref = ko.backward(f["q"], f["k"], f["v"], f["g"], f["beta"], cu, d_o.double().numpy(),
+                      dfinal=d_final.double().numpy(), h0=h0.double().numpy())
+    for key, want in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), ref):
+        have = got[key].double().cpu().numpy()
+        assert np.isfinite(have).all(), key
+        for h in range(H):
+            scale = np.abs(want[:, h]).max()
+            err = np.abs(have[:, h] - want[:, h]).max()
+            print(f"[mixed paths] {key} head {h}: {err / scale:.2e}", flush=True)
+            assert err <= GRAD_RTOL * scale, (key, h, err / scale)
+
+
 def test_backward_deterministic():
     T, H, cu = 150, 2, [0, 60, 150]
     x = synth.make_inputs(T, H, 128, 128, seed=31, cu_seqlens=cu)
