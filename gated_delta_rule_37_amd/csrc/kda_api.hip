@@ -414,6 +414,7 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
     c.ckpt = reinterpret_cast<float*>(ws + W.ck32);
     c.item_flag = reinterpret_cast<int32_t*>(ws + W.iflag);
     c.slot_map = reinterpret_cast<int32_t*>(ws + W.smap);
+    c.rv_out = reinterpret_cast<float*>(ws + W.rv);
     dim3 grid;
     st = chunk_grid(plan->F, head_count, kda::kCarryThreads, &grid);
     if (st != KDA_OK) return st;
@@ -452,6 +453,8 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.tcache = reinterpret_cast<const uint16_t*>(ws + W.tcache);
   p.iflag = reinterpret_cast<const int32_t*>(ws + W.iflag);
   p.smap = reinterpret_cast<int32_t*>(ws + W.smap);
+  p.rvbuf = reinterpret_cast<const float*>(ws + W.rv);
+  p.dubuf = reinterpret_cast<float*>(ws + W.du);
   // E_r: the chunked chain over each carried segment's first fragment, then
   // the token-by-token summaries of the flagged ones
   (void)hipGetLastError();

@@ -19,8 +19,8 @@
 //                                        fragment's end e^{Gc - a} o dS_end)
 //     dU  = P^T dO + Kc D_c,  dR = (T diag(beta))^T dU
 //     Delta_c = D_c + Qr^T dO - Kr^T dR,   dS_start = e^{a_0} o Delta_0
-// and stores every D_c.  Pass 3 (kda_bwd_grad_kernel) takes every chunk on
-// its own from R_c and D_c:
+// and stores every D_c and dU.  Pass 3 (kda_bwd_grad_kernel) takes every
+// chunk on its own from R_c, D_c, dU and the checkpoint launch's V - Kr R_c:
 //     W = Kr R,  X = diag(beta)(V - W),  U = T X,  dU = P^T dO + Kc D
 //     dX = T^T dU,  dv = dR = diag(beta) dX,  dA = strict_lower(-dX U^T)
 //     dbeta = rowsum(dX o (V - W)) + rowsum(dA o A'),  dA' = diag(beta) dA
@@ -148,13 +148,6 @@ __device__ __forceinline__ f32x4 tile16c(const bf16* xh, const bf16* xl, const b
   }
   mfma_result_fence(acc);
   return acc;
-}
-
-// The sum of x over the 32 lanes that share l / 32.
-__device__ __forceinline__ float sum32(float x) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 32);
-  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -422,6 +415,15 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
     __syncthreads();
     // ---- step 2m+3
     mfma_result_fence(Y);
+    if (!E) {
+      // dU for the gradient launch, [token][V]
+      const auto rsu = res(p.dubuf + (static_cast<size_t>(ck0 + c) * H + h) * CH * VD, CH * VD * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Y[4 * r + e]), rsu, voff, 4 * (8 * r + e) * VD, 0);
+    }
     bf16x8 uh[2], ul[2];
     tile_kslots_split(Y, uh, ul);
     f32x16 dR = zero16();
@@ -582,23 +584,26 @@ __device__ __forceinline__ void chain_run(const BwdParams& p, const int f, const
 }
 
 // ===========================================================================
-// Pass 3: one chunk's gradients from its R_c and D_c.  Sixteen waves in
-// phases, each ending with a barrier.  The state fragments each phase
-// multiplies are loaded a phase ahead, by waves that have nothing else to
-// do, so that their latency overlaps the phase before:
-//   0  waves 8-11 build Kr, Kc, Qr, dO and G - a; beta.  Waves 0-3 load the
-//      column fragments of R (value block w), waves 4-7 those of D.
-//   1  waves 0-3: W = Kr R;  waves 4-7: Kc D;  wave 8: A';  wave 9: P^T
-//   2  waves 8, 9: the diagonal blocks of T;  then waves 8-11: T and T^T
-//   3  waves 0-3: U^T = X^T T^T -> U plane;  waves 4-7: dU = Kc D + P^T dO,
-//      dX = T^T dU and dX^T -> dX plane, dv
-//   4  waves 0-3: rowsum(dX o (V - W)), and the row fragments of R (channel
-//      block w);  waves 4-7: those of D;  wave 8: dP;  wave 9: dA, dA';
-//      waves 12-15: rowsum(D o R)
-//   5  waves 0-3 (channel block w): dO R^T + dP Kc, -dR R^T + dA' Kc;
-//      waves 4-7: U D^T + dP^T Qr + dA'^T Kr, through LDS to waves 0-3;
-//      wave 12: dbeta
-//   6  waves 0-3: dq, dk, dg
+// Pass 3: one chunk's gradients from R_c and D_c (their row fragments), the
+// checkpoint launch's V - Kr R_c and the chain launch's dU.  Sixteen waves in
+// four roles, each running its own sequence of the same seven barriers (no
+// role's registers stay live in another's branch):
+//   phase  waves 0-3           waves 4-7           waves 8-11          waves 12-15
+//   0                                              Kr, Kc, Qr, dO       V - W and dU
+//                                                  planes, G - a, beta  (value block w)
+//   1      R's row fragments   D's row fragments   A' (8), P^T (9)
+//          (channel block w)   (channel block w)
+//   2                                              T and T^T
+//   3                                                                   U^T -> U plane,
+//                                                                       dX, dX^T -> dX
+//                                                                       plane, dv
+//   4                                              dP (8); dA, dA' (9)  rowsum(dX o (V-W))
+//   5      dO R^T + dP Kc,     U D^T + dP^T Qr                          rowsum(D o R),
+//          -dR R^T + dA' Kc    + dA'^T Kr -> LDS                        dbeta (12)
+//   6      dq, dk, dg
+// The row fragments (the only large reads) are issued after phase 0, so the
+// inputs the operand build waits on go first and the fragments have four
+// phases to arrive.
 // ===========================================================================
 constexpr int XWS = 33;   // row stride (fp32) of the phase-5 exchange tiles
 
@@ -713,72 +718,21 @@ __device__ __forceinline__ void plane_col(const bf16* ph, const bf16* pl, const 
 
 // One chunk of the gradient launch: its fields, shared by the wave roles.
 struct GradCtx {
+  int64_t slot;
   int H, h, c0, n, lane, lh, wave, w4, pro, trb, tbo;
   uint32_t rowb;   // one token of a bf16 [T, H, 128] tensor
   const float* Rg;
   const float* Dg;
 };
 
-// Waves 0-3 (w = value block in phases 0-4, channel block in 5-6).
+// Waves 0-3 (channel block w).
 __device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
-  float fr[64], vv[16];
-  const int colv = 32 * w + (lane & 31);
-  // ---- phase 0: R's column fragments and V at the W tile's rows
-  load_colfrags(x.Rg, colv, lane, fr);
-  {
-    const auto rv = res(p.v + (static_cast<size_t>(x.c0) * x.H + x.h) * VD, (x.n - 1) * x.rowb + VD * 2);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vv[4 * r + e] = __uint_as_float(
-            static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(
-                rv, static_cast<int>(4 * lh * x.rowb + 2 * colv), static_cast<int>((8 * r + e) * x.rowb), 0)))
-            << 16);
-  }
-  __syncthreads();
-  // ---- phase 1: W = Kr R
-  f32x16 W = prod_frags(sm.kr_h, sm.kr_l, fr, x.pro, zero16());
-  __syncthreads();
-  __syncthreads();   // phase 2: the solve
-  __syncthreads();
-  // ---- phase 3: V - W, X = diag(beta)(V - W), U^T = X^T T^T -> U plane
-  mfma_result_fence(W);
-  f32x16 X;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      W[4 * r + e] = vv[4 * r + e] - W[4 * r + e];
-      X[4 * r + e] = sm.beta[8 * r + 4 * lh + e] * W[4 * r + e];
-    }
-  {
-    bf16x8 xh[2], xl[2];
-    tile_kslots_split(X, xh, xl);
-    f32x16 UT = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      UT = mfma3(xh[s], xl[s], smallrow(sm.m.a.t_h, s, x.tbo), smallrow(sm.m.a.t_l, s, x.tbo), UT);
-    mfma_result_fence(UT);
-    store_plane_t(UT, sm.u_h, sm.u_l, 32 * w, lane);
-  }
-  __syncthreads();
-  // ---- phase 4: rowsum(dX o (V - W)) over value block w (dX read back from
-  // its plane); R's row fragments for channel block w
-  {
-    float dxv[16];
-    plane_col(sm.dx_h, sm.dx_l, 32 * w, x.trb, dxv);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float s32 = sum32(dxv[4 * r + e] * W[4 * r + e]);
-        if ((lane & 31) == 0) sm.red[w][8 * r + 4 * lh + e] = s32;
-      }
-  }
+  float fr[64];
+  __syncthreads();   // phase 0
+  // ---- phases 1-4 (five barriers): R's row fragments, in flight until phase 5
   load_rowfrags(x.Rg, 32 * w + (lane & 31), lane, fr);
-  __syncthreads();
+  for (int i = 0; i < 5; ++i) __syncthreads();
   // ---- phase 5: dO R^T + dP Kc and -dR R^T + dA' Kc for channel block w
   f32x16 vq = prod_frags(sm.do_h, sm.do_l, fr, x.pro, zero16());
   f32x16 vd = prod_frags(sm.dx_h, sm.dx_l, fr, x.pro, zero16());
@@ -845,47 +799,14 @@ __device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, co
   store_rows(p.dg + ob, x.H, x.n, col, lane, dg);
 }
 
-// Waves 4-7 (w = value block in phases 0-3, channel block in 4-5).
+// Waves 4-7 (channel block w).
 __device__ __forceinline__ void grad_role_b(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
   float fr[64];
-  // ---- phase 0: D's column fragments
-  load_colfrags(x.Dg, 32 * w + (lane & 31), lane, fr);
-  __syncthreads();
-  // ---- phase 1: Kc D
-  f32x16 Y = prod_frags(sm.kc_h, sm.kc_l, fr, x.pro, zero16());
-  __syncthreads();
-  __syncthreads();   // phase 2: the solve
-  __syncthreads();
-  // ---- phase 3: dU = Kc D + P^T dO, dX = T^T dU, dX^T = dU^T T -> dX plane, dv
-  {
-    const int col = 32 * w + (lane & 31);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      Y = mfma3(smallrow(sm.m.a.pt_h, s, x.tbo), smallrow(sm.m.a.pt_l, s, x.tbo), colfrag(sm.do_h, s, 32 * w, x.trb),
-                colfrag(sm.do_l, s, 32 * w, x.trb), Y);
-    mfma_result_fence(Y);
-    bf16x8 uh[2], ul[2];
-    tile_kslots_split(Y, uh, ul);
-    f32x16 dX = zero16(), dXT = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      dX = mfma3(smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), uh[s], ul[s], dX);
-      dXT = mfma3(uh[s], ul[s], smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), dXT);
-    }
-    mfma_result_fence(dX);
-    mfma_result_fence(dXT);
-    store_plane_t(dXT, sm.dx_h, sm.dx_l, 32 * w, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dX[4 * r + e] *= sm.beta[8 * r + 4 * lh + e];
-    store_rows(p.dv + (static_cast<size_t>(x.c0) * x.H + x.h) * VD, x.H, x.n, col, lane, dX);
-  }
-  __syncthreads();
-  // ---- phase 4: D's row fragments for channel block w
+  __syncthreads();   // phase 0
+  // ---- phases 1-4 (five barriers): D's row fragments, in flight until phase 5
   load_rowfrags(x.Dg, 32 * w + (lane & 31), lane, fr);
-  __syncthreads();
+  for (int i = 0; i < 5; ++i) __syncthreads();
   // ---- phase 5: (U D^T + dP^T Qr + dA'^T Kr) e^{a-G} to the exchange, with
   // colsum(k o U D^T e^{a-G})
   const int col = 32 * w + (lane & 31);
@@ -1030,52 +951,137 @@ __device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, co
   }
   __syncthreads();
   __syncthreads();   // phase 3
-  // ---- phase 4: dP = lower_incl(dO U^T);  dA = strict_lower(-dX U^T),
-  // rowsum(dA o A'), dA' = diag(beta) dA
+  // ---- phase 4: dP = lower_incl(dO U^T) (wave 8);  dA^T = strict_upper(-U dX^T)
+  // (rows j, columns i: token i's sums over j stay in its lane and its
+  // partner's), rowsum(dA o A'), dA' = diag(beta) dA (wave 9)
   if (wave == 8 || wave == 9) {
     f32x16 acc = zero16();
-    const bf16* xh = wave == 8 ? sm.do_h : sm.dx_h;
-    const bf16* xl = wave == 8 ? sm.do_l : sm.dx_l;
+    const bf16* ah = wave == 8 ? sm.do_h : sm.u_h;
+    const bf16* al = wave == 8 ? sm.do_l : sm.u_l;
+    const bf16* bh = wave == 8 ? sm.u_h : sm.dx_h;
+    const bf16* bl = wave == 8 ? sm.u_l : sm.dx_l;
 #pragma unroll
     for (int kk = 0; kk < VD / 16; ++kk)
-      acc = mfma3(rowfrag(xh, kk, x.pro), rowfrag(xl, kk, x.pro), rowfrag(sm.u_h, kk, x.pro), rowfrag(sm.u_l, kk, x.pro),
-                  acc);
+      acc = mfma3(rowfrag(ah, kk, x.pro), rowfrag(al, kk, x.pro), rowfrag(bh, kk, x.pro), rowfrag(bl, kk, x.pro), acc);
     mfma_result_fence(acc);
-    const int j = lane & 31;
+    const int cl = lane & 31;
     if (wave == 8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
+          if (cl > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
       store_n(acc, sm.m.b.dp_h, sm.m.b.dp_l, lane);
       store_t(acc, sm.m.b.dpt_h, sm.m.b.dpt_l, lane);
     } else {
+      // acc[j][i] = (U dX^T)[j][i] = (dX U^T)[i][j]; this lane's column is i
+      const int i = cl;
+      const float bi = sm.beta[i];
+      float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 8 * r + 4 * lh + e;
+          const int j = 8 * r + 4 * lh + e;
           const float da = j < i ? -acc[4 * r + e] : 0.f;
-          const float s32 = sum32(da * sm.e.s.ap[i * AS + j]);
-          if (j == 0) sm.red2[i] = s32;
-          acc[4 * r + e] = sm.beta[i] * da;
+          part = fmaf(da, sm.e.s.ap[i * AS + j], part);
+          acc[4 * r + e] = bi * da;
         }
-      store_n(acc, sm.m.b.da_h, sm.m.b.da_l, lane);
-      store_t(acc, sm.m.b.dat_h, sm.m.b.dat_l, lane);
+      part += __shfl_xor(part, 32);
+      if (lh == 0) sm.red2[i] = part;
+      // acc holds dA'^T [j][i]: its rows to dat, its transpose to da
+      store_n(acc, sm.m.b.dat_h, sm.m.b.dat_l, lane);
+      store_t(acc, sm.m.b.da_h, sm.m.b.da_l, lane);
     }
   }
   __syncthreads();
   __syncthreads();   // phase 5
 }
 
-// Waves 12-15: rowsum(D o R) (phase 4), dbeta (phase 5).
+// Waves 12-15 (value block w): V - W and dU (phase 0), U^T, dX, dX^T and dv
+// (phase 3), rowsum(dX o (V - W)) (phase 4), rowsum(D o R) and dbeta
+// (phase 5).
 __device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
-  for (int i = 0; i < 5; ++i) __syncthreads();   // phases 0-3
+  const int col = 32 * w + (lane & 31);
+  // ---- phase 0: V - W and dU at the tile's rows (token 8r + 4lh + e, value
+  // col), and V - W transposed (value 32w + 8r + 4lh + e, token l % 32)
+  f32x16 rv, du, rvt;
   {
-    // channels of block w: row 32w + l % 32, the lane's half of the values,
-    // in two passes of 32
+    const auto rs1 = res(p.rvbuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
+    const auto rs2 = res(p.dubuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
+    const int voff = 4 * (4 * lh * VD + col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rv[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs1, voff, 4 * (8 * r + e) * VD, 0));
+        du[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, voff, 4 * (8 * r + e) * VD, 0));
+      }
+    const int toff = 4 * ((lane & 31) * VD + 32 * w + 4 * lh);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 v4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs1, toff, 32 * r, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rvt[4 * r + e] = v4[e];
+    }
+  }
+  __syncthreads();
+  __syncthreads();   // phase 1
+  __syncthreads();   // phase 2: the diagonal blocks of T
+  __syncthreads();   // phase 2: T and T^T
+  // ---- phase 3: X = diag(beta)(V - W), U^T = X^T T^T -> U plane;
+  // dX = T^T dU, dX^T = dU^T T -> dX plane;  dv = diag(beta) dX
+  {
+    f32x16 X;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[4 * r + e] = sm.beta[8 * r + 4 * lh + e] * rv[4 * r + e];
+    bf16x8 xh[2], xl[2];
+    tile_kslots_split(X, xh, xl);
+    f32x16 UT = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      UT = mfma3(xh[s], xl[s], smallrow(sm.m.a.t_h, s, x.tbo), smallrow(sm.m.a.t_l, s, x.tbo), UT);
+    mfma_result_fence(UT);
+    store_plane_t(UT, sm.u_h, sm.u_l, 32 * w, lane);
+  }
+  f32x16 dXT = zero16();
+  {
+    bf16x8 uh[2], ul[2];
+    tile_kslots_split(du, uh, ul);
+    f32x16 dX = zero16();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      dX = mfma3(smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), uh[s], ul[s], dX);
+      dXT = mfma3(uh[s], ul[s], smallrow(sm.m.a.tt_h, s, x.tbo), smallrow(sm.m.a.tt_l, s, x.tbo), dXT);
+    }
+    mfma_result_fence(dX);
+    mfma_result_fence(dXT);
+    store_plane_t(dXT, sm.dx_h, sm.dx_l, 32 * w, lane);
+    f32x16 dv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dv[4 * r + e] = sm.beta[8 * r + 4 * lh + e] * dX[4 * r + e];
+    store_rows(p.dv + (static_cast<size_t>(x.c0) * x.H + x.h) * VD, x.H, x.n, col, lane, dv);
+  }
+  __syncthreads();
+  // ---- phase 4: rowsum(dX o (V - W)) over value block w, from the
+  // transposed tiles (token l % 32: the lane's 16 values and its partner's)
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) part = fmaf(dXT[q], rvt[q], part);
+    part += __shfl_xor(part, 32);
+    if (lh == 0) sm.red[w][lane & 31] = part;
+  }
+  __syncthreads();
+  // ---- phase 5: rowsum(D o R) for the channels of block w (read in phase
+  // 6; row 32w + l % 32, the lane's half of the values, in two passes of 32),
+  // and dbeta
+  {
     const int row = 32 * w + (lane & 31);
     const auto rr = res(x.Rg, MATF * 4);
     const auto rd = res(x.Dg, MATF * 4);
@@ -1100,8 +1106,6 @@ __device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, co
     s += __shfl_xor(s, 32);
     if (lh == 0) sm.rs[row] = s;
   }
-  __syncthreads();
-  // ---- phase 5: dbeta
   if (x.wave == 12 && lane < CH) {
     const float db = sm.red2[lane] + ((sm.red[0][lane] + sm.red[1][lane]) + (sm.red[2][lane] + sm.red[3][lane]));
     const auto rb = res(p.dbeta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 4 + 4);
@@ -1119,6 +1123,7 @@ __device__ __forceinline__ void grad_chunk(const BwdParams& p) {
   if (f < 0) return;
   if (p.iflag[static_cast<size_t>(f) * hn + hi] != 0) return;
   GradCtx x;
+  x.slot = slot;
   x.H = p.H;
   x.h = p.h0 + hi;
   const int32_t beg = p.plan[p.L.frag_begin + f];

@@ -47,6 +47,7 @@ struct ChunkParams {
   float* ckpt;
   int32_t* item_flag;
   int32_t* slot_map;   // per chunk slot: the fragment whose chunk it holds, -1 where none
+  float* rv_out;       // per chunk slot: V - Kr R of the chunk, [32 tokens][V] FP32
 };
 
 // Chunk cache: slot of chunk `it` of the fragment that ends segment r and
@@ -111,6 +112,8 @@ struct BwdParams {
   const uint16_t* tcache;
   const int32_t* iflag;
   int32_t* smap;
+  const float* rvbuf;     // per chunk slot: V - Kr R (checkpoint launch), [32][V]
+  float* dubuf;           // per chunk slot: dU = P^T dO + Kc D (chain launch), [32][V]
 };
 
 __global__ void kda_chunk_kernel(ChunkParams p);

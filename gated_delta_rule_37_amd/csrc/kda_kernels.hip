@@ -521,6 +521,17 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 #pragma unroll
       for (int e = 0; e < 4; ++e) D[4 * r + e] = vv[e] - Y[4 * r + e];
     }
+    if (MODE == kModeCkpt) {
+      // V - Kr R of the chunk for the backward's gradient launch, [token][V]
+      const auto rsv = __builtin_amdgcn_make_buffer_rsrc(p.rv_out + (static_cast<size_t>(ck0 + n) * H + h) * CH * VD, 0,
+                                                         CH * VD * 4, kBufDword3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(D[4 * r + e]), rsv, 4 * (4 * lh * VD + col),
+                                                4 * (8 * r + e) * VD, 0);
+    }
     // D and U feed the next products as B operands in k-slot order (tokens):
     // T diag(beta) and P are stored in that column order, Kc^T is read in it
     bf16x8 dh[2], dl[2];

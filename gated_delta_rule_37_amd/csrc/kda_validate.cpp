@@ -112,6 +112,10 @@ BwdLayout backward_layout(const kda_plan* plan, int32_t H) {
   o += slots * H * mat;
   L.tcache = o;
   o += slots * H * kChunkCacheBytes;
+  L.rv = o;
+  o += slots * H * 32 * 128 * sizeof(float);
+  L.du = o;
+  o += slots * H * 32 * 128 * sizeof(float);
   L.iflag = o;
   o += aligned(static_cast<size_t>(plan->F) * H * sizeof(int32_t));
   L.smap = o;

@@ -28,10 +28,11 @@ size_t workspace_need(const kda_plan* plan, int32_t H);
 // (T x H x 2 x 128 floats) of the token-by-token path; for the chunked path
 // the anchored states and cotangents of every 32-token chunk
 // ((ceil(T/32) + F) x H states each), every chunk's T diag(beta)
-// ((ceil(T/32) + F) x H x 4 KB), the fragments' path flags (F x H int32) and
-// the chunk-slot-to-fragment map (ceil(T/32) + F int32).
+// ((ceil(T/32) + F) x H x 4 KB), every chunk's V - Kr R and dU
+// ((ceil(T/32) + F) x H x 16 KB each), the fragments' path flags (F x H
+// int32) and the chunk-slot-to-fragment map (ceil(T/32) + F int32).
 struct BwdLayout {
-  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, up, ck32, dcot, tcache, iflag, smap, total;
+  size_t cache, transitions, updates, carry, esum, dcarry, ckpt, up, ck32, dcot, tcache, rv, du, iflag, smap, total;
 };
 // Chunk slots of the chunked backward: chunk c of fragment f at
 // floor(begin_f / 32) + f + c, below ceil(T / 32) + F.

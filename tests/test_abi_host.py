@@ -296,15 +296,17 @@ def test_backward_validates_before_launch():
     # (floor(T/16) + F) x H checkpoints and every token's u and p (1 KiB per
     # token and head) for the token-by-token path; for the chunked path, per
     # chunk slot (ceil(T/32) + F of them) and head an anchored state, an
-    # anchored cotangent and a 4 KiB T diag(beta), then F x H path flags and
-    # the slot map (int32, each 256-byte aligned)
+    # anchored cotangent, a 4 KiB T diag(beta) and the chunk's V - Kr R and dU
+    # (16 KiB each), then F x H path flags and the slot map (int32, each
+    # 256-byte aligned)
     S, F = 2, plan.F
     cache = ((T + 31) // 32 + S) * H * 4096
     cache = (cache + 255) // 256 * 256
     slots = (T + 31) // 32 + F
     al = lambda x: (x + 255) // 256 * 256
     assert need["ws"] == (cache + 5 * S * H * 65536 + (T // 16 + F) * H * 65536 + T * H * 1024
-                          + 2 * slots * H * 65536 + slots * H * 4096 + al(F * H * 4) + al(slots * 4))
+                          + 2 * slots * H * 65536 + slots * H * 4096 + 2 * slots * H * 16384 + al(F * H * 4)
+                          + al(slots * 4))
     order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "dq", "dk", "dv", "dg", "dbeta",
              "dh0", "ws")
 
