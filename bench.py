@@ -481,19 +481,27 @@ def measure(args, w, x, torch, kda, synth):
     }
 
 
-# Algorithmic FP32 flops of the backward per (token, head): the forward
+# Algorithmic FP32-grade flops of the backward per (token, head): the forward
 # quantities it needs (p = S~^T k: 2KV, S_t = S~ + k u^T: 3KV) and the
 # reverse step (dS += q do^T: 2KV, du: 2KV, dq: 2KV, dk: 4KV, dS~: 2KV,
-# dg: 2KV, dS_{t-1}: KV) -- 20 K V; recomputation is not counted.
+# dg: 2KV, dS_{t-1}: KV) -- 20 K V; recomputation is not counted.  The
+# chunked backward runs them as split-bf16 products on the matrix cores,
+# charged three times against the bf16 peak as the forward's chunk kernels
+# are.
 BWD_FLOPS_PER_TOKEN_HEAD = 20 * 128 * 128
+# Algorithmic HBM bytes of the backward per (token, head): q, k, v, g (bf16),
+# beta (bf16) and d_o (FP32) in; dq, dk, dv, dg (FP32) and dbeta (FP32) out.
+BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 2 + 4 * 128 + 4 * 4 * 128 + 4
 
 
 def measure_backward(args, w, x, torch, kda):
     """Time kda_backward (the gradients of q, k, v, g, beta for a seeded
     d_o) on the same workload: one untimed call, then args.backward_steps
-    calls between events on the calling stream.  The roofline is the ALU
-    bound of the whole call (five launches; the fragment launch dominates,
-    its own duration is in the committed kernel trace)."""
+    calls between events on the calling stream.  The roofline covers the
+    whole call (every launch; the gradient launch dominates, its own
+    duration is in the committed kernel trace): the larger of the
+    algorithmic HBM bytes at 8 TB/s and the algorithmic multiply-adds as
+    split bf16 at 2.5 PFLOP/s."""
     dev = torch.device("cuda:0")
     d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
     cu = x["cu_seqlens"].tolist()
@@ -513,17 +521,31 @@ def measure_backward(args, w, x, torch, kda):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.backward_steps
-    flops = BWD_FLOPS_PER_TOKEN_HEAD * w.T * w.H
-    achieved = flops / (ms * 1e-3) / 1e12
+    th = w.T * w.H
+    flops = BWD_FLOPS_PER_TOKEN_HEAD * th          # FP32-grade
+    split = 3 * flops                              # as executed on bf16 matrix cores
+    nbytes = BWD_BYTES_PER_TOKEN_HEAD * th
+    bound_mfma = split / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    bound_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    if bound_hbm >= bound_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(bound_hbm / ms, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(split / (ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(bound_mfma / ms, 4)}
+    roof.update({
+        "scope": "whole call (every launch of kda_backward)",
+        "bounds_ms": {"mfma": round(bound_mfma, 4), "hbm": round(bound_hbm, 4)},
+        "flops_per_token_head": BWD_FLOPS_PER_TOKEN_HEAD, "bytes_per_token_head": BWD_BYTES_PER_TOKEN_HEAD,
+        "fp32grade": {"achieved": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                      "fp32_mfma_peak": PEAK_FP32_TFLOPS,
+                      "ratio_to_fp32_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+    })
     return {
         "ms_per_call": round(ms, 3),
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "calls": args.backward_steps,
-        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-                     "flops_per_token_head": BWD_FLOPS_PER_TOKEN_HEAD,
-                     "peak_without_packed_fp32": PEAK_FP32_TFLOPS / 2,
-                     "frac_without_packed_fp32": round(achieved / (PEAK_FP32_TFLOPS / 2), 4)},
+        "roofline": roof,
     }
 
 

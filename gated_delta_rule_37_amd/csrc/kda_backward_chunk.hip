@@ -17,7 +17,7 @@
 // the same anchored frame:
 //     D_c = fac_c o Delta_{c+1}         (fac_c = e^{a_{c+1} + Gc_c - a_c}; at the
 //                                        fragment's end e^{Gc - a} o dS_end)
-//     dU  = P^T dO + Kc D_c,  dR = (T diag(beta))^T dU
+//     dU  = P^T dO + Kc D_c,  dR = diag(beta) T^T dU
 //     Delta_c = D_c + Qr^T dO - Kr^T dR,   dS_start = e^{a_0} o Delta_0
 // and stores every D_c and dU.  Pass 3 (kda_bwd_grad_kernel) takes every
 // chunk on its own from R_c, D_c, dU and the checkpoint launch's V - Kr R_c:
@@ -47,7 +47,8 @@ namespace {
 constexpr int KD = 128;
 constexpr int VD = 128;
 constexpr int CH = 32;
-constexpr int NB = 136;   // row stride (bf16) of the token-major [32][128] planes
+constexpr int NB = 136;   // row stride (bf16) of the gradient launch's token-major [32][128] planes
+constexpr int NC = 152;   // the chain launch's (conflict-free transposed reads; more LDS)
 constexpr int TB = 40;    // row stride (bf16) of the 32 x 32 matrices (columns in k-slot order)
 constexpr int FS = 36;    // row stride (fp32) of the 16 x 16 solve tiles
 constexpr int AS = 33;    // row stride (fp32) of A'
@@ -63,12 +64,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t res(const void* base, const ui
 // Column fragment of a token-major plane: lane l receives column c0 + l % 32,
 // tokens 16s + 4(l/32) + 0..3 and 16s + 8 + 4(l/32) + 0..3 (the k-slot order
 // of k-step s), by two transposed reads.
+template <int S = NB>
 __device__ __forceinline__ int tr_base(const int lane) {
-  return (4 * (lane >> 5) + ((lane & 15) >> 2)) * NB + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return (4 * (lane >> 5) + ((lane & 15) >> 2)) * S + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 }
+template <int S = NB>
 __device__ __forceinline__ bf16x8 colfrag(const bf16* plane, const int s, const int c0, const int trb) {
-  const bf16* p = plane + trb + 16 * s * NB + c0;
-  return join8(lds_read_tr(p), lds_read_tr(p + 8 * NB));
+  const bf16* p = plane + trb + 16 * s * S + c0;
+  return join8(lds_read_tr(p), lds_read_tr(p + 8 * S));
 }
 // Row fragment: row l % 32, columns 16kk + 4(l/32) + 0..3 and 16kk + 8 +
 // 4(l/32) + 0..3 (the same k-slot order over the 128 channels).
@@ -134,6 +137,7 @@ __device__ __forceinline__ void store_plane_t(const f32x16& t, bf16* ph, bf16* p
 
 // 16 x 16 block (rb, ct) of X C^T over the 128 channels (16x16x32 MFMAs):
 // lane l gets rows 16rb + 4(l/16) + e, e = 0..3, of column 16ct + l % 16.
+template <int S = NB>
 __device__ __forceinline__ f32x4 tile16c(const bf16* xh, const bf16* xl, const bf16* ch, const bf16* cl, const int rb,
                                          const int ct, const int lane) {
   const int lm = lane & 15;
@@ -141,8 +145,8 @@ __device__ __forceinline__ f32x4 tile16c(const bf16* xh, const bf16* xl, const b
   f32x4 acc = zero4();
 #pragma unroll
   for (int kk = 0; kk < KD / 32; ++kk) {
-    const int ao = (16 * rb + lm) * NB + 32 * kk + 8 * lg;
-    const int bo = (16 * ct + lm) * NB + 32 * kk + 8 * lg;
+    const int ao = (16 * rb + lm) * S + 32 * kk + 8 * lg;
+    const int bo = (16 * ct + lm) * S + 32 * kk + 8 * lg;
     acc = mfma16x3(*reinterpret_cast<const bf16x8*>(xh + ao), *reinterpret_cast<const bf16x8*>(xl + ao),
                    *reinterpret_cast<const bf16x8*>(ch + bo), *reinterpret_cast<const bf16x8*>(cl + bo), acc);
   }
@@ -195,8 +199,24 @@ struct Planes {
 // eight channels in log2 units.  The in-chunk prefix runs across the 16
 // lanes of a DPP row (4 row shifts); the anchor and G_31 are the rows' last
 // lanes.
+// Kr's two 16-byte row pieces of the lane (tokens l % 16 and 16 + l % 16),
+// hi and lo, for a builder that stores them a step later.
+struct KrHeld {
+  u32x4 h[2], l[2];
+};
+template <int S = NB>
+__device__ __forceinline__ void store_kr(const KrHeld& k, bf16* krh, bf16* krl, const int ob, const int lane) {
+  const int tk = lane & 15;
+  const int c8 = 32 * ob + 8 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    st4(krh + (tk + 16 * j) * S + c8, k.h[j]);
+    st4(krl + (tk + 16 * j) * S + c8, k.l[j]);
+  }
+}
+template <int S = NB>
 __device__ __forceinline__ void build_chunk(const ChunkIn& x, const Planes& P, float* gl, const int ob, const int lane,
-                                            float (&a)[8], float (&gc)[8]) {
+                                            float (&a)[8], float (&gc)[8], KrHeld* held = nullptr) {
   const int tk = lane & 15;
   const int c8 = 32 * ob + 8 * (lane >> 4);
   float kf[2][8], qf[2][8], G[2][8];
@@ -244,9 +264,14 @@ __device__ __forceinline__ void build_chunk(const ChunkIn& x, const Planes& P, f
       const f32x4& dv = x.d[j][w >> 1];
       split_pair(dv[2 * (w & 1)], dv[2 * (w & 1) + 1], dh[w], dl[w]);
     }
-    const int off = (tk + 16 * j) * NB + c8;
-    st4(P.krh + off, u32x4{krh[0], krh[1], krh[2], krh[3]});
-    st4(P.krl + off, u32x4{krl[0], krl[1], krl[2], krl[3]});
+    const int off = (tk + 16 * j) * S + c8;
+    if (held != nullptr) {
+      held->h[j] = u32x4{krh[0], krh[1], krh[2], krh[3]};
+      held->l[j] = u32x4{krl[0], krl[1], krl[2], krl[3]};
+    } else {
+      st4(P.krh + off, u32x4{krh[0], krh[1], krh[2], krh[3]});
+      st4(P.krl + off, u32x4{krl[0], krl[1], krl[2], krl[3]});
+    }
     st4(P.kch + off, u32x4{kch[0], kch[1], kch[2], kch[3]});
     st4(P.kcl + off, u32x4{kcl[0], kcl[1], kcl[2], kcl[3]});
     st4(P.qrh + off, u32x4{qrh[0], qrh[1], qrh[2], qrh[3]});
@@ -267,34 +292,38 @@ __device__ __forceinline__ void build_chunk(const ChunkIn& x, const Planes& P, f
 //                          as four 32 x 32 FP32 accumulator tiles (rows =
 //                          channels 32dt + 8r + 4(l/32) + e)
 //   operand builders (4-7) Kr, Kc, Qr, dO and fac of a chunk
-//   T helpers (8-11)       P^T from Kr, Kc planes; T diag(beta) transposed
-//                          from the checkpoint launch's cache
+//   T helpers (8-11)       P^T from Kr, Kc planes; T transposed from the
+//                          checkpoint launch's cache
 // With m the position of chunk c = nc-1-m in that order, each step ending
 // with a barrier:
-//   step 2m     builders: chunk m's planes and fac into buffer m & 1
-//   step 2m+1   T helpers: P(m)^T, and the cache load of T diag(beta)(m)
-//   step 2m+2   T helpers: T diag(beta)(m)^T;  owners: D = fac o Delta,
-//               store D, dU = Kc D + P^T dO
-//   step 2m+3   owners: dR = (T diag(beta))^T dU, Delta = D + Qr^T dO - Kr^T dR
+//   step 2m     builders: chunk m's planes and fac into buffer m & 1 (its Kr
+//               into the single Kr plane at step 2m+2, after the owners'
+//               last read of chunk m-1's)
+//   step 2m+1   T helpers: P(m)^T, and the cache load of T(m)
+//   step 2m+2   T helpers: T(m)^T;  owners: D = fac o Delta, store D,
+//               dU = Kc D + P^T dO
+//   step 2m+3   owners: dR = diag(beta) T^T dU, Delta = D + Qr^T dO - Kr^T dR
 //   step 2nc    builders: e^{a_0} (the last rescale) into buffer nc & 1
-// (every wave takes 2nc + 2 barriers).  The planes are double-buffered by m;
-// P^T and T diag(beta)^T are single (each written one step after its last
-// reader).
+// (every wave takes 2nc + 2 barriers).  The planes are double-buffered by m
+// except Kr; P^T and T diag(beta)^T are single (each written one step after
+// its last reader).  Rows are 152 elements apart, which keeps the transposed
+// reads free of bank conflicts.
 // ===========================================================================
 struct alignas(16) ChainSmem {
-  bf16 kr_h[2][CH * NB], kr_l[2][CH * NB];
-  bf16 kc_h[2][CH * NB], kc_l[2][CH * NB];
-  bf16 qr_h[2][CH * NB], qr_l[2][CH * NB];
-  bf16 do_h[2][CH * NB], do_l[2][CH * NB];
+  bf16 kr_h[CH * NC], kr_l[CH * NC];   // single: stored a step after the others
+  bf16 kc_h[2][CH * NC], kc_l[2][CH * NC];
+  bf16 qr_h[2][CH * NC], qr_l[2][CH * NC];
+  bf16 do_h[2][CH * NC], do_l[2][CH * NC];
   bf16 pt_h[CH * TB], pt_l[CH * TB];   // P^T, columns in k-slot order
-  bf16 tt_h[CH * TB], tt_l[CH * TB];   // (T diag(beta))^T, columns in k-slot order
+  bf16 tt_h[CH * TB], tt_l[CH * TB];   // T^T, columns in k-slot order
+  float beta[2][CH];
   float fac[2][KD];
   alignas(16) int16_t fexp[2][KD];     // power-of-two part of fac (0: none)
   int32_t fsplit[2][4];                // per builder: some channel has one
 };
 
 __device__ __forceinline__ Planes chain_planes(ChainSmem& sm, const int b) {
-  return Planes{sm.kr_h[b], sm.kr_l[b], sm.kc_h[b], sm.kc_l[b], sm.qr_h[b], sm.qr_l[b], sm.do_h[b], sm.do_l[b]};
+  return Planes{sm.kr_h, sm.kr_l, sm.kc_h[b], sm.kc_l[b], sm.qr_h[b], sm.qr_l[b], sm.do_h[b], sm.do_l[b]};
 }
 
 // fac = 2^t for the lane's eight channels (lanes with l % 16 = 0 write).
@@ -366,8 +395,8 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
   };
   if (end1 != nullptr) add_end(end1);
   if (end2 != nullptr) add_end(end2);
-  const int pro = (lane & 31) * NB + 4 * lh;
-  const int trb = tr_base(lane);
+  const int pro = (lane & 31) * NC + 4 * lh;
+  const int trb = tr_base<NC>(lane);
   const int tbo = (lane & 31) * TB + 8 * lh;
   __syncthreads();   // steps 0, 1
   __syncthreads();
@@ -408,8 +437,8 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
     bf16x8 doh[2], dol[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      doh[s] = colfrag(sm.do_h[b], s, 32 * ow, trb);
-      dol[s] = colfrag(sm.do_l[b], s, 32 * ow, trb);
+      doh[s] = colfrag<NC>(sm.do_h[b], s, 32 * ow, trb);
+      dol[s] = colfrag<NC>(sm.do_l[b], s, 32 * ow, trb);
       Y = mfma3(smallrow(sm.pt_h, s, tbo), smallrow(sm.pt_l, s, tbo), doh[s], dol[s], Y);
     }
     __syncthreads();
@@ -430,17 +459,22 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
 #pragma unroll
     for (int s = 0; s < 2; ++s) dR = mfma3(smallrow(sm.tt_h, s, tbo), smallrow(sm.tt_l, s, tbo), uh[s], ul[s], dR);
     mfma_result_fence(dR);
+    // dR = diag(beta) T^T dU, negated for Delta -= Kr^T dR
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dR[i] = -dR[i];
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 bv = ld4(&sm.beta[b][8 * r + 4 * lh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dR[4 * r + e] *= -bv[e];
+    }
     bf16x8 rh[2], rl[2];
     tile_kslots_split(dR, rh, rl);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        Dl[dt] = mfma3(colfrag(sm.qr_h[b], s, 32 * dt, trb), colfrag(sm.qr_l[b], s, 32 * dt, trb), doh[s], dol[s],
+        Dl[dt] = mfma3(colfrag<NC>(sm.qr_h[b], s, 32 * dt, trb), colfrag<NC>(sm.qr_l[b], s, 32 * dt, trb), doh[s], dol[s],
                        Dl[dt]);
-        Dl[dt] = mfma3(colfrag(sm.kr_h[b], s, 32 * dt, trb), colfrag(sm.kr_l[b], s, 32 * dt, trb), rh[s], rl[s],
+        Dl[dt] = mfma3(colfrag<NC>(sm.kr_h, s, 32 * dt, trb), colfrag<NC>(sm.kr_l, s, 32 * dt, trb), rh[s], rl[s],
                        Dl[dt]);
       }
     }
@@ -479,11 +513,21 @@ __device__ __forceinline__ void chain_builder(const BwdParams& p, ChainSmem& sm,
   float anext[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) anext[c] = 0.f;
+  KrHeld kr;   // chunk m's Kr, stored at step 2m+2 (the owners read the
+               // previous chunk's until the end of step 2m+1)
   for (int m = 0; m < nc; ++m) {
     const int b = m & 1;
     const int c = nc - 1 - m;
+    if (m > 0) store_kr<NC>(kr, sm.kr_h, sm.kr_l, ob, lane);
+    if (ob == 0 && lane < CH) {
+      const int n = ntok(c);
+      const auto rb = res(p.beta + static_cast<size_t>(beg + CH * c) * p.H + h, (n - 1) * p.H * 2 + 2);
+      sm.beta[b][lane] = __uint_as_float(
+          static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rb, lane * p.H * 2, 0, 0)))
+          << 16);
+    }
     float a[8], gc[8];
-    build_chunk(x, chain_planes(sm, b), nullptr, ob, lane, a, gc);
+    build_chunk<NC>(x, chain_planes(sm, b), nullptr, ob, lane, a, gc, &kr);
     if (c > 0) fetch_chunk(p, h, beg + CH * (c - 1), ntok(c - 1), ob, lane, x);
     float t[8];
 #pragma unroll
@@ -495,6 +539,7 @@ __device__ __forceinline__ void chain_builder(const BwdParams& p, ChainSmem& sm,
     __syncthreads();   // step 2m
     __syncthreads();   // step 2m+1
   }
+  store_kr<NC>(kr, sm.kr_h, sm.kr_l, ob, lane);   // the last chunk's, at step 2nc
   put_fac(sm, nc & 1, ob, lane, anext);   // e^{a_0}
   __syncthreads();   // step 2nc
   __syncthreads();   // step 2nc+1
@@ -520,7 +565,7 @@ __device__ __forceinline__ void chain_thelper(const BwdParams& p, ChainSmem& sm,
     if (th < 3) {
       const int rb = th > 0;
       const int ct = th > 1;
-      const f32x4 acc = tile16c(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], rb, ct, lane);
+      const f32x4 acc = tile16c<NC>(sm.qr_h[b], sm.qr_l[b], sm.kc_h[b], sm.kc_l[b], rb, ct, lane);
       // P[i][j], i = 16rb + 4lg + e, j = 16ct + lm, kept where j <= i, to
       // P^T[j][kpos(i)]
       uint32_t hv[2], lv[2];
@@ -539,8 +584,8 @@ __device__ __forceinline__ void chain_thelper(const BwdParams& p, ChainSmem& sm,
       *reinterpret_cast<uint2*>(sm.pt_l + pos) = make_uint2(0u, 0u);
     }
     __syncthreads();
-    // ---- step 2m+2: (T diag(beta))^T[j][kpos(i)] = T diag(beta)[i][j]; the
-    // cache row holds column j = kpos(8 tq + x) at position 8 tq + x
+    // ---- step 2m+2: T^T[j][kpos(i)] = T[i][j]; the cache row holds column
+    // j = kpos(8 tq + x) at position 8 tq + x
     {
       bf16* dst = which ? sm.tt_l : sm.tt_h;
       const int pi = kpos(ti);
@@ -625,13 +670,10 @@ struct alignas(16) GradSmem {
       bf16 da_h[CH * TB], da_l[CH * TB], dat_h[CH * TB], dat_l[CH * TB];
     } b;
   } m;
-  // A' and the solve scratch (phases 1-4), then the exchange (phase 5)
+  // A' (phases 1-4), then the exchange (phase 5)
   union {
     struct {
       float ap[CH * AS];    // A' (strictly lower)
-      float t00[16 * FS];   // t00[c][i] = T00[i][c]
-      float t11[16 * FS];   // t11[c][i] = T11[i][c]
-      float xm[16 * FS];    // xm[c][i] = (A10 T00)[i][c]
     } s;
     struct {
       float xw[4][CH * XWS];   // (dk_i + dk_h)[token][channel] per channel block
@@ -660,19 +702,6 @@ __device__ __forceinline__ void store_rows(float* base, const int H, const int n
                                             0);
 }
 
-// Column fragments of a state (value column col, all 128 channels in the
-// k-slot order of the eight k-steps): x[8kk + j] = S[16kk + 4(l/32) + j'][col],
-// j' = j (j < 4) or 8 + j - 4.
-__device__ __forceinline__ void load_colfrags(const float* S, const int col, const int lane, float (&x)[64]) {
-  const auto rs = res(S, MATF * 4);
-  const int voff = 4 * (4 * (lane >> 5) * VD + col);
-#pragma unroll
-  for (int kk = 0; kk < KD / 16; ++kk)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      x[8 * kk + j] = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 4 * (16 * kk + (j < 4 ? j : 8 + j - 4)) * VD, 0));
-}
 // Row fragments of a state (channel row, all 128 values in k-slot order):
 // x[8ks + j] = S[row][16ks + 4(l/32) + j'].
 __device__ __forceinline__ void load_rowfrags(const float* S, const int row, const int lane, float (&x)[64]) {
@@ -730,12 +759,22 @@ __device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, co
   const int lane = x.lane, lh = x.lh, w = x.w4;
   float fr[64];
   __syncthreads();   // phase 0
-  // ---- phases 1-4 (five barriers): R's row fragments, in flight until phase 5
+  // ---- phases 1-4 (three barriers): R's row fragments, in flight until phase 5
   load_rowfrags(x.Rg, 32 * w + (lane & 31), lane, fr);
-  for (int i = 0; i < 5; ++i) __syncthreads();
+  for (int i = 0; i < 3; ++i) __syncthreads();
   // ---- phase 5: dO R^T + dP Kc and -dR R^T + dA' Kc for channel block w
-  f32x16 vq = prod_frags(sm.do_h, sm.do_l, fr, x.pro, zero16());
-  f32x16 vd = prod_frags(sm.dx_h, sm.dx_l, fr, x.pro, zero16());
+  // (one split of each R fragment serves both products)
+  f32x16 vq = zero16(), vd = zero16();
+#pragma unroll
+  for (int kk = 0; kk < VD / 16; ++kk) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fr[8 * kk + j];
+    bf16x8 bh, bl;
+    split8<true>(v, bh, bl);
+    vq = mfma3(rowfrag(sm.do_h, kk, x.pro), rowfrag(sm.do_l, kk, x.pro), bh, bl, vq);
+    vd = mfma3(rowfrag(sm.dx_h, kk, x.pro), rowfrag(sm.dx_l, kk, x.pro), bh, bl, vd);
+  }
   mfma_result_fence(vd);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -804,9 +843,9 @@ __device__ __forceinline__ void grad_role_b(const BwdParams& p, GradSmem& sm, co
   const int lane = x.lane, lh = x.lh, w = x.w4;
   float fr[64];
   __syncthreads();   // phase 0
-  // ---- phases 1-4 (five barriers): D's row fragments, in flight until phase 5
+  // ---- phases 1-4 (three barriers): D's row fragments, in flight until phase 5
   load_rowfrags(x.Dg, 32 * w + (lane & 31), lane, fr);
-  for (int i = 0; i < 5; ++i) __syncthreads();
+  for (int i = 0; i < 3; ++i) __syncthreads();
   // ---- phase 5: (U D^T + dP^T Qr + dA'^T Kr) e^{a-G} to the exchange, with
   // colsum(k o U D^T e^{a-G})
   const int col = 32 * w + (lane & 31);
@@ -857,7 +896,31 @@ __device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, co
                 a, gc);
   }
   __syncthreads();
-  // ---- phase 1: A' = Kr Kc^T (strictly lower, FP32) or P = Qr Kc^T -> P^T
+  // ---- phase 1: A' = Kr Kc^T (strictly lower, FP32) (wave 8) or P = Qr Kc^T
+  // -> P^T (wave 9);  T and T^T from the checkpoint launch's cache (waves 10,
+  // 11: each lane moves two 16-byte pieces; a cache row holds column
+  // j = kpos(p) at position p)
+  if (wave >= 10) {
+    const uint16_t* tc =
+        p.tcache + (static_cast<size_t>(x.slot) * x.H + x.h) * (kChunkCacheBytes / 2);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ci = lane + 64 * (wave - 10) + 128 * k2;
+      const int which = ci >> 7;
+      const int ti = (ci >> 2) & 31;
+      const int tq = ci & 3;
+      const u32x4 tv = *reinterpret_cast<const u32x4*>(tc + which * (CH * CH) + ti * CH + 8 * tq);
+      bf16* tn = which ? sm.m.a.t_l : sm.m.a.t_h;
+      bf16* tt = which ? sm.m.a.tt_l : sm.m.a.tt_h;
+      *reinterpret_cast<u32x4*>(tn + ti * TB + 8 * tq) = tv;
+      const int pi = kpos(ti);
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        tt[kpos(8 * tq + 2 * w2) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] & 0xffffu));
+        tt[kpos(8 * tq + 2 * w2 + 1) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] >> 16));
+      }
+    }
+  }
   if (wave == 8 || wave == 9) {
     f32x16 acc = zero16();
     const bf16* xh = wave == 8 ? sm.kr_h : sm.qr_h;
@@ -884,70 +947,6 @@ __device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, co
           if (j > 8 * r + 4 * lh + e) acc[4 * r + e] = 0.f;
       store_t(acc, sm.m.a.pt_h, sm.m.a.pt_l, lane);
     }
-  }
-  __syncthreads();
-  // ---- phase 2: T = (I + diag(beta) A')^-1 by 16 x 16 blocks; column c of
-  // diagonal block wave - 8 by forward substitution
-  if (wave == 8 || wave == 9) {
-    const int cc = lane & 15;
-    const int o = 16 * (wave - 8);
-    float xs[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xs[i] = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 15; ++jj)
-#pragma unroll
-      for (int i = jj + 1; i < 16; ++i) xs[i] -= sm.beta[o + i] * sm.e.s.ap[(o + i) * AS + o + jj] * xs[jj];
-    float* dst = wave == 8 ? sm.e.s.t00 : sm.e.s.t11;
-    if (lane < 16) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        st4(&dst[cc * FS + 4 * q4], f32x4{xs[4 * q4], xs[4 * q4 + 1], xs[4 * q4 + 2], xs[4 * q4 + 3]});
-    }
-  }
-  __syncthreads();
-  {
-    // X = A10 T00 (column tc), then T10 = -T11 X; T and T^T as split bf16
-    const int ti = lane & 15;
-    const int tc = 4 * w + (lane >> 4);
-    float xsum = 0.f;
-#pragma unroll
-    for (int mm = 0; mm < 16; ++mm) xsum += sm.e.s.ap[(16 + ti) * AS + mm] * sm.e.s.t00[tc * FS + mm];
-    xsum *= sm.beta[16 + ti];
-    sm.e.s.xm[tc * FS + ti] = xsum;
-    wave_lds_order();
-    float t10 = 0.f;
-#pragma unroll
-    for (int kq = 0; kq < 16; ++kq) t10 -= sm.e.s.t11[kq * FS + ti] * sm.e.s.xm[tc * FS + kq];
-    const float t00 = sm.e.s.t00[tc * FS + ti];
-    const float t11 = sm.e.s.t11[tc * FS + ti];
-    const int pc = kpos(tc);
-    const int pi = kpos(ti);
-    bf16* th = sm.m.a.t_h;
-    bf16* tl = sm.m.a.t_l;
-    bf16* uh = sm.m.a.tt_h;
-    bf16* ul = sm.m.a.tt_l;
-    bf16 hh, ll;
-    const bf16 z = static_cast<bf16>(0.f);
-    split(t00, hh, ll);
-    th[ti * TB + pc] = hh;
-    tl[ti * TB + pc] = ll;
-    uh[tc * TB + pi] = hh;
-    ul[tc * TB + pi] = ll;
-    split(t11, hh, ll);
-    th[(16 + ti) * TB + 16 + pc] = hh;
-    tl[(16 + ti) * TB + 16 + pc] = ll;
-    uh[(16 + tc) * TB + 16 + pi] = hh;
-    ul[(16 + tc) * TB + 16 + pi] = ll;
-    split(t10, hh, ll);
-    th[(16 + ti) * TB + pc] = hh;
-    tl[(16 + ti) * TB + pc] = ll;
-    uh[tc * TB + 16 + pi] = hh;
-    ul[tc * TB + 16 + pi] = ll;
-    th[ti * TB + 16 + pc] = z;
-    tl[ti * TB + 16 + pc] = z;
-    uh[(16 + tc) * TB + pi] = z;
-    ul[(16 + tc) * TB + pi] = z;
   }
   __syncthreads();
   __syncthreads();   // phase 3
@@ -1028,8 +1027,6 @@ __device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, co
   }
   __syncthreads();
   __syncthreads();   // phase 1
-  __syncthreads();   // phase 2: the diagonal blocks of T
-  __syncthreads();   // phase 2: T and T^T
   // ---- phase 3: X = diag(beta)(V - W), U^T = X^T T^T -> U plane;
   // dX = T^T dU, dX^T = dU^T T -> dX plane;  dv = diag(beta) dX
   {

@@ -239,10 +239,11 @@ __device__ __forceinline__ void p_store(const f32x4& acc, const int rbp, const i
   }
 }
 
-// T10 = -T11 A10 T00 and T diag(beta) as split bf16 (columns in k-slot
-// order), for the columns
+// T10 = -T11 A10 T00 and T diag(beta) (T itself with UNSC) as split bf16
+// (columns in k-slot order), for the columns
 // tc = 4q .. 4q+3 (q = 0..3), lane (row ti, column tc); X = A10 T00 goes
 // through LDS inside the wave, which needs no barrier.
+template <bool UNSC = false>
 __device__ __forceinline__ void t_merge(const float* an, const float* tt, const float* tn, float* xt,
                                         const float* beta, bf16* tbh, bf16* tbl, const int q, const int lane_s) {
   const int ti = lane_s & 15;
@@ -260,8 +261,8 @@ __device__ __forceinline__ void t_merge(const float* an, const float* tt, const 
   xt[tc * XS + ti] = xs;   // X = A10 T00, stored by column
   const float t00 = tt[tc * FS + ti];               // T00[ti][tc]
   const float t11 = tn[(16 + ti) * FS + 16 + tc];    // T11[ti][tc]
-  const float b0 = beta[tc];
-  const float b1 = beta[16 + tc];
+  const float b0 = UNSC ? 1.f : beta[tc];
+  const float b1 = UNSC ? 1.f : beta[16 + tc];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) u[q4] = ld4(&tn[(16 + ti) * FS + 16 + 4 * q4]);   // T11[ti, :]
   wave_lds_order();
@@ -481,10 +482,15 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
     }
   };
 
+  f32x4 bkeep[4];   // kModeCkpt: beta of chunk n's tokens 8r + 4lh + 0..3
   // step 2n: Y = Kr R and O = Qr R (R already anchored for chunk n), operand
   // loads one k-step ahead
   auto products = [&](const int n) __attribute__((always_inline)) {
     const int b = n & 1;
+    if (MODE == kModeCkpt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bkeep[r] = ld4(&sm.beta[b][8 * r + 4 * lh]);
+    }
     Y = zero16();
     if (fwd) O = zero16();
     bf16x8 opa[2][4];
@@ -531,6 +537,13 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
         for (int e = 0; e < 4; ++e)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(D[4 * r + e]), rsv, 4 * (4 * lh * VD + col),
                                                 4 * (8 * r + e) * VD, 0);
+      // the T helpers leave T unscaled in this mode (the cache keeps T for
+      // the backward): U = T diag(beta) D, with beta read in products(n)
+      // (the operand helpers rewrite this buffer in step 2n+1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[4 * r + e] *= bkeep[r][e];
     }
     // D and U feed the next products as B operands in k-slot order (tokens):
     // T diag(beta) and P are stored in that column order, Kc^T is read in it
@@ -1019,7 +1032,7 @@ __device__ __forceinline__ void pipe_ophelper(const ChunkParams& p, PipeSmem& sm
 // their segment).  It also computes the three blocks of P in part 1 and
 // stores them in part 2: one block on each of th 0-2 where T diag(beta) comes
 // from the cache, all three on th 3 where th 0-2 build it.
-template <bool FILL>
+template <bool FILL, bool UNSC = false>
 __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm, const int h, const int th,
                                              const int32_t flags,
                                              const int32_t seg, const int32_t beg, const int32_t end) {
@@ -1070,7 +1083,7 @@ __device__ __forceinline__ void pipe_thelper(const ChunkParams& p, PipeSmem& sm,
     {
       const int lane_s = opaque(lane);
       if (cached) st4(&((ci >> 7) ? sm.tb_l : sm.tb_h)[cache_lds(ci)], tbv);
-      else t_merge(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
+      else t_merge<UNSC>(sm.an, sm.tt, sm.tn, sm.xt, sm.beta[b], sm.tb_h, sm.tb_l, th, lane_s);
       if (!FILL) {
         if (cached) {
           if (th < 3) p_store(pacc[0], th > 0, th > 1, sm.p_h, sm.p_l, lane_s);
@@ -1174,8 +1187,8 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_carry_kernel(ChunkParams
 
 // Checkpoint launch of the chunked backward: every fragment, forward from its
 // segment's carry-in (or its sequence's initial state, or zero) without o,
-// storing the anchored state entering each chunk and each chunk's
-// T diag(beta) at slot floor(begin / 32) + f + chunk (the fragment index f in
+// storing the anchored state entering each chunk, V - Kr R and T (without
+// diag(beta)) of each chunk at slot floor(begin / 32) + f + chunk (the fragment index f in
 // place of the segment's: every fragment gets its own slots), and whether the
 // fragment left the anchored form's range.  Waves as in the carry launch.
 __global__ void __launch_bounds__(kCarryThreads, 1) kda_ckpt_kernel(ChunkParams p) {
@@ -1204,7 +1217,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) kda_ckpt_kernel(ChunkParams 
     pipe_owner<kModeCkpt>(p, sm, h, wave, flags, seg, seq, beg, end, start_state(p, h, flags, seg, seq, true),
                           static_cast<int64_t>(beg / CH) + f);
   else if (wave < 2 * NOWN) pipe_ophelper<kModeSumS>(p, sm, h, wave - NOWN, beg, end);
-  else pipe_thelper<true>(p, sm, h, wave - 2 * NOWN, flags, f, beg, end);
+  else pipe_thelper<true, true>(p, sm, h, wave - 2 * NOWN, flags, f, beg, end);
 }
 
 }  // namespace kda
