@@ -376,6 +376,18 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   const int64_t seg_blocks = static_cast<int64_t>(plan->P) * head_count;   // the backward works on pieces
   const int64_t items = static_cast<int64_t>(plan->F) * head_count;
   if (seg_blocks > 2147483647LL || items > 2147483647LL) return KDA_ERR_UNSUPPORTED;
+  // the gradient launch is persistent, one workgroup per CU at most: the
+  // device's CU count, before anything is enqueued
+  int cus = 0;
+  {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) {
+      g_last_hip_error = static_cast<int>(e);
+      return KDA_ERR_HIP;
+    }
+  }
   const kda::BwdLayout W = kda::backward_layout(plan, H);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* transitions = reinterpret_cast<float*>(ws + W.transitions);
@@ -455,6 +467,7 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   p.smap = reinterpret_cast<int32_t*>(ws + W.smap);
   p.rvbuf = reinterpret_cast<const float*>(ws + W.rv);
   p.dubuf = reinterpret_cast<float*>(ws + W.du);
+  p.nslots = static_cast<int32_t>(slots);
   // E_r: the chunked chain over each carried segment's first fragment, then
   // the token-by-token summaries of the flagged ones
   (void)hipGetLastError();
@@ -491,7 +504,8 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   // gradients
   hipLaunchKernelGGL(kda::kda_bwd_chain_kernel, dim3(static_cast<uint32_t>(items)), dim3(kda::kChainThreads), 0,
                      stream, p);
-  hipLaunchKernelGGL(kda::kda_bwd_grad_kernel, dim3(static_cast<uint32_t>(slots * head_count)),
-                     dim3(kda::kGradThreads), 0, stream, p);
+  const int64_t ggrid = static_cast<int64_t>(slots) * head_count < cus ? static_cast<int64_t>(slots) * head_count : cus;
+  hipLaunchKernelGGL(kda::kda_bwd_grad_kernel, dim3(static_cast<uint32_t>(ggrid)), dim3(kda::kGradThreads), 0,
+                     stream, p);
   return finish_launch();
 }

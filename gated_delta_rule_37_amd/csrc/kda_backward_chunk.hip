@@ -754,12 +754,14 @@ struct GradCtx {
   const float* Dg;
 };
 
-// Waves 0-3 (channel block w).
+// Waves 0-3 (channel block w), one chunk.
 __device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
   float fr[64];
   __syncthreads();   // phase 0
-  // ---- phases 1-4 (three barriers): R's row fragments, in flight until phase 5
+  // ---- phases 1-4 (three barriers): R's row fragments, in flight until phase
+  // 5 (issued a chunk earlier they were slower: the phase-5 re-read of R and D
+  // for rowsum(D o R) then misses L2)
   load_rowfrags(x.Rg, 32 * w + (lane & 31), lane, fr);
   for (int i = 0; i < 3; ++i) __syncthreads();
   // ---- phase 5: dO R^T + dP Kc and -dR R^T + dA' Kc for channel block w
@@ -838,7 +840,7 @@ __device__ __forceinline__ void grad_role_a(const BwdParams& p, GradSmem& sm, co
   store_rows(p.dg + ob, x.H, x.n, col, lane, dg);
 }
 
-// Waves 4-7 (channel block w).
+// Waves 4-7 (channel block w), one chunk.
 __device__ __forceinline__ void grad_role_b(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
   float fr[64];
@@ -878,49 +880,57 @@ __device__ __forceinline__ void grad_role_b(const BwdParams& p, GradSmem& sm, co
   __syncthreads();
 }
 
-// Waves 8-11: the operands, A', P^T, the solve for T, dP and dA.
-__device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+// Waves 8-11, one chunk: the operands and the copies of T (phase 0), A' and
+// P^T (phase 1), dP and dA (phase 4); in phase 5 the next chunk's inputs are
+// fetched into `in` (held across its barriers to its phase 0).
+struct GradPre {
+  ChunkIn in;
+  u32x4 t;      // 16 bytes of the chunk's cached T
+  float beta;   // wave 8, lanes below 32
+};
+
+__device__ __forceinline__ void grad_prefetch_c(const BwdParams& p, const GradCtx& x, GradPre& pre) {
+  fetch_chunk(p, x.h, x.c0, x.n, x.w4, x.lane, pre.in);
+  const uint16_t* tc = p.tcache + (static_cast<size_t>(x.slot) * x.H + x.h) * (kChunkCacheBytes / 2);
+  const int ci = x.lane + 64 * x.w4;
+  pre.t = *reinterpret_cast<const u32x4*>(tc + (ci >> 7) * (CH * CH) + ((ci >> 2) & 31) * CH + 8 * (ci & 3));
+  pre.beta = 0.f;
+  if (x.wave == 8 && x.lane < CH) {
+    const auto rb = res(p.beta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 2 + 2);
+    pre.beta = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(
+                                   __builtin_amdgcn_raw_buffer_load_b16(rb, x.lane * x.H * 2, 0, 0)))
+                               << 16);
+  }
+}
+
+__device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, const GradCtx& x, const GradCtx& xn,
+                                            GradPre& pre) {
   const int lane = x.lane, lh = x.lh, wave = x.wave, w = x.w4;
-  // ---- phase 0: Kr, Kc, Qr, dO planes and G - a; beta
+  // ---- phase 0: Kr, Kc, Qr, dO planes and G - a; beta; T and T^T (a cache
+  // row holds column j = kpos(p) at position p)
   {
-    ChunkIn in;
-    fetch_chunk(p, x.h, x.c0, x.n, w, lane, in);
-    if (wave == 8 && lane < CH) {
-      const auto rb = res(p.beta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 2 + 2);
-      sm.beta[lane] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(
-                          __builtin_amdgcn_raw_buffer_load_b16(rb, lane * x.H * 2, 0, 0)))
-                      << 16);
-    }
+    if (wave == 8 && lane < CH) sm.beta[lane] = pre.beta;
     float a[8], gc[8];
-    build_chunk(in, Planes{sm.kr_h, sm.kr_l, sm.kc_h, sm.kc_l, sm.qr_h, sm.qr_l, sm.do_h, sm.do_l}, sm.gl, w, lane,
-                a, gc);
+    build_chunk(pre.in, Planes{sm.kr_h, sm.kr_l, sm.kc_h, sm.kc_l, sm.qr_h, sm.qr_l, sm.do_h, sm.do_l}, sm.gl, w,
+                lane, a, gc);
+    const int ci = lane + 64 * w;
+    const int which = ci >> 7;
+    const int ti = (ci >> 2) & 31;
+    const int tq = ci & 3;
+    const u32x4 tv = pre.t;
+    bf16* tn = which ? sm.m.a.t_l : sm.m.a.t_h;
+    bf16* tt = which ? sm.m.a.tt_l : sm.m.a.tt_h;
+    *reinterpret_cast<u32x4*>(tn + ti * TB + 8 * tq) = tv;
+    const int pi = kpos(ti);
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      tt[kpos(8 * tq + 2 * w2) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] & 0xffffu));
+      tt[kpos(8 * tq + 2 * w2 + 1) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] >> 16));
+    }
   }
   __syncthreads();
   // ---- phase 1: A' = Kr Kc^T (strictly lower, FP32) (wave 8) or P = Qr Kc^T
-  // -> P^T (wave 9);  T and T^T from the checkpoint launch's cache (waves 10,
-  // 11: each lane moves two 16-byte pieces; a cache row holds column
-  // j = kpos(p) at position p)
-  if (wave >= 10) {
-    const uint16_t* tc =
-        p.tcache + (static_cast<size_t>(x.slot) * x.H + x.h) * (kChunkCacheBytes / 2);
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int ci = lane + 64 * (wave - 10) + 128 * k2;
-      const int which = ci >> 7;
-      const int ti = (ci >> 2) & 31;
-      const int tq = ci & 3;
-      const u32x4 tv = *reinterpret_cast<const u32x4*>(tc + which * (CH * CH) + ti * CH + 8 * tq);
-      bf16* tn = which ? sm.m.a.t_l : sm.m.a.t_h;
-      bf16* tt = which ? sm.m.a.tt_l : sm.m.a.tt_h;
-      *reinterpret_cast<u32x4*>(tn + ti * TB + 8 * tq) = tv;
-      const int pi = kpos(ti);
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        tt[kpos(8 * tq + 2 * w2) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] & 0xffffu));
-        tt[kpos(8 * tq + 2 * w2 + 1) * TB + pi] = __builtin_bit_cast(bf16, static_cast<uint16_t>(tv[w2] >> 16));
-      }
-    }
-  }
+  // -> P^T (wave 9)
   if (wave == 8 || wave == 9) {
     f32x16 acc = zero16();
     const bf16* xh = wave == 8 ? sm.kr_h : sm.qr_h;
@@ -994,37 +1004,48 @@ __device__ __forceinline__ void grad_role_c(const BwdParams& p, GradSmem& sm, co
     }
   }
   __syncthreads();
+  // ---- phase 5: the next chunk's inputs (this chunk's again after the last
+  // one: an unconditional fetch lets the old values die here)
+  grad_prefetch_c(p, xn, pre);
   __syncthreads();   // phase 5
 }
 
-// Waves 12-15 (value block w): V - W and dU (phase 0), U^T, dX, dX^T and dv
-// (phase 3), rowsum(dX o (V - W)) (phase 4), rowsum(D o R) and dbeta
-// (phase 5).
-__device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, const GradCtx& x) {
+// V - W and dU of a chunk at the tile's rows (token 8r + 4lh + e, value
+// 32w + l % 32), and V - W transposed (value 32w + 8r + 4lh + e, token l % 32).
+struct GradPreD {
+  f32x16 rv, du, rvt;
+};
+
+__device__ __forceinline__ void grad_prefetch_d(const BwdParams& p, const GradCtx& x, GradPreD& pre) {
   const int lane = x.lane, lh = x.lh, w = x.w4;
   const int col = 32 * w + (lane & 31);
-  // ---- phase 0: V - W and dU at the tile's rows (token 8r + 4lh + e, value
-  // col), and V - W transposed (value 32w + 8r + 4lh + e, token l % 32)
-  f32x16 rv, du, rvt;
-  {
-    const auto rs1 = res(p.rvbuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
-    const auto rs2 = res(p.dubuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
-    const int voff = 4 * (4 * lh * VD + col);
+  const auto rs1 = res(p.rvbuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
+  const auto rs2 = res(p.dubuf + (static_cast<size_t>(x.slot) * x.H + x.h) * CH * VD, CH * VD * 4);
+  const int voff = 4 * (4 * lh * VD + col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rv[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs1, voff, 4 * (8 * r + e) * VD, 0));
-        du[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, voff, 4 * (8 * r + e) * VD, 0));
-      }
-    const int toff = 4 * ((lane & 31) * VD + 32 * w + 4 * lh);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 v4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs1, toff, 32 * r, 0));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rvt[4 * r + e] = v4[e];
+    for (int e = 0; e < 4; ++e) {
+      pre.rv[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs1, voff, 4 * (8 * r + e) * VD, 0));
+      pre.du[4 * r + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, voff, 4 * (8 * r + e) * VD, 0));
     }
+  const int toff = 4 * ((lane & 31) * VD + 32 * w + 4 * lh);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const f32x4 v4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs1, toff, 32 * r, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pre.rvt[4 * r + e] = v4[e];
   }
+}
+
+// Waves 12-15 (value block w), one chunk: U^T, dX, dX^T and dv (phase 3),
+// rowsum(dX o (V - W)) and rowsum(D o R) (phase 4), dbeta (phase 5); in
+// phase 6 the next chunk's V - W and dU are fetched into `pre`.
+__device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, const GradCtx& x, const GradCtx& xn,
+                                            GradPreD& pre) {
+  const int lane = x.lane, lh = x.lh, w = x.w4;
+  const int col = 32 * w + (lane & 31);
+  const f32x16 rv = pre.rv, du = pre.du, rvt = pre.rvt;
   __syncthreads();
   __syncthreads();   // phase 1
   // ---- phase 3: X = diag(beta)(V - W), U^T = X^T T^T -> U plane;
@@ -1074,10 +1095,9 @@ __device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, co
     part += __shfl_xor(part, 32);
     if (lh == 0) sm.red[w][lane & 31] = part;
   }
-  __syncthreads();
-  // ---- phase 5: rowsum(D o R) for the channels of block w (read in phase
-  // 6; row 32w + l % 32, the lane's half of the values, in two passes of 32),
-  // and dbeta
+  // rowsum(D o R) for the channels of block w (read in phase 6; row
+  // 32w + l % 32, the lane's half of the values, in two passes of 32): R and
+  // D were fetched in phase 1 by waves 0-7, so these reads find them in L2
   {
     const int row = 32 * w + (lane & 31);
     const auto rr = res(x.Rg, MATF * 4);
@@ -1103,45 +1123,117 @@ __device__ __forceinline__ void grad_role_d(const BwdParams& p, GradSmem& sm, co
     s += __shfl_xor(s, 32);
     if (lh == 0) sm.rs[row] = s;
   }
+  __syncthreads();
+  // ---- phase 5: dbeta
   if (x.wave == 12 && lane < CH) {
     const float db = sm.red2[lane] + ((sm.red[0][lane] + sm.red[1][lane]) + (sm.red[2][lane] + sm.red[3][lane]));
     const auto rb = res(p.dbeta + static_cast<size_t>(x.c0) * x.H + x.h, (x.n - 1) * x.H * 4 + 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(db), rb, lane * x.H * 4, 0, 0);
   }
   __syncthreads();
+  // ---- phase 6: the next chunk's V - W and dU (see grad_role_c)
+  grad_prefetch_d(p, xn, pre);
 }
 
-__device__ __forceinline__ void grad_chunk(const BwdParams& p) {
-  __shared__ GradSmem sm;
-  const int hn = p.hn;
-  const int64_t slot = blockIdx.x / hn;
-  const int hi = blockIdx.x % hn;
+// The next chunk item at or after `it` (stepping by the grid) that is on the
+// chunked path: item = slot * hn + head offset; `total` when none is left.
+__device__ __forceinline__ int grad_next(const BwdParams& p, int it, const int total) {
+  for (; it < total; it += static_cast<int>(gridDim.x)) {
+    const int slot = it / p.hn;
+    const int f = p.smap[slot];
+    if (f >= 0 && p.iflag[static_cast<size_t>(f) * p.hn + (it - slot * p.hn)] == 0) return it;
+  }
+  return total;
+}
+
+__device__ __forceinline__ void grad_ctx(const BwdParams& p, const int it, GradCtx& x) {
+  const int slot = it / p.hn;
   const int f = p.smap[slot];
-  if (f < 0) return;
-  if (p.iflag[static_cast<size_t>(f) * hn + hi] != 0) return;
-  GradCtx x;
   x.slot = slot;
-  x.H = p.H;
-  x.h = p.h0 + hi;
+  x.h = p.h0 + (it - slot * p.hn);
   const int32_t beg = p.plan[p.L.frag_begin + f];
   const int32_t end = p.plan[p.L.frag_end + f];
-  x.c0 = beg + CH * static_cast<int>(slot - (beg / CH + f));
+  x.c0 = beg + CH * (slot - (beg / CH + f));
   x.n = min(CH, end - x.c0);
   x.Rg = p.ck32 + (static_cast<size_t>(slot) * x.H + x.h) * MATF;
   x.Dg = p.dcot + (static_cast<size_t>(slot) * x.H + x.h) * MATF;
-  const int tid = threadIdx.x;
+}
+
+// Persistent: each workgroup (one per CU) walks the items it + k * grid; the
+// operand waves and the V - W / dU waves fetch the next item's inputs during
+// the current one's last phases.  Every wave walks the same items and takes
+// the same six barriers per item, the last of which keeps the next item's
+// phase-0 writes behind this item's phase-6 reads.
+// The lane's fields of an item's context, from a value the compiler cannot
+// see through: so the per-lane LDS addresses of every phase are recomputed in
+// each item instead of being hoisted out of the item loop and kept live
+// (which spilled).
+__device__ __forceinline__ void grad_lane(GradCtx& x) {
+  const int tid = opaque(static_cast<int>(threadIdx.x));
   x.lane = tid & 63;
   x.lh = x.lane >> 5;
-  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  x.w4 = x.wave & 3;
   x.pro = (x.lane & 31) * NB + 4 * x.lh;
   x.trb = tr_base(x.lane);
   x.tbo = (x.lane & 31) * TB + 8 * x.lh;
+}
+
+// Persistent: each workgroup (one per CU) walks the items it + k * grid; the
+// operand waves and the V - W / dU waves fetch the next item's inputs during
+// the current one's last phases.  Every wave walks the same items and takes
+// the same six barriers per item, the last of which keeps the next item's
+// phase-0 writes behind this item's phase-6 reads.
+__device__ __forceinline__ void grad_chunks(const BwdParams& p) {
+  __shared__ GradSmem sm;
+  const int total = p.nslots * p.hn;
+  GradCtx x, xn;
+  x.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  x.w4 = x.wave & 3;
+  x.H = p.H;
   x.rowb = static_cast<uint32_t>(x.H) * 128 * 2;
-  if (x.wave < 4) grad_role_a(p, sm, x);
-  else if (x.wave < 8) grad_role_b(p, sm, x);
-  else if (x.wave < 12) grad_role_c(p, sm, x);
-  else grad_role_d(p, sm, x);
+  grad_lane(x);
+  xn = x;
+  int it = grad_next(p, static_cast<int>(blockIdx.x), total);
+  if (it >= total) return;
+  grad_ctx(p, it, x);
+  if (x.wave < 8) {
+    while (true) {
+      grad_lane(x);
+      if (x.wave < 4) grad_role_a(p, sm, x);
+      else grad_role_b(p, sm, x);
+      __syncthreads();
+      it = grad_next(p, it + static_cast<int>(gridDim.x), total);
+      if (it >= total) break;
+      grad_ctx(p, it, x);
+    }
+  } else if (x.wave < 12) {
+    GradPre pre;
+    grad_prefetch_c(p, x, pre);
+    while (true) {
+      const int nx = grad_next(p, it + static_cast<int>(gridDim.x), total);
+      grad_ctx(p, nx < total ? nx : it, xn);
+      grad_lane(x);
+      grad_lane(xn);
+      grad_role_c(p, sm, x, xn, pre);
+      __syncthreads();
+      if (nx >= total) break;
+      it = nx;
+      x = xn;
+    }
+  } else {
+    GradPreD pre;
+    grad_prefetch_d(p, x, pre);
+    while (true) {
+      const int nx = grad_next(p, it + static_cast<int>(gridDim.x), total);
+      grad_ctx(p, nx < total ? nx : it, xn);
+      grad_lane(x);
+      grad_lane(xn);
+      grad_role_d(p, sm, x, xn, pre);
+      __syncthreads();
+      if (nx >= total) break;
+      it = nx;
+      x = xn;
+    }
+  }
 }
 
 }  // namespace
@@ -1177,7 +1269,8 @@ __global__ void __launch_bounds__(kChainThreads, 1) kda_bwd_chain_kernel(BwdPara
 }
 
 // Every chunk slot and head: that chunk's gradients (slots of no fragment,
-// and fragments on the token-by-token path, return at once).
-__global__ void __launch_bounds__(kGradThreads, 1) kda_bwd_grad_kernel(BwdParams p) { grad_chunk(p); }
+// and fragments on the token-by-token path, are skipped); a persistent grid
+// of at most one workgroup per CU.
+__global__ void __launch_bounds__(kGradThreads, 1) kda_bwd_grad_kernel(BwdParams p) { grad_chunks(p); }
 
 }  // namespace kda

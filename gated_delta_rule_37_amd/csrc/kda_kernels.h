@@ -114,6 +114,7 @@ struct BwdParams {
   int32_t* smap;
   const float* rvbuf;     // per chunk slot: V - Kr R (checkpoint launch), [32][V]
   float* dubuf;           // per chunk slot: dU = P^T dO + Kc D (chain launch), [32][V]
+  int32_t nslots;         // chunk slots (slots x hn < 2^31)
 };
 
 __global__ void kda_chunk_kernel(ChunkParams p);
@@ -125,7 +126,7 @@ __global__ void kda_carry_kernel(ChunkParams p);
 __global__ void kda_ckpt_kernel(ChunkParams p);   // kCarryThreads threads
 __global__ void kda_bwd_chain_e_kernel(BwdParams p);   // kChainThreads threads, one per (piece, head)
 __global__ void kda_bwd_chain_kernel(BwdParams p);     // kChainThreads threads, one per (fragment, head)
-__global__ void kda_bwd_grad_kernel(BwdParams p);      // kGradThreads threads, one per (chunk slot, head)
+__global__ void kda_bwd_grad_kernel(BwdParams p);      // kGradThreads threads, persistent over (chunk slot, head)
 __global__ void kda_compose_kernel(ComposeParams p);
 __global__ void kda_compose_reverse_kernel(ComposeParams p);
 __global__ void kda_fold_pieces_kernel(ComposeParams p);
