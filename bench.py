@@ -541,12 +541,33 @@ def measure_backward(args, w, x, torch, kda):
                       "fp32_mfma_peak": PEAK_FP32_TFLOPS,
                       "ratio_to_fp32_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
     })
-    return {
+    res = {
         "ms_per_call": round(ms, 3),
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "calls": args.backward_steps,
         "roofline": roof,
     }
+    if not plan.pieces:
+        # kda_backward_from_forward: the same gradients from the forward's own
+        # transitions and carry-ins (a training step keeps them), timed alike
+        fwd = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"])
+        saved = (fwd["transitions"], fwd["carry_in"])
+
+        def call_saved():
+            return kda.backward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, saved=saved)
+
+        call_saved()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.backward_steps):
+            call_saved()
+        e1.record()
+        torch.cuda.synchronize()
+        ms2 = e0.elapsed_time(e1) / args.backward_steps
+        res["from_forward"] = {"ms_per_call": round(ms2, 3), "tokens_per_s": round(w.T / (ms2 * 1e-3), 1),
+                               "scope": "kda_backward_from_forward: the forward's transitions and carry-ins "
+                                        "read, not recomputed"}
+    return res
 
 
 if __name__ == "__main__":

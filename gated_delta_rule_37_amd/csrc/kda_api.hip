@@ -353,17 +353,17 @@ extern "C" size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, 
   return backward_workspace_need(plan, H);
 }
 
-extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
-                            const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
-                            const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
-                            const uint16_t* beta, size_t beta_bytes, const float* initial_state,
-                            size_t initial_state_bytes, const float* d_o, size_t d_o_bytes,
-                            const float* d_final, size_t d_final_bytes, int32_t H, int32_t K, int32_t V,
-                            int32_t head_begin, int32_t head_count, float* dq, size_t dq_bytes, float* dk,
-                            size_t dk_bytes, float* dv, size_t dv_bytes, float* dg, size_t dg_bytes,
-                            float* dbeta, size_t dbeta_bytes, float* d_initial_state,
-                            size_t d_initial_state_bytes, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+// kda_backward, and with `saved_transitions` / `saved_carry` non-null its
+// variant that takes the forward's A_r and C_r instead of recomputing them.
+int backward_impl(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes, const uint16_t* q,
+                  size_t q_bytes, const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes,
+                  const uint16_t* g, size_t g_bytes, const uint16_t* beta, size_t beta_bytes,
+                  const float* initial_state, size_t initial_state_bytes, const float* d_o, size_t d_o_bytes,
+                  const float* d_final, size_t d_final_bytes, int32_t H, int32_t K, int32_t V, int32_t head_begin,
+                  int32_t head_count, float* dq, size_t dq_bytes, float* dk, size_t dk_bytes, float* dv,
+                  size_t dv_bytes, float* dg, size_t dg_bytes, float* dbeta, size_t dbeta_bytes,
+                  float* d_initial_state, size_t d_initial_state_bytes, const float* saved_transitions,
+                  const float* saved_carry, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_backward(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes,
                                 beta, beta_bytes, initial_state, initial_state_bytes, d_o, d_o_bytes, d_final,
                                 d_final_bytes, H, K, V, head_begin, head_count, dq, dq_bytes, dk, dk_bytes, dv,
@@ -390,18 +390,22 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   }
   const kda::BwdLayout W = kda::backward_layout(plan, H);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* transitions = reinterpret_cast<float*>(ws + W.transitions);
+  const bool saved = saved_transitions != nullptr;
+  float* transitions = saved ? const_cast<float*>(saved_transitions) : reinterpret_cast<float*>(ws + W.transitions);
   float* updates = reinterpret_cast<float*>(ws + W.updates);
-  float* carry = reinterpret_cast<float*>(ws + W.carry);
+  float* carry = saved ? const_cast<float*>(saved_carry) : reinterpret_cast<float*>(ws + W.carry);
   float* esum = reinterpret_cast<float*>(ws + W.esum);
   float* dcarry = reinterpret_cast<float*>(ws + W.dcarry);
-  // the forward's summaries and carry-ins, without the safe gate
-  st = launch_summaries(plan, plan_dev, k, v, g, beta, -INFINITY, initial_state, H, head_begin, head_count,
-                        transitions, updates, ws + W.cache, stream, /*fold=*/false);
-  if (st != KDA_OK) return st;
-  st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream,
-                      /*pieces=*/true);
-  if (st != KDA_OK) return st;
+  // the forward's summaries and carry-ins, without the safe gate (read-only
+  // from here on when the caller saved them)
+  if (!saved) {
+    st = launch_summaries(plan, plan_dev, k, v, g, beta, -INFINITY, initial_state, H, head_begin, head_count,
+                          transitions, updates, ws + W.cache, stream, /*fold=*/false);
+    if (st != KDA_OK) return st;
+    st = launch_compose(plan, plan_dev, transitions, updates, H, head_begin, head_count, carry, stream,
+                        /*pieces=*/true);
+    if (st != KDA_OK) return st;
+  }
   // the checkpoint launch: every fragment forward from its carry-in (or its
   // initial state, or zero), the anchored state entering every 32-token chunk
   // and its T diag(beta); fragments that leave the anchored form's range are
@@ -508,4 +512,48 @@ extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_
   hipLaunchKernelGGL(kda::kda_bwd_grad_kernel, dim3(static_cast<uint32_t>(ggrid)), dim3(kda::kGradThreads), 0,
                      stream, p);
   return finish_launch();
+}
+
+extern "C" int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                            const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                            const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                            const uint16_t* beta, size_t beta_bytes, const float* initial_state,
+                            size_t initial_state_bytes, const float* d_o, size_t d_o_bytes,
+                            const float* d_final, size_t d_final_bytes, int32_t H, int32_t K, int32_t V,
+                            int32_t head_begin, int32_t head_count, float* dq, size_t dq_bytes, float* dk,
+                            size_t dk_bytes, float* dv, size_t dv_bytes, float* dg, size_t dg_bytes,
+                            float* dbeta, size_t dbeta_bytes, float* d_initial_state,
+                            size_t d_initial_state_bytes, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return backward_impl(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                       beta_bytes, initial_state, initial_state_bytes, d_o, d_o_bytes, d_final, d_final_bytes, H, K,
+                       V, head_begin, head_count, dq, dq_bytes, dk, dk_bytes, dv, dv_bytes, dg, dg_bytes, dbeta,
+                       dbeta_bytes, d_initial_state, d_initial_state_bytes, nullptr, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" int kda_backward_from_forward(
+    const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes, const uint16_t* q, size_t q_bytes,
+    const uint16_t* k, size_t k_bytes, const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+    const uint16_t* beta, size_t beta_bytes, const float* initial_state, size_t initial_state_bytes,
+    const float* d_o, size_t d_o_bytes, const float* d_final, size_t d_final_bytes, int32_t H, int32_t K,
+    int32_t V, int32_t head_begin, int32_t head_count, const float* transitions, size_t transitions_bytes,
+    const float* carry_in, size_t carry_in_bytes, float* dq, size_t dq_bytes, float* dk, size_t dk_bytes,
+    float* dv, size_t dv_bytes, float* dg, size_t dg_bytes, float* dbeta, size_t dbeta_bytes,
+    float* d_initial_state, size_t d_initial_state_bytes, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  int st = check_dims(plan, plan_dev, H, K, V);
+  if (st != KDA_OK) return st;
+  // a pieces plan's backward works on the pieces' transitions, which the
+  // forward folds into its segments' and does not return
+  if (plan->pieces) return KDA_ERR_UNSUPPORTED;
+  // (the carry-ins stand in for the updates, which this call does not read)
+  st = check_compose(plan, plan_dev, plan_dev_bytes, transitions, transitions_bytes, carry_in, carry_in_bytes, H,
+                     K, V, head_begin, head_count, carry_in, carry_in_bytes);
+  if (st != KDA_OK) return st;
+  return backward_impl(plan, plan_dev, plan_dev_bytes, q, q_bytes, k, k_bytes, v, v_bytes, g, g_bytes, beta,
+                       beta_bytes, initial_state, initial_state_bytes, d_o, d_o_bytes, d_final, d_final_bytes, H, K,
+                       V, head_begin, head_count, dq, dq_bytes, dk, dk_bytes, dv, dv_bytes, dg, dg_bytes, dbeta,
+                       dbeta_bytes, d_initial_state, d_initial_state_bytes, transitions, carry_in, workspace,
+                       workspace_bytes, stream);
 }

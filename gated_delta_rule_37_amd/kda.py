@@ -51,7 +51,7 @@ SYMBOLS = (
     "kda_plan_destroy",
     "kda_summary_bytes", "kda_workspace_bytes", "kda_segment_summaries", "kda_compose_summaries",
     "kda_apply_carry", "kda_forward", "kda_forward_noalloc", "kda_noalloc_max_workspace_bytes",
-    "kda_backward", "kda_backward_workspace_bytes", "kda_status_string", "kda_last_hip_error",
+    "kda_backward", "kda_backward_from_forward", "kda_backward_workspace_bytes", "kda_status_string", "kda_last_hip_error",
 )
 
 
@@ -113,6 +113,9 @@ def lib() -> ctypes.CDLL:
     L.kda_forward_noalloc.restype = ctypes.c_int
     L.kda_backward.argtypes = [p, *buf, *buf * 5, *buf, *buf, *buf, *dims, *buf * 6, *buf, p]
     L.kda_backward.restype = ctypes.c_int
+    L.kda_backward_from_forward.argtypes = [p, *buf, *buf * 5, *buf, *buf, *buf, *dims, *buf * 2, *buf * 6, *buf,
+                                            p]
+    L.kda_backward_from_forward.restype = ctypes.c_int
     L.kda_backward_workspace_bytes.argtypes = [p, i32, i32, i32]
     L.kda_backward_workspace_bytes.restype = sz
     L.kda_noalloc_max_workspace_bytes.argtypes = []
@@ -347,11 +350,14 @@ def forward_noalloc(plan: Plan, plan_dev: torch.Tensor, q, k, v, g, beta, out, s
 
 
 def backward(plan: Plan, q, k, v, g, beta, d_o, d_final=None, initial_state=None, want_dh0=False,
-             stream=None, heads=None, sentinel=None):
+             stream=None, heads=None, sentinel=None, saved=None):
     """``kda_backward``: gradients of L = sum <o, d_o> + sum <final, d_final>.
     Returns dict(dq, dk, dv, dg, dbeta, dh0) (fp32; dh0 None unless wanted).
     ``heads`` = (begin, count) restricts the call to those heads; the output
-    buffers are filled with ``sentinel`` first when it is given."""
+    buffers are filled with ``sentinel`` first when it is given.  ``saved`` =
+    (transitions, carry_in) as the forward wrote them (no gate lower bound)
+    calls ``kda_backward_from_forward``, which reads them instead of
+    recomputing them."""
     T, H, K = k.shape
     V = v.shape[2]
     dev = q.device
@@ -375,10 +381,18 @@ def backward(plan: Plan, q, k, v, g, beta, d_o, d_final=None, initial_state=None
     ])
     ws_bytes = int(lib().kda_backward_workspace_bytes(plan.handle, H, K, V))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    st = lib().kda_backward(plan.handle, *_plan_dev(plan, plan.device_blob(dev)), *ins, H, K, V,
-                            *_heads(H, heads), *grads, *_buf(ws, torch.uint8, None, "workspace"),
-                            _stream(q, stream))
-    _check(st, "kda_backward")
+    if saved is None:
+        st = lib().kda_backward(plan.handle, *_plan_dev(plan, plan.device_blob(dev)), *ins, H, K, V,
+                                *_heads(H, heads), *grads, *_buf(ws, torch.uint8, None, "workspace"),
+                                _stream(q, stream))
+        _check(st, "kda_backward")
+        return out
+    kept = _flat([_buf(saved[0], torch.float32, (plan.S, H, K, V), "transitions"),
+                  _buf(saved[1], torch.float32, (plan.S, H, K, V), "carry_in")])
+    st = lib().kda_backward_from_forward(plan.handle, *_plan_dev(plan, plan.device_blob(dev)), *ins, H, K, V,
+                                         *_heads(H, heads), *kept, *grads,
+                                         *_buf(ws, torch.uint8, None, "workspace"), _stream(q, stream))
+    _check(st, "kda_backward_from_forward")
     return out
 
 

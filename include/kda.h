@@ -368,11 +368,14 @@ size_t kda_noalloc_max_workspace_bytes(void);
  * following summaries): the call recomputes the forward's transitions and
  * carry-ins, forms each carried segment's backward summary E_r (the
  * cotangent at its start due to its first fragment's own outputs), scans
- * D_{r-1} = A_r^T D_r + E_r in reverse, and reverses every (fragment, head)
- * in FP32 one token at a time from its carry-in and D_r.  Workspace:
- * kda_backward_workspace_bytes(plan, H, K, V) bytes, caller-owned, contents
- * not needed afterwards.  Arguments, sizes and errors as for the forward's
- * device calls (each buffer with its byte count).
+ * D_{r-1} = A_r^T D_r + E_r in reverse, and then works per 32-token chunk on
+ * the matrix cores: the state entering every chunk (forward from its
+ * carry-in), the cotangent leaving every chunk (backward from D_r), and every
+ * chunk's gradients from those two.  A (fragment, head) whose gates leave the
+ * chunk form's exponent range is reversed in FP32 one token at a time
+ * instead.  Workspace: kda_backward_workspace_bytes(plan, H, K, V) bytes,
+ * caller-owned, contents not needed afterwards.  Arguments, sizes and errors
+ * as for the forward's device calls (each buffer with its byte count).
  */
 int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
                  const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
@@ -387,12 +390,43 @@ int kda_backward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_
                  float* d_initial_state, size_t d_initial_state_bytes,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kda_backward_from_forward -- kda_backward for a caller that kept the
+ * forward's segment transitions A_r and carry-ins C_r (`transitions` and
+ * `carry_in` [S, H, K, V] fp32 as kda_forward, or kda_segment_summaries and
+ * kda_compose_summaries, wrote them for this plan, these inputs and initial
+ * states, and no gate lower bound): the call reads them instead of
+ * recomputing them (it skips kda_backward's first two launches) and
+ * otherwise does and returns exactly what kda_backward does.  Read only;
+ * the heads [head_begin, head_begin + head_count) of both must be current.
+ * A plan with pieces gives KDA_ERR_UNSUPPORTED: its backward works on the
+ * pieces' own transitions, which the forward folds away.  Other arguments,
+ * sizes, workspace and errors as kda_backward.
+ */
+int kda_backward_from_forward(const kda_plan* plan, const int32_t* plan_dev, size_t plan_dev_bytes,
+                              const uint16_t* q, size_t q_bytes, const uint16_t* k, size_t k_bytes,
+                              const uint16_t* v, size_t v_bytes, const uint16_t* g, size_t g_bytes,
+                              const uint16_t* beta, size_t beta_bytes,
+                              const float* initial_state, size_t initial_state_bytes,
+                              const float* d_o, size_t d_o_bytes, const float* d_final, size_t d_final_bytes,
+                              int32_t H, int32_t K, int32_t V, int32_t head_begin, int32_t head_count,
+                              const float* transitions, size_t transitions_bytes,
+                              const float* carry_in, size_t carry_in_bytes,
+                              float* dq, size_t dq_bytes, float* dk, size_t dk_bytes,
+                              float* dv, size_t dv_bytes, float* dg, size_t dg_bytes,
+                              float* dbeta, size_t dbeta_bytes,
+                              float* d_initial_state, size_t d_initial_state_bytes,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of kda_backward's workspace for H heads (each part 256-byte
- * aligned): kda_workspace_bytes(plan, H); five arrays of S * H states
+ * aligned): kda_workspace_bytes(plan, H); five arrays of P * H states
  * (transitions, updates, carry-ins, backward summaries and their reverse
- * compose, per piece); (floor(T/16) + F) * H state checkpoints (a state is
- * 64 KiB); T * H * 1 KiB for every token's u and p.  0 for a NULL plan, H <= 0 or
- * K, V other than 128. */
+ * compose, per piece; P = S without pieces); (floor(T/16) + F) * H state
+ * checkpoints and T * H * 1 KiB (every token's u and p) for the
+ * token-by-token path; per 32-token chunk slot (ceil(T/32) + F of them) and
+ * head, a state and a cotangent (64 KiB each), the chunk's T (4 KiB) and two
+ * [32, V] fp32 tiles (16 KiB each); F * H path flags and the slot map (int32).
+ * A state is 64 KiB.  0 for a NULL plan, H <= 0 or K, V other than 128. */
 size_t kda_backward_workspace_bytes(const kda_plan* plan, int32_t H, int32_t K, int32_t V);
 
 /* Human-readable name of a kda_status value. */

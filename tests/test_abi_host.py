@@ -332,6 +332,48 @@ def test_backward_validates_before_launch():
     assert L.kda_last_hip_error() == 0
 
 
+def test_backward_from_forward_validates_before_launch():
+    """kda_backward_from_forward checks the saved transitions and carry-ins
+    (shape [S, H, K, V] fp32 each) beside kda_backward's arguments, and
+    refuses a plan with pieces (fake, never dereferenced buffers)."""
+    L = kda.lib()
+    H, T, N = 2, 100, 2
+
+    def sizes(plan):
+        S = plan.S
+        return dict(plan_dev=4 * len(plan.blob), q=T * H * 256, k=T * H * 256, v=T * H * 256, g=T * H * 256,
+                    beta=T * H * 2, init=N * H * 65536, do=T * H * 512, dfinal=N * H * 65536,
+                    trans=S * H * 65536, carry=S * H * 65536, dq=T * H * 512, dk=T * H * 512, dv=T * H * 512,
+                    dg=T * H * 512, dbeta=T * H * 4, dh0=N * H * 65536,
+                    ws=L.kda_backward_workspace_bytes(plan.handle, H, 128, 128))
+
+    def call(plan, K=128, **over):
+        need = sizes(plan)
+        order = ("plan_dev", "q", "k", "v", "g", "beta", "init", "do", "dfinal", "trans", "carry", "dq", "dk",
+                 "dv", "dg", "dbeta", "dh0", "ws")
+        args = [plan.handle]
+        for name in order:
+            if name == "trans":
+                args += [H, K, 128, 0, H]
+            args += [over.get(name, _FAKE), over.get(name + "_bytes", need[name])]
+        args.append(None)
+        return L.kda_backward_from_forward(*args)
+
+    plan = kda.Plan([0, 70, 100], 2)
+    need = sizes(plan)
+    assert call(plan, K=64) == -4
+    assert call(plan, trans=0) == -1
+    assert call(plan, carry=0) == -1
+    assert call(plan, trans_bytes=need["trans"] - 1) == -9
+    assert call(plan, carry_bytes=need["carry"] - 1) == -9
+    assert call(plan, carry=_FAKE + 4) == -5
+    assert call(plan, ws_bytes=need["ws"] - 1) == -8
+    pieces = kda.Plan([0, 100], 1, None, 32)
+    assert pieces.pieces
+    assert call(pieces) == -4
+    assert L.kda_last_hip_error() == 0
+
+
 PIECES_GOLDEN = os.path.join(ROOT, "tests", "golden", "plan_pieces_cases.json")
 
 

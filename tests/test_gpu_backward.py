@@ -131,6 +131,36 @@ def test_backward_deterministic():
             assert torch.equal(o[key], outs[0][key]), key
 
 
+def test_backward_from_forward_matches_backward():
+    """kda_backward_from_forward with the forward's own transitions and
+    carry-ins (kda_forward's outputs, no gate bound) gives kda_backward's
+    gradients bit for bit (the same launches on the same values), over all
+    heads and over a head range, with initial states and a final cotangent."""
+    T, H, cu = 300, 4, [0, 100, 300]
+    x = synth.make_inputs(T, H, 128, 128, seed=81, cu_seqlens=cu)
+    N = len(cu) - 1
+    gen = torch.Generator().manual_seed(82)
+    d_o = torch.randn(T, H, 128, generator=gen).cuda()
+    d_final = torch.randn(N, H, 128, 128, generator=gen).cuda()
+    h0 = synth.initial_states(N, H, 128, 128, seed=83).cuda()
+    plan = kda.Plan(cu, 5)
+    d = pu.to_device(x)
+    fwd = kda.forward(plan, d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=h0)
+    saved = (fwd["transitions"], fwd["carry_in"])
+    args = (plan, d["q"], d["k"], d["v"], d["g"], d["beta"], d_o)
+    kw = dict(d_final=d_final, initial_state=h0, want_dh0=True)
+    full = kda.backward(*args, **kw)
+    kept = kda.backward(*args, **kw, saved=saved)
+    part = kda.backward(*args, **kw, saved=saved, heads=(1, 2), sentinel=-5.0)
+    torch.cuda.synchronize()
+    print(f"[from_forward] T={T} H={H} segments=5", flush=True)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(full[key], kept[key]), key
+        hs = (slice(None), slice(1, 3))
+        assert torch.equal(full[key][hs], part[key][hs]), key
+        assert (part[key][:, 0] == -5.0).all() and (part[key][:, 3] == -5.0).all(), key
+
+
 def test_bench_workload_last_segments_sampled_head():
     """The backward at the bench workload's full size (65536 tokens x 32
     heads, 64 segments) as bench.py runs it.  One head's gradients over the
