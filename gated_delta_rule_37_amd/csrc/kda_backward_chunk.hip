@@ -49,6 +49,10 @@ constexpr int VD = 128;
 constexpr int CH = 32;
 constexpr int NB = 136;   // row stride (bf16) of the gradient launch's token-major [32][128] planes
 constexpr int NC = 152;   // the chain launch's (conflict-free transposed reads; more LDS)
+// Cache policy of stores that nothing in the same launch reads back (the
+// cotangents, dU and the gradients): non-temporal, leaving the caches to the
+// launch's own inputs.
+constexpr int kWriteOnce = 2;
 constexpr int TB = 40;    // row stride (bf16) of the 32 x 32 matrices (columns in k-slot order)
 constexpr int FS = 36;    // row stride (fp32) of the 16 x 16 solve tiles
 constexpr int AS = 33;    // row stride (fp32) of A'
@@ -422,7 +426,7 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Dl[dt][4 * r + e]), rsd, voff,
-                                                  4 * (32 * dt + 8 * r + e) * VD, 0);
+                                                  4 * (32 * dt + 8 * r + e) * VD, kWriteOnce);
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -451,7 +455,8 @@ __device__ __forceinline__ void chain_owner(const BwdParams& p, ChainSmem& sm, c
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Y[4 * r + e]), rsu, voff, 4 * (8 * r + e) * VD, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Y[4 * r + e]), rsu, voff, 4 * (8 * r + e) * VD,
+                                                kWriteOnce);
     }
     bf16x8 uh[2], ul[2];
     tile_kslots_split(Y, uh, ul);
@@ -699,7 +704,7 @@ __device__ __forceinline__ void store_rows(float* base, const int H, const int n
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(t[4 * r + e]), rs, voff, static_cast<int>((8 * r + e) * rowf),
-                                            0);
+                                            kWriteOnce);
 }
 
 // Row fragments of a state (channel row, all 128 values in k-slot order):

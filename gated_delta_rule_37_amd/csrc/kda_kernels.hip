@@ -63,9 +63,10 @@ constexpr float kGateFloor = -300.f;
 // Buffer resource word 3 for gfx9 raw (unswizzled, 32-bit) buffer access;
 // accesses at or past num_records read zero and drop writes.
 constexpr int kBufDword3 = 0x00020000;
-// Cache policy of the o stores: non-temporal (nt).  o is written once per
-// launch and read by nothing in it; streaming it past the caches leaves
-// them to the inputs and the chunk cache (the carry launch ~1% faster).
+// Cache policy of the o stores (and the checkpoint launch's states and
+// V - Kr R tiles): non-temporal (nt).  They are written once per launch and
+// read by nothing in it; streaming them past the caches leaves them to the
+// inputs and the chunk cache (the carry launch ~1% faster).
 constexpr int kStreamAux = 2;
 
 enum Mode { kModeFwd = 0, kModeSumS = 1, kModeSumPhi = 2, kModeCkpt = 3 };
@@ -536,7 +537,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(D[4 * r + e]), rsv, 4 * (4 * lh * VD + col),
-                                                4 * (8 * r + e) * VD, 0);
+                                                4 * (8 * r + e) * VD, kStreamAux);
       // the T helpers leave T unscaled in this mode (the cache keeps T for
       // the backward): U = T diag(beta) D, with beta read in products(n)
       // (the operand helpers rewrite this buffer in step 2n+1)
@@ -709,7 +710,7 @@ __device__ __forceinline__ void pipe_owner(const ChunkParams& p, PipeSmem& sm, c
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(R[dt][4 * r + e]), rs, voff,
-                                                4 * (32 * dt + 8 * r + e) * VD, 0);
+                                                4 * (32 * dt + 8 * r + e) * VD, kStreamAux);
   };
 
   block_sync();   // steps -3 .. -1: the helpers fill the pipeline
